@@ -1,0 +1,242 @@
+"""CPU oracle for LRMoE's pruned MoE expert backward -- TEST INFRASTRUCTURE.
+
+Only the test suite, the smoke check and the CPU-baseline leg of the benchmark
+may import this module.  The product path (the HIP library and its Python
+binding) never calls it, and this module imports nothing from the product.
+
+It is a plain, slow, step-by-step restatement of what the pages describe,
+in float64 arithmetic with exact Python/numpy integers for quotas and
+indices.  Page titles used in citations:
+
+  [EN] "LRMoE: Trimming Backward Work in Memory-Bound MoE Training"
+       (aimodeling.com news article, English text).
+  [PT] "LRMoE poda a passagem reversa do MoE e acelera o treinamento em 21-45%"
+       (news.hamidun.com, Portuguese write-up).
+
+Steps, in the pages' order:
+  plan_quota      quota q_e per expert, fixed before the backward
+                  ([EN] "Backward demand is not a constant"; [PT] bullet
+                  "Cotas antes do calculo").
+  lrm_scores      R_u = alpha_u^2 * ||g_t||^2 * ||phi_u||^2
+                  ([EN] "LRM: a decomposable contribution score").
+  select_top_quota  per expert, keep the q_e highest-scoring pairs
+                  ([PT] bullet "Selecao pela metrica LRM").
+  compact         pack kept rows into contiguous expert segments
+                  ([EN] "The part that is easy to get wrong"; [PT] bullet
+                  "Compactacao fisica").
+  weight_grad     dW_e = sum over kept u of (alpha_u g_t) phi_u^T
+                  ([EN] "LRM: ..." defines the per-pair outer product).
+  input_grad      dphi_u = alpha_u W_e^T g_t for kept u, zero for dropped u,
+                  in the original pair layout ([PT] "Compactacao fisica":
+                  the result goes back to the original layout afterwards).
+
+Readings where the pages are silent (each also listed in the design notes):
+  * quota rounding: q_e = floor(n_e * num / den) for a keep ratio num/den,
+    or floor(n_e * Q / P) for a budget of Q pairs over P routed pairs;
+  * ties in R go to the lower original pair index;
+  * segments in ascending expert id, ascending pair index inside a segment;
+  * dropped pairs contribute nothing: their dphi rows are zero.
+
+Pins: every function here is checked in tests/test_oracle_pins.py against
+something other than itself (brute force of the definition, the pages'
+worked example, autograd of the dense layer, algebraic identities).  The
+budget quota rule is a workload definition with no external value to pin
+against: parity unpinned for plan_quota's "budget" mode.
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import numpy as np
+
+
+# ---------------------------------------------------------------- storage
+
+def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 value of stored inputs: bfloat16 bit patterns (uint16)
+    are widened by placing them in the top half of a float32."""
+    if dtype == "bf16":
+        assert a.dtype == np.uint16
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    assert a.dtype == np.float32
+    return a.astype(np.float64)
+
+
+# ---------------------------------------------------------------- a0: quota
+
+def plan_quota(counts: Sequence[int], policy: tuple) -> list:
+    """Per-expert backward retention quota, fixed before the backward.
+
+    ("ratio", num, den): keep floor(n_e * num / den) pairs -- C-level Cx keeps
+    (100 - x)/100 of each expert's pairs ([EN] "What the measurements show"
+    names C0..C30 by the fraction of backward pairs dropped).
+    ("budget", Q): a fixed number Q of pairs for the layer call, shared in
+    proportion to demand, q_e = floor(n_e * Q / P)."""
+    n = [int(c) for c in counts]
+    assert all(c >= 0 for c in n)
+    if policy[0] == "ratio":
+        num, den = int(policy[1]), int(policy[2])
+        assert den > 0 and 0 <= num <= den
+        q = [(c * num) // den for c in n]
+    elif policy[0] == "budget":
+        Q, P = int(policy[1]), sum(n)
+        assert Q >= 0
+        q = [c if P == 0 else min(c, (c * Q) // P) for c in n]
+    else:
+        raise ValueError(policy)
+    return q
+
+
+# ---------------------------------------------------------------- a1: score
+
+def lrm_scores(alpha, g, phi, row_index, dtype, block_rows: int = 4096) -> np.ndarray:
+    """R_u = alpha_u^2 * ||g_t(u)||_2^2 * ||phi_u||_2^2 for every pair u.
+
+    This is the squared Frobenius norm of the rank-one per-pair weight
+    gradient (alpha_u g_t) phi_u^T, factorised ([EN] "LRM: a decomposable
+    contribution score")."""
+    P = phi.shape[0]
+    a = alpha.astype(np.float64)
+    gsq = np.empty(g.shape[0])
+    for lo in range(0, g.shape[0], block_rows):
+        gb = to_f64(g[lo:lo + block_rows], dtype)
+        gsq[lo:lo + block_rows] = np.einsum("ij,ij->i", gb, gb)
+    psq = np.empty(P)
+    for lo in range(0, P, block_rows):
+        pb = to_f64(phi[lo:lo + block_rows], dtype)
+        psq[lo:lo + block_rows] = np.einsum("ij,ij->i", pb, pb)
+    rows = np.arange(P) if row_index is None else row_index.astype(np.int64)
+    assert np.all(np.isfinite(a)) and np.all(np.isfinite(gsq)) and np.all(np.isfinite(psq))
+    return a * a * gsq[rows] * psq
+
+
+# ---------------------------------------------------------------- a2: select
+
+def select_top_quota(scores: np.ndarray, counts, quotas):
+    """Per expert, keep the q_e pairs with the highest score; equal scores
+    are ordered by ascending pair index.  Returns (keep bool[P],
+    tau list): tau[e] is the score of the q_e-th kept pair (None when
+    q_e is 0)."""
+    P = scores.shape[0]
+    keep = np.zeros(P, dtype=bool)
+    taus = []
+    lo = 0
+    for n, q in zip(counts, quotas):
+        n, q = int(n), int(q)
+        assert 0 <= q <= n
+        idx = np.arange(lo, lo + n)
+        order = np.lexsort((idx, -scores[lo:lo + n]))   # by (-R, u)
+        chosen = idx[order[:q]]
+        keep[chosen] = True
+        taus.append(float(scores[chosen[-1]]) if q > 0 else None)
+        lo += n
+    assert lo == P
+    return keep, taus
+
+
+# ---------------------------------------------------------------- a3: compact
+
+def compact(keep: np.ndarray, counts, quotas):
+    """Kept pair indices packed per expert (ascending expert, ascending pair
+    index inside), and the segment offsets [0, q_0, q_0+q_1, ...]."""
+    perm, seg = [], [0]
+    lo = 0
+    for n, q in zip(counts, quotas):
+        kept = lo + np.nonzero(keep[lo:lo + int(n)])[0]      # ascending u
+        assert len(kept) == int(q)
+        perm.append(kept)
+        seg.append(seg[-1] + len(kept))
+        lo += int(n)
+    perm = np.concatenate(perm) if perm else np.zeros(0)
+    return perm.astype(np.int64), np.array(seg, dtype=np.int64)
+
+
+def gather(perm, row_index, g, phi, alpha):
+    """The compacted buffers: rows of g and phi and entries of alpha of the
+    kept pairs, in segment order.  Pure copies of the stored values."""
+    rows = perm if row_index is None else row_index.astype(np.int64)[perm]
+    return g[rows], phi[perm], alpha[perm]
+
+
+# ---------------------------------------------------------------- a4/a5: GEMMs
+
+def weight_grad(seg, alpha_c, g_c, phi_c, dtype, E: int, d_out: int, d_in: int):
+    """dW_e = sum over the kept pairs j of expert e of (alpha_j g_j) phi_j^T,
+    i.e. G_e^T diag(alpha) Phi_e; zero for an expert that keeps nothing."""
+    dW = np.zeros((E, d_out, d_in))
+    for e in range(E):
+        s, t = int(seg[e]), int(seg[e + 1])
+        if t > s:
+            ga = alpha_c[s:t].astype(np.float64)[:, None] * to_f64(g_c[s:t], dtype)
+            dW[e] = ga.T @ to_f64(phi_c[s:t], dtype)
+    return dW
+
+
+def input_grad(seg, perm, alpha_c, g_c, W, dtype, P: int):
+    """dphi_u = alpha_u W_e^T g_t for kept pairs, written back at the pair's
+    original row; rows of dropped pairs stay zero."""
+    E, d_out, d_in = W.shape
+    dphi = np.zeros((P, d_in))
+    for e in range(E):
+        s, t = int(seg[e]), int(seg[e + 1])
+        if t > s:
+            rows = to_f64(g_c[s:t], dtype) @ to_f64(W[e], dtype)
+            dphi[perm[s:t]] = alpha_c[s:t].astype(np.float64)[:, None] * rows
+    return dphi
+
+
+# ---------------------------------------------------------------- whole path
+
+def pruned_backward(counts, policy, alpha, g, phi, W, row_index, dtype,
+                    with_grads: bool = True, gate_up=None) -> dict:
+    """plan -> score -> select -> compact -> dW, dphi (and, when gate_up =
+    (g2, x, W2) is given, the second projection's dW and dx on the same keep
+    set and permutation)."""
+    E, d_out, d_in = W.shape
+    P = phi.shape[0]
+    q = plan_quota(counts, policy)
+    R = lrm_scores(alpha, g, phi, row_index, dtype)
+    keep, taus = select_top_quota(R, counts, q)
+    perm, seg = compact(keep, counts, q)
+    out = dict(quotas=q, scores=R, keep=keep, taus=taus, perm=perm, seg=seg)
+    if with_grads:
+        g_c, phi_c, alpha_c = gather(perm, row_index, g, phi, alpha)
+        out["dW"] = weight_grad(seg, alpha_c, g_c, phi_c, dtype, E, d_out, d_in)
+        out["dphi"] = input_grad(seg, perm, alpha_c, g_c, W, dtype, P)
+        if gate_up is not None:
+            g2, x, W2 = gate_up
+            g2_c, x_c, _ = gather(perm, None, g2, x, alpha)
+            out["dW2"] = weight_grad(seg, alpha_c, g2_c, x_c, dtype, E, W2.shape[1], W2.shape[2])
+            out["dx"] = input_grad(seg, perm, alpha_c, g2_c, W2, dtype, P)
+    return out
+
+
+# ---------------------------------------------------------------- sampled outputs
+
+def weight_grad_block(seg, perm, row_index, alpha, g, phi, dtype, e: int,
+                      o_idx, i_idx) -> np.ndarray:
+    """dW_e[o_idx][:, i_idx] for large problems: the same sum over the kept
+    pairs of expert e, restricted to the requested rows and columns."""
+    s, t = int(seg[e]), int(seg[e + 1])
+    o_idx, i_idx = np.asarray(o_idx), np.asarray(i_idx)
+    if t == s:
+        return np.zeros((len(o_idx), len(i_idx)))
+    u = perm[s:t]
+    rows = u if row_index is None else row_index.astype(np.int64)[u]
+    ga = alpha[u].astype(np.float64)[:, None] * to_f64(g[rows][:, o_idx], dtype)
+    return ga.T @ to_f64(phi[u][:, i_idx], dtype)
+
+
+def input_grad_rows(counts, keep, row_index, alpha, g, W, dtype, pairs) -> np.ndarray:
+    """dphi for the requested original pair indices (zero rows for dropped
+    pairs)."""
+    offs = np.concatenate([[0], np.cumsum(np.asarray(counts, dtype=np.int64))])
+    out = np.zeros((len(pairs), W.shape[2]))
+    for k, u in enumerate(pairs):
+        u = int(u)
+        if not keep[u]:
+            continue
+        e = int(np.searchsorted(offs, u, side="right") - 1)
+        r = u if row_index is None else int(row_index[u])
+        out[k] = float(alpha[u]) * (to_f64(W[e], dtype).T @ to_f64(g[r], dtype))
+    return out
