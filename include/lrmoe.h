@@ -1,0 +1,195 @@
+/*
+ * lrmoe.h -- C ABI of the MI355X (gfx950) pruned MoE expert backward.
+ *
+ * The library implements, for the experts local to one GPU, the backward of
+ * one expert projection y = W_e phi under LRMoE's pruning:
+ *
+ *   1. quota     q_e pairs kept per expert, fixed before the backward
+ *                ("LRMoE: Trimming Backward Work in Memory-Bound MoE Training",
+ *                section "Backward demand is not a constant").
+ *   2. score     R_u = alpha_u^2 * ||g_t||^2 * ||phi_u||^2 for each routed pair
+ *                u = (t, e) (same article, section "LRM: a decomposable
+ *                contribution score").
+ *   3. select    per expert, the q_e pairs with the highest R_u
+ *                ("LRMoE poda a passagem reversa do MoE ...", bullet on
+ *                selection by the LRM metric).
+ *   4. compact   kept g rows, phi rows and alpha packed into contiguous,
+ *                expert-segmented, unpadded buffers (English article, section
+ *                "The part that is easy to get wrong"; Portuguese write-up,
+ *                bullet on physical compaction).
+ *   5. GEMMs     dW_e = sum_kept (alpha_u g_t) phi_u^T and
+ *                dphi_u = alpha_u W_e^T g_t, written back to the original pair
+ *                layout (English article, "LRM: ..." for the per-pair outer
+ *                product; Portuguese write-up, compaction bullet, for the
+ *                return to the original layout).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pairs are expert-sorted: pairs [off_e, off_e + n_e) belong to local
+ *    expert e, off_e = n_0 + ... + n_{e-1}.  Pair index u is the row of phi.
+ *  - Tensors are dense row-major.  g is [T, d_out], phi is [P, d_in], W is
+ *    [E, d_out, d_in] (W_e maps phi in R^d_in to y in R^d_out), dW is
+ *    [E, d_out, d_in] float32, dphi is [P, d_in] float32.
+ *  - Storage type of g, phi, W and of the compacted g_c, phi_c is given by
+ *    lrmoe_problem.dtype (bfloat16 or float32).  Arithmetic is float32
+ *    (bf16 matrix cores with float32 accumulation for the GEMMs).
+ *  - Counts and quotas are HOST arrays, read during the call only.  Every
+ *    other pointer is a DEVICE pointer, used asynchronously in the order of
+ *    `stream` (a hipStream_t; NULL means the null stream).  The caller owns
+ *    all memory; the library allocates nothing and keeps no state between
+ *    calls, so calls on different streams may run concurrently if their
+ *    buffers are disjoint.  Outputs must not alias inputs.
+ *  - Device pointers must be 16-byte aligned.  d_out and d_in must be
+ *    multiples of 8 (bf16) or 4 (float32).
+ *  - Errors: every host-detectable problem is reported before anything is
+ *    launched, and no entry point aborts or prints.  A failed kernel launch
+ *    returns LRMOE_ERR_HIP; faults inside kernels surface at the caller's
+ *    next synchronisation.
+ */
+#ifndef LRMOE_H
+#define LRMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LRMOE_ABI_VERSION 1
+#define LRMOE_MAX_EXPERTS 256
+
+typedef enum {
+  LRMOE_OK = 0,
+  LRMOE_ERR_NULL = 1,      /* a required pointer is NULL                     */
+  LRMOE_ERR_INVALID = 2,   /* bad expert count, quota or policy              */
+  LRMOE_ERR_SHAPE = 3,     /* sizes inconsistent or out of range             */
+  LRMOE_ERR_ALIGN = 4,     /* pointer or row length misaligned               */
+  LRMOE_ERR_DTYPE = 5,     /* unknown storage type                           */
+  LRMOE_ERR_WORKSPACE = 6, /* workspace smaller than lrmoe_workspace_size    */
+  LRMOE_ERR_HIP = 7        /* a HIP runtime call or launch failed            */
+} lrmoe_status;
+
+typedef enum { LRMOE_F32 = 0, LRMOE_BF16 = 1 } lrmoe_dtype;
+
+typedef enum {
+  /* keep floor(n_e * num / den) pairs of every expert (C-level Cx is
+   * num/den = (100 - x)/100; C0 keeps everything)                          */
+  LRMOE_QUOTA_RATIO = 0,
+  /* a fixed number of pairs for the layer call, shared in proportion to
+   * demand: q_e = min(n_e, floor(n_e * budget_pairs / P))                  */
+  LRMOE_QUOTA_BUDGET = 1
+} lrmoe_quota_mode;
+
+typedef struct {
+  int32_t mode;          /* lrmoe_quota_mode                                */
+  int64_t num, den;      /* RATIO: 0 <= num <= den, den > 0                 */
+  int64_t budget_pairs;  /* BUDGET: >= 0                                    */
+} lrmoe_quota_policy;
+
+/* How the GEMMs fold alpha into the weight gradient.
+ * EXACT (default): alpha*g is split into a bf16 high part and a bf16
+ *   residual and both are multiplied (two matrix-core passes for dW), so dW
+ *   carries float32-level error.
+ * BF16: alpha*g is rounded once to bf16 (the rounding a bf16 training step
+ *   applies); one pass, about 2e-3 relative error in dW.
+ * dphi always applies alpha in float32 after the product.  float32 storage
+ * always splits both operands (three bf16 passes). */
+typedef enum { LRMOE_DW_EXACT = 0, LRMOE_DW_BF16 = 1 } lrmoe_dw_mode;
+
+typedef struct {
+  int32_t E;               /* local experts, 1 .. LRMOE_MAX_EXPERTS          */
+  int32_t dtype;           /* lrmoe_dtype                                    */
+  int64_t P;               /* routed pairs, 0 <= P < 2^31                     */
+  int64_t T;               /* rows of g (T == P when every pair has its row) */
+  int32_t d_out;           /* length of g rows = rows of W_e                 */
+  int32_t d_in;            /* length of phi rows = columns of W_e            */
+  const int64_t* counts;   /* host [E]: n_e, sum = P                          */
+  const int64_t* quotas;   /* host [E]: q_e, 0 <= q_e <= n_e                  */
+  int32_t dw_mode;         /* lrmoe_dw_mode                                  */
+  int32_t reserved;        /* must be 0                                      */
+} lrmoe_problem;
+
+/* ABI version of the loaded library (LRMOE_ABI_VERSION at build time). */
+int32_t lrmoe_abi_version(void);
+
+/* Static English text for a status code (never NULL). */
+const char* lrmoe_status_string(lrmoe_status s);
+
+/* Step 1 (host only, no GPU): quotas_out[e] from counts[e] under `policy`.
+ * Integer arithmetic, floor rounding, no minimum of one (an expert with one
+ * pair at C20 keeps none).  The quota is fixed for the whole layer call.
+ * Errors: NULL pointers; E outside 1..LRMOE_MAX_EXPERTS, a negative count or
+ * a bad policy -> LRMOE_ERR_INVALID. */
+lrmoe_status lrmoe_plan_quota(int32_t E, const int64_t* counts,
+                              const lrmoe_quota_policy* policy,
+                              int64_t* quotas_out);
+
+/* Workspace bytes needed by lrmoe_score_select_compact,
+ * lrmoe_select_compact and lrmoe_grouped_backward for this problem (one
+ * buffer may serve all of them when they run in order on one stream).
+ * Validates the problem like the calls that use it. */
+lrmoe_status lrmoe_workspace_size(const lrmoe_problem* pb, size_t* bytes_out);
+
+/* Steps 2-4.  Inputs: alpha f32 [P]; g [T, d_out]; phi [P, d_in];
+ * g_row_index int32 [P] gives the g row of each pair (NULL when T == P and
+ * pair u uses row u).
+ * Outputs (M = sum of quotas, known to the caller from the host quotas):
+ *   scores      f32 [P]   R_u (float32 arithmetic, norms summed in float32)
+ *   keep        u8  [P]   1 if the pair is kept
+ *   seg_offsets i32 [E+1] exclusive prefix sum of the quotas
+ *   perm        i32 [M]   original pair index of each compacted row; segments
+ *                         in ascending expert order, ascending pair index
+ *                         inside a segment
+ *   g_c [M, d_out], phi_c [M, d_in], alpha_c f32 [M]: bit-exact copies of the
+ *                         kept rows
+ *   dphi_zero   f32 [P, d_in] or NULL: rows of dropped pairs are set to 0 (the
+ *                         kept rows are left for lrmoe_grouped_backward)
+ * Selection: the q_e-th largest score of expert e is the threshold tau_e;
+ * every pair above it is kept and pairs equal to it are kept in ascending
+ * pair index until q_e pairs are kept.  Scores must be finite. */
+lrmoe_status lrmoe_score_select_compact(
+    const lrmoe_problem* pb, const int32_t* g_row_index, const float* alpha,
+    const void* g, const void* phi, float* scores, uint8_t* keep,
+    int32_t* seg_offsets, int32_t* perm, void* g_c, void* phi_c, float* alpha_c,
+    float* dphi_zero, void* workspace, size_t ws_bytes, void* stream);
+
+/* Steps 3-4 on caller-provided scores (float32 [P], finite; -0.0 counts as
+ * 0.0), for scoring rules other than LRM.  Arguments as above. */
+lrmoe_status lrmoe_select_compact(
+    const lrmoe_problem* pb, const float* scores, const int32_t* g_row_index,
+    const float* alpha, const void* g, const void* phi, uint8_t* keep,
+    int32_t* seg_offsets, int32_t* perm, void* g_c, void* phi_c, float* alpha_c,
+    float* dphi_zero, void* workspace, size_t ws_bytes, void* stream);
+
+/* Step 4 alone, for a second projection of the same pairs that inherits an
+ * existing keep set (the gate/up projection of the expert MLP: a pair whose
+ * down-projection input gradient is zero has zero gate/up gradient, so it is
+ * not rescored).  pb describes the second projection (its d_out, d_in, T and
+ * dtype; the same counts and quotas); perm and keep come from an earlier
+ * lrmoe_score_select_compact.  g_row_index / phi_row_index (int32 [P], or
+ * NULL for row u of pair u) pick the source rows of g and phi; the kept
+ * rows are copied bit for bit into g_c [M, d_out] and phi_c [M, d_in], alpha
+ * into alpha_c [M], and dphi_zero (or NULL) gets zero rows for dropped
+ * pairs. */
+lrmoe_status lrmoe_gather_compact(
+    const lrmoe_problem* pb, const int32_t* perm, const uint8_t* keep,
+    const int32_t* g_row_index, const int32_t* phi_row_index,
+    const float* alpha, const void* g, const void* phi, void* g_c,
+    void* phi_c, float* alpha_c, float* dphi_zero, void* stream);
+
+/* Step 5: variable-length grouped GEMMs over the compacted buffers.
+ *   dW   f32 [E, d_out, d_in]: fully overwritten (zero for q_e = 0)
+ *   dphi f32 [P, d_in] or NULL: rows perm[j] receive alpha_c[j] W_e^T g_c[j];
+ *        other rows are not touched (see dphi_zero above).
+ * W is [E, d_out, d_in] in the storage type; segments are given by the host
+ * quotas of pb. */
+lrmoe_status lrmoe_grouped_backward(
+    const lrmoe_problem* pb, const int32_t* perm, const float* alpha_c,
+    const void* g_c, const void* phi_c, const void* W, float* dW, float* dphi,
+    void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LRMOE_H */

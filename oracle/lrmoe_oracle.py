@@ -232,11 +232,13 @@ def input_grad_rows(counts, keep, row_index, alpha, g, W, dtype, pairs) -> np.nd
     pairs)."""
     offs = np.concatenate([[0], np.cumsum(np.asarray(counts, dtype=np.int64))])
     out = np.zeros((len(pairs), W.shape[2]))
-    for k, u in enumerate(pairs):
-        u = int(u)
-        if not keep[u]:
-            continue
-        e = int(np.searchsorted(offs, u, side="right") - 1)
-        r = u if row_index is None else int(row_index[u])
-        out[k] = float(alpha[u]) * (to_f64(W[e], dtype).T @ to_f64(g[r], dtype))
+    expert = np.searchsorted(offs, np.asarray(pairs, dtype=np.int64), side="right") - 1
+    for e in np.unique(expert):
+        We = to_f64(W[e], dtype)
+        for k in np.nonzero(expert == e)[0]:
+            u = int(pairs[k])
+            if not keep[u]:
+                continue
+            r = u if row_index is None else int(row_index[u])
+            out[k] = float(alpha[u]) * (We.T @ to_f64(g[r], dtype))
     return out

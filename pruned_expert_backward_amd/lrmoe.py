@@ -1,0 +1,250 @@
+"""Thin Python binding of liblrmoe (C ABI in include/lrmoe.h).
+
+Argument marshalling only: torch tensors supply device memory and the
+current HIP stream; every step of the path runs in the library's HIP
+kernels.  There is no fallback -- without the built library on a GPU every
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblrmoe.so")
+
+F32, BF16 = 0, 1
+DW_EXACT, DW_BF16 = 0, 1
+QUOTA_RATIO, QUOTA_BUDGET = 0, 1
+MAX_EXPERTS = 256
+ABI_VERSION = 1
+
+STATUS = {0: "LRMOE_OK", 1: "LRMOE_ERR_NULL", 2: "LRMOE_ERR_INVALID", 3: "LRMOE_ERR_SHAPE",
+          4: "LRMOE_ERR_ALIGN", 5: "LRMOE_ERR_DTYPE", 6: "LRMOE_ERR_WORKSPACE",
+          7: "LRMOE_ERR_HIP"}
+
+EXPORTS = ["lrmoe_abi_version", "lrmoe_status_string", "lrmoe_plan_quota",
+           "lrmoe_workspace_size", "lrmoe_score_select_compact", "lrmoe_select_compact",
+           "lrmoe_gather_compact", "lrmoe_grouped_backward"]
+
+
+class LrmoeError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} -> {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class Problem(C.Structure):
+    _fields_ = [("E", C.c_int32), ("dtype", C.c_int32), ("P", C.c_int64), ("T", C.c_int64),
+                ("d_out", C.c_int32), ("d_in", C.c_int32),
+                ("counts", C.POINTER(C.c_int64)), ("quotas", C.POINTER(C.c_int64)),
+                ("dw_mode", C.c_int32), ("reserved", C.c_int32)]
+
+
+class QuotaPolicy(C.Structure):
+    _fields_ = [("mode", C.c_int32), ("num", C.c_int64), ("den", C.c_int64),
+                ("budget_pairs", C.c_int64)]
+
+
+_lib_handle = None
+_P = C.c_void_p
+
+
+def lib() -> C.CDLL:
+    """Load liblrmoe.so once; raise if it has not been built."""
+    global _lib_handle
+    if _lib_handle is not None:
+        return _lib_handle
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} not found: build it with "
+                           "`python -m pruned_expert_backward_amd.build`")
+    L = C.CDLL(LIB_PATH)
+    L.lrmoe_abi_version.restype = C.c_int32
+    L.lrmoe_status_string.restype = C.c_char_p
+    L.lrmoe_status_string.argtypes = [C.c_int]
+    L.lrmoe_plan_quota.restype = C.c_int
+    L.lrmoe_plan_quota.argtypes = [C.c_int32, C.POINTER(C.c_int64), C.POINTER(QuotaPolicy),
+                                   C.POINTER(C.c_int64)]
+    L.lrmoe_workspace_size.restype = C.c_int
+    L.lrmoe_workspace_size.argtypes = [C.POINTER(Problem), C.POINTER(C.c_size_t)]
+    L.lrmoe_score_select_compact.restype = C.c_int
+    L.lrmoe_score_select_compact.argtypes = [C.POINTER(Problem)] + [_P] * 13 + [C.c_size_t, _P]
+    L.lrmoe_select_compact.restype = C.c_int
+    L.lrmoe_select_compact.argtypes = [C.POINTER(Problem)] + [_P] * 13 + [C.c_size_t, _P]
+    L.lrmoe_gather_compact.restype = C.c_int
+    L.lrmoe_gather_compact.argtypes = [C.POINTER(Problem)] + [_P] * 12
+    L.lrmoe_grouped_backward.restype = C.c_int
+    L.lrmoe_grouped_backward.argtypes = [C.POINTER(Problem)] + [_P] * 8 + [C.c_size_t, _P]
+    if L.lrmoe_abi_version() != ABI_VERSION:
+        raise RuntimeError("liblrmoe ABI version mismatch; rebuild the library")
+    _lib_handle = L
+    return L
+
+
+def check(fn: str, status: int) -> None:
+    if status != 0:
+        raise LrmoeError(fn, status, lib().lrmoe_status_string(status).decode())
+
+
+# ------------------------------------------------------------------ host side
+
+def _i64_array(vals: Sequence[int]):
+    arr = (C.c_int64 * len(vals))(*[int(v) for v in vals])
+    return arr
+
+
+def plan_quota(counts: Sequence[int], policy: tuple) -> list:
+    """Quotas per expert: policy ("ratio", num, den) or ("budget", pairs)."""
+    E = len(counts)
+    cnt = _i64_array(counts)
+    out = (C.c_int64 * max(E, 1))()
+    if policy[0] == "ratio":
+        pol = QuotaPolicy(QUOTA_RATIO, int(policy[1]), int(policy[2]), 0)
+    elif policy[0] == "budget":
+        pol = QuotaPolicy(QUOTA_BUDGET, 0, 1, int(policy[1]))
+    else:
+        raise ValueError(policy)
+    check("lrmoe_plan_quota", lib().lrmoe_plan_quota(E, cnt, C.byref(pol), out))
+    return [int(out[e]) for e in range(E)]
+
+
+class Plan:
+    """Host description of one call: counts, quotas, sizes, storage type."""
+
+    def __init__(self, counts, quotas, d_out: int, d_in: int, dtype: int, T: Optional[int] = None,
+                 dw_mode: int = DW_EXACT):
+        self.counts = [int(c) for c in counts]
+        self.quotas = [int(q) for q in quotas]
+        self.E = len(self.counts)
+        self.P = sum(self.counts)
+        self.M = sum(self.quotas)
+        self.T = self.P if T is None else int(T)
+        self.d_out, self.d_in, self.dtype, self.dw_mode = int(d_out), int(d_in), int(dtype), int(dw_mode)
+        self._cnt = _i64_array(self.counts)
+        self._q = _i64_array(self.quotas)
+        self.struct = Problem(self.E, self.dtype, self.P, self.T, self.d_out, self.d_in,
+                              C.cast(self._cnt, C.POINTER(C.c_int64)),
+                              C.cast(self._q, C.POINTER(C.c_int64)), self.dw_mode, 0)
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == BF16 else torch.float32
+
+    def workspace_bytes(self) -> int:
+        n = C.c_size_t(0)
+        check("lrmoe_workspace_size", lib().lrmoe_workspace_size(C.byref(self.struct), C.byref(n)))
+        return int(n.value)
+
+
+def storage_dtype(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return BF16
+    if t == torch.float32:
+        return F32
+    raise TypeError(f"unsupported storage dtype {t}")
+
+
+# ------------------------------------------------------------------ device side
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("liblrmoe takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("liblrmoe takes contiguous tensors")
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _empty(shape, dtype, device):
+    return torch.empty(shape, dtype=dtype, device=device)
+
+
+def alloc_select_outputs(plan: Plan, device, zero_target: bool = True) -> dict:
+    """Output buffers of score_select_compact (caller-owned memory)."""
+    dt = plan.torch_dtype
+    out = dict(scores=_empty((plan.P,), torch.float32, device),
+               keep=_empty((plan.P,), torch.uint8, device),
+               seg_offsets=_empty((plan.E + 1,), torch.int32, device),
+               perm=_empty((plan.M,), torch.int32, device),
+               g_c=_empty((plan.M, plan.d_out), dt, device),
+               phi_c=_empty((plan.M, plan.d_in), dt, device),
+               alpha_c=_empty((plan.M,), torch.float32, device))
+    if zero_target:
+        out["dphi"] = _empty((plan.P, plan.d_in), torch.float32, device)
+    return out
+
+
+def workspace(plan: Plan, device) -> torch.Tensor:
+    return torch.empty((max(plan.workspace_bytes(), 16),), dtype=torch.uint8, device=device)
+
+
+def score_select_compact(plan: Plan, alpha, g, phi, g_row_index=None, out=None, ws=None,
+                         scores=None) -> dict:
+    """LRM score -> per-expert top-quota select -> compaction.  With
+    `scores` given, the LRM scoring is skipped and those scores are used."""
+    dev = phi.device
+    if out is None:
+        out = alloc_select_outputs(plan, dev)
+    if ws is None:
+        ws = workspace(plan, dev)
+    L = lib()
+    common = (_ptr(g_row_index), _ptr(alpha), _ptr(g), _ptr(phi))
+    tail = (_ptr(out["keep"]), _ptr(out["seg_offsets"]), _ptr(out["perm"]), _ptr(out["g_c"]),
+            _ptr(out["phi_c"]), _ptr(out["alpha_c"]), _ptr(out.get("dphi")), _ptr(ws),
+            ws.numel(), _stream())
+    if scores is None:
+        st = L.lrmoe_score_select_compact(C.byref(plan.struct), *common, _ptr(out["scores"]), *tail)
+        check("lrmoe_score_select_compact", st)
+    else:
+        st = L.lrmoe_select_compact(C.byref(plan.struct), _ptr(scores), *common, *tail)
+        check("lrmoe_select_compact", st)
+    return out
+
+
+def gather_compact(plan: Plan, perm, keep, alpha, g, phi, g_row_index=None, phi_row_index=None,
+                   out=None, zero_target: bool = True) -> dict:
+    dev = phi.device
+    dt = plan.torch_dtype
+    if out is None:
+        out = dict(g_c=_empty((plan.M, plan.d_out), dt, dev),
+                   phi_c=_empty((plan.M, plan.d_in), dt, dev),
+                   alpha_c=_empty((plan.M,), torch.float32, dev))
+        if zero_target:
+            out["dphi"] = _empty((plan.P, plan.d_in), torch.float32, dev)
+    st = lib().lrmoe_gather_compact(C.byref(plan.struct), _ptr(perm), _ptr(keep),
+                                    _ptr(g_row_index), _ptr(phi_row_index), _ptr(alpha), _ptr(g),
+                                    _ptr(phi), _ptr(out["g_c"]), _ptr(out["phi_c"]),
+                                    _ptr(out["alpha_c"]), _ptr(out.get("dphi")), _stream())
+    check("lrmoe_gather_compact", st)
+    return out
+
+
+def grouped_backward(plan: Plan, perm, alpha_c, g_c, phi_c, W, dW=None, dphi=None,
+                     ws=None) -> torch.Tensor:
+    """dW [E, d_out, d_in] (returned) and the kept rows of dphi (in place)."""
+    dev = W.device
+    if dW is None:
+        dW = _empty((plan.E, plan.d_out, plan.d_in), torch.float32, dev)
+    if ws is None:
+        ws = workspace(plan, dev)
+    st = lib().lrmoe_grouped_backward(C.byref(plan.struct), _ptr(perm), _ptr(alpha_c), _ptr(g_c),
+                                      _ptr(phi_c), _ptr(W), _ptr(dW), _ptr(dphi), _ptr(ws),
+                                      ws.numel(), _stream())
+    check("lrmoe_grouped_backward", st)
+    return dW
+
+
+def pruned_backward(plan: Plan, alpha, g, phi, W, g_row_index=None, out=None, ws=None) -> dict:
+    """The whole path: score, select, compact, dW and dphi."""
+    out = score_select_compact(plan, alpha, g, phi, g_row_index=g_row_index, out=out, ws=ws)
+    out["dW"] = grouped_backward(plan, out["perm"], out["alpha_c"], out["g_c"], out["phi_c"], W,
+                                 dW=out.get("dW"), dphi=out.get("dphi"), ws=ws)
+    return out

@@ -1,0 +1,129 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times.  Keep sets, offsets, permutation and compacted buffers are
+compared in full; dW and dphi on sampled outputs the oracle computes one by
+one (a row/column block of every expert's dW; kept and dropped dphi rows),
+with the tolerance taken against the sample's own max |ref| (stricter than
+the whole tensor's)."""
+import concurrent.futures as fut
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import lrmoe_oracle as O
+from pruned_expert_backward_amd import lrmoe
+from pruned_expert_backward_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from tests import gpu_util as U  # noqa: E402
+
+
+def oracle_scores(p, block=8192):
+    """The oracle's scores, computed on row blocks in parallel (same
+    arithmetic per pair as one call over all rows)."""
+    if p.row_index is not None or p.P <= block:
+        return O.lrm_scores(p.alpha, p.g, p.phi, p.row_index, p.dtype)
+    spans = [(lo, min(p.P, lo + block)) for lo in range(0, p.P, block)]
+    with fut.ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        parts = list(ex.map(lambda s: O.lrm_scores(p.alpha[s[0]:s[1]], p.g[s[0]:s[1]],
+                                                   p.phi[s[0]:s[1]], None, p.dtype), spans))
+    return np.concatenate(parts)
+
+
+def check_fullsize(p, dw_mode=lrmoe.DW_EXACT, gate_up=False, seed=0):
+    q = lrmoe.plan_quota(p.counts, p.policy)
+    assert q == O.plan_quota(p.counts, p.policy)
+    plan, out, t = U.run_gpu(p, q, dw_mode=dw_mode)
+    R = oracle_scores(p)
+    keep_ref, taus = O.select_top_quota(R, p.counts, q)
+    keep_gpu = out["keep"].cpu().numpy().astype(bool)
+    same = U.check_keep(R, p.counts, q, keep_gpu, keep_ref, taus)
+    keep_used = keep_ref if same else keep_gpu
+    perm, seg = O.compact(keep_used, p.counts, q)
+    assert np.array_equal(out["seg_offsets"].cpu().numpy(), seg)
+    assert np.array_equal(out["perm"].cpu().numpy(), perm)
+    s = out["scores"].cpu().numpy().astype(np.float64)
+    score_err = float(np.max(np.abs(s - R) / np.maximum(R, 1e-30)))
+    assert score_err <= 1e-5
+    # compacted buffers, bit for bit
+    g_c = U.host_bits(out["g_c"])
+    phi_c = U.host_bits(out["phi_c"])
+    assert np.array_equal(g_c, p.g[perm])
+    assert np.array_equal(phi_c, p.phi[perm])
+    assert np.array_equal(out["alpha_c"].cpu().numpy(), p.alpha[perm])
+    del g_c, phi_c
+    rng = np.random.default_rng(seed)
+    # dW: one block per expert, including the last row and column
+    o_idx = np.unique(np.concatenate([[0, p.d_out - 1], rng.integers(0, p.d_out, 40)]))
+    i_idx = np.unique(np.concatenate([[0, p.d_in - 1], rng.integers(0, p.d_in, 40)]))
+    dW = out["dW"]
+    got, ref = [], []
+    for e in range(p.E):
+        ref.append(O.weight_grad_block(seg, perm, None, p.alpha, p.g, p.phi, p.dtype, e,
+                                       o_idx, i_idx))
+        got.append(dW[e][torch.as_tensor(o_idx, device=dW.device)][
+            :, torch.as_tensor(i_idx, device=dW.device)].cpu().numpy())
+    dw_err = U.rel_err(np.stack(got), np.stack(ref))
+    # dphi: kept and dropped rows, including the first and last pair
+    kept = np.nonzero(keep_used)[0]
+    dropped = np.nonzero(~keep_used)[0]
+    pairs = np.unique(np.concatenate([
+        [0, p.P - 1], rng.choice(kept, min(256, len(kept)), replace=False),
+        rng.choice(dropped, min(64, len(dropped)), replace=False) if len(dropped) else []]
+    ).astype(np.int64))
+    ref_rows = O.input_grad_rows(p.counts, keep_used, None, p.alpha, p.g, p.W, p.dtype, pairs)
+    got_rows = out["dphi"][torch.as_tensor(pairs, device=out["dphi"].device)].cpu().numpy()
+    dphi_err = U.rel_err(got_rows, ref_rows)
+    assert np.all(got_rows[~keep_used[pairs]] == 0)
+    print(f"{p.name}: M={sum(q)} keep identical={same} score rel err={score_err:.2e} "
+          f"dW err={dw_err:.3e} dphi err={dphi_err:.3e}", flush=True)
+    assert dw_err <= U.TOL and dphi_err <= U.TOL
+    res = dict(out=out, t=t, q=q, perm=perm, keep=keep_used, plan=plan)
+    return res
+
+
+@pytest.mark.parametrize("c", [1, 3])
+def test_fullsize_down_projection(c):
+    check_fullsize(W.config(c), seed=c)
+
+
+def test_fullsize_qwen3_c30_with_gate_up():
+    p = W.config(2)
+    r = check_fullsize(p, seed=2)
+    gu = p.gate_up
+    plan2 = lrmoe.Plan(p.counts, r["q"], gu.d_out, gu.d_in, lrmoe.BF16)
+    out = r["out"]
+    c2 = lrmoe.gather_compact(plan2, out["perm"], out["keep"], r["t"]["alpha"], U.dev(gu.g2),
+                              U.dev(gu.x))
+    dW2 = lrmoe.grouped_backward(plan2, out["perm"], c2["alpha_c"], c2["g_c"], c2["phi_c"],
+                                 U.dev(gu.W2), dphi=c2["dphi"])
+    torch.cuda.synchronize()
+    perm = r["perm"]
+    assert np.array_equal(U.host_bits(c2["g_c"]), gu.g2[perm])
+    assert np.array_equal(U.host_bits(c2["phi_c"]), gu.x[perm])
+    seg = np.concatenate([[0], np.cumsum(r["q"])])
+    rng = np.random.default_rng(22)
+    o_idx = np.unique(np.concatenate([[0, gu.d_out - 1], rng.integers(0, gu.d_out, 40)]))
+    i_idx = np.unique(np.concatenate([[0, gu.d_in - 1], rng.integers(0, gu.d_in, 40)]))
+    got = np.stack([dW2[e][torch.as_tensor(o_idx, device=dW2.device)][
+        :, torch.as_tensor(i_idx, device=dW2.device)].cpu().numpy() for e in range(p.E)])
+    ref = np.stack([O.weight_grad_block(seg, perm, None, p.alpha, gu.g2, gu.x, "bf16", e,
+                                        o_idx, i_idx) for e in range(p.E)])
+    e1 = U.rel_err(got, ref)
+    pairs = np.unique(np.concatenate([[0, p.P - 1], rng.choice(perm, 256, replace=False),
+                                      rng.choice(np.nonzero(~r["keep"])[0], 64, replace=False)]))
+    ref_rows = O.input_grad_rows(p.counts, r["keep"], None, p.alpha, gu.g2, gu.W2, "bf16", pairs)
+    got_rows = c2["dphi"][torch.as_tensor(pairs, device=c2["dphi"].device)].cpu().numpy()
+    e2 = U.rel_err(got_rows, ref_rows)
+    print(f"gate/up: dW err={e1:.3e} dx err={e2:.3e}")
+    assert e1 <= U.TOL and e2 <= U.TOL
+
+
+@pytest.mark.timeout(600)
+def test_fullsize_glm45_20x_budget():
+    check_fullsize(W.config(4), seed=4)

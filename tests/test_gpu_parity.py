@@ -1,0 +1,138 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Small and medium problems are compared element by element: several 128x128
+tiles, ragged row and column tails, empty experts, zero and full quotas,
+fp32 and bf16 storage, per-token g (row indirection) and per-pair g, ties.
+Full-size workloads are in test_gpu_fullsize.py."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import lrmoe_oracle as O
+from pruned_expert_backward_amd import lrmoe
+from pruned_expert_backward_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from tests import gpu_util as U  # noqa: E402
+
+
+def test_tiny_config_fp32_per_token():
+    p = W.config(0)
+    q = lrmoe.plan_quota(p.counts, p.policy)
+    plan, out, _ = U.run_gpu(p, q)
+    errs, same = U.compare_full(p, q, out)
+    assert same
+    print("tiny-fp32", errs)
+
+
+MEDIUM = [
+    # name, kwargs of make_problem, policy
+    ("ragged-bf16-c20", dict(P=3000, E=5, d_out=264, d_in=200, dtype="bf16",
+                             counts=[1400, 0, 977, 7, 616]), ("ratio", 80, 100)),
+    ("ragged-bf16-c30", dict(P=2500, E=6, d_out=136, d_in=392, dtype="bf16", zipf=1.6),
+     ("ratio", 70, 100)),
+    ("bf16-c0-full", dict(P=1000, E=3, d_out=256, d_in=128, dtype="bf16", zipf=1.0),
+     ("ratio", 1, 1)),
+    ("bf16-drop-all", dict(P=700, E=4, d_out=128, d_in=128, dtype="bf16", zipf=1.2),
+     ("ratio", 0, 1)),
+    ("bf16-budget", dict(P=4000, E=16, d_out=256, d_in=176, dtype="bf16", zipf=1.4),
+     ("budget", 900)),
+    ("fp32-ragged", dict(P=1500, E=4, d_out=196, d_in=140, dtype="f32", zipf=1.2),
+     ("ratio", 80, 100)),
+    ("bf16-one-expert", dict(P=777, E=1, d_out=128, d_in=264, dtype="bf16", zipf=1.0),
+     ("ratio", 1, 2)),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(MEDIUM)), ids=[m[0] for m in MEDIUM])
+def test_medium(idx):
+    name, kw, policy = MEDIUM[idx]
+    p = W.make_problem(seed=100 + idx, policy=policy, name=name, **kw)
+    q = lrmoe.plan_quota(p.counts, policy)
+    assert q == O.plan_quota(p.counts, policy)
+    plan, out, _ = U.run_gpu(p, q)
+    errs, same = U.compare_full(p, q, out)
+    print(name, errs, "keep identical" if same else "keep differs inside band")
+
+
+def test_dw_single_rounding_mode():
+    """The one-pass bf16(alpha*g) mode: same keep set and dphi; dW within the
+    bf16-rounding error (bounded here at 2e-3 on a medium problem)."""
+    p = W.make_problem(P=3000, E=4, d_out=256, d_in=256, dtype="bf16", zipf=1.2, seed=77)
+    q = lrmoe.plan_quota(p.counts, ("ratio", 80, 100))
+    plan, out, _ = U.run_gpu(p, q, dw_mode=lrmoe.DW_BF16)
+    errs, _ = U.compare_full(p, q, out)
+    print("dw bf16 mode", errs)
+
+
+@pytest.mark.parametrize("distinct", [1, 3, 17])
+def test_ties_given_scores(distinct):
+    """Caller-provided scores with many equal values: the keep set must be
+    exactly the oracle's (ties to the lower pair index), no band."""
+    p = W.make_problem(P=5000, E=7, d_out=64, d_in=64, dtype="bf16", zipf=1.3, seed=distinct)
+    s = W.random_scores(p.P, seed=distinct, distinct=distinct)
+    for policy in (("ratio", 80, 100), ("ratio", 1, 3), ("ratio", 1, 1)):
+        q = lrmoe.plan_quota(p.counts, policy)
+        plan, out, _ = U.run_gpu(p, q, scores=s)
+        keep_ref, _ = O.select_top_quota(s.astype(np.float64), p.counts, q)
+        assert np.array_equal(out["keep"].cpu().numpy().astype(bool), keep_ref)
+        U.compare_full(p, q, out, scores_in=s)
+
+
+def test_negative_and_signed_zero_scores():
+    """The order-preserving key handles negative scores and -0.0 == 0.0."""
+    p = W.make_problem(P=600, E=3, d_out=32, d_in=32, dtype="bf16", counts=[200, 250, 150], seed=5)
+    rng = np.random.default_rng(3)
+    s = rng.choice(np.array([-2.5, -1.0, -0.0, 0.0, 1e-30, 3.0], dtype=np.float32), size=p.P)
+    q = lrmoe.plan_quota(p.counts, ("ratio", 1, 2))
+    plan, out, _ = U.run_gpu(p, q, scores=s)
+    keep_ref, _ = O.select_top_quota(s.astype(np.float64), p.counts, q)
+    assert np.array_equal(out["keep"].cpu().numpy().astype(bool), keep_ref)
+
+
+def test_deterministic_bitwise():
+    p = W.make_problem(P=4000, E=8, d_out=256, d_in=136, dtype="bf16", zipf=1.2, seed=9)
+    q = lrmoe.plan_quota(p.counts, ("ratio", 80, 100))
+    _, a, _ = U.run_gpu(p, q)
+    _, b, _ = U.run_gpu(p, q)
+    for k in ("scores", "keep", "perm", "seg_offsets", "g_c", "phi_c", "alpha_c", "dW", "dphi"):
+        assert torch.equal(a[k].view(torch.uint8) if a[k].dtype == torch.bfloat16 else a[k],
+                           b[k].view(torch.uint8) if b[k].dtype == torch.bfloat16 else b[k]), k
+
+
+def test_gate_up_inherits_keep_set():
+    """Second projection (gate/up) on the first one's keep set and perm."""
+    p = W.make_problem(P=2000, E=4, d_out=128, d_in=96, dtype="bf16", zipf=1.6, seed=12,
+                       gate_up=(144, 256))
+    q = lrmoe.plan_quota(p.counts, ("ratio", 70, 100))
+    plan, out, t = U.run_gpu(p, q)
+    gu = p.gate_up
+    plan2 = lrmoe.Plan(p.counts, q, gu.d_out, gu.d_in, lrmoe.BF16)
+    c2 = lrmoe.gather_compact(plan2, out["perm"], out["keep"], t["alpha"], U.dev(gu.g2),
+                              U.dev(gu.x))
+    dW2 = lrmoe.grouped_backward(plan2, out["perm"], c2["alpha_c"], c2["g_c"], c2["phi_c"],
+                                 U.dev(gu.W2), dphi=c2["dphi"])
+    torch.cuda.synchronize()
+    ref = O.pruned_backward(p.counts, ("ratio", 70, 100), p.alpha, p.g, p.phi, p.W, None, "bf16",
+                            gate_up=(gu.g2, gu.x, gu.W2))
+    assert np.array_equal(out["keep"].cpu().numpy().astype(bool), ref["keep"])
+    assert np.array_equal(U.host_bits(c2["g_c"]), gu.g2[ref["perm"]])
+    assert np.array_equal(U.host_bits(c2["phi_c"]), gu.x[ref["perm"]])
+    e1 = U.rel_err(dW2.cpu().numpy(), ref["dW2"])
+    e2 = U.rel_err(c2["dphi"].cpu().numpy(), ref["dx"])
+    assert e1 <= U.TOL and e2 <= U.TOL, (e1, e2)
+
+
+def test_empty_problem_pieces():
+    """All experts empty but one; quotas zero everywhere (M = 0)."""
+    p = W.make_problem(P=300, E=4, d_out=64, d_in=64, dtype="bf16", counts=[0, 300, 0, 0], seed=2)
+    q = [0, 0, 0, 0]
+    plan, out, _ = U.run_gpu(p, q)
+    assert out["seg_offsets"].cpu().tolist() == [0, 0, 0, 0, 0]
+    assert not out["keep"].cpu().numpy().any()
+    assert float(out["dW"].abs().max()) == 0.0
+    assert float(out["dphi"].abs().max()) == 0.0
