@@ -50,7 +50,7 @@ def gemm_floor_bytes(p, M):
             + p.E * p.d_out * p.d_in * 4 + M * p.d_in * 4)
 
 
-def cpu_baseline(p, budget_s: float = 20.0):
+def cpu_baseline(p, budget_s: float = 12.0):
     """The oracle as it stands on the host cores: whole path on the same
     workload, repeated while under the time budget."""
     from oracle import lrmoe_oracle as O
@@ -66,7 +66,7 @@ def cpu_baseline(p, budget_s: float = 20.0):
         M = int(out["seg"][-1])
         runs += 1
         el = time.perf_counter() - t0
-        if el > budget_s / 2 or runs >= 3:
+        if el >= budget_s or runs >= 200:
             break
     return dict(value=M * runs / el, unit="kept pairs/s", cores=int(threads), kind="oracle",
                 sample=f"{runs} full pass(es) of the same workload ({p.name}, P={p.P}, M={M}), "

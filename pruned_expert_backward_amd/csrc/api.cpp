@@ -72,7 +72,64 @@ lrmoe_status check_problem(const lrmoe_problem* pb, Checked& c) {
   return LRMOE_OK;
 }
 
-size_t workspace_bytes(const lrmoe_problem*, const Checked&) { return 0; }
+size_t round256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// Workspace of lrmoe_grouped_backward: bf16 operand planes prepared by the
+// prologue.  bf16 storage: alpha times the narrower of g_c / phi_c, as hi +
+// lo planes (exact) or hi only.  float32 storage: hi + lo planes of g_c,
+// alpha*phi_c and W.
+struct GemmWorkspace {
+  bool alpha_on_phi = true;
+  size_t a_hi = 0, a_lo = 0, b_hi = 0, b_lo = 0, w_hi = 0, w_lo = 0, total = 0;
+};
+
+GemmWorkspace gemm_workspace(const lrmoe_problem* pb, int64_t M) {
+  GemmWorkspace w;
+  const size_t Mz = (size_t)M;
+  if (pb->dtype == LRMOE_BF16) {
+    w.alpha_on_phi = pb->d_in <= pb->d_out;
+    const size_t plane = round256(Mz * (size_t)(w.alpha_on_phi ? pb->d_in : pb->d_out) * 2);
+    w.b_hi = 0;                 // offsets of the scaled operand's planes
+    w.b_lo = plane;
+    w.total = pb->dw_mode == LRMOE_DW_EXACT ? 2 * plane : plane;
+  } else {
+    w.alpha_on_phi = true;
+    const size_t gpl = round256(Mz * (size_t)pb->d_out * 2);
+    const size_t ppl = round256(Mz * (size_t)pb->d_in * 2);
+    const size_t wpl = round256((size_t)pb->E * (size_t)pb->d_out * (size_t)pb->d_in * 2);
+    w.a_hi = 0;
+    w.a_lo = gpl;
+    w.b_hi = 2 * gpl;
+    w.b_lo = 2 * gpl + ppl;
+    w.w_hi = 2 * gpl + 2 * ppl;
+    w.w_lo = w.w_hi + wpl;
+    w.total = w.w_lo + wpl;
+  }
+  return w;
+}
+
+size_t workspace_bytes(const lrmoe_problem* pb, const Checked& c) {
+  return gemm_workspace(pb, c.M).total;
+}
+
+// Group shape gm x gn (gm * gn = kGroupSlots) over an expert's tile grid with
+// nt column tiles: gn among the divisors of kGroupSlots, least idle slots at
+// the grid edge, ties to `pref`.
+void group_shape(int nt, int pref, int32_t& gm, int32_t& gn) {
+  const int cands[6] = {1, 2, 3, 4, 6, 12};
+  int best = -1, best_waste = 1 << 30, best_dist = 1 << 30;
+  for (int c : cands) {
+    const int waste = ((nt + c - 1) / c) * c - nt;
+    const int dist = c > pref ? c - pref : pref - c;
+    if (waste < best_waste || (waste == best_waste && dist < best_dist)) {
+      best = c;
+      best_waste = waste;
+      best_dist = dist;
+    }
+  }
+  gn = best;
+  gm = kGroupSlots / best;
+}
 
 lrmoe_status hip_status(hipError_t e) { return e == hipSuccess ? LRMOE_OK : LRMOE_ERR_HIP; }
 
@@ -105,8 +162,8 @@ lrmoe_status select_compact(const lrmoe_problem* pb, bool compute_scores, const 
   LRMOE_TRY(need(phi_c, M));
   LRMOE_TRY(need(alpha_c, M));
   LRMOE_TRY(optional(dphi_zero));
-  if (ws_bytes < workspace_bytes(pb, c)) return LRMOE_ERR_WORKSPACE;
-  (void)workspace;
+  (void)workspace;   // selection and compaction need no workspace
+  (void)ws_bytes;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const float* scores = scores_in;
   if (compute_scores) {
@@ -240,35 +297,98 @@ lrmoe_status lrmoe_grouped_backward(const lrmoe_problem* pb, const int32_t* perm
   LRMOE_TRY(need(dW, 1));
   LRMOE_TRY(optional(dphi));
   if (dphi != nullptr) LRMOE_TRY(need(perm, M));
-  if (ws_bytes < workspace_bytes(pb, c)) return LRMOE_ERR_WORKSPACE;
-  (void)workspace;
+  const GemmWorkspace wl = gemm_workspace(pb, M);
+  if (ws_bytes < wl.total) return LRMOE_ERR_WORKSPACE;
+  LRMOE_TRY(need(workspace, (int64_t)wl.total));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
   const int E = pb->E;
+  const int d_out = pb->d_out, d_in = pb->d_in;
   GemmTable t;
   memset(&t, 0, sizeof(t));
   t.E = E;
-  t.tiles_n = (pb->d_in + 127) / 128;
-  t.tiles_m_fixed = (pb->d_out + 127) / 128;
+  t.tiles_n = (d_in + 127) / 128;
+  t.dw_tiles_m = (d_out + 127) / 128;
+  group_shape(t.tiles_n, 3, t.dw_gm, t.dw_gn);
+  group_shape(t.tiles_n, 6, t.dp_gm, t.dp_gn);
   for (int e = 0; e <= E; ++e) t.seg_off[e] = c.tab.seg_off[e];
 
-  // Weight gradient: every expert's tiles (zeros for q_e = 0), heaviest
-  // experts first so that the longest K loops start earliest.
+  // Weight-gradient groups: every expert (zeros for q_e = 0), heaviest first.
   std::vector<int> order(E);
   std::iota(order.begin(), order.end(), 0);
   std::stable_sort(order.begin(), order.end(),
                    [&](int a, int b) { return pb->quotas[a] > pb->quotas[b]; });
-  for (int i = 0; i < E; ++i) t.order[i] = (int16_t)order[i];
-  t.dw_tiles = E * t.tiles_m_fixed * t.tiles_n;
-  int32_t tiles = 0;
-  for (int e = 0; e < E; ++e) {
-    t.tile_off[e] = tiles;
-    tiles += (int32_t)((pb->quotas[e] + 127) / 128) * t.tiles_n;
+  const int ngn_dw = (t.tiles_n + t.dw_gn - 1) / t.dw_gn;
+  const int dw_per_expert = ((t.dw_tiles_m + t.dw_gm - 1) / t.dw_gm) * ngn_dw;
+  for (int r = 0; r < E; ++r) {
+    t.order[r] = (uint8_t)order[r];
+    t.dw_goff[r] = r * dw_per_expert;
   }
-  t.tile_off[E] = tiles;
-  t.dp_tiles = (dphi != nullptr) ? tiles : 0;
-  LRMOE_TRY(hip_status(launch_grouped_backward(pb->dtype, pb->dw_mode, t, perm, alpha_c, g_c,
-                                               phi_c, W, dW, dphi, pb->d_out, pb->d_in,
+  t.dw_goff[E] = E * dw_per_expert;
+  t.dw_groups = E * dw_per_expert;
+  // Input-gradient groups, expert by expert.
+  const int ngn_dp = (t.tiles_n + t.dp_gn - 1) / t.dp_gn;
+  int32_t g = t.dw_groups;
+  for (int e = 0; e < E; ++e) {
+    t.dp_goff[e] = g;
+    if (dphi != nullptr) {
+      const int64_t mt = (pb->quotas[e] + 127) / 128;
+      g += (int32_t)(((mt + t.dp_gm - 1) / t.dp_gm) * ngn_dp);
+    }
+  }
+  t.dp_goff[E] = g;
+  t.total_groups = g;
+
+  // Prologue: bf16 operand planes.
+  char* ws = reinterpret_cast<char*>(workspace);
+  auto plane = [&](size_t off) { return reinterpret_cast<uint16_t*>(ws + off); };
+  GemmOperands ops;
+  memset(&ops, 0, sizeof(ops));
+  const uint16_t* g16 = reinterpret_cast<const uint16_t*>(g_c);
+  const uint16_t* p16 = reinterpret_cast<const uint16_t*>(phi_c);
+  const uint16_t* w16 = reinterpret_cast<const uint16_t*>(W);
+  if (pb->dtype == LRMOE_BF16) {
+    const bool exact = pb->dw_mode == LRMOE_DW_EXACT;
+    uint16_t* hi = plane(wl.b_hi);
+    uint16_t* lo = exact ? plane(wl.b_lo) : nullptr;
+    const void* src = wl.alpha_on_phi ? phi_c : g_c;
+    const int cols = wl.alpha_on_phi ? d_in : d_out;
+    LRMOE_TRY(hip_status(launch_split(LRMOE_BF16, src, M, cols, alpha_c, hi, lo, s)));
+    const int np = exact ? 2 : 1;
+    if (wl.alpha_on_phi) {
+      ops.dw_a[0] = g16;
+      ops.dw_b[0] = hi;
+      ops.dw_b[1] = lo;
+      ops.dw_pa = 1;
+      ops.dw_pb = np;
+    } else {
+      ops.dw_a[0] = hi;
+      ops.dw_a[1] = lo;
+      ops.dw_b[0] = p16;
+      ops.dw_pa = np;
+      ops.dw_pb = 1;
+    }
+    ops.dp_a[0] = g16;
+    ops.dp_b[0] = w16;
+    ops.dp_pa = ops.dp_pb = 1;
+  } else {
+    LRMOE_TRY(hip_status(launch_split(LRMOE_F32, g_c, M, d_out, nullptr, plane(wl.a_hi),
+                                      plane(wl.a_lo), s)));
+    LRMOE_TRY(hip_status(launch_split(LRMOE_F32, phi_c, M, d_in, alpha_c, plane(wl.b_hi),
+                                      plane(wl.b_lo), s)));
+    if (dphi != nullptr)
+      LRMOE_TRY(hip_status(launch_split(LRMOE_F32, W, (int64_t)E * d_out, d_in, nullptr,
+                                        plane(wl.w_hi), plane(wl.w_lo), s)));
+    ops.dw_a[0] = ops.dp_a[0] = plane(wl.a_hi);
+    ops.dw_a[1] = ops.dp_a[1] = plane(wl.a_lo);
+    ops.dw_b[0] = plane(wl.b_hi);
+    ops.dw_b[1] = plane(wl.b_lo);
+    ops.dp_b[0] = plane(wl.w_hi);
+    ops.dp_b[1] = plane(wl.w_lo);
+    ops.dw_pa = ops.dw_pb = ops.dp_pa = ops.dp_pb = 2;
+  }
+  (void)w16;
+  LRMOE_TRY(hip_status(launch_grouped_backward(t, ops, perm, alpha_c, dW, dphi, d_out, d_in,
                                                (int32_t)pb->P, s)));
   return LRMOE_OK;
 }

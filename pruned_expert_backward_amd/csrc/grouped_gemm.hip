@@ -14,232 +14,235 @@
 //                    row -- Portuguese write-up, compaction bullet): M = q_e
 //                    (varlen), N = d_in, K = d_out.
 //
-// gfx950 mapping: 256-thread workgroups (4 wave64s in a 2x2 grid) own a
-// 128x128 fp32 output tile; each wave accumulates 64x64 with
-// v_mfma_f32_32x32x16_bf16.  Operand tiles are staged through LDS as bf16 in
-// a K-contiguous layout when global memory is K-contiguous (g_c rows for the
-// input gradient; 16-byte fragment reads), and in the global MN-contiguous
-// layout otherwise (g_c, phi_c and W rows), read back K-wise.  Global loads
-// of the next K step are issued before the MFMAs of the current one.
-//
-// Exact alpha folding: alpha multiplies the reduction index of dW, so it
-// cannot be applied after the product.  alpha*g is formed in fp32 and split
-// into bf16 hi + lo (two MFMA terms); float32 storage splits both operands
-// (three terms: hi*hi + hi*lo + lo*hi).  The single-rounding mode keeps only
-// the hi term.
+// gfx950 mapping
+//   * 256-thread workgroups (4 wave64s, 2x2) own a 128x128 fp32 tile; each
+//     wave accumulates 64x64 with v_mfma_f32_32x32x16_bf16 (fp32 accumulate).
+//   * Every operand is a bf16 plane in global memory.  alpha multiplies the
+//     reduction index of dW, so it cannot be applied after the product: a
+//     prologue writes alpha * (the narrower of g_c, phi_c) as bf16 hi + lo
+//     planes (exact mode; hi only in single-rounding mode), and float32
+//     storage is pre-split into hi + lo planes.  Products of split operands
+//     sum hi*hi + hi*lo + lo*hi.  The MFMA loop does no conversions.
+//   * Operand tiles of one K step (32) live in LDS in the global layout:
+//     "KC" tiles (rows along M/N, K contiguous: g_c rows of the input
+//     gradient) are read with 16-byte ds_read_b128 fragments; "MC" tiles
+//     (rows along K, M/N contiguous: both operands of the weight gradient, W
+//     of the input gradient) are read with ds_read_b64_tr_b16, which
+//     transposes 4x16 bf16 blocks across each 16-lane group, so no operand is
+//     ever transposed in memory.  16-byte chunks are XOR-swizzled per row so
+//     that fragment reads spread over the LDS banks.
+//   * Two LDS stages, one barrier per K step; global loads run two K steps
+//     ahead of the MFMAs through two register stages.
+//   * Scheduling: dW and dphi tiles share one launch.  Tiles are grouped in
+//     blocks of an expert's tile grid that share operand panels; group g runs
+//     on XCD g % 8 (workgroups are dispatched round-robin over the 8 XCDs), so
+//     a group's panels are fetched into one L2.  dW groups come first, heaviest
+//     experts first; the uniform dphi groups fill the tail.
 #include "lrmoe_internal.h"
 
 namespace lrmoe {
 namespace {
 
+#define LDS_AS __attribute__((address_space(3)))
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 128, BN = 128, BK = 32;
-constexpr int KC_LD = BK + 8;      // bf16 per row of a K-contiguous tile (80 B)
-constexpr int MC_LD = 128 + 4;     // bf16 per K row of an MN-contiguous tile (264 B)
 constexpr int kThreads = 256;
+constexpr int kPlaneBytes = 128 * BK * 2;   // one bf16 operand plane of one K step
+
+// ------------------------------------------------------------ LDS layouts
+// KC: row r (0..127) holds K 0..31 as 4 chunks of 16 B.
+__device__ __forceinline__ int kc_off(int r, int c) {
+  return r * 64 + ((c ^ (((r >> 1) ^ (r >> 3)) & 3)) << 4);
+}
+// MC: row k (0..31) holds M/N 0..127 as 16 chunks of 16 B.
+__device__ __forceinline__ int mc_off(int k, int c) { return k * 256 + ((c ^ ((k & 3) << 2)) << 4); }
+
+// Fragment: 8 bf16 along K for MN index (mb + lane%32), K = kb + 8*(lane/32) + 0..7.
+__device__ __forceinline__ i16x8 frag_kc(LDS_AS const char* t, int mb, int kb, int lane) {
+  const int r = mb + (lane & 31);
+  const int c = (kb >> 3) + (lane >> 5);
+  return *reinterpret_cast<LDS_AS const i16x8*>(t + kc_off(r, c));
+}
+
+// ds_read_b64_tr_b16: within each 16-lane group, source lane s reads 4 bf16
+// of row k0 + s/4 at columns n + 4*(s%4); lane l then holds column n + l%16
+// for rows k0 .. k0+3.
+__device__ __forceinline__ i16x8 frag_mc(LDS_AS const char* t, int mb, int kb, int lane) {
+  const int G = lane >> 4, s = lane & 15;
+  const int c = (mb >> 3) + 2 * (G & 1) + ((s & 3) >> 1);
+  const int half = (s & 1) * 8;
+  const int k0 = kb + 8 * (G >> 1) + (s >> 2);
+  LDS_AS char* base = const_cast<LDS_AS char*>(t);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<LDS_AS i16x4*>(base + mc_off(k0, c) + half));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<LDS_AS i16x4*>(base + mc_off(k0 + 4, c) + half));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
 template <bool MC>
-struct TileSize;
-template <> struct TileSize<true> { static constexpr int elems = BK * MC_LD; };
-template <> struct TileSize<false> { static constexpr int elems = BM * KC_LD; };
+__device__ __forceinline__ i16x8 frag(LDS_AS const char* t, int mb, int kb, int lane) {
+  if constexpr (MC) return frag_mc(t, mb, kb, lane);
+  else return frag_kc(t, mb, kb, lane);
+}
 
-// Eight consecutive global elements of one operand row, widened to fp32.
-template <typename TIn>
-struct Raw8 {
-  float v[8];
+__device__ __forceinline__ f32x16 mfma(i16x8 a, i16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+struct TileJob {
+  int e, m0, n0;
 };
 
-template <typename TIn>
-__device__ __forceinline__ void load8(const TIn* __restrict__ p, int valid_elems, Raw8<TIn>& r);
-
-template <>
-__device__ __forceinline__ void load8<uint16_t>(const uint16_t* __restrict__ p, int valid_elems,
-                                                Raw8<uint16_t>& r) {
-  uint4 w = make_uint4(0, 0, 0, 0);
-  if (valid_elems >= 8) w = *reinterpret_cast<const uint4*>(p);
-  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r.v[2 * i] = __uint_as_float(ws[i] << 16);
-    r.v[2 * i + 1] = __uint_as_float(ws[i] & 0xFFFF0000u);
+// Decode the workgroup's tile from the group schedule; false = idle slot.
+__device__ __forceinline__ bool decode(const GemmTable& tab, bool& is_dw, TileJob& job) {
+  const int b = blockIdx.x;
+  const int x = b % kXcds, i = b / kXcds;
+  const int g = (i / kGroupSlots) * kXcds + x;   // group of this XCD's queue
+  const int t = i % kGroupSlots;                 // slot inside the group
+  if (g >= tab.total_groups) return false;
+  is_dw = g < tab.dw_groups;
+  const int32_t* goff = is_dw ? tab.dw_goff : tab.dp_goff;
+  int lo = 0, hi = tab.E - 1;   // last rank r with goff[r] <= g
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (goff[mid] <= g) lo = mid; else hi = mid - 1;
   }
+  const int e = is_dw ? (int)tab.order[lo] : lo;
+  const int lg = g - goff[lo];
+  const int gm = is_dw ? tab.dw_gm : tab.dp_gm;
+  const int gn = is_dw ? tab.dw_gn : tab.dp_gn;
+  if (t >= gm * gn) return false;
+  const int ngn = (tab.tiles_n + gn - 1) / gn;
+  const int tm = (lg / ngn) * gm + t / gn;
+  const int tn = (lg % ngn) * gn + t % gn;
+  const int q = tab.seg_off[e + 1] - tab.seg_off[e];
+  const int tiles_m = is_dw ? tab.dw_tiles_m : (q + BM - 1) / BM;
+  if (tm >= tiles_m || tn >= tab.tiles_n) return false;
+  job.e = e;
+  job.m0 = tm * BM;
+  job.n0 = tn * BN;
+  return true;
 }
 
-template <>
-__device__ __forceinline__ void load8<float>(const float* __restrict__ p, int valid_elems,
-                                             Raw8<float>& r) {
-  float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-  if (valid_elems >= 4) a = *reinterpret_cast<const float4*>(p);
-  if (valid_elems >= 8) b = *reinterpret_cast<const float4*>(p + 4);
-  r.v[0] = a.x; r.v[1] = a.y; r.v[2] = a.z; r.v[3] = a.w;
-  r.v[4] = b.x; r.v[5] = b.y; r.v[6] = b.z; r.v[7] = b.w;
-}
+template <int PA, int PB>
+struct Stage {
+  u32x4 a[PA][2], b[PB][2];
+};
 
-// Write 8 values as bf16 hi (and lo residual) planes into LDS.
-template <int SPLIT>
-__device__ __forceinline__ void store8(const float (&x)[8], __bf16* hi, __bf16* lo, bool aligned16) {
-  __bf16 h[8], l[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    h[i] = (__bf16)x[i];
-    if (SPLIT == 2) l[i] = (__bf16)(x[i] - (float)h[i]);
-  }
-  if (aligned16) {
-    *reinterpret_cast<bf16x8*>(hi) = *reinterpret_cast<const bf16x8*>(h);
-    if (SPLIT == 2) *reinterpret_cast<bf16x8*>(lo) = *reinterpret_cast<const bf16x8*>(l);
-  } else {
-    uint2* dh = reinterpret_cast<uint2*>(hi);
-    dh[0] = reinterpret_cast<const uint2*>(h)[0];
-    dh[1] = reinterpret_cast<const uint2*>(h)[1];
-    if (SPLIT == 2) {
-      uint2* dl = reinterpret_cast<uint2*>(lo);
-      dl[0] = reinterpret_cast<const uint2*>(l)[0];
-      dl[1] = reinterpret_cast<const uint2*>(l)[1];
-    }
-  }
-}
-
-// MFMA operand fragment (8 bf16 along K) for MN index mn, K offset k.
-template <bool MC>
-__device__ __forceinline__ bf16x8 frag(const __bf16* tile, int mn, int k);
-
-template <>
-__device__ __forceinline__ bf16x8 frag<false>(const __bf16* tile, int mn, int k) {
-  return *reinterpret_cast<const bf16x8*>(tile + mn * KC_LD + k);
-}
-
-template <>
-__device__ __forceinline__ bf16x8 frag<true>(const __bf16* tile, int mn, int k) {
-  bf16x8 f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) f[i] = tile[(k + i) * MC_LD + mn];
-  return f;
-}
-
-struct GemmArgs {
-  const void* a;         // dW: g_c (MC)   dphi: g_c (KC)
-  const void* b;         // dW: phi_c (MC) dphi: W (MC)
+struct Args {
+  GemmOperands ops;
   const float* alpha_c;
   const int32_t* perm;
-  float* out;            // dW or dphi
-  int32_t d_out, d_in;
-  int32_t P;             // rows of dphi
+  float* dW;
+  float* dphi;
+  int32_t d_out, d_in, P;
 };
 
-// One operand tile of one K step, held in registers between the global load
-// and the LDS store.
-template <typename TIn>
-struct Stage {
-  Raw8<TIn> r[2];
-  float s[2];
-};
+// Buffer resource over [base, base + bytes): loads at or beyond `bytes`
+// return zero, which masks ragged row and column edges without branches.
+constexpr uint32_t kBufferFlags = 0x00020000u;   // gfx9 family: raw 32-bit data
+constexpr uint32_t kOutOfRange = 0x80000000u;     // voffset that is never in range
 
-template <bool IS_DW, int SPLIT_A, int SPLIT_B>
-struct TileLds {
-  static constexpr int a_elems = TileSize<IS_DW>::elems;
-  static constexpr int b_elems = TileSize<true>::elems;
-  static constexpr int bytes = 2 * (SPLIT_A * a_elems + SPLIT_B * b_elems);
-};
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint16_t* base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (int)(bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, n,
+                                           (int)kBufferFlags);
+}
 
-// One 128x128 output tile.  IS_DW: weight gradient (A = alpha * g_c,
-// MN-contiguous) else input gradient (A = g_c, K-contiguous).  B is
-// MN-contiguous in both.  `bid` indexes this product's tiles.
-template <typename TIn, bool IS_DW, int SPLIT_A, int SPLIT_B>
-__device__ __forceinline__ void gemm_tile(const GemmArgs& args, const GemmTable& tab, int bid,
-                                          __bf16* lds) {
+__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+}
+
+// One 128x128 output tile.  IS_DW: A (MC, rows = K) and B (MC, rows = K) are
+// [M, d_out] / [M, d_in] segment rows.  Else A (KC, rows = M) = g_c segment
+// rows and B (MC) = W_e.  PA/PB: bf16 planes of each operand.
+template <bool IS_DW, int PA, int PB>
+__device__ __forceinline__ void gemm_tile(const Args& args, const GemmTable& tab,
+                                          const TileJob& job, LDS_AS char* smem) {
   constexpr bool A_MC = IS_DW;
-  using L = TileLds<IS_DW, SPLIT_A, SPLIT_B>;
-  __bf16* lds_a[2] = {lds, lds + (SPLIT_A - 1) * L::a_elems};
-  __bf16* lds_b[2] = {lds + SPLIT_A * L::a_elems, lds + SPLIT_A * L::a_elems + (SPLIT_B - 1) * L::b_elems};
-
+  constexpr int kStage = (PA + PB) * kPlaneBytes;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int d_out = args.d_out, d_in = args.d_in;
-
-  // ---- which expert / tile this workgroup owns
-  int e, m0, n0, seg, q;
-  if (IS_DW) {
-    const int tpe = tab.tiles_m_fixed * tab.tiles_n;
-    e = tab.order[bid / tpe];
-    const int t = bid % tpe;
-    m0 = (t / tab.tiles_n) * BM;
-    n0 = (t % tab.tiles_n) * BN;
-  } else {
-    int lo = 0, hi = tab.E - 1;   // largest e with tile_off[e] <= bid
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (tab.tile_off[mid] <= bid) lo = mid; else hi = mid - 1;
-    }
-    e = lo;
-    const int t = bid - tab.tile_off[e];
-    m0 = (t / tab.tiles_n) * BM;
-    n0 = (t % tab.tiles_n) * BN;
-  }
-  seg = tab.seg_off[e];
-  q = tab.seg_off[e + 1] - seg;
+  const int e = job.e, m0 = job.m0, n0 = job.n0;
+  const int seg = tab.seg_off[e];
+  const int q = tab.seg_off[e + 1] - seg;
   const int K = IS_DW ? q : d_out;
 
-  const TIn* A = reinterpret_cast<const TIn*>(args.a);
-  const TIn* B = reinterpret_cast<const TIn*>(args.b);
-  if (!IS_DW) B += (int64_t)e * d_out * d_in;
+  const uint16_t* A[2];
+  const uint16_t* B[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    A[p] = IS_DW ? args.ops.dw_a[p] : args.ops.dp_a[p];
+    B[p] = IS_DW ? args.ops.dw_b[p] : args.ops.dp_b[p];
+  }
+  // Per-thread byte offsets inside one K step (fixed over the loop).
+  uint32_t aoff[2], boff[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int idx = tid + h * kThreads;
+    if (A_MC) {   // row k of the step, 8-element chunk along M (o)
+      const int k = idx >> 4, col = m0 + 8 * (idx & 15);
+      aoff[h] = col < d_out ? (uint32_t)(k * d_out + col) * 2u : kOutOfRange;
+    } else {      // row r of the tile, chunk along K (o); K offset added per step
+      const int r = idx >> 2;
+      aoff[h] = (uint32_t)(r * d_out + 8 * (idx & 3)) * 2u;
+    }
+    const int k = idx >> 4, col = n0 + 8 * (idx & 15);
+    boff[h] = col < d_in ? (uint32_t)(k * d_in + col) * 2u : kOutOfRange;
+  }
 
-  // ---- global -> register staging
-  auto load_a = [&](int k0, Stage<TIn>& st) {
+  // ---- global -> registers for the K step starting at k0
+  auto gload = [&](int k0, Stage<PA, PB>& st) {
+    const int krows = K - k0 < BK ? K - k0 : BK;
+    __amdgpu_buffer_rsrc_t ra[PA], rb[PB];
+#pragma unroll
+    for (int p = 0; p < PA; ++p) {
+      if (A_MC) ra[p] = rsrc(A[p] + ((int64_t)seg + k0) * d_out, (int64_t)krows * d_out * 2);
+      else ra[p] = rsrc(A[p] + ((int64_t)seg + m0) * d_out, (int64_t)(q - m0) * d_out * 2);
+    }
+#pragma unroll
+    for (int p = 0; p < PB; ++p) {
+      const uint16_t* b0 = IS_DW ? B[p] + ((int64_t)seg + k0) * d_in
+                                 : B[p] + ((int64_t)e * d_out + k0) * d_in;
+      rb[p] = rsrc(b0, (int64_t)krows * d_in * 2);
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int c = tid + h * kThreads;
-      if (A_MC) {   // rows are K (segment rows), columns are M (= o)
-        const int k = c >> 4, mn = (c & 15) * 8;
-        const bool kv = (k0 + k) < K;
-        const int valid = kv ? (d_out - (m0 + mn)) : 0;
-        const int64_t row = (int64_t)seg + k0 + k;
-        load8<TIn>(A + row * d_out + m0 + mn, valid, st.r[h]);
-        st.s[h] = kv ? args.alpha_c[row] : 0.f;
-      } else {      // rows are M (segment rows), columns are K (= o)
-        const int r = c >> 2, kc = (c & 3) * 8;
-        const bool rv = (m0 + r) < q;
-        const int valid = rv ? (K - (k0 + kc)) : 0;
-        load8<TIn>(A + ((int64_t)seg + m0 + r) * d_out + k0 + kc, valid, st.r[h]);
-        st.s[h] = 1.f;
+      uint32_t ao = aoff[h];
+      if (!A_MC) {   // K columns of this step; past d_out reads zero
+        const int kcol = k0 + 8 * ((tid + h * kThreads) & 3);
+        ao = kcol < K ? ao + (uint32_t)k0 * 2u : kOutOfRange;
       }
+#pragma unroll
+      for (int p = 0; p < PA; ++p) st.a[p][h] = bload(ra[p], ao);
+#pragma unroll
+      for (int p = 0; p < PB; ++p) st.b[p][h] = bload(rb[p], boff[h]);
     }
   };
-  auto load_b = [&](int k0, Stage<TIn>& st) {
+  // ---- registers -> one LDS stage: A planes then B planes
+  auto lstore = [&](const Stage<PA, PB>& st, LDS_AS char* stage) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int c = tid + h * kThreads;
-      const int k = c >> 4, mn = (c & 15) * 8;
-      const bool kv = (k0 + k) < K;
-      const int valid = kv ? (d_in - (n0 + mn)) : 0;
-      const int64_t row = IS_DW ? ((int64_t)seg + k0 + k) : (int64_t)(k0 + k);
-      load8<TIn>(B + row * d_in + n0 + mn, valid, st.r[h]);
-      st.s[h] = 1.f;
-    }
-  };
-  auto store_a = [&](const Stage<TIn>& st) {
+      const int idx = tid + h * kThreads;
+      const int ao = A_MC ? mc_off(idx >> 4, idx & 15) : kc_off(idx >> 2, idx & 3);
+      const int bo = mc_off(idx >> 4, idx & 15);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = tid + h * kThreads;
-      float x[8];
+      for (int p = 0; p < PA; ++p)
+        *reinterpret_cast<LDS_AS u32x4*>(stage + p * kPlaneBytes + ao) = st.a[p][h];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = IS_DW ? st.s[h] * st.r[h].v[i] : st.r[h].v[i];
-      if (A_MC) {
-        const int k = c >> 4, mn = (c & 15) * 8;
-        store8<SPLIT_A>(x, lds_a[0] + k * MC_LD + mn, lds_a[1] + k * MC_LD + mn, false);
-      } else {
-        const int r = c >> 2, kc = (c & 3) * 8;
-        store8<SPLIT_A>(x, lds_a[0] + r * KC_LD + kc, lds_a[1] + r * KC_LD + kc, true);
-      }
-    }
-  };
-  auto store_b = [&](const Stage<TIn>& st) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = tid + h * kThreads;
-      const int k = c >> 4, mn = (c & 15) * 8;
-      store8<SPLIT_B>(st.r[h].v, lds_b[0] + k * MC_LD + mn, lds_b[1] + k * MC_LD + mn, false);
+      for (int p = 0; p < PB; ++p)
+        *reinterpret_cast<LDS_AS u32x4*>(stage + (PA + p) * kPlaneBytes + bo) = st.b[p][h];
     }
   };
 
@@ -251,47 +254,72 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const GemmTable&
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  const int nk = (K + BK - 1) / BK;
-  Stage<TIn> sa, sb;
-  if (nk > 0) {
-    load_a(0, sa);
-    load_b(0, sb);
-  }
-  const int fl = lane & 31, fk = 8 * (lane >> 5);
-  for (int kt = 0; kt < nk; ++kt) {
-    __syncthreads();
-    store_a(sa);
-    store_b(sb);
-    __syncthreads();
-    if (kt + 1 < nk) {
-      load_a((kt + 1) * BK, sa);
-      load_b((kt + 1) * BK, sb);
-    }
+  // ---- MFMAs of one K step: hi*hi (+ hi*lo_B) (+ lo_A*hi)
+  auto compute = [&](LDS_AS const char* stage) {
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8 fa[SPLIT_A][2], fb[SPLIT_B][2];
+      i16x8 fb[PB][2], fa[PA][2];
 #pragma unroll
-      for (int s = 0; s < SPLIT_A; ++s)
+      for (int p = 0; p < PB; ++p)
 #pragma unroll
-        for (int a = 0; a < 2; ++a) fa[s][a] = frag<A_MC>(lds_a[s], wm * 64 + a * 32 + fl, kk + fk);
+        for (int b = 0; b < 2; ++b)
+          fb[p][b] = frag_mc(stage + (PA + p) * kPlaneBytes, wn * 64 + b * 32, kk, lane);
 #pragma unroll
-      for (int s = 0; s < SPLIT_B; ++s)
+      for (int p = 0; p < PA; ++p)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) fb[s][b] = frag<true>(lds_b[s], wn * 64 + b * 32 + fl, kk + fk);
+        for (int a = 0; a < 2; ++a)
+          fa[p][a] = frag<A_MC>(stage + p * kPlaneBytes, wm * 64 + a * 32, kk, lane);
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][a], fb[0][b], acc[a][b], 0, 0, 0);
-          if (SPLIT_B == 2)
-            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0][a], fb[SPLIT_B - 1][b], acc[a][b], 0, 0, 0);
-          if (SPLIT_A == 2)
-            acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[SPLIT_A - 1][a], fb[0][b], acc[a][b], 0, 0, 0);
+          acc[a][b] = mfma(fa[0][a], fb[0][b], acc[a][b]);
+          if (PB == 2) acc[a][b] = mfma(fa[0][a], fb[PB - 1][b], acc[a][b]);
+          if (PA == 2) acc[a][b] = mfma(fa[PA - 1][a], fb[0][b], acc[a][b]);
         }
     }
+  };
+
+  // ---- pipeline: loads two steps ahead, two LDS stages, one barrier per
+  // step; unrolled by two so that each register stage has a fixed name.
+  const int nk = (K + BK - 1) / BK;
+  Stage<PA, PB> r0, r1;
+  LDS_AS char* st0 = smem;
+  LDS_AS char* st1 = smem + kStage;
+  if (nk > 0) {
+    gload(0, r0);
+    gload(BK, r1);
+    lstore(r0, st0);
+    __syncthreads();
+  }
+  // Loads past the end of K see an empty buffer and return zeros without
+  // touching memory, so they are issued unconditionally: branch-free code
+  // lets each wait cover exactly the older register stage.
+  for (int kt = 0; kt < nk; kt += 2) {
+    gload((kt + 2) * BK, r0);
+    compute(st0);
+    lstore(r1, st1);
+    __syncthreads();
+    if (kt + 1 >= nk) break;
+    gload((kt + 3) * BK, r1);
+    compute(st1);
+    lstore(r0, st0);
+    __syncthreads();
   }
 
   // ---- epilogue: D[i][j] sits in lane j + 32*((i/4)%2), register (i%4) + 4*(i/8)
+  const int fl = lane & 31;
+  LDS_AS int32_t* s_perm = reinterpret_cast<LDS_AS int32_t*>(smem);
+  LDS_AS float* s_alpha = reinterpret_cast<LDS_AS float*>(smem + BM * 4);
+  if (!IS_DW) {   // destination row and alpha of the tile's 128 rows, via LDS
+    if (tid < BM) {
+      const bool ok = m0 + tid < q;
+      const int32_t u = ok ? args.perm[seg + m0 + tid] : -1;
+      s_perm[tid] = (uint32_t)u < (uint32_t)args.P ? u : -1;   // perm holds pair indices < P
+      s_alpha[tid] = ok ? args.alpha_c[seg + m0 + tid] : 0.f;
+    }
+    __syncthreads();
+  }
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
 #pragma unroll
@@ -300,19 +328,19 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const GemmTable&
       const int mrow = m0 + wm * 64 + a * 32 + i;
       if (IS_DW) {
         if (mrow < d_out) {
-          float* orow = args.out + ((int64_t)e * d_out + mrow) * d_in;
+          float* orow = args.dW + ((int64_t)e * d_out + mrow) * d_in;
 #pragma unroll
           for (int b = 0; b < 2; ++b) {
             const int col = n0 + wn * 64 + b * 32 + fl;
             if (col < d_in) orow[col] = acc[a][b][r];
           }
         }
-      } else if (mrow < q) {
-        const int64_t jj = (int64_t)seg + mrow;
-        const int32_t u = args.perm[jj];
-        const float al = args.alpha_c[jj];
-        if ((uint32_t)u < (uint32_t)args.P) {   // perm holds pair indices < P
-          float* orow = args.out + (int64_t)u * d_in;
+      } else {
+        const int lr = mrow - m0;
+        const int32_t u = s_perm[lr];
+        const float al = s_alpha[lr];
+        if (u >= 0) {
+          float* orow = args.dphi + (int64_t)u * d_in;
 #pragma unroll
           for (int b = 0; b < 2; ++b) {
             const int col = n0 + wn * 64 + b * 32 + fl;
@@ -324,42 +352,100 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, const GemmTable&
   }
 }
 
-// One launch for both products: blocks [0, dw_tiles) are weight-gradient
-// tiles (heaviest experts first), the rest are input-gradient tiles, which
-// have uniform work and fill the tail left by skewed expert sizes.
-template <typename TIn, int DW_SA, int DW_SB, int DP_SA, int DP_SB>
-__global__ __launch_bounds__(kThreads, 2) void grouped_backward_kernel(GemmArgs dw, GemmArgs dp,
-                                                                       GemmTable tab) {
-  constexpr int kDw = TileLds<true, DW_SA, DW_SB>::bytes;
-  constexpr int kDp = TileLds<false, DP_SA, DP_SB>::bytes;
-  __shared__ __attribute__((aligned(16))) __bf16 lds[(kDw > kDp ? kDw : kDp) / 2];
-  const int bid = blockIdx.x;
-  if (bid < tab.dw_tiles)
-    gemm_tile<TIn, true, DW_SA, DW_SB>(dw, tab, bid, lds);
+template <int DW_PA, int DW_PB, int DP_PA, int DP_PB>
+struct Cfg {
+  static constexpr int dw_bytes = 2 * (DW_PA + DW_PB) * kPlaneBytes;
+  static constexpr int dp_bytes = 2 * (DP_PA + DP_PB) * kPlaneBytes;
+  static constexpr int bytes = dw_bytes > dp_bytes ? dw_bytes : dp_bytes;
+};
+
+template <int DW_PA, int DW_PB, int DP_PA, int DP_PB>
+__global__ __launch_bounds__(kThreads, 2) void grouped_backward_kernel(Args args, GemmTable tab) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[Cfg<DW_PA, DW_PB, DP_PA, DP_PB>::bytes];
+  LDS_AS char* smem = (LDS_AS char*)(smem_raw);
+  bool is_dw;
+  TileJob job;
+  if (!decode(tab, is_dw, job)) return;
+  if (is_dw)
+    gemm_tile<true, DW_PA, DW_PB>(args, tab, job, smem);
   else
-    gemm_tile<TIn, false, DP_SA, DP_SB>(dp, tab, bid - tab.dw_tiles, lds);
+    gemm_tile<false, DP_PA, DP_PB>(args, tab, job, smem);
 }
 
-template <typename TIn, int DW_SA, int DW_SB, int DP_SA, int DP_SB>
-hipError_t launch(const GemmArgs& dw, const GemmArgs& dp, const GemmTable& tab, hipStream_t s) {
-  const int blocks = tab.dw_tiles + tab.dp_tiles;
+template <int DW_PA, int DW_PB, int DP_PA, int DP_PB>
+hipError_t launch(const Args& args, const GemmTable& tab, hipStream_t s) {
+  const int64_t queue = (tab.total_groups + kXcds - 1) / kXcds;
+  const int64_t blocks = queue * kXcds * kGroupSlots;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_backward_kernel<TIn, DW_SA, DW_SB, DP_SA, DP_SB>), dim3(blocks),
-                     dim3(kThreads), 0, s, dw, dp, tab);
+  hipLaunchKernelGGL((grouped_backward_kernel<DW_PA, DW_PB, DP_PA, DP_PB>), dim3((unsigned)blocks),
+                     dim3(kThreads), 0, s, args, tab);
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------ operand prologue
+// hi/lo bf16 planes of alpha[row] * src[row][4c .. 4c+3].
+template <bool F32>
+__global__ __launch_bounds__(256) void split_kernel(const void* __restrict__ src, int64_t rows,
+                                                    int32_t cols, const float* __restrict__ alpha,
+                                                    uint16_t* __restrict__ hi,
+                                                    uint16_t* __restrict__ lo) {
+  const int64_t quads = rows * (cols / 4);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t qd = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; qd < quads; qd += stride) {
+    const int64_t row = qd / (cols / 4);
+    float x[4];
+    if (F32) {
+      const f32x4 v = reinterpret_cast<const f32x4*>(src)[qd];
+      x[0] = v[0]; x[1] = v[1]; x[2] = v[2]; x[3] = v[3];
+    } else {
+      const u32x2 v = reinterpret_cast<const u32x2*>(src)[qd];
+      x[0] = __uint_as_float(v[0] << 16); x[1] = __uint_as_float(v[0] & 0xFFFF0000u);
+      x[2] = __uint_as_float(v[1] << 16); x[3] = __uint_as_float(v[1] & 0xFFFF0000u);
+    }
+    const float a = alpha ? alpha[row] : 1.f;
+    bf16x8 hl;   // hi in 0..3, lo in 4..7
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float y = a * x[i];
+      hl[i] = (__bf16)y;
+      hl[4 + i] = (__bf16)(y - (float)hl[i]);
+    }
+    const u32x4 w = __builtin_bit_cast(u32x4, hl);
+    reinterpret_cast<u32x2*>(hi)[qd] = u32x2{w[0], w[1]};
+    if (lo) reinterpret_cast<u32x2*>(lo)[qd] = u32x2{w[2], w[3]};
+  }
 }
 
 }  // namespace
 
-hipError_t launch_grouped_backward(int dtype, int dw_mode, const GemmTable& tab,
-                                   const int32_t* perm, const float* alpha_c, const void* g_c,
-                                   const void* phi_c, const void* W, float* dW, float* dphi,
-                                   int32_t d_out, int32_t d_in, int32_t P, hipStream_t s) {
-  GemmArgs dw{g_c, phi_c, alpha_c, nullptr, dW, d_out, d_in, P};
-  GemmArgs dp{g_c, W, alpha_c, perm, dphi, d_out, d_in, P};
-  if (dtype == LRMOE_F32) return launch<float, 2, 2, 2, 2>(dw, dp, tab, s);
-  if (dw_mode == LRMOE_DW_BF16) return launch<uint16_t, 1, 1, 1, 1>(dw, dp, tab, s);
-  return launch<uint16_t, 2, 1, 1, 1>(dw, dp, tab, s);
+hipError_t launch_split(int src_dtype, const void* src, int64_t rows, int32_t cols,
+                        const float* alpha, uint16_t* hi, uint16_t* lo, hipStream_t s) {
+  const int64_t quads = rows * (cols / 4);
+  if (quads <= 0) return hipSuccess;
+  int64_t blocks = (quads + 255) / 256;
+  if (blocks > 256 * 16) blocks = 256 * 16;
+  if (src_dtype == LRMOE_F32)
+    hipLaunchKernelGGL(split_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, src, rows,
+                       cols, alpha, hi, lo);
+  else
+    hipLaunchKernelGGL(split_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, src, rows,
+                       cols, alpha, hi, lo);
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_backward(const GemmTable& tab, const GemmOperands& ops,
+                                   const int32_t* perm, const float* alpha_c, float* dW,
+                                   float* dphi, int32_t d_out, int32_t d_in, int32_t P,
+                                   hipStream_t s) {
+  const Args args{ops, alpha_c, perm, dW, dphi, d_out, d_in, P};
+  const int key = ops.dw_pa * 1000 + ops.dw_pb * 100 + ops.dp_pa * 10 + ops.dp_pb;
+  switch (key) {
+    case 1211: return launch<1, 2, 1, 1>(args, tab, s);   // bf16, alpha folded into phi
+    case 2111: return launch<2, 1, 1, 1>(args, tab, s);   // bf16, alpha folded into g
+    case 1111: return launch<1, 1, 1, 1>(args, tab, s);   // bf16, single rounding
+    case 2222: return launch<2, 2, 2, 2>(args, tab, s);   // float32 storage
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace lrmoe

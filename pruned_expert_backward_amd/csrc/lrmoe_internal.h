@@ -21,16 +21,35 @@ struct ExpertTable {
   int32_t seg_off[kMaxE + 1];     // first compacted row of expert e
 };
 
-// Tile schedule of the grouped GEMMs (also host-built, by value).
+// Tile schedule of the grouped GEMMs (host-built, by value).  Output tiles
+// are 128x128.  Tiles are handed out in groups of kGroupSlots workgroup slots
+// (a gm x gn block of tiles of one expert that share operand panels); group g
+// runs on XCD g % 8, so the tiles of a group meet in one L2.
+constexpr int kGroupSlots = 12;
+constexpr int kXcds = 8;
+
 struct GemmTable {
   int32_t E;
-  int32_t tiles_n;                // tiles along the output columns (d_in)
-  int32_t tiles_m_fixed;          // dW: tiles along d_out (same for all experts)
-  int32_t dw_tiles;               // weight-gradient blocks (first in the grid)
-  int32_t dp_tiles;               // input-gradient blocks (after them)
+  int32_t tiles_n;                // output column tiles (over d_in)
+  int32_t dw_tiles_m;             // dW row tiles (over d_out)
+  int32_t dw_gm, dw_gn;           // dW group shape, dw_gm * dw_gn <= kGroupSlots
+  int32_t dp_gm, dp_gn;           // dphi group shape
+  int32_t dw_groups;              // dW groups come first ...
+  int32_t total_groups;           // ... then dphi groups
   int32_t seg_off[kMaxE + 1];     // compacted segment offsets
-  int32_t tile_off[kMaxE + 1];    // dphi: first block of expert e
-  int16_t order[kMaxE];           // dW: experts by descending quota
+  int32_t dw_goff[kMaxE + 1];     // first dW group of the expert of LPT rank r
+  int32_t dp_goff[kMaxE + 1];     // first dphi group of expert e (from dw_groups)
+  uint8_t order[kMaxE];           // dW: expert of LPT rank r (descending quota)
+};
+
+// Device operand planes of the two products.  Every plane is bf16; a second
+// plane holds the residual of a float32 value split as hi + lo.
+struct GemmOperands {
+  const uint16_t* dw_a[2];        // [M, d_out]: g_c, or alpha*g_c split
+  const uint16_t* dw_b[2];        // [M, d_in]: phi_c, or alpha*phi_c split
+  const uint16_t* dp_a[2];        // [M, d_out]: g_c
+  const uint16_t* dp_b[2];        // [E, d_out, d_in]: W
+  int32_t dw_pa, dw_pb, dp_pa, dp_pb;   // planes in use (1 or 2)
 };
 
 // Launchers (return hipSuccess or the launch error).
@@ -47,9 +66,14 @@ hipError_t launch_gather(int dtype, const int32_t* perm, const uint8_t* keep,
                          void* phi_c, float* alpha_c, float* dphi_zero, int32_t M,
                          int32_t P, int32_t d_out, int32_t d_in, hipStream_t s);
 
-hipError_t launch_grouped_backward(int dtype, int dw_mode, const GemmTable& tab,
-                                   const int32_t* perm, const float* alpha_c, const void* g_c,
-                                   const void* phi_c, const void* W, float* dW, float* dphi,
-                                   int32_t d_out, int32_t d_in, int32_t P, hipStream_t s);
+// hi (and lo, if non-null) bf16 planes of alpha[row] * src[row][col] (alpha
+// may be null); src is bf16 or float32 storage.
+hipError_t launch_split(int src_dtype, const void* src, int64_t rows, int32_t cols,
+                        const float* alpha, uint16_t* hi, uint16_t* lo, hipStream_t s);
+
+hipError_t launch_grouped_backward(const GemmTable& tab, const GemmOperands& ops,
+                                   const int32_t* perm, const float* alpha_c, float* dW,
+                                   float* dphi, int32_t d_out, int32_t d_in, int32_t P,
+                                   hipStream_t s);
 
 }  // namespace lrmoe
