@@ -75,13 +75,19 @@ lrmoe_status check_problem(const lrmoe_problem* pb, Checked& c) {
 size_t round256(size_t n) { return (n + 255) & ~size_t(255); }
 
 // Workspace of lrmoe_grouped_backward: bf16 operand planes prepared by the
-// prologue.  bf16 storage: alpha times the narrower of g_c / phi_c, as hi +
-// lo planes (exact) or hi only.  float32 storage: hi + lo planes of g_c,
-// alpha*phi_c and W.
+// prologue, then the fp32 partial dW tiles of experts split along K.
+// bf16 storage: alpha times the narrower of g_c / phi_c, as hi + lo planes
+// (exact) or hi only.  float32 storage: hi + lo planes of g_c, alpha*phi_c
+// and W.
 struct GemmWorkspace {
   bool alpha_on_phi = true;
-  size_t a_hi = 0, a_lo = 0, b_hi = 0, b_lo = 0, w_hi = 0, w_lo = 0, total = 0;
+  size_t a_hi = 0, a_lo = 0, b_hi = 0, b_lo = 0, w_hi = 0, w_lo = 0, partials = 0, total = 0;
+  int dw_pa = 1, dw_pb = 1, dp_pa = 1, dp_pb = 1;
+  int32_t kc = 0;          // dW K-chunk length
+  int64_t part_tiles = 0;  // partial tiles of split experts
 };
+
+constexpr int kStepK = 32;   // K rows per pipeline step of the GEMM kernel
 
 GemmWorkspace gemm_workspace(const lrmoe_problem* pb, int64_t M) {
   GemmWorkspace w;
@@ -89,9 +95,13 @@ GemmWorkspace gemm_workspace(const lrmoe_problem* pb, int64_t M) {
   if (pb->dtype == LRMOE_BF16) {
     w.alpha_on_phi = pb->d_in <= pb->d_out;
     const size_t plane = round256(Mz * (size_t)(w.alpha_on_phi ? pb->d_in : pb->d_out) * 2);
+    const bool exact = pb->dw_mode == LRMOE_DW_EXACT;
     w.b_hi = 0;                 // offsets of the scaled operand's planes
     w.b_lo = plane;
-    w.total = pb->dw_mode == LRMOE_DW_EXACT ? 2 * plane : plane;
+    w.total = exact ? 2 * plane : plane;
+    const int np = exact ? 2 : 1;
+    w.dw_pa = w.alpha_on_phi ? 1 : np;
+    w.dw_pb = w.alpha_on_phi ? np : 1;
   } else {
     w.alpha_on_phi = true;
     const size_t gpl = round256(Mz * (size_t)pb->d_out * 2);
@@ -104,7 +114,32 @@ GemmWorkspace gemm_workspace(const lrmoe_problem* pb, int64_t M) {
     w.w_hi = 2 * gpl + 2 * ppl;
     w.w_lo = w.w_hi + wpl;
     w.total = w.w_lo + wpl;
+    w.dw_pa = w.dw_pb = w.dp_pa = w.dp_pb = 2;
   }
+  // K chunk: about two work items per CU, counting MFMA passes of both
+  // products, and never under 1024 rows (fewer partial tiles).
+  const int terms_dw = 1 + (w.dw_pa == 2) + (w.dw_pb == 2);
+  const int terms_dp = 1 + (w.dp_pa == 2) + (w.dp_pb == 2);
+  const int64_t tiles_n = (pb->d_in + kTile - 1) / kTile;
+  const int64_t tiles_m = (pb->d_out + kTile - 1) / kTile;
+  int64_t rows_steps = 0, mtiles = 0;
+  for (int e = 0; e < pb->E; ++e) {
+    rows_steps += (pb->quotas[e] + kStepK - 1) / kStepK;
+    mtiles += (pb->quotas[e] + kTile - 1) / kTile;
+  }
+  const int64_t units = tiles_m * tiles_n * rows_steps * terms_dw +
+                        tiles_n * mtiles * ((pb->d_out + kStepK - 1) / kStepK) * terms_dp;
+  int64_t kc = units / (256 * 2) * kStepK / terms_dw;
+  if (kc < 1024) kc = 1024;
+  kc = (kc + kStepK - 1) / kStepK * kStepK;
+  if (kc > (int64_t(1) << 30)) kc = int64_t(1) << 30;
+  w.kc = (int32_t)kc;
+  for (int e = 0; e < pb->E; ++e) {
+    const int S = dw_chunks((int)pb->quotas[e], w.kc);
+    if (S > 1) w.part_tiles += tiles_m * tiles_n * S;
+  }
+  w.partials = round256(w.total);
+  w.total = w.partials + (size_t)w.part_tiles * kTile * kTile * 4;
   return w;
 }
 
@@ -307,32 +342,35 @@ lrmoe_status lrmoe_grouped_backward(const lrmoe_problem* pb, const int32_t* perm
   GemmTable t;
   memset(&t, 0, sizeof(t));
   t.E = E;
-  t.tiles_n = (d_in + 127) / 128;
-  t.dw_tiles_m = (d_out + 127) / 128;
+  t.tiles_n = (d_in + kTile - 1) / kTile;
+  t.dw_tiles_m = (d_out + kTile - 1) / kTile;
+  t.kc = wl.kc;
   group_shape(t.tiles_n, 3, t.dw_gm, t.dw_gn);
   group_shape(t.tiles_n, 6, t.dp_gm, t.dp_gn);
   for (int e = 0; e <= E; ++e) t.seg_off[e] = c.tab.seg_off[e];
 
-  // Weight-gradient groups: every expert (zeros for q_e = 0), heaviest first.
+  // Weight-gradient groups: every expert (zeros for q_e = 0), heaviest first,
+  // K chunks of one expert consecutive.
   std::vector<int> order(E);
   std::iota(order.begin(), order.end(), 0);
   std::stable_sort(order.begin(), order.end(),
                    [&](int a, int b) { return pb->quotas[a] > pb->quotas[b]; });
   const int ngn_dw = (t.tiles_n + t.dw_gn - 1) / t.dw_gn;
-  const int dw_per_expert = ((t.dw_tiles_m + t.dw_gm - 1) / t.dw_gm) * ngn_dw;
+  const int per_chunk = ((t.dw_tiles_m + t.dw_gm - 1) / t.dw_gm) * ngn_dw;
+  int32_t g = 0;
   for (int r = 0; r < E; ++r) {
     t.order[r] = (uint8_t)order[r];
-    t.dw_goff[r] = r * dw_per_expert;
+    t.dw_goff[r] = g;
+    g += per_chunk * dw_chunks((int)pb->quotas[order[r]], t.kc);
   }
-  t.dw_goff[E] = E * dw_per_expert;
-  t.dw_groups = E * dw_per_expert;
+  t.dw_goff[E] = g;
+  t.dw_groups = g;
   // Input-gradient groups, expert by expert.
   const int ngn_dp = (t.tiles_n + t.dp_gn - 1) / t.dp_gn;
-  int32_t g = t.dw_groups;
   for (int e = 0; e < E; ++e) {
     t.dp_goff[e] = g;
     if (dphi != nullptr) {
-      const int64_t mt = (pb->quotas[e] + 127) / 128;
+      const int64_t mt = (pb->quotas[e] + kTile - 1) / kTile;
       g += (int32_t)(((mt + t.dp_gm - 1) / t.dp_gm) * ngn_dp);
     }
   }
@@ -354,20 +392,17 @@ lrmoe_status lrmoe_grouped_backward(const lrmoe_problem* pb, const int32_t* perm
     const void* src = wl.alpha_on_phi ? phi_c : g_c;
     const int cols = wl.alpha_on_phi ? d_in : d_out;
     LRMOE_TRY(hip_status(launch_split(LRMOE_BF16, src, M, cols, alpha_c, hi, lo, s)));
-    const int np = exact ? 2 : 1;
     if (wl.alpha_on_phi) {
       ops.dw_a[0] = g16;
       ops.dw_b[0] = hi;
       ops.dw_b[1] = lo;
-      ops.dw_pa = 1;
-      ops.dw_pb = np;
     } else {
       ops.dw_a[0] = hi;
       ops.dw_a[1] = lo;
       ops.dw_b[0] = p16;
-      ops.dw_pa = np;
-      ops.dw_pb = 1;
     }
+    ops.dw_pa = wl.dw_pa;
+    ops.dw_pb = wl.dw_pb;
     ops.dp_a[0] = g16;
     ops.dp_b[0] = w16;
     ops.dp_pa = ops.dp_pb = 1;
@@ -388,8 +423,10 @@ lrmoe_status lrmoe_grouped_backward(const lrmoe_problem* pb, const int32_t* perm
     ops.dw_pa = ops.dw_pb = ops.dp_pa = ops.dp_pb = 2;
   }
   (void)w16;
+  ops.partials = reinterpret_cast<float*>(ws + wl.partials);
   LRMOE_TRY(hip_status(launch_grouped_backward(t, ops, perm, alpha_c, dW, dphi, d_out, d_in,
                                                (int32_t)pb->P, s)));
+  LRMOE_TRY(hip_status(launch_reduce_partials(t, ops.partials, dW, d_out, d_in, s)));
   return LRMOE_OK;
 }
 

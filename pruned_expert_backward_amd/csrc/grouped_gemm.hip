@@ -15,8 +15,11 @@
 //                    (varlen), N = d_in, K = d_out.
 //
 // gfx950 mapping
-//   * 256-thread workgroups (4 wave64s, 2x2) own a 128x128 fp32 tile; each
-//     wave accumulates 64x64 with v_mfma_f32_32x32x16_bf16 (fp32 accumulate).
+//   * 512-thread workgroups (8 wave64s, 2 x 4, two per SIMD) own a 256x256
+//     fp32 tile; each wave accumulates 128x64 (128 accumulator registers)
+//     with v_mfma_f32_32x32x16_bf16 (fp32 accumulate).  Large tiles keep
+//     operand bytes per FLOP low enough for L2 and LDS; two waves per SIMD
+//     let one issue MFMAs while the other waits on LDS or the barrier.
 //   * Every operand is a bf16 plane in global memory.  alpha multiplies the
 //     reduction index of dW, so it cannot be applied after the product: a
 //     prologue writes alpha * (the narrower of g_c, phi_c) as bf16 hi + lo
@@ -31,13 +34,22 @@
 //     transposes 4x16 bf16 blocks across each 16-lane group, so no operand is
 //     ever transposed in memory.  16-byte chunks are XOR-swizzled per row so
 //     that fragment reads spread over the LDS banks.
-//   * Two LDS stages, one barrier per K step; global loads run two K steps
-//     ahead of the MFMAs through two register stages.
+//   * Operands move global -> LDS with buffer_load_dwordx4 ... lds (no
+//     register staging): each wave instruction fills one 1 KiB LDS block, lane
+//     i writing bytes 16i..16i+15, so each lane fetches the global chunk that
+//     the swizzled layout puts in its slot; lanes past a row or column edge
+//     get an out-of-range offset and write zeros.  Three LDS stages keep the
+//     loads two K steps ahead of the MFMAs (two for float32 storage, whose
+//     four planes would not fit three times); each step waits only for its
+//     own stage and then crosses one barrier.
 //   * Scheduling: dW and dphi tiles share one launch.  Tiles are grouped in
 //     blocks of an expert's tile grid that share operand panels; group g runs
 //     on XCD g % 8 (workgroups are dispatched round-robin over the 8 XCDs), so
 //     a group's panels are fetched into one L2.  dW groups come first, heaviest
-//     experts first; the uniform dphi groups fill the tail.
+//     experts first; the uniform dphi groups fill the tail.  An expert whose
+//     kept rows exceed one K chunk has its dW split along K: each chunk writes
+//     an fp32 partial tile and a second kernel sums them in chunk order, so
+//     the result does not depend on timing.
 #include "lrmoe_internal.h"
 
 namespace lrmoe {
@@ -53,17 +65,19 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128, BN = 128, BK = 32;
-constexpr int kThreads = 256;
-constexpr int kPlaneBytes = 128 * BK * 2;   // one bf16 operand plane of one K step
+constexpr int BM = kTile, BN = kTile, BK = 32;
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int kPlaneBytes = kTile * BK * 2;   // one bf16 operand plane of one K step (16 KB)
+constexpr int kChunksPerPlane = kTile * BK / 8 / kThreads;   // 16-byte chunks per thread
 
 // ------------------------------------------------------------ LDS layouts
-// KC: row r (0..127) holds K 0..31 as 4 chunks of 16 B.
+// KC: row r (0..255) holds K 0..31 as 4 chunks of 16 B.
 __device__ __forceinline__ int kc_off(int r, int c) {
   return r * 64 + ((c ^ (((r >> 1) ^ (r >> 3)) & 3)) << 4);
 }
-// MC: row k (0..31) holds M/N 0..127 as 16 chunks of 16 B.
-__device__ __forceinline__ int mc_off(int k, int c) { return k * 256 + ((c ^ ((k & 3) << 2)) << 4); }
+// MC: row k (0..31) holds M/N 0..255 as 32 chunks of 16 B.
+__device__ __forceinline__ int mc_off(int k, int c) { return k * 512 + ((c ^ ((k & 3) << 2)) << 4); }
 
 // Fragment: 8 bf16 along K for MN index (mb + lane%32), K = kb + 8*(lane/32) + 0..7.
 __device__ __forceinline__ i16x8 frag_kc(LDS_AS const char* t, int mb, int kb, int lane) {
@@ -101,6 +115,7 @@ __device__ __forceinline__ f32x16 mfma(i16x8 a, i16x8 b, f32x16 c) {
 
 struct TileJob {
   int e, m0, n0;
+  int chunk, chunks;   // dW K chunk of this tile and the expert's chunk count
 };
 
 // Decode the workgroup's tile from the group schedule; false = idle slot.
@@ -118,26 +133,30 @@ __device__ __forceinline__ bool decode(const GemmTable& tab, bool& is_dw, TileJo
     if (goff[mid] <= g) lo = mid; else hi = mid - 1;
   }
   const int e = is_dw ? (int)tab.order[lo] : lo;
-  const int lg = g - goff[lo];
+  int lg = g - goff[lo];
   const int gm = is_dw ? tab.dw_gm : tab.dp_gm;
   const int gn = is_dw ? tab.dw_gn : tab.dp_gn;
   if (t >= gm * gn) return false;
   const int ngn = (tab.tiles_n + gn - 1) / gn;
+  const int q = tab.seg_off[e + 1] - tab.seg_off[e];
+  int chunk = 0, chunks = 1;
+  if (is_dw) {   // groups of one expert: chunk-major
+    chunks = dw_chunks(q, tab.kc);
+    const int per_chunk = ((tab.dw_tiles_m + gm - 1) / gm) * ngn;
+    chunk = lg / per_chunk;
+    lg -= chunk * per_chunk;
+  }
   const int tm = (lg / ngn) * gm + t / gn;
   const int tn = (lg % ngn) * gn + t % gn;
-  const int q = tab.seg_off[e + 1] - tab.seg_off[e];
   const int tiles_m = is_dw ? tab.dw_tiles_m : (q + BM - 1) / BM;
   if (tm >= tiles_m || tn >= tab.tiles_n) return false;
   job.e = e;
   job.m0 = tm * BM;
   job.n0 = tn * BN;
+  job.chunk = chunk;
+  job.chunks = chunks;
   return true;
 }
-
-template <int PA, int PB>
-struct Stage {
-  u32x4 a[PA][2], b[PB][2];
-};
 
 struct Args {
   GemmOperands ops;
@@ -163,21 +182,60 @@ __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff) 
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
 }
 
-// One 128x128 output tile.  IS_DW: A (MC, rows = K) and B (MC, rows = K) are
+// global -> LDS copy of 16 bytes per lane: lane i writes LDS bytes
+// [lds + 16i, lds + 16i + 16).  Issued as inline asm so that the compiler
+// does not treat later LDS reads of other stages as waiting on it; the
+// explicit wait + barrier below orders every stage.  M0 is not used by the
+// compiler anywhere in these kernels.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff),
+               "s"(r)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_addr(LDS_AS const char* p) {
+  return (uint32_t)(uintptr_t)p;
+}
+
+// Wait until at most N of this wave's loads are outstanding, then cross the
+// workgroup barrier.  One asm block, so that the compiler adds no wait of its
+// own for the loads still in flight into other LDS stages.
+template <int N>
+__device__ __forceinline__ void wait_loads_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// One 256x256 output tile.  IS_DW: A (MC, rows = K) and B (MC, rows = K) are
 // [M, d_out] / [M, d_in] segment rows.  Else A (KC, rows = M) = g_c segment
-// rows and B (MC) = W_e.  PA/PB: bf16 planes of each operand.
-template <bool IS_DW, int PA, int PB>
+// rows and B (MC) = W_e.  PA/PB: bf16 planes of each operand; NS: LDS stages.
+template <bool IS_DW, int PA, int PB, int NS>
 __device__ __forceinline__ void gemm_tile(const Args& args, const GemmTable& tab,
                                           const TileJob& job, LDS_AS char* smem) {
   constexpr bool A_MC = IS_DW;
   constexpr int kStage = (PA + PB) * kPlaneBytes;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  constexpr int kDist = NS - 1;                 // prefetch distance in K steps
+  constexpr int kBlocks = kPlaneBytes / 1024;   // 1 KiB LDS blocks per plane
+  constexpr int kPerWave = kBlocks / kWaves;    // ... filled by each wave
+  constexpr int kLoads = (PA + PB) * kPerWave;  // load instructions per stage per wave
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;   // wave tile rows wm*128, cols wn*64
   const int d_out = args.d_out, d_in = args.d_in;
-  const int e = job.e, m0 = job.m0, n0 = job.n0;
-  const int seg = tab.seg_off[e];
-  const int q = tab.seg_off[e + 1] - seg;
-  const int K = IS_DW ? q : d_out;
+  // Tile coordinates are workgroup-uniform; say so, so that buffer
+  // descriptors and LDS bases stay in scalar registers.
+  const int e = __builtin_amdgcn_readfirstlane(job.e);
+  const int m0 = __builtin_amdgcn_readfirstlane(job.m0);
+  const int n0 = __builtin_amdgcn_readfirstlane(job.n0);
+  const int chunk = __builtin_amdgcn_readfirstlane(job.chunk);
+  const int q = tab.seg_off[e + 1] - tab.seg_off[e];
+  // dW: this chunk's rows of the segment; dphi: the whole segment (M) and d_out (K)
+  const int kbeg = IS_DW ? chunk * tab.kc : 0;
+  const int seg = tab.seg_off[e] + kbeg;
+  const int K = IS_DW ? (q - kbeg < tab.kc ? q - kbeg : tab.kc) : d_out;
+  const int mrows = IS_DW ? d_out : q;       // valid rows of the output along M
 
   const uint16_t* A[2];
   const uint16_t* B[2];
@@ -186,132 +244,116 @@ __device__ __forceinline__ void gemm_tile(const Args& args, const GemmTable& tab
     A[p] = IS_DW ? args.ops.dw_a[p] : args.ops.dp_a[p];
     B[p] = IS_DW ? args.ops.dw_b[p] : args.ops.dp_b[p];
   }
-  // Per-thread byte offsets inside one K step (fixed over the loop).
-  uint32_t aoff[2], boff[2];
+  // Byte offsets (within one K step) of the global chunk each lane fetches
+  // for each of its LDS blocks: block b = wave*kPerWave + j.
+  uint32_t aoff[kPerWave], boff[kPerWave];
+  int acol[kPerWave];   // KC only: K column of the chunk within the step
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int idx = tid + h * kThreads;
-    if (A_MC) {   // row k of the step, 8-element chunk along M (o)
-      const int k = idx >> 4, col = m0 + 8 * (idx & 15);
-      aoff[h] = col < d_out ? (uint32_t)(k * d_out + col) * 2u : kOutOfRange;
-    } else {      // row r of the tile, chunk along K (o); K offset added per step
-      const int r = idx >> 2;
-      aoff[h] = (uint32_t)(r * d_out + 8 * (idx & 3)) * 2u;
+  for (int j = 0; j < kPerWave; ++j) {
+    const int blk = wave * kPerWave + j;
+    {   // MC block: rows 2*blk, 2*blk+1 of the step, 32 chunks each
+      const int k = 2 * blk + (lane >> 5), pc = lane & 31;
+      const int lc = pc ^ ((k & 3) << 2);
+      const int col = n0 + 8 * lc;
+      boff[j] = col < d_in ? (uint32_t)(k * d_in + col) * 2u : kOutOfRange;
+      if (A_MC) {
+        const int acolm = m0 + 8 * lc;
+        aoff[j] = acolm < d_out ? (uint32_t)(k * d_out + acolm) * 2u : kOutOfRange;
+      }
     }
-    const int k = idx >> 4, col = n0 + 8 * (idx & 15);
-    boff[h] = col < d_in ? (uint32_t)(k * d_in + col) * 2u : kOutOfRange;
+    if (!A_MC) {   // KC block: rows 16*blk .. +15 of the tile, 4 chunks each
+      const int r = 16 * blk + (lane >> 2), pc = lane & 3;
+      const int lc = pc ^ (((r >> 1) ^ (r >> 3)) & 3);
+      acol[j] = 8 * lc;
+      aoff[j] = (uint32_t)(r * d_out + 8 * lc) * 2u;
+    }
   }
 
-  // ---- global -> registers for the K step starting at k0
-  auto gload = [&](int k0, Stage<PA, PB>& st) {
+  // ---- global -> LDS stage for the K step starting at k0
+  auto issue = [&](int k0, LDS_AS char* stage) {
     const int krows = K - k0 < BK ? K - k0 : BK;
-    __amdgpu_buffer_rsrc_t ra[PA], rb[PB];
 #pragma unroll
     for (int p = 0; p < PA; ++p) {
-      if (A_MC) ra[p] = rsrc(A[p] + ((int64_t)seg + k0) * d_out, (int64_t)krows * d_out * 2);
-      else ra[p] = rsrc(A[p] + ((int64_t)seg + m0) * d_out, (int64_t)(q - m0) * d_out * 2);
+      __amdgpu_buffer_rsrc_t r =
+          A_MC ? rsrc(A[p] + ((int64_t)seg + k0) * d_out, (int64_t)krows * d_out * 2)
+               : rsrc(A[p] + ((int64_t)seg + m0) * d_out, (int64_t)(q - m0) * d_out * 2);
+#pragma unroll
+      for (int j = 0; j < kPerWave; ++j) {
+        uint32_t off = aoff[j];
+        if (!A_MC) off = (k0 + acol[j]) < K ? off + (uint32_t)k0 * 2u : kOutOfRange;
+        load_lds16(r, lds_addr(stage + p * kPlaneBytes + (wave * kPerWave + j) * 1024), off);
+      }
     }
 #pragma unroll
     for (int p = 0; p < PB; ++p) {
       const uint16_t* b0 = IS_DW ? B[p] + ((int64_t)seg + k0) * d_in
                                  : B[p] + ((int64_t)e * d_out + k0) * d_in;
-      rb[p] = rsrc(b0, (int64_t)krows * d_in * 2);
-    }
+      __amdgpu_buffer_rsrc_t r = rsrc(b0, (int64_t)krows * d_in * 2);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      uint32_t ao = aoff[h];
-      if (!A_MC) {   // K columns of this step; past d_out reads zero
-        const int kcol = k0 + 8 * ((tid + h * kThreads) & 3);
-        ao = kcol < K ? ao + (uint32_t)k0 * 2u : kOutOfRange;
-      }
-#pragma unroll
-      for (int p = 0; p < PA; ++p) st.a[p][h] = bload(ra[p], ao);
-#pragma unroll
-      for (int p = 0; p < PB; ++p) st.b[p][h] = bload(rb[p], boff[h]);
-    }
-  };
-  // ---- registers -> one LDS stage: A planes then B planes
-  auto lstore = [&](const Stage<PA, PB>& st, LDS_AS char* stage) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int idx = tid + h * kThreads;
-      const int ao = A_MC ? mc_off(idx >> 4, idx & 15) : kc_off(idx >> 2, idx & 3);
-      const int bo = mc_off(idx >> 4, idx & 15);
-#pragma unroll
-      for (int p = 0; p < PA; ++p)
-        *reinterpret_cast<LDS_AS u32x4*>(stage + p * kPlaneBytes + ao) = st.a[p][h];
-#pragma unroll
-      for (int p = 0; p < PB; ++p)
-        *reinterpret_cast<LDS_AS u32x4*>(stage + (PA + p) * kPlaneBytes + bo) = st.b[p][h];
+      for (int j = 0; j < kPerWave; ++j)
+        load_lds16(r, lds_addr(stage + (PA + p) * kPlaneBytes + (wave * kPerWave + j) * 1024),
+                   boff[j]);
     }
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[4][2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  // ---- MFMAs of one K step: hi*hi (+ hi*lo_B) (+ lo_A*hi)
+  // ---- MFMAs of one K step: hi*hi (+ hi*lo_B) (+ lo_A*hi).  All fragments
+  // of the step are read first, so the second half's LDS reads overlap the
+  // first half's MFMAs.
   auto compute = [&](LDS_AS const char* stage) {
+    i16x8 fb[2][PB][2], fa[2][PA][4];
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      i16x8 fb[PB][2], fa[PA][2];
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
       for (int p = 0; p < PB; ++p)
 #pragma unroll
         for (int b = 0; b < 2; ++b)
-          fb[p][b] = frag_mc(stage + (PA + p) * kPlaneBytes, wn * 64 + b * 32, kk, lane);
+          fb[h][p][b] = frag_mc(stage + (PA + p) * kPlaneBytes, wn * 64 + b * 32, 16 * h, lane);
 #pragma unroll
       for (int p = 0; p < PA; ++p)
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
-          fa[p][a] = frag<A_MC>(stage + p * kPlaneBytes, wm * 64 + a * 32, kk, lane);
+        for (int a = 0; a < 4; ++a)
+          fa[h][p][a] = frag<A_MC>(stage + p * kPlaneBytes, wm * 128 + a * 32, 16 * h, lane);
+    }
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-          acc[a][b] = mfma(fa[0][a], fb[0][b], acc[a][b]);
-          if (PB == 2) acc[a][b] = mfma(fa[0][a], fb[PB - 1][b], acc[a][b]);
-          if (PA == 2) acc[a][b] = mfma(fa[PA - 1][a], fb[0][b], acc[a][b]);
+          acc[a][b] = mfma(fa[h][0][a], fb[h][0][b], acc[a][b]);
+          if (PB == 2) acc[a][b] = mfma(fa[h][0][a], fb[h][PB - 1][b], acc[a][b]);
+          if (PA == 2) acc[a][b] = mfma(fa[h][PA - 1][a], fb[h][0][b], acc[a][b]);
         }
-    }
   };
 
-  // ---- pipeline: loads two steps ahead, two LDS stages, one barrier per
-  // step; unrolled by two so that each register stage has a fixed name.
+  // ---- pipeline: stage kt lives in LDS buffer kt % NS; the loads of step
+  // kt + kDist go into the buffer that step kt - 1 used, after the barrier
+  // that follows everyone's MFMAs of step kt - 1.
   const int nk = (K + BK - 1) / BK;
-  Stage<PA, PB> r0, r1;
-  LDS_AS char* st0 = smem;
-  LDS_AS char* st1 = smem + kStage;
-  if (nk > 0) {
-    gload(0, r0);
-    gload(BK, r1);
-    lstore(r0, st0);
-    __syncthreads();
+#pragma unroll
+  for (int d = 0; d < kDist; ++d) issue(d * BK, smem + d * kStage);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_loads_barrier<(kDist - 1) * kLoads>();
+    issue((kt + kDist) * BK, smem + ((kt + kDist) % NS) * kStage);
+    compute(smem + (kt % NS) * kStage);
   }
-  // Loads past the end of K see an empty buffer and return zeros without
-  // touching memory, so they are issued unconditionally: branch-free code
-  // lets each wait cover exactly the older register stage.
-  for (int kt = 0; kt < nk; kt += 2) {
-    gload((kt + 2) * BK, r0);
-    compute(st0);
-    lstore(r1, st1);
-    __syncthreads();
-    if (kt + 1 >= nk) break;
-    gload((kt + 3) * BK, r1);
-    compute(st1);
-    lstore(r0, st0);
-    __syncthreads();
-  }
+  // Loads past the end of K wrote zeros into LDS: drain them before the
+  // epilogue reuses the stages.
+  wait_loads_barrier<0>();
 
   // ---- epilogue: D[i][j] sits in lane j + 32*((i/4)%2), register (i%4) + 4*(i/8)
   const int fl = lane & 31;
   LDS_AS int32_t* s_perm = reinterpret_cast<LDS_AS int32_t*>(smem);
   LDS_AS float* s_alpha = reinterpret_cast<LDS_AS float*>(smem + BM * 4);
-  if (!IS_DW) {   // destination row and alpha of the tile's 128 rows, via LDS
+  if (!IS_DW) {   // destination row and alpha of the tile's rows, via LDS
     if (tid < BM) {
       const bool ok = m0 + tid < q;
       const int32_t u = ok ? args.perm[seg + m0 + tid] : -1;
@@ -320,14 +362,25 @@ __device__ __forceinline__ void gemm_tile(const Args& args, const GemmTable& tab
     }
     __syncthreads();
   }
+  // Split dW tiles go to their chunk's partial tile (full 256x256, row-major).
+  float* part = nullptr;
+  if (IS_DW && job.chunks > 1) {
+    const int tile = (m0 / BM) * tab.tiles_n + n0 / BN;
+    part = args.ops.partials +
+           ((partial_base(tab, e) + (int64_t)tile * job.chunks + chunk) << 16);
+  }
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
+  for (int a = 0; a < 4; ++a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int i = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      const int mrow = m0 + wm * 64 + a * 32 + i;
+      const int lrow = wm * 128 + a * 32 + i;
+      const int mrow = m0 + lrow;
       if (IS_DW) {
-        if (mrow < d_out) {
+        if (part != nullptr) {
+#pragma unroll
+          for (int b = 0; b < 2; ++b) part[lrow * BN + wn * 64 + b * 32 + fl] = acc[a][b][r];
+        } else if (mrow < mrows) {
           float* orow = args.dW + ((int64_t)e * d_out + mrow) * d_in;
 #pragma unroll
           for (int b = 0; b < 2; ++b) {
@@ -336,9 +389,8 @@ __device__ __forceinline__ void gemm_tile(const Args& args, const GemmTable& tab
           }
         }
       } else {
-        const int lr = mrow - m0;
-        const int32_t u = s_perm[lr];
-        const float al = s_alpha[lr];
+        const int32_t u = s_perm[lrow];
+        const float al = s_alpha[lrow];
         if (u >= 0) {
           float* orow = args.dphi + (int64_t)u * d_in;
 #pragma unroll
@@ -352,34 +404,65 @@ __device__ __forceinline__ void gemm_tile(const Args& args, const GemmTable& tab
   }
 }
 
-template <int DW_PA, int DW_PB, int DP_PA, int DP_PB>
+template <int DW_PA, int DW_PB, int DP_PA, int DP_PB, int NS>
 struct Cfg {
-  static constexpr int dw_bytes = 2 * (DW_PA + DW_PB) * kPlaneBytes;
-  static constexpr int dp_bytes = 2 * (DP_PA + DP_PB) * kPlaneBytes;
+  static constexpr int dw_bytes = NS * (DW_PA + DW_PB) * kPlaneBytes;
+  static constexpr int dp_bytes = NS * (DP_PA + DP_PB) * kPlaneBytes;
   static constexpr int bytes = dw_bytes > dp_bytes ? dw_bytes : dp_bytes;
 };
 
-template <int DW_PA, int DW_PB, int DP_PA, int DP_PB>
-__global__ __launch_bounds__(kThreads, 2) void grouped_backward_kernel(Args args, GemmTable tab) {
-  __shared__ __attribute__((aligned(16))) char smem_raw[Cfg<DW_PA, DW_PB, DP_PA, DP_PB>::bytes];
+template <int DW_PA, int DW_PB, int DP_PA, int DP_PB, int NS>
+__global__ __launch_bounds__(kThreads, 1) void grouped_backward_kernel(Args args, GemmTable tab) {
+  __shared__ __attribute__((aligned(16))) char smem_raw[Cfg<DW_PA, DW_PB, DP_PA, DP_PB, NS>::bytes];
   LDS_AS char* smem = (LDS_AS char*)(smem_raw);
   bool is_dw;
   TileJob job;
   if (!decode(tab, is_dw, job)) return;
   if (is_dw)
-    gemm_tile<true, DW_PA, DW_PB>(args, tab, job, smem);
+    gemm_tile<true, DW_PA, DW_PB, NS>(args, tab, job, smem);
   else
-    gemm_tile<false, DP_PA, DP_PB>(args, tab, job, smem);
+    gemm_tile<false, DP_PA, DP_PB, NS>(args, tab, job, smem);
 }
 
-template <int DW_PA, int DW_PB, int DP_PA, int DP_PB>
+template <int DW_PA, int DW_PB, int DP_PA, int DP_PB, int NS>
 hipError_t launch(const Args& args, const GemmTable& tab, hipStream_t s) {
   const int64_t queue = (tab.total_groups + kXcds - 1) / kXcds;
   const int64_t blocks = queue * kXcds * kGroupSlots;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_backward_kernel<DW_PA, DW_PB, DP_PA, DP_PB>), dim3((unsigned)blocks),
-                     dim3(kThreads), 0, s, args, tab);
+  hipLaunchKernelGGL((grouped_backward_kernel<DW_PA, DW_PB, DP_PA, DP_PB, NS>),
+                     dim3((unsigned)blocks), dim3(kThreads), 0, s, args, tab);
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------ split-K reduction
+// One workgroup per (split expert, tile): dW tile = sum over chunks (in chunk
+// order) of the partial tiles, cropped to the matrix edge.
+__global__ __launch_bounds__(256) void reduce_partials_kernel(GemmTable tab,
+                                                              const float* __restrict__ partials,
+                                                              float* __restrict__ dW, int32_t d_out,
+                                                              int32_t d_in) {
+  const int tiles = tab.dw_tiles_m * tab.tiles_n;
+  int b = blockIdx.x;
+  int e = 0, S = 1;
+  for (; e < tab.E; ++e) {   // find the b-th tile among split experts
+    S = dw_chunks(tab.seg_off[e + 1] - tab.seg_off[e], tab.kc);
+    if (S > 1) {
+      if (b < tiles) break;
+      b -= tiles;
+    }
+  }
+  if (e >= tab.E) return;
+  const int tile = b;
+  const int m0 = (tile / tab.tiles_n) * BM, n0 = (tile % tab.tiles_n) * BN;
+  const f32x4* src = reinterpret_cast<const f32x4*>(
+      partials + ((partial_base(tab, e) + (int64_t)tile * S) << 16));
+  for (int v = threadIdx.x; v < BM * BN / 4; v += blockDim.x) {
+    const int row = v / (BN / 4), col = (v % (BN / 4)) * 4;
+    if (m0 + row >= d_out || n0 + col >= d_in) continue;
+    f32x4 acc = src[v];
+    for (int c = 1; c < S; ++c) acc += src[(int64_t)c * (BM * BN / 4) + v];
+    *reinterpret_cast<f32x4*>(dW + ((int64_t)e * d_out + m0 + row) * d_in + n0 + col) = acc;
+  }
 }
 
 // ------------------------------------------------------------ operand prologue
@@ -433,6 +516,18 @@ hipError_t launch_split(int src_dtype, const void* src, int64_t rows, int32_t co
   return hipGetLastError();
 }
 
+hipError_t launch_reduce_partials(const GemmTable& tab, const float* partials, float* dW,
+                                  int32_t d_out, int32_t d_in, hipStream_t s) {
+  int64_t blocks = 0;
+  for (int e = 0; e < tab.E; ++e)
+    if (dw_chunks(tab.seg_off[e + 1] - tab.seg_off[e], tab.kc) > 1)
+      blocks += (int64_t)tab.dw_tiles_m * tab.tiles_n;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)blocks), dim3(256), 0, s, tab,
+                     partials, dW, d_out, d_in);
+  return hipGetLastError();
+}
+
 hipError_t launch_grouped_backward(const GemmTable& tab, const GemmOperands& ops,
                                    const int32_t* perm, const float* alpha_c, float* dW,
                                    float* dphi, int32_t d_out, int32_t d_in, int32_t P,
@@ -440,10 +535,10 @@ hipError_t launch_grouped_backward(const GemmTable& tab, const GemmOperands& ops
   const Args args{ops, alpha_c, perm, dW, dphi, d_out, d_in, P};
   const int key = ops.dw_pa * 1000 + ops.dw_pb * 100 + ops.dp_pa * 10 + ops.dp_pb;
   switch (key) {
-    case 1211: return launch<1, 2, 1, 1>(args, tab, s);   // bf16, alpha folded into phi
-    case 2111: return launch<2, 1, 1, 1>(args, tab, s);   // bf16, alpha folded into g
-    case 1111: return launch<1, 1, 1, 1>(args, tab, s);   // bf16, single rounding
-    case 2222: return launch<2, 2, 2, 2>(args, tab, s);   // float32 storage
+    case 1211: return launch<1, 2, 1, 1, 3>(args, tab, s);   // bf16, alpha folded into phi
+    case 2111: return launch<2, 1, 1, 1, 3>(args, tab, s);   // bf16, alpha folded into g
+    case 1111: return launch<1, 1, 1, 1, 3>(args, tab, s);   // bf16, single rounding
+    case 2222: return launch<2, 2, 2, 2, 2>(args, tab, s);   // float32 storage
     default: return hipErrorInvalidValue;
   }
 }

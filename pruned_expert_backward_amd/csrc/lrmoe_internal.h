@@ -22,9 +22,13 @@ struct ExpertTable {
 };
 
 // Tile schedule of the grouped GEMMs (host-built, by value).  Output tiles
-// are 128x128.  Tiles are handed out in groups of kGroupSlots workgroup slots
-// (a gm x gn block of tiles of one expert that share operand panels); group g
-// runs on XCD g % 8, so the tiles of a group meet in one L2.
+// are kTile x kTile.  Work is handed out in groups of kGroupSlots workgroup
+// slots (a gm x gn block of tiles of one expert and K chunk, sharing operand
+// panels); group g runs on XCD g % 8, so the tiles of a group meet in one L2.
+// The weight gradient of an expert with many kept rows is split along K into
+// chunks of kc rows whose fp32 partial tiles are summed afterwards in chunk
+// order.
+constexpr int kTile = 256;
 constexpr int kGroupSlots = 12;
 constexpr int kXcds = 8;
 
@@ -34,6 +38,7 @@ struct GemmTable {
   int32_t dw_tiles_m;             // dW row tiles (over d_out)
   int32_t dw_gm, dw_gn;           // dW group shape, dw_gm * dw_gn <= kGroupSlots
   int32_t dp_gm, dp_gn;           // dphi group shape
+  int32_t kc;                     // dW K-chunk length (multiple of the K step)
   int32_t dw_groups;              // dW groups come first ...
   int32_t total_groups;           // ... then dphi groups
   int32_t seg_off[kMaxE + 1];     // compacted segment offsets
@@ -50,7 +55,22 @@ struct GemmOperands {
   const uint16_t* dp_a[2];        // [M, d_out]: g_c
   const uint16_t* dp_b[2];        // [E, d_out, d_in]: W
   int32_t dw_pa, dw_pb, dp_pa, dp_pb;   // planes in use (1 or 2)
+  float* partials;                // fp32 partial dW tiles of split experts
 };
+
+// Number of K chunks of an expert with q kept rows.
+__host__ __device__ inline int dw_chunks(int q, int kc) { return q <= kc ? 1 : (q + kc - 1) / kc; }
+
+// First partial tile of expert e (tiles of split experts, chunk-minor).
+__host__ __device__ inline int64_t partial_base(const GemmTable& t, int e) {
+  int64_t base = 0;
+  const int tiles = t.dw_tiles_m * t.tiles_n;
+  for (int x = 0; x < e; ++x) {
+    const int S = dw_chunks(t.seg_off[x + 1] - t.seg_off[x], t.kc);
+    if (S > 1) base += (int64_t)tiles * S;
+  }
+  return base;
+}
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_score(int dtype, const void* g, const void* phi, const float* alpha,
@@ -75,5 +95,9 @@ hipError_t launch_grouped_backward(const GemmTable& tab, const GemmOperands& ops
                                    const int32_t* perm, const float* alpha_c, float* dW,
                                    float* dphi, int32_t d_out, int32_t d_in, int32_t P,
                                    hipStream_t s);
+
+// dW tiles of split experts: sum of the chunk partials, in chunk order.
+hipError_t launch_reduce_partials(const GemmTable& tab, const float* partials, float* dW,
+                                  int32_t d_out, int32_t d_in, hipStream_t s);
 
 }  // namespace lrmoe
