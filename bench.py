@@ -6,9 +6,10 @@ the fused varlen grouped GEMM for dW and dphi (lrmoe_grouped_backward).
 Inputs are resident in HBM before timing starts; outputs are preallocated.
 
 Prints ONE JSON line.  value = kept pairs per second of the whole path.
-`roofline` is for the dominant kernel (measured with HIP events on the
-stream the library launches on, over the timed steps); `kernels` gives both
-calls; `cpu_baseline` times the CPU oracle on the host cores.
+`roofline` is for the dominant kernel, the fused grouped GEMM (HIP events
+recorded by the library around that launch, on the stream it launches on,
+over every timed step); `kernels` gives each kernel's mean time and rate;
+`cpu_baseline` times the CPU oracle on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps 1000] [--warmup 50] [--config 1]
 """
@@ -113,49 +114,52 @@ def main():
     dW = torch.empty((p.E, p.d_out, p.d_in), dtype=torch.float32, device=dev)
     ws = lrmoe.workspace(plan, dev)
     stream = torch.cuda.current_stream()
+    ssc_timer = lrmoe.KernelTimer(args.steps)
+    gb_timer = lrmoe.KernelTimer(args.steps)
 
-    def step(evs=None):
-        if evs:
-            evs[0].record(stream)
-        lrmoe.score_select_compact(plan, alpha, g, phi, g_row_index=row, out=out, ws=ws)
-        if evs:
-            evs[1].record(stream)
+    def step(timed=False):
+        lrmoe.score_select_compact(plan, alpha, g, phi, g_row_index=row, out=out, ws=ws,
+                                   timing=ssc_timer if timed else None)
         lrmoe.grouped_backward(plan, out["perm"], out["alpha_c"], out["g_c"], out["phi_c"], W,
-                               dW=dW, dphi=out["dphi"], ws=ws)
-        if evs:
-            evs[2].record(stream)
+                               dW=dW, dphi=out["dphi"], ws=ws, timing=gb_timer if timed else None)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(events[k])
+    for _ in range(args.steps):
+        step(timed=True)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    t_ssc = float(np.mean([e[0].elapsed_time(e[1]) for e in events])) * 1e-3
-    t_gb = float(np.mean([e[1].elapsed_time(e[2]) for e in events])) * 1e-3
+    es = 2 if p.dtype == "bf16" else 4
+    P, d_o, d_i = p.P, p.d_out, p.d_in
+    us = {"lrm_score": ssc_timer.mean_us(0), "select_scan": ssc_timer.mean_us(1),
+          "gather": ssc_timer.mean_us(2), "operand_prologue": gb_timer.mean_us(0),
+          "grouped_gemm": gb_timer.mean_us(1), "splitk_reduce": gb_timer.mean_us(2)}
+    # algorithmic bytes (HBM-bound kernels) and FLOP (the GEMM) per launch
+    work = {"lrm_score": P * (es * (d_o + d_i) + 8),
+            "select_scan": P * 5,
+            "gather": M * (2 * es * (d_o + d_i) + 12) + (P - M) * 4 * d_i,
+            "grouped_gemm": gemm_flops(p, M)}
+    kernels = {}
+    for name, t in us.items():
+        if t is None:
+            continue
+        k = {"us": t}
+        if name == "grouped_gemm":
+            k.update(algorithmic_flops=work[name], TFLOPs=work[name] / t / 1e6,
+                     mfma_frac=work[name] / t / 1e6 / MFMA_BF16_PEAK_TFLOPS)
+        elif name in work:
+            k.update(algorithmic_bytes=work[name], GBps=work[name] / t / 1e3,
+                     hbm_frac=work[name] / t / 1e3 / HBM_PEAK_GBS)
+        kernels[name] = k
+    ssc_us = sum(us[n] for n in ("lrm_score", "select_scan", "gather") if us[n] is not None)
     nbytes = algorithmic_bytes(p, M)
-    flops = gemm_flops(p, M)
-    ssc_gbs = nbytes / t_ssc / 1e9
-    gb_tflops = flops / t_gb / 1e12
-    kernels = {
-        "score_select_compact": dict(us=t_ssc * 1e6, launches=3, algorithmic_bytes=nbytes,
-                                     GBps=ssc_gbs, hbm_frac=ssc_gbs / HBM_PEAK_GBS),
-        "grouped_backward": dict(us=t_gb * 1e6, launches=1, algorithmic_flops=flops,
-                                 TFLOPs=gb_tflops, mfma_frac=gb_tflops / MFMA_BF16_PEAK_TFLOPS,
-                                 hbm_floor_bytes=gemm_floor_bytes(p, M)),
-    }
-    if t_gb >= t_ssc:
-        roof = dict(kernel="grouped_backward_kernel", bound="mfma", achieved=gb_tflops,
-                    peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=gb_tflops / MFMA_BF16_PEAK_TFLOPS, traffic=None)
-    else:
-        roof = dict(kernel="score_select_compact (3 launches)", bound="hbm", achieved=ssc_gbs,
-                    peak=HBM_PEAK_GBS, unit="GB/s", frac=ssc_gbs / HBM_PEAK_GBS, traffic=None)
+    gemm_tf = kernels["grouped_gemm"]["TFLOPs"]
+    roof = dict(kernel="grouped_backward_kernel", bound="mfma", achieved=gemm_tf,
+                peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s", frac=gemm_tf / MFMA_BF16_PEAK_TFLOPS,
+                traffic=None)
     rec = {
         "metric": "kept pairs/s + grouped-GEMM TFLOP/s (% MFMA peak), score/compact % HBM BW",
         "value": M * args.steps / elapsed,
@@ -169,8 +173,13 @@ def main():
                    "kept_pairs": M, "policy": list(p.policy), "dw_mode": args.dw_mode,
                    "parallelism": "single GPU (one expert-parallel rank's share)"},
         "roofline": roof,
+        "score_select_compact": {"us": ssc_us, "algorithmic_bytes": nbytes,
+                                 "GBps": nbytes / ssc_us / 1e3,
+                                 "hbm_frac": nbytes / ssc_us / 1e3 / HBM_PEAK_GBS},
         "kernels": kernels,
     }
+    ssc_timer.close()
+    gb_timer.close()
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(p)
     print(json.dumps(rec), flush=True)

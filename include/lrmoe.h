@@ -189,6 +189,34 @@ lrmoe_status lrmoe_grouped_backward(
     const void* g_c, const void* phi_c, const void* W, float* dW, float* dphi,
     void* workspace, size_t ws_bytes, void* stream);
 
+/* Per-kernel timing.  Each entry point below launches a fixed sequence of
+ * kernels; for every non-NULL pair, `before` and `after` (hipEvent_t created
+ * by the caller with timing enabled) are recorded on `stream` right before
+ * and right after that kernel's launch.  Kernels not launched for a problem
+ * (an empty range) leave their events unrecorded.
+ *   lrmoe_score_select_compact_timed: [0] score  [1] select+scan  [2] gather
+ *   lrmoe_grouped_backward_timed:     [0] operand prologue  [1] grouped GEMM
+ *                                     [2] split-K reduction */
+#define LRMOE_TIMING_SLOTS 4
+typedef struct {
+  void* before[LRMOE_TIMING_SLOTS];
+  void* after[LRMOE_TIMING_SLOTS];
+} lrmoe_timing;
+
+/* lrmoe_score_select_compact with per-kernel events (timing may be NULL). */
+lrmoe_status lrmoe_score_select_compact_timed(
+    const lrmoe_problem* pb, const int32_t* g_row_index, const float* alpha,
+    const void* g, const void* phi, float* scores, uint8_t* keep,
+    int32_t* seg_offsets, int32_t* perm, void* g_c, void* phi_c, float* alpha_c,
+    float* dphi_zero, void* workspace, size_t ws_bytes, void* stream,
+    const lrmoe_timing* timing);
+
+/* lrmoe_grouped_backward with per-kernel events (timing may be NULL). */
+lrmoe_status lrmoe_grouped_backward_timed(
+    const lrmoe_problem* pb, const int32_t* perm, const float* alpha_c,
+    const void* g_c, const void* phi_c, const void* W, float* dW, float* dphi,
+    void* workspace, size_t ws_bytes, void* stream, const lrmoe_timing* timing);
+
 #ifdef __cplusplus
 }
 #endif

@@ -168,6 +168,14 @@ void group_shape(int nt, int pref, int32_t& gm, int32_t& gn) {
 
 lrmoe_status hip_status(hipError_t e) { return e == hipSuccess ? LRMOE_OK : LRMOE_ERR_HIP; }
 
+// Records the caller's event of one timing slot (if any) on the stream.
+lrmoe_status mark(const lrmoe_timing* t, bool after, int slot, hipStream_t s) {
+  if (t == nullptr) return LRMOE_OK;
+  void* ev = after ? t->after[slot] : t->before[slot];
+  if (ev == nullptr) return LRMOE_OK;
+  return hip_status(hipEventRecord(reinterpret_cast<hipEvent_t>(ev), s));
+}
+
 int64_t elem_bytes(const lrmoe_problem* pb) { return pb->dtype == LRMOE_BF16 ? 2 : 4; }
 
 // Shared body of the two select entry points.
@@ -176,7 +184,7 @@ lrmoe_status select_compact(const lrmoe_problem* pb, bool compute_scores, const 
                             const void* phi, float* scores_out, uint8_t* keep,
                             int32_t* seg_offsets, int32_t* perm, void* g_c, void* phi_c,
                             float* alpha_c, float* dphi_zero, void* workspace, size_t ws_bytes,
-                            void* stream) {
+                            void* stream, const lrmoe_timing* timing) {
   Checked c;
   LRMOE_TRY(check_problem(pb, c));
   const int64_t P = pb->P, M = c.M;
@@ -202,14 +210,20 @@ lrmoe_status select_compact(const lrmoe_problem* pb, bool compute_scores, const 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const float* scores = scores_in;
   if (compute_scores) {
+    LRMOE_TRY(mark(timing, false, 0, s));
     LRMOE_TRY(hip_status(launch_score(pb->dtype, g, phi, alpha, g_row_index, (int32_t)P,
                                       pb->d_out, pb->d_in, scores_out, s)));
+    LRMOE_TRY(mark(timing, true, 0, s));
     scores = scores_out;
   }
+  LRMOE_TRY(mark(timing, false, 1, s));
   LRMOE_TRY(hip_status(launch_select_scan(c.tab, scores, keep, perm, seg_offsets, s)));
+  LRMOE_TRY(mark(timing, true, 1, s));
+  LRMOE_TRY(mark(timing, false, 2, s));
   LRMOE_TRY(hip_status(launch_gather(pb->dtype, perm, keep, g_row_index, nullptr, alpha, g, phi,
                                      g_c, phi_c, alpha_c, dphi_zero, (int32_t)M, (int32_t)P,
                                      pb->d_out, pb->d_in, s)));
+  LRMOE_TRY(mark(timing, true, 2, s));
   return LRMOE_OK;
 }
 
@@ -279,7 +293,19 @@ lrmoe_status lrmoe_score_select_compact(const lrmoe_problem* pb, const int32_t* 
                                         float* dphi_zero, void* workspace, size_t ws_bytes,
                                         void* stream) {
   return select_compact(pb, true, nullptr, g_row_index, alpha, g, phi, scores, keep, seg_offsets,
-                        perm, g_c, phi_c, alpha_c, dphi_zero, workspace, ws_bytes, stream);
+                        perm, g_c, phi_c, alpha_c, dphi_zero, workspace, ws_bytes, stream,
+                        nullptr);
+}
+
+lrmoe_status lrmoe_score_select_compact_timed(const lrmoe_problem* pb, const int32_t* g_row_index,
+                                              const float* alpha, const void* g, const void* phi,
+                                              float* scores, uint8_t* keep, int32_t* seg_offsets,
+                                              int32_t* perm, void* g_c, void* phi_c,
+                                              float* alpha_c, float* dphi_zero, void* workspace,
+                                              size_t ws_bytes, void* stream,
+                                              const lrmoe_timing* timing) {
+  return select_compact(pb, true, nullptr, g_row_index, alpha, g, phi, scores, keep, seg_offsets,
+                        perm, g_c, phi_c, alpha_c, dphi_zero, workspace, ws_bytes, stream, timing);
 }
 
 lrmoe_status lrmoe_select_compact(const lrmoe_problem* pb, const float* scores,
@@ -289,7 +315,8 @@ lrmoe_status lrmoe_select_compact(const lrmoe_problem* pb, const float* scores,
                                   float* dphi_zero, void* workspace, size_t ws_bytes,
                                   void* stream) {
   return select_compact(pb, false, scores, g_row_index, alpha, g, phi, nullptr, keep, seg_offsets,
-                        perm, g_c, phi_c, alpha_c, dphi_zero, workspace, ws_bytes, stream);
+                        perm, g_c, phi_c, alpha_c, dphi_zero, workspace, ws_bytes, stream,
+                        nullptr);
 }
 
 lrmoe_status lrmoe_gather_compact(const lrmoe_problem* pb, const int32_t* perm,
@@ -322,6 +349,15 @@ lrmoe_status lrmoe_grouped_backward(const lrmoe_problem* pb, const int32_t* perm
                                     const float* alpha_c, const void* g_c, const void* phi_c,
                                     const void* W, float* dW, float* dphi, void* workspace,
                                     size_t ws_bytes, void* stream) {
+  return lrmoe_grouped_backward_timed(pb, perm, alpha_c, g_c, phi_c, W, dW, dphi, workspace,
+                                      ws_bytes, stream, nullptr);
+}
+
+lrmoe_status lrmoe_grouped_backward_timed(const lrmoe_problem* pb, const int32_t* perm,
+                                          const float* alpha_c, const void* g_c,
+                                          const void* phi_c, const void* W, float* dW,
+                                          float* dphi, void* workspace, size_t ws_bytes,
+                                          void* stream, const lrmoe_timing* timing) {
   Checked c;
   LRMOE_TRY(check_problem(pb, c));
   const int64_t M = c.M;
@@ -378,6 +414,7 @@ lrmoe_status lrmoe_grouped_backward(const lrmoe_problem* pb, const int32_t* perm
   t.total_groups = g;
 
   // Prologue: bf16 operand planes.
+  LRMOE_TRY(mark(timing, false, 0, s));
   char* ws = reinterpret_cast<char*>(workspace);
   auto plane = [&](size_t off) { return reinterpret_cast<uint16_t*>(ws + off); };
   GemmOperands ops;
@@ -423,10 +460,15 @@ lrmoe_status lrmoe_grouped_backward(const lrmoe_problem* pb, const int32_t* perm
     ops.dw_pa = ops.dw_pb = ops.dp_pa = ops.dp_pb = 2;
   }
   (void)w16;
+  LRMOE_TRY(mark(timing, true, 0, s));
   ops.partials = reinterpret_cast<float*>(ws + wl.partials);
+  LRMOE_TRY(mark(timing, false, 1, s));
   LRMOE_TRY(hip_status(launch_grouped_backward(t, ops, perm, alpha_c, dW, dphi, d_out, d_in,
                                                (int32_t)pb->P, s)));
+  LRMOE_TRY(mark(timing, true, 1, s));
+  LRMOE_TRY(mark(timing, false, 2, s));
   LRMOE_TRY(hip_status(launch_reduce_partials(t, ops.partials, dW, d_out, d_in, s)));
+  LRMOE_TRY(mark(timing, true, 2, s));
   return LRMOE_OK;
 }
 

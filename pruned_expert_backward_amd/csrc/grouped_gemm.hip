@@ -435,16 +435,22 @@ hipError_t launch(const Args& args, const GemmTable& tab, hipStream_t s) {
 }
 
 // ------------------------------------------------------------ split-K reduction
-// One workgroup per (split expert, tile): dW tile = sum over chunks (in chunk
-// order) of the partial tiles, cropped to the matrix edge.
-__global__ __launch_bounds__(256) void reduce_partials_kernel(GemmTable tab,
-                                                              const float* __restrict__ partials,
-                                                              float* __restrict__ dW, int32_t d_out,
-                                                              int32_t d_in) {
+// dW tile of a split expert = sum over its K chunks (in chunk order) of the
+// fp32 partial tiles, cropped to the matrix edge.  Each workgroup reduces a
+// 16 KiB slice of one tile; each thread keeps 4 independent 16-byte loads per
+// chunk in flight.
+constexpr int kRedThreads = 256;
+constexpr int kRedVec = 4;                                        // f32x4 per thread
+constexpr int kRedSlices = kTile * kTile / 4 / (kRedThreads * kRedVec);   // slices per tile
+
+__global__ __launch_bounds__(kRedThreads) void reduce_partials_kernel(
+    GemmTable tab, const float* __restrict__ partials, float* __restrict__ dW, int32_t d_out,
+    int32_t d_in) {
   const int tiles = tab.dw_tiles_m * tab.tiles_n;
-  int b = blockIdx.x;
+  int b = blockIdx.x / kRedSlices;
+  const int slice = blockIdx.x % kRedSlices;
   int e = 0, S = 1;
-  for (; e < tab.E; ++e) {   // find the b-th tile among split experts
+  for (; e < tab.E; ++e) {   // the b-th tile among split experts
     S = dw_chunks(tab.seg_off[e + 1] - tab.seg_off[e], tab.kc);
     if (S > 1) {
       if (b < tiles) break;
@@ -456,17 +462,30 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(GemmTable tab,
   const int m0 = (tile / tab.tiles_n) * BM, n0 = (tile % tab.tiles_n) * BN;
   const f32x4* src = reinterpret_cast<const f32x4*>(
       partials + ((partial_base(tab, e) + (int64_t)tile * S) << 16));
-  for (int v = threadIdx.x; v < BM * BN / 4; v += blockDim.x) {
+  const int v0 = slice * (kRedThreads * kRedVec) + threadIdx.x;
+  f32x4 acc[kRedVec];
+#pragma unroll
+  for (int i = 0; i < kRedVec; ++i) acc[i] = src[v0 + i * kRedThreads];
+  for (int c = 1; c < S; ++c) {
+    const f32x4* sc = src + (int64_t)c * (BM * BN / 4);
+    f32x4 x[kRedVec];
+#pragma unroll
+    for (int i = 0; i < kRedVec; ++i) x[i] = sc[v0 + i * kRedThreads];
+#pragma unroll
+    for (int i = 0; i < kRedVec; ++i) acc[i] += x[i];
+  }
+#pragma unroll
+  for (int i = 0; i < kRedVec; ++i) {
+    const int v = v0 + i * kRedThreads;
     const int row = v / (BN / 4), col = (v % (BN / 4)) * 4;
-    if (m0 + row >= d_out || n0 + col >= d_in) continue;
-    f32x4 acc = src[v];
-    for (int c = 1; c < S; ++c) acc += src[(int64_t)c * (BM * BN / 4) + v];
-    *reinterpret_cast<f32x4*>(dW + ((int64_t)e * d_out + m0 + row) * d_in + n0 + col) = acc;
+    if (m0 + row < d_out && n0 + col < d_in)
+      *reinterpret_cast<f32x4*>(dW + ((int64_t)e * d_out + m0 + row) * d_in + n0 + col) = acc[i];
   }
 }
 
 // ------------------------------------------------------------ operand prologue
-// hi/lo bf16 planes of alpha[row] * src[row][4c .. 4c+3].
+// hi/lo bf16 planes of alpha[row] * src[row][8c .. 8c+7] (cols % 8 == 0 for
+// bf16 sources; float32 sources also allow cols % 4 == 0 via a 4-wide tail).
 template <bool F32>
 __global__ __launch_bounds__(256) void split_kernel(const void* __restrict__ src, int64_t rows,
                                                     int32_t cols, const float* __restrict__ alpha,
@@ -474,28 +493,45 @@ __global__ __launch_bounds__(256) void split_kernel(const void* __restrict__ src
                                                     uint16_t* __restrict__ lo) {
   const int64_t quads = rows * (cols / 4);
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t qd = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; qd < quads; qd += stride) {
-    const int64_t row = qd / (cols / 4);
-    float x[4];
+  const int qpr = cols / 4;   // 4-element groups per row
+  for (int64_t oc = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; 2 * oc < quads;
+       oc += stride) {
+    // this thread: 4-element groups 2*oc and 2*oc+1 (the second may be on the next row
+    // for float32 sources with an odd number of groups per row)
+    float x[8];
+    int64_t qd0 = 2 * oc;
+    const bool two = qd0 + 1 < quads;
     if (F32) {
-      const f32x4 v = reinterpret_cast<const f32x4*>(src)[qd];
-      x[0] = v[0]; x[1] = v[1]; x[2] = v[2]; x[3] = v[3];
-    } else {
-      const u32x2 v = reinterpret_cast<const u32x2*>(src)[qd];
-      x[0] = __uint_as_float(v[0] << 16); x[1] = __uint_as_float(v[0] & 0xFFFF0000u);
-      x[2] = __uint_as_float(v[1] << 16); x[3] = __uint_as_float(v[1] & 0xFFFF0000u);
-    }
-    const float a = alpha ? alpha[row] : 1.f;
-    bf16x8 hl;   // hi in 0..3, lo in 4..7
+      const f32x4* s4 = reinterpret_cast<const f32x4*>(src);
+      const f32x4 a = s4[qd0];
+      const f32x4 b = two ? s4[qd0 + 1] : f32x4{0.f, 0.f, 0.f, 0.f};
+      x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
+      x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
+    } else {   // cols % 8 == 0: both groups are on one row, one 16-byte load
+      const u32x4 v = reinterpret_cast<const u32x4*>(src)[oc];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float y = a * x[i];
-      hl[i] = (__bf16)y;
-      hl[4 + i] = (__bf16)(y - (float)hl[i]);
+      for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(v[i] << 16);
+        x[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+      }
     }
-    const u32x4 w = __builtin_bit_cast(u32x4, hl);
-    reinterpret_cast<u32x2*>(hi)[qd] = u32x2{w[0], w[1]};
-    if (lo) reinterpret_cast<u32x2*>(lo)[qd] = u32x2{w[2], w[3]};
+    const float a0 = alpha ? alpha[qd0 / qpr] : 1.f;
+    const float a1 = alpha ? alpha[(qd0 + 1) / qpr] : 1.f;
+    bf16x8 h, l;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float y = (i < 4 ? a0 : a1) * x[i];
+      h[i] = (__bf16)y;
+      l[i] = (__bf16)(y - (float)h[i]);
+    }
+    const u32x4 hw = __builtin_bit_cast(u32x4, h), lw = __builtin_bit_cast(u32x4, l);
+    if (two) {
+      reinterpret_cast<u32x4*>(hi)[oc] = hw;
+      if (lo) reinterpret_cast<u32x4*>(lo)[oc] = lw;
+    } else {
+      reinterpret_cast<u32x2*>(hi)[qd0] = u32x2{hw[0], hw[1]};
+      if (lo) reinterpret_cast<u32x2*>(lo)[qd0] = u32x2{lw[0], lw[1]};
+    }
   }
 }
 
@@ -505,7 +541,7 @@ hipError_t launch_split(int src_dtype, const void* src, int64_t rows, int32_t co
                         const float* alpha, uint16_t* hi, uint16_t* lo, hipStream_t s) {
   const int64_t quads = rows * (cols / 4);
   if (quads <= 0) return hipSuccess;
-  int64_t blocks = (quads + 255) / 256;
+  int64_t blocks = (quads / 2 + 255) / 256 + 1;
   if (blocks > 256 * 16) blocks = 256 * 16;
   if (src_dtype == LRMOE_F32)
     hipLaunchKernelGGL(split_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, src, rows,
@@ -523,8 +559,8 @@ hipError_t launch_reduce_partials(const GemmTable& tab, const float* partials, f
     if (dw_chunks(tab.seg_off[e + 1] - tab.seg_off[e], tab.kc) > 1)
       blocks += (int64_t)tab.dw_tiles_m * tab.tiles_n;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)blocks), dim3(256), 0, s, tab,
-                     partials, dW, d_out, d_in);
+  hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)(blocks * kRedSlices)),
+                     dim3(kRedThreads), 0, s, tab, partials, dW, d_out, d_in);
   return hipGetLastError();
 }
 

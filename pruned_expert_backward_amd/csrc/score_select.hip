@@ -29,48 +29,37 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Sum of squares of one row held in 16-byte chunks; lane-strided.
-__device__ __forceinline__ float row_sumsq_bf16(const uint4* __restrict__ row, int nchunk, int lane) {
-  float a0 = 0.f, a1 = 0.f;
-  int c = lane;
-  for (; c + 64 < nchunk; c += 128) {
-    uint4 x = row[c];
-    uint4 y = row[c + 64];
-    float v;
-    v = bf16_lo(x.x); a0 = fmaf(v, v, a0); v = bf16_hi(x.x); a0 = fmaf(v, v, a0);
-    v = bf16_lo(x.y); a0 = fmaf(v, v, a0); v = bf16_hi(x.y); a0 = fmaf(v, v, a0);
-    v = bf16_lo(x.z); a0 = fmaf(v, v, a0); v = bf16_hi(x.z); a0 = fmaf(v, v, a0);
-    v = bf16_lo(x.w); a0 = fmaf(v, v, a0); v = bf16_hi(x.w); a0 = fmaf(v, v, a0);
-    v = bf16_lo(y.x); a1 = fmaf(v, v, a1); v = bf16_hi(y.x); a1 = fmaf(v, v, a1);
-    v = bf16_lo(y.y); a1 = fmaf(v, v, a1); v = bf16_hi(y.y); a1 = fmaf(v, v, a1);
-    v = bf16_lo(y.z); a1 = fmaf(v, v, a1); v = bf16_hi(y.z); a1 = fmaf(v, v, a1);
-    v = bf16_lo(y.w); a1 = fmaf(v, v, a1); v = bf16_hi(y.w); a1 = fmaf(v, v, a1);
-  }
-  if (c < nchunk) {
-    uint4 x = row[c];
-    float v;
-    v = bf16_lo(x.x); a0 = fmaf(v, v, a0); v = bf16_hi(x.x); a0 = fmaf(v, v, a0);
-    v = bf16_lo(x.y); a0 = fmaf(v, v, a0); v = bf16_hi(x.y); a0 = fmaf(v, v, a0);
-    v = bf16_lo(x.z); a0 = fmaf(v, v, a0); v = bf16_hi(x.z); a0 = fmaf(v, v, a0);
-    v = bf16_lo(x.w); a0 = fmaf(v, v, a0); v = bf16_hi(x.w); a0 = fmaf(v, v, a0);
-  }
-  return a0 + a1;
+__device__ __forceinline__ float sumsq8(uint4 x) {
+  float a = 0.f, v;
+  v = bf16_lo(x.x); a = fmaf(v, v, a); v = bf16_hi(x.x); a = fmaf(v, v, a);
+  v = bf16_lo(x.y); a = fmaf(v, v, a); v = bf16_hi(x.y); a = fmaf(v, v, a);
+  v = bf16_lo(x.z); a = fmaf(v, v, a); v = bf16_hi(x.z); a = fmaf(v, v, a);
+  v = bf16_lo(x.w); a = fmaf(v, v, a); v = bf16_hi(x.w); a = fmaf(v, v, a);
+  return a;
+}
+__device__ __forceinline__ float sumsq4(float4 x) {
+  return fmaf(x.w, x.w, fmaf(x.z, x.z, fmaf(x.y, x.y, x.x * x.x)));
 }
 
-__device__ __forceinline__ float row_sumsq_f32(const float4* __restrict__ row, int nchunk, int lane) {
-  float a0 = 0.f, a1 = 0.f;
+// Sum of squares of one row held in 16-byte chunks, lane-strided, four
+// independent loads in flight per lane.
+template <typename V>
+__device__ __forceinline__ float row_sumsq(const V* __restrict__ row, int nchunk, int lane) {
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
   int c = lane;
-  for (; c + 64 < nchunk; c += 128) {
-    float4 x = row[c];
-    float4 y = row[c + 64];
-    a0 = fmaf(x.x, x.x, a0); a0 = fmaf(x.y, x.y, a0); a0 = fmaf(x.z, x.z, a0); a0 = fmaf(x.w, x.w, a0);
-    a1 = fmaf(y.x, y.x, a1); a1 = fmaf(y.y, y.y, a1); a1 = fmaf(y.z, y.z, a1); a1 = fmaf(y.w, y.w, a1);
+  for (; c + 192 < nchunk; c += 256) {
+    const V x0 = row[c], x1 = row[c + 64], x2 = row[c + 128], x3 = row[c + 192];
+    if constexpr (sizeof(V) == 16 && __is_same(V, uint4)) {
+      a0 += sumsq8(x0); a1 += sumsq8(x1); a2 += sumsq8(x2); a3 += sumsq8(x3);
+    } else {
+      a0 += sumsq4(x0); a1 += sumsq4(x1); a2 += sumsq4(x2); a3 += sumsq4(x3);
+    }
   }
-  if (c < nchunk) {
-    float4 x = row[c];
-    a0 = fmaf(x.x, x.x, a0); a0 = fmaf(x.y, x.y, a0); a0 = fmaf(x.z, x.z, a0); a0 = fmaf(x.w, x.w, a0);
+  for (; c < nchunk; c += 64) {
+    const V x = row[c];
+    if constexpr (__is_same(V, uint4)) a0 += sumsq8(x); else a0 += sumsq4(x);
   }
-  return a0 + a1;
+  return (a0 + a1) + (a2 + a3);
 }
 
 template <bool BF16>
@@ -87,11 +76,11 @@ __global__ __launch_bounds__(256) void lrm_score_kernel(
     const int64_t r = row_index ? (int64_t)row_index[u] : (int64_t)u;
     float gs, ps;
     if (BF16) {
-      gs = row_sumsq_bf16(reinterpret_cast<const uint4*>(g) + r * gc, gc, lane);
-      ps = row_sumsq_bf16(reinterpret_cast<const uint4*>(phi) + (int64_t)u * pc, pc, lane);
+      gs = row_sumsq(reinterpret_cast<const uint4*>(g) + r * gc, gc, lane);
+      ps = row_sumsq(reinterpret_cast<const uint4*>(phi) + (int64_t)u * pc, pc, lane);
     } else {
-      gs = row_sumsq_f32(reinterpret_cast<const float4*>(g) + r * gc, gc, lane);
-      ps = row_sumsq_f32(reinterpret_cast<const float4*>(phi) + (int64_t)u * pc, pc, lane);
+      gs = row_sumsq(reinterpret_cast<const float4*>(g) + r * gc, gc, lane);
+      ps = row_sumsq(reinterpret_cast<const float4*>(phi) + (int64_t)u * pc, pc, lane);
     }
     gs = wave_sum(gs);
     ps = wave_sum(ps);
@@ -112,6 +101,7 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kSelLdsKeys = 24576;   // 96 KiB: experts up to this size select from LDS
 
 __global__ __launch_bounds__(kSelThreads) void select_scan_kernel(
     ExpertTable tab, const float* __restrict__ scores, uint8_t* __restrict__ keep,
@@ -119,6 +109,7 @@ __global__ __launch_bounds__(kSelThreads) void select_scan_kernel(
   __shared__ uint32_t hist[kSelWaves][256];
   __shared__ uint32_t sh_digit, sh_k;
   __shared__ uint32_t wcnt[2][kSelWaves];
+  __shared__ uint32_t keys_lds[kSelLdsKeys];   // the expert's keys, when they fit
 
   const int e = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -132,6 +123,14 @@ __global__ __launch_bounds__(kSelThreads) void select_scan_kernel(
     if (e == tab.E - 1) seg_offsets_out[tab.E] = tab.seg_off[tab.E];
   }
   if (n == 0) return;
+  const bool cached = n <= kSelLdsKeys;
+  if (cached) {
+    for (int i = tid; i < n; i += kSelThreads) keys_lds[i] = score_key(scores[base + i]);
+    __syncthreads();
+  }
+  auto key_at = [&](int i) -> uint32_t {
+    return cached ? keys_lds[i] : score_key(scores[base + i]);
+  };
 
   // ---- radix select: tau = q-th largest key, need = #(key == tau) to keep
   uint32_t tau = 0xFFFFFFFFu, need = 0;   // q == 0: nothing is above or equal
@@ -141,7 +140,7 @@ __global__ __launch_bounds__(kSelThreads) void select_scan_kernel(
       for (int i = tid; i < kSelWaves * 256; i += kSelThreads) (&hist[0][0])[i] = 0;
       __syncthreads();
       for (int i = tid; i < n; i += kSelThreads) {
-        const uint32_t key = score_key(scores[base + i]);
+        const uint32_t key = key_at(i);
         if ((key & mask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1u);
       }
       __syncthreads();
@@ -190,7 +189,7 @@ __global__ __launch_bounds__(kSelThreads) void select_scan_kernel(
   for (int c0 = 0; c0 < n; c0 += kSelThreads) {
     const int i = c0 + tid;
     const bool valid = i < n;
-    const uint32_t key = valid ? score_key(scores[base + i]) : 0u;
+    const uint32_t key = valid ? key_at(i) : 0u;
     const bool gt = valid && key > tau;
     const bool eq = valid && key == tau;
     const uint64_t beq = __ballot(eq);
@@ -232,7 +231,7 @@ hipError_t launch_score(int dtype, const void* g, const void* phi, const float* 
   if (P <= 0) return hipSuccess;
   const int waves_per_block = 4;
   int blocks = (P + waves_per_block - 1) / waves_per_block;
-  if (blocks > 256 * 32) blocks = 256 * 32;   // grid-stride beyond 32 blocks per CU
+  if (blocks > 256 * 8) blocks = 256 * 8;   // 32 waves per CU, each looping over pairs
   if (dtype == LRMOE_BF16)
     hipLaunchKernelGGL(lrm_score_kernel<true>, dim3(blocks), dim3(256), 0, s, g, phi, alpha,
                        row_index, P, d_out, d_in, scores);

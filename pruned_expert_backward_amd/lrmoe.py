@@ -28,7 +28,9 @@ STATUS = {0: "LRMOE_OK", 1: "LRMOE_ERR_NULL", 2: "LRMOE_ERR_INVALID", 3: "LRMOE_
 
 EXPORTS = ["lrmoe_abi_version", "lrmoe_status_string", "lrmoe_plan_quota",
            "lrmoe_workspace_size", "lrmoe_score_select_compact", "lrmoe_select_compact",
-           "lrmoe_gather_compact", "lrmoe_grouped_backward"]
+           "lrmoe_gather_compact", "lrmoe_grouped_backward", "lrmoe_score_select_compact_timed",
+           "lrmoe_grouped_backward_timed"]
+TIMING_SLOTS = 4
 
 
 class LrmoeError(RuntimeError):
@@ -42,6 +44,10 @@ class Problem(C.Structure):
                 ("d_out", C.c_int32), ("d_in", C.c_int32),
                 ("counts", C.POINTER(C.c_int64)), ("quotas", C.POINTER(C.c_int64)),
                 ("dw_mode", C.c_int32), ("reserved", C.c_int32)]
+
+
+class Timing(C.Structure):
+    _fields_ = [("before", C.c_void_p * TIMING_SLOTS), ("after", C.c_void_p * TIMING_SLOTS)]
 
 
 class QuotaPolicy(C.Structure):
@@ -78,6 +84,12 @@ def lib() -> C.CDLL:
     L.lrmoe_gather_compact.argtypes = [C.POINTER(Problem)] + [_P] * 12
     L.lrmoe_grouped_backward.restype = C.c_int
     L.lrmoe_grouped_backward.argtypes = [C.POINTER(Problem)] + [_P] * 8 + [C.c_size_t, _P]
+    L.lrmoe_score_select_compact_timed.restype = C.c_int
+    L.lrmoe_score_select_compact_timed.argtypes = ([C.POINTER(Problem)] + [_P] * 13 +
+                                                   [C.c_size_t, _P, C.POINTER(Timing)])
+    L.lrmoe_grouped_backward_timed.restype = C.c_int
+    L.lrmoe_grouped_backward_timed.argtypes = ([C.POINTER(Problem)] + [_P] * 8 +
+                                               [C.c_size_t, _P, C.POINTER(Timing)])
     if L.lrmoe_abi_version() != ABI_VERSION:
         raise RuntimeError("liblrmoe ABI version mismatch; rebuild the library")
     _lib_handle = L
@@ -187,9 +199,10 @@ def workspace(plan: Plan, device) -> torch.Tensor:
 
 
 def score_select_compact(plan: Plan, alpha, g, phi, g_row_index=None, out=None, ws=None,
-                         scores=None) -> dict:
+                         scores=None, timing: Optional["KernelTimer"] = None) -> dict:
     """LRM score -> per-expert top-quota select -> compaction.  With
-    `scores` given, the LRM scoring is skipped and those scores are used."""
+    `scores` given, the LRM scoring is skipped and those scores are used.
+    `timing` (a KernelTimer) records events around each kernel."""
     dev = phi.device
     if out is None:
         out = alloc_select_outputs(plan, dev)
@@ -200,7 +213,11 @@ def score_select_compact(plan: Plan, alpha, g, phi, g_row_index=None, out=None, 
     tail = (_ptr(out["keep"]), _ptr(out["seg_offsets"]), _ptr(out["perm"]), _ptr(out["g_c"]),
             _ptr(out["phi_c"]), _ptr(out["alpha_c"]), _ptr(out.get("dphi")), _ptr(ws),
             ws.numel(), _stream())
-    if scores is None:
+    if scores is None and timing is not None:
+        st = L.lrmoe_score_select_compact_timed(C.byref(plan.struct), *common, _ptr(out["scores"]),
+                                                *tail, C.byref(timing.next_slots()))
+        check("lrmoe_score_select_compact_timed", st)
+    elif scores is None:
         st = L.lrmoe_score_select_compact(C.byref(plan.struct), *common, _ptr(out["scores"]), *tail)
         check("lrmoe_score_select_compact", st)
     else:
@@ -228,18 +245,72 @@ def gather_compact(plan: Plan, perm, keep, alpha, g, phi, g_row_index=None, phi_
 
 
 def grouped_backward(plan: Plan, perm, alpha_c, g_c, phi_c, W, dW=None, dphi=None,
-                     ws=None) -> torch.Tensor:
+                     ws=None, timing: Optional["KernelTimer"] = None) -> torch.Tensor:
     """dW [E, d_out, d_in] (returned) and the kept rows of dphi (in place)."""
     dev = W.device
     if dW is None:
         dW = _empty((plan.E, plan.d_out, plan.d_in), torch.float32, dev)
     if ws is None:
         ws = workspace(plan, dev)
-    st = lib().lrmoe_grouped_backward(C.byref(plan.struct), _ptr(perm), _ptr(alpha_c), _ptr(g_c),
-                                      _ptr(phi_c), _ptr(W), _ptr(dW), _ptr(dphi), _ptr(ws),
-                                      ws.numel(), _stream())
-    check("lrmoe_grouped_backward", st)
+    args = (C.byref(plan.struct), _ptr(perm), _ptr(alpha_c), _ptr(g_c), _ptr(phi_c), _ptr(W),
+            _ptr(dW), _ptr(dphi), _ptr(ws), ws.numel(), _stream())
+    if timing is not None:
+        check("lrmoe_grouped_backward_timed",
+              lib().lrmoe_grouped_backward_timed(*args, C.byref(timing.next_slots())))
+    else:
+        check("lrmoe_grouped_backward", lib().lrmoe_grouped_backward(*args))
     return dW
+
+
+class KernelTimer:
+    """HIP events recorded by the library around each kernel of a call.
+
+    Create one per (call site, number of calls); each call takes the next
+    set of slots.  After synchronising, mean_us(slot) is the mean duration of
+    that kernel over the calls that launched it."""
+
+    def __init__(self, calls: int):
+        self._hip = C.CDLL("libamdhip64.so")
+        self._hip.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self._hip.hipEventQuery.argtypes = [C.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [C.c_void_p]
+        self.timings = []
+        for _ in range(calls):
+            t = Timing()
+            for k in range(TIMING_SLOTS):
+                for arr in (t.before, t.after):
+                    ev = C.c_void_p()
+                    if self._hip.hipEventCreate(C.byref(ev)) != 0:
+                        raise RuntimeError("hipEventCreate failed")
+                    arr[k] = ev
+            self.timings.append(t)
+        self._next = 0
+
+    def next_slots(self) -> Timing:
+        t = self.timings[self._next]
+        self._next += 1
+        return t
+
+    def durations_us(self, slot: int) -> list:
+        out = []
+        for t in self.timings[:self._next]:
+            ms = C.c_float()
+            # hipEventElapsedTime fails for events that were never recorded
+            if self._hip.hipEventElapsedTime(C.byref(ms), t.before[slot], t.after[slot]) == 0:
+                out.append(ms.value * 1e3)
+        return out
+
+    def mean_us(self, slot: int) -> Optional[float]:
+        d = self.durations_us(slot)
+        return sum(d) / len(d) if d else None
+
+    def close(self):
+        for t in self.timings:
+            for k in range(TIMING_SLOTS):
+                self._hip.hipEventDestroy(t.before[k])
+                self._hip.hipEventDestroy(t.after[k])
+        self.timings = []
 
 
 def pruned_backward(plan: Plan, alpha, g, phi, W, g_row_index=None, out=None, ws=None) -> dict:
