@@ -85,6 +85,7 @@ struct GemmWorkspace {
   int dw_pa = 1, dw_pb = 1, dp_pa = 1, dp_pb = 1;
   int32_t kc = 0;          // dW K-chunk length
   int64_t part_tiles = 0;  // partial tiles of split experts
+  size_t heads = 0;        // queue counters
 };
 
 constexpr int kStepK = 32;   // K rows per pipeline step of the GEMM kernel
@@ -139,7 +140,8 @@ GemmWorkspace gemm_workspace(const lrmoe_problem* pb, int64_t M) {
     if (S > 1) w.part_tiles += tiles_m * tiles_n * S;
   }
   w.partials = round256(w.total);
-  w.total = w.partials + (size_t)w.part_tiles * kTile * kTile * 4;
+  w.heads = w.partials + (size_t)w.part_tiles * kTile * kTile * 4;
+  w.total = w.heads + 256;   // per-XCD queue counters of the grouped GEMM
   return w;
 }
 
@@ -385,33 +387,75 @@ lrmoe_status lrmoe_grouped_backward_timed(const lrmoe_problem* pb, const int32_t
   group_shape(t.tiles_n, 6, t.dp_gm, t.dp_gn);
   for (int e = 0; e <= E; ++e) t.seg_off[e] = c.tab.seg_off[e];
 
-  // Weight-gradient groups: every expert (zeros for q_e = 0), heaviest first,
-  // K chunks of one expert consecutive.
+  // Groups.  Weight gradient: every expert (zeros for q_e = 0) and K chunk;
+  // input gradient: the experts' row tiles.  Work of a group ~ tiles x K steps
+  // x MFMA passes.
   std::vector<int> order(E);
   std::iota(order.begin(), order.end(), 0);
   std::stable_sort(order.begin(), order.end(),
                    [&](int a, int b) { return pb->quotas[a] > pb->quotas[b]; });
   const int ngn_dw = (t.tiles_n + t.dw_gn - 1) / t.dw_gn;
   const int per_chunk = ((t.dw_tiles_m + t.dw_gm - 1) / t.dw_gm) * ngn_dw;
+  const int ngn_dp = (t.tiles_n + t.dp_gn - 1) / t.dp_gn;
+  const int terms_dw = 1 + (wl.dw_pa == 2) + (wl.dw_pb == 2);
+  const int terms_dp = 1 + (wl.dp_pa == 2) + (wl.dp_pb == 2);
+  struct G { int64_t work; uint32_t desc; };
+  std::vector<G> groups;
   int32_t g = 0;
   for (int r = 0; r < E; ++r) {
-    t.order[r] = (uint8_t)order[r];
-    t.dw_goff[r] = g;
-    g += per_chunk * dw_chunks((int)pb->quotas[order[r]], t.kc);
-  }
-  t.dw_goff[E] = g;
-  t.dw_groups = g;
-  // Input-gradient groups, expert by expert.
-  const int ngn_dp = (t.tiles_n + t.dp_gn - 1) / t.dp_gn;
-  for (int e = 0; e < E; ++e) {
-    t.dp_goff[e] = g;
-    if (dphi != nullptr) {
-      const int64_t mt = (pb->quotas[e] + kTile - 1) / kTile;
-      g += (int32_t)(((mt + t.dp_gm - 1) / t.dp_gm) * ngn_dp);
+    const int e = order[r];
+    const int q = (int)pb->quotas[e];
+    const int S = dw_chunks(q, t.kc);
+    t.f.dw_goff[r] = g;
+    t.f.order[r] = (uint8_t)e;
+    g += per_chunk * S;
+    for (int ch = 0; ch < S; ++ch) {
+      const int klen = S > 1 ? std::min(t.kc, q - ch * t.kc) : q;
+      for (int sg = 0; sg < per_chunk; ++sg)
+        groups.push_back({(int64_t)((klen + kStepK - 1) / kStepK + 1) * terms_dw * kGroupSlots,
+                          group_desc(true, e, ch, sg)});
     }
   }
-  t.dp_goff[E] = g;
+  t.f.dw_goff[E] = g;
+  t.dw_groups = g;
+  for (int e = 0; e < E; ++e) {
+    t.f.dp_goff[e] = g;
+    if (dphi == nullptr) continue;
+    const int64_t mt = (pb->quotas[e] + kTile - 1) / kTile;
+    const int n = (int)(((mt + t.dp_gm - 1) / t.dp_gm) * ngn_dp);
+    g += n;
+    for (int sg = 0; sg < n; ++sg)
+      groups.push_back({(int64_t)((d_out + kStepK - 1) / kStepK + 1) * terms_dp * kGroupSlots,
+                        group_desc(false, e, 0, sg)});
+  }
+  t.f.dp_goff[E] = g;
   t.total_groups = g;
+  bool table_ok = (int)groups.size() <= kMaxGroups && E <= 256;
+  for (int e = 0; e < E && table_ok; ++e) table_ok = dw_chunks((int)pb->quotas[e], t.kc) <= 256;
+  if (table_ok) {
+    // Longest first, each to the XCD with the least work so far; queues keep
+    // that order.  (The formula-order tables above are overwritten: union.)
+    std::vector<int> idx(groups.size());
+    std::iota(idx.begin(), idx.end(), 0);
+    std::stable_sort(idx.begin(), idx.end(),
+                     [&](int a, int b) { return groups[a].work > groups[b].work; });
+    std::vector<std::vector<uint32_t>> qs(kXcds);
+    int64_t load[kXcds] = {0};
+    for (int i : idx) {
+      int best = 0;
+      for (int x = 1; x < kXcds; ++x)
+        if (load[x] < load[best]) best = x;
+      load[best] += groups[i].work;
+      qs[best].push_back(groups[i].desc);
+    }
+    t.use_table = 1;
+    int32_t o = 0;
+    for (int x = 0; x < kXcds; ++x) {
+      t.qoff[x] = o;
+      for (uint32_t d : qs[x]) t.groups[o++] = d;
+    }
+    t.qoff[kXcds] = o;
+  }
 
   // Prologue: bf16 operand planes.
   LRMOE_TRY(mark(timing, false, 0, s));
@@ -462,6 +506,8 @@ lrmoe_status lrmoe_grouped_backward_timed(const lrmoe_problem* pb, const int32_t
   (void)w16;
   LRMOE_TRY(mark(timing, true, 0, s));
   ops.partials = reinterpret_cast<float*>(ws + wl.partials);
+  ops.queue_heads = reinterpret_cast<int32_t*>(ws + wl.heads);
+  LRMOE_TRY(hip_status(launch_zero(ops.queue_heads, kXcds, s)));
   LRMOE_TRY(mark(timing, false, 1, s));
   LRMOE_TRY(hip_status(launch_grouped_backward(t, ops, perm, alpha_c, dW, dphi, d_out, d_in,
                                                (int32_t)pb->P, s)));

@@ -118,33 +118,50 @@ struct TileJob {
   int chunk, chunks;   // dW K chunk of this tile and the expert's chunk count
 };
 
-// Decode the workgroup's tile from the group schedule; false = idle slot.
-__device__ __forceinline__ bool decode(const GemmTable& tab, bool& is_dw, TileJob& job) {
-  const int b = blockIdx.x;
-  const int x = b % kXcds, i = b / kXcds;
-  const int g = (i / kGroupSlots) * kXcds + x;   // group of this XCD's queue
-  const int t = i % kGroupSlots;                 // slot inside the group
-  if (g >= tab.total_groups) return false;
-  is_dw = g < tab.dw_groups;
-  const int32_t* goff = is_dw ? tab.dw_goff : tab.dp_goff;
-  int lo = 0, hi = tab.E - 1;   // last rank r with goff[r] <= g
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (goff[mid] <= g) lo = mid; else hi = mid - 1;
+// Queue length of XCD x in item slots.
+__device__ __forceinline__ int queue_items(const GemmTable& tab, int x) {
+  if (tab.use_table) return (tab.qoff[x + 1] - tab.qoff[x]) * kGroupSlots;
+  const int ng = tab.total_groups > x ? (tab.total_groups - 1 - x) / kXcds + 1 : 0;
+  return ng * kGroupSlots;
+}
+
+// Item `i` of XCD x's queue -> tile; false for an idle slot.
+__device__ __forceinline__ bool decode(const GemmTable& tab, int x, int i, bool& is_dw,
+                                      TileJob& job) {
+  const int p = i / kGroupSlots, t = i % kGroupSlots;
+  int e, chunk, lg;
+  if (tab.use_table) {
+    const uint32_t d = tab.groups[tab.qoff[x] + p];
+    is_dw = (d >> 31) != 0;
+    e = (int)((d >> 23) & 0xFF);
+    chunk = (int)((d >> 15) & 0xFF);
+    lg = (int)(d & 0x7FFF);
+  } else {
+    const int g = p * kXcds + x;   // global group order: dW (LPT) then dphi
+    is_dw = g < tab.dw_groups;
+    const int32_t* goff = is_dw ? tab.f.dw_goff : tab.f.dp_goff;
+    int lo = 0, hi = tab.E - 1;   // last rank r with goff[r] <= g
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (goff[mid] <= g) lo = mid; else hi = mid - 1;
+    }
+    e = is_dw ? (int)tab.f.order[lo] : lo;
+    lg = g - goff[lo];
+    chunk = 0;
   }
-  const int e = is_dw ? (int)tab.order[lo] : lo;
-  int lg = g - goff[lo];
   const int gm = is_dw ? tab.dw_gm : tab.dp_gm;
   const int gn = is_dw ? tab.dw_gn : tab.dp_gn;
   if (t >= gm * gn) return false;
   const int ngn = (tab.tiles_n + gn - 1) / gn;
   const int q = tab.seg_off[e + 1] - tab.seg_off[e];
-  int chunk = 0, chunks = 1;
-  if (is_dw) {   // groups of one expert: chunk-major
+  int chunks = 1;
+  if (is_dw) {
     chunks = dw_chunks(q, tab.kc);
-    const int per_chunk = ((tab.dw_tiles_m + gm - 1) / gm) * ngn;
-    chunk = lg / per_chunk;
-    lg -= chunk * per_chunk;
+    if (!tab.use_table) {   // formula order: the expert's groups are chunk-major
+      const int per_chunk = ((tab.dw_tiles_m + gm - 1) / gm) * ngn;
+      chunk = lg / per_chunk;
+      lg -= chunk * per_chunk;
+    }
   }
   const int tm = (lg / ngn) * gm + t / gn;
   const int tn = (lg % ngn) * gn + t % gn;
@@ -200,6 +217,12 @@ __device__ __forceinline__ uint32_t lds_addr(LDS_AS const char* p) {
   return (uint32_t)(uintptr_t)p;
 }
 
+// Workgroup barrier that waits for this wave's LDS accesses only (not for
+// global loads or stores still in flight).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Wait until at most N of this wave's loads are outstanding, then cross the
 // workgroup barrier.  One asm block, so that the compiler adds no wait of its
 // own for the loads still in flight into other LDS stages.
@@ -208,69 +231,81 @@ __device__ __forceinline__ void wait_loads_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// One 256x256 output tile.  IS_DW: A (MC, rows = K) and B (MC, rows = K) are
-// [M, d_out] / [M, d_in] segment rows.  Else A (KC, rows = M) = g_c segment
-// rows and B (MC) = W_e.  PA/PB: bf16 planes of each operand; NS: LDS stages.
-template <bool IS_DW, int PA, int PB, int NS>
-__device__ __forceinline__ void gemm_tile(const Args& args, const GemmTable& tab,
-                                          const TileJob& job, LDS_AS char* smem) {
-  constexpr bool A_MC = IS_DW;
-  constexpr int kStage = (PA + PB) * kPlaneBytes;
-  constexpr int kDist = NS - 1;                 // prefetch distance in K steps
-  constexpr int kBlocks = kPlaneBytes / 1024;   // 1 KiB LDS blocks per plane
-  constexpr int kPerWave = kBlocks / kWaves;    // ... filled by each wave
-  constexpr int kLoads = (PA + PB) * kPerWave;  // load instructions per stage per wave
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;   // wave tile rows wm*128, cols wn*64
-  const int d_out = args.d_out, d_in = args.d_in;
-  // Tile coordinates are workgroup-uniform; say so, so that buffer
-  // descriptors and LDS bases stay in scalar registers.
-  const int e = __builtin_amdgcn_readfirstlane(job.e);
-  const int m0 = __builtin_amdgcn_readfirstlane(job.m0);
-  const int n0 = __builtin_amdgcn_readfirstlane(job.n0);
-  const int chunk = __builtin_amdgcn_readfirstlane(job.chunk);
-  const int q = tab.seg_off[e + 1] - tab.seg_off[e];
-  // dW: this chunk's rows of the segment; dphi: the whole segment (M) and d_out (K)
-  const int kbeg = IS_DW ? chunk * tab.kc : 0;
-  const int seg = tab.seg_off[e] + kbeg;
-  const int K = IS_DW ? (q - kbeg < tab.kc ? q - kbeg : tab.kc) : d_out;
-  const int mrows = IS_DW ? d_out : q;       // valid rows of the output along M
+constexpr int kPermBytes = BM * 8;   // dphi epilogue: destination row + alpha per tile row
 
+// Everything one tile needs, derived from its job.  IS_DW: A (MC, rows = K)
+// and B (MC, rows = K) are [M, d_out] / [M, d_in] segment rows.  Else A (KC,
+// rows = M) = g_c segment rows and B (MC) = W_e.  PA/PB: bf16 planes of each
+// operand; NS: LDS stages.
+template <bool IS_DW, int PA, int PB, int NS>
+struct Tile {
+  static constexpr bool A_MC = IS_DW;
+  static constexpr int kStage = (PA + PB) * kPlaneBytes;
+  static constexpr int kDist = NS - 1;                 // prefetch distance in K steps
+  static constexpr int kBlocks = kPlaneBytes / 1024;   // 1 KiB LDS blocks per plane
+  static constexpr int kPerWave = kBlocks / kWaves;    // ... filled by each wave
+  static constexpr int kLoads = (PA + PB) * kPerWave;  // load instructions per stage per wave
+
+  int e, m0, n0, chunk, chunks, q, seg, K, mrows, nk;
+  int lane, wave, wm, wn;
   const uint16_t* A[2];
   const uint16_t* B[2];
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    A[p] = IS_DW ? args.ops.dw_a[p] : args.ops.dp_a[p];
-    B[p] = IS_DW ? args.ops.dw_b[p] : args.ops.dp_b[p];
-  }
-  // Byte offsets (within one K step) of the global chunk each lane fetches
-  // for each of its LDS blocks: block b = wave*kPerWave + j.
   uint32_t aoff[kPerWave], boff[kPerWave];
-  int acol[kPerWave];   // KC only: K column of the chunk within the step
+  int acol[kPerWave];
+
+  __device__ __forceinline__ Tile(const Args& args, const GemmTable& tab, const TileJob& job) {
+    const int tid = threadIdx.x;
+    lane = tid & 63;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    wm = wave >> 2;   // wave tile rows wm*128, cols wn*64
+    wn = wave & 3;
+    // Tile coordinates are workgroup-uniform; say so, so that buffer
+    // descriptors and LDS bases stay in scalar registers.
+    e = __builtin_amdgcn_readfirstlane(job.e);
+    m0 = __builtin_amdgcn_readfirstlane(job.m0);
+    n0 = __builtin_amdgcn_readfirstlane(job.n0);
+    chunk = __builtin_amdgcn_readfirstlane(job.chunk);
+    chunks = __builtin_amdgcn_readfirstlane(job.chunks);
+    const int d_out = args.d_out, d_in = args.d_in;
+    q = tab.seg_off[e + 1] - tab.seg_off[e];
+    // dW: this chunk's rows of the segment; dphi: the whole segment (M) and d_out (K)
+    const int kbeg = IS_DW ? chunk * tab.kc : 0;
+    seg = tab.seg_off[e] + kbeg;
+    K = IS_DW ? (q - kbeg < tab.kc ? q - kbeg : tab.kc) : d_out;
+    mrows = IS_DW ? d_out : q;
+    nk = (K + BK - 1) / BK;
 #pragma unroll
-  for (int j = 0; j < kPerWave; ++j) {
-    const int blk = wave * kPerWave + j;
-    {   // MC block: rows 2*blk, 2*blk+1 of the step, 32 chunks each
-      const int k = 2 * blk + (lane >> 5), pc = lane & 31;
-      const int lc = pc ^ ((k & 3) << 2);
-      const int col = n0 + 8 * lc;
-      boff[j] = col < d_in ? (uint32_t)(k * d_in + col) * 2u : kOutOfRange;
-      if (A_MC) {
-        const int acolm = m0 + 8 * lc;
-        aoff[j] = acolm < d_out ? (uint32_t)(k * d_out + acolm) * 2u : kOutOfRange;
-      }
+    for (int p = 0; p < 2; ++p) {
+      A[p] = IS_DW ? args.ops.dw_a[p] : args.ops.dp_a[p];
+      B[p] = IS_DW ? args.ops.dw_b[p] : args.ops.dp_b[p];
     }
-    if (!A_MC) {   // KC block: rows 16*blk .. +15 of the tile, 4 chunks each
-      const int r = 16 * blk + (lane >> 2), pc = lane & 3;
-      const int lc = pc ^ (((r >> 1) ^ (r >> 3)) & 3);
-      acol[j] = 8 * lc;
-      aoff[j] = (uint32_t)(r * d_out + 8 * lc) * 2u;
+    // Byte offsets (within one K step) of the global chunk each lane fetches
+    // for each of its LDS blocks: block b = wave*kPerWave + j.
+#pragma unroll
+    for (int j = 0; j < kPerWave; ++j) {
+      const int blk = wave * kPerWave + j;
+      {   // MC block: rows 2*blk, 2*blk+1 of the step, 32 chunks each
+        const int k = 2 * blk + (lane >> 5), pc = lane & 31;
+        const int lc = pc ^ ((k & 3) << 2);
+        const int col = n0 + 8 * lc;
+        boff[j] = col < d_in ? (uint32_t)(k * d_in + col) * 2u : kOutOfRange;
+        if (A_MC) {
+          const int acolm = m0 + 8 * lc;
+          aoff[j] = acolm < d_out ? (uint32_t)(k * d_out + acolm) * 2u : kOutOfRange;
+        }
+      }
+      if (!A_MC) {   // KC block: rows 16*blk .. +15 of the tile, 4 chunks each
+        const int r = 16 * blk + (lane >> 2), pc = lane & 3;
+        const int lc = pc ^ (((r >> 1) ^ (r >> 3)) & 3);
+        acol[j] = 8 * lc;
+        aoff[j] = (uint32_t)(r * d_out + 8 * lc) * 2u;
+      }
     }
   }
 
   // ---- global -> LDS stage for the K step starting at k0
-  auto issue = [&](int k0, LDS_AS char* stage) {
+  __device__ __forceinline__ void issue(const Args& args, int k0, LDS_AS char* stage) const {
+    const int d_out = args.d_out, d_in = args.d_in;
     const int krows = K - k0 < BK ? K - k0 : BK;
 #pragma unroll
     for (int p = 0; p < PA; ++p) {
@@ -294,20 +329,19 @@ __device__ __forceinline__ void gemm_tile(const Args& args, const GemmTable& tab
         load_lds16(r, lds_addr(stage + (PA + p) * kPlaneBytes + (wave * kPerWave + j) * 1024),
                    boff[j]);
     }
-  };
+  }
 
-  f32x16 acc[4][2];
+  // First kDist stages (fewer if K is short).
+  __device__ __forceinline__ void prologue(const Args& args, LDS_AS char* smem) const {
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+    for (int d = 0; d < kDist; ++d)
+      if (d < nk) issue(args, d * BK, smem + d * kStage);
+  }
 
   // ---- MFMAs of one K step: hi*hi (+ hi*lo_B) (+ lo_A*hi).  All fragments
   // of the step are read first, so the second half's LDS reads overlap the
   // first half's MFMAs.
-  auto compute = [&](LDS_AS const char* stage) {
+  __device__ __forceinline__ void compute(LDS_AS const char* stage, f32x16 (&acc)[4][2]) const {
     i16x8 fb[2][PB][2], fa[2][PA][4];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -332,105 +366,166 @@ __device__ __forceinline__ void gemm_tile(const Args& args, const GemmTable& tab
           if (PB == 2) acc[a][b] = mfma(fa[h][0][a], fb[h][PB - 1][b], acc[a][b]);
           if (PA == 2) acc[a][b] = mfma(fa[h][PA - 1][a], fb[h][0][b], acc[a][b]);
         }
-  };
-
-  // ---- pipeline: stage kt lives in LDS buffer kt % NS; the loads of step
-  // kt + kDist go into the buffer that step kt - 1 used, after the barrier
-  // that follows everyone's MFMAs of step kt - 1.
-  const int nk = (K + BK - 1) / BK;
-#pragma unroll
-  for (int d = 0; d < kDist; ++d) issue(d * BK, smem + d * kStage);
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_loads_barrier<(kDist - 1) * kLoads>();
-    issue((kt + kDist) * BK, smem + ((kt + kDist) % NS) * kStage);
-    compute(smem + (kt % NS) * kStage);
   }
-  // Loads past the end of K wrote zeros into LDS: drain them before the
-  // epilogue reuses the stages.
-  wait_loads_barrier<0>();
 
-  // ---- epilogue: D[i][j] sits in lane j + 32*((i/4)%2), register (i%4) + 4*(i/8)
-  const int fl = lane & 31;
-  LDS_AS int32_t* s_perm = reinterpret_cast<LDS_AS int32_t*>(smem);
-  LDS_AS float* s_alpha = reinterpret_cast<LDS_AS float*>(smem + BM * 4);
-  if (!IS_DW) {   // destination row and alpha of the tile's rows, via LDS
+  // ---- K loop: stage kt lives in LDS buffer kt % NS; the loads of step
+  // kt + kDist go into the buffer that step kt - 1 used, after the barrier
+  // that follows everyone's MFMAs of step kt - 1.  The prologue's loads must
+  // have been issued.  Ends with every load of the tile consumed.
+  __device__ __forceinline__ void mainloop(const Args& args, LDS_AS char* smem,
+                                           f32x16 (&acc)[4][2]) const {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+    for (int kt = 0; kt < nk; ++kt) {
+      // loads of steps kt .. min(nk, kt + kDist) - 1 are in flight; keep the later ones
+      if (kDist == 2 && kt + 1 < nk) wait_loads_barrier<kLoads>();
+      else wait_loads_barrier<0>();
+      if (kt + kDist < nk) issue(args, (kt + kDist) * BK, smem + ((kt + kDist) % NS) * kStage);
+      compute(smem + (kt % NS) * kStage, acc);
+    }
+  }
+
+  // dphi: destination row and alpha of the tile's rows into LDS (before the
+  // next tile's loads are issued, so that this wait covers only them).
+  __device__ __forceinline__ void stage_rows(const Args& args, LDS_AS char* prm) const {
+    if (IS_DW) return;
+    const int tid = threadIdx.x;
+    LDS_AS int32_t* s_perm = reinterpret_cast<LDS_AS int32_t*>(prm);
+    LDS_AS float* s_alpha = reinterpret_cast<LDS_AS float*>(prm + BM * 4);
     if (tid < BM) {
       const bool ok = m0 + tid < q;
       const int32_t u = ok ? args.perm[seg + m0 + tid] : -1;
       s_perm[tid] = (uint32_t)u < (uint32_t)args.P ? u : -1;   // perm holds pair indices < P
       s_alpha[tid] = ok ? args.alpha_c[seg + m0 + tid] : 0.f;
     }
-    __syncthreads();
   }
-  // Split dW tiles go to their chunk's partial tile (full 256x256, row-major).
-  float* part = nullptr;
-  if (IS_DW && job.chunks > 1) {
-    const int tile = (m0 / BM) * tab.tiles_n + n0 / BN;
-    part = args.ops.partials +
-           ((partial_base(tab, e) + (int64_t)tile * job.chunks + chunk) << 16);
-  }
+
+  // ---- epilogue: D[i][j] sits in lane j + 32*((i/4)%2), register (i%4) + 4*(i/8)
+  __device__ __forceinline__ void epilogue(const Args& args, const GemmTable& tab,
+                                           LDS_AS const char* prm,
+                                           const f32x16 (&acc)[4][2]) const {
+    const int d_out = args.d_out, d_in = args.d_in;
+    const int fl = lane & 31;
+    LDS_AS const int32_t* s_perm = reinterpret_cast<LDS_AS const int32_t*>(prm);
+    LDS_AS const float* s_alpha = reinterpret_cast<LDS_AS const float*>(prm + BM * 4);
+    // Split dW tiles go to their chunk's partial tile (full 256x256, row-major).
+    float* part = nullptr;
+    if (IS_DW && chunks > 1) {
+      const int tile = (m0 / BM) * tab.tiles_n + n0 / BN;
+      part = args.ops.partials + ((partial_base(tab, e) + (int64_t)tile * chunks + chunk) << 16);
+    }
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
+    for (int a = 0; a < 4; ++a) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      const int lrow = wm * 128 + a * 32 + i;
-      const int mrow = m0 + lrow;
-      if (IS_DW) {
-        if (part != nullptr) {
+      for (int r = 0; r < 16; ++r) {
+        const int i = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int lrow = wm * 128 + a * 32 + i;
+        const int mrow = m0 + lrow;
+        if (IS_DW) {
+          if (part != nullptr) {
 #pragma unroll
-          for (int b = 0; b < 2; ++b) part[lrow * BN + wn * 64 + b * 32 + fl] = acc[a][b][r];
-        } else if (mrow < mrows) {
-          float* orow = args.dW + ((int64_t)e * d_out + mrow) * d_in;
+            for (int b = 0; b < 2; ++b) part[lrow * BN + wn * 64 + b * 32 + fl] = acc[a][b][r];
+          } else if (mrow < mrows) {
+            float* orow = args.dW + ((int64_t)e * d_out + mrow) * d_in;
 #pragma unroll
-          for (int b = 0; b < 2; ++b) {
-            const int col = n0 + wn * 64 + b * 32 + fl;
-            if (col < d_in) orow[col] = acc[a][b][r];
+            for (int b = 0; b < 2; ++b) {
+              const int col = n0 + wn * 64 + b * 32 + fl;
+              if (col < d_in) orow[col] = acc[a][b][r];
+            }
           }
-        }
-      } else {
-        const int32_t u = s_perm[lrow];
-        const float al = s_alpha[lrow];
-        if (u >= 0) {
-          float* orow = args.dphi + (int64_t)u * d_in;
+        } else {
+          const int32_t u = s_perm[lrow];
+          const float al = s_alpha[lrow];
+          if (u >= 0) {
+            float* orow = args.dphi + (int64_t)u * d_in;
 #pragma unroll
-          for (int b = 0; b < 2; ++b) {
-            const int col = n0 + wn * 64 + b * 32 + fl;
-            if (col < d_in) orow[col] = al * acc[a][b][r];
+            for (int b = 0; b < 2; ++b) {
+              const int col = n0 + wn * 64 + b * 32 + fl;
+              if (col < d_in) orow[col] = al * acc[a][b][r];
+            }
           }
         }
       }
     }
   }
-}
+};
 
 template <int DW_PA, int DW_PB, int DP_PA, int DP_PB, int NS>
 struct Cfg {
   static constexpr int dw_bytes = NS * (DW_PA + DW_PB) * kPlaneBytes;
   static constexpr int dp_bytes = NS * (DP_PA + DP_PB) * kPlaneBytes;
-  static constexpr int bytes = dw_bytes > dp_bytes ? dw_bytes : dp_bytes;
+  static constexpr int stages = dw_bytes > dp_bytes ? dw_bytes : dp_bytes;
+  static constexpr int bytes = stages + kPermBytes + 16;
 };
 
+// Persistent: one workgroup per CU drains its XCD's queue.  Between tiles the
+// next tile's first loads are issued before the finished tile's stores, so
+// the store drain overlaps the next load latency.  Every workgroup exits when
+// its queue's counter passes the queue length.
 template <int DW_PA, int DW_PB, int DP_PA, int DP_PB, int NS>
 __global__ __launch_bounds__(kThreads, 1) void grouped_backward_kernel(Args args, GemmTable tab) {
-  __shared__ __attribute__((aligned(16))) char smem_raw[Cfg<DW_PA, DW_PB, DP_PA, DP_PB, NS>::bytes];
+  using C = Cfg<DW_PA, DW_PB, DP_PA, DP_PB, NS>;
+  using DwTile = Tile<true, DW_PA, DW_PB, NS>;
+  using DpTile = Tile<false, DP_PA, DP_PB, NS>;
+  __shared__ __attribute__((aligned(16))) char smem_raw[C::bytes];
   LDS_AS char* smem = (LDS_AS char*)(smem_raw);
-  bool is_dw;
-  TileJob job;
-  if (!decode(tab, is_dw, job)) return;
-  if (is_dw)
-    gemm_tile<true, DW_PA, DW_PB, NS>(args, tab, job, smem);
-  else
-    gemm_tile<false, DP_PA, DP_PB, NS>(args, tab, job, smem);
+  LDS_AS char* prm = smem + C::stages;
+  LDS_AS int32_t* s_next = reinterpret_cast<LDS_AS int32_t*>(prm + kPermBytes);
+  const int x = blockIdx.x % kXcds;
+  const int nitems = queue_items(tab, x);
+  int32_t* head = args.ops.queue_heads + x;
+
+  // Next valid item of this XCD's queue (idle slots skipped); -1 when done.
+  auto fetch = [&](bool& is_dw, TileJob& job) -> int {
+    for (;;) {
+      if (threadIdx.x == 0) s_next[0] = atomicAdd(head, 1);
+      lds_barrier();
+      const int i = __builtin_amdgcn_readfirstlane(s_next[0]);
+      lds_barrier();   // everyone has read s_next before it is rewritten
+      if (i >= nitems) return -1;
+      if (decode(tab, x, i, is_dw, job)) return i;
+    }
+  };
+
+  f32x16 acc[4][2];
+  bool cur_dw;
+  TileJob cur;
+  if (fetch(cur_dw, cur) < 0) return;
+  if (cur_dw) DwTile(args, tab, cur).prologue(args, smem);
+  else DpTile(args, tab, cur).prologue(args, smem);
+  for (;;) {
+    if (cur_dw) DwTile(args, tab, cur).mainloop(args, smem, acc);
+    else DpTile(args, tab, cur).mainloop(args, smem, acc);
+    if (!cur_dw) DpTile(args, tab, cur).stage_rows(args, prm);
+    bool nxt_dw;
+    TileJob nxt;
+    const bool more = fetch(nxt_dw, nxt) >= 0;   // its barrier also frees every stage
+    if (more) {
+      if (nxt_dw) DwTile(args, tab, nxt).prologue(args, smem);
+      else DpTile(args, tab, nxt).prologue(args, smem);
+    }
+    if (cur_dw) DwTile(args, tab, cur).epilogue(args, tab, prm, acc);
+    else DpTile(args, tab, cur).epilogue(args, tab, prm, acc);
+    if (!more) break;
+    lds_barrier();   // the perm/alpha rows are read before the next tile restages them
+    cur_dw = nxt_dw;
+    cur = nxt;
+  }
 }
 
 template <int DW_PA, int DW_PB, int DP_PA, int DP_PB, int NS>
 hipError_t launch(const Args& args, const GemmTable& tab, hipStream_t s) {
-  const int64_t queue = (tab.total_groups + kXcds - 1) / kXcds;
-  const int64_t blocks = queue * kXcds * kGroupSlots;
-  if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_backward_kernel<DW_PA, DW_PB, DP_PA, DP_PB, NS>),
-                     dim3((unsigned)blocks), dim3(kThreads), 0, s, args, tab);
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  const int blocks = (cus + kXcds - 1) / kXcds * kXcds;   // one per CU, a multiple of 8
+  hipLaunchKernelGGL((grouped_backward_kernel<DW_PA, DW_PB, DP_PA, DP_PB, NS>), dim3(blocks),
+                     dim3(kThreads), 0, s, args, tab);
   return hipGetLastError();
 }
 
@@ -535,7 +630,18 @@ __global__ __launch_bounds__(256) void split_kernel(const void* __restrict__ src
   }
 }
 
+__global__ void zero_kernel(int32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
 }  // namespace
+
+hipError_t launch_zero(int32_t* p, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_split(int src_dtype, const void* src, int64_t rows, int32_t cols,
                         const float* alpha, uint16_t* hi, uint16_t* lo, hipStream_t s) {

@@ -22,15 +22,23 @@ struct ExpertTable {
 };
 
 // Tile schedule of the grouped GEMMs (host-built, by value).  Output tiles
-// are kTile x kTile.  Work is handed out in groups of kGroupSlots workgroup
-// slots (a gm x gn block of tiles of one expert and K chunk, sharing operand
-// panels); group g runs on XCD g % 8, so the tiles of a group meet in one L2.
-// The weight gradient of an expert with many kept rows is split along K into
+// are kTile x kTile.  Tiles are handed out in groups of kGroupSlots slots
+// (a gm x gn block of tiles of one expert and K chunk, sharing operand
+// panels).  Each XCD owns a queue of groups that its resident workgroups
+// drain through an atomic counter, so a group's panels meet in one L2.  The
+// weight gradient of an expert with many kept rows is split along K into
 // chunks of kc rows whose fp32 partial tiles are summed afterwards in chunk
 // order.
 constexpr int kTile = 256;
 constexpr int kGroupSlots = 12;
 constexpr int kXcds = 8;
+constexpr int kMaxGroups = 600;
+
+// Group descriptor: bit 31 = weight gradient, bits 23..30 expert,
+// bits 15..22 K chunk, bits 0..14 sub-group inside the expert (and chunk).
+__host__ __device__ inline uint32_t group_desc(bool dw, int e, int chunk, int sub) {
+  return (dw ? 0x80000000u : 0u) | ((uint32_t)e << 23) | ((uint32_t)chunk << 15) | (uint32_t)sub;
+}
 
 struct GemmTable {
   int32_t E;
@@ -39,12 +47,19 @@ struct GemmTable {
   int32_t dw_gm, dw_gn;           // dW group shape, dw_gm * dw_gn <= kGroupSlots
   int32_t dp_gm, dp_gn;           // dphi group shape
   int32_t kc;                     // dW K-chunk length (multiple of the K step)
-  int32_t dw_groups;              // dW groups come first ...
+  int32_t use_table;              // 1: groups[] below; 0: formula order (fallback)
+  int32_t dw_groups;              // formula order: dW groups first ...
   int32_t total_groups;           // ... then dphi groups
+  int32_t qoff[kXcds + 1];        // table: XCD x drains groups [qoff[x], qoff[x+1])
   int32_t seg_off[kMaxE + 1];     // compacted segment offsets
-  int32_t dw_goff[kMaxE + 1];     // first dW group of the expert of LPT rank r
-  int32_t dp_goff[kMaxE + 1];     // first dphi group of expert e (from dw_groups)
-  uint8_t order[kMaxE];           // dW: expert of LPT rank r (descending quota)
+  union {
+    uint32_t groups[kMaxGroups];  // table: group descriptors, XCD-major
+    struct {
+      int32_t dw_goff[kMaxE + 1]; // formula: first dW group of the expert of LPT rank r
+      int32_t dp_goff[kMaxE + 1]; // formula: first dphi group of expert e
+      uint8_t order[kMaxE];       // formula: expert of LPT rank r
+    } f;
+  };
 };
 
 // Device operand planes of the two products.  Every plane is bf16; a second
@@ -56,6 +71,7 @@ struct GemmOperands {
   const uint16_t* dp_b[2];        // [E, d_out, d_in]: W
   int32_t dw_pa, dw_pb, dp_pa, dp_pb;   // planes in use (1 or 2)
   float* partials;                // fp32 partial dW tiles of split experts
+  int32_t* queue_heads;           // kXcds counters, zeroed by the prologue
 };
 
 // Number of K chunks of an expert with q kept rows.
@@ -90,6 +106,9 @@ hipError_t launch_gather(int dtype, const int32_t* perm, const uint8_t* keep,
 // may be null); src is bf16 or float32 storage.
 hipError_t launch_split(int src_dtype, const void* src, int64_t rows, int32_t cols,
                         const float* alpha, uint16_t* hi, uint16_t* lo, hipStream_t s);
+
+// Zeroes n int32 counters (a fill kernel, safe inside captured graphs).
+hipError_t launch_zero(int32_t* p, int n, hipStream_t s);
 
 hipError_t launch_grouped_backward(const GemmTable& tab, const GemmOperands& ops,
                                    const int32_t* perm, const float* alpha_c, float* dW,
