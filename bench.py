@@ -27,6 +27,14 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, TFLOP/s
 
+# Sources that define the grouped GEMM kernel and its launch; HBM counters
+# taken on another version of them are not reported.
+GEMM_SOURCES = ("pruned_expert_backward_amd/csrc/grouped_gemm.hip",
+                "pruned_expert_backward_amd/csrc/lrmoe_internal.h",
+                "pruned_expert_backward_amd/csrc/api.cpp")
+COUNTERS_FILE = "profiles/grouped_backward_kernel.qwen3-down-c20.counters.txt"
+COPY_BYTES = 1 << 30           # plain copy used to calibrate FETCH_SIZE / WRITE_SIZE
+
 
 def algorithmic_bytes(p, M):
     """Bytes the method must move in score + select + compaction (each row
@@ -49,6 +57,70 @@ def gemm_floor_bytes(p, M):
     es = 2 if p.dtype == "bf16" else 4
     return (M * es * (p.d_out + p.d_in) + p.E * p.d_out * p.d_in * es
             + p.E * p.d_out * p.d_in * 4 + M * p.d_in * 4)
+
+
+def gemm_sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def read_counters(workload: str, dw_mode: str):
+    """HBM bytes per launch of the grouped GEMM from the committed rocprofv3
+    counter summary: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
+    scaled by bytes / counter of a plain copy of known size.  None when the
+    summary is missing, was taken on another workload, or the kernel sources
+    changed since."""
+    path = os.path.join(ROOT, COUNTERS_FILE)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#") and "=" in line:
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    try:
+        if (kv["workload"] != workload or kv["dw_mode"] != dw_mode
+                or kv["kernel_sources_sha256"] != gemm_sources_sha256()):
+            return None
+        fetch = float(kv["gemm_fetch_kib"]) * float(kv["copy_bytes"]) / float(kv["copy_fetch_kib"])
+        write = float(kv["gemm_write_kib"]) * float(kv["copy_bytes"]) / float(kv["copy_write_kib"])
+    except (KeyError, ValueError, ZeroDivisionError):
+        return None
+    return fetch + write
+
+
+def copy_calibration(reps: int = 10):
+    """A plain device copy of COPY_BYTES, for scaling the HBM counters."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = COPY_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    print(json.dumps({"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES,
+                      "reps": reps, "GBps_read_plus_write": 2 * COPY_BYTES * reps / el / 1e9}),
+          flush=True)
+
+
+def stats_us(d: list):
+    """Mean, median, p10 and p90 of per-launch durations (microseconds)."""
+    if not d:
+        return None
+    s = sorted(d)
+    pick = lambda f: s[min(len(s) - 1, int(f * (len(s) - 1) + 0.5))]
+    return {"mean": sum(s) / len(s), "median": pick(0.5), "p10": pick(0.1), "p90": pick(0.9),
+            "launches": len(s)}
 
 
 def cpu_baseline(p, budget_s: float = 12.0):
@@ -82,7 +154,12 @@ def main():
     ap.add_argument("--config", type=int, default=1)
     ap.add_argument("--dw-mode", choices=["exact", "bf16"], default="exact")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the path shards by expert across GPUs but no multi-GPU run is implemented.",
@@ -116,12 +193,39 @@ def main():
     stream = torch.cuda.current_stream()
     ssc_timer = lrmoe.KernelTimer(args.steps)
     gb_timer = lrmoe.KernelTimer(args.steps)
+    gu = p.gate_up
+    if gu is not None:
+        # second projection (gate/up) on the same keep set: gather its rows
+        # with the down projection's perm, then its own grouped backward
+        plan2 = lrmoe.Plan(p.counts, q, gu.d_out, gu.d_in, dtc, T=p.P, dw_mode=mode)
+        g2, x, W2 = d(gu.g2), d(gu.x), d(gu.W2)
+        out2 = dict(g_c=torch.empty((M, gu.d_out), dtype=g2.dtype, device=dev),
+                    phi_c=torch.empty((M, gu.d_in), dtype=x.dtype, device=dev),
+                    alpha_c=torch.empty((M,), dtype=torch.float32, device=dev),
+                    dphi=torch.empty((p.P, gu.d_in), dtype=torch.float32, device=dev))
+        dW2 = torch.empty((p.E, gu.d_out, gu.d_in), dtype=torch.float32, device=dev)
+        ws2 = lrmoe.workspace(plan2, dev)
+        gu_timer = lrmoe.KernelTimer(args.steps)
+        gu_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(args.steps)]
+    n_timed = [0]
 
     def step(timed=False):
         lrmoe.score_select_compact(plan, alpha, g, phi, g_row_index=row, out=out, ws=ws,
                                    timing=ssc_timer if timed else None)
         lrmoe.grouped_backward(plan, out["perm"], out["alpha_c"], out["g_c"], out["phi_c"], W,
                                dW=dW, dphi=out["dphi"], ws=ws, timing=gb_timer if timed else None)
+        if gu is not None:
+            if timed:
+                gu_ev[n_timed[0]][0].record(stream)
+            lrmoe.gather_compact(plan2, out["perm"], out["keep"], alpha, g2, x, out=out2)
+            if timed:
+                gu_ev[n_timed[0]][1].record(stream)
+            lrmoe.grouped_backward(plan2, out["perm"], out2["alpha_c"], out2["g_c"],
+                                   out2["phi_c"], W2, dW=dW2, dphi=out2["dphi"], ws=ws2,
+                                   timing=gu_timer if timed else None)
+        if timed:
+            n_timed[0] += 1
 
     for _ in range(args.warmup):
         step()
@@ -134,9 +238,13 @@ def main():
 
     es = 2 if p.dtype == "bf16" else 4
     P, d_o, d_i = p.P, p.d_out, p.d_in
-    us = {"lrm_score": ssc_timer.mean_us(0), "select_scan": ssc_timer.mean_us(1),
-          "gather": ssc_timer.mean_us(2), "operand_prologue": gb_timer.mean_us(0),
-          "grouped_gemm": gb_timer.mean_us(1), "splitk_reduce": gb_timer.mean_us(2)}
+    dist = {"lrm_score": stats_us(ssc_timer.durations_us(0)),
+            "select_scan": stats_us(ssc_timer.durations_us(1)),
+            "gather": stats_us(ssc_timer.durations_us(2)),
+            "operand_prologue": stats_us(gb_timer.durations_us(0)),
+            "grouped_gemm": stats_us(gb_timer.durations_us(1)),
+            "splitk_reduce": stats_us(gb_timer.durations_us(2))}
+    us = {k: (v["mean"] if v else None) for k, v in dist.items()}
     # algorithmic bytes (HBM-bound kernels) and FLOP (the GEMM) per launch
     work = {"lrm_score": P * (es * (d_o + d_i) + 8),
             "select_scan": P * 5,
@@ -146,7 +254,8 @@ def main():
     for name, t in us.items():
         if t is None:
             continue
-        k = {"us": t}
+        k = {"us": t, "us_median": dist[name]["median"], "us_p10": dist[name]["p10"],
+             "us_p90": dist[name]["p90"]}
         if name == "grouped_gemm":
             k.update(algorithmic_flops=work[name], TFLOPs=work[name] / t / 1e6,
                      mfma_frac=work[name] / t / 1e6 / MFMA_BF16_PEAK_TFLOPS)
@@ -159,7 +268,8 @@ def main():
     gemm_tf = kernels["grouped_gemm"]["TFLOPs"]
     roof = dict(kernel="grouped_backward_kernel", bound="mfma", achieved=gemm_tf,
                 peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s", frac=gemm_tf / MFMA_BF16_PEAK_TFLOPS,
-                traffic=None)
+                traffic=read_counters(p.name, args.dw_mode), traffic_unit="bytes per launch",
+                algorithmic_bytes_floor=gemm_floor_bytes(p, M))
     rec = {
         "metric": "kept pairs/s + grouped-GEMM TFLOP/s (% MFMA peak), score/compact % HBM BW",
         "value": M * args.steps / elapsed,
@@ -178,6 +288,21 @@ def main():
                                  "hbm_frac": nbytes / ssc_us / 1e3 / HBM_PEAK_GBS},
         "kernels": kernels,
     }
+    if gu is not None:
+        gd = stats_us([a.elapsed_time(b) * 1e3 for a, b in gu_ev])
+        gg = stats_us(gu_timer.durations_us(1))
+        gbytes = M * (2 * es * (gu.d_out + gu.d_in) + 12) + (P - M) * 4 * gu.d_in
+        gfl = 4.0 * M * gu.d_out * gu.d_in
+        rec["gate_up"] = {
+            "d_out": gu.d_out, "d_in": gu.d_in,
+            "gather_compact": {"us": gd["mean"], "us_median": gd["median"],
+                               "algorithmic_bytes": gbytes, "GBps": gbytes / gd["mean"] / 1e3,
+                               "hbm_frac": gbytes / gd["mean"] / 1e3 / HBM_PEAK_GBS},
+            "grouped_gemm": {"us": gg["mean"], "us_median": gg["median"],
+                             "algorithmic_flops": gfl, "TFLOPs": gfl / gg["mean"] / 1e6,
+                             "mfma_frac": gfl / gg["mean"] / 1e6 / MFMA_BF16_PEAK_TFLOPS},
+            "operand_prologue_us": gu_timer.mean_us(0), "splitk_reduce_us": gu_timer.mean_us(2)}
+        gu_timer.close()
     ssc_timer.close()
     gb_timer.close()
     if not args.no_cpu_baseline:
