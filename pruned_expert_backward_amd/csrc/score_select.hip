@@ -9,12 +9,14 @@
 // Select + scan: within each expert's quota the highest-scoring pairs are kept
 // (Portuguese write-up "LRMoE poda a passagem reversa do MoE ...", selection
 // bullet).  One 1024-thread workgroup per expert runs an MSB-first radix
-// select (4 x 8-bit digits) on an order-preserving integer image of the
+// select (12 + 12 + 8-bit digits) on an order-preserving integer image of the
 // float32 scores to find the q_e-th largest key tau_e and how many keys equal
-// to tau_e are still needed; ties go to the lower pair index.  The same
-// workgroup then scans the expert's pairs in index order, writes the keep
-// flags and the compacted permutation (ascending pair index inside the
-// segment).
+// to tau_e are still needed; ties go to the lower pair index.  Keys of experts
+// up to 24576 pairs are cached in LDS; for larger experts only the keys in the
+// first digit's bin are gathered into LDS for the later digits.  The same
+// workgroup then scans the expert's pairs in index order (8 consecutive keys
+// per thread, one workgroup prefix sum per 8192 keys), writes the keep flags
+// and the compacted permutation (ascending pair index inside the segment).
 #include "lrmoe_internal.h"
 
 namespace lrmoe {
@@ -101,22 +103,87 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kSelLdsKeys = 24576;   // 96 KiB: experts up to this size select from LDS
+constexpr int kSelLdsKeys = 24576;   // 96 KiB: keys of one expert, or first-digit candidates
+constexpr int kBins = 4096;          // first and second digits: 12 bits; last digit: 8 bits
+constexpr int kScanPer = 8;          // keys per thread per scan tile
+constexpr int kScanTile = kSelThreads * kScanPer;
+
+// Inclusive prefix sum of v over the workgroup in thread order; `total`
+// receives the workgroup sum.  wsum: kSelWaves LDS words.
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wsum, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  uint32_t before = 0, t = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    const uint32_t sw = wsum[w];
+    before += (w < wave) ? sw : 0u;
+    t += sw;
+  }
+  __syncthreads();   // wsum may be reused
+  total = t;
+  return before + x;
+}
+
+struct Digit {
+  uint32_t digit;   // bin holding the k-th largest key among the counted ones
+  uint32_t k;       // its rank inside that bin (1-based, from the top)
+  uint32_t count;   // keys in that bin
+};
+
+// Given a histogram of `nbins` (<= 4 per thread) bins in LDS, find the bin
+// that holds the k-th largest counted key.  Thread t owns the 4 bins just
+// below bin nbins - 4t, so the thread-order scan counts from the top bin.
+__device__ __forceinline__ Digit find_digit(const uint32_t* hist, int nbins, uint32_t k,
+                                            uint32_t* wsum, Digit* out) {
+  const int tid = threadIdx.x;
+  const int top = nbins - 4 * tid;   // this thread's bins: top-1 .. top-4
+  uint32_t c[4] = {0u, 0u, 0u, 0u};
+  if (top > 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c[j] = hist[top - 1 - j];
+  }
+  const uint32_t local = c[0] + c[1] + c[2] + c[3];
+  uint32_t total;
+  const uint32_t incl = block_scan(local, wsum, total);
+  const uint32_t above = incl - local;
+  if (local > 0 && above < k && k <= incl) {
+    uint32_t cum = above;
+    int j = 0;
+    while (cum + c[j] < k) cum += c[j++];   // terminates: cum + sum(c) >= k
+    out->digit = (uint32_t)(top - 1 - j);
+    out->k = k - cum;
+    out->count = c[j];
+  }
+  __syncthreads();
+  const Digit d = *out;
+  __syncthreads();
+  return d;
+}
 
 __global__ __launch_bounds__(kSelThreads) void select_scan_kernel(
     ExpertTable tab, const float* __restrict__ scores, uint8_t* __restrict__ keep,
     int32_t* __restrict__ perm, int32_t* __restrict__ seg_offsets_out) {
-  __shared__ uint32_t hist[kSelWaves][256];
-  __shared__ uint32_t sh_digit, sh_k;
-  __shared__ uint32_t wcnt[2][kSelWaves];
-  __shared__ uint32_t keys_lds[kSelLdsKeys];   // the expert's keys, when they fit
+  __shared__ uint32_t keys_lds[kSelLdsKeys];   // the expert's keys, or the candidates
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t wsum[kSelWaves];
+  __shared__ uint32_t cand_n;
+  __shared__ Digit dig;
 
   const int e = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int base = tab.pair_off[e];
   const int n = tab.pair_off[e + 1] - base;
   const int seg = tab.seg_off[e];
   const uint32_t q = (uint32_t)(tab.seg_off[e + 1] - seg);
+  const float* __restrict__ src = scores + base;
 
   if (tid == 0) {
     seg_offsets_out[e] = seg;
@@ -125,101 +192,129 @@ __global__ __launch_bounds__(kSelThreads) void select_scan_kernel(
   if (n == 0) return;
   const bool cached = n <= kSelLdsKeys;
   if (cached) {
-    for (int i = tid; i < n; i += kSelThreads) keys_lds[i] = score_key(scores[base + i]);
+    int i = tid;
+    for (; i + 3 * kSelThreads < n; i += 4 * kSelThreads) {
+      const float a = src[i], b = src[i + kSelThreads], c = src[i + 2 * kSelThreads],
+                  d = src[i + 3 * kSelThreads];
+      keys_lds[i] = score_key(a);
+      keys_lds[i + kSelThreads] = score_key(b);
+      keys_lds[i + 2 * kSelThreads] = score_key(c);
+      keys_lds[i + 3 * kSelThreads] = score_key(d);
+    }
+    for (; i < n; i += kSelThreads) keys_lds[i] = score_key(src[i]);
     __syncthreads();
   }
-  auto key_at = [&](int i) -> uint32_t {
-    return cached ? keys_lds[i] : score_key(scores[base + i]);
-  };
 
-  // ---- radix select: tau = q-th largest key, need = #(key == tau) to keep
-  uint32_t tau = 0xFFFFFFFFu, need = 0;   // q == 0: nothing is above or equal
+  // ---- radix select, most significant digit first: 12 + 12 + 8 bits.
+  // tau = the q-th largest key; need = how many keys equal to tau are kept.
+  uint32_t tau = 0xFFFFFFFFu, need = 0;   // q == 0: no key is above or equal
   if (q > 0) {
-    uint32_t prefix = 0, mask = 0, k = q;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = tid; i < kSelWaves * 256; i += kSelThreads) (&hist[0][0])[i] = 0;
-      __syncthreads();
-      for (int i = tid; i < n; i += kSelThreads) {
-        const uint32_t key = key_at(i);
-        if ((key & mask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1u);
+    // digit 1 (key bits 31..20) over every key
+    for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0;
+    __syncthreads();
+    if (cached) {
+      for (int i = tid; i < n; i += kSelThreads) atomicAdd(&hist[keys_lds[i] >> 20], 1u);
+    } else {
+      int i = tid;
+      for (; i + 3 * kSelThreads < n; i += 4 * kSelThreads) {
+        const float a = src[i], b = src[i + kSelThreads], c = src[i + 2 * kSelThreads],
+                    d = src[i + 3 * kSelThreads];
+        atomicAdd(&hist[score_key(a) >> 20], 1u);
+        atomicAdd(&hist[score_key(b) >> 20], 1u);
+        atomicAdd(&hist[score_key(c) >> 20], 1u);
+        atomicAdd(&hist[score_key(d) >> 20], 1u);
       }
-      __syncthreads();
-      if (tid < 256) {
-        uint32_t s = 0;
-#pragma unroll
-        for (int w = 0; w < kSelWaves; ++w) s += hist[w][tid];
-        hist[0][tid] = s;
-      }
-      __syncthreads();
-      if (wave == 0) {
-        // lane l owns bins 4l .. 4l+3; count from the top bin down.
-        const uint32_t c0 = hist[0][4 * lane], c1 = hist[0][4 * lane + 1];
-        const uint32_t c2 = hist[0][4 * lane + 2], c3 = hist[0][4 * lane + 3];
-        const uint32_t local = c0 + c1 + c2 + c3;
-        uint32_t suffix = local;  // inclusive sum over lanes >= lane
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const uint32_t o = __shfl_down(suffix, off, 64);
-          if (lane + off < 64) suffix += o;
+      for (; i < n; i += kSelThreads) atomicAdd(&hist[score_key(src[i]) >> 20], 1u);
+    }
+    __syncthreads();
+    Digit d1 = find_digit(hist, kBins, q, wsum, &dig);
+    uint32_t prefix = d1.digit << 20;
+    uint32_t k = d1.k;
+
+    // Remaining digits look only at keys whose top bits equal `prefix`: the
+    // cached keys, or (large experts) the first-digit candidates collected
+    // into LDS, or -- if there are too many of those -- all keys again.
+    const uint32_t* list = keys_lds;
+    int nlist = n;
+    bool from_global = false;
+    if (!cached) {
+      if (d1.count <= (uint32_t)kSelLdsKeys) {
+        if (tid == 0) cand_n = 0;
+        __syncthreads();
+        for (int i = tid; i < n; i += kSelThreads) {
+          const uint32_t key = score_key(src[i]);
+          if ((key >> 20) == d1.digit) keys_lds[atomicAdd(&cand_n, 1u)] = key;
         }
-        const uint32_t above = suffix - local;
-        if (above < k && k <= suffix) {
-          uint32_t cum = above, d;
-          if (cum + c3 >= k) d = 3;
-          else if ((cum += c3) + c2 >= k) d = 2;
-          else if ((cum += c2) + c1 >= k) d = 1;
-          else { cum += c1; d = 0; }
-          sh_digit = 4u * lane + d;
-          sh_k = k - cum;
-        }
+        __syncthreads();
+        nlist = (int)d1.count;   // == cand_n
+      } else {
+        from_global = true;
+      }
+    }
+    auto list_key = [&](int i) -> uint32_t {
+      return from_global ? score_key(src[i]) : list[i];
+    };
+    // digit 2 (bits 19..8), then digit 3 (bits 7..0)
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {
+      const int shift = pass == 0 ? 8 : 0;
+      const int nb = pass == 0 ? kBins : 256;
+      const uint32_t pmask = pass == 0 ? 0xFFF00000u : 0xFFFFFF00u;
+      for (int i = tid; i < nb; i += kSelThreads) hist[i] = 0;
+      __syncthreads();
+      for (int i = tid; i < nlist; i += kSelThreads) {
+        const uint32_t key = list_key(i);
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
       }
       __syncthreads();
-      prefix |= sh_digit << shift;
-      mask |= 0xFFu << shift;
-      k = sh_k;
-      __syncthreads();
+      const Digit dd = find_digit(hist, nb, k, wsum, &dig);
+      prefix |= dd.digit << shift;
+      k = dd.k;
     }
     tau = prefix;
     need = k;
   }
 
-  // ---- stable scan: keep = key > tau, or key == tau among the first `need`
-  uint32_t run_keep = 0, run_eq = 0;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int c0 = 0; c0 < n; c0 += kSelThreads) {
-    const int i = c0 + tid;
-    const bool valid = i < n;
-    const uint32_t key = valid ? key_at(i) : 0u;
-    const bool gt = valid && key > tau;
-    const bool eq = valid && key == tau;
-    const uint64_t beq = __ballot(eq);
-    if (lane == 0) wcnt[0][wave] = (uint32_t)__popcll(beq);
-    __syncthreads();
-    uint32_t eq_before = 0, eq_total = 0;
-    for (int w = 0; w < kSelWaves; ++w) {
-      const uint32_t v = wcnt[0][w];
-      eq_before += (w < wave) ? v : 0u;
-      eq_total += v;
+  // ---- stable scan in pair order: keep = key > tau, or key == tau among
+  // the first `need` of those.  Thread t owns 8 consecutive keys of a tile;
+  // one workgroup scan of (#gt, #eq) per tile gives every position.
+  uint32_t run_gt = 0, run_eq = 0;
+  for (int c0 = 0; c0 < n; c0 += kScanTile) {
+    const int i0 = c0 + tid * kScanPer;
+    uint32_t key[kScanPer];
+    uint32_t ngt = 0, neq = 0;
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) {
+      const int i = i0 + j;
+      key[j] = i < n ? (cached ? keys_lds[i] : score_key(src[i])) : 0u;
+      const bool ok = i < n;
+      ngt += (ok && key[j] > tau) ? 1u : 0u;
+      neq += (ok && key[j] == tau) ? 1u : 0u;
     }
-    const uint32_t eq_rank = run_eq + eq_before + (uint32_t)__popcll(beq & lt_mask);
-    const bool kp = gt || (eq && eq_rank < need);
-    const uint64_t bk = __ballot(kp);
-    if (lane == 0) wcnt[1][wave] = (uint32_t)__popcll(bk);
-    __syncthreads();
-    uint32_t k_before = 0, k_total = 0;
-    for (int w = 0; w < kSelWaves; ++w) {
-      const uint32_t v = wcnt[1][w];
-      k_before += (w < wave) ? v : 0u;
-      k_total += v;
+    uint32_t tot;
+    const uint32_t incl = block_scan((ngt << 16) | neq, wsum, tot);   // per tile < 2^16 each
+    const uint32_t excl = incl - ((ngt << 16) | neq);
+    uint32_t gt_before = run_gt + (excl >> 16);
+    uint32_t eq_before = run_eq + (excl & 0xFFFFu);
+    // kept keys before this thread: every greater key, and the equal keys
+    // among the first `need` equal ones
+    uint32_t pos = gt_before + (eq_before < need ? eq_before : need);
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) {
+      const int i = i0 + j;
+      if (i < n) {
+        const bool gt = key[j] > tau, eq = key[j] == tau;
+        const bool kp = gt || (eq && eq_before < need);
+        eq_before += eq ? 1u : 0u;
+        keep[base + i] = kp ? 1 : 0;
+        if (kp) {
+          if (pos < q) perm[seg + pos] = base + i;   // pos < q holds by construction
+          ++pos;
+        }
+      }
     }
-    if (valid) {
-      keep[base + i] = kp ? 1 : 0;
-      const uint32_t pos = run_keep + k_before + (uint32_t)__popcll(bk & lt_mask);
-      if (kp && pos < q) perm[seg + pos] = base + i;   // pos < q holds by construction
-    }
-    run_eq += eq_total;
-    run_keep += k_total;
-    __syncthreads();
+    run_gt += tot >> 16;
+    run_eq += tot & 0xFFFFu;
   }
 }
 

@@ -83,6 +83,25 @@ def test_ties_given_scores(distinct):
         U.compare_full(p, q, out, scores_in=s)
 
 
+@pytest.mark.parametrize("distinct", [0, 3, 1])
+def test_select_large_experts(distinct):
+    """Experts larger than the LDS key cache: the first digit's candidates are
+    gathered into LDS (continuous scores), or the later digits run over every
+    key again when one first-digit bin holds more than the cache (3 values or
+    one value over 90000 pairs)."""
+    counts = [90000, 30000, 4000, 1, 0]
+    p = W.make_problem(P=sum(counts), E=5, d_out=8, d_in=8, dtype="bf16", counts=counts, seed=40)
+    s = W.random_scores(p.P, seed=40 + distinct, distinct=distinct)
+    for policy in (("ratio", 80, 100), ("ratio", 1, 3), ("ratio", 1, 1), ("budget", 5000)):
+        q = lrmoe.plan_quota(p.counts, policy)
+        plan, out, _ = U.run_gpu(p, q, scores=s)
+        keep_ref, _ = O.select_top_quota(s.astype(np.float64), p.counts, q)
+        assert np.array_equal(out["keep"].cpu().numpy().astype(bool), keep_ref), policy
+        perm, seg = O.compact(keep_ref, p.counts, q)
+        assert np.array_equal(out["perm"].cpu().numpy(), perm), policy
+        assert np.array_equal(out["seg_offsets"].cpu().numpy(), seg), policy
+
+
 def test_negative_and_signed_zero_scores():
     """The order-preserving key handles negative scores and -0.0 == 0.0."""
     p = W.make_problem(P=600, E=3, d_out=32, d_in=32, dtype="bf16", counts=[200, 250, 150], seed=5)
