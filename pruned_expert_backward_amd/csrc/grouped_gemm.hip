@@ -15,11 +15,16 @@
 //                    (varlen), N = d_in, K = d_out.
 //
 // gfx950 mapping
-//   * 512-thread workgroups (8 wave64s, 2 x 4, two per SIMD) own a 256x256
-//     fp32 tile; each wave accumulates 128x64 (128 accumulator registers)
-//     with v_mfma_f32_32x32x16_bf16 (fp32 accumulate).  Large tiles keep
-//     operand bytes per FLOP low enough for L2 and LDS; two waves per SIMD
-//     let one issue MFMAs while the other waits on LDS or the barrier.
+//   * 256-thread workgroups (4 wave64s, 2 x 2, one per SIMD) own a 256x256
+//     fp32 tile; each wave accumulates 128x128 in its 256 accumulation
+//     registers with v_mfma_f32_32x32x16_bf16 (fp32 accumulate).  Large wave
+//     tiles keep LDS bytes per MFMA low (the LDS, not the matrix cores, bounds
+//     a 128x64 wave tile).  With one wave per SIMD the K loop is software
+//     pipelined by hand: fragments are double-buffered in registers by half
+//     K step, and LDS reads and global->LDS loads are placed between MFMAs
+//     (see Tile).  Accumulators hold each 32x32 block transposed (lane = row,
+//     register quad = 4 consecutive columns), so results leave as 16-byte
+//     stores.
 //   * Every operand is a bf16 plane in global memory.  alpha multiplies the
 //     reduction index of dW, so it cannot be applied after the product: a
 //     prologue writes alpha * (the narrower of g_c, phi_c) as bf16 hi + lo
@@ -38,10 +43,11 @@
 //     register staging): each wave instruction fills one 1 KiB LDS block, lane
 //     i writing bytes 16i..16i+15, so each lane fetches the global chunk that
 //     the swizzled layout puts in its slot; lanes past a row or column edge
-//     get an out-of-range offset and write zeros.  Three LDS stages keep the
-//     loads two K steps ahead of the MFMAs (two for float32 storage, whose
-//     four planes would not fit three times); each step waits only for its
-//     own stage and then crosses one barrier.
+//     get an out-of-range offset and write zeros.  Each tile kind gets as
+//     many LDS stages as fit in 144 KiB, up to four: two planes (dphi, and dW
+//     in single-rounding mode) -> 4 stages; three planes (dW with a hi + lo
+//     operand) -> 3; four (float32 storage) -> 2.  Each K step crosses one
+//     barrier, between its two halves.
 //   * Scheduling: dW and dphi tiles share one launch.  Tiles are grouped in
 //     blocks of an expert's tile grid that share operand panels; group g runs
 //     on XCD g % 8 (workgroups are dispatched round-robin over the 8 XCDs), so
@@ -66,16 +72,20 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = kTile, BN = kTile, BK = 32;
-constexpr int kThreads = 512;
+constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kPlaneBytes = kTile * BK * 2;   // one bf16 operand plane of one K step (16 KB)
 constexpr int kChunksPerPlane = kTile * BK / 8 / kThreads;   // 16-byte chunks per thread
 
 // ------------------------------------------------------------ LDS layouts
-// KC: row r (0..255) holds K 0..31 as 4 chunks of 16 B.
-__device__ __forceinline__ int kc_off(int r, int c) {
-  return r * 64 + ((c ^ (((r >> 1) ^ (r >> 3)) & 3)) << 4);
-}
+// KC: row r (0..255) holds K 0..31 as 4 chunks of 16 B; chunk c of row r
+// sits at slot c ^ kc_swz(r).  A fragment read (ds_read_b128) serves 16
+// consecutive lanes = 16 consecutive rows per LDS cycle; this swizzle gives
+// them 16 distinct 16-byte bank slots (measured on gfx950: twice the read
+// rate of the ((r >> 1) ^ (r >> 3)) & 3 variant, and the same rate as a
+// linear b128 read).
+__device__ __forceinline__ int kc_swz(int r) { return (r ^ (r >> 2)) & 3; }
+__device__ __forceinline__ int kc_off(int r, int c) { return r * 64 + ((c ^ kc_swz(r)) << 4); }
 // MC: row k (0..31) holds M/N 0..255 as 32 chunks of 16 B.
 __device__ __forceinline__ int mc_off(int k, int c) { return k * 512 + ((c ^ ((k & 3) << 2)) << 4); }
 
@@ -100,6 +110,19 @@ __device__ __forceinline__ i16x8 frag_mc(LDS_AS const char* t, int mb, int kb, i
   const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       reinterpret_cast<LDS_AS i16x4*>(base + mc_off(k0 + 4, c) + half));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// The same fragments read at a precomputed LDS byte address (see the tile's
+// la / lb): MC = two transposing reads 4 rows apart, KC = one 16-byte read.
+__device__ __forceinline__ i16x8 frag_mc_at(uint32_t addr) {
+  LDS_AS char* p = (LDS_AS char*)(uintptr_t)addr;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<LDS_AS i16x4*>(p));
+  const i16x4 hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<LDS_AS i16x4*>(p + 2048));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ i16x8 frag_kc_at(uint32_t addr) {
+  return *reinterpret_cast<LDS_AS const i16x8*>((LDS_AS char*)(uintptr_t)addr);
 }
 
 template <bool MC>
@@ -237,14 +260,35 @@ constexpr int kPermBytes = BM * 8;   // dphi epilogue: destination row + alpha p
 // and B (MC, rows = K) are [M, d_out] / [M, d_in] segment rows.  Else A (KC,
 // rows = M) = g_c segment rows and B (MC) = W_e.  PA/PB: bf16 planes of each
 // operand; NS: LDS stages.
+//
+// Software pipeline of one K step kt (stage S = kt % NS), per wave:
+//   phase 1  MFMAs of half 0 (registers f0), interleaved with the LDS reads
+//            of half 1 of stage S into f1;
+//   barrier  wait for this wave's loads of stage kt + 1 and its LDS reads,
+//            then s_barrier: stage kt + 1 is in LDS and nobody reads stage S
+//            any more;
+//   phase 3  MFMAs of half 1 (f1), interleaved with the LDS reads of half 0
+//            of stage kt + 1 into f0 and with this wave's loads of stage
+//            kt + NS into buffer S.
+// The matrix core always has independent MFMAs queued while fragments and
+// stages move, and the global loads trickle out between MFMAs instead of
+// stalling the wave in a burst.
 template <bool IS_DW, int PA, int PB, int NS>
 struct Tile {
   static constexpr bool A_MC = IS_DW;
   static constexpr int kStage = (PA + PB) * kPlaneBytes;
-  static constexpr int kDist = NS - 1;                 // prefetch distance in K steps
-  static constexpr int kBlocks = kPlaneBytes / 1024;   // 1 KiB LDS blocks per plane
-  static constexpr int kPerWave = kBlocks / kWaves;    // ... filled by each wave
-  static constexpr int kLoads = (PA + PB) * kPerWave;  // load instructions per stage per wave
+  static constexpr int kBlocks = kPlaneBytes / 1024;     // 1 KiB LDS blocks per plane
+  static constexpr int kPerWave = kBlocks / kWaves;      // ... filled by each wave
+  static constexpr int kLoads = (PA + PB) * kPerWave;    // load instructions per stage per wave
+  static constexpr int kTerms = 1 + (PA == 2) + (PB == 2);
+  static constexpr int kHalfMfmas = 16 * kTerms;         // per wave per half step
+  static constexpr int kFrags = (PA + PB) * 4;           // fragments per half step
+  static_assert(kFrags <= kHalfMfmas && kLoads <= kHalfMfmas, "interleave slots");
+
+  struct Frags {
+    i16x8 a[PA][4];
+    i16x8 b[PB][4];
+  };
 
   int e, m0, n0, chunk, chunks, q, seg, K, mrows, nk;
   int lane, wave, wm, wn;
@@ -252,13 +296,19 @@ struct Tile {
   const uint16_t* B[2];
   uint32_t aoff[kPerWave], boff[kPerWave];
   int acol[kPerWave];
+  // LDS byte addresses of this lane's fragment reads in stage 0, plane 0:
+  // MC operands: one per 32-wide fragment (half 0; half 1 is +8 KiB);
+  // KC operand: one per half (fragment a is +2 KiB * a).
+  uint32_t la[4], lb[4];
+  LDS_AS char* sink;   // kWaves x 1 KiB of LDS that only dead loads write
 
-  __device__ __forceinline__ Tile(const Args& args, const GemmTable& tab, const TileJob& job) {
+  __device__ __forceinline__ Tile(const Args& args, const GemmTable& tab, const TileJob& job,
+                                  LDS_AS char* smem, LDS_AS char* sink_) : sink(sink_) {
     const int tid = threadIdx.x;
     lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    wm = wave >> 2;   // wave tile rows wm*128, cols wn*64
-    wn = wave & 3;
+    wm = wave >> 1;   // wave tile rows wm*128, cols wn*128
+    wn = wave & 1;
     // Tile coordinates are workgroup-uniform; say so, so that buffer
     // descriptors and LDS bases stay in scalar registers.
     e = __builtin_amdgcn_readfirstlane(job.e);
@@ -296,97 +346,170 @@ struct Tile {
       }
       if (!A_MC) {   // KC block: rows 16*blk .. +15 of the tile, 4 chunks each
         const int r = 16 * blk + (lane >> 2), pc = lane & 3;
-        const int lc = pc ^ (((r >> 1) ^ (r >> 3)) & 3);
+        const int lc = pc ^ kc_swz(r);
         acol[j] = 8 * lc;
         aoff[j] = (uint32_t)(r * d_out + 8 * lc) * 2u;
       }
     }
-  }
-
-  // ---- global -> LDS stage for the K step starting at k0
-  __device__ __forceinline__ void issue(const Args& args, int k0, LDS_AS char* stage) const {
-    const int d_out = args.d_out, d_in = args.d_in;
-    const int krows = K - k0 < BK ? K - k0 : BK;
+    // Fragment addresses (see frag_mc / frag_kc for the lane layouts).
+    const uint32_t base = lds_addr(smem);
+    {
+      const int G = lane >> 4, s = lane & 15;
+      const int k0 = 8 * (G >> 1) + (s >> 2);
+      const int cl = 2 * (G & 1) + ((s & 3) >> 1);
+      const int half = (s & 1) * 8;
 #pragma unroll
-    for (int p = 0; p < PA; ++p) {
-      __amdgpu_buffer_rsrc_t r =
-          A_MC ? rsrc(A[p] + ((int64_t)seg + k0) * d_out, (int64_t)krows * d_out * 2)
-               : rsrc(A[p] + ((int64_t)seg + m0) * d_out, (int64_t)(q - m0) * d_out * 2);
-#pragma unroll
-      for (int j = 0; j < kPerWave; ++j) {
-        uint32_t off = aoff[j];
-        if (!A_MC) off = (k0 + acol[j]) < K ? off + (uint32_t)k0 * 2u : kOutOfRange;
-        load_lds16(r, lds_addr(stage + p * kPlaneBytes + (wave * kPerWave + j) * 1024), off);
+      for (int f = 0; f < 4; ++f) {
+        lb[f] = base + (uint32_t)(mc_off(k0, (wn * 128 + f * 32) / 8 + cl) + half);
+        if (A_MC) la[f] = base + (uint32_t)(mc_off(k0, (wm * 128 + f * 32) / 8 + cl) + half);
       }
     }
+    if (!A_MC) {
+      const int r = wm * 128 + (lane & 31);
 #pragma unroll
-    for (int p = 0; p < PB; ++p) {
-      const uint16_t* b0 = IS_DW ? B[p] + ((int64_t)seg + k0) * d_in
-                                 : B[p] + ((int64_t)e * d_out + k0) * d_in;
-      __amdgpu_buffer_rsrc_t r = rsrc(b0, (int64_t)krows * d_in * 2);
-#pragma unroll
-      for (int j = 0; j < kPerWave; ++j)
-        load_lds16(r, lds_addr(stage + (PA + p) * kPlaneBytes + (wave * kPerWave + j) * 1024),
-                   boff[j]);
+      for (int h = 0; h < 2; ++h) la[h] = base + (uint32_t)kc_off(r, 2 * h + (lane >> 5));
+      la[2] = la[3] = 0;
     }
   }
 
-  // First kDist stages (fewer if K is short).
+  // ---- global -> LDS: load instruction `idx` (0 .. kLoads-1) of this wave
+  // for the K step starting at k0.  Instruction idx fills LDS block
+  // wave * kPerWave + idx % kPerWave of plane idx / kPerWave (A planes first).
+  // When !live the instruction keeps its place in the stream but reads an
+  // empty range and writes only zeros, into this wave's sink block.
+  __device__ __forceinline__ void issue_one(const Args& args, int k0, LDS_AS char* stage,
+                                            int idx, bool live = true) const {
+    const int d_out = args.d_out, d_in = args.d_in;
+    const int krows = live ? (K - k0 < BK ? K - k0 : BK) : 0;
+    const int p = idx / kPerWave, j = idx % kPerWave;
+    LDS_AS char* dst = live ? stage + p * kPlaneBytes + (wave * kPerWave + j) * 1024
+                            : sink + wave * 1024;
+    if (p < PA) {
+      __amdgpu_buffer_rsrc_t r =
+          A_MC ? rsrc(A[p] + ((int64_t)seg + k0) * d_out, (int64_t)krows * d_out * 2)
+               : rsrc(A[p] + ((int64_t)seg + m0) * d_out,
+                      live ? (int64_t)(q - m0) * d_out * 2 : 0);
+      uint32_t off = aoff[j];
+      if (!A_MC) off = (k0 + acol[j]) < K ? off + (uint32_t)k0 * 2u : kOutOfRange;
+      load_lds16(r, lds_addr(dst), off);
+    } else {
+      const uint16_t* b0 = IS_DW ? B[p - PA] + ((int64_t)seg + k0) * d_in
+                                 : B[p - PA] + ((int64_t)e * d_out + k0) * d_in;
+      load_lds16(rsrc(b0, (int64_t)krows * d_in * 2), lds_addr(dst), boff[j]);
+    }
+  }
+
+  // First min(NS, nk) stages.
   __device__ __forceinline__ void prologue(const Args& args, LDS_AS char* smem) const {
 #pragma unroll
-    for (int d = 0; d < kDist; ++d)
-      if (d < nk) issue(args, d * BK, smem + d * kStage);
+    for (int d = 0; d < NS; ++d)
+      if (d < nk) {
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) issue_one(args, d * BK, smem + d * kStage, i);
+      }
   }
 
-  // ---- MFMAs of one K step: hi*hi (+ hi*lo_B) (+ lo_A*hi).  All fragments
-  // of the step are read first, so the second half's LDS reads overlap the
-  // first half's MFMAs.
-  __device__ __forceinline__ void compute(LDS_AS const char* stage, f32x16 (&acc)[4][2]) const {
-    i16x8 fb[2][PB][2], fa[2][PA][4];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int p = 0; p < PB; ++p)
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-          fb[h][p][b] = frag_mc(stage + (PA + p) * kPlaneBytes, wn * 64 + b * 32, 16 * h, lane);
-#pragma unroll
-      for (int p = 0; p < PA; ++p)
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-          fa[h][p][a] = frag<A_MC>(stage + p * kPlaneBytes, wm * 128 + a * 32, 16 * h, lane);
+  // ---- fragment i (0 .. kFrags-1) of half h of stage s: A fragments first.
+  __device__ __forceinline__ void read_frag(int s, int h, Frags& f, int i) const {
+    const uint32_t so = (uint32_t)(s * kStage);
+    if (i < PA * 4) {
+      const int p = i / 4, a = i % 4;
+      const uint32_t po = so + (uint32_t)(p * kPlaneBytes);
+      if (A_MC) f.a[p][a] = frag_mc_at(la[a] + po + (uint32_t)(h * 8192));
+      else f.a[p][a] = frag_kc_at(la[h] + po + (uint32_t)(a * 2048));
+    } else {
+      const int p = (i - PA * 4) / 4, b = (i - PA * 4) % 4;
+      f.b[p][b] = frag_mc_at(lb[b] + so + (uint32_t)((PA + p) * kPlaneBytes + h * 8192));
     }
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          acc[a][b] = mfma(fa[h][0][a], fb[h][0][b], acc[a][b]);
-          if (PB == 2) acc[a][b] = mfma(fa[h][0][a], fb[h][PB - 1][b], acc[a][b]);
-          if (PA == 2) acc[a][b] = mfma(fa[h][PA - 1][a], fb[h][0][b], acc[a][b]);
-        }
   }
 
-  // ---- K loop: stage kt lives in LDS buffer kt % NS; the loads of step
-  // kt + kDist go into the buffer that step kt - 1 used, after the barrier
-  // that follows everyone's MFMAs of step kt - 1.  The prologue's loads must
-  // have been issued.  Ends with every load of the tile consumed.
+  // ---- MFMA i (0 .. kHalfMfmas-1) of a half: terms hi*hi, hi*lo_B, lo_A*hi.
+  // The B fragment goes in the MFMA's first operand slot, so each 32x32
+  // accumulator holds the block transposed: lane = tile row (M), registers =
+  // columns (N), four consecutive columns per register quad.  That lets the
+  // epilogue write 16 bytes per lane.
+  __device__ __forceinline__ static void mfma_i(const Frags& f, f32x16 (&acc)[4][4], int i) {
+    const int t = i / 16, a = (i % 16) / 4, b = i % 4;
+    const int pa = (t == 2 || (t == 1 && PB == 1)) ? PA - 1 : 0;
+    const int pb = (t == 1 && PB == 2) ? 1 : 0;
+    acc[a][b] = mfma(f.b[pb][b], f.a[pa][a], acc[a][b]);
+  }
+
+  // Barrier of step kt: stage kt + 1 is complete for every wave.  Stages
+  // kt + 1 .. last are this wave's outstanding loads (in issue order).
+  __device__ __forceinline__ static void wait_next(int later) {
+    if (later >= 2) wait_loads_barrier<2 * kLoads>();
+    else if (later == 1) wait_loads_barrier<kLoads>();
+    else wait_loads_barrier<0>();
+  }
+
+  // This wave's loads of one stage are split in two halves: the first half
+  // of stage kt + NS goes out during phase 3 of step kt (into buffer S, free
+  // after that step's barrier), the second half during phase 1 of step
+  // kt + 1 (same buffer).  Both halves are spread evenly over the MFMAs.
+  static constexpr int kLoadsLo = kLoads / 2;
+  static constexpr int kLoadsHi = kLoads - kLoadsLo;
+  // n loads over kHalfMfmas slots: load d goes after MFMA (d * kHalfMfmas) / n.
+  // Index of the load after MFMA i, or -1.
+  __device__ __forceinline__ static constexpr int load_at(int i, int n) {
+    for (int d = 0; d < n; ++d)
+      if ((d * kHalfMfmas) / n == i) return d;
+    return -1;
+  }
+
+  __device__ __forceinline__ void step(const Args& args, LDS_AS char* smem, int kt, Frags& f0,
+                                       Frags& f1, f32x16 (&acc)[4][4]) const {
+    const int S = kt % NS, SN = S + 1 == NS ? 0 : S + 1, SP = S == 0 ? NS - 1 : S - 1;
+    // phase 1: second half of stage kt + NS - 1 (buffer SP); the prologue
+    // already issued it when kt == 0
+    const bool live1 = kt >= 1 && kt + NS - 1 < nk;
+#pragma unroll
+    for (int i = 0; i < kHalfMfmas; ++i) {
+      mfma_i(f0, acc, i);
+      if (i < kFrags) read_frag(S, 1, f1, i);
+      if (load_at(i, kLoadsHi) >= 0)
+        issue_one(args, (kt + NS - 1) * BK, smem + SP * kStage, kLoadsLo + load_at(i, kLoadsHi),
+                  live1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const bool next = kt + 1 < nk;
+    if (next) {
+      const int last = kt + NS - 1 < nk - 1 ? kt + NS - 1 : nk - 1;   // last stage issued
+      wait_next(last - (kt + 1));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // phase 3: first half of stage kt + NS (buffer S).  Branch-free: past the
+    // last step the reads fetch unused data and the loads (with an empty
+    // range) only write zeros into this wave's sink block, so every step runs
+    // the same instruction stream.
+    const bool live3 = kt + NS < nk;
+#pragma unroll
+    for (int i = 0; i < kHalfMfmas; ++i) {
+      mfma_i(f1, acc, i);
+      if (i < kFrags) read_frag(SN, 0, f0, i);
+      if (load_at(i, kLoadsLo) >= 0)
+        issue_one(args, (kt + NS) * BK, smem + S * kStage, load_at(i, kLoadsLo), live3);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // ---- K loop.  The prologue issued stages 0 .. min(NS, nk) - 1.  Ends with
+  // every load of the tile consumed; LDS reads of the last stage may still be
+  // in flight (the caller's barrier covers them).
   __device__ __forceinline__ void mainloop(const Args& args, LDS_AS char* smem,
-                                           f32x16 (&acc)[4][2]) const {
+                                           f32x16 (&acc)[4][4]) const {
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < 4; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
-    for (int kt = 0; kt < nk; ++kt) {
-      // loads of steps kt .. min(nk, kt + kDist) - 1 are in flight; keep the later ones
-      if (kDist == 2 && kt + 1 < nk) wait_loads_barrier<kLoads>();
-      else wait_loads_barrier<0>();
-      if (kt + kDist < nk) issue(args, (kt + kDist) * BK, smem + ((kt + kDist) % NS) * kStage);
-      compute(smem + (kt % NS) * kStage, acc);
-    }
+    if (nk == 0) return;
+    wait_next((nk < NS ? nk : NS) - 1);   // stage 0
+    Frags f0, f1;
+#pragma unroll
+    for (int i = 0; i < kFrags; ++i) read_frag(0, 0, f0, i);
+    for (int kt = 0; kt < nk; ++kt) step(args, smem, kt, f0, f1, acc);
   }
 
   // dphi: destination row and alpha of the tile's rows into LDS (before the
@@ -404,12 +527,15 @@ struct Tile {
     }
   }
 
-  // ---- epilogue: D[i][j] sits in lane j + 32*((i/4)%2), register (i%4) + 4*(i/8)
+  // ---- epilogue.  Accumulator block (a, b) holds D[m][n] for tile row
+  // m = wm*128 + a*32 + lane%32 and column n = wn*128 + b*32 + 8*(r/4) +
+  // 4*(lane/32) + r%4 in register r: each register quad is 4 consecutive
+  // columns, stored as one 16-byte write.  Column counts are multiples of 4,
+  // so a quad never straddles the matrix edge.
   __device__ __forceinline__ void epilogue(const Args& args, const GemmTable& tab,
                                            LDS_AS const char* prm,
-                                           const f32x16 (&acc)[4][2]) const {
+                                           const f32x16 (&acc)[4][4]) const {
     const int d_out = args.d_out, d_in = args.d_in;
-    const int fl = lane & 31;
     LDS_AS const int32_t* s_perm = reinterpret_cast<LDS_AS const int32_t*>(prm);
     LDS_AS const float* s_alpha = reinterpret_cast<LDS_AS const float*>(prm + BM * 4);
     // Split dW tiles go to their chunk's partial tile (full 256x256, row-major).
@@ -418,63 +544,73 @@ struct Tile {
       const int tile = (m0 / BM) * tab.tiles_n + n0 / BN;
       part = args.ops.partials + ((partial_base(tab, e) + (int64_t)tile * chunks + chunk) << 16);
     }
+    const int cq = 4 * (lane >> 5);   // this lane's column offset inside each group of 8
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int lrow = wm * 128 + a * 32 + i;
-        const int mrow = m0 + lrow;
-        if (IS_DW) {
-          if (part != nullptr) {
-#pragma unroll
-            for (int b = 0; b < 2; ++b) part[lrow * BN + wn * 64 + b * 32 + fl] = acc[a][b][r];
-          } else if (mrow < mrows) {
-            float* orow = args.dW + ((int64_t)e * d_out + mrow) * d_in;
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-              const int col = n0 + wn * 64 + b * 32 + fl;
-              if (col < d_in) orow[col] = acc[a][b][r];
-            }
-          }
-        } else {
-          const int32_t u = s_perm[lrow];
-          const float al = s_alpha[lrow];
-          if (u >= 0) {
-            float* orow = args.dphi + (int64_t)u * d_in;
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-              const int col = n0 + wn * 64 + b * 32 + fl;
-              if (col < d_in) orow[col] = al * acc[a][b][r];
-            }
-          }
+      const int lrow = wm * 128 + a * 32 + (lane & 31);
+      const int mrow = m0 + lrow;
+      // destination of tile column 0 of this row, and how many columns exist
+      float* orow = nullptr;
+      int ncols = d_in - n0;
+      float scale = 1.f;
+      if (IS_DW) {
+        if (part != nullptr) {
+          orow = part + lrow * BN;
+          ncols = BN;
+        } else if (mrow < mrows) {
+          orow = args.dW + ((int64_t)e * d_out + mrow) * d_in + n0;
         }
+      } else {
+        const int32_t u = s_perm[lrow];
+        scale = s_alpha[lrow];
+        if (u >= 0) orow = args.dphi + (int64_t)u * d_in + n0;
       }
+      if (orow == nullptr) continue;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = wn * 128 + b * 32 + 8 * g + cq;
+          f32x4 v = {acc[a][b][4 * g], acc[a][b][4 * g + 1], acc[a][b][4 * g + 2],
+                     acc[a][b][4 * g + 3]};
+          if (!IS_DW) v *= scale;
+          if (col < ncols) *reinterpret_cast<f32x4*>(orow + col) = v;
+        }
     }
   }
 };
 
-template <int DW_PA, int DW_PB, int DP_PA, int DP_PB, int NS>
+// LDS stages for a tile with `planes` operand planes: as many as fit in
+// 144 KiB, at most 4.
+constexpr int stages_for(int planes) {
+  return planes * 4 * kPlaneBytes <= 144 * 1024 ? 4 : planes * 3 * kPlaneBytes <= 144 * 1024 ? 3 : 2;
+}
+
+template <int DW_PA, int DW_PB, int DP_PA, int DP_PB>
 struct Cfg {
-  static constexpr int dw_bytes = NS * (DW_PA + DW_PB) * kPlaneBytes;
-  static constexpr int dp_bytes = NS * (DP_PA + DP_PB) * kPlaneBytes;
+  static constexpr int NS_DW = stages_for(DW_PA + DW_PB);
+  static constexpr int NS_DP = stages_for(DP_PA + DP_PB);
+  static constexpr int dw_bytes = NS_DW * (DW_PA + DW_PB) * kPlaneBytes;
+  static constexpr int dp_bytes = NS_DP * (DP_PA + DP_PB) * kPlaneBytes;
   static constexpr int stages = dw_bytes > dp_bytes ? dw_bytes : dp_bytes;
-  static constexpr int bytes = stages + kPermBytes + 16;
+  static constexpr int sink = stages + kPermBytes + 16;   // kWaves x 1 KiB
+  static constexpr int bytes = sink + kWaves * 1024;
 };
 
 // Persistent: one workgroup per CU drains its XCD's queue.  Between tiles the
 // next tile's first loads are issued before the finished tile's stores, so
 // the store drain overlaps the next load latency.  Every workgroup exits when
 // its queue's counter passes the queue length.
-template <int DW_PA, int DW_PB, int DP_PA, int DP_PB, int NS>
+template <int DW_PA, int DW_PB, int DP_PA, int DP_PB>
 __global__ __launch_bounds__(kThreads, 1) void grouped_backward_kernel(Args args, GemmTable tab) {
-  using C = Cfg<DW_PA, DW_PB, DP_PA, DP_PB, NS>;
-  using DwTile = Tile<true, DW_PA, DW_PB, NS>;
-  using DpTile = Tile<false, DP_PA, DP_PB, NS>;
+  using C = Cfg<DW_PA, DW_PB, DP_PA, DP_PB>;
+  using DwTile = Tile<true, DW_PA, DW_PB, C::NS_DW>;
+  using DpTile = Tile<false, DP_PA, DP_PB, C::NS_DP>;
   __shared__ __attribute__((aligned(16))) char smem_raw[C::bytes];
   LDS_AS char* smem = (LDS_AS char*)(smem_raw);
   LDS_AS char* prm = smem + C::stages;
   LDS_AS int32_t* s_next = reinterpret_cast<LDS_AS int32_t*>(prm + kPermBytes);
+  LDS_AS char* sink = smem + C::sink;
   const int x = blockIdx.x % kXcds;
   const int nitems = queue_items(tab, x);
   int32_t* head = args.ops.queue_heads + x;
@@ -491,25 +627,25 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_backward_kernel(Args args
     }
   };
 
-  f32x16 acc[4][2];
+  f32x16 acc[4][4];
   bool cur_dw;
   TileJob cur;
   if (fetch(cur_dw, cur) < 0) return;
-  if (cur_dw) DwTile(args, tab, cur).prologue(args, smem);
-  else DpTile(args, tab, cur).prologue(args, smem);
+  if (cur_dw) DwTile(args, tab, cur, smem, sink).prologue(args, smem);
+  else DpTile(args, tab, cur, smem, sink).prologue(args, smem);
   for (;;) {
-    if (cur_dw) DwTile(args, tab, cur).mainloop(args, smem, acc);
-    else DpTile(args, tab, cur).mainloop(args, smem, acc);
-    if (!cur_dw) DpTile(args, tab, cur).stage_rows(args, prm);
+    if (cur_dw) DwTile(args, tab, cur, smem, sink).mainloop(args, smem, acc);
+    else DpTile(args, tab, cur, smem, sink).mainloop(args, smem, acc);
+    if (!cur_dw) DpTile(args, tab, cur, smem, sink).stage_rows(args, prm);
     bool nxt_dw;
     TileJob nxt;
     const bool more = fetch(nxt_dw, nxt) >= 0;   // its barrier also frees every stage
     if (more) {
-      if (nxt_dw) DwTile(args, tab, nxt).prologue(args, smem);
-      else DpTile(args, tab, nxt).prologue(args, smem);
+      if (nxt_dw) DwTile(args, tab, nxt, smem, sink).prologue(args, smem);
+      else DpTile(args, tab, nxt, smem, sink).prologue(args, smem);
     }
-    if (cur_dw) DwTile(args, tab, cur).epilogue(args, tab, prm, acc);
-    else DpTile(args, tab, cur).epilogue(args, tab, prm, acc);
+    if (cur_dw) DwTile(args, tab, cur, smem, sink).epilogue(args, tab, prm, acc);
+    else DpTile(args, tab, cur, smem, sink).epilogue(args, tab, prm, acc);
     if (!more) break;
     lds_barrier();   // the perm/alpha rows are read before the next tile restages them
     cur_dw = nxt_dw;
@@ -517,14 +653,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_backward_kernel(Args args
   }
 }
 
-template <int DW_PA, int DW_PB, int DP_PA, int DP_PB, int NS>
+template <int DW_PA, int DW_PB, int DP_PA, int DP_PB>
 hipError_t launch(const Args& args, const GemmTable& tab, hipStream_t s) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
   const int blocks = (cus + kXcds - 1) / kXcds * kXcds;   // one per CU, a multiple of 8
-  hipLaunchKernelGGL((grouped_backward_kernel<DW_PA, DW_PB, DP_PA, DP_PB, NS>), dim3(blocks),
+  hipLaunchKernelGGL((grouped_backward_kernel<DW_PA, DW_PB, DP_PA, DP_PB>), dim3(blocks),
                      dim3(kThreads), 0, s, args, tab);
   return hipGetLastError();
 }
@@ -677,10 +813,10 @@ hipError_t launch_grouped_backward(const GemmTable& tab, const GemmOperands& ops
   const Args args{ops, alpha_c, perm, dW, dphi, d_out, d_in, P};
   const int key = ops.dw_pa * 1000 + ops.dw_pb * 100 + ops.dp_pa * 10 + ops.dp_pb;
   switch (key) {
-    case 1211: return launch<1, 2, 1, 1, 3>(args, tab, s);   // bf16, alpha folded into phi
-    case 2111: return launch<2, 1, 1, 1, 3>(args, tab, s);   // bf16, alpha folded into g
-    case 1111: return launch<1, 1, 1, 1, 3>(args, tab, s);   // bf16, single rounding
-    case 2222: return launch<2, 2, 2, 2, 2>(args, tab, s);   // float32 storage
+    case 1211: return launch<1, 2, 1, 1>(args, tab, s);   // bf16, alpha folded into phi
+    case 2111: return launch<2, 1, 1, 1>(args, tab, s);   // bf16, alpha folded into g
+    case 1111: return launch<1, 1, 1, 1>(args, tab, s);   // bf16, single rounding
+    case 2222: return launch<2, 2, 2, 2>(args, tab, s);   // float32 storage
     default: return hipErrorInvalidValue;
   }
 }
