@@ -5,11 +5,12 @@ per-expert top-quota select -> compaction (lrmoe_score_select_compact), then
 the fused varlen grouped GEMM for dW and dphi (lrmoe_grouped_backward).
 Inputs are resident in HBM before timing starts; outputs are preallocated.
 
-Prints ONE JSON line.  value = kept pairs per second of the whole path.
-`roofline` is for the dominant kernel, the fused grouped GEMM (HIP events
-recorded by the library around that launch, on the stream it launches on,
-over every timed step); `kernels` gives each kernel's mean time and rate;
-`cpu_baseline` times the CPU oracle on the host cores.
+Prints ONE JSON line.  value = kept pairs per second of the whole path over
+the timed steps.  `roofline` is for the dominant kernel, the fused grouped
+GEMM: HIP events recorded by the library around that launch, on the stream it
+launches on, in every timed step (the only events in the timed region).
+`kernels` gives every kernel's time and rate from a separate pass with events
+around each kernel; `cpu_baseline` times the CPU oracle on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps 1000] [--warmup 50] [--config 1]
 """
@@ -191,8 +192,6 @@ def main():
     dW = torch.empty((p.E, p.d_out, p.d_in), dtype=torch.float32, device=dev)
     ws = lrmoe.workspace(plan, dev)
     stream = torch.cuda.current_stream()
-    ssc_timer = lrmoe.KernelTimer(args.steps)
-    gb_timer = lrmoe.KernelTimer(args.steps)
     gu = p.gate_up
     if gu is not None:
         # second projection (gate/up) on the same keep set: gather its rows
@@ -205,36 +204,50 @@ def main():
                     dphi=torch.empty((p.P, gu.d_in), dtype=torch.float32, device=dev))
         dW2 = torch.empty((p.E, gu.d_out, gu.d_in), dtype=torch.float32, device=dev)
         ws2 = lrmoe.workspace(plan2, dev)
-        gu_timer = lrmoe.KernelTimer(args.steps)
-        gu_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                 for _ in range(args.steps)]
-    n_timed = [0]
 
-    def step(timed=False):
+    def step(ssc_t=None, gb_t=None, gu_t=None, gu_events=None):
         lrmoe.score_select_compact(plan, alpha, g, phi, g_row_index=row, out=out, ws=ws,
-                                   timing=ssc_timer if timed else None)
+                                   timing=ssc_t)
         lrmoe.grouped_backward(plan, out["perm"], out["alpha_c"], out["g_c"], out["phi_c"], W,
-                               dW=dW, dphi=out["dphi"], ws=ws, timing=gb_timer if timed else None)
+                               dW=dW, dphi=out["dphi"], ws=ws, timing=gb_t)
         if gu is not None:
-            if timed:
-                gu_ev[n_timed[0]][0].record(stream)
+            if gu_events is not None:
+                gu_events[0].record(stream)
             lrmoe.gather_compact(plan2, out["perm"], out["keep"], alpha, g2, x, out=out2)
-            if timed:
-                gu_ev[n_timed[0]][1].record(stream)
+            if gu_events is not None:
+                gu_events[1].record(stream)
             lrmoe.grouped_backward(plan2, out["perm"], out2["alpha_c"], out2["g_c"],
                                    out2["phi_c"], W2, dW=dW2, dphi=out2["dphi"], ws=ws2,
-                                   timing=gu_timer if timed else None)
-        if timed:
-            n_timed[0] += 1
+                                   timing=gu_t)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # Timed region: whole steps.  The only events in it bracket the dominant
+    # kernel (the grouped GEMM launch), recorded by the library on the stream
+    # it launches on; events around every kernel would add gaps to the step.
+    gemm_timer = lrmoe.KernelTimer(args.steps, slots=(1,))
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(timed=True)
+        step(gb_t=gemm_timer)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    gemm_live = stats_us(gemm_timer.durations_us(1))
+    gemm_timer.close()
+
+    # Per-kernel breakdown: a separate pass after the timed region, with HIP
+    # events around every kernel.
+    nb = min(args.steps, 200)
+    ssc_timer = lrmoe.KernelTimer(nb)
+    gb_timer = lrmoe.KernelTimer(nb)
+    if gu is not None:
+        gu_timer = lrmoe.KernelTimer(nb)
+        gu_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(nb)]
+    for i in range(nb):
+        step(ssc_timer, gb_timer, gu_timer if gu is not None else None,
+             gu_ev[i] if gu is not None else None)
+    torch.cuda.synchronize()
 
     es = 2 if p.dtype == "bf16" else 4
     P, d_o, d_i = p.P, p.d_out, p.d_in
@@ -265,9 +278,11 @@ def main():
         kernels[name] = k
     ssc_us = sum(us[n] for n in ("lrm_score", "select_scan", "gather") if us[n] is not None)
     nbytes = algorithmic_bytes(p, M)
-    gemm_tf = kernels["grouped_gemm"]["TFLOPs"]
+    gemm_tf = work["grouped_gemm"] / gemm_live["mean"] / 1e6
     roof = dict(kernel="grouped_backward_kernel", bound="mfma", achieved=gemm_tf,
                 peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s", frac=gemm_tf / MFMA_BF16_PEAK_TFLOPS,
+                launch_us_mean=gemm_live["mean"], launch_us_median=gemm_live["median"],
+                launches=gemm_live["launches"],
                 traffic=read_counters(p.name, args.dw_mode), traffic_unit="bytes per launch",
                 algorithmic_bytes_floor=gemm_floor_bytes(p, M))
     rec = {
@@ -284,9 +299,11 @@ def main():
                    "parallelism": "single GPU (one expert-parallel rank's share)"},
         "roofline": roof,
         "score_select_compact": {"us": ssc_us, "algorithmic_bytes": nbytes,
-                                 "GBps": nbytes / ssc_us / 1e3,
-                                 "hbm_frac": nbytes / ssc_us / 1e3 / HBM_PEAK_GBS},
+                                 "GBps": nbytes / ssc_us / 1e3 if ssc_us else None,
+                                 "hbm_frac": nbytes / ssc_us / 1e3 / HBM_PEAK_GBS if ssc_us else None},
         "kernels": kernels,
+        "kernels_note": f"separate pass of {nb} steps after the timed region, HIP events "
+                        "around every kernel",
     }
     if gu is not None:
         gd = stats_us([a.elapsed_time(b) * 1e3 for a, b in gu_ev])

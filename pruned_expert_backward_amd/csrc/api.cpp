@@ -461,6 +461,7 @@ lrmoe_status lrmoe_grouped_backward_timed(const lrmoe_problem* pb, const int32_t
   LRMOE_TRY(mark(timing, false, 0, s));
   char* ws = reinterpret_cast<char*>(workspace);
   auto plane = [&](size_t off) { return reinterpret_cast<uint16_t*>(ws + off); };
+  int32_t* heads = reinterpret_cast<int32_t*>(ws + wl.heads);
   GemmOperands ops;
   memset(&ops, 0, sizeof(ops));
   const uint16_t* g16 = reinterpret_cast<const uint16_t*>(g_c);
@@ -472,7 +473,7 @@ lrmoe_status lrmoe_grouped_backward_timed(const lrmoe_problem* pb, const int32_t
     uint16_t* lo = exact ? plane(wl.b_lo) : nullptr;
     const void* src = wl.alpha_on_phi ? phi_c : g_c;
     const int cols = wl.alpha_on_phi ? d_in : d_out;
-    LRMOE_TRY(hip_status(launch_split(LRMOE_BF16, src, M, cols, alpha_c, hi, lo, s)));
+    LRMOE_TRY(hip_status(launch_split(LRMOE_BF16, src, M, cols, alpha_c, hi, lo, s, heads, kXcds)));
     if (wl.alpha_on_phi) {
       ops.dw_a[0] = g16;
       ops.dw_b[0] = hi;
@@ -489,7 +490,7 @@ lrmoe_status lrmoe_grouped_backward_timed(const lrmoe_problem* pb, const int32_t
     ops.dp_pa = ops.dp_pb = 1;
   } else {
     LRMOE_TRY(hip_status(launch_split(LRMOE_F32, g_c, M, d_out, nullptr, plane(wl.a_hi),
-                                      plane(wl.a_lo), s)));
+                                      plane(wl.a_lo), s, heads, kXcds)));
     LRMOE_TRY(hip_status(launch_split(LRMOE_F32, phi_c, M, d_in, alpha_c, plane(wl.b_hi),
                                       plane(wl.b_lo), s)));
     if (dphi != nullptr)
@@ -506,8 +507,7 @@ lrmoe_status lrmoe_grouped_backward_timed(const lrmoe_problem* pb, const int32_t
   (void)w16;
   LRMOE_TRY(mark(timing, true, 0, s));
   ops.partials = reinterpret_cast<float*>(ws + wl.partials);
-  ops.queue_heads = reinterpret_cast<int32_t*>(ws + wl.heads);
-  LRMOE_TRY(hip_status(launch_zero(ops.queue_heads, kXcds, s)));
+  ops.queue_heads = heads;   // cleared by the first prologue launch
   LRMOE_TRY(mark(timing, false, 1, s));
   LRMOE_TRY(hip_status(launch_grouped_backward(t, ops, perm, alpha_c, dW, dphi, d_out, d_in,
                                                (int32_t)pb->P, s)));

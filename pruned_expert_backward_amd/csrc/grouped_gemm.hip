@@ -721,7 +721,10 @@ template <bool F32>
 __global__ __launch_bounds__(256) void split_kernel(const void* __restrict__ src, int64_t rows,
                                                     int32_t cols, const float* __restrict__ alpha,
                                                     uint16_t* __restrict__ hi,
-                                                    uint16_t* __restrict__ lo) {
+                                                    uint16_t* __restrict__ lo,
+                                                    int32_t* __restrict__ zero, int nzero) {
+  // also clears the grouped GEMM's work-queue counters (saves a launch)
+  if (blockIdx.x == 0 && (int)threadIdx.x < nzero) zero[threadIdx.x] = 0;
   const int64_t quads = rows * (cols / 4);
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int qpr = cols / 4;   // 4-element groups per row
@@ -780,17 +783,18 @@ hipError_t launch_zero(int32_t* p, int n, hipStream_t s) {
 }
 
 hipError_t launch_split(int src_dtype, const void* src, int64_t rows, int32_t cols,
-                        const float* alpha, uint16_t* hi, uint16_t* lo, hipStream_t s) {
+                        const float* alpha, uint16_t* hi, uint16_t* lo, hipStream_t s,
+                        int32_t* zero, int nzero) {
   const int64_t quads = rows * (cols / 4);
-  if (quads <= 0) return hipSuccess;
+  if (quads <= 0) return nzero > 0 ? launch_zero(zero, nzero, s) : hipSuccess;
   int64_t blocks = (quads / 2 + 255) / 256 + 1;
   if (blocks > 256 * 16) blocks = 256 * 16;
   if (src_dtype == LRMOE_F32)
     hipLaunchKernelGGL(split_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, src, rows,
-                       cols, alpha, hi, lo);
+                       cols, alpha, hi, lo, zero, nzero);
   else
     hipLaunchKernelGGL(split_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, src, rows,
-                       cols, alpha, hi, lo);
+                       cols, alpha, hi, lo, zero, nzero);
   return hipGetLastError();
 }
 

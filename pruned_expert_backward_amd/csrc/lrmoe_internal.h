@@ -105,7 +105,8 @@ hipError_t launch_gather(int dtype, const int32_t* perm, const uint8_t* keep,
 // hi (and lo, if non-null) bf16 planes of alpha[row] * src[row][col] (alpha
 // may be null); src is bf16 or float32 storage.
 hipError_t launch_split(int src_dtype, const void* src, int64_t rows, int32_t cols,
-                        const float* alpha, uint16_t* hi, uint16_t* lo, hipStream_t s);
+                        const float* alpha, uint16_t* hi, uint16_t* lo, hipStream_t s,
+                        int32_t* zero = nullptr, int nzero = 0);
 
 // Zeroes n int32 counters (a fill kernel, safe inside captured graphs).
 hipError_t launch_zero(int32_t* p, int n, hipStream_t s);

@@ -269,7 +269,9 @@ class KernelTimer:
     set of slots.  After synchronising, mean_us(slot) is the mean duration of
     that kernel over the calls that launched it."""
 
-    def __init__(self, calls: int):
+    def __init__(self, calls: int, slots=None):
+        """slots: the timing slots to record (default all); the library skips
+        the others, so they cost nothing."""
         self._hip = C.CDLL("libamdhip64.so")
         self._hip.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
         self._hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
@@ -279,6 +281,8 @@ class KernelTimer:
         for _ in range(calls):
             t = Timing()
             for k in range(TIMING_SLOTS):
+                if slots is not None and k not in slots:
+                    continue
                 for arr in (t.before, t.after):
                     ev = C.c_void_p()
                     if self._hip.hipEventCreate(C.byref(ev)) != 0:
@@ -295,6 +299,8 @@ class KernelTimer:
     def durations_us(self, slot: int) -> list:
         out = []
         for t in self.timings[:self._next]:
+            if not t.before[slot]:
+                continue
             ms = C.c_float()
             # hipEventElapsedTime fails for events that were never recorded
             if self._hip.hipEventElapsedTime(C.byref(ms), t.before[slot], t.after[slot]) == 0:
@@ -308,8 +314,10 @@ class KernelTimer:
     def close(self):
         for t in self.timings:
             for k in range(TIMING_SLOTS):
-                self._hip.hipEventDestroy(t.before[k])
-                self._hip.hipEventDestroy(t.after[k])
+                if t.before[k]:
+                    self._hip.hipEventDestroy(t.before[k])
+                if t.after[k]:
+                    self._hip.hipEventDestroy(t.after[k])
         self.timings = []
 
 
