@@ -67,6 +67,12 @@ lrmoe_status check_problem(const lrmoe_problem* pb, Checked& c) {
   if (P != pb->P) return LRMOE_ERR_SHAPE;
   c.tab.pair_off[pb->E] = (int32_t)P;
   c.tab.seg_off[pb->E] = (int32_t)M;
+  int32_t hc = 0;
+  for (int e = 0; e < pb->E; ++e) {
+    c.tab.hist_off[e] = hc;
+    hc += hist_chunks(pb->counts[e]);
+  }
+  c.tab.hist_off[pb->E] = hc;
   c.tab.M = (int32_t)M;
   c.M = M;
   return LRMOE_OK;
@@ -145,8 +151,14 @@ GemmWorkspace gemm_workspace(const lrmoe_problem* pb, int64_t M) {
   return w;
 }
 
+// Selection: one kHistBins-bin histogram per chunk of a large expert.
+size_t select_workspace(const Checked& c) {
+  return (size_t)c.tab.hist_off[c.tab.E] * kHistBins * sizeof(uint32_t);
+}
+
 size_t workspace_bytes(const lrmoe_problem* pb, const Checked& c) {
-  return gemm_workspace(pb, c.M).total;
+  const size_t g = gemm_workspace(pb, c.M).total, sel = select_workspace(c);
+  return g > sel ? g : sel;
 }
 
 // Group shape gm x gn (gm * gn = kGroupSlots) over an expert's tile grid with
@@ -207,8 +219,11 @@ lrmoe_status select_compact(const lrmoe_problem* pb, bool compute_scores, const 
   LRMOE_TRY(need(phi_c, M));
   LRMOE_TRY(need(alpha_c, M));
   LRMOE_TRY(optional(dphi_zero));
-  (void)workspace;   // selection and compaction need no workspace
-  (void)ws_bytes;
+  const size_t ws_need = select_workspace(c);   // 0 unless an expert is large
+  if (ws_need > 0) {
+    LRMOE_TRY(need(workspace, 1));
+    if (ws_bytes < ws_need) return LRMOE_ERR_WORKSPACE;
+  }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const float* scores = scores_in;
   if (compute_scores) {
@@ -219,7 +234,8 @@ lrmoe_status select_compact(const lrmoe_problem* pb, bool compute_scores, const 
     scores = scores_out;
   }
   LRMOE_TRY(mark(timing, false, 1, s));
-  LRMOE_TRY(hip_status(launch_select_scan(c.tab, scores, keep, perm, seg_offsets, s)));
+  LRMOE_TRY(hip_status(launch_select_scan(c.tab, scores, keep, perm, seg_offsets,
+                                          reinterpret_cast<uint32_t*>(workspace), s)));
   LRMOE_TRY(mark(timing, true, 1, s));
   LRMOE_TRY(mark(timing, false, 2, s));
   LRMOE_TRY(hip_status(launch_gather(pb->dtype, perm, keep, g_row_index, nullptr, alpha, g, phi,

@@ -14,12 +14,26 @@ constexpr int kMaxE = LRMOE_MAX_EXPERTS;
 // Per-expert offsets, known on the host before the backward starts (the
 // quotas are fixed ahead of it), passed to kernels by value so that no
 // host-to-device copy or device-side prefix sum is needed.
+// Selection: experts with more pairs than fit in the select kernel's LDS key
+// cache get their first radix digit counted by many workgroups, one per
+// chunk of kHistChunk pairs, each writing a kHistBins-bin histogram to the
+// workspace.
+constexpr int kSelLdsKeys = 24576;
+constexpr int kHistChunk = 16384;
+constexpr int kHistBins = 4096;
+
 struct ExpertTable {
   int32_t E;
   int32_t M;                      // total kept pairs
   int32_t pair_off[kMaxE + 1];    // first pair of expert e (expert-sorted)
   int32_t seg_off[kMaxE + 1];     // first compacted row of expert e
+  int32_t hist_off[kMaxE + 1];    // first histogram chunk of expert e (large experts only)
 };
+
+// Histogram chunks of expert e (0 unless it has more than kSelLdsKeys pairs).
+inline int hist_chunks(int64_t n) {
+  return n > kSelLdsKeys ? (int)((n + kHistChunk - 1) / kHistChunk) : 0;
+}
 
 // Tile schedule of the grouped GEMMs (host-built, by value).  Output tiles
 // are kTile x kTile.  Tiles are handed out in groups of kGroupSlots slots
@@ -94,7 +108,8 @@ hipError_t launch_score(int dtype, const void* g, const void* phi, const float* 
                         float* scores, hipStream_t s);
 
 hipError_t launch_select_scan(const ExpertTable& tab, const float* scores, uint8_t* keep,
-                              int32_t* perm, int32_t* seg_offsets_out, hipStream_t s);
+                              int32_t* perm, int32_t* seg_offsets_out, uint32_t* hist,
+                              hipStream_t s);
 
 hipError_t launch_gather(int dtype, const int32_t* perm, const uint8_t* keep,
                          const int32_t* g_row_index, const int32_t* phi_row_index,

@@ -12,11 +12,15 @@
 // select (12 + 12 + 8-bit digits) on an order-preserving integer image of the
 // float32 scores to find the q_e-th largest key tau_e and how many keys equal
 // to tau_e are still needed; ties go to the lower pair index.  Keys of experts
-// up to 24576 pairs are cached in LDS; for larger experts only the keys in the
-// first digit's bin are gathered into LDS for the later digits.  The same
+// up to 24576 pairs are cached in LDS.  For larger experts the first digit is
+// counted by many workgroups at once (select_hist_kernel, one per 16384-pair
+// chunk, histograms in the workspace), and only the keys in that digit's bin
+// are gathered into LDS for the later digits.  The same
 // workgroup then scans the expert's pairs in index order (8 consecutive keys
 // per thread, one workgroup prefix sum per 8192 keys), writes the keep flags
 // and the compacted permutation (ascending pair index inside the segment).
+// Global score reads are 16-byte vectors from an aligned start (a single
+// workgroup's bandwidth is bounded by its vector memory instructions).
 #include "lrmoe_internal.h"
 
 namespace lrmoe {
@@ -101,10 +105,13 @@ __device__ __forceinline__ uint32_t score_key(float s) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kSelLdsKeys = 24576;   // 96 KiB: keys of one expert, or first-digit candidates
-constexpr int kBins = 4096;          // first and second digits: 12 bits; last digit: 8 bits
+// kSelLdsKeys (96 KiB): keys of one expert, or first-digit candidates
+constexpr int kBins = kHistBins;     // first and second digits: 12 bits; last digit: 8 bits
+constexpr int kHistPer = kHistChunk / kSelThreads;   // keys per thread in a histogram chunk
 constexpr int kScanPer = 8;          // keys per thread per scan tile
 constexpr int kScanTile = kSelThreads * kScanPer;
 
@@ -168,22 +175,62 @@ __device__ __forceinline__ Digit find_digit(const uint32_t* hist, int nbins, uin
   return d;
 }
 
+// First-digit (key bits 31..20) histogram of one kHistChunk-pair chunk of a
+// large expert, written to hist[chunk][kBins].
+__global__ __launch_bounds__(kSelThreads) void select_hist_kernel(
+    ExpertTable tab, const float* __restrict__ scores, uint32_t* __restrict__ hist_out) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  int e = 0;
+  while (e + 1 < tab.E && tab.hist_off[e + 1] <= b) ++e;   // chunk b belongs to expert e
+  const int lo = tab.pair_off[e] + (b - tab.hist_off[e]) * kHistChunk;
+  const int hi = min(lo + kHistChunk, tab.pair_off[e + 1]);
+  for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0;
+  __syncthreads();
+  float v[kHistPer];
+#pragma unroll
+  for (int j = 0; j < kHistPer; ++j) {
+    const int i = lo + j * kSelThreads + tid;
+    v[j] = i < hi ? scores[i] : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < kHistPer; ++j)
+    if (lo + j * kSelThreads + tid < hi) atomicAdd(&hist[score_key(v[j]) >> 20], 1u);
+  __syncthreads();
+  reinterpret_cast<u32x4*>(hist_out + (size_t)b * kBins)[tid] =
+      reinterpret_cast<const u32x4*>(hist)[tid];
+}
+
+// Scores [a, a + 4) for a multiple of 4 (the score array is 16-byte
+// aligned), zeros past its end P.
+__device__ __forceinline__ float4 load4(const float* __restrict__ scores, int a, int P) {
+  if (a + 4 <= P) return *reinterpret_cast<const float4*>(scores + a);
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (a < P) v.x = scores[a];
+  if (a + 1 < P) v.y = scores[a + 1];
+  if (a + 2 < P) v.z = scores[a + 2];
+  return v;
+}
+
 __global__ __launch_bounds__(kSelThreads) void select_scan_kernel(
     ExpertTable tab, const float* __restrict__ scores, uint8_t* __restrict__ keep,
-    int32_t* __restrict__ perm, int32_t* __restrict__ seg_offsets_out) {
+    int32_t* __restrict__ perm, int32_t* __restrict__ seg_offsets_out,
+    const uint32_t* __restrict__ hist_in) {
   __shared__ uint32_t keys_lds[kSelLdsKeys];   // the expert's keys, or the candidates
-  __shared__ uint32_t hist[kBins];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
   __shared__ uint32_t wsum[kSelWaves];
   __shared__ uint32_t cand_n;
   __shared__ Digit dig;
 
   const int e = blockIdx.x;
   const int tid = threadIdx.x;
+  const int P = tab.pair_off[tab.E];
   const int base = tab.pair_off[e];
-  const int n = tab.pair_off[e + 1] - base;
+  const int end = tab.pair_off[e + 1];
+  const int n = end - base;
+  const int gbeg = base & ~3;   // 16-byte aligned start for vector reads of global scores
   const int seg = tab.seg_off[e];
   const uint32_t q = (uint32_t)(tab.seg_off[e + 1] - seg);
-  const float* __restrict__ src = scores + base;
 
   if (tid == 0) {
     seg_offsets_out[e] = seg;
@@ -192,16 +239,13 @@ __global__ __launch_bounds__(kSelThreads) void select_scan_kernel(
   if (n == 0) return;
   const bool cached = n <= kSelLdsKeys;
   if (cached) {
-    int i = tid;
-    for (; i + 3 * kSelThreads < n; i += 4 * kSelThreads) {
-      const float a = src[i], b = src[i + kSelThreads], c = src[i + 2 * kSelThreads],
-                  d = src[i + 3 * kSelThreads];
-      keys_lds[i] = score_key(a);
-      keys_lds[i + kSelThreads] = score_key(b);
-      keys_lds[i + 2 * kSelThreads] = score_key(c);
-      keys_lds[i + 3 * kSelThreads] = score_key(d);
+    for (int a = gbeg + 4 * tid; a < end; a += 4 * kSelThreads) {
+      const float4 v = load4(scores, a, P);
+      const float x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (a + j >= base && a + j < end) keys_lds[a + j - base] = score_key(x[j]);
     }
-    for (; i < n; i += kSelThreads) keys_lds[i] = score_key(src[i]);
     __syncthreads();
   }
 
@@ -209,22 +253,17 @@ __global__ __launch_bounds__(kSelThreads) void select_scan_kernel(
   // tau = the q-th largest key; need = how many keys equal to tau are kept.
   uint32_t tau = 0xFFFFFFFFu, need = 0;   // q == 0: no key is above or equal
   if (q > 0) {
-    // digit 1 (key bits 31..20) over every key
-    for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0;
-    __syncthreads();
+    // digit 1 (key bits 31..20) over every key: counted here from the LDS
+    // cache, or summed from the chunk histograms of select_hist_kernel
     if (cached) {
+      for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0;
+      __syncthreads();
       for (int i = tid; i < n; i += kSelThreads) atomicAdd(&hist[keys_lds[i] >> 20], 1u);
     } else {
-      int i = tid;
-      for (; i + 3 * kSelThreads < n; i += 4 * kSelThreads) {
-        const float a = src[i], b = src[i + kSelThreads], c = src[i + 2 * kSelThreads],
-                    d = src[i + 3 * kSelThreads];
-        atomicAdd(&hist[score_key(a) >> 20], 1u);
-        atomicAdd(&hist[score_key(b) >> 20], 1u);
-        atomicAdd(&hist[score_key(c) >> 20], 1u);
-        atomicAdd(&hist[score_key(d) >> 20], 1u);
-      }
-      for (; i < n; i += kSelThreads) atomicAdd(&hist[score_key(src[i]) >> 20], 1u);
+      u32x4 h = {0u, 0u, 0u, 0u};
+      for (int c = tab.hist_off[e]; c < tab.hist_off[e + 1]; ++c)
+        h += reinterpret_cast<const u32x4*>(hist_in + (size_t)c * kBins)[tid];
+      reinterpret_cast<u32x4*>(hist)[tid] = h;   // kSelThreads * 4 == kBins
     }
     __syncthreads();
     Digit d1 = find_digit(hist, kBins, q, wsum, &dig);
@@ -234,16 +273,28 @@ __global__ __launch_bounds__(kSelThreads) void select_scan_kernel(
     // Remaining digits look only at keys whose top bits equal `prefix`: the
     // cached keys, or (large experts) the first-digit candidates collected
     // into LDS, or -- if there are too many of those -- all keys again.
-    const uint32_t* list = keys_lds;
     int nlist = n;
     bool from_global = false;
     if (!cached) {
       if (d1.count <= (uint32_t)kSelLdsKeys) {
         if (tid == 0) cand_n = 0;
         __syncthreads();
-        for (int i = tid; i < n; i += kSelThreads) {
-          const uint32_t key = score_key(src[i]);
-          if ((key >> 20) == d1.digit) keys_lds[atomicAdd(&cand_n, 1u)] = key;
+        // four 16-byte loads in flight per thread: one workgroup streams the expert
+        for (int a0 = gbeg; a0 < end; a0 += 16 * kSelThreads) {
+          float4 v[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[j] = load4(scores, a0 + 4 * (j * kSelThreads + tid), P);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int a = a0 + 4 * (j * kSelThreads + tid);
+            const float x[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const uint32_t key = score_key(x[t]);
+              if (a + t >= base && a + t < end && (key >> 20) == d1.digit)
+                keys_lds[atomicAdd(&cand_n, 1u)] = key;
+            }
+          }
         }
         __syncthreads();
         nlist = (int)d1.count;   // == cand_n
@@ -252,7 +303,7 @@ __global__ __launch_bounds__(kSelThreads) void select_scan_kernel(
       }
     }
     auto list_key = [&](int i) -> uint32_t {
-      return from_global ? score_key(src[i]) : list[i];
+      return from_global ? score_key(scores[base + i]) : keys_lds[i];
     };
     // digit 2 (bits 19..8), then digit 3 (bits 7..0)
 #pragma unroll 1
@@ -276,18 +327,39 @@ __global__ __launch_bounds__(kSelThreads) void select_scan_kernel(
   }
 
   // ---- stable scan in pair order: keep = key > tau, or key == tau among
-  // the first `need` of those.  Thread t owns 8 consecutive keys of a tile;
-  // one workgroup scan of (#gt, #eq) per tile gives every position.
+  // the first `need` of those.  Tiles start at the aligned index gbeg; thread
+  // t owns 8 consecutive pairs of a tile (those outside the expert are
+  // skipped); one workgroup scan of (#gt, #eq) per tile gives every
+  // position.  The next tile's loads go out before this tile is scanned.
   uint32_t run_gt = 0, run_eq = 0;
-  for (int c0 = 0; c0 < n; c0 += kScanTile) {
-    const int i0 = c0 + tid * kScanPer;
-    uint32_t key[kScanPer];
+  auto load_tile = [&](int c, uint32_t (&kk)[kScanPer]) {
+    const int g0 = c + tid * kScanPer;
+    if (cached) {
+#pragma unroll
+      for (int j = 0; j < kScanPer; ++j) {
+        const int g = g0 + j;
+        kk[j] = (g >= base && g < end) ? keys_lds[g - base] : 0u;
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < kScanPer / 4; ++h) {
+        const float4 v = load4(scores, g0 + 4 * h, P);
+        kk[4 * h] = score_key(v.x);
+        kk[4 * h + 1] = score_key(v.y);
+        kk[4 * h + 2] = score_key(v.z);
+        kk[4 * h + 3] = score_key(v.w);
+      }
+    }
+  };
+  uint32_t key[kScanPer], key_next[kScanPer];
+  load_tile(gbeg, key);
+  for (int c = gbeg; c < end; c += kScanTile) {
+    const int g0 = c + tid * kScanPer;
+    if (c + kScanTile < end) load_tile(c + kScanTile, key_next);
     uint32_t ngt = 0, neq = 0;
 #pragma unroll
     for (int j = 0; j < kScanPer; ++j) {
-      const int i = i0 + j;
-      key[j] = i < n ? (cached ? keys_lds[i] : score_key(src[i])) : 0u;
-      const bool ok = i < n;
+      const bool ok = g0 + j >= base && g0 + j < end;
       ngt += (ok && key[j] > tau) ? 1u : 0u;
       neq += (ok && key[j] == tau) ? 1u : 0u;
     }
@@ -299,22 +371,40 @@ __global__ __launch_bounds__(kSelThreads) void select_scan_kernel(
     // kept keys before this thread: every greater key, and the equal keys
     // among the first `need` equal ones
     uint32_t pos = gt_before + (eq_before < need ? eq_before : need);
+    uint32_t kept_bits = 0, valid_bits = 0;
 #pragma unroll
     for (int j = 0; j < kScanPer; ++j) {
-      const int i = i0 + j;
-      if (i < n) {
+      const int g = g0 + j;
+      if (g >= base && g < end) {
         const bool gt = key[j] > tau, eq = key[j] == tau;
         const bool kp = gt || (eq && eq_before < need);
         eq_before += eq ? 1u : 0u;
-        keep[base + i] = kp ? 1 : 0;
+        valid_bits |= 1u << j;
+        kept_bits |= (kp ? 1u : 0u) << j;
         if (kp) {
-          if (pos < q) perm[seg + pos] = base + i;   // pos < q holds by construction
+          if (pos < q) perm[seg + pos] = g;   // pos < q holds by construction
           ++pos;
         }
       }
     }
+    // keep flags: whole 4-byte groups at once when the expert owns all four
+#pragma unroll
+    for (int h = 0; h < kScanPer / 4; ++h) {
+      const uint32_t vb = (valid_bits >> (4 * h)) & 15u, kb = (kept_bits >> (4 * h)) & 15u;
+      const int g = g0 + 4 * h;
+      if (vb == 15u) {
+        *reinterpret_cast<uint32_t*>(keep + g) =
+            (kb & 1u) | ((kb & 2u) << 7) | ((kb & 4u) << 14) | ((kb & 8u) << 21);
+      } else if (vb != 0u) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          if (vb & (1u << t)) keep[g + t] = (kb >> t) & 1u;
+      }
+    }
     run_gt += tot >> 16;
     run_eq += tot & 0xFFFFu;
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) key[j] = key_next[j];
   }
 }
 
@@ -337,9 +427,17 @@ hipError_t launch_score(int dtype, const void* g, const void* phi, const float* 
 }
 
 hipError_t launch_select_scan(const ExpertTable& tab, const float* scores, uint8_t* keep,
-                              int32_t* perm, int32_t* seg_offsets_out, hipStream_t s) {
+                              int32_t* perm, int32_t* seg_offsets_out, uint32_t* hist,
+                              hipStream_t s) {
+  const int chunks = tab.hist_off[tab.E];
+  if (chunks > 0) {
+    hipLaunchKernelGGL(select_hist_kernel, dim3(chunks), dim3(kSelThreads), 0, s, tab, scores,
+                       hist);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   hipLaunchKernelGGL(select_scan_kernel, dim3(tab.E), dim3(kSelThreads), 0, s, tab, scores,
-                     keep, perm, seg_offsets_out);
+                     keep, perm, seg_offsets_out, hist);
   return hipGetLastError();
 }
 

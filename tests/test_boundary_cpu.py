@@ -148,6 +148,22 @@ def test_workspace_size_and_check():
     assert p1.workspace_bytes() == plane + 256
 
 
+def test_select_workspace_for_large_experts():
+    """An expert with more than 24576 pairs gets its first radix digit counted
+    by one workgroup per 16384-pair chunk, into 16 KiB histograms in the
+    workspace: the selection calls then need that much workspace."""
+    counts, quotas = (60000, 24576, 100), (48000, 19660, 80)
+    p = plan(counts=counts, quotas=quotas, d_out=8, d_in=8)
+    hist = ((60000 + 16383) // 16384) * 4096 * 4   # only the first expert is large
+    n = p.workspace_bytes()
+    assert n >= hist
+    assert sscc(p, ws=FAKE, ws_bytes=hist - 1) == 6
+    assert sscc(p, ws=None, ws_bytes=hist) == 1
+    assert sscc(p, ws=FAKE + 4, ws_bytes=hist) == 4
+    # no large expert: the selection needs no workspace at all
+    assert sscc(plan(counts=(24576, 10), quotas=(10, 5), d_out=8, d_in=8), alpha=None) == 1
+
+
 def test_grouped_backward_validation():
     p = plan()
     f = L.lib().lrmoe_grouped_backward
