@@ -123,8 +123,9 @@ GemmWorkspace gemm_workspace(const lrmoe_problem* pb, int64_t M) {
     w.total = w.w_lo + wpl;
     w.dw_pa = w.dw_pb = w.dp_pa = w.dp_pb = 2;
   }
-  // K chunk: about two work items per CU, counting MFMA passes of both
-  // products, and never under 1024 rows (fewer partial tiles).
+  // K chunk: about one CU's share of the MFMA work (both products) per dW
+  // tile chunk, and never under 1024 rows (fewer partial tiles); the many
+  // shorter tiles fill in around the long ones.
   const int terms_dw = 1 + (w.dw_pa == 2) + (w.dw_pb == 2);
   const int terms_dp = 1 + (w.dp_pa == 2) + (w.dp_pb == 2);
   const int64_t tiles_n = (pb->d_in + kTile - 1) / kTile;
@@ -136,7 +137,7 @@ GemmWorkspace gemm_workspace(const lrmoe_problem* pb, int64_t M) {
   }
   const int64_t units = tiles_m * tiles_n * rows_steps * terms_dw +
                         tiles_n * mtiles * ((pb->d_out + kStepK - 1) / kStepK) * terms_dp;
-  int64_t kc = units / (256 * 2) * kStepK / terms_dw;
+  int64_t kc = units / 256 * kStepK / terms_dw;
   if (kc < 1024) kc = 1024;
   kc = (kc + kStepK - 1) / kStepK * kStepK;
   if (kc > (int64_t(1) << 30)) kc = int64_t(1) << 30;
