@@ -612,19 +612,28 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_backward_kernel(Args args
   LDS_AS int32_t* s_next = reinterpret_cast<LDS_AS int32_t*>(prm + kPermBytes);
   LDS_AS char* sink = smem + C::sink;
   const int x = blockIdx.x % kXcds;
-  const int nitems = queue_items(tab, x);
-  int32_t* head = args.ops.queue_heads + x;
+  int qx = x;   // the queue this workgroup currently drains
 
-  // Next valid item of this XCD's queue (idle slots skipped); -1 when done.
+  // Next valid item (idle slots skipped): from this XCD's queue, then --
+  // once that is exhausted -- from the other XCDs' queues in turn, so that no
+  // CU idles while another XCD still has tiles.  -1 when every queue is done.
+  // A stolen tile loses the L2 locality of its group, which only matters at
+  // the end of the launch.
   auto fetch = [&](bool& is_dw, TileJob& job) -> int {
-    for (;;) {
-      if (threadIdx.x == 0) s_next[0] = atomicAdd(head, 1);
+    for (int hop = 0; hop < kXcds;) {
+      const int nit = queue_items(tab, qx);
+      if (threadIdx.x == 0) s_next[0] = atomicAdd(args.ops.queue_heads + qx, 1);
       lds_barrier();
       const int i = __builtin_amdgcn_readfirstlane(s_next[0]);
       lds_barrier();   // everyone has read s_next before it is rewritten
-      if (i >= nitems) return -1;
-      if (decode(tab, x, i, is_dw, job)) return i;
+      if (i >= nit) {   // this queue is exhausted: move to the next XCD's
+        qx = qx + 1 == kXcds ? 0 : qx + 1;
+        ++hop;
+        continue;
+      }
+      if (decode(tab, qx, i, is_dw, job)) return i;
     }
+    return -1;
   };
 
   f32x16 acc[4][4];
