@@ -37,14 +37,16 @@ COUNTERS_FILE = "profiles/grouped_backward_kernel.qwen3-down-c20.counters.txt"
 COPY_BYTES = 1 << 30           # plain copy used to calibrate FETCH_SIZE / WRITE_SIZE
 
 
-def algorithmic_bytes(p, M):
+def algorithmic_bytes(p, M, score_mode="lrm"):
     """Bytes the method must move in score + select + compaction (each row
     read or written once): score reads every g and phi row plus alpha and
-    writes R; select reads R and writes the keep flag; compaction reads and
-    writes the kept rows, alpha and perm, and zeroes dropped dphi rows."""
+    writes R (gradient-only rules: g rows only; given random scores: none);
+    select reads R and writes the keep flag; compaction reads and writes the
+    kept rows, alpha and perm, and zeroes dropped dphi rows."""
     es = 2 if p.dtype == "bf16" else 4
     P = p.P
-    score = P * (es * (p.d_out + p.d_in) + 8)
+    score = {"lrm": P * (es * (p.d_out + p.d_in) + 8),
+             "random": 0}.get(score_mode, P * (es * p.d_out + 4))
     select = P * 5
     compact = M * (2 * es * (p.d_out + p.d_in) + 12) + (P - M) * 4 * p.d_in
     return score + select + compact
@@ -154,6 +156,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=1)
     ap.add_argument("--dw-mode", choices=["exact", "bf16"], default="exact")
+    ap.add_argument("--score-mode", choices=["lrm", "grad-sqnorm", "grad-l1", "random"],
+                    default="lrm", help="scoring rule (the method, or an ablation baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
@@ -179,7 +183,9 @@ def main():
     torch.cuda.set_device(dev)
     dtc = lrmoe.BF16 if p.dtype == "bf16" else lrmoe.F32
     mode = lrmoe.DW_EXACT if args.dw_mode == "exact" else lrmoe.DW_BF16
-    plan = lrmoe.Plan(p.counts, q, p.d_out, p.d_in, dtc, T=p.T, dw_mode=mode)
+    smode = {"lrm": lrmoe.SCORE_LRM, "grad-sqnorm": lrmoe.SCORE_GRAD_SQNORM,
+             "grad-l1": lrmoe.SCORE_GRAD_L1, "random": lrmoe.SCORE_LRM}[args.score_mode]
+    plan = lrmoe.Plan(p.counts, q, p.d_out, p.d_in, dtc, T=p.T, dw_mode=mode, score_mode=smode)
 
     def d(a):
         if a is None:
@@ -205,9 +211,15 @@ def main():
         dW2 = torch.empty((p.E, gu.d_out, gu.d_in), dtype=torch.float32, device=dev)
         ws2 = lrmoe.workspace(plan2, dev)
 
+    given_scores = None
+    if args.score_mode == "random":   # random dropping: seeded scores drawn once, as input
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(2024)
+        given_scores = torch.rand(p.P, generator=gen, device=dev, dtype=torch.float32)
+
     def step(ssc_t=None, gb_t=None, gu_t=None, gu_events=None):
         lrmoe.score_select_compact(plan, alpha, g, phi, g_row_index=row, out=out, ws=ws,
-                                   timing=ssc_t)
+                                   scores=given_scores, timing=ssc_t)
         lrmoe.grouped_backward(plan, out["perm"], out["alpha_c"], out["g_c"], out["phi_c"], W,
                                dW=dW, dphi=out["dphi"], ws=ws, timing=gb_t)
         if gu is not None:
@@ -259,7 +271,9 @@ def main():
             "splitk_reduce": stats_us(gb_timer.durations_us(2))}
     us = {k: (v["mean"] if v else None) for k, v in dist.items()}
     # algorithmic bytes (HBM-bound kernels) and FLOP (the GEMM) per launch
-    work = {"lrm_score": P * (es * (d_o + d_i) + 8),
+    score_bytes = (P * (es * (d_o + d_i) + 8) if args.score_mode == "lrm"
+                   else P * (es * d_o + 4))   # gradient-only rules read no phi, no alpha
+    work = {"lrm_score": score_bytes,
             "select_scan": P * 5,
             "gather": M * (2 * es * (d_o + d_i) + 12) + (P - M) * 4 * d_i,
             "grouped_gemm": gemm_flops(p, M)}
@@ -277,7 +291,7 @@ def main():
                      hbm_frac=work[name] / t / 1e3 / HBM_PEAK_GBS)
         kernels[name] = k
     ssc_us = sum(us[n] for n in ("lrm_score", "select_scan", "gather") if us[n] is not None)
-    nbytes = algorithmic_bytes(p, M)
+    nbytes = algorithmic_bytes(p, M, args.score_mode)
     gemm_tf = work["grouped_gemm"] / gemm_live["mean"] / 1e6
     roof = dict(kernel="grouped_backward_kernel", bound="mfma", achieved=gemm_tf,
                 peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s", frac=gemm_tf / MFMA_BF16_PEAK_TFLOPS,
@@ -296,6 +310,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": p.name, "P": p.P, "E": p.E, "d_out": p.d_out, "d_in": p.d_in,
                    "kept_pairs": M, "policy": list(p.policy), "dw_mode": args.dw_mode,
+                   "score_mode": args.score_mode,
                    "parallelism": "single GPU (one expert-parallel rank's share)"},
         "roofline": roof,
         "score_select_compact": {"us": ssc_us, "algorithmic_bytes": nbytes,

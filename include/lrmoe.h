@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define LRMOE_ABI_VERSION 1
+#define LRMOE_ABI_VERSION 2
 #define LRMOE_MAX_EXPERTS 256
 
 typedef enum {
@@ -97,6 +97,21 @@ typedef struct {
  * always splits both operands (three bf16 passes). */
 typedef enum { LRMOE_DW_EXACT = 0, LRMOE_DW_BF16 = 1 } lrmoe_dw_mode;
 
+/* Scoring rule of lrmoe_score_select_compact.  LRM is the method's metric
+ * R_u = alpha_u^2 * ||g_t||^2 * ||phi_u||^2.  The others are the ablation
+ * baselines the pages compare it with ("LRMoE: Trimming Backward Work in
+ * Memory-Bound MoE Training", section "What the measurements show"): the
+ * squared norm of the upstream gradient alone, ||g_t||^2, and its absolute
+ * magnitude, read here as the L1 norm sum_i |g_t,i| (the Euclidean norm
+ * would rank pairs exactly like the squared norm).  Random dropping, the
+ * third baseline, takes caller-drawn scores through lrmoe_select_compact.
+ * The gradient-only rules read no phi row.  Sums are float32. */
+typedef enum {
+  LRMOE_SCORE_LRM = 0,
+  LRMOE_SCORE_GRAD_SQNORM = 1,
+  LRMOE_SCORE_GRAD_L1 = 2
+} lrmoe_score_mode;
+
 typedef struct {
   int32_t E;               /* local experts, 1 .. LRMOE_MAX_EXPERTS          */
   int32_t dtype;           /* lrmoe_dtype                                    */
@@ -107,7 +122,7 @@ typedef struct {
   const int64_t* counts;   /* host [E]: n_e, sum = P                          */
   const int64_t* quotas;   /* host [E]: q_e, 0 <= q_e <= n_e                  */
   int32_t dw_mode;         /* lrmoe_dw_mode                                  */
-  int32_t reserved;        /* must be 0                                      */
+  int32_t score_mode;      /* lrmoe_score_mode (0 = LRM)                     */
 } lrmoe_problem;
 
 /* ABI version of the loaded library (LRMOE_ABI_VERSION at build time). */
@@ -195,6 +210,7 @@ lrmoe_status lrmoe_grouped_backward(
  * and right after that kernel's launch.  Kernels not launched for a problem
  * (an empty range) leave their events unrecorded.
  *   lrmoe_score_select_compact_timed: [0] score  [1] select+scan  [2] gather
+ *   lrmoe_select_compact_timed:       [1] select+scan  [2] gather
  *   lrmoe_grouped_backward_timed:     [0] operand prologue  [1] grouped GEMM
  *                                     [2] split-K reduction */
 #define LRMOE_TIMING_SLOTS 4
@@ -207,6 +223,14 @@ typedef struct {
 lrmoe_status lrmoe_score_select_compact_timed(
     const lrmoe_problem* pb, const int32_t* g_row_index, const float* alpha,
     const void* g, const void* phi, float* scores, uint8_t* keep,
+    int32_t* seg_offsets, int32_t* perm, void* g_c, void* phi_c, float* alpha_c,
+    float* dphi_zero, void* workspace, size_t ws_bytes, void* stream,
+    const lrmoe_timing* timing);
+
+/* lrmoe_select_compact with per-kernel events (timing may be NULL). */
+lrmoe_status lrmoe_select_compact_timed(
+    const lrmoe_problem* pb, const float* scores, const int32_t* g_row_index,
+    const float* alpha, const void* g, const void* phi, uint8_t* keep,
     int32_t* seg_offsets, int32_t* perm, void* g_c, void* phi_c, float* alpha_c,
     float* dphi_zero, void* workspace, size_t ws_bytes, void* stream,
     const lrmoe_timing* timing);

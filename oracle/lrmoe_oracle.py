@@ -19,6 +19,8 @@ Steps, in the pages' order:
                   "Cotas antes do calculo").
   lrm_scores      R_u = alpha_u^2 * ||g_t||^2 * ||phi_u||^2
                   ([EN] "LRM: a decomposable contribution score").
+  gradient_scores the ablation baselines ||g_t||^2 and sum_i |g_t,i|
+                  ([EN] "What the measurements show").
   select_top_quota  per expert, keep the q_e highest-scoring pairs
                   ([PT] bullet "Selecao pela metrica LRM").
   compact         pack kept rows into contiguous expert segments
@@ -110,6 +112,31 @@ def lrm_scores(alpha, g, phi, row_index, dtype, block_rows: int = 4096) -> np.nd
     return a * a * gsq[rows] * psq
 
 
+def gradient_scores(g, row_index, dtype, P: int, rule: str, block_rows: int = 4096) -> np.ndarray:
+    """Ablation baselines that score a pair by its upstream gradient alone
+    ([EN] "What the measurements show": squared gradient norm and absolute
+    gradient magnitude).  rule "sqnorm": ||g_t||_2^2.  rule "l1": the sum of
+    |g_t,i| -- read as the L1 norm, since the Euclidean norm ranks pairs
+    exactly like its square."""
+    assert rule in ("sqnorm", "l1")
+    v = np.empty(g.shape[0])
+    for lo in range(0, g.shape[0], block_rows):
+        gb = to_f64(g[lo:lo + block_rows], dtype)
+        v[lo:lo + block_rows] = (np.einsum("ij,ij->i", gb, gb) if rule == "sqnorm"
+                                 else np.abs(gb).sum(axis=1))
+    rows = np.arange(P) if row_index is None else row_index.astype(np.int64)
+    assert np.all(np.isfinite(v))
+    return v[rows]
+
+
+def pair_scores(mode: str, alpha, g, phi, row_index, dtype) -> np.ndarray:
+    """Scores of the selectable rules: "lrm" (the method) or a gradient-only
+    ablation ("sqnorm", "l1")."""
+    if mode == "lrm":
+        return lrm_scores(alpha, g, phi, row_index, dtype)
+    return gradient_scores(g, row_index, dtype, phi.shape[0], mode)
+
+
 # ---------------------------------------------------------------- a2: select
 
 def select_top_quota(scores: np.ndarray, counts, quotas):
@@ -188,14 +215,14 @@ def input_grad(seg, perm, alpha_c, g_c, W, dtype, P: int):
 # ---------------------------------------------------------------- whole path
 
 def pruned_backward(counts, policy, alpha, g, phi, W, row_index, dtype,
-                    with_grads: bool = True, gate_up=None) -> dict:
+                    with_grads: bool = True, gate_up=None, score_mode: str = "lrm") -> dict:
     """plan -> score -> select -> compact -> dW, dphi (and, when gate_up =
     (g2, x, W2) is given, the second projection's dW and dx on the same keep
-    set and permutation)."""
+    set and permutation).  score_mode picks the scoring rule (pair_scores)."""
     E, d_out, d_in = W.shape
     P = phi.shape[0]
     q = plan_quota(counts, policy)
-    R = lrm_scores(alpha, g, phi, row_index, dtype)
+    R = pair_scores(score_mode, alpha, g, phi, row_index, dtype)
     keep, taus = select_top_quota(R, counts, q)
     perm, seg = compact(keep, counts, q)
     out = dict(quotas=q, scores=R, keep=keep, taus=taus, perm=perm, seg=seg)

@@ -44,7 +44,8 @@ lrmoe_status check_problem(const lrmoe_problem* pb, Checked& c) {
   if (pb == nullptr || pb->counts == nullptr || pb->quotas == nullptr) return LRMOE_ERR_NULL;
   if (pb->E < 1 || pb->E > kMaxE) return LRMOE_ERR_INVALID;
   if (pb->dtype != LRMOE_F32 && pb->dtype != LRMOE_BF16) return LRMOE_ERR_DTYPE;
-  if ((pb->dw_mode != LRMOE_DW_EXACT && pb->dw_mode != LRMOE_DW_BF16) || pb->reserved != 0)
+  if (pb->dw_mode != LRMOE_DW_EXACT && pb->dw_mode != LRMOE_DW_BF16) return LRMOE_ERR_INVALID;
+  if (pb->score_mode < LRMOE_SCORE_LRM || pb->score_mode > LRMOE_SCORE_GRAD_L1)
     return LRMOE_ERR_INVALID;
   if (pb->P < 0 || pb->P >= (int64_t(1) << 31)) return LRMOE_ERR_SHAPE;
   if (pb->T < 0 || pb->T >= (int64_t(1) << 31)) return LRMOE_ERR_SHAPE;
@@ -229,8 +230,8 @@ lrmoe_status select_compact(const lrmoe_problem* pb, bool compute_scores, const 
   const float* scores = scores_in;
   if (compute_scores) {
     LRMOE_TRY(mark(timing, false, 0, s));
-    LRMOE_TRY(hip_status(launch_score(pb->dtype, g, phi, alpha, g_row_index, (int32_t)P,
-                                      pb->d_out, pb->d_in, scores_out, s)));
+    LRMOE_TRY(hip_status(launch_score(pb->dtype, pb->score_mode, g, phi, alpha, g_row_index,
+                                      (int32_t)P, pb->d_out, pb->d_in, scores_out, s)));
     LRMOE_TRY(mark(timing, true, 0, s));
     scores = scores_out;
   }
@@ -336,6 +337,18 @@ lrmoe_status lrmoe_select_compact(const lrmoe_problem* pb, const float* scores,
   return select_compact(pb, false, scores, g_row_index, alpha, g, phi, nullptr, keep, seg_offsets,
                         perm, g_c, phi_c, alpha_c, dphi_zero, workspace, ws_bytes, stream,
                         nullptr);
+}
+
+lrmoe_status lrmoe_select_compact_timed(const lrmoe_problem* pb, const float* scores,
+                                        const int32_t* g_row_index, const float* alpha,
+                                        const void* g, const void* phi, uint8_t* keep,
+                                        int32_t* seg_offsets, int32_t* perm, void* g_c,
+                                        void* phi_c, float* alpha_c, float* dphi_zero,
+                                        void* workspace, size_t ws_bytes, void* stream,
+                                        const lrmoe_timing* timing) {
+  return select_compact(pb, false, scores, g_row_index, alpha, g, phi, nullptr, keep, seg_offsets,
+                        perm, g_c, phi_c, alpha_c, dphi_zero, workspace, ws_bytes, stream,
+                        timing);
 }
 
 lrmoe_status lrmoe_gather_compact(const lrmoe_problem* pb, const int32_t* perm,

@@ -103,7 +103,7 @@ __host__ __device__ inline int64_t partial_base(const GemmTable& t, int e) {
 }
 
 // Launchers (return hipSuccess or the launch error).
-hipError_t launch_score(int dtype, const void* g, const void* phi, const float* alpha,
+hipError_t launch_score(int dtype, int mode, const void* g, const void* phi, const float* alpha,
                         const int32_t* row_index, int32_t P, int32_t d_out, int32_t d_in,
                         float* scores, hipStream_t s);
 

@@ -46,29 +46,42 @@ __device__ __forceinline__ float sumsq8(uint4 x) {
 __device__ __forceinline__ float sumsq4(float4 x) {
   return fmaf(x.w, x.w, fmaf(x.z, x.z, fmaf(x.y, x.y, x.x * x.x)));
 }
+__device__ __forceinline__ float sumabs8(uint4 x) {
+  // |bf16| = clear the sign bit of each half
+  const float a = (bf16_lo(x.x & 0x7FFF7FFFu) + bf16_hi(x.x & 0x7FFF7FFFu)) +
+                  (bf16_lo(x.y & 0x7FFF7FFFu) + bf16_hi(x.y & 0x7FFF7FFFu));
+  const float b = (bf16_lo(x.z & 0x7FFF7FFFu) + bf16_hi(x.z & 0x7FFF7FFFu)) +
+                  (bf16_lo(x.w & 0x7FFF7FFFu) + bf16_hi(x.w & 0x7FFF7FFFu));
+  return a + b;
+}
+__device__ __forceinline__ float sumabs4(float4 x) {
+  return (fabsf(x.x) + fabsf(x.y)) + (fabsf(x.z) + fabsf(x.w));
+}
 
-// Sum of squares of one row held in 16-byte chunks, lane-strided, four
-// independent loads in flight per lane.
-template <typename V>
+template <bool ABS, typename V>
+__device__ __forceinline__ float reduce16(const V& x) {
+  if constexpr (__is_same(V, uint4)) return ABS ? sumabs8(x) : sumsq8(x);
+  else return ABS ? sumabs4(x) : sumsq4(x);
+}
+
+// Sum of squares (ABS: of absolute values) of one row held in 16-byte
+// chunks, lane-strided, four independent loads in flight per lane.
+template <bool ABS = false, typename V>
 __device__ __forceinline__ float row_sumsq(const V* __restrict__ row, int nchunk, int lane) {
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
   int c = lane;
   for (; c + 192 < nchunk; c += 256) {
     const V x0 = row[c], x1 = row[c + 64], x2 = row[c + 128], x3 = row[c + 192];
-    if constexpr (sizeof(V) == 16 && __is_same(V, uint4)) {
-      a0 += sumsq8(x0); a1 += sumsq8(x1); a2 += sumsq8(x2); a3 += sumsq8(x3);
-    } else {
-      a0 += sumsq4(x0); a1 += sumsq4(x1); a2 += sumsq4(x2); a3 += sumsq4(x3);
-    }
+    a0 += reduce16<ABS>(x0); a1 += reduce16<ABS>(x1);
+    a2 += reduce16<ABS>(x2); a3 += reduce16<ABS>(x3);
   }
-  for (; c < nchunk; c += 64) {
-    const V x = row[c];
-    if constexpr (__is_same(V, uint4)) a0 += sumsq8(x); else a0 += sumsq4(x);
-  }
+  for (; c < nchunk; c += 64) a0 += reduce16<ABS>(row[c]);
   return (a0 + a1) + (a2 + a3);
 }
 
-template <bool BF16>
+// MODE: LRMOE_SCORE_LRM (alpha^2 ||g||^2 ||phi||^2), _GRAD_SQNORM (||g||^2)
+// or _GRAD_L1 (sum |g_i|); the gradient-only rules never touch phi.
+template <bool BF16, int MODE>
 __global__ __launch_bounds__(256) void lrm_score_kernel(
     const void* __restrict__ g, const void* __restrict__ phi, const float* __restrict__ alpha,
     const int32_t* __restrict__ row_index, int32_t P, int32_t d_out, int32_t d_in,
@@ -80,19 +93,26 @@ __global__ __launch_bounds__(256) void lrm_score_kernel(
   const int gc = d_out / per, pc = d_in / per;
   for (int u = wave; u < P; u += nwaves) {
     const int64_t r = row_index ? (int64_t)row_index[u] : (int64_t)u;
-    float gs, ps;
+    constexpr bool L1 = MODE == LRMOE_SCORE_GRAD_L1;
+    float gs, ps = 1.f;
     if (BF16) {
-      gs = row_sumsq(reinterpret_cast<const uint4*>(g) + r * gc, gc, lane);
-      ps = row_sumsq(reinterpret_cast<const uint4*>(phi) + (int64_t)u * pc, pc, lane);
+      gs = row_sumsq<L1>(reinterpret_cast<const uint4*>(g) + r * gc, gc, lane);
+      if (MODE == LRMOE_SCORE_LRM)
+        ps = row_sumsq(reinterpret_cast<const uint4*>(phi) + (int64_t)u * pc, pc, lane);
     } else {
-      gs = row_sumsq(reinterpret_cast<const float4*>(g) + r * gc, gc, lane);
-      ps = row_sumsq(reinterpret_cast<const float4*>(phi) + (int64_t)u * pc, pc, lane);
+      gs = row_sumsq<L1>(reinterpret_cast<const float4*>(g) + r * gc, gc, lane);
+      if (MODE == LRMOE_SCORE_LRM)
+        ps = row_sumsq(reinterpret_cast<const float4*>(phi) + (int64_t)u * pc, pc, lane);
     }
     gs = wave_sum(gs);
-    ps = wave_sum(ps);
+    if (MODE == LRMOE_SCORE_LRM) ps = wave_sum(ps);
     if (lane == 0) {
-      const float a = alpha[u];
-      scores[u] = ((a * a) * gs) * ps;
+      if (MODE == LRMOE_SCORE_LRM) {
+        const float a = alpha[u];
+        scores[u] = ((a * a) * gs) * ps;
+      } else {
+        scores[u] = gs;
+      }
     }
   }
 }
@@ -410,19 +430,35 @@ __global__ __launch_bounds__(kSelThreads) void select_scan_kernel(
 
 }  // namespace
 
-hipError_t launch_score(int dtype, const void* g, const void* phi, const float* alpha,
+template <int MODE>
+void launch_score_mode(int dtype, dim3 grid, hipStream_t s, const void* g, const void* phi,
+                       const float* alpha, const int32_t* row_index, int32_t P, int32_t d_out,
+                       int32_t d_in, float* scores) {
+  if (dtype == LRMOE_BF16)
+    hipLaunchKernelGGL((lrm_score_kernel<true, MODE>), grid, dim3(256), 0, s, g, phi, alpha,
+                       row_index, P, d_out, d_in, scores);
+  else
+    hipLaunchKernelGGL((lrm_score_kernel<false, MODE>), grid, dim3(256), 0, s, g, phi, alpha,
+                       row_index, P, d_out, d_in, scores);
+}
+
+hipError_t launch_score(int dtype, int mode, const void* g, const void* phi, const float* alpha,
                         const int32_t* row_index, int32_t P, int32_t d_out, int32_t d_in,
                         float* scores, hipStream_t s) {
   if (P <= 0) return hipSuccess;
   const int waves_per_block = 4;
   int blocks = (P + waves_per_block - 1) / waves_per_block;
   if (blocks > 256 * 8) blocks = 256 * 8;   // 32 waves per CU, each looping over pairs
-  if (dtype == LRMOE_BF16)
-    hipLaunchKernelGGL(lrm_score_kernel<true>, dim3(blocks), dim3(256), 0, s, g, phi, alpha,
-                       row_index, P, d_out, d_in, scores);
+  const dim3 grid(blocks);
+  if (mode == LRMOE_SCORE_GRAD_SQNORM)
+    launch_score_mode<LRMOE_SCORE_GRAD_SQNORM>(dtype, grid, s, g, phi, alpha, row_index, P,
+                                               d_out, d_in, scores);
+  else if (mode == LRMOE_SCORE_GRAD_L1)
+    launch_score_mode<LRMOE_SCORE_GRAD_L1>(dtype, grid, s, g, phi, alpha, row_index, P, d_out,
+                                           d_in, scores);
   else
-    hipLaunchKernelGGL(lrm_score_kernel<false>, dim3(blocks), dim3(256), 0, s, g, phi, alpha,
-                       row_index, P, d_out, d_in, scores);
+    launch_score_mode<LRMOE_SCORE_LRM>(dtype, grid, s, g, phi, alpha, row_index, P, d_out, d_in,
+                                       scores);
   return hipGetLastError();
 }
 

@@ -18,9 +18,10 @@ LIB_PATH = os.path.join(_PKG, "liblrmoe.so")
 
 F32, BF16 = 0, 1
 DW_EXACT, DW_BF16 = 0, 1
+SCORE_LRM, SCORE_GRAD_SQNORM, SCORE_GRAD_L1 = 0, 1, 2
 QUOTA_RATIO, QUOTA_BUDGET = 0, 1
 MAX_EXPERTS = 256
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 STATUS = {0: "LRMOE_OK", 1: "LRMOE_ERR_NULL", 2: "LRMOE_ERR_INVALID", 3: "LRMOE_ERR_SHAPE",
           4: "LRMOE_ERR_ALIGN", 5: "LRMOE_ERR_DTYPE", 6: "LRMOE_ERR_WORKSPACE",
@@ -29,7 +30,7 @@ STATUS = {0: "LRMOE_OK", 1: "LRMOE_ERR_NULL", 2: "LRMOE_ERR_INVALID", 3: "LRMOE_
 EXPORTS = ["lrmoe_abi_version", "lrmoe_status_string", "lrmoe_plan_quota",
            "lrmoe_workspace_size", "lrmoe_score_select_compact", "lrmoe_select_compact",
            "lrmoe_gather_compact", "lrmoe_grouped_backward", "lrmoe_score_select_compact_timed",
-           "lrmoe_grouped_backward_timed"]
+           "lrmoe_select_compact_timed", "lrmoe_grouped_backward_timed"]
 TIMING_SLOTS = 4
 
 
@@ -43,7 +44,7 @@ class Problem(C.Structure):
     _fields_ = [("E", C.c_int32), ("dtype", C.c_int32), ("P", C.c_int64), ("T", C.c_int64),
                 ("d_out", C.c_int32), ("d_in", C.c_int32),
                 ("counts", C.POINTER(C.c_int64)), ("quotas", C.POINTER(C.c_int64)),
-                ("dw_mode", C.c_int32), ("reserved", C.c_int32)]
+                ("dw_mode", C.c_int32), ("score_mode", C.c_int32)]
 
 
 class Timing(C.Structure):
@@ -87,6 +88,9 @@ def lib() -> C.CDLL:
     L.lrmoe_score_select_compact_timed.restype = C.c_int
     L.lrmoe_score_select_compact_timed.argtypes = ([C.POINTER(Problem)] + [_P] * 13 +
                                                    [C.c_size_t, _P, C.POINTER(Timing)])
+    L.lrmoe_select_compact_timed.restype = C.c_int
+    L.lrmoe_select_compact_timed.argtypes = ([C.POINTER(Problem)] + [_P] * 13 +
+                                             [C.c_size_t, _P, C.POINTER(Timing)])
     L.lrmoe_grouped_backward_timed.restype = C.c_int
     L.lrmoe_grouped_backward_timed.argtypes = ([C.POINTER(Problem)] + [_P] * 8 +
                                                [C.c_size_t, _P, C.POINTER(Timing)])
@@ -127,7 +131,7 @@ class Plan:
     """Host description of one call: counts, quotas, sizes, storage type."""
 
     def __init__(self, counts, quotas, d_out: int, d_in: int, dtype: int, T: Optional[int] = None,
-                 dw_mode: int = DW_EXACT):
+                 dw_mode: int = DW_EXACT, score_mode: int = SCORE_LRM):
         self.counts = [int(c) for c in counts]
         self.quotas = [int(q) for q in quotas]
         self.E = len(self.counts)
@@ -139,7 +143,8 @@ class Plan:
         self._q = _i64_array(self.quotas)
         self.struct = Problem(self.E, self.dtype, self.P, self.T, self.d_out, self.d_in,
                               C.cast(self._cnt, C.POINTER(C.c_int64)),
-                              C.cast(self._q, C.POINTER(C.c_int64)), self.dw_mode, 0)
+                              C.cast(self._q, C.POINTER(C.c_int64)), self.dw_mode,
+                              int(score_mode))
 
     @property
     def torch_dtype(self):
@@ -220,6 +225,10 @@ def score_select_compact(plan: Plan, alpha, g, phi, g_row_index=None, out=None, 
     elif scores is None:
         st = L.lrmoe_score_select_compact(C.byref(plan.struct), *common, _ptr(out["scores"]), *tail)
         check("lrmoe_score_select_compact", st)
+    elif timing is not None:
+        st = L.lrmoe_select_compact_timed(C.byref(plan.struct), _ptr(scores), *common, *tail,
+                                          C.byref(timing.next_slots()))
+        check("lrmoe_select_compact_timed", st)
     else:
         st = L.lrmoe_select_compact(C.byref(plan.struct), _ptr(scores), *common, *tail)
         check("lrmoe_select_compact", st)

@@ -40,8 +40,9 @@ def dtype_code(p):
     return lrmoe.BF16 if p.dtype == "bf16" else lrmoe.F32
 
 
-def run_gpu(p, quotas, dw_mode=lrmoe.DW_EXACT, scores=None):
-    plan = lrmoe.Plan(p.counts, quotas, p.d_out, p.d_in, dtype_code(p), T=p.T, dw_mode=dw_mode)
+def run_gpu(p, quotas, dw_mode=lrmoe.DW_EXACT, scores=None, score_mode=lrmoe.SCORE_LRM):
+    plan = lrmoe.Plan(p.counts, quotas, p.d_out, p.d_in, dtype_code(p), T=p.T, dw_mode=dw_mode,
+                      score_mode=score_mode)
     t = dict(alpha=dev(p.alpha), g=dev(p.g), phi=dev(p.phi), W=dev(p.W),
              row=dev(p.row_index))
     sc = dev(scores) if scores is not None else None
@@ -74,10 +75,10 @@ def rel_err(got, ref):
     return float(np.abs(got.astype(np.float64) - ref).max() / m)
 
 
-def compare_full(p, quotas, out, dw_mode=lrmoe.DW_EXACT, scores_in=None):
+def compare_full(p, quotas, out, dw_mode=lrmoe.DW_EXACT, scores_in=None, score_mode="lrm"):
     """Full oracle comparison (small and medium problems)."""
     ref = O.pruned_backward(p.counts, ("ratio", 1, 1), p.alpha, p.g, p.phi, p.W, p.row_index,
-                            p.dtype, with_grads=False)
+                            p.dtype, with_grads=False, score_mode=score_mode)
     R = ref["scores"] if scores_in is None else scores_in.astype(np.float64)
     keep_ref, taus = O.select_top_quota(R, p.counts, quotas)
     keep_gpu = out["keep"].cpu().numpy().astype(bool)

@@ -96,7 +96,8 @@ def plan(counts=(4, 2, 3), quotas=(3, 1, 2), d_out=16, d_in=8, dtype=L.BF16, **k
     (lambda p: setattr(p.struct, "E", 257), 2),
     (lambda p: setattr(p.struct, "dtype", 9), 5),
     (lambda p: setattr(p.struct, "dw_mode", 3), 2),
-    (lambda p: setattr(p.struct, "reserved", 1), 2),
+    (lambda p: setattr(p.struct, "score_mode", 3), 2),
+    (lambda p: setattr(p.struct, "score_mode", -1), 2),
     (lambda p: setattr(p.struct, "P", 8), 3),             # sum of counts != P
     (lambda p: setattr(p.struct, "P", 2**31), 3),
     (lambda p: setattr(p.struct, "d_out", 12), 4),        # not a multiple of 8 (bf16)

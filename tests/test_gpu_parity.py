@@ -102,6 +102,20 @@ def test_select_large_experts(distinct):
         assert np.array_equal(out["seg_offsets"].cpu().numpy(), seg), policy
 
 
+@pytest.mark.parametrize("mode,name", [(lrmoe.SCORE_GRAD_SQNORM, "sqnorm"),
+                                       (lrmoe.SCORE_GRAD_L1, "l1")])
+def test_ablation_score_modes(mode, name):
+    """Gradient-only scoring rules (the pages' ablation baselines): scores,
+    keep sets, compaction and gradients against the oracle's same rule, on a
+    bf16 problem and on the per-token float32 one."""
+    for p in (W.make_problem(P=4000, E=6, d_out=256, d_in=136, dtype="bf16", zipf=1.3, seed=31),
+              W.config(0)):
+        q = lrmoe.plan_quota(p.counts, ("ratio", 80, 100))
+        plan, out, _ = U.run_gpu(p, q, score_mode=mode)
+        errs, _ = U.compare_full(p, q, out, score_mode=name)
+        print(name, p.name, errs)
+
+
 def test_negative_and_signed_zero_scores():
     """The order-preserving key handles negative scores and -0.0 == 0.0."""
     p = W.make_problem(P=600, E=3, d_out=32, d_in=32, dtype="bf16", counts=[200, 250, 150], seed=5)

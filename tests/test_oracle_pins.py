@@ -87,6 +87,26 @@ def O_exact(a, dtype):
     return out
 
 
+def check_gradient_scores(orc):
+    """The ablation baselines ([EN] "What the measurements show"): squared
+    gradient norm and absolute gradient magnitude (L1), by brute force over
+    independently decoded values, through the per-token row index."""
+    for dtype in ("f32", "bf16"):
+        p = tiny(13, dtype=dtype, T=9, E=4, d_out=7, d_in=16)
+        gf = O_exact(p.g, dtype)
+        sq = orc.pair_scores("sqnorm", p.alpha, p.g, p.phi, p.row_index, p.dtype)
+        l1 = orc.pair_scores("l1", p.alpha, p.g, p.phi, p.row_index, p.dtype)
+        for u in range(p.P):
+            row = gf[int(p.row_index[u])]
+            ref_sq = sum(v * v for v in row)
+            ref_l1 = sum(abs(v) for v in row)
+            assert abs(sq[u] - ref_sq) <= 1e-12 * ref_sq
+            assert abs(l1[u] - ref_l1) <= 1e-12 * ref_l1
+        # the method's rule through the same dispatcher
+        assert np.array_equal(orc.pair_scores("lrm", p.alpha, p.g, p.phi, p.row_index, p.dtype),
+                              orc.lrm_scores(p.alpha, p.g, p.phi, p.row_index, p.dtype))
+
+
 def check_select_bruteforce(orc):
     """Within a quota the highest-scoring pairs are kept ([PT] "Selecao pela
     metrica LRM"): the kept set maximises the additive objective sum R over
@@ -223,7 +243,8 @@ def check_sampled_match_full(orc):
     assert np.allclose(rows, out["dphi"][pairs], rtol=1e-13, atol=0)
 
 
-CHECKS = [check_quota_example, check_score_bruteforce, check_select_bruteforce,
+CHECKS = [check_quota_example, check_score_bruteforce, check_gradient_scores,
+          check_select_bruteforce,
           check_compact_invariants, check_dense_equivalence, check_drop_identities,
           check_gate_up_inherits, check_sampled_match_full]
 
@@ -314,6 +335,15 @@ def _input_grad_keep_dropped_rows(seg, perm, alpha_c, g_c, W, dtype, P):
 
 to_f64 = O.to_f64
 
+
+def _gradient_scores_l1_squares(g, row_index, dtype, P, rule, block_rows=4096):
+    return O.gradient_scores(g, row_index, dtype, P, "sqnorm", block_rows)
+
+
+def _gradient_scores_unsquared(g, row_index, dtype, P, rule, block_rows=4096):
+    v = O.gradient_scores(g, row_index, dtype, P, rule, block_rows)
+    return np.sqrt(v) if rule == "sqnorm" else v
+
 MUTANTS = {
     "score_alpha_not_squared": dict(lrm_scores=_scores_alpha_not_squared),
     "score_drops_phi_term": dict(lrm_scores=_scores_no_phi),
@@ -324,6 +354,8 @@ MUTANTS = {
     "perm_descending": dict(compact=_compact_unsorted),
     "quota_rounds": dict(plan_quota=_quota_round),
     "dropped_rows_nonzero": dict(input_grad=_input_grad_keep_dropped_rows),
+    "l1_rule_uses_squares": dict(gradient_scores=_gradient_scores_l1_squares),
+    "sqnorm_rule_not_squared": dict(gradient_scores=_gradient_scores_unsquared),
 }
 
 
