@@ -158,6 +158,9 @@ def main():
     ap.add_argument("--dw-mode", choices=["exact", "bf16"], default="exact")
     ap.add_argument("--score-mode", choices=["lrm", "grad-sqnorm", "grad-l1", "random"],
                     default="lrm", help="scoring rule (the method, or an ablation baseline)")
+    ap.add_argument("--path", choices=["compacted", "masked-dense"], default="compacted",
+                    help="masked-dense: the zero-masked alternative (alpha := 0 on dropped "
+                         "pairs, GEMMs over every routed pair), for the A/B against compaction")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
@@ -217,7 +220,33 @@ def main():
         gen.manual_seed(2024)
         given_scores = torch.rand(p.P, generator=gen, device=dev, dtype=torch.float32)
 
+    dense_path = args.path == "masked-dense"
+    if dense_path:
+        if gu is not None or p.T != p.P or given_scores is not None:
+            print("bench.py: the masked-dense path runs one projection with one g row per "
+                  "pair and a computed score", file=sys.stderr)
+            sys.exit(2)
+        dense = lrmoe.Plan(p.counts, p.counts, p.d_out, p.d_in, dtc, dw_mode=mode)
+        dws = lrmoe.workspace(dense, dev)
+        sel = dict(scores=torch.empty(p.P, dtype=torch.float32, device=dev),
+                   keep=torch.empty(p.P, dtype=torch.uint8, device=dev),
+                   seg_offsets=torch.empty(p.E + 1, dtype=torch.int32, device=dev),
+                   perm=torch.empty(M, dtype=torch.int32, device=dev))
+        am = torch.empty(p.P, dtype=torch.float32, device=dev)
+        pid = torch.empty(p.P, dtype=torch.int32, device=dev)
+        dphi_full = torch.empty((p.P, p.d_in), dtype=torch.float32, device=dev)
+
     def step(ssc_t=None, gb_t=None, gu_t=None, gu_events=None):
+        if dense_path:   # same selection, no compaction, GEMMs over all P pairs
+            if gu_events is not None:
+                gu_events[0].record(stream)
+            lrmoe.score_select(plan, alpha, g, phi, out=sel, ws=ws)
+            lrmoe.mask_alpha(sel["keep"], alpha, am, pid)
+            if gu_events is not None:
+                gu_events[1].record(stream)
+            lrmoe.grouped_backward(dense, pid, am, g, phi, W, dW=dW, dphi=dphi_full, ws=dws,
+                                   timing=gb_t)
+            return
         lrmoe.score_select_compact(plan, alpha, g, phi, g_row_index=row, out=out, ws=ws,
                                    scores=given_scores, timing=ssc_t)
         lrmoe.grouped_backward(plan, out["perm"], out["alpha_c"], out["g_c"], out["phi_c"], W,
@@ -252,13 +281,13 @@ def main():
     nb = min(args.steps, 200)
     ssc_timer = lrmoe.KernelTimer(nb)
     gb_timer = lrmoe.KernelTimer(nb)
-    if gu is not None:
+    if gu is not None or dense_path:
         gu_timer = lrmoe.KernelTimer(nb)
         gu_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                  for _ in range(nb)]
     for i in range(nb):
         step(ssc_timer, gb_timer, gu_timer if gu is not None else None,
-             gu_ev[i] if gu is not None else None)
+             gu_ev[i] if (gu is not None or dense_path) else None)
     torch.cuda.synchronize()
 
     es = 2 if p.dtype == "bf16" else 4
@@ -276,7 +305,7 @@ def main():
     work = {"lrm_score": score_bytes,
             "select_scan": P * 5,
             "gather": M * (2 * es * (d_o + d_i) + 12) + (P - M) * 4 * d_i,
-            "grouped_gemm": gemm_flops(p, M)}
+            "grouped_gemm": gemm_flops(p, p.P if dense_path else M)}
     kernels = {}
     for name, t in us.items():
         if t is None:
@@ -308,7 +337,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if p.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": p.name, "P": p.P, "E": p.E, "d_out": p.d_out, "d_in": p.d_in,
+        "config": {"workload": p.name + ("+masked-dense" if dense_path else ""),
+                   "P": p.P, "E": p.E, "d_out": p.d_out, "d_in": p.d_in,
                    "kept_pairs": M, "policy": list(p.policy), "dw_mode": args.dw_mode,
                    "score_mode": args.score_mode,
                    "parallelism": "single GPU (one expert-parallel rank's share)"},
@@ -334,6 +364,15 @@ def main():
                              "algorithmic_flops": gfl, "TFLOPs": gfl / gg["mean"] / 1e6,
                              "mfma_frac": gfl / gg["mean"] / 1e6 / MFMA_BF16_PEAK_TFLOPS},
             "operand_prologue_us": gu_timer.mean_us(0), "splitk_reduce_us": gu_timer.mean_us(2)}
+        gu_timer.close()
+    if dense_path:
+        sd = stats_us([a.elapsed_time(b) * 1e3 for a, b in gu_ev])
+        rec["masked_dense"] = {
+            "note": "same selection, alpha := 0 on dropped pairs, grouped GEMMs over all P "
+                    "routed pairs of the uncompacted g and phi; value counts kept pairs, so it "
+                    "compares directly with the compacted path",
+            "score_select_mask_us": sd["mean"],
+            "gemm_executed_flops": gemm_flops(p, P), "gemm_kept_flops": gemm_flops(p, M)}
         gu_timer.close()
     ssc_timer.close()
     gb_timer.close()

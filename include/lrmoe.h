@@ -177,6 +177,27 @@ lrmoe_status lrmoe_select_compact(
     int32_t* seg_offsets, int32_t* perm, void* g_c, void* phi_c, float* alpha_c,
     float* dphi_zero, void* workspace, size_t ws_bytes, void* stream);
 
+/* Steps 2-3 without compaction: scores, keep flags, seg_offsets and perm as
+ * in lrmoe_score_select_compact, no row is moved.  For the zero-masked dense
+ * alternative below. */
+lrmoe_status lrmoe_score_select(
+    const lrmoe_problem* pb, const int32_t* g_row_index, const float* alpha,
+    const void* g, const void* phi, float* scores, uint8_t* keep,
+    int32_t* seg_offsets, int32_t* perm, void* workspace, size_t ws_bytes,
+    void* stream);
+
+/* Zero-masked dense alternative to compaction (what the pages argue against:
+ * masking the surplus rows of full-size tensors saves neither time nor
+ * memory -- "LRMoE poda a passagem reversa do MoE e acelera o treinamento em
+ * 21-45%", the paragraph after the bullets).  alpha_masked f32 [P] = alpha
+ * where keep, 0 where dropped; perm_identity int32 [P] (or NULL) = 0..P-1.
+ * Running lrmoe_grouped_backward with quotas = counts, perm_identity,
+ * alpha_masked and the uncompacted g (one row per pair) and phi yields the
+ * same dW and dphi as the compacted path, dropped dphi rows included (0).
+ * Errors: NULL / misaligned pointers, P outside 0..2^31-1. */
+lrmoe_status lrmoe_mask_alpha(int64_t P, const uint8_t* keep, const float* alpha,
+                              float* alpha_masked, int32_t* perm_identity, void* stream);
+
 /* Step 4 alone, for a second projection of the same pairs that inherits an
  * existing keep set (the gate/up projection of the expert MLP: a pair whose
  * down-projection input gradient is zero has zero gate/up gradient, so it is

@@ -200,7 +200,7 @@ lrmoe_status select_compact(const lrmoe_problem* pb, bool compute_scores, const 
                             const void* phi, float* scores_out, uint8_t* keep,
                             int32_t* seg_offsets, int32_t* perm, void* g_c, void* phi_c,
                             float* alpha_c, float* dphi_zero, void* workspace, size_t ws_bytes,
-                            void* stream, const lrmoe_timing* timing) {
+                            void* stream, const lrmoe_timing* timing, bool gather = true) {
   Checked c;
   LRMOE_TRY(check_problem(pb, c));
   const int64_t P = pb->P, M = c.M;
@@ -217,10 +217,12 @@ lrmoe_status select_compact(const lrmoe_problem* pb, bool compute_scores, const 
   LRMOE_TRY(need(keep, P));
   LRMOE_TRY(need(seg_offsets, pb->E + 1));
   LRMOE_TRY(need(perm, M));
-  LRMOE_TRY(need(g_c, M));
-  LRMOE_TRY(need(phi_c, M));
-  LRMOE_TRY(need(alpha_c, M));
-  LRMOE_TRY(optional(dphi_zero));
+  if (gather) {
+    LRMOE_TRY(need(g_c, M));
+    LRMOE_TRY(need(phi_c, M));
+    LRMOE_TRY(need(alpha_c, M));
+    LRMOE_TRY(optional(dphi_zero));
+  }
   const size_t ws_need = select_workspace(c);   // 0 unless an expert is large
   if (ws_need > 0) {
     LRMOE_TRY(need(workspace, 1));
@@ -239,6 +241,7 @@ lrmoe_status select_compact(const lrmoe_problem* pb, bool compute_scores, const 
   LRMOE_TRY(hip_status(launch_select_scan(c.tab, scores, keep, perm, seg_offsets,
                                           reinterpret_cast<uint32_t*>(workspace), s)));
   LRMOE_TRY(mark(timing, true, 1, s));
+  if (!gather) return LRMOE_OK;
   LRMOE_TRY(mark(timing, false, 2, s));
   LRMOE_TRY(hip_status(launch_gather(pb->dtype, perm, keep, g_row_index, nullptr, alpha, g, phi,
                                      g_c, phi_c, alpha_c, dphi_zero, (int32_t)M, (int32_t)P,
@@ -349,6 +352,26 @@ lrmoe_status lrmoe_select_compact_timed(const lrmoe_problem* pb, const float* sc
   return select_compact(pb, false, scores, g_row_index, alpha, g, phi, nullptr, keep, seg_offsets,
                         perm, g_c, phi_c, alpha_c, dphi_zero, workspace, ws_bytes, stream,
                         timing);
+}
+
+lrmoe_status lrmoe_score_select(const lrmoe_problem* pb, const int32_t* g_row_index,
+                                const float* alpha, const void* g, const void* phi, float* scores,
+                                uint8_t* keep, int32_t* seg_offsets, int32_t* perm,
+                                void* workspace, size_t ws_bytes, void* stream) {
+  return select_compact(pb, true, nullptr, g_row_index, alpha, g, phi, scores, keep, seg_offsets,
+                        perm, nullptr, nullptr, nullptr, nullptr, workspace, ws_bytes, stream,
+                        nullptr, false);
+}
+
+lrmoe_status lrmoe_mask_alpha(int64_t P, const uint8_t* keep, const float* alpha,
+                              float* alpha_masked, int32_t* perm_identity, void* stream) {
+  if (P < 0 || P >= (int64_t(1) << 31)) return LRMOE_ERR_SHAPE;
+  LRMOE_TRY(need(keep, P));
+  LRMOE_TRY(need(alpha, P));
+  LRMOE_TRY(need(alpha_masked, P));
+  LRMOE_TRY(optional(perm_identity));
+  return hip_status(launch_mask_alpha((int32_t)P, keep, alpha, alpha_masked, perm_identity,
+                                      reinterpret_cast<hipStream_t>(stream)));
 }
 
 lrmoe_status lrmoe_gather_compact(const lrmoe_problem* pb, const int32_t* perm,

@@ -51,7 +51,34 @@ __global__ __launch_bounds__(256) void gather_kernel(
   }
 }
 
+// Zero-masked dense alternative: alpha of dropped pairs set to 0 in the
+// original layout (and, optionally, the identity permutation), so that the
+// same grouped GEMMs run over every routed pair with the dropped ones
+// contributing exactly nothing.  The pages weigh this masking against
+// compaction and find that it saves neither time nor memory (Portuguese
+// write-up, the paragraph after the bullets); this path measures that.
+__global__ __launch_bounds__(256) void mask_alpha_kernel(const uint8_t* __restrict__ keep,
+                                                         const float* __restrict__ alpha,
+                                                         float* __restrict__ alpha_masked,
+                                                         int32_t* __restrict__ perm_identity,
+                                                         int32_t P) {
+  for (int u = blockIdx.x * blockDim.x + threadIdx.x; u < P; u += gridDim.x * blockDim.x) {
+    alpha_masked[u] = keep[u] ? alpha[u] : 0.f;
+    if (perm_identity != nullptr) perm_identity[u] = u;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_mask_alpha(int32_t P, const uint8_t* keep, const float* alpha,
+                             float* alpha_masked, int32_t* perm_identity, hipStream_t s) {
+  if (P <= 0) return hipSuccess;
+  int blocks = (P + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  hipLaunchKernelGGL(mask_alpha_kernel, dim3(blocks), dim3(256), 0, s, keep, alpha, alpha_masked,
+                     perm_identity, P);
+  return hipGetLastError();
+}
 
 hipError_t launch_gather(int dtype, const int32_t* perm, const uint8_t* keep,
                          const int32_t* g_row_index, const int32_t* phi_row_index,

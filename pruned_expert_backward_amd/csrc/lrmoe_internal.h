@@ -111,6 +111,9 @@ hipError_t launch_select_scan(const ExpertTable& tab, const float* scores, uint8
                               int32_t* perm, int32_t* seg_offsets_out, uint32_t* hist,
                               hipStream_t s);
 
+hipError_t launch_mask_alpha(int32_t P, const uint8_t* keep, const float* alpha,
+                             float* alpha_masked, int32_t* perm_identity, hipStream_t s);
+
 hipError_t launch_gather(int dtype, const int32_t* perm, const uint8_t* keep,
                          const int32_t* g_row_index, const int32_t* phi_row_index,
                          const float* alpha, const void* g, const void* phi, void* g_c,

@@ -30,7 +30,8 @@ STATUS = {0: "LRMOE_OK", 1: "LRMOE_ERR_NULL", 2: "LRMOE_ERR_INVALID", 3: "LRMOE_
 EXPORTS = ["lrmoe_abi_version", "lrmoe_status_string", "lrmoe_plan_quota",
            "lrmoe_workspace_size", "lrmoe_score_select_compact", "lrmoe_select_compact",
            "lrmoe_gather_compact", "lrmoe_grouped_backward", "lrmoe_score_select_compact_timed",
-           "lrmoe_select_compact_timed", "lrmoe_grouped_backward_timed"]
+           "lrmoe_select_compact_timed", "lrmoe_grouped_backward_timed", "lrmoe_score_select",
+           "lrmoe_mask_alpha"]
 TIMING_SLOTS = 4
 
 
@@ -91,6 +92,10 @@ def lib() -> C.CDLL:
     L.lrmoe_select_compact_timed.restype = C.c_int
     L.lrmoe_select_compact_timed.argtypes = ([C.POINTER(Problem)] + [_P] * 13 +
                                              [C.c_size_t, _P, C.POINTER(Timing)])
+    L.lrmoe_score_select.restype = C.c_int
+    L.lrmoe_score_select.argtypes = [C.POINTER(Problem)] + [_P] * 9 + [C.c_size_t, _P]
+    L.lrmoe_mask_alpha.restype = C.c_int
+    L.lrmoe_mask_alpha.argtypes = [C.c_int64, _P, _P, _P, _P, _P]
     L.lrmoe_grouped_backward_timed.restype = C.c_int
     L.lrmoe_grouped_backward_timed.argtypes = ([C.POINTER(Problem)] + [_P] * 8 +
                                                [C.c_size_t, _P, C.POINTER(Timing)])
@@ -232,6 +237,60 @@ def score_select_compact(plan: Plan, alpha, g, phi, g_row_index=None, out=None, 
     else:
         st = L.lrmoe_select_compact(C.byref(plan.struct), _ptr(scores), *common, *tail)
         check("lrmoe_select_compact", st)
+    return out
+
+
+def score_select(plan: Plan, alpha, g, phi, g_row_index=None, out=None, ws=None) -> dict:
+    """Scores and keep flags (with perm and seg_offsets) without compaction."""
+    dev = phi.device
+    if out is None:
+        out = dict(scores=_empty((plan.P,), torch.float32, dev),
+                   keep=_empty((plan.P,), torch.uint8, dev),
+                   seg_offsets=_empty((plan.E + 1,), torch.int32, dev),
+                   perm=_empty((plan.M,), torch.int32, dev))
+    if ws is None:
+        ws = workspace(plan, dev)
+    st = lib().lrmoe_score_select(C.byref(plan.struct), _ptr(g_row_index), _ptr(alpha), _ptr(g),
+                                  _ptr(phi), _ptr(out["scores"]), _ptr(out["keep"]),
+                                  _ptr(out["seg_offsets"]), _ptr(out["perm"]), _ptr(ws),
+                                  ws.numel(), _stream())
+    check("lrmoe_score_select", st)
+    return out
+
+
+def mask_alpha(keep, alpha, alpha_masked=None, perm_identity=None, identity: bool = True):
+    """alpha where kept, 0 where dropped (and the identity permutation)."""
+    P = alpha.numel()
+    if alpha_masked is None:
+        alpha_masked = _empty((P,), torch.float32, alpha.device)
+    if identity and perm_identity is None:
+        perm_identity = _empty((P,), torch.int32, alpha.device)
+    st = lib().lrmoe_mask_alpha(P, _ptr(keep), _ptr(alpha), _ptr(alpha_masked),
+                                _ptr(perm_identity), _stream())
+    check("lrmoe_mask_alpha", st)
+    return alpha_masked, perm_identity
+
+
+def masked_dense_backward(plan: Plan, alpha, g, phi, W, out=None, ws=None, dense_ws=None,
+                          timing: Optional["KernelTimer"] = None) -> dict:
+    """Zero-masked dense alternative to compaction: select the same keep set,
+    set alpha of dropped pairs to 0, and run the grouped GEMMs over every
+    routed pair of the uncompacted g (one row per pair) and phi.  Same dW and
+    dphi as pruned_backward; for timing the two paths against each other."""
+    if plan.T != plan.P:
+        raise ValueError("the dense path needs one g row per pair (T == P)")
+    dense = Plan(plan.counts, plan.counts, plan.d_out, plan.d_in, plan.dtype, dw_mode=plan.dw_mode)
+    dev = phi.device
+    if out is None:
+        out = {}
+    sel = score_select(plan, alpha, g, phi, out=out.get("sel"), ws=ws)
+    am, pid = mask_alpha(sel["keep"], alpha, out.get("alpha_masked"), out.get("perm_identity"))
+    if "dphi" not in out:
+        out["dphi"] = _empty((plan.P, plan.d_in), torch.float32, dev)
+    out.update(sel=sel, alpha_masked=am, perm_identity=pid, keep=sel["keep"])
+    out["dW"] = grouped_backward(dense, pid, am, g, phi, W, dW=out.get("dW"), dphi=out["dphi"],
+                                 ws=dense_ws if dense_ws is not None else workspace(dense, dev),
+                                 timing=timing)
     return out
 
 

@@ -193,3 +193,20 @@ def test_gather_compact_validation():
     a[1] = None
     a[10] = FAKE       # zero target needs the keep flags
     assert f(C.byref(p.struct), *a) == 1
+
+
+def test_mask_alpha_and_score_select_validation():
+    f = L.lib().lrmoe_mask_alpha
+    assert f(-1, FAKE, FAKE, FAKE, None, None) == 3
+    assert f(2**31, FAKE, FAKE, FAKE, None, None) == 3
+    assert f(10, None, FAKE, FAKE, None, None) == 1
+    assert f(10, FAKE, FAKE, FAKE + 4, None, None) == 4
+    assert f(10, FAKE, FAKE, FAKE, FAKE + 8, None) == 4
+    g = L.lib().lrmoe_score_select
+    p = plan()
+    # required: alpha, g, phi, scores, keep, seg_offsets, perm (compacted rows are not)
+    args = [None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None]
+    for i in range(1, 8):
+        a = list(args)
+        a[i] = None
+        assert g(C.byref(p.struct), *a) == 1, i

@@ -116,6 +116,42 @@ def test_ablation_score_modes(mode, name):
         print(name, p.name, errs)
 
 
+@pytest.mark.parametrize("dw_mode", [lrmoe.DW_EXACT, lrmoe.DW_BF16])
+def test_masked_dense_matches_compacted(dw_mode):
+    """The zero-masked dense alternative (alpha := 0 on dropped pairs, the
+    same GEMMs over every routed pair, nothing compacted) reproduces the
+    compacted result: same keep set, dW and dphi within tolerance, dropped
+    dphi rows exactly 0."""
+    p = W.make_problem(P=3000, E=5, d_out=256, d_in=136, dtype="bf16", zipf=1.3, seed=41)
+    policy = ("ratio", 70, 100)
+    q = lrmoe.plan_quota(p.counts, policy)
+    plan = lrmoe.Plan(p.counts, q, p.d_out, p.d_in, lrmoe.BF16, dw_mode=dw_mode)
+    t = dict(alpha=U.dev(p.alpha), g=U.dev(p.g), phi=U.dev(p.phi), W=U.dev(p.W))
+    out = lrmoe.masked_dense_backward(plan, t["alpha"], t["g"], t["phi"], t["W"])
+    torch.cuda.synchronize()
+    ref = O.pruned_backward(p.counts, policy, p.alpha, p.g, p.phi, p.W, None, "bf16",
+                            with_grads=False)
+    keep = out["keep"].cpu().numpy().astype(bool)
+    U.check_keep(ref["scores"], p.counts, q, keep, ref["keep"], ref["taus"])
+    perm, seg = O.compact(keep, p.counts, q)
+    g_c, phi_c, a_c = O.gather(perm, None, p.g, p.phi, p.alpha)
+    dW_ref = O.weight_grad(seg, a_c, g_c, phi_c, "bf16", p.E, p.d_out, p.d_in)
+    dphi_ref = O.input_grad(seg, perm, a_c, g_c, p.W, "bf16", p.P)
+    dphi = out["dphi"].cpu().numpy()
+    assert U.rel_err(dphi, dphi_ref) <= U.TOL
+    assert np.all(dphi[~keep] == 0)
+    if dw_mode == lrmoe.DW_EXACT:
+        assert U.rel_err(out["dW"].cpu().numpy(), dW_ref) <= U.TOL
+    else:
+        # single rounding of alpha * operand: the compacted GPU path rounds the
+        # same products, so the two agree up to float32 summation order
+        _, comp, _ = U.run_gpu(p, q, dw_mode=dw_mode)
+        assert U.rel_err(out["dW"].cpu().numpy(), comp["dW"].cpu().numpy().astype(np.float64)) <= 1e-5
+    am = out["alpha_masked"].cpu().numpy()
+    assert np.array_equal(am, np.where(keep, p.alpha, np.float32(0)))
+    assert np.array_equal(out["perm_identity"].cpu().numpy(), np.arange(p.P))
+
+
 def test_negative_and_signed_zero_scores():
     """The order-preserving key handles negative scores and -0.0 == 0.0."""
     p = W.make_problem(P=600, E=3, d_out=32, d_in=32, dtype="bf16", counts=[200, 250, 150], seed=5)
