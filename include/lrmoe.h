@@ -140,6 +140,28 @@ lrmoe_status lrmoe_plan_quota(int32_t E, const int64_t* counts,
                               const lrmoe_quota_policy* policy,
                               int64_t* quotas_out);
 
+/* Step 1 on the device, from the forward's routing instead of host counts
+ * (the quota is fixed before the backward from how many pairs reached each
+ * expert -- "LRMoE poda a passagem reversa do MoE e acelera o treinamento
+ * em 21-45%", bullet "Cotas antes do calculo").
+ *   expert_ids   int32 [n_ids] device: local expert index of every routed
+ *                pair, any order; an index outside 0..E-1 is not routed and
+ *                is counted in *invalid_out instead
+ *   counts_out   int64 [E] device: n_e
+ *   quotas_out   int64 [E] device: q_e, the same integer rules and results
+ *                as lrmoe_plan_quota on counts_out (budget P = sum n_e)
+ *   seg_offsets_out int64 [E+1] device: exclusive prefix sum of q_e (the
+ *                last entry is M)
+ *   invalid_out  int64 [1] device or NULL
+ * Asynchronous on `stream`; device pointers 16-byte aligned.  Errors (before
+ * any launch): NULL policy or required pointer, misalignment, E outside
+ * 1..LRMOE_MAX_EXPERTS or a bad policy (LRMOE_ERR_INVALID), n_ids outside
+ * 0..2^31-1 (LRMOE_ERR_SHAPE). */
+lrmoe_status lrmoe_plan_quota_device(int32_t E, const int32_t* expert_ids, int64_t n_ids,
+                                     const lrmoe_quota_policy* policy, int64_t* counts_out,
+                                     int64_t* quotas_out, int64_t* seg_offsets_out,
+                                     int64_t* invalid_out, void* stream);
+
 /* Workspace bytes needed by lrmoe_score_select_compact,
  * lrmoe_select_compact and lrmoe_grouped_backward for this problem (one
  * buffer may serve all of them when they run in order on one stream).

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblrmoe.so")
-SOURCES = ["api.cpp", "score_select.hip", "gather.hip", "grouped_gemm.hip"]
+SOURCES = ["api.cpp", "score_select.hip", "gather.hip", "grouped_gemm.hip", "plan_quota.hip"]
 ARCH = "gfx950"
 
 

@@ -301,6 +301,33 @@ lrmoe_status lrmoe_plan_quota(int32_t E, const int64_t* counts, const lrmoe_quot
   return LRMOE_OK;
 }
 
+lrmoe_status lrmoe_plan_quota_device(int32_t E, const int32_t* expert_ids, int64_t n_ids,
+                                     const lrmoe_quota_policy* policy, int64_t* counts_out,
+                                     int64_t* quotas_out, int64_t* seg_offsets_out,
+                                     int64_t* invalid_out, void* stream) {
+  if (policy == nullptr) return LRMOE_ERR_NULL;
+  if (E < 1 || E > kMaxE) return LRMOE_ERR_INVALID;
+  if (n_ids < 0 || n_ids >= (int64_t(1) << 31)) return LRMOE_ERR_SHAPE;
+  if (policy->mode == LRMOE_QUOTA_RATIO) {
+    if (policy->den <= 0 || policy->num < 0 || policy->num > policy->den ||
+        policy->den >= (int64_t(1) << 31))
+      return LRMOE_ERR_INVALID;
+  } else if (policy->mode == LRMOE_QUOTA_BUDGET) {
+    if (policy->budget_pairs < 0) return LRMOE_ERR_INVALID;
+  } else {
+    return LRMOE_ERR_INVALID;
+  }
+  LRMOE_TRY(need(expert_ids, n_ids));
+  LRMOE_TRY(need(counts_out, E));
+  LRMOE_TRY(need(quotas_out, E));
+  LRMOE_TRY(need(seg_offsets_out, E + 1));
+  LRMOE_TRY(optional(invalid_out));
+  return hip_status(launch_plan_quota_device(
+      expert_ids, (int32_t)n_ids, E, policy->mode, policy->num, policy->den,
+      policy->budget_pairs, counts_out, quotas_out, seg_offsets_out, invalid_out,
+      reinterpret_cast<hipStream_t>(stream)));
+}
+
 lrmoe_status lrmoe_workspace_size(const lrmoe_problem* pb, size_t* bytes_out) {
   if (bytes_out == nullptr) return LRMOE_ERR_NULL;
   Checked c;

@@ -111,6 +111,11 @@ hipError_t launch_select_scan(const ExpertTable& tab, const float* scores, uint8
                               int32_t* perm, int32_t* seg_offsets_out, uint32_t* hist,
                               hipStream_t s);
 
+hipError_t launch_plan_quota_device(const int32_t* ids, int32_t n_ids, int32_t E, int32_t mode,
+                                    int64_t num, int64_t den, int64_t Q, int64_t* counts,
+                                    int64_t* quotas, int64_t* seg_offsets, int64_t* invalid,
+                                    hipStream_t s);
+
 hipError_t launch_mask_alpha(int32_t P, const uint8_t* keep, const float* alpha,
                              float* alpha_masked, int32_t* perm_identity, hipStream_t s);
 

@@ -31,7 +31,7 @@ EXPORTS = ["lrmoe_abi_version", "lrmoe_status_string", "lrmoe_plan_quota",
            "lrmoe_workspace_size", "lrmoe_score_select_compact", "lrmoe_select_compact",
            "lrmoe_gather_compact", "lrmoe_grouped_backward", "lrmoe_score_select_compact_timed",
            "lrmoe_select_compact_timed", "lrmoe_grouped_backward_timed", "lrmoe_score_select",
-           "lrmoe_mask_alpha"]
+           "lrmoe_mask_alpha", "lrmoe_plan_quota_device"]
 TIMING_SLOTS = 4
 
 
@@ -94,6 +94,9 @@ def lib() -> C.CDLL:
                                              [C.c_size_t, _P, C.POINTER(Timing)])
     L.lrmoe_score_select.restype = C.c_int
     L.lrmoe_score_select.argtypes = [C.POINTER(Problem)] + [_P] * 9 + [C.c_size_t, _P]
+    L.lrmoe_plan_quota_device.restype = C.c_int
+    L.lrmoe_plan_quota_device.argtypes = [C.c_int32, _P, C.c_int64, C.POINTER(QuotaPolicy),
+                                          _P, _P, _P, _P, _P]
     L.lrmoe_mask_alpha.restype = C.c_int
     L.lrmoe_mask_alpha.argtypes = [C.c_int64, _P, _P, _P, _P, _P]
     L.lrmoe_grouped_backward_timed.restype = C.c_int
@@ -117,19 +120,37 @@ def _i64_array(vals: Sequence[int]):
     return arr
 
 
+def _policy(policy: tuple) -> QuotaPolicy:
+    if policy[0] == "ratio":
+        return QuotaPolicy(QUOTA_RATIO, int(policy[1]), int(policy[2]), 0)
+    if policy[0] == "budget":
+        return QuotaPolicy(QUOTA_BUDGET, 0, 1, int(policy[1]))
+    raise ValueError(policy)
+
+
 def plan_quota(counts: Sequence[int], policy: tuple) -> list:
     """Quotas per expert: policy ("ratio", num, den) or ("budget", pairs)."""
     E = len(counts)
     cnt = _i64_array(counts)
     out = (C.c_int64 * max(E, 1))()
-    if policy[0] == "ratio":
-        pol = QuotaPolicy(QUOTA_RATIO, int(policy[1]), int(policy[2]), 0)
-    elif policy[0] == "budget":
-        pol = QuotaPolicy(QUOTA_BUDGET, 0, 1, int(policy[1]))
-    else:
-        raise ValueError(policy)
+    pol = _policy(policy)
     check("lrmoe_plan_quota", lib().lrmoe_plan_quota(E, cnt, C.byref(pol), out))
     return [int(out[e]) for e in range(E)]
+
+
+def plan_quota_device(E: int, expert_ids, policy: tuple) -> dict:
+    """Counts, quotas and quota offsets on the device from the routing (the
+    local expert index of every routed pair); nothing visits the host."""
+    dev = expert_ids.device
+    out = dict(counts=_empty((E,), torch.int64, dev), quotas=_empty((E,), torch.int64, dev),
+               seg_offsets=_empty((E + 1,), torch.int64, dev),
+               invalid=_empty((1,), torch.int64, dev))
+    pol = _policy(policy)
+    st = lib().lrmoe_plan_quota_device(E, _ptr(expert_ids), expert_ids.numel(), C.byref(pol),
+                                       _ptr(out["counts"]), _ptr(out["quotas"]),
+                                       _ptr(out["seg_offsets"]), _ptr(out["invalid"]), _stream())
+    check("lrmoe_plan_quota_device", st)
+    return out
 
 
 class Plan:

@@ -210,3 +210,16 @@ def test_mask_alpha_and_score_select_validation():
         a = list(args)
         a[i] = None
         assert g(C.byref(p.struct), *a) == 1, i
+
+
+def test_plan_quota_device_validation():
+    f = L.lib().lrmoe_plan_quota_device
+    ok = L.QuotaPolicy(L.QUOTA_RATIO, 80, 100, 0)
+    bad = L.QuotaPolicy(L.QUOTA_RATIO, 120, 100, 0)
+    assert f(4, FAKE, 10, None, FAKE, FAKE, FAKE, None, None) == 1
+    assert f(0, FAKE, 10, C.byref(ok), FAKE, FAKE, FAKE, None, None) == 2
+    assert f(4, FAKE, 10, C.byref(bad), FAKE, FAKE, FAKE, None, None) == 2
+    assert f(4, FAKE, -1, C.byref(ok), FAKE, FAKE, FAKE, None, None) == 3
+    assert f(4, None, 10, C.byref(ok), FAKE, FAKE, FAKE, None, None) == 1
+    assert f(4, FAKE, 10, C.byref(ok), FAKE + 4, FAKE, FAKE, None, None) == 4
+    assert f(4, FAKE, 10, C.byref(ok), FAKE, FAKE, FAKE, FAKE + 8, None) == 4

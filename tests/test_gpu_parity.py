@@ -205,3 +205,24 @@ def test_empty_problem_pieces():
     assert not out["keep"].cpu().numpy().any()
     assert float(out["dW"].abs().max()) == 0.0
     assert float(out["dphi"].abs().max()) == 0.0
+
+
+@pytest.mark.parametrize("policy", [("ratio", 80, 100), ("ratio", 7, 10), ("budget", 3000),
+                                    ("budget", 10**6), ("ratio", 0, 1)])
+def test_plan_quota_device(policy):
+    """Quotas from the routing on the device equal the oracle's plan on the
+    histogram of the same routing (bit-exact), including unrouted indices."""
+    rng = np.random.default_rng(5)
+    for E, n in ((16, 200003), (1, 17), (5, 0), (256, 4096)):
+        ids = rng.integers(0, E, size=n).astype(np.int32)
+        if n > 10:
+            ids[rng.choice(n, 7, replace=False)] = rng.choice([-1, E, E + 3], size=7)
+        out = lrmoe.plan_quota_device(E, torch.from_numpy(ids).to(U.DEV), policy)
+        torch.cuda.synchronize()
+        valid = ids[(ids >= 0) & (ids < E)]
+        counts = np.bincount(valid, minlength=E).astype(np.int64)
+        q = np.array(O.plan_quota(counts.tolist(), policy), dtype=np.int64)
+        assert np.array_equal(out["counts"].cpu().numpy(), counts)
+        assert np.array_equal(out["quotas"].cpu().numpy(), q)
+        assert np.array_equal(out["seg_offsets"].cpu().numpy(), np.concatenate([[0], np.cumsum(q)]))
+        assert int(out["invalid"].cpu()[0]) == n - valid.size
