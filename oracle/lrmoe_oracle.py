@@ -31,13 +31,21 @@ Steps, in the pages' order:
   input_grad      dphi_u = alpha_u W_e^T g_t for kept u, zero for dropped u,
                   in the original pair layout ([PT] "Compactacao fisica":
                   the result goes back to the original layout afterwards).
+  silu_glu_grad   the expert MLP's activation backward between the down and
+                  the gate/up projection, phi = SiLU(a) * b; the pages imply
+                  this step without spelling it out.  On the compacted
+                  layout (glu_chain_grad) it feeds the gate/up projection's
+                  backward on the same keep set.
 
 Readings where the pages are silent (each also listed in the design notes):
   * quota rounding: q_e = floor(n_e * num / den) for a keep ratio num/den,
     or floor(n_e * Q / P) for a budget of Q pairs over P routed pairs;
   * ties in R go to the lower original pair index;
   * segments in ascending expert id, ascending pair index inside a segment;
-  * dropped pairs contribute nothing: their dphi rows are zero.
+  * dropped pairs contribute nothing: their dphi rows are zero;
+  * the routing weight enters the MLP chain once: the gate/up output gradient
+    is formed from W_e^T g before alpha, and the gate/up backward applies
+    alpha, as for a projection whose output gradient is given pre-alpha.
 
 Pins: every function here is checked in tests/test_oracle_pins.py against
 something other than itself (brute force of the definition, the pages'
@@ -60,6 +68,9 @@ def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         assert a.dtype == np.uint16
         return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if dtype == "f64":   # values the oracle itself produced
+        assert a.dtype == np.float64
+        return a
     assert a.dtype == np.float32
     return a.astype(np.float64)
 
@@ -212,13 +223,45 @@ def input_grad(seg, perm, alpha_c, g_c, W, dtype, P: int):
     return dphi
 
 
+# ---------------------------------------------------------------- SiLU-GLU chain
+
+def silu_glu_grad(dphi, a, b) -> np.ndarray:
+    """Backward of phi = SiLU(a) * b (SiLU(a) = a sigmoid(a)) for float64
+    rows: with s = sigmoid(a), d phi/d a = b s (1 + a (1 - s)) and
+    d phi/d b = SiLU(a).  Returns [dL/da | dL/db], gate part first."""
+    s = 1.0 / (1.0 + np.exp(-a))
+    return np.concatenate([dphi * b * s * (1.0 + a * (1.0 - s)), dphi * a * s], axis=1)
+
+
+def glu_chain_grad(seg, perm, g_c, W, a, b, dtype) -> np.ndarray:
+    """Gate/up output gradient of every kept pair, in segment order: row j
+    (pair u = perm[j] of expert e) is silu_glu_grad(W_e^T g_j, a_u, b_u),
+    before the routing weight.  a, b [P, d_in] are the pair's saved gate and
+    up pre-activations."""
+    E, d_out, d_in = W.shape
+    out = np.zeros((len(perm), 2 * d_in))
+    for e in range(E):
+        s, t = int(seg[e]), int(seg[e + 1])
+        if t > s:
+            u = perm[s:t]
+            dphi = to_f64(g_c[s:t], dtype) @ to_f64(W[e], dtype)
+            out[s:t] = silu_glu_grad(dphi, to_f64(a[u], dtype), to_f64(b[u], dtype))
+    return out
+
+
 # ---------------------------------------------------------------- whole path
 
 def pruned_backward(counts, policy, alpha, g, phi, W, row_index, dtype,
-                    with_grads: bool = True, gate_up=None, score_mode: str = "lrm") -> dict:
+                    with_grads: bool = True, gate_up=None, score_mode: str = "lrm",
+                    glu=None) -> dict:
     """plan -> score -> select -> compact -> dW, dphi (and, when gate_up =
     (g2, x, W2) is given, the second projection's dW and dx on the same keep
-    set and permutation).  score_mode picks the scoring rule (pair_scores)."""
+    set and permutation).  score_mode picks the scoring rule (pair_scores).
+    glu = (a, b, x, W2) chains the MLP instead: the gate/up output gradient
+    of the kept pairs comes from the down projection through the SiLU-GLU
+    backward (dgu_c, compacted) and drives the gate/up projection's dW2 and
+    dx; x [P, d_model] is the hidden state each pair saw and W2 [E, 2 d_in,
+    d_model] stacks the gate rows over the up rows."""
     E, d_out, d_in = W.shape
     P = phi.shape[0]
     q = plan_quota(counts, policy)
@@ -235,6 +278,14 @@ def pruned_backward(counts, policy, alpha, g, phi, W, row_index, dtype,
             g2_c, x_c, _ = gather(perm, None, g2, x, alpha)
             out["dW2"] = weight_grad(seg, alpha_c, g2_c, x_c, dtype, E, W2.shape[1], W2.shape[2])
             out["dx"] = input_grad(seg, perm, alpha_c, g2_c, W2, dtype, P)
+        if glu is not None:
+            a, b, x, W2 = glu
+            dgu_c = glu_chain_grad(seg, perm, g_c, W, a, b, dtype)
+            x_c = to_f64(x[perm], dtype)
+            W2f = to_f64(W2.reshape(-1, W2.shape[2]), dtype).reshape(W2.shape)
+            out["dgu_c"] = dgu_c
+            out["dW2"] = weight_grad(seg, alpha_c, dgu_c, x_c, "f64", E, W2.shape[1], W2.shape[2])
+            out["dx"] = input_grad(seg, perm, alpha_c, dgu_c, W2f, "f64", P)
     return out
 
 
@@ -268,4 +319,59 @@ def input_grad_rows(counts, keep, row_index, alpha, g, W, dtype, pairs) -> np.nd
                 continue
             r = u if row_index is None else int(row_index[u])
             out[k] = float(alpha[u]) * (We.T @ to_f64(g[r], dtype))
+    return out
+
+
+def _expert_of_rows(seg, js) -> np.ndarray:
+    return np.searchsorted(np.asarray(seg, dtype=np.int64), np.asarray(js, dtype=np.int64),
+                           side="right") - 1
+
+
+def glu_chain_rows(seg, perm, row_index, g, W, a, b, dtype, js) -> np.ndarray:
+    """Rows js of the compacted gate/up output gradient (glu_chain_grad),
+    each computed on its own from the original-layout inputs."""
+    out = np.zeros((len(js), 2 * W.shape[2]))
+    for k, (j, e) in enumerate(zip(js, _expert_of_rows(seg, js))):
+        u = int(perm[j])
+        r = u if row_index is None else int(row_index[u])
+        dphi = to_f64(g[r:r + 1], dtype) @ to_f64(W[e], dtype)
+        out[k] = silu_glu_grad(dphi, to_f64(a[u:u + 1], dtype), to_f64(b[u:u + 1], dtype))[0]
+    return out
+
+
+def glu_weight_grad_block(seg, perm, row_index, alpha, g, W, a, b, x, dtype, e: int,
+                          o_idx, i_idx) -> np.ndarray:
+    """dW2_e[o_idx][:, i_idx] of the chained gate/up projection: the sum over
+    expert e's kept pairs of alpha_u dgu_u[o] x_u[i], with only the needed
+    gate/up columns of dgu formed (gate column c and up column c both need
+    column c of W_e^T g)."""
+    s, t = int(seg[e]), int(seg[e + 1])
+    o_idx, i_idx = np.asarray(o_idx), np.asarray(i_idx)
+    if t == s:
+        return np.zeros((len(o_idx), len(i_idx)))
+    d_in = W.shape[2]
+    u = perm[s:t]
+    rows = u if row_index is None else row_index.astype(np.int64)[u]
+    cols = np.unique(o_idx % d_in)
+    dphi = to_f64(g[rows], dtype) @ to_f64(W[e][:, cols], dtype)
+    full = silu_glu_grad(dphi, to_f64(a[u][:, cols], dtype), to_f64(b[u][:, cols], dtype))
+    pos = np.searchsorted(cols, o_idx % d_in) + np.where(o_idx >= d_in, len(cols), 0)
+    ga = alpha[u].astype(np.float64)[:, None] * full[:, pos]
+    return ga.T @ to_f64(x[u][:, i_idx], dtype)
+
+
+def glu_input_grad_rows(counts, keep, row_index, alpha, g, W, a, b, W2, dtype, pairs) -> np.ndarray:
+    """dx of the chained gate/up projection for the requested original pair
+    indices: alpha_u W2_e^T dgu_u, zero rows for dropped pairs."""
+    offs = np.concatenate([[0], np.cumsum(np.asarray(counts, dtype=np.int64))])
+    out = np.zeros((len(pairs), W2.shape[2]))
+    expert = np.searchsorted(offs, np.asarray(pairs, dtype=np.int64), side="right") - 1
+    for k, (u, e) in enumerate(zip(pairs, expert)):
+        u = int(u)
+        if not keep[u]:
+            continue
+        r = u if row_index is None else int(row_index[u])
+        dphi = to_f64(g[r:r + 1], dtype) @ to_f64(W[e], dtype)
+        dgu = silu_glu_grad(dphi, to_f64(a[u:u + 1], dtype), to_f64(b[u:u + 1], dtype))[0]
+        out[k] = float(alpha[u]) * (to_f64(W2[e], dtype).T @ dgu)
     return out

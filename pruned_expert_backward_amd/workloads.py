@@ -24,6 +24,9 @@ Recipe (all draws from numpy's PCG64, one stream per (seed, tensor, block)):
   * g rows: N(0,1) elementwise times one lognormal(0, 0.5) factor per row;
   * phi: SiLU(z) with z ~ N(0,1) elementwise;
   * W: N(0, 0.02) elementwise;
+  * MLP-chain variant: saved gate and up pre-activations a, b ~ N(0,1)
+    elementwise (stored), and phi = SiLU(a) * b from the stored a, b in
+    float32, then stored;
   * bf16 storage: draw in float32 and round to nearest even (kept as uint16
     bit patterns, since numpy has no bfloat16).
 """
@@ -39,7 +42,8 @@ import numpy as np
 BLOCK_ROWS = 2048  # rows per independent random stream (thread-count independent)
 
 _TENSOR_IDS = {"counts": 1, "alpha": 2, "g": 3, "phi": 4, "W": 5,
-               "g2": 6, "x": 7, "W2": 8, "route": 9, "scores": 10}
+               "g2": 6, "x": 7, "W2": 8, "route": 9, "scores": 10,
+               "glu_a": 11, "glu_b": 12}
 
 
 def _rng(seed: int, tensor: str, block: int = 0) -> np.random.Generator:
@@ -75,6 +79,14 @@ class GateUp:
 
 
 @dataclasses.dataclass
+class Glu:
+    """Saved pre-activations of the expert MLP phi = SiLU(a) * b, one row per
+    pair: a (gate) and b (up), each [P, d_in] like phi."""
+    a: np.ndarray
+    b: np.ndarray
+
+
+@dataclasses.dataclass
 class Problem:
     name: str
     dtype: str                 # "bf16" (uint16 bit arrays) or "f32"
@@ -91,6 +103,7 @@ class Problem:
     W: np.ndarray              # [E, d_out, d_in]
     policy: tuple              # ("ratio", num, den) or ("budget", pairs)
     gate_up: Optional[GateUp] = None
+    glu: Optional[Glu] = None   # phi = SiLU(a) * b; gate_up.W2 stacks gate over up
 
     @property
     def offsets(self) -> np.ndarray:
@@ -100,6 +113,8 @@ class Problem:
         n = self.g.nbytes + self.phi.nbytes + self.W.nbytes + self.alpha.nbytes
         if self.gate_up is not None:
             n += self.gate_up.g2.nbytes + self.gate_up.x.nbytes + self.gate_up.W2.nbytes
+        if self.glu is not None:
+            n += self.glu.a.nbytes + self.glu.b.nbytes
         return n
 
 
@@ -169,6 +184,18 @@ def _alpha_topk_of_128(rng, rows):
     return w[np.arange(rows), pick].astype(np.float32)
 
 
+def _load(x: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 values of stored inputs (bf16 bits widened)."""
+    if dtype == "bf16":
+        return (x.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    return x
+
+
+def _glu_forward(a32: np.ndarray, b32: np.ndarray) -> np.ndarray:
+    """The MLP forward's activation, float32: SiLU(a) * b."""
+    return a32 / (np.float32(1.0) + np.exp(-a32)) * b32
+
+
 def _tensor(shape, dtype, seed, tensor, make_block):
     out = np.empty(shape, dtype=np.uint16 if dtype == "bf16" else np.float32)
     flat = out.reshape(-1, shape[-1])
@@ -178,9 +205,11 @@ def _tensor(shape, dtype, seed, tensor, make_block):
 
 def make_problem(*, P: int, E: int, d_out: int, d_in: int, dtype: str = "bf16",
                  zipf: float = 1.2, counts=None, policy=("ratio", 80, 100),
-                 seed: int = 0, name: str = "custom", gate_up=None) -> Problem:
+                 seed: int = 0, name: str = "custom", gate_up=None, glu: bool = False) -> Problem:
     """Expert-sorted pairs with one g row per pair (the expert side's view
-    after the expert-parallel dispatch)."""
+    after the expert-parallel dispatch).  glu=True (with gate_up = (2 d_in,
+    d_model)) makes phi the SiLU-GLU of saved pre-activations, so that the
+    down projection's input gradient chains into the gate/up projection."""
     if counts is None:
         counts = zipf_counts(P, E, zipf, seed)
     counts = np.asarray(counts, dtype=np.int64)
@@ -189,8 +218,15 @@ def make_problem(*, P: int, E: int, d_out: int, d_in: int, dtype: str = "bf16",
     _fill_rows(alpha, seed, "alpha", lambda r, n: _alpha_topk_of_128(r, n)[:, None])
     alpha = alpha[:, 0].copy()
     g = _tensor((P, d_out), dtype, seed, "g", _g_block(d_out, dtype))
-    phi = _tensor((P, d_in), dtype, seed, "phi", _phi_block(d_in, dtype))
     W = _tensor((E, d_out, d_in), dtype, seed, "W", _normal_block(d_in, dtype, 0.02))
+    gl = None
+    if glu:
+        assert gate_up is not None and gate_up[0] == 2 * d_in
+        gl = Glu(_tensor((P, d_in), dtype, seed, "glu_a", _normal_block(d_in, dtype, 1.0)),
+                 _tensor((P, d_in), dtype, seed, "glu_b", _normal_block(d_in, dtype, 1.0)))
+        phi = _store(_glu_forward(_load(gl.a, dtype), _load(gl.b, dtype)), dtype)
+    else:
+        phi = _tensor((P, d_in), dtype, seed, "phi", _phi_block(d_in, dtype))
     gu = None
     if gate_up is not None:
         d2o, d2i = gate_up
@@ -199,7 +235,7 @@ def make_problem(*, P: int, E: int, d_out: int, d_in: int, dtype: str = "bf16",
                     _tensor((P, d2i), dtype, seed, "x", _normal_block(d2i, dtype, 1.0)),
                     _tensor((E, d2o, d2i), dtype, seed, "W2", _normal_block(d2i, dtype, 0.02)))
     return Problem(name, dtype, E, P, P, d_out, d_in, counts, None, alpha, g, phi, W,
-                   tuple(policy), gu)
+                   tuple(policy), gu, gl)
 
 
 def make_token_problem(*, T: int, E: int, topk: int, d_out: int, d_in: int,
@@ -250,11 +286,17 @@ CONFIGS = {
 }
 
 
-def config(c: int) -> Problem:
-    """The named workload c (0 tiny fp32, 1-4 one-GPU shares), seed 1000+c."""
+def config(c: int, glu: bool = False) -> Problem:
+    """The named workload c (0 tiny fp32, 1-4 one-GPU shares), seed 1000+c.
+    glu=True (config 2 only) draws the MLP-chain variant: phi from saved
+    gate/up pre-activations, for the down -> SiLU-GLU -> gate/up chain."""
     spec = dict(CONFIGS[c])
     kind = spec.pop("kind")
     seed = 1000 + c
+    if glu:
+        assert "gate_up" in spec
+        spec["glu"] = True
+        spec["name"] = spec["name"] + "-glu-chain"
     if kind == "token":
         return make_token_problem(seed=seed, **spec)
     return make_problem(seed=seed, **spec)

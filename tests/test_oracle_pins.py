@@ -229,6 +229,89 @@ def check_gate_up_inherits(orc):
     assert np.abs(cut["dx"] - dxm).max() <= 1e-12 * np.abs(dxm).max()
 
 
+def _mlp_moe(seed, T=10, E=3, topk=2, d_model=7, d_in=5, d_out=6):
+    """Token-routed expert MLP in float64: routing from the workload
+    generator, x, W_gate, W_up, W_down, g drawn here."""
+    p = W.make_token_problem(T=T, E=E, topk=topk, d_out=d_out, d_in=d_in, seed=seed)
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, d_model))
+    Wg = 0.5 * rng.standard_normal((E, d_in, d_model))
+    Wu = 0.5 * rng.standard_normal((E, d_in, d_model))
+    Wd = 0.5 * rng.standard_normal((E, d_out, d_in))
+    g = rng.standard_normal((T, d_out))
+    e_of_u = np.repeat(np.arange(E), p.counts)
+    xt = x[p.row_index.astype(np.int64)]                       # hidden state of each pair
+    a = np.einsum("pij,pj->pi", Wg[e_of_u], xt)
+    b = np.einsum("pij,pj->pi", Wu[e_of_u], xt)
+    phi = a / (1.0 + np.exp(-a)) * b
+    return p, x, xt, Wg, Wu, Wd, g, a, b, phi, e_of_u
+
+
+def _mlp_autograd(p, x, Wg, Wu, Wd, g, e_of_u, alpha):
+    """torch.autograd (float64) of y_t = sum over pairs u of token t of
+    alpha_u W_down,e (SiLU(W_gate,e x_t) * (W_up,e x_t)), loss sum(y * g)."""
+    t = lambda v: torch.tensor(v, dtype=torch.float64, requires_grad=True)
+    xt, Wgt, Wut, Wdt = t(x), t(Wg), t(Wu), t(Wd)
+    eu = torch.tensor(e_of_u)
+    rows = torch.tensor(p.row_index.astype(np.int64))
+    h = xt[rows]
+    a = torch.einsum("pij,pj->pi", Wgt[eu], h)
+    b = torch.einsum("pij,pj->pi", Wut[eu], h)
+    phi = torch.nn.functional.silu(a) * b
+    contrib = torch.tensor(alpha, dtype=torch.float64)[:, None] * torch.einsum(
+        "pij,pj->pi", Wdt[eu], phi)
+    y = torch.zeros(x.shape[0], Wd.shape[1], dtype=torch.float64).index_add(0, rows, contrib)
+    (y * torch.tensor(g)).sum().backward()
+    return (Wdt.grad.numpy(), np.concatenate([Wgt.grad.numpy(), Wut.grad.numpy()], axis=1),
+            xt.grad.numpy())
+
+
+def check_glu_chain_autograd(orc):
+    """The chained MLP backward (down -> SiLU-GLU -> gate/up on the compacted
+    layout): with q = n it is torch.autograd of the routed expert MLP, the
+    token's input gradient being the sum of its pairs' dx; with a real quota
+    it is the same autograd with the routing weight of dropped pairs set to 0,
+    and dropped pairs get zero dx.  Gate rows come first in W2."""
+    p, x, xt, Wg, Wu, Wd, g, a, b, phi, e_of_u = _mlp_moe(51)
+    W2 = np.concatenate([Wg, Wu], axis=1)
+    tok = p.row_index.astype(np.int64)
+    for policy in (("ratio", 1, 1), ("ratio", 1, 2)):
+        out = orc.pruned_backward(p.counts, policy, p.alpha, g, phi, Wd, p.row_index, "f64",
+                                  glu=(a, b, xt, W2))
+        keep = out["keep"]
+        if policy[1] != policy[2]:
+            assert 0 < keep.sum() < p.P
+        dWd, dW2, dx = _mlp_autograd(p, x, Wg, Wu, Wd, g, e_of_u, np.where(keep, p.alpha, 0.0))
+        assert np.abs(out["dW"] - dWd).max() <= 1e-12 * np.abs(dWd).max()
+        assert np.abs(out["dW2"] - dW2).max() <= 1e-12 * np.abs(dW2).max()
+        dx_tok = np.zeros_like(x)
+        np.add.at(dx_tok, tok, out["dx"])
+        assert np.abs(dx_tok - dx).max() <= 1e-12 * np.abs(dx).max()
+        assert np.all(out["dx"][~keep] == 0)
+        assert out["dgu_c"].shape == (int(keep.sum()), 2 * a.shape[1])
+
+
+def check_glu_chain_sampled(orc):
+    """The sampled chain helpers agree with the full chain."""
+    p = W.make_problem(P=60, E=3, d_out=16, d_in=8, counts=[30, 5, 25], gate_up=(16, 12),
+                       glu=True, seed=8)
+    gu, gl = p.gate_up, p.glu
+    out = orc.pruned_backward(p.counts, ("ratio", 3, 4), p.alpha, p.g, p.phi, p.W, None,
+                              p.dtype, glu=(gl.a, gl.b, gu.x, gu.W2))
+    o_idx, i_idx = [0, 3, 9, 15], [2, 11]
+    for e in range(p.E):
+        blk = orc.glu_weight_grad_block(out["seg"], out["perm"], None, p.alpha, p.g, p.W,
+                                        gl.a, gl.b, gu.x, p.dtype, e, o_idx, i_idx)
+        assert np.allclose(blk, out["dW2"][e][np.ix_(o_idx, i_idx)], rtol=1e-13, atol=1e-300)
+    js = [0, 7, len(out["perm"]) - 1]
+    rows = orc.glu_chain_rows(out["seg"], out["perm"], None, p.g, p.W, gl.a, gl.b, p.dtype, js)
+    assert np.allclose(rows, out["dgu_c"][js], rtol=1e-13, atol=0)
+    pairs = [0, 4, 31, 36, 59]
+    dx = orc.glu_input_grad_rows(p.counts, out["keep"], None, p.alpha, p.g, p.W, gl.a, gl.b,
+                                 gu.W2, p.dtype, pairs)
+    assert np.allclose(dx, out["dx"][pairs], rtol=1e-13, atol=0)
+
+
 def check_sampled_match_full(orc):
     """The sampled-output helpers agree with the full computation."""
     p = tiny(9, dtype="bf16", E=4, counts=[30, 0, 17, 21], d_out=24, d_in=16)
@@ -246,7 +329,8 @@ def check_sampled_match_full(orc):
 CHECKS = [check_quota_example, check_score_bruteforce, check_gradient_scores,
           check_select_bruteforce,
           check_compact_invariants, check_dense_equivalence, check_drop_identities,
-          check_gate_up_inherits, check_sampled_match_full]
+          check_gate_up_inherits, check_glu_chain_autograd, check_glu_chain_sampled,
+          check_sampled_match_full]
 
 
 @pytest.mark.parametrize("check", CHECKS, ids=lambda c: c.__name__)
@@ -344,6 +428,27 @@ def _gradient_scores_unsquared(g, row_index, dtype, P, rule, block_rows=4096):
     v = O.gradient_scores(g, row_index, dtype, P, rule, block_rows)
     return np.sqrt(v) if rule == "sqnorm" else v
 
+def _glu_derivative_is_sigmoid(dphi, a, b):
+    s = 1.0 / (1.0 + np.exp(-a))
+    return np.concatenate([dphi * b * s, dphi * a * s], axis=1)
+
+
+def _glu_halves_swapped(dphi, a, b):
+    d = a.shape[1]
+    r = O.silu_glu_grad(dphi, a, b)
+    return np.concatenate([r[:, d:], r[:, :d]], axis=1)
+
+
+def _glu_up_uses_b(dphi, a, b):
+    r = O.silu_glu_grad(dphi, a, b)
+    r[:, a.shape[1]:] = dphi * b
+    return r
+
+
+def _glu_chain_transposed_ab(seg, perm, g_c, W, a, b, dtype):
+    return O.glu_chain_grad(seg, perm, g_c, W, b, a, dtype)
+
+
 MUTANTS = {
     "score_alpha_not_squared": dict(lrm_scores=_scores_alpha_not_squared),
     "score_drops_phi_term": dict(lrm_scores=_scores_no_phi),
@@ -356,6 +461,10 @@ MUTANTS = {
     "dropped_rows_nonzero": dict(input_grad=_input_grad_keep_dropped_rows),
     "l1_rule_uses_squares": dict(gradient_scores=_gradient_scores_l1_squares),
     "sqnorm_rule_not_squared": dict(gradient_scores=_gradient_scores_unsquared),
+    "glu_derivative_is_sigmoid": dict(silu_glu_grad=_glu_derivative_is_sigmoid),
+    "glu_halves_swapped": dict(silu_glu_grad=_glu_halves_swapped),
+    "glu_up_uses_b": dict(silu_glu_grad=_glu_up_uses_b),
+    "glu_chain_swaps_a_b": dict(glu_chain_grad=_glu_chain_transposed_ab),
 }
 
 
