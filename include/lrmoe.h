@@ -229,7 +229,9 @@ lrmoe_status lrmoe_mask_alpha(int64_t P, const uint8_t* keep, const float* alpha
  * NULL for row u of pair u) pick the source rows of g and phi; the kept
  * rows are copied bit for bit into g_c [M, d_out] and phi_c [M, d_in], alpha
  * into alpha_c [M], and dphi_zero (or NULL) gets zero rows for dropped
- * pairs. */
+ * pairs.  g and g_c may both be NULL: only phi rows and alpha are gathered
+ * (the gate/up output gradient of lrmoe_grouped_backward_glu is already
+ * compacted). */
 lrmoe_status lrmoe_gather_compact(
     const lrmoe_problem* pb, const int32_t* perm, const uint8_t* keep,
     const int32_t* g_row_index, const int32_t* phi_row_index,
@@ -247,6 +249,34 @@ lrmoe_status lrmoe_grouped_backward(
     const void* g_c, const void* phi_c, const void* W, float* dW, float* dphi,
     void* workspace, size_t ws_bytes, void* stream);
 
+/* The expert MLP's activation backward, chained on the compacted layout.
+ * The models trained in "What the measurements show" ("LRMoE: Trimming
+ * Backward Work in Memory-Bound MoE Training": Qwen3-30B-A3B,
+ * GLM4.5-106B-A12B) have gated-MLP experts whose down projection reads
+ * phi = SiLU(a) * b, a and b being the saved gate and up pre-activations.
+ * The pages do not spell this step out (a reading); they only say that the
+ * original layout is restored after the compacted GEMMs ("LRMoE poda a
+ * passagem reversa do MoE e acelera o treinamento em 21-45%", compaction
+ * bullet), which this entry point postpones past the activation backward.  Same as lrmoe_grouped_backward for dW (the down projection's),
+ * but instead of dphi it writes, for every compacted row j (pair
+ * u = perm[j] of expert e), with d = W_e^T g_c[j] before the routing weight:
+ *   dgu_c[j] = [ d * b_u * SiLU'(a_u)  |  d * SiLU(a_u) ]
+ * SiLU'(a) = s (1 + a (1 - s)), s = sigmoid(a), in float32, each entry
+ * rounded once to bf16.  dgu_c is bf16 [M, 2 d_in], gate half first: the
+ * gate/up projection's output gradient, already compacted, so that
+ * lrmoe_gather_compact (g = g_c = NULL) of that projection's inputs and
+ * lrmoe_grouped_backward with g_c = dgu_c and the same perm and alpha_c
+ * (alpha applied once, there) finish the chain.  No original-layout dphi is
+ * written and none needs zeroing.
+ *   act_a, act_b  bf16 [P, d_in], pair-indexed like phi.
+ * bf16 storage only (LRMOE_ERR_DTYPE otherwise); other errors as for
+ * lrmoe_grouped_backward. */
+lrmoe_status lrmoe_grouped_backward_glu(
+    const lrmoe_problem* pb, const int32_t* perm, const float* alpha_c,
+    const void* g_c, const void* phi_c, const void* W, float* dW,
+    const void* act_a, const void* act_b, void* dgu_c, void* workspace,
+    size_t ws_bytes, void* stream);
+
 /* Per-kernel timing.  Each entry point below launches a fixed sequence of
  * kernels; for every non-NULL pair, `before` and `after` (hipEvent_t created
  * by the caller with timing enabled) are recorded on `stream` right before
@@ -254,7 +284,8 @@ lrmoe_status lrmoe_grouped_backward(
  * (an empty range) leave their events unrecorded.
  *   lrmoe_score_select_compact_timed: [0] score  [1] select+scan  [2] gather
  *   lrmoe_select_compact_timed:       [1] select+scan  [2] gather
- *   lrmoe_grouped_backward_timed:     [0] operand prologue  [1] grouped GEMM
+ *   lrmoe_grouped_backward_timed,
+ *   lrmoe_grouped_backward_glu_timed: [0] operand prologue  [1] grouped GEMM
  *                                     [2] split-K reduction */
 #define LRMOE_TIMING_SLOTS 4
 typedef struct {
@@ -283,6 +314,13 @@ lrmoe_status lrmoe_grouped_backward_timed(
     const lrmoe_problem* pb, const int32_t* perm, const float* alpha_c,
     const void* g_c, const void* phi_c, const void* W, float* dW, float* dphi,
     void* workspace, size_t ws_bytes, void* stream, const lrmoe_timing* timing);
+
+/* lrmoe_grouped_backward_glu with per-kernel events (timing may be NULL). */
+lrmoe_status lrmoe_grouped_backward_glu_timed(
+    const lrmoe_problem* pb, const int32_t* perm, const float* alpha_c,
+    const void* g_c, const void* phi_c, const void* W, float* dW,
+    const void* act_a, const void* act_b, void* dgu_c, void* workspace,
+    size_t ws_bytes, void* stream, const lrmoe_timing* timing);
 
 #ifdef __cplusplus
 }

@@ -250,6 +250,181 @@ lrmoe_status select_compact(const lrmoe_problem* pb, bool compute_scores, const 
   return LRMOE_OK;
 }
 
+// Shared body of the grouped-backward entry points.  glu_out != nullptr: the
+// SiLU-GLU chain (dphi is then nullptr and the input-gradient tiles write the
+// compacted gate/up output gradient instead).
+lrmoe_status grouped_backward(const lrmoe_problem* pb, const int32_t* perm, const float* alpha_c,
+                              const void* g_c, const void* phi_c, const void* W, float* dW,
+                              float* dphi, const uint16_t* glu_a, const uint16_t* glu_b,
+                              uint16_t* glu_out, void* workspace, size_t ws_bytes, void* stream,
+                              const lrmoe_timing* timing) {
+  Checked c;
+  LRMOE_TRY(check_problem(pb, c));
+  const int64_t M = c.M;
+  LRMOE_TRY(need(alpha_c, M));
+  LRMOE_TRY(need(g_c, M));
+  LRMOE_TRY(need(phi_c, M));
+  LRMOE_TRY(need(W, 1));
+  LRMOE_TRY(need(dW, 1));
+  LRMOE_TRY(optional(dphi));
+  const bool glu = glu_out != nullptr;
+  if (glu) {
+    LRMOE_TRY(need(glu_a, pb->P));
+    LRMOE_TRY(need(glu_b, pb->P));
+    LRMOE_TRY(need(glu_out, M));
+  }
+  if (dphi != nullptr || glu) LRMOE_TRY(need(perm, M));
+  const GemmWorkspace wl = gemm_workspace(pb, M);
+  if (ws_bytes < wl.total) return LRMOE_ERR_WORKSPACE;
+  LRMOE_TRY(need(workspace, (int64_t)wl.total));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  const int E = pb->E;
+  const int d_out = pb->d_out, d_in = pb->d_in;
+  GemmTable t;
+  memset(&t, 0, sizeof(t));
+  t.E = E;
+  t.tiles_n = (d_in + kTile - 1) / kTile;
+  t.dw_tiles_m = (d_out + kTile - 1) / kTile;
+  t.kc = wl.kc;
+  group_shape(t.tiles_n, 3, t.dw_gm, t.dw_gn);
+  group_shape(t.tiles_n, 6, t.dp_gm, t.dp_gn);
+  for (int e = 0; e <= E; ++e) t.seg_off[e] = c.tab.seg_off[e];
+
+  // Groups.  Weight gradient: every expert (zeros for q_e = 0) and K chunk;
+  // input gradient: the experts' row tiles.  Work of a group ~ tiles x K steps
+  // x MFMA passes.
+  std::vector<int> order(E);
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int a, int b) { return pb->quotas[a] > pb->quotas[b]; });
+  const int ngn_dw = (t.tiles_n + t.dw_gn - 1) / t.dw_gn;
+  const int per_chunk = ((t.dw_tiles_m + t.dw_gm - 1) / t.dw_gm) * ngn_dw;
+  const int ngn_dp = (t.tiles_n + t.dp_gn - 1) / t.dp_gn;
+  const int terms_dw = 1 + (wl.dw_pa == 2) + (wl.dw_pb == 2);
+  const int terms_dp = 1 + (wl.dp_pa == 2) + (wl.dp_pb == 2);
+  struct G { int64_t work; uint32_t desc; };
+  std::vector<G> groups;
+  int32_t g = 0;
+  for (int r = 0; r < E; ++r) {
+    const int e = order[r];
+    const int q = (int)pb->quotas[e];
+    const int S = dw_chunks(q, t.kc);
+    t.f.dw_goff[r] = g;
+    t.f.order[r] = (uint8_t)e;
+    g += per_chunk * S;
+    for (int ch = 0; ch < S; ++ch) {
+      const int klen = S > 1 ? std::min(t.kc, q - ch * t.kc) : q;
+      for (int sg = 0; sg < per_chunk; ++sg)
+        groups.push_back({(int64_t)((klen + kStepK - 1) / kStepK + 1) * terms_dw * kGroupSlots,
+                          group_desc(true, e, ch, sg)});
+    }
+  }
+  t.f.dw_goff[E] = g;
+  t.dw_groups = g;
+  for (int e = 0; e < E; ++e) {
+    t.f.dp_goff[e] = g;
+    if (dphi == nullptr && !glu) continue;
+    const int64_t mt = (pb->quotas[e] + kTile - 1) / kTile;
+    const int n = (int)(((mt + t.dp_gm - 1) / t.dp_gm) * ngn_dp);
+    g += n;
+    for (int sg = 0; sg < n; ++sg)
+      groups.push_back({(int64_t)((d_out + kStepK - 1) / kStepK + 1) * terms_dp * kGroupSlots,
+                        group_desc(false, e, 0, sg)});
+  }
+  t.f.dp_goff[E] = g;
+  t.total_groups = g;
+  bool table_ok = (int)groups.size() <= kMaxGroups && E <= 256;
+  for (int e = 0; e < E && table_ok; ++e) table_ok = dw_chunks((int)pb->quotas[e], t.kc) <= 256;
+  if (table_ok) {
+    // Longest first, each to the XCD with the least work so far; queues keep
+    // that order.  (The formula-order tables above are overwritten: union.)
+    std::vector<int> idx(groups.size());
+    std::iota(idx.begin(), idx.end(), 0);
+    std::stable_sort(idx.begin(), idx.end(),
+                     [&](int a, int b) { return groups[a].work > groups[b].work; });
+    std::vector<std::vector<uint32_t>> qs(kXcds);
+    int64_t load[kXcds] = {0};
+    for (int i : idx) {
+      int best = 0;
+      for (int x = 1; x < kXcds; ++x)
+        if (load[x] < load[best]) best = x;
+      load[best] += groups[i].work;
+      qs[best].push_back(groups[i].desc);
+    }
+    t.use_table = 1;
+    int32_t o = 0;
+    for (int x = 0; x < kXcds; ++x) {
+      t.qoff[x] = o;
+      for (uint32_t d : qs[x]) t.groups[o++] = d;
+    }
+    t.qoff[kXcds] = o;
+  }
+
+  // Prologue: bf16 operand planes.
+  LRMOE_TRY(mark(timing, false, 0, s));
+  char* ws = reinterpret_cast<char*>(workspace);
+  auto plane = [&](size_t off) { return reinterpret_cast<uint16_t*>(ws + off); };
+  int32_t* heads = reinterpret_cast<int32_t*>(ws + wl.heads);
+  GemmOperands ops;
+  memset(&ops, 0, sizeof(ops));
+  const uint16_t* g16 = reinterpret_cast<const uint16_t*>(g_c);
+  const uint16_t* p16 = reinterpret_cast<const uint16_t*>(phi_c);
+  const uint16_t* w16 = reinterpret_cast<const uint16_t*>(W);
+  if (pb->dtype == LRMOE_BF16) {
+    const bool exact = pb->dw_mode == LRMOE_DW_EXACT;
+    uint16_t* hi = plane(wl.b_hi);
+    uint16_t* lo = exact ? plane(wl.b_lo) : nullptr;
+    const void* src = wl.alpha_on_phi ? phi_c : g_c;
+    const int cols = wl.alpha_on_phi ? d_in : d_out;
+    LRMOE_TRY(hip_status(launch_split(LRMOE_BF16, src, M, cols, alpha_c, hi, lo, s, heads, kXcds)));
+    if (wl.alpha_on_phi) {
+      ops.dw_a[0] = g16;
+      ops.dw_b[0] = hi;
+      ops.dw_b[1] = lo;
+    } else {
+      ops.dw_a[0] = hi;
+      ops.dw_a[1] = lo;
+      ops.dw_b[0] = p16;
+    }
+    ops.dw_pa = wl.dw_pa;
+    ops.dw_pb = wl.dw_pb;
+    ops.dp_a[0] = g16;
+    ops.dp_b[0] = w16;
+    ops.dp_pa = ops.dp_pb = 1;
+  } else {
+    LRMOE_TRY(hip_status(launch_split(LRMOE_F32, g_c, M, d_out, nullptr, plane(wl.a_hi),
+                                      plane(wl.a_lo), s, heads, kXcds)));
+    LRMOE_TRY(hip_status(launch_split(LRMOE_F32, phi_c, M, d_in, alpha_c, plane(wl.b_hi),
+                                      plane(wl.b_lo), s)));
+    if (dphi != nullptr)
+      LRMOE_TRY(hip_status(launch_split(LRMOE_F32, W, (int64_t)E * d_out, d_in, nullptr,
+                                        plane(wl.w_hi), plane(wl.w_lo), s)));
+    ops.dw_a[0] = ops.dp_a[0] = plane(wl.a_hi);
+    ops.dw_a[1] = ops.dp_a[1] = plane(wl.a_lo);
+    ops.dw_b[0] = plane(wl.b_hi);
+    ops.dw_b[1] = plane(wl.b_lo);
+    ops.dp_b[0] = plane(wl.w_hi);
+    ops.dp_b[1] = plane(wl.w_lo);
+    ops.dw_pa = ops.dw_pb = ops.dp_pa = ops.dp_pb = 2;
+  }
+  (void)w16;
+  LRMOE_TRY(mark(timing, true, 0, s));
+  ops.partials = reinterpret_cast<float*>(ws + wl.partials);
+  ops.queue_heads = heads;   // cleared by the first prologue launch
+  ops.glu_a = glu_a;
+  ops.glu_b = glu_b;
+  ops.glu_out = glu_out;
+  LRMOE_TRY(mark(timing, false, 1, s));
+  LRMOE_TRY(hip_status(launch_grouped_backward(t, ops, perm, alpha_c, dW, dphi, d_out, d_in,
+                                               (int32_t)pb->P, s)));
+  LRMOE_TRY(mark(timing, true, 1, s));
+  LRMOE_TRY(mark(timing, false, 2, s));
+  LRMOE_TRY(hip_status(launch_reduce_partials(t, ops.partials, dW, d_out, d_in, s)));
+  LRMOE_TRY(mark(timing, true, 2, s));
+  return LRMOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -409,14 +584,17 @@ lrmoe_status lrmoe_gather_compact(const lrmoe_problem* pb, const int32_t* perm,
   Checked c;
   LRMOE_TRY(check_problem(pb, c));
   const int64_t P = pb->P, M = c.M;
-  if (g_row_index == nullptr && pb->T != P) return LRMOE_ERR_SHAPE;
+  const bool with_g = g != nullptr || g_c != nullptr;   // both NULL: phi rows only
+  if (with_g && g_row_index == nullptr && pb->T != P) return LRMOE_ERR_SHAPE;
   LRMOE_TRY(need(perm, M));
   LRMOE_TRY(need(alpha, P));
-  LRMOE_TRY(need(g, M > 0 ? pb->T : 0));
+  if (with_g) {
+    LRMOE_TRY(need(g, M > 0 ? pb->T : 0));
+    LRMOE_TRY(need(g_c, M));
+  }
   LRMOE_TRY(need(phi, M));
   LRMOE_TRY(optional(g_row_index));
   LRMOE_TRY(optional(phi_row_index));
-  LRMOE_TRY(need(g_c, M));
   LRMOE_TRY(need(phi_c, M));
   LRMOE_TRY(need(alpha_c, M));
   LRMOE_TRY(optional(dphi_zero));
@@ -440,162 +618,33 @@ lrmoe_status lrmoe_grouped_backward_timed(const lrmoe_problem* pb, const int32_t
                                           const void* phi_c, const void* W, float* dW,
                                           float* dphi, void* workspace, size_t ws_bytes,
                                           void* stream, const lrmoe_timing* timing) {
-  Checked c;
-  LRMOE_TRY(check_problem(pb, c));
-  const int64_t M = c.M;
-  LRMOE_TRY(need(alpha_c, M));
-  LRMOE_TRY(need(g_c, M));
-  LRMOE_TRY(need(phi_c, M));
-  LRMOE_TRY(need(W, 1));
-  LRMOE_TRY(need(dW, 1));
-  LRMOE_TRY(optional(dphi));
-  if (dphi != nullptr) LRMOE_TRY(need(perm, M));
-  const GemmWorkspace wl = gemm_workspace(pb, M);
-  if (ws_bytes < wl.total) return LRMOE_ERR_WORKSPACE;
-  LRMOE_TRY(need(workspace, (int64_t)wl.total));
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return grouped_backward(pb, perm, alpha_c, g_c, phi_c, W, dW, dphi, nullptr, nullptr, nullptr,
+                          workspace, ws_bytes, stream, timing);
+}
 
-  const int E = pb->E;
-  const int d_out = pb->d_out, d_in = pb->d_in;
-  GemmTable t;
-  memset(&t, 0, sizeof(t));
-  t.E = E;
-  t.tiles_n = (d_in + kTile - 1) / kTile;
-  t.dw_tiles_m = (d_out + kTile - 1) / kTile;
-  t.kc = wl.kc;
-  group_shape(t.tiles_n, 3, t.dw_gm, t.dw_gn);
-  group_shape(t.tiles_n, 6, t.dp_gm, t.dp_gn);
-  for (int e = 0; e <= E; ++e) t.seg_off[e] = c.tab.seg_off[e];
+lrmoe_status lrmoe_grouped_backward_glu(const lrmoe_problem* pb, const int32_t* perm,
+                                        const float* alpha_c, const void* g_c, const void* phi_c,
+                                        const void* W, float* dW, const void* act_a,
+                                        const void* act_b, void* dgu_c, void* workspace,
+                                        size_t ws_bytes, void* stream) {
+  return lrmoe_grouped_backward_glu_timed(pb, perm, alpha_c, g_c, phi_c, W, dW, act_a, act_b,
+                                          dgu_c, workspace, ws_bytes, stream, nullptr);
+}
 
-  // Groups.  Weight gradient: every expert (zeros for q_e = 0) and K chunk;
-  // input gradient: the experts' row tiles.  Work of a group ~ tiles x K steps
-  // x MFMA passes.
-  std::vector<int> order(E);
-  std::iota(order.begin(), order.end(), 0);
-  std::stable_sort(order.begin(), order.end(),
-                   [&](int a, int b) { return pb->quotas[a] > pb->quotas[b]; });
-  const int ngn_dw = (t.tiles_n + t.dw_gn - 1) / t.dw_gn;
-  const int per_chunk = ((t.dw_tiles_m + t.dw_gm - 1) / t.dw_gm) * ngn_dw;
-  const int ngn_dp = (t.tiles_n + t.dp_gn - 1) / t.dp_gn;
-  const int terms_dw = 1 + (wl.dw_pa == 2) + (wl.dw_pb == 2);
-  const int terms_dp = 1 + (wl.dp_pa == 2) + (wl.dp_pb == 2);
-  struct G { int64_t work; uint32_t desc; };
-  std::vector<G> groups;
-  int32_t g = 0;
-  for (int r = 0; r < E; ++r) {
-    const int e = order[r];
-    const int q = (int)pb->quotas[e];
-    const int S = dw_chunks(q, t.kc);
-    t.f.dw_goff[r] = g;
-    t.f.order[r] = (uint8_t)e;
-    g += per_chunk * S;
-    for (int ch = 0; ch < S; ++ch) {
-      const int klen = S > 1 ? std::min(t.kc, q - ch * t.kc) : q;
-      for (int sg = 0; sg < per_chunk; ++sg)
-        groups.push_back({(int64_t)((klen + kStepK - 1) / kStepK + 1) * terms_dw * kGroupSlots,
-                          group_desc(true, e, ch, sg)});
-    }
-  }
-  t.f.dw_goff[E] = g;
-  t.dw_groups = g;
-  for (int e = 0; e < E; ++e) {
-    t.f.dp_goff[e] = g;
-    if (dphi == nullptr) continue;
-    const int64_t mt = (pb->quotas[e] + kTile - 1) / kTile;
-    const int n = (int)(((mt + t.dp_gm - 1) / t.dp_gm) * ngn_dp);
-    g += n;
-    for (int sg = 0; sg < n; ++sg)
-      groups.push_back({(int64_t)((d_out + kStepK - 1) / kStepK + 1) * terms_dp * kGroupSlots,
-                        group_desc(false, e, 0, sg)});
-  }
-  t.f.dp_goff[E] = g;
-  t.total_groups = g;
-  bool table_ok = (int)groups.size() <= kMaxGroups && E <= 256;
-  for (int e = 0; e < E && table_ok; ++e) table_ok = dw_chunks((int)pb->quotas[e], t.kc) <= 256;
-  if (table_ok) {
-    // Longest first, each to the XCD with the least work so far; queues keep
-    // that order.  (The formula-order tables above are overwritten: union.)
-    std::vector<int> idx(groups.size());
-    std::iota(idx.begin(), idx.end(), 0);
-    std::stable_sort(idx.begin(), idx.end(),
-                     [&](int a, int b) { return groups[a].work > groups[b].work; });
-    std::vector<std::vector<uint32_t>> qs(kXcds);
-    int64_t load[kXcds] = {0};
-    for (int i : idx) {
-      int best = 0;
-      for (int x = 1; x < kXcds; ++x)
-        if (load[x] < load[best]) best = x;
-      load[best] += groups[i].work;
-      qs[best].push_back(groups[i].desc);
-    }
-    t.use_table = 1;
-    int32_t o = 0;
-    for (int x = 0; x < kXcds; ++x) {
-      t.qoff[x] = o;
-      for (uint32_t d : qs[x]) t.groups[o++] = d;
-    }
-    t.qoff[kXcds] = o;
-  }
-
-  // Prologue: bf16 operand planes.
-  LRMOE_TRY(mark(timing, false, 0, s));
-  char* ws = reinterpret_cast<char*>(workspace);
-  auto plane = [&](size_t off) { return reinterpret_cast<uint16_t*>(ws + off); };
-  int32_t* heads = reinterpret_cast<int32_t*>(ws + wl.heads);
-  GemmOperands ops;
-  memset(&ops, 0, sizeof(ops));
-  const uint16_t* g16 = reinterpret_cast<const uint16_t*>(g_c);
-  const uint16_t* p16 = reinterpret_cast<const uint16_t*>(phi_c);
-  const uint16_t* w16 = reinterpret_cast<const uint16_t*>(W);
-  if (pb->dtype == LRMOE_BF16) {
-    const bool exact = pb->dw_mode == LRMOE_DW_EXACT;
-    uint16_t* hi = plane(wl.b_hi);
-    uint16_t* lo = exact ? plane(wl.b_lo) : nullptr;
-    const void* src = wl.alpha_on_phi ? phi_c : g_c;
-    const int cols = wl.alpha_on_phi ? d_in : d_out;
-    LRMOE_TRY(hip_status(launch_split(LRMOE_BF16, src, M, cols, alpha_c, hi, lo, s, heads, kXcds)));
-    if (wl.alpha_on_phi) {
-      ops.dw_a[0] = g16;
-      ops.dw_b[0] = hi;
-      ops.dw_b[1] = lo;
-    } else {
-      ops.dw_a[0] = hi;
-      ops.dw_a[1] = lo;
-      ops.dw_b[0] = p16;
-    }
-    ops.dw_pa = wl.dw_pa;
-    ops.dw_pb = wl.dw_pb;
-    ops.dp_a[0] = g16;
-    ops.dp_b[0] = w16;
-    ops.dp_pa = ops.dp_pb = 1;
-  } else {
-    LRMOE_TRY(hip_status(launch_split(LRMOE_F32, g_c, M, d_out, nullptr, plane(wl.a_hi),
-                                      plane(wl.a_lo), s, heads, kXcds)));
-    LRMOE_TRY(hip_status(launch_split(LRMOE_F32, phi_c, M, d_in, alpha_c, plane(wl.b_hi),
-                                      plane(wl.b_lo), s)));
-    if (dphi != nullptr)
-      LRMOE_TRY(hip_status(launch_split(LRMOE_F32, W, (int64_t)E * d_out, d_in, nullptr,
-                                        plane(wl.w_hi), plane(wl.w_lo), s)));
-    ops.dw_a[0] = ops.dp_a[0] = plane(wl.a_hi);
-    ops.dw_a[1] = ops.dp_a[1] = plane(wl.a_lo);
-    ops.dw_b[0] = plane(wl.b_hi);
-    ops.dw_b[1] = plane(wl.b_lo);
-    ops.dp_b[0] = plane(wl.w_hi);
-    ops.dp_b[1] = plane(wl.w_lo);
-    ops.dw_pa = ops.dw_pb = ops.dp_pa = ops.dp_pb = 2;
-  }
-  (void)w16;
-  LRMOE_TRY(mark(timing, true, 0, s));
-  ops.partials = reinterpret_cast<float*>(ws + wl.partials);
-  ops.queue_heads = heads;   // cleared by the first prologue launch
-  LRMOE_TRY(mark(timing, false, 1, s));
-  LRMOE_TRY(hip_status(launch_grouped_backward(t, ops, perm, alpha_c, dW, dphi, d_out, d_in,
-                                               (int32_t)pb->P, s)));
-  LRMOE_TRY(mark(timing, true, 1, s));
-  LRMOE_TRY(mark(timing, false, 2, s));
-  LRMOE_TRY(hip_status(launch_reduce_partials(t, ops.partials, dW, d_out, d_in, s)));
-  LRMOE_TRY(mark(timing, true, 2, s));
-  return LRMOE_OK;
+lrmoe_status lrmoe_grouped_backward_glu_timed(const lrmoe_problem* pb, const int32_t* perm,
+                                              const float* alpha_c, const void* g_c,
+                                              const void* phi_c, const void* W, float* dW,
+                                              const void* act_a, const void* act_b, void* dgu_c,
+                                              void* workspace, size_t ws_bytes, void* stream,
+                                              const lrmoe_timing* timing) {
+  if (pb == nullptr) return LRMOE_ERR_NULL;
+  if (pb->dtype != LRMOE_BF16) return LRMOE_ERR_DTYPE;
+  if (act_a == nullptr || act_b == nullptr || dgu_c == nullptr) return LRMOE_ERR_NULL;
+  return grouped_backward(pb, perm, alpha_c, g_c, phi_c, W, dW, nullptr,
+                          reinterpret_cast<const uint16_t*>(act_a),
+                          reinterpret_cast<const uint16_t*>(act_b),
+                          reinterpret_cast<uint16_t*>(dgu_c), workspace, ws_bytes, stream,
+                          timing);
 }
 
 }  // extern "C"

@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256) void gather_kernel(
     if ((uint32_t)u >= (uint32_t)P) return;   // perm holds pair indices < P
     const int64_t gr = g_row_index ? (int64_t)g_row_index[u] : (int64_t)u;
     const int64_t pr = phi_row_index ? (int64_t)phi_row_index[u] : (int64_t)u;
-    copy_row(g + gr * gch, g_c + (int64_t)j * gch, gch, lane);
+    if (g_c != nullptr) copy_row(g + gr * gch, g_c + (int64_t)j * gch, gch, lane);
     copy_row(phi + pr * pch, phi_c + (int64_t)j * pch, pch, lane);
     if (lane == 0) alpha_c[j] = alpha[u];
   } else if (dphi_zero != nullptr && job < (int64_t)M + P) {

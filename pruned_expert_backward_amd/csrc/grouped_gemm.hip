@@ -64,6 +64,7 @@ namespace {
 #define LDS_AS __attribute__((address_space(3)))
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -273,7 +274,7 @@ constexpr int kPermBytes = BM * 8;   // dphi epilogue: destination row + alpha p
 // The matrix core always has independent MFMAs queued while fragments and
 // stages move, and the global loads trickle out between MFMAs instead of
 // stalling the wave in a burst.
-template <bool IS_DW, int PA, int PB, int NS>
+template <bool IS_DW, int PA, int PB, int NS, bool GLU = false>
 struct Tile {
   static constexpr bool A_MC = IS_DW;
   static constexpr int kStage = (PA + PB) * kPlaneBytes;
@@ -527,6 +528,46 @@ struct Tile {
     }
   }
 
+  // ---- SiLU-GLU chain, one tile row: this lane holds dphi (before alpha)
+  // of compacted row j = pair u for 4 x 4 quads of columns.  With the saved
+  // pre-activations a, b of pair u: s = sigmoid(a), silu = a s,
+  // silu' = s (1 + a (1 - s)); gate gradient dphi * b * silu', up gradient
+  // dphi * silu, rounded to bf16 into glu_out[j] = [gate | up].
+  __device__ __forceinline__ void glu_row(const Args& args, int32_t u, int64_t j,
+                                          const f32x16 (&acc)[4][4], int a) const {
+    const int d_in = args.d_in;
+    const uint16_t* arow = args.ops.glu_a + (int64_t)u * d_in + n0;
+    const uint16_t* brow = args.ops.glu_b + (int64_t)u * d_in + n0;
+    uint16_t* gate = args.ops.glu_out + j * (2 * (int64_t)d_in) + n0;
+    uint16_t* up = gate + d_in;
+    const int cq = 4 * (lane >> 5);
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = wn * 128 + b * 32 + 8 * g + cq;
+        if (col >= d_in - n0) continue;
+        const u32x2 av = *reinterpret_cast<const u32x2*>(arow + col);
+        const u32x2 bv = *reinterpret_cast<const u32x2*>(brow + col);
+        bf16x4 go, uo;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t aw = av[k >> 1], bw = bv[k >> 1];
+          const float x = __uint_as_float((k & 1) ? (aw & 0xFFFF0000u) : (aw << 16));
+          const float y = __uint_as_float((k & 1) ? (bw & 0xFFFF0000u) : (bw << 16));
+          const float sg = 1.f / (1.f + expf(-x));
+          const float d = acc[a][b][4 * g + k];
+          go[k] = (__bf16)(d * y * (sg * (1.f + x * (1.f - sg))));
+          uo[k] = (__bf16)(d * (x * sg));
+        }
+        *reinterpret_cast<u32x2*>(gate + col) = __builtin_bit_cast(u32x2, go);
+        *reinterpret_cast<u32x2*>(up + col) = __builtin_bit_cast(u32x2, uo);
+        // keep the scheduler from hoisting every row's loads at once: the
+        // accumulators already hold all AGPRs and half the VGPR file is free
+        if (g == 3) __builtin_amdgcn_sched_barrier(0);
+      }
+  }
+
   // ---- epilogue.  Accumulator block (a, b) holds D[m][n] for tile row
   // m = wm*128 + a*32 + lane%32 and column n = wn*128 + b*32 + 8*(r/4) +
   // 4*(lane/32) + r%4 in register r: each register quad is 4 consecutive
@@ -562,6 +603,10 @@ struct Tile {
         }
       } else {
         const int32_t u = s_perm[lrow];
+        if constexpr (GLU) {   // SiLU-GLU chain: no dphi, no alpha
+          if (u >= 0) glu_row(args, u, seg + m0 + lrow, acc, a);
+          continue;
+        }
         scale = s_alpha[lrow];
         if (u >= 0) orow = args.dphi + (int64_t)u * d_in + n0;
       }
@@ -601,11 +646,11 @@ struct Cfg {
 // next tile's first loads are issued before the finished tile's stores, so
 // the store drain overlaps the next load latency.  Every workgroup exits when
 // its queue's counter passes the queue length.
-template <int DW_PA, int DW_PB, int DP_PA, int DP_PB>
+template <int DW_PA, int DW_PB, int DP_PA, int DP_PB, bool GLU>
 __global__ __launch_bounds__(kThreads, 1) void grouped_backward_kernel(Args args, GemmTable tab) {
   using C = Cfg<DW_PA, DW_PB, DP_PA, DP_PB>;
   using DwTile = Tile<true, DW_PA, DW_PB, C::NS_DW>;
-  using DpTile = Tile<false, DP_PA, DP_PB, C::NS_DP>;
+  using DpTile = Tile<false, DP_PA, DP_PB, C::NS_DP, GLU>;
   __shared__ __attribute__((aligned(16))) char smem_raw[C::bytes];
   LDS_AS char* smem = (LDS_AS char*)(smem_raw);
   LDS_AS char* prm = smem + C::stages;
@@ -662,14 +707,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_backward_kernel(Args args
   }
 }
 
-template <int DW_PA, int DW_PB, int DP_PA, int DP_PB>
+template <int DW_PA, int DW_PB, int DP_PA, int DP_PB, bool GLU = false>
 hipError_t launch(const Args& args, const GemmTable& tab, hipStream_t s) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
   const int blocks = (cus + kXcds - 1) / kXcds * kXcds;   // one per CU, a multiple of 8
-  hipLaunchKernelGGL((grouped_backward_kernel<DW_PA, DW_PB, DP_PA, DP_PB>), dim3(blocks),
+  hipLaunchKernelGGL((grouped_backward_kernel<DW_PA, DW_PB, DP_PA, DP_PB, GLU>), dim3(blocks),
                      dim3(kThreads), 0, s, args, tab);
   return hipGetLastError();
 }
@@ -825,6 +870,14 @@ hipError_t launch_grouped_backward(const GemmTable& tab, const GemmOperands& ops
                                    hipStream_t s) {
   const Args args{ops, alpha_c, perm, dW, dphi, d_out, d_in, P};
   const int key = ops.dw_pa * 1000 + ops.dw_pb * 100 + ops.dp_pa * 10 + ops.dp_pb;
+  if (ops.glu_out != nullptr) {   // SiLU-GLU chain: bf16 storage only
+    switch (key) {
+      case 1211: return launch<1, 2, 1, 1, true>(args, tab, s);
+      case 2111: return launch<2, 1, 1, 1, true>(args, tab, s);
+      case 1111: return launch<1, 1, 1, 1, true>(args, tab, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (key) {
     case 1211: return launch<1, 2, 1, 1>(args, tab, s);   // bf16, alpha folded into phi
     case 2111: return launch<2, 1, 1, 1>(args, tab, s);   // bf16, alpha folded into g

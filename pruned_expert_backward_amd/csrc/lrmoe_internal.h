@@ -86,6 +86,14 @@ struct GemmOperands {
   int32_t dw_pa, dw_pb, dp_pa, dp_pb;   // planes in use (1 or 2)
   float* partials;                // fp32 partial dW tiles of split experts
   int32_t* queue_heads;           // kXcds counters, zeroed by the prologue
+  // SiLU-GLU chain (glu_out != nullptr): the input-gradient tiles, instead of
+  // writing alpha * dphi, write the gate/up output gradient of each kept
+  // pair from its saved pre-activations a = glu_a[u], b = glu_b[u] ([P,
+  // d_in] bf16, u = perm[j]): glu_out[j] = [dphi*b*silu'(a), dphi*silu(a)]
+  // ([M, 2 d_in] bf16), dphi before alpha.
+  const uint16_t* glu_a;
+  const uint16_t* glu_b;
+  uint16_t* glu_out;
 };
 
 // Number of K chunks of an expert with q kept rows.

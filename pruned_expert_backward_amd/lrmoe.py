@@ -31,7 +31,8 @@ EXPORTS = ["lrmoe_abi_version", "lrmoe_status_string", "lrmoe_plan_quota",
            "lrmoe_workspace_size", "lrmoe_score_select_compact", "lrmoe_select_compact",
            "lrmoe_gather_compact", "lrmoe_grouped_backward", "lrmoe_score_select_compact_timed",
            "lrmoe_select_compact_timed", "lrmoe_grouped_backward_timed", "lrmoe_score_select",
-           "lrmoe_mask_alpha", "lrmoe_plan_quota_device"]
+           "lrmoe_mask_alpha", "lrmoe_plan_quota_device", "lrmoe_grouped_backward_glu",
+           "lrmoe_grouped_backward_glu_timed"]
 TIMING_SLOTS = 4
 
 
@@ -102,6 +103,11 @@ def lib() -> C.CDLL:
     L.lrmoe_grouped_backward_timed.restype = C.c_int
     L.lrmoe_grouped_backward_timed.argtypes = ([C.POINTER(Problem)] + [_P] * 8 +
                                                [C.c_size_t, _P, C.POINTER(Timing)])
+    L.lrmoe_grouped_backward_glu.restype = C.c_int
+    L.lrmoe_grouped_backward_glu.argtypes = [C.POINTER(Problem)] + [_P] * 10 + [C.c_size_t, _P]
+    L.lrmoe_grouped_backward_glu_timed.restype = C.c_int
+    L.lrmoe_grouped_backward_glu_timed.argtypes = ([C.POINTER(Problem)] + [_P] * 10 +
+                                                   [C.c_size_t, _P, C.POINTER(Timing)])
     if L.lrmoe_abi_version() != ABI_VERSION:
         raise RuntimeError("liblrmoe ABI version mismatch; rebuild the library")
     _lib_handle = L
@@ -317,17 +323,19 @@ def masked_dense_backward(plan: Plan, alpha, g, phi, W, out=None, ws=None, dense
 
 def gather_compact(plan: Plan, perm, keep, alpha, g, phi, g_row_index=None, phi_row_index=None,
                    out=None, zero_target: bool = True) -> dict:
+    """Kept rows of a projection that inherits a keep set; g=None gathers
+    the phi rows and alpha only."""
     dev = phi.device
     dt = plan.torch_dtype
     if out is None:
-        out = dict(g_c=_empty((plan.M, plan.d_out), dt, dev),
+        out = dict(g_c=_empty((plan.M, plan.d_out), dt, dev) if g is not None else None,
                    phi_c=_empty((plan.M, plan.d_in), dt, dev),
                    alpha_c=_empty((plan.M,), torch.float32, dev))
         if zero_target:
             out["dphi"] = _empty((plan.P, plan.d_in), torch.float32, dev)
     st = lib().lrmoe_gather_compact(C.byref(plan.struct), _ptr(perm), _ptr(keep),
                                     _ptr(g_row_index), _ptr(phi_row_index), _ptr(alpha), _ptr(g),
-                                    _ptr(phi), _ptr(out["g_c"]), _ptr(out["phi_c"]),
+                                    _ptr(phi), _ptr(out.get("g_c")), _ptr(out["phi_c"]),
                                     _ptr(out["alpha_c"]), _ptr(out.get("dphi")), _stream())
     check("lrmoe_gather_compact", st)
     return out
@@ -349,6 +357,54 @@ def grouped_backward(plan: Plan, perm, alpha_c, g_c, phi_c, W, dW=None, dphi=Non
     else:
         check("lrmoe_grouped_backward", lib().lrmoe_grouped_backward(*args))
     return dW
+
+
+def grouped_backward_glu(plan: Plan, perm, alpha_c, g_c, phi_c, W, act_a, act_b, dW=None,
+                         dgu_c=None, ws=None, timing: Optional["KernelTimer"] = None):
+    """Down projection's dW and, through the SiLU-GLU backward, the gate/up
+    output gradient of the kept pairs, compacted: returns (dW, dgu_c) with
+    dgu_c bf16 [M, 2 d_in] (gate half first, before alpha)."""
+    dev = W.device
+    if dW is None:
+        dW = _empty((plan.E, plan.d_out, plan.d_in), torch.float32, dev)
+    if dgu_c is None:
+        dgu_c = _empty((plan.M, 2 * plan.d_in), torch.bfloat16, dev)
+    if ws is None:
+        ws = workspace(plan, dev)
+    args = (C.byref(plan.struct), _ptr(perm), _ptr(alpha_c), _ptr(g_c), _ptr(phi_c), _ptr(W),
+            _ptr(dW), _ptr(act_a), _ptr(act_b), _ptr(dgu_c), _ptr(ws), ws.numel(), _stream())
+    if timing is not None:
+        check("lrmoe_grouped_backward_glu_timed",
+              lib().lrmoe_grouped_backward_glu_timed(*args, C.byref(timing.next_slots())))
+    else:
+        check("lrmoe_grouped_backward_glu", lib().lrmoe_grouped_backward_glu(*args))
+    return dW, dgu_c
+
+
+def glu_chain_backward(plan: Plan, plan2: Plan, alpha, g, phi, W, act_a, act_b, x, W2,
+                       g_row_index=None, x_row_index=None, out=None, ws=None) -> dict:
+    """The expert MLP's backward on one keep set: score, select, compact
+    (down projection), dW, the SiLU-GLU backward into the compacted gate/up
+    output gradient, the gather of the gate/up inputs x, and that
+    projection's dW2 and dx (dx rows of dropped pairs zeroed).  plan2
+    describes the gate/up projection (d_out = 2 d_in of plan, d_in =
+    d_model, the same counts and quotas)."""
+    dev = phi.device
+    if out is None:
+        out = alloc_select_outputs(plan, dev, zero_target=False)
+    if ws is None:   # one buffer for both projections
+        ws = torch.empty((max(plan.workspace_bytes(), plan2.workspace_bytes(), 16),),
+                         dtype=torch.uint8, device=dev)
+    out = score_select_compact(plan, alpha, g, phi, g_row_index=g_row_index, out=out, ws=ws)
+    out["dW"], out["dgu_c"] = grouped_backward_glu(plan, out["perm"], out["alpha_c"], out["g_c"],
+                                                   out["phi_c"], W, act_a, act_b, ws=ws)
+    c2 = gather_compact(plan2, out["perm"], out["keep"], alpha, None, x,
+                        phi_row_index=x_row_index)
+    out["x_c"] = c2["phi_c"]
+    out["dx"] = c2["dphi"]
+    out["dW2"] = grouped_backward(plan2, out["perm"], c2["alpha_c"], out["dgu_c"], c2["phi_c"],
+                                  W2, dphi=c2["dphi"], ws=ws)
+    return out
 
 
 class KernelTimer:

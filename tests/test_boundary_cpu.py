@@ -181,6 +181,29 @@ def test_grouped_backward_validation():
     assert f(C.byref(p.struct), *a) == 4
 
 
+def test_grouped_backward_glu_validation():
+    """The SiLU-GLU chain entry point: bf16 only; the saved pre-activations,
+    the gate/up output and perm are required; the usual workspace and
+    alignment rules hold."""
+    f = L.lib().lrmoe_grouped_backward_glu
+    p = plan()
+    n = p.workspace_bytes()
+    ok = [FAKE] * 10 + [n, None]   # perm alpha_c g_c phi_c W dW act_a act_b dgu_c ws
+    assert f(C.byref(plan(dtype=L.F32).struct), *ok) == 5
+    for i in (0, 1, 2, 3, 4, 5, 6, 7, 8, 9):
+        a = list(ok)
+        a[i] = None
+        assert f(C.byref(p.struct), *a) == 1, i
+    for i in (6, 7, 8):
+        a = list(ok)
+        a[i] = FAKE + 4
+        assert f(C.byref(p.struct), *a) == 4, i
+    a = list(ok)
+    a[10] = n - 1
+    assert f(C.byref(p.struct), *a) == 6
+    assert f(None, *ok) == 1
+
+
 def test_gather_compact_validation():
     p = plan()
     f = L.lib().lrmoe_gather_compact
@@ -193,6 +216,9 @@ def test_gather_compact_validation():
     a[1] = None
     a[10] = FAKE       # zero target needs the keep flags
     assert f(C.byref(p.struct), *a) == 1
+    a = list(ok)
+    a[5], a[7], a[8] = None, None, None   # g and g_c both NULL: phi rows only ...
+    assert f(C.byref(p.struct), *a) == 1  # ... and phi_c is still required
 
 
 def test_mask_alpha_and_score_select_validation():

@@ -196,6 +196,57 @@ def test_gate_up_inherits_keep_set():
     assert e1 <= U.TOL and e2 <= U.TOL, (e1, e2)
 
 
+GLU_CASES = [
+    # name, make_problem kwargs, dw_mode (the GEMM variant the chain runs in)
+    ("glu-alpha-on-phi", dict(P=2400, E=5, d_out=264, d_in=200, counts=[1100, 0, 700, 9, 591],
+                              gate_up=(400, 136)), lrmoe.DW_EXACT),
+    ("glu-alpha-on-g", dict(P=1800, E=4, d_out=136, d_in=328, zipf=1.6,
+                            gate_up=(656, 264)), lrmoe.DW_EXACT),
+    ("glu-bf16-single-rounding", dict(P=2000, E=6, d_out=256, d_in=256, zipf=1.2,
+                                      gate_up=(512, 128)), lrmoe.DW_BF16),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(GLU_CASES)), ids=[c[0] for c in GLU_CASES])
+def test_glu_chain(idx):
+    """The expert MLP chained on the compacted layout: down projection dW,
+    the SiLU-GLU backward written compacted by the input-gradient tiles
+    (dgu_c, bf16), then the gate/up projection's dW2 and dx on the same keep
+    set.  dgu_c holds one bf16 rounding of a float32 value: each entry within
+    2^-8 of its magnitude (the bf16 unit roundoff) plus 2e-5 max|ref| (float32
+    accumulation) of the oracle's float64 value; dW, dW2 and dx within the
+    usual 2e-3 max|ref| of the oracle chain, which stores dgu in bf16 too."""
+    name, kw, dw_mode = GLU_CASES[idx]
+    p = W.make_problem(seed=300 + idx, dtype="bf16", glu=True, policy=("ratio", 70, 100),
+                       name=name, **kw)
+    gu, gl = p.gate_up, p.glu
+    q = lrmoe.plan_quota(p.counts, p.policy)
+    plan = lrmoe.Plan(p.counts, q, p.d_out, p.d_in, lrmoe.BF16, dw_mode=dw_mode)
+    plan2 = lrmoe.Plan(p.counts, q, gu.d_out, gu.d_in, lrmoe.BF16, dw_mode=dw_mode)
+    d = U.dev
+    out = lrmoe.glu_chain_backward(plan, plan2, d(p.alpha), d(p.g), d(p.phi), d(p.W), d(gl.a),
+                                   d(gl.b), d(gu.x), d(gu.W2))
+    torch.cuda.synchronize()
+    ref = O.pruned_backward(p.counts, p.policy, p.alpha, p.g, p.phi, p.W, None, "bf16",
+                            glu=(gl.a, gl.b, gu.x, gu.W2))
+    assert U.check_keep(ref["scores"], p.counts, q, out["keep"].cpu().numpy().astype(bool),
+                        ref["keep"], ref["taus"]), "keep set inside the band: reseed"
+    assert np.array_equal(out["perm"].cpu().numpy(), ref["perm"])
+    assert np.array_equal(U.host_bits(out["x_c"]), gu.x[ref["perm"]])
+    dgu = U.host_bits(out["dgu_c"])
+    dgu = (dgu.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    r = ref["dgu_c"]
+    bound = 2.0 ** -8 * np.abs(r) + 2e-5 * np.abs(r).max()
+    assert np.all(np.abs(dgu - r) <= bound), float(np.max(np.abs(dgu - r) - bound))
+    errs = dict(dW=U.rel_err(out["dW"].cpu().numpy(), ref["dW"]),
+                dW2=U.rel_err(out["dW2"].cpu().numpy(), ref["dW2"]),
+                dx=U.rel_err(out["dx"].cpu().numpy(), ref["dx"]))
+    print(name, errs)
+    for k, v in errs.items():
+        assert v <= U.TOL, (k, v)
+    assert np.all(out["dx"].cpu().numpy()[~ref["keep"]] == 0)
+
+
 def test_empty_problem_pieces():
     """All experts empty but one; quotas zero everywhere (M = 0)."""
     p = W.make_problem(P=300, E=4, d_out=64, d_in=64, dtype="bf16", counts=[0, 300, 0, 0], seed=2)
