@@ -126,9 +126,10 @@ def stats_us(d: list):
             "launches": len(s)}
 
 
-def cpu_baseline(p, budget_s: float = 12.0):
+def cpu_baseline(p, budget_s: float = 12.0, chain: bool = False):
     """The oracle as it stands on the host cores: whole path on the same
-    workload, repeated while under the time budget."""
+    workload (with chain, the MLP chain through the gate/up projection),
+    repeated while under the time budget."""
     from oracle import lrmoe_oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -138,7 +139,9 @@ def cpu_baseline(p, budget_s: float = 12.0):
     runs, t0 = 0, time.perf_counter()
     M = 0
     while True:
-        out = O.pruned_backward(p.counts, p.policy, p.alpha, p.g, p.phi, p.W, p.row_index, p.dtype)
+        glu = (p.glu.a, p.glu.b, p.gate_up.x, p.gate_up.W2) if chain else None
+        out = O.pruned_backward(p.counts, p.policy, p.alpha, p.g, p.phi, p.W, p.row_index,
+                                p.dtype, glu=glu)
         M = int(out["seg"][-1])
         runs += 1
         el = time.perf_counter() - t0
@@ -158,9 +161,13 @@ def main():
     ap.add_argument("--dw-mode", choices=["exact", "bf16"], default="exact")
     ap.add_argument("--score-mode", choices=["lrm", "grad-sqnorm", "grad-l1", "random"],
                     default="lrm", help="scoring rule (the method, or an ablation baseline)")
-    ap.add_argument("--path", choices=["compacted", "masked-dense"], default="compacted",
+    ap.add_argument("--path", choices=["compacted", "masked-dense", "glu-chain"],
+                    default="compacted",
                     help="masked-dense: the zero-masked alternative (alpha := 0 on dropped "
-                         "pairs, GEMMs over every routed pair), for the A/B against compaction")
+                         "pairs, GEMMs over every routed pair), for the A/B against compaction; "
+                         "glu-chain (a config with a gate/up projection): the expert MLP "
+                         "chained on the compacted layout, down GEMM with the SiLU-GLU "
+                         "backward in its epilogue, then the gate/up GEMM")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
@@ -179,7 +186,12 @@ def main():
 
     from pruned_expert_backward_amd import lrmoe, workloads
 
-    p = workloads.config(args.config)
+    chain = args.path == "glu-chain"
+    if chain and "gate_up" not in workloads.CONFIGS[args.config]:
+        print("bench.py: the glu-chain path needs a config with a gate/up projection",
+              file=sys.stderr)
+        sys.exit(2)
+    p = workloads.config(args.config, glu=chain)
     q = lrmoe.plan_quota(p.counts, p.policy)
     M = sum(q)
     dev = torch.device("cuda:0")
@@ -197,7 +209,7 @@ def main():
         return (t.view(torch.bfloat16) if a.dtype == np.uint16 else t).to(dev)
 
     alpha, g, phi, W, row = d(p.alpha), d(p.g), d(p.phi), d(p.W), d(p.row_index)
-    out = lrmoe.alloc_select_outputs(plan, dev)
+    out = lrmoe.alloc_select_outputs(plan, dev, zero_target=not chain)
     dW = torch.empty((p.E, p.d_out, p.d_in), dtype=torch.float32, device=dev)
     ws = lrmoe.workspace(plan, dev)
     stream = torch.cuda.current_stream()
@@ -213,6 +225,10 @@ def main():
                     dphi=torch.empty((p.P, gu.d_in), dtype=torch.float32, device=dev))
         dW2 = torch.empty((p.E, gu.d_out, gu.d_in), dtype=torch.float32, device=dev)
         ws2 = lrmoe.workspace(plan2, dev)
+        if chain:   # gate/up output gradient comes from the down GEMM, already compacted
+            act_a, act_b = d(p.glu.a), d(p.glu.b)
+            out2["g_c"] = None
+            dgu = torch.empty((M, gu.d_out), dtype=torch.bfloat16, device=dev)
 
     given_scores = None
     if args.score_mode == "random":   # random dropping: seeded scores drawn once, as input
@@ -249,6 +265,18 @@ def main():
             return
         lrmoe.score_select_compact(plan, alpha, g, phi, g_row_index=row, out=out, ws=ws,
                                    scores=given_scores, timing=ssc_t)
+        if chain:
+            lrmoe.grouped_backward_glu(plan, out["perm"], out["alpha_c"], out["g_c"],
+                                       out["phi_c"], W, act_a, act_b, dW=dW, dgu_c=dgu, ws=ws,
+                                       timing=gb_t)
+            if gu_events is not None:
+                gu_events[0].record(stream)
+            lrmoe.gather_compact(plan2, out["perm"], out["keep"], alpha, None, x, out=out2)
+            if gu_events is not None:
+                gu_events[1].record(stream)
+            lrmoe.grouped_backward(plan2, out["perm"], out2["alpha_c"], dgu, out2["phi_c"], W2,
+                                   dW=dW2, dphi=out2["dphi"], ws=ws2, timing=gu_t)
+            return
         lrmoe.grouped_backward(plan, out["perm"], out["alpha_c"], out["g_c"], out["phi_c"], W,
                                dW=dW, dphi=out["dphi"], ws=ws, timing=gb_t)
         if gu is not None:
@@ -265,12 +293,16 @@ def main():
         step()
     torch.cuda.synchronize()
     # Timed region: whole steps.  The only events in it bracket the dominant
-    # kernel (the grouped GEMM launch), recorded by the library on the stream
-    # it launches on; events around every kernel would add gaps to the step.
+    # kernel (the grouped GEMM launch; in the MLP chain the larger gate/up
+    # one), recorded by the library on the stream it launches on; events
+    # around every kernel would add gaps to the step.
     gemm_timer = lrmoe.KernelTimer(args.steps, slots=(1,))
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(gb_t=gemm_timer)
+        if chain:
+            step(gu_t=gemm_timer)
+        else:
+            step(gb_t=gemm_timer)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     gemm_live = stats_us(gemm_timer.durations_us(1))
@@ -304,7 +336,7 @@ def main():
                    else P * (es * d_o + 4))   # gradient-only rules read no phi, no alpha
     work = {"lrm_score": score_bytes,
             "select_scan": P * 5,
-            "gather": M * (2 * es * (d_o + d_i) + 12) + (P - M) * 4 * d_i,
+            "gather": M * (2 * es * (d_o + d_i) + 12) + (0 if chain else (P - M) * 4 * d_i),
             "grouped_gemm": gemm_flops(p, p.P if dense_path else M)}
     kernels = {}
     for name, t in us.items():
@@ -321,13 +353,23 @@ def main():
         kernels[name] = k
     ssc_us = sum(us[n] for n in ("lrm_score", "select_scan", "gather") if us[n] is not None)
     nbytes = algorithmic_bytes(p, M, args.score_mode)
-    gemm_tf = work["grouped_gemm"] / gemm_live["mean"] / 1e6
+    if chain:   # no dphi rows to zero in the original layout
+        nbytes -= (P - M) * 4 * d_i
+    dominant_flops = 4.0 * M * gu.d_out * gu.d_in if chain else work["grouped_gemm"]
+    gemm_tf = dominant_flops / gemm_live["mean"] / 1e6
     roof = dict(kernel="grouped_backward_kernel", bound="mfma", achieved=gemm_tf,
                 peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s", frac=gemm_tf / MFMA_BF16_PEAK_TFLOPS,
                 launch_us_mean=gemm_live["mean"], launch_us_median=gemm_live["median"],
                 launches=gemm_live["launches"],
-                traffic=read_counters(p.name, args.dw_mode), traffic_unit="bytes per launch",
+                traffic=None if chain else read_counters(p.name, args.dw_mode),
+                traffic_unit="bytes per launch",
                 algorithmic_bytes_floor=gemm_floor_bytes(p, M))
+    if chain:
+        roof["note"] = "the gate/up projection's grouped GEMM (its flops 4 M d_out2 d_in2)"
+        es2 = 2
+        roof["algorithmic_bytes_floor"] = (M * es2 * (gu.d_out + gu.d_in)
+                                           + p.E * gu.d_out * gu.d_in * (es2 + 4)
+                                           + M * gu.d_in * 4)
     rec = {
         "metric": "kept pairs/s + grouped-GEMM TFLOP/s (% MFMA peak), score/compact % HBM BW",
         "value": M * args.steps / elapsed,
@@ -338,6 +380,8 @@ def main():
         "dtype": "bf16" if p.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": p.name + ("+masked-dense" if dense_path else ""),
+                   **({"chain": "down GEMM + SiLU-GLU epilogue -> gather x -> gate/up GEMM"}
+                      if chain else {}),
                    "P": p.P, "E": p.E, "d_out": p.d_out, "d_in": p.d_in,
                    "kept_pairs": M, "policy": list(p.policy), "dw_mode": args.dw_mode,
                    "score_mode": args.score_mode,
@@ -353,7 +397,10 @@ def main():
     if gu is not None:
         gd = stats_us([a.elapsed_time(b) * 1e3 for a, b in gu_ev])
         gg = stats_us(gu_timer.durations_us(1))
-        gbytes = M * (2 * es * (gu.d_out + gu.d_in) + 12) + (P - M) * 4 * gu.d_in
+        if chain:   # x rows and alpha only: the gate/up gradient is already compacted
+            gbytes = M * (2 * es * gu.d_in + 12) + (P - M) * 4 * gu.d_in
+        else:
+            gbytes = M * (2 * es * (gu.d_out + gu.d_in) + 12) + (P - M) * 4 * gu.d_in
         gfl = 4.0 * M * gu.d_out * gu.d_in
         rec["gate_up"] = {
             "d_out": gu.d_out, "d_in": gu.d_in,
@@ -377,7 +424,7 @@ def main():
     ssc_timer.close()
     gb_timer.close()
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(p)
+        rec["cpu_baseline"] = cpu_baseline(p, chain=chain)
     print(json.dumps(rec), flush=True)
 
 

@@ -528,44 +528,150 @@ struct Tile {
     }
   }
 
-  // ---- SiLU-GLU chain, one tile row: this lane holds dphi (before alpha)
-  // of compacted row j = pair u for 4 x 4 quads of columns.  With the saved
+  // ---- SiLU-GLU chain.  For tile row a this lane holds dphi (before alpha)
+  // of compacted row j = pair u in 4 x 4 quads of columns.  With the saved
   // pre-activations a, b of pair u: s = sigmoid(a), silu = a s,
   // silu' = s (1 + a (1 - s)); gate gradient dphi * b * silu', up gradient
   // dphi * silu, rounded to bf16 into glu_out[j] = [gate | up].
-  __device__ __forceinline__ void glu_row(const Args& args, int32_t u, int64_t j,
-                                          const f32x16 (&acc)[4][4], int a) const {
+  // Lanes l and l + 32 hold the two 4-column halves of each 8-column group
+  // of the same row.  Memory is accessed 16 bytes per lane: for the column
+  // groups g0 = 2h and g1 = 2h + 1 of block b, lane l moves group g0 and lane
+  // l + 32 group g1, and the two swap the halves that belong to the other
+  // (ds_bpermute) -- half as many load and store instructions, each touching
+  // the same 32 rows, as 8-byte accesses.  The a and b rows are gathered from
+  // the original pair layout; the next row's loads stay in flight while the
+  // current row is computed.  Nothing branches but the stores: lanes without
+  // a row (u < 0) or past the matrix edge (column counts are multiples of 8)
+  // load column 0 of row 0 instead.
+  struct GluRow {
+    u32x4 a[4][2], b[4][2];   // [block b][group pair h]
+  };
+
+  // First column of the 8-column group this lane moves for pair (b, h).
+  __device__ __forceinline__ int glu_col(int ln, int b, int h) const {
+    return wn * 128 + b * 32 + 16 * h + 8 * (ln >> 5);
+  }
+
+  __device__ __forceinline__ void glu_load(const Args& args, int32_t u, int ln, int ncols,
+                                           GluRow& r) const {
     const int d_in = args.d_in;
-    const uint16_t* arow = args.ops.glu_a + (int64_t)u * d_in + n0;
-    const uint16_t* brow = args.ops.glu_b + (int64_t)u * d_in + n0;
-    uint16_t* gate = args.ops.glu_out + j * (2 * (int64_t)d_in) + n0;
-    uint16_t* up = gate + d_in;
-    const int cq = 4 * (lane >> 5);
+    const bool row_ok = u >= 0;
+    const int64_t src = row_ok ? (int64_t)u * d_in + n0 : 0;
+    const uint16_t* arow = args.ops.glu_a + src;
+    const uint16_t* brow = args.ops.glu_b + src;
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = wn * 128 + b * 32 + 8 * g + cq;
-        if (col >= d_in - n0) continue;
-        const u32x2 av = *reinterpret_cast<const u32x2*>(arow + col);
-        const u32x2 bv = *reinterpret_cast<const u32x2*>(brow + col);
-        bf16x4 go, uo;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t aw = av[k >> 1], bw = bv[k >> 1];
-          const float x = __uint_as_float((k & 1) ? (aw & 0xFFFF0000u) : (aw << 16));
-          const float y = __uint_as_float((k & 1) ? (bw & 0xFFFF0000u) : (bw << 16));
-          const float sg = 1.f / (1.f + expf(-x));
-          const float d = acc[a][b][4 * g + k];
-          go[k] = (__bf16)(d * y * (sg * (1.f + x * (1.f - sg))));
-          uo[k] = (__bf16)(d * (x * sg));
-        }
-        *reinterpret_cast<u32x2*>(gate + col) = __builtin_bit_cast(u32x2, go);
-        *reinterpret_cast<u32x2*>(up + col) = __builtin_bit_cast(u32x2, uo);
-        // keep the scheduler from hoisting every row's loads at once: the
-        // accumulators already hold all AGPRs and half the VGPR file is free
-        if (g == 3) __builtin_amdgcn_sched_barrier(0);
+      for (int h = 0; h < 2; ++h) {
+        const int col = glu_col(ln, b, h);
+        const int c = row_ok && col < ncols ? col : 0;
+        r.a[b][h] = *reinterpret_cast<const u32x4*>(arow + c);
+        r.b[b][h] = *reinterpret_cast<const u32x4*>(brow + c);
       }
+  }
+
+  // Value of the partner lane (l ^ 32).
+  __device__ __forceinline__ static uint32_t swap32(uint32_t v, int ln) {
+    return (uint32_t)__builtin_amdgcn_ds_bpermute((ln ^ 32) << 2, (int)v);
+  }
+
+  // Gate and up gradients of one 4-column quad (bf16, packed in pairs).
+  __device__ __forceinline__ static void glu_quad(u32x2 av, u32x2 bv, const float (&d)[4],
+                                                  u32x2& gate, u32x2& up) {
+    bf16x4 go, uo;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t aw = av[k >> 1], bw = bv[k >> 1];
+      const float x = __uint_as_float((k & 1) ? (aw & 0xFFFF0000u) : (aw << 16));
+      const float y = __uint_as_float((k & 1) ? (bw & 0xFFFF0000u) : (bw << 16));
+      // Sigmoid from the hardware exp2 and reciprocal (about 1 ulp each, far
+      // below the bf16 rounding of the result); exp(-x) = 2^(-x log2(e)),
+      // whose overflow to +inf gives s = 0, as it should.
+      const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.44269504f * x));
+      go[k] = (__bf16)(d[k] * y * (sg * (1.f + x * (1.f - sg))));
+      uo[k] = (__bf16)(d[k] * (x * sg));
+    }
+    gate = __builtin_bit_cast(u32x2, go);
+    up = __builtin_bit_cast(u32x2, uo);
+  }
+
+  __device__ __forceinline__ void glu_store(const Args& args, int32_t u, int64_t j, int ln,
+                                            int ncols, const f32x16 (&acc)[4][4], int a,
+                                            const GluRow& r) const {
+    const int d_in = args.d_in;
+    uint16_t* gate = args.ops.glu_out + j * (2 * (int64_t)d_in) + n0;
+    uint16_t* up = gate + d_in;
+    const bool hi = ln >= 32;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        // this lane's quads of groups g0 and g1: its own half of the 16 bytes
+        // it loaded, and the partner's half of the partner's load
+        u32x2 qa[2], qb[2];
+        {
+          const u32x4 A = r.a[b][h], B = r.b[b][h];
+          const uint32_t ra0 = swap32(hi ? A[0] : A[2], ln), ra1 = swap32(hi ? A[1] : A[3], ln);
+          const uint32_t rb0 = swap32(hi ? B[0] : B[2], ln), rb1 = swap32(hi ? B[1] : B[3], ln);
+          qa[0] = hi ? u32x2{ra0, ra1} : u32x2{A[0], A[1]};
+          qa[1] = hi ? u32x2{A[2], A[3]} : u32x2{ra0, ra1};
+          qb[0] = hi ? u32x2{rb0, rb1} : u32x2{B[0], B[1]};
+          qb[1] = hi ? u32x2{B[2], B[3]} : u32x2{rb0, rb1};
+        }
+        u32x2 go[2], uo[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int g = 2 * h + t;
+          // read the accumulators straight from their AGPRs, here: a plain
+          // use makes the compiler copy all 256 accumulators to VGPRs at once
+          float d[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(d[k]) : "a"(acc[a][b][4 * g + k]));
+          glu_quad(qa[t], qb[t], d, go[t], uo[t]);
+        }
+        // lane l stores group g0 (its quad, then the partner's); lane l + 32
+        // group g1 (the partner's quad, then its own)
+        const u32x2 gs = hi ? go[0] : go[1], us = hi ? uo[0] : uo[1];
+        const u32x2 gr{swap32(gs[0], ln), swap32(gs[1], ln)};
+        const u32x2 ur{swap32(us[0], ln), swap32(us[1], ln)};
+        const u32x4 gv = hi ? u32x4{gr[0], gr[1], go[1][0], go[1][1]}
+                            : u32x4{go[0][0], go[0][1], gr[0], gr[1]};
+        const u32x4 uv = hi ? u32x4{ur[0], ur[1], uo[1][0], uo[1][1]}
+                            : u32x4{uo[0][0], uo[0][1], ur[0], ur[1]};
+        const int col = glu_col(ln, b, h);
+        if (u >= 0 && col < ncols) {
+          *reinterpret_cast<u32x4*>(gate + col) = gv;
+          *reinterpret_cast<u32x4*>(up + col) = uv;
+        }
+      }
+  }
+
+  __device__ __forceinline__ void glu_epilogue(const Args& args, LDS_AS const char* prm,
+                                               const f32x16 (&acc)[4][4]) const {
+    LDS_AS const int32_t* s_perm = reinterpret_cast<LDS_AS const int32_t*>(prm);
+    // Opaque copies: keep the compiler from computing the column offsets and
+    // edge predicates of every quad ahead of the main loop, where they would
+    // stay live across it.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    int ncols = args.d_in - n0;
+    asm volatile("" : "+s"(ncols));
+    int32_t u[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) u[a] = s_perm[wm * 128 + a * 32 + (ln & 31)];
+    GluRow r[2];
+    glu_load(args, u[0], ln, ncols, r[0]);
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      if (a < 3) glu_load(args, u[a + 1], ln, ncols, r[(a + 1) & 1]);
+      // at most two rows of loads live (128 VGPRs): the accumulators hold
+      // every AGPR, so nothing more may be hoisted
+      __builtin_amdgcn_sched_barrier(0);
+      glu_store(args, u[a], seg + m0 + wm * 128 + a * 32 + (ln & 31), ln, ncols, acc, a,
+                r[a & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   // ---- epilogue.  Accumulator block (a, b) holds D[m][n] for tile row
@@ -585,6 +691,10 @@ struct Tile {
       const int tile = (m0 / BM) * tab.tiles_n + n0 / BN;
       part = args.ops.partials + ((partial_base(tab, e) + (int64_t)tile * chunks + chunk) << 16);
     }
+    if constexpr (GLU) {   // SiLU-GLU chain: no dphi, no alpha
+      glu_epilogue(args, prm, acc);
+      return;
+    }
     const int cq = 4 * (lane >> 5);   // this lane's column offset inside each group of 8
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
@@ -603,10 +713,6 @@ struct Tile {
         }
       } else {
         const int32_t u = s_perm[lrow];
-        if constexpr (GLU) {   // SiLU-GLU chain: no dphi, no alpha
-          if (u >= 0) glu_row(args, u, seg + m0 + lrow, acc, a);
-          continue;
-        }
         scale = s_alpha[lrow];
         if (u >= 0) orow = args.dphi + (int64_t)u * d_in + n0;
       }

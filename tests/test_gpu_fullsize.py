@@ -127,3 +127,63 @@ def test_fullsize_qwen3_c30_with_gate_up():
 @pytest.mark.timeout(600)
 def test_fullsize_glm45_20x_budget():
     check_fullsize(W.config(4), seed=4)
+
+
+def test_fullsize_qwen3_c30_glu_chain():
+    """The expert MLP chained on the compacted layout at the Qwen3 C30 share
+    (MLP-chain variant of the workload, as the benchmark's glu-chain path):
+    keep set, perm and the gathered x rows in full; sampled rows of the
+    compacted gate/up gradient, blocks of dW and dW2, kept and dropped rows
+    of dx."""
+    p = W.config(2, glu=True)
+    gu, gl = p.gate_up, p.glu
+    q = lrmoe.plan_quota(p.counts, p.policy)
+    plan = lrmoe.Plan(p.counts, q, p.d_out, p.d_in, lrmoe.BF16)
+    plan2 = lrmoe.Plan(p.counts, q, gu.d_out, gu.d_in, lrmoe.BF16)
+    d = U.dev
+    out = lrmoe.glu_chain_backward(plan, plan2, d(p.alpha), d(p.g), d(p.phi), d(p.W), d(gl.a),
+                                   d(gl.b), d(gu.x), d(gu.W2))
+    torch.cuda.synchronize()
+    R = oracle_scores(p)
+    keep_ref, taus = O.select_top_quota(R, p.counts, q)
+    keep_gpu = out["keep"].cpu().numpy().astype(bool)
+    same = U.check_keep(R, p.counts, q, keep_gpu, keep_ref, taus)
+    keep = keep_ref if same else keep_gpu
+    perm, seg = O.compact(keep, p.counts, q)
+    assert np.array_equal(out["perm"].cpu().numpy(), perm)
+    assert np.array_equal(U.host_bits(out["x_c"]), gu.x[perm])
+    rng = np.random.default_rng(23)
+    M = len(perm)
+    js = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 254)]))
+    ref = O.glu_chain_rows(seg, perm, None, p.g, p.W, gl.a, gl.b, "bf16", js)
+    got = U.host_bits(out["dgu_c"][torch.as_tensor(js, device=out["dgu_c"].device)])
+    got = (got.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    bound = 2.0 ** -8 * np.abs(ref) + 2e-5 * np.abs(ref).max()
+    assert np.all(np.abs(got - ref) <= bound)
+
+    def block(t, o_idx, i_idx, e):
+        return t[e][torch.as_tensor(o_idx, device=t.device)][
+            :, torch.as_tensor(i_idx, device=t.device)].cpu().numpy()
+
+    o1 = np.unique(np.concatenate([[0, p.d_out - 1], rng.integers(0, p.d_out, 40)]))
+    i1 = np.unique(np.concatenate([[0, p.d_in - 1], rng.integers(0, p.d_in, 40)]))
+    e_dw = U.rel_err(np.stack([block(out["dW"], o1, i1, e) for e in range(p.E)]),
+                     np.stack([O.weight_grad_block(seg, perm, None, p.alpha, p.g, p.phi, "bf16",
+                                                   e, o1, i1) for e in range(p.E)]))
+    o2 = np.unique(np.concatenate([[0, p.d_in - 1, p.d_in, gu.d_out - 1],
+                                   rng.integers(0, gu.d_out, 40)]))
+    i2 = np.unique(np.concatenate([[0, gu.d_in - 1], rng.integers(0, gu.d_in, 40)]))
+    e_dw2 = U.rel_err(np.stack([block(out["dW2"], o2, i2, e) for e in range(p.E)]),
+                      np.stack([O.glu_weight_grad_block(seg, perm, None, p.alpha, p.g, p.W,
+                                                        gl.a, gl.b, gu.x, "bf16", e, o2, i2)
+                                for e in range(p.E)]))
+    pairs = np.unique(np.concatenate([[0, p.P - 1], rng.choice(perm, 256, replace=False),
+                                      rng.choice(np.nonzero(~keep)[0], 64, replace=False)]))
+    ref_dx = O.glu_input_grad_rows(p.counts, keep, None, p.alpha, p.g, p.W, gl.a, gl.b, gu.W2,
+                                   "bf16", pairs)
+    got_dx = out["dx"][torch.as_tensor(pairs, device=out["dx"].device)].cpu().numpy()
+    e_dx = U.rel_err(got_dx, ref_dx)
+    assert np.all(got_dx[~keep[pairs]] == 0)
+    print(f"glu chain: M={M} keep identical={same} dW err={e_dw:.3e} dW2 err={e_dw2:.3e} "
+          f"dx err={e_dx:.3e}")
+    assert e_dw <= U.TOL and e_dw2 <= U.TOL and e_dx <= U.TOL
