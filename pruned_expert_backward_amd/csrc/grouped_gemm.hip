@@ -48,14 +48,19 @@
 //     in single-rounding mode) -> 4 stages; three planes (dW with a hi + lo
 //     operand) -> 3; four (float32 storage) -> 2.  Each K step crosses one
 //     barrier, between its two halves.
-//   * Scheduling: dW and dphi tiles share one launch.  Tiles are grouped in
-//     blocks of an expert's tile grid that share operand panels; group g runs
-//     on XCD g % 8 (workgroups are dispatched round-robin over the 8 XCDs), so
-//     a group's panels are fetched into one L2.  dW groups come first, heaviest
-//     experts first; the uniform dphi groups fill the tail.  An expert whose
-//     kept rows exceed one K chunk has its dW split along K: each chunk writes
-//     an fp32 partial tile and a second kernel sums them in chunk order, so
-//     the result does not depend on timing.
+//   * Scheduling: dW and dphi tiles share one persistent launch, one
+//     workgroup per CU.  Tiles are grouped in blocks of an expert's tile grid
+//     that share operand panels.  The host deals the groups, longest first,
+//     to the XCD with the least work so far; workgroup b runs on XCD b % 8
+//     (dispatch is round-robin over the 8 XCDs) and drains that XCD's queue
+//     through an atomic counter, so a group's panels are fetched into one L2.
+//     A workgroup whose queue is empty takes tiles from the other XCDs'
+//     queues.  An expert whose kept rows exceed one K chunk has its dW split
+//     along K: each chunk writes an fp32 partial tile and a second kernel
+//     sums them in chunk order, so the result does not depend on timing.
+//   * SiLU-GLU variant (GLU = true): the input-gradient tiles write the
+//     gate/up output gradient of the expert MLP, compacted, instead of dphi
+//     (see Tile::glu_epilogue).
 #include "lrmoe_internal.h"
 
 namespace lrmoe {
