@@ -269,7 +269,8 @@ lrmoe_status lrmoe_grouped_backward(
  * (alpha applied once, there) finish the chain.  No original-layout dphi is
  * written and none needs zeroing.
  *   act_a, act_b  bf16 [P, d_in], pair-indexed like phi.
- * bf16 storage only (LRMOE_ERR_DTYPE otherwise); other errors as for
+ * act_a, act_b and dgu_c may be NULL when no pair is kept (M = 0).  bf16
+ * storage only (LRMOE_ERR_DTYPE otherwise); other errors as for
  * lrmoe_grouped_backward. */
 lrmoe_status lrmoe_grouped_backward_glu(
     const lrmoe_problem* pb, const int32_t* perm, const float* alpha_c,

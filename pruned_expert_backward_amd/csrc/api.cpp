@@ -250,14 +250,15 @@ lrmoe_status select_compact(const lrmoe_problem* pb, bool compute_scores, const 
   return LRMOE_OK;
 }
 
-// Shared body of the grouped-backward entry points.  glu_out != nullptr: the
-// SiLU-GLU chain (dphi is then nullptr and the input-gradient tiles write the
-// compacted gate/up output gradient instead).
+// Shared body of the grouped-backward entry points.  glu: the SiLU-GLU chain
+// (dphi is then nullptr and the input-gradient tiles write the compacted
+// gate/up output gradient glu_out instead; with no kept pair at all there is
+// nothing to write and the pointers may be NULL).
 lrmoe_status grouped_backward(const lrmoe_problem* pb, const int32_t* perm, const float* alpha_c,
                               const void* g_c, const void* phi_c, const void* W, float* dW,
-                              float* dphi, const uint16_t* glu_a, const uint16_t* glu_b,
-                              uint16_t* glu_out, void* workspace, size_t ws_bytes, void* stream,
-                              const lrmoe_timing* timing) {
+                              float* dphi, bool glu, const uint16_t* glu_a,
+                              const uint16_t* glu_b, uint16_t* glu_out, void* workspace,
+                              size_t ws_bytes, void* stream, const lrmoe_timing* timing) {
   Checked c;
   LRMOE_TRY(check_problem(pb, c));
   const int64_t M = c.M;
@@ -267,11 +268,11 @@ lrmoe_status grouped_backward(const lrmoe_problem* pb, const int32_t* perm, cons
   LRMOE_TRY(need(W, 1));
   LRMOE_TRY(need(dW, 1));
   LRMOE_TRY(optional(dphi));
-  const bool glu = glu_out != nullptr;
   if (glu) {
-    LRMOE_TRY(need(glu_a, pb->P));
-    LRMOE_TRY(need(glu_b, pb->P));
+    LRMOE_TRY(need(glu_a, M > 0 ? pb->P : 0));
+    LRMOE_TRY(need(glu_b, M > 0 ? pb->P : 0));
     LRMOE_TRY(need(glu_out, M));
+    if (M == 0) glu_out = nullptr;   // no input-gradient tile: the plain kernel runs
   }
   if (dphi != nullptr || glu) LRMOE_TRY(need(perm, M));
   const GemmWorkspace wl = gemm_workspace(pb, M);
@@ -618,8 +619,8 @@ lrmoe_status lrmoe_grouped_backward_timed(const lrmoe_problem* pb, const int32_t
                                           const void* phi_c, const void* W, float* dW,
                                           float* dphi, void* workspace, size_t ws_bytes,
                                           void* stream, const lrmoe_timing* timing) {
-  return grouped_backward(pb, perm, alpha_c, g_c, phi_c, W, dW, dphi, nullptr, nullptr, nullptr,
-                          workspace, ws_bytes, stream, timing);
+  return grouped_backward(pb, perm, alpha_c, g_c, phi_c, W, dW, dphi, false, nullptr, nullptr,
+                          nullptr, workspace, ws_bytes, stream, timing);
 }
 
 lrmoe_status lrmoe_grouped_backward_glu(const lrmoe_problem* pb, const int32_t* perm,
@@ -639,8 +640,7 @@ lrmoe_status lrmoe_grouped_backward_glu_timed(const lrmoe_problem* pb, const int
                                               const lrmoe_timing* timing) {
   if (pb == nullptr) return LRMOE_ERR_NULL;
   if (pb->dtype != LRMOE_BF16) return LRMOE_ERR_DTYPE;
-  if (act_a == nullptr || act_b == nullptr || dgu_c == nullptr) return LRMOE_ERR_NULL;
-  return grouped_backward(pb, perm, alpha_c, g_c, phi_c, W, dW, nullptr,
+  return grouped_backward(pb, perm, alpha_c, g_c, phi_c, W, dW, nullptr, true,
                           reinterpret_cast<const uint16_t*>(act_a),
                           reinterpret_cast<const uint16_t*>(act_b),
                           reinterpret_cast<uint16_t*>(dgu_c), workspace, ws_bytes, stream,

@@ -247,6 +247,43 @@ def test_glu_chain(idx):
     assert np.all(out["dx"].cpu().numpy()[~ref["keep"]] == 0)
 
 
+def test_glu_chain_edges():
+    """The MLP chain at its edges: no kept pair at all (M = 0: dW, dW2 and dx
+    all zero, nothing else written); tiny ragged shapes (d_in = 8, two
+    experts, one of them empty); one expert whose kept rows and columns
+    straddle tile edges (q = 301, d_in = 264)."""
+    cases = [
+        (dict(P=120, E=3, d_out=64, d_in=32, counts=[50, 40, 30], gate_up=(64, 48)), ("ratio", 0, 1)),
+        (dict(P=40, E=2, d_out=8, d_in=8, counts=[40, 0], gate_up=(16, 8)), ("ratio", 3, 4)),
+        (dict(P=430, E=1, d_out=136, d_in=264, counts=[430], gate_up=(528, 40)), ("ratio", 7, 10)),
+    ]
+    for i, (kw, policy) in enumerate(cases):
+        p = W.make_problem(seed=320 + i, dtype="bf16", glu=True, policy=policy, **kw)
+        gu, gl = p.gate_up, p.glu
+        q = lrmoe.plan_quota(p.counts, policy)
+        plan = lrmoe.Plan(p.counts, q, p.d_out, p.d_in, lrmoe.BF16)
+        plan2 = lrmoe.Plan(p.counts, q, gu.d_out, gu.d_in, lrmoe.BF16)
+        d = U.dev
+        out = lrmoe.glu_chain_backward(plan, plan2, d(p.alpha), d(p.g), d(p.phi), d(p.W),
+                                       d(gl.a), d(gl.b), d(gu.x), d(gu.W2))
+        torch.cuda.synchronize()
+        ref = O.pruned_backward(p.counts, policy, p.alpha, p.g, p.phi, p.W, None, "bf16",
+                                glu=(gl.a, gl.b, gu.x, gu.W2))
+        assert np.array_equal(out["keep"].cpu().numpy().astype(bool), ref["keep"]), i
+        assert np.array_equal(out["perm"].cpu().numpy(), ref["perm"]), i
+        assert tuple(out["dgu_c"].shape) == (sum(q), 2 * p.d_in)
+        if sum(q) == 0:
+            for k in ("dW", "dW2", "dx"):
+                assert float(out[k].abs().max()) == 0.0, (i, k)
+            continue
+        dgu = (U.host_bits(out["dgu_c"]).astype(np.uint32) << 16).view(np.float32)
+        r = ref["dgu_c"]
+        assert np.all(np.abs(dgu - r) <= 2.0 ** -8 * np.abs(r) + 2e-5 * np.abs(r).max()), i
+        for k in ("dW", "dW2", "dx"):
+            e = U.rel_err(out[k].cpu().numpy(), ref[k])
+            assert e <= U.TOL, (i, k, e)
+
+
 def test_empty_problem_pieces():
     """All experts empty but one; quotas zero everywhere (M = 0)."""
     p = W.make_problem(P=300, E=4, d_out=64, d_in=64, dtype="bf16", counts=[0, 300, 0, 0], seed=2)
