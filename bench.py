@@ -357,8 +357,18 @@ def main():
         nbytes -= (P - M) * 4 * d_i
     dominant_flops = 4.0 * M * gu.d_out * gu.d_in if chain else work["grouped_gemm"]
     gemm_tf = dominant_flops / gemm_live["mean"] / 1e6
+    # MFMA work the kernel executes: products of split operands cost one MFMA
+    # pass per term (exact mode: alpha * (narrower operand) as hi + lo).
+    terms_dw = 1 + (args.dw_mode == "exact" or p.dtype != "bf16") + (p.dtype != "bf16")
+    terms_dp = 1 if p.dtype == "bf16" else 3
+    if chain:
+        exec_flops = 2.0 * M * gu.d_out * gu.d_in * (terms_dw + terms_dp)
+    else:
+        Mx = p.P if dense_path else M
+        exec_flops = 2.0 * Mx * p.d_out * p.d_in * (terms_dw + terms_dp)
     roof = dict(kernel="grouped_backward_kernel", bound="mfma", achieved=gemm_tf,
                 peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s", frac=gemm_tf / MFMA_BF16_PEAK_TFLOPS,
+                mfma_executed_TFLOPs=exec_flops / gemm_live["mean"] / 1e6,
                 launch_us_mean=gemm_live["mean"], launch_us_median=gemm_live["median"],
                 launches=gemm_live["launches"],
                 traffic=None if chain else read_counters(p.name, args.dw_mode),
