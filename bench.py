@@ -1,8 +1,9 @@
 """Benchmark of the pruned MoE expert backward on one MI355X.
 
 One step = one pass of the whole hot path over one batch: LRM score ->
-per-expert top-quota select -> compaction (lrmoe_score_select_compact), then
-the fused varlen grouped GEMM for dW and dphi (lrmoe_grouped_backward).
+per-expert top-quota select -> compaction -> the fused varlen grouped GEMM for
+dW and dphi, in one library call (lrmoe_pruned_backward; the gather also
+writes the GEMM's operand planes).
 Inputs are resident in HBM before timing starts; outputs are preallocated.
 
 Prints ONE JSON line.  value = kept pairs per second of the whole path over
@@ -237,6 +238,10 @@ def main():
         given_scores = torch.rand(p.P, generator=gen, device=dev, dtype=torch.float32)
 
     dense_path = args.path == "masked-dense"
+    # the whole path in one call, except where the step needs the separate
+    # calls: given scores (random rule), the MLP chain
+    whole = not dense_path and not chain and given_scores is None
+    out["dW"] = dW
     if dense_path:
         if gu is not None or p.T != p.P or given_scores is not None:
             print("bench.py: the masked-dense path runs one projection with one g row per "
@@ -263,8 +268,12 @@ def main():
             lrmoe.grouped_backward(dense, pid, am, g, phi, W, dW=dW, dphi=dphi_full, ws=dws,
                                    timing=gb_t)
             return
-        lrmoe.score_select_compact(plan, alpha, g, phi, g_row_index=row, out=out, ws=ws,
-                                   scores=given_scores, timing=ssc_t)
+        if whole:
+            lrmoe.pruned_backward(plan, alpha, g, phi, W, g_row_index=row, out=out, ws=ws,
+                                  timing=ssc_t)
+        else:
+            lrmoe.score_select_compact(plan, alpha, g, phi, g_row_index=row, out=out, ws=ws,
+                                       scores=given_scores, timing=ssc_t)
         if chain:
             lrmoe.grouped_backward_glu(plan, out["perm"], out["alpha_c"], out["g_c"],
                                        out["phi_c"], W, act_a, act_b, dW=dW, dgu_c=dgu, ws=ws,
@@ -277,8 +286,9 @@ def main():
             lrmoe.grouped_backward(plan2, out["perm"], out2["alpha_c"], dgu, out2["phi_c"], W2,
                                    dW=dW2, dphi=out2["dphi"], ws=ws2, timing=gu_t)
             return
-        lrmoe.grouped_backward(plan, out["perm"], out["alpha_c"], out["g_c"], out["phi_c"], W,
-                               dW=dW, dphi=out["dphi"], ws=ws, timing=gb_t)
+        if not whole:
+            lrmoe.grouped_backward(plan, out["perm"], out["alpha_c"], out["g_c"], out["phi_c"],
+                                   W, dW=dW, dphi=out["dphi"], ws=ws, timing=gb_t)
         if gu is not None:
             if gu_events is not None:
                 gu_events[0].record(stream)
@@ -296,16 +306,19 @@ def main():
     # kernel (the grouped GEMM launch; in the MLP chain the larger gate/up
     # one), recorded by the library on the stream it launches on; events
     # around every kernel would add gaps to the step.
-    gemm_timer = lrmoe.KernelTimer(args.steps, slots=(1,))
+    gemm_slot = 3 if whole else 1
+    gemm_timer = lrmoe.KernelTimer(args.steps, slots=(gemm_slot,))
     t0 = time.perf_counter()
     for _ in range(args.steps):
         if chain:
             step(gu_t=gemm_timer)
+        elif whole:
+            step(ssc_t=gemm_timer)
         else:
             step(gb_t=gemm_timer)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    gemm_live = stats_us(gemm_timer.durations_us(1))
+    gemm_live = stats_us(gemm_timer.durations_us(gemm_slot))
     gemm_timer.close()
 
     # Per-kernel breakdown: a separate pass after the timed region, with HIP
@@ -324,12 +337,20 @@ def main():
 
     es = 2 if p.dtype == "bf16" else 4
     P, d_o, d_i = p.P, p.d_out, p.d_in
-    dist = {"lrm_score": stats_us(ssc_timer.durations_us(0)),
-            "select_scan": stats_us(ssc_timer.durations_us(1)),
-            "gather": stats_us(ssc_timer.durations_us(2)),
-            "operand_prologue": stats_us(gb_timer.durations_us(0)),
-            "grouped_gemm": stats_us(gb_timer.durations_us(1)),
-            "splitk_reduce": stats_us(gb_timer.durations_us(2))}
+    if whole:   # one call, its slots: score, select, gather (+ planes), GEMM, reduction
+        dist = {"lrm_score": stats_us(ssc_timer.durations_us(0)),
+                "select_scan": stats_us(ssc_timer.durations_us(1)),
+                "gather": stats_us(ssc_timer.durations_us(2)),
+                "operand_prologue": stats_us(ssc_timer.durations_us(5)),
+                "grouped_gemm": stats_us(ssc_timer.durations_us(3)),
+                "splitk_reduce": stats_us(ssc_timer.durations_us(4))}
+    else:
+        dist = {"lrm_score": stats_us(ssc_timer.durations_us(0)),
+                "select_scan": stats_us(ssc_timer.durations_us(1)),
+                "gather": stats_us(ssc_timer.durations_us(2)),
+                "operand_prologue": stats_us(gb_timer.durations_us(0)),
+                "grouped_gemm": stats_us(gb_timer.durations_us(1)),
+                "splitk_reduce": stats_us(gb_timer.durations_us(2))}
     us = {k: (v["mean"] if v else None) for k, v in dist.items()}
     # algorithmic bytes (HBM-bound kernels) and FLOP (the GEMM) per launch
     score_bytes = (P * (es * (d_o + d_i) + 8) if args.score_mode == "lrm"
@@ -351,6 +372,11 @@ def main():
             k.update(algorithmic_bytes=work[name], GBps=work[name] / t / 1e3,
                      hbm_frac=work[name] / t / 1e3 / HBM_PEAK_GBS)
         kernels[name] = k
+    if whole and p.dtype == "bf16" and "gather" in kernels:
+        # what the gather writes beyond the method's bytes: the GEMM's operand
+        # planes (alpha times the narrower operand, hi + lo in exact mode)
+        kernels["gather"]["gemm_plane_bytes"] = (M * min(d_o, d_i) * 2 *
+                                                 (2 if args.dw_mode == "exact" else 1))
     ssc_us = sum(us[n] for n in ("lrm_score", "select_scan", "gather") if us[n] is not None)
     nbytes = algorithmic_bytes(p, M, args.score_mode)
     if chain:   # no dphi rows to zero in the original layout
@@ -400,6 +426,11 @@ def main():
         "score_select_compact": {"us": ssc_us, "algorithmic_bytes": nbytes,
                                  "GBps": nbytes / ssc_us / 1e3 if ssc_us else None,
                                  "hbm_frac": nbytes / ssc_us / 1e3 / HBM_PEAK_GBS if ssc_us else None},
+        "score_select_compact_note": ("the gather also writes the GEMM's operand planes "
+                                      "(kernels.gather.gemm_plane_bytes), which the operand "
+                                      "prologue would otherwise write; they are not counted "
+                                      "in algorithmic_bytes") if whole and p.dtype == "bf16"
+                                     else None,
         "kernels": kernels,
         "kernels_note": f"separate pass of {nb} steps after the timed region, HIP events "
                         "around every kernel",

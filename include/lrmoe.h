@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define LRMOE_ABI_VERSION 2
+#define LRMOE_ABI_VERSION 3
 #define LRMOE_MAX_EXPERTS 256
 
 typedef enum {
@@ -278,6 +278,21 @@ lrmoe_status lrmoe_grouped_backward_glu(
     const void* act_a, const void* act_b, void* dgu_c, void* workspace,
     size_t ws_bytes, void* stream);
 
+/* Steps 2-5 in one call: lrmoe_score_select_compact followed by
+ * lrmoe_grouped_backward on the same buffers, with the same arguments and
+ * results (dphi is both the zero target of dropped rows and the output of
+ * kept rows; NULL for dW only).  With bf16 storage the gather also writes the
+ * GEMM's operand planes (alpha times the narrower compacted operand, as bf16
+ * hi and, in exact mode, lo) from the rows it moves, so no separate pass
+ * reads the compacted operand again; the planes and every result are bit for
+ * bit those of the two separate calls.  workspace: lrmoe_workspace_size
+ * bytes.  Errors as for the two calls. */
+lrmoe_status lrmoe_pruned_backward(
+    const lrmoe_problem* pb, const int32_t* g_row_index, const float* alpha,
+    const void* g, const void* phi, const void* W, float* scores, uint8_t* keep,
+    int32_t* seg_offsets, int32_t* perm, void* g_c, void* phi_c, float* alpha_c,
+    float* dW, float* dphi, void* workspace, size_t ws_bytes, void* stream);
+
 /* Per-kernel timing.  Each entry point below launches a fixed sequence of
  * kernels; for every non-NULL pair, `before` and `after` (hipEvent_t created
  * by the caller with timing enabled) are recorded on `stream` right before
@@ -287,8 +302,11 @@ lrmoe_status lrmoe_grouped_backward_glu(
  *   lrmoe_select_compact_timed:       [1] select+scan  [2] gather
  *   lrmoe_grouped_backward_timed,
  *   lrmoe_grouped_backward_glu_timed: [0] operand prologue  [1] grouped GEMM
- *                                     [2] split-K reduction */
-#define LRMOE_TIMING_SLOTS 4
+ *                                     [2] split-K reduction
+ *   lrmoe_pruned_backward_timed:      [0] score  [1] select+scan  [2] gather
+ *                                     [3] grouped GEMM  [4] split-K reduction
+ *                                     [5] operand prologue (float32 storage) */
+#define LRMOE_TIMING_SLOTS 8
 typedef struct {
   void* before[LRMOE_TIMING_SLOTS];
   void* after[LRMOE_TIMING_SLOTS];
@@ -315,6 +333,14 @@ lrmoe_status lrmoe_grouped_backward_timed(
     const lrmoe_problem* pb, const int32_t* perm, const float* alpha_c,
     const void* g_c, const void* phi_c, const void* W, float* dW, float* dphi,
     void* workspace, size_t ws_bytes, void* stream, const lrmoe_timing* timing);
+
+/* lrmoe_pruned_backward with per-kernel events (timing may be NULL). */
+lrmoe_status lrmoe_pruned_backward_timed(
+    const lrmoe_problem* pb, const int32_t* g_row_index, const float* alpha,
+    const void* g, const void* phi, const void* W, float* scores, uint8_t* keep,
+    int32_t* seg_offsets, int32_t* perm, void* g_c, void* phi_c, float* alpha_c,
+    float* dW, float* dphi, void* workspace, size_t ws_bytes, void* stream,
+    const lrmoe_timing* timing);
 
 /* lrmoe_grouped_backward_glu with per-kernel events (timing may be NULL). */
 lrmoe_status lrmoe_grouped_backward_glu_timed(

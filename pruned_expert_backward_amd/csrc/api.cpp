@@ -200,7 +200,8 @@ lrmoe_status select_compact(const lrmoe_problem* pb, bool compute_scores, const 
                             const void* phi, float* scores_out, uint8_t* keep,
                             int32_t* seg_offsets, int32_t* perm, void* g_c, void* phi_c,
                             float* alpha_c, float* dphi_zero, void* workspace, size_t ws_bytes,
-                            void* stream, const lrmoe_timing* timing, bool gather = true) {
+                            void* stream, const lrmoe_timing* timing, bool gather = true,
+                            const GatherPlanes& planes = GatherPlanes()) {
   Checked c;
   LRMOE_TRY(check_problem(pb, c));
   const int64_t P = pb->P, M = c.M;
@@ -245,7 +246,7 @@ lrmoe_status select_compact(const lrmoe_problem* pb, bool compute_scores, const 
   LRMOE_TRY(mark(timing, false, 2, s));
   LRMOE_TRY(hip_status(launch_gather(pb->dtype, perm, keep, g_row_index, nullptr, alpha, g, phi,
                                      g_c, phi_c, alpha_c, dphi_zero, (int32_t)M, (int32_t)P,
-                                     pb->d_out, pb->d_in, s)));
+                                     pb->d_out, pb->d_in, s, planes)));
   LRMOE_TRY(mark(timing, true, 2, s));
   return LRMOE_OK;
 }
@@ -254,11 +255,20 @@ lrmoe_status select_compact(const lrmoe_problem* pb, bool compute_scores, const 
 // (dphi is then nullptr and the input-gradient tiles write the compacted
 // gate/up output gradient glu_out instead; with no kept pair at all there is
 // nothing to write and the pointers may be NULL).
+// planes_ready: the gather already wrote the bf16 operand planes (and
+// cleared the queue counters), so no prologue runs.  Timing slots: sp
+// (prologue), sp + 1 (GEMM), sp + 2 (reduction), or for the whole-path call
+// the slots of TimingSlots.
+struct TimingSlots {
+  int prologue = 0, gemm = 1, reduce = 2;
+};
+
 lrmoe_status grouped_backward(const lrmoe_problem* pb, const int32_t* perm, const float* alpha_c,
                               const void* g_c, const void* phi_c, const void* W, float* dW,
                               float* dphi, bool glu, const uint16_t* glu_a,
                               const uint16_t* glu_b, uint16_t* glu_out, void* workspace,
-                              size_t ws_bytes, void* stream, const lrmoe_timing* timing) {
+                              size_t ws_bytes, void* stream, const lrmoe_timing* timing,
+                              bool planes_ready = false, TimingSlots ts = TimingSlots()) {
   Checked c;
   LRMOE_TRY(check_problem(pb, c));
   const int64_t M = c.M;
@@ -362,8 +372,8 @@ lrmoe_status grouped_backward(const lrmoe_problem* pb, const int32_t* perm, cons
     t.qoff[kXcds] = o;
   }
 
-  // Prologue: bf16 operand planes.
-  LRMOE_TRY(mark(timing, false, 0, s));
+  // Prologue: bf16 operand planes (unless the gather wrote them).
+  if (!planes_ready) LRMOE_TRY(mark(timing, false, ts.prologue, s));
   char* ws = reinterpret_cast<char*>(workspace);
   auto plane = [&](size_t off) { return reinterpret_cast<uint16_t*>(ws + off); };
   int32_t* heads = reinterpret_cast<int32_t*>(ws + wl.heads);
@@ -378,7 +388,8 @@ lrmoe_status grouped_backward(const lrmoe_problem* pb, const int32_t* perm, cons
     uint16_t* lo = exact ? plane(wl.b_lo) : nullptr;
     const void* src = wl.alpha_on_phi ? phi_c : g_c;
     const int cols = wl.alpha_on_phi ? d_in : d_out;
-    LRMOE_TRY(hip_status(launch_split(LRMOE_BF16, src, M, cols, alpha_c, hi, lo, s, heads, kXcds)));
+    if (!planes_ready)
+      LRMOE_TRY(hip_status(launch_split(LRMOE_BF16, src, M, cols, alpha_c, hi, lo, s, heads, kXcds)));
     if (wl.alpha_on_phi) {
       ops.dw_a[0] = g16;
       ops.dw_b[0] = hi;
@@ -410,20 +421,59 @@ lrmoe_status grouped_backward(const lrmoe_problem* pb, const int32_t* perm, cons
     ops.dw_pa = ops.dw_pb = ops.dp_pa = ops.dp_pb = 2;
   }
   (void)w16;
-  LRMOE_TRY(mark(timing, true, 0, s));
+  if (!planes_ready) LRMOE_TRY(mark(timing, true, ts.prologue, s));
   ops.partials = reinterpret_cast<float*>(ws + wl.partials);
   ops.queue_heads = heads;   // cleared by the first prologue launch
   ops.glu_a = glu_a;
   ops.glu_b = glu_b;
   ops.glu_out = glu_out;
-  LRMOE_TRY(mark(timing, false, 1, s));
+  LRMOE_TRY(mark(timing, false, ts.gemm, s));
   LRMOE_TRY(hip_status(launch_grouped_backward(t, ops, perm, alpha_c, dW, dphi, d_out, d_in,
                                                (int32_t)pb->P, s)));
-  LRMOE_TRY(mark(timing, true, 1, s));
-  LRMOE_TRY(mark(timing, false, 2, s));
+  LRMOE_TRY(mark(timing, true, ts.gemm, s));
+  LRMOE_TRY(mark(timing, false, ts.reduce, s));
   LRMOE_TRY(hip_status(launch_reduce_partials(t, ops.partials, dW, d_out, d_in, s)));
-  LRMOE_TRY(mark(timing, true, 2, s));
+  LRMOE_TRY(mark(timing, true, ts.reduce, s));
   return LRMOE_OK;
+}
+
+// The whole path in one call.  bf16 storage: the gather writes the GEMM's
+// operand planes from the rows it moves (no prologue kernel reads the
+// compacted operand again); float32 storage: the separate steps.
+lrmoe_status pruned_backward(const lrmoe_problem* pb, const int32_t* g_row_index,
+                             const float* alpha, const void* g, const void* phi, const void* W,
+                             float* scores, uint8_t* keep, int32_t* seg_offsets, int32_t* perm,
+                             void* g_c, void* phi_c, float* alpha_c, float* dW, float* dphi,
+                             void* workspace, size_t ws_bytes, void* stream,
+                             const lrmoe_timing* timing) {
+  Checked c;
+  LRMOE_TRY(check_problem(pb, c));
+  const int64_t M = c.M;
+  LRMOE_TRY(need(W, 1));
+  LRMOE_TRY(need(dW, 1));
+  const GemmWorkspace wl = gemm_workspace(pb, M);
+  if (ws_bytes < workspace_bytes(pb, c)) return LRMOE_ERR_WORKSPACE;
+  LRMOE_TRY(need(workspace, (int64_t)wl.total));
+  GatherPlanes planes;
+  const bool fused = pb->dtype == LRMOE_BF16;
+  if (fused) {
+    char* ws = reinterpret_cast<char*>(workspace);
+    planes.hi = reinterpret_cast<uint16_t*>(ws + wl.b_hi);
+    planes.lo = pb->dw_mode == LRMOE_DW_EXACT ? reinterpret_cast<uint16_t*>(ws + wl.b_lo)
+                                              : nullptr;
+    planes.from_phi = wl.alpha_on_phi;
+    planes.zero = reinterpret_cast<int32_t*>(ws + wl.heads);
+    planes.nzero = kXcds;
+  }
+  LRMOE_TRY(select_compact(pb, true, nullptr, g_row_index, alpha, g, phi, scores, keep,
+                           seg_offsets, perm, g_c, phi_c, alpha_c, dphi, workspace, ws_bytes,
+                           stream, timing, true, planes));
+  TimingSlots ts;
+  ts.gemm = 3;
+  ts.reduce = 4;
+  ts.prologue = 5;
+  return grouped_backward(pb, perm, alpha_c, g_c, phi_c, W, dW, dphi, false, nullptr, nullptr,
+                          nullptr, workspace, ws_bytes, stream, timing, fused, ts);
 }
 
 }  // namespace
@@ -621,6 +671,27 @@ lrmoe_status lrmoe_grouped_backward_timed(const lrmoe_problem* pb, const int32_t
                                           void* stream, const lrmoe_timing* timing) {
   return grouped_backward(pb, perm, alpha_c, g_c, phi_c, W, dW, dphi, false, nullptr, nullptr,
                           nullptr, workspace, ws_bytes, stream, timing);
+}
+
+lrmoe_status lrmoe_pruned_backward(const lrmoe_problem* pb, const int32_t* g_row_index,
+                                   const float* alpha, const void* g, const void* phi,
+                                   const void* W, float* scores, uint8_t* keep,
+                                   int32_t* seg_offsets, int32_t* perm, void* g_c, void* phi_c,
+                                   float* alpha_c, float* dW, float* dphi, void* workspace,
+                                   size_t ws_bytes, void* stream) {
+  return pruned_backward(pb, g_row_index, alpha, g, phi, W, scores, keep, seg_offsets, perm, g_c,
+                         phi_c, alpha_c, dW, dphi, workspace, ws_bytes, stream, nullptr);
+}
+
+lrmoe_status lrmoe_pruned_backward_timed(const lrmoe_problem* pb, const int32_t* g_row_index,
+                                         const float* alpha, const void* g, const void* phi,
+                                         const void* W, float* scores, uint8_t* keep,
+                                         int32_t* seg_offsets, int32_t* perm, void* g_c,
+                                         void* phi_c, float* alpha_c, float* dW, float* dphi,
+                                         void* workspace, size_t ws_bytes, void* stream,
+                                         const lrmoe_timing* timing) {
+  return pruned_backward(pb, g_row_index, alpha, g, phi, W, scores, keep, seg_offsets, perm, g_c,
+                         phi_c, alpha_c, dW, dphi, workspace, ws_bytes, stream, timing);
 }
 
 lrmoe_status lrmoe_grouped_backward_glu(const lrmoe_problem* pb, const int32_t* perm,

@@ -13,6 +13,8 @@
 namespace lrmoe {
 namespace {
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
 __device__ __forceinline__ void copy_row(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                          int nchunk, int lane) {
   int c = lane;
@@ -23,14 +25,47 @@ __device__ __forceinline__ void copy_row(const uint4* __restrict__ src, uint4* _
   for (; c < nchunk; c += 64) dst[c] = src[c];
 }
 
+// copy_row that also writes the bf16 hi (+ lo) planes of a * row (bf16 rows).
+__device__ __forceinline__ void copy_row_split(const uint4* __restrict__ src,
+                                               uint4* __restrict__ dst, uint4* __restrict__ hi,
+                                               uint4* __restrict__ lo, float a, int nchunk,
+                                               int lane) {
+  auto split = [&](int c, const uint4& x) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    bf16x8 h, l;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const HiLo e0 = alpha_split(a, __uint_as_float(w[i] << 16));
+      const HiLo e1 = alpha_split(a, __uint_as_float(w[i] & 0xFFFF0000u));
+      h[2 * i] = e0.h; l[2 * i] = e0.l;
+      h[2 * i + 1] = e1.h; l[2 * i + 1] = e1.l;
+    }
+    hi[c] = __builtin_bit_cast(uint4, h);
+    if (lo != nullptr) lo[c] = __builtin_bit_cast(uint4, l);
+  };
+  int c = lane;
+  for (; c + 64 < nchunk; c += 128) {
+    const uint4 x0 = src[c], x1 = src[c + 64];
+    dst[c] = x0; dst[c + 64] = x1;
+    split(c, x0); split(c + 64, x1);
+  }
+  for (; c < nchunk; c += 64) {
+    const uint4 x = src[c];
+    dst[c] = x;
+    split(c, x);
+  }
+}
+
 __global__ __launch_bounds__(256) void gather_kernel(
     const int32_t* __restrict__ perm, const uint8_t* __restrict__ keep,
     const int32_t* __restrict__ g_row_index, const int32_t* __restrict__ phi_row_index,
     const float* __restrict__ alpha, const uint4* __restrict__ g, const uint4* __restrict__ phi,
     uint4* __restrict__ g_c, uint4* __restrict__ phi_c, float* __restrict__ alpha_c,
     float4* __restrict__ dphi_zero, int32_t M, int32_t P, int32_t gch, int32_t pch,
-    int32_t zch) {
+    int32_t zch, uint4* __restrict__ pl_hi, uint4* __restrict__ pl_lo, int pl_from_phi,
+    int32_t* __restrict__ zero, int nzero) {
   const int lane = threadIdx.x & 63;
+  if (blockIdx.x == 0 && (int)threadIdx.x < nzero) zero[threadIdx.x] = 0;
   const int64_t job = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (job < M) {
     const int32_t j = (int32_t)job;
@@ -38,9 +73,18 @@ __global__ __launch_bounds__(256) void gather_kernel(
     if ((uint32_t)u >= (uint32_t)P) return;   // perm holds pair indices < P
     const int64_t gr = g_row_index ? (int64_t)g_row_index[u] : (int64_t)u;
     const int64_t pr = phi_row_index ? (int64_t)phi_row_index[u] : (int64_t)u;
-    if (g_c != nullptr) copy_row(g + gr * gch, g_c + (int64_t)j * gch, gch, lane);
-    copy_row(phi + pr * pch, phi_c + (int64_t)j * pch, pch, lane);
-    if (lane == 0) alpha_c[j] = alpha[u];
+    const float a = alpha[u];
+    if (pl_hi != nullptr && !pl_from_phi)
+      copy_row_split(g + gr * gch, g_c + (int64_t)j * gch, pl_hi + (int64_t)j * gch,
+                     pl_lo ? pl_lo + (int64_t)j * gch : nullptr, a, gch, lane);
+    else if (g_c != nullptr)
+      copy_row(g + gr * gch, g_c + (int64_t)j * gch, gch, lane);
+    if (pl_hi != nullptr && pl_from_phi)
+      copy_row_split(phi + pr * pch, phi_c + (int64_t)j * pch, pl_hi + (int64_t)j * pch,
+                     pl_lo ? pl_lo + (int64_t)j * pch : nullptr, a, pch, lane);
+    else
+      copy_row(phi + pr * pch, phi_c + (int64_t)j * pch, pch, lane);
+    if (lane == 0) alpha_c[j] = a;
   } else if (dphi_zero != nullptr && job < (int64_t)M + P) {
     const int64_t u = job - M;
     if (!keep[u]) {
@@ -84,15 +128,18 @@ hipError_t launch_gather(int dtype, const int32_t* perm, const uint8_t* keep,
                          const int32_t* g_row_index, const int32_t* phi_row_index,
                          const float* alpha, const void* g, const void* phi, void* g_c,
                          void* phi_c, float* alpha_c, float* dphi_zero, int32_t M,
-                         int32_t P, int32_t d_out, int32_t d_in, hipStream_t s) {
+                         int32_t P, int32_t d_out, int32_t d_in, hipStream_t s,
+                         const GatherPlanes& planes) {
   const int per = (dtype == LRMOE_BF16) ? 8 : 4;
+  if (planes.hi != nullptr && dtype != LRMOE_BF16) return hipErrorInvalidValue;
   const int64_t jobs = (int64_t)M + (dphi_zero ? (int64_t)P : 0);
-  if (jobs == 0) return hipSuccess;
+  if (jobs == 0) return planes.nzero > 0 ? launch_zero(planes.zero, planes.nzero, s) : hipSuccess;
   const int64_t blocks = (jobs + 3) / 4;
   hipLaunchKernelGGL(gather_kernel, dim3((unsigned)blocks), dim3(256), 0, s, perm, keep,
                      g_row_index, phi_row_index, alpha, (const uint4*)g, (const uint4*)phi,
                      (uint4*)g_c, (uint4*)phi_c, alpha_c, (float4*)dphi_zero, M, P,
-                     d_out / per, d_in / per, d_in / 4);
+                     d_out / per, d_in / per, d_in / 4, (uint4*)planes.hi, (uint4*)planes.lo,
+                     planes.from_phi ? 1 : 0, planes.zero, planes.nzero);
   return hipGetLastError();
 }
 

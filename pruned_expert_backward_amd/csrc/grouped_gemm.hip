@@ -919,9 +919,9 @@ __global__ __launch_bounds__(256) void split_kernel(const void* __restrict__ src
     bf16x8 h, l;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float y = (i < 4 ? a0 : a1) * x[i];
-      h[i] = (__bf16)y;
-      l[i] = (__bf16)(y - (float)h[i]);
+      const HiLo e = alpha_split(i < 4 ? a0 : a1, x[i]);
+      h[i] = e.h;
+      l[i] = e.l;
     }
     const u32x4 hw = __builtin_bit_cast(u32x4, h), lw = __builtin_bit_cast(u32x4, l);
     if (two) {

@@ -110,6 +110,18 @@ __host__ __device__ inline int64_t partial_base(const GemmTable& t, int e) {
   return base;
 }
 
+// alpha * x split into bf16 hi = RNE(alpha x) and lo = RNE(alpha x - hi),
+// the residual from one explicit FMA (exact product, one rounding), so that
+// the operand planes are bit for bit the same wherever they are written --
+// no compiler choice of contraction is involved.
+struct HiLo {
+  __bf16 h, l;
+};
+__device__ __forceinline__ HiLo alpha_split(float a, float x) {
+  const __bf16 h = (__bf16)(a * x);
+  return {h, (__bf16)__builtin_fmaf(a, x, -(float)h)};
+}
+
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_score(int dtype, int mode, const void* g, const void* phi, const float* alpha,
                         const int32_t* row_index, int32_t P, int32_t d_out, int32_t d_in,
@@ -127,11 +139,24 @@ hipError_t launch_plan_quota_device(const int32_t* ids, int32_t n_ids, int32_t E
 hipError_t launch_mask_alpha(int32_t P, const uint8_t* keep, const float* alpha,
                              float* alpha_masked, int32_t* perm_identity, hipStream_t s);
 
+// Operand planes the gather may write in passing (bf16 storage): alpha[u] *
+// (the kept row of phi if from_phi, else of g) as bf16 hi (+ lo) planes,
+// [M, width], row j for compacted row j -- what launch_split would write
+// from the compacted buffer -- and the GEMM's queue counters cleared.
+struct GatherPlanes {
+  uint16_t* hi = nullptr;   // nullptr: no planes
+  uint16_t* lo = nullptr;
+  bool from_phi = true;
+  int32_t* zero = nullptr;
+  int nzero = 0;
+};
+
 hipError_t launch_gather(int dtype, const int32_t* perm, const uint8_t* keep,
                          const int32_t* g_row_index, const int32_t* phi_row_index,
                          const float* alpha, const void* g, const void* phi, void* g_c,
                          void* phi_c, float* alpha_c, float* dphi_zero, int32_t M,
-                         int32_t P, int32_t d_out, int32_t d_in, hipStream_t s);
+                         int32_t P, int32_t d_out, int32_t d_in, hipStream_t s,
+                         const GatherPlanes& planes = GatherPlanes());
 
 // hi (and lo, if non-null) bf16 planes of alpha[row] * src[row][col] (alpha
 // may be null); src is bf16 or float32 storage.

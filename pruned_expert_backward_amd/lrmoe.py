@@ -21,7 +21,7 @@ DW_EXACT, DW_BF16 = 0, 1
 SCORE_LRM, SCORE_GRAD_SQNORM, SCORE_GRAD_L1 = 0, 1, 2
 QUOTA_RATIO, QUOTA_BUDGET = 0, 1
 MAX_EXPERTS = 256
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 STATUS = {0: "LRMOE_OK", 1: "LRMOE_ERR_NULL", 2: "LRMOE_ERR_INVALID", 3: "LRMOE_ERR_SHAPE",
           4: "LRMOE_ERR_ALIGN", 5: "LRMOE_ERR_DTYPE", 6: "LRMOE_ERR_WORKSPACE",
@@ -32,8 +32,9 @@ EXPORTS = ["lrmoe_abi_version", "lrmoe_status_string", "lrmoe_plan_quota",
            "lrmoe_gather_compact", "lrmoe_grouped_backward", "lrmoe_score_select_compact_timed",
            "lrmoe_select_compact_timed", "lrmoe_grouped_backward_timed", "lrmoe_score_select",
            "lrmoe_mask_alpha", "lrmoe_plan_quota_device", "lrmoe_grouped_backward_glu",
-           "lrmoe_grouped_backward_glu_timed"]
-TIMING_SLOTS = 4
+           "lrmoe_grouped_backward_glu_timed", "lrmoe_pruned_backward",
+           "lrmoe_pruned_backward_timed"]
+TIMING_SLOTS = 8
 
 
 class LrmoeError(RuntimeError):
@@ -103,6 +104,11 @@ def lib() -> C.CDLL:
     L.lrmoe_grouped_backward_timed.restype = C.c_int
     L.lrmoe_grouped_backward_timed.argtypes = ([C.POINTER(Problem)] + [_P] * 8 +
                                                [C.c_size_t, _P, C.POINTER(Timing)])
+    L.lrmoe_pruned_backward.restype = C.c_int
+    L.lrmoe_pruned_backward.argtypes = [C.POINTER(Problem)] + [_P] * 15 + [C.c_size_t, _P]
+    L.lrmoe_pruned_backward_timed.restype = C.c_int
+    L.lrmoe_pruned_backward_timed.argtypes = ([C.POINTER(Problem)] + [_P] * 15 +
+                                              [C.c_size_t, _P, C.POINTER(Timing)])
     L.lrmoe_grouped_backward_glu.restype = C.c_int
     L.lrmoe_grouped_backward_glu.argtypes = [C.POINTER(Problem)] + [_P] * 10 + [C.c_size_t, _P]
     L.lrmoe_grouped_backward_glu_timed.restype = C.c_int
@@ -466,9 +472,25 @@ class KernelTimer:
         self.timings = []
 
 
-def pruned_backward(plan: Plan, alpha, g, phi, W, g_row_index=None, out=None, ws=None) -> dict:
-    """The whole path: score, select, compact, dW and dphi."""
-    out = score_select_compact(plan, alpha, g, phi, g_row_index=g_row_index, out=out, ws=ws)
-    out["dW"] = grouped_backward(plan, out["perm"], out["alpha_c"], out["g_c"], out["phi_c"], W,
-                                 dW=out.get("dW"), dphi=out.get("dphi"), ws=ws)
+def pruned_backward(plan: Plan, alpha, g, phi, W, g_row_index=None, out=None, ws=None,
+                    timing: Optional["KernelTimer"] = None) -> dict:
+    """The whole path in one library call (lrmoe_pruned_backward): score,
+    select, compact, dW and dphi.  `out` holds the buffers of
+    alloc_select_outputs plus "dW"; missing ones are allocated."""
+    dev = phi.device
+    if out is None:
+        out = alloc_select_outputs(plan, dev)
+    if out.get("dW") is None:
+        out["dW"] = _empty((plan.E, plan.d_out, plan.d_in), torch.float32, dev)
+    if ws is None:
+        ws = workspace(plan, dev)
+    args = (C.byref(plan.struct), _ptr(g_row_index), _ptr(alpha), _ptr(g), _ptr(phi), _ptr(W),
+            _ptr(out["scores"]), _ptr(out["keep"]), _ptr(out["seg_offsets"]), _ptr(out["perm"]),
+            _ptr(out["g_c"]), _ptr(out["phi_c"]), _ptr(out["alpha_c"]), _ptr(out["dW"]),
+            _ptr(out.get("dphi")), _ptr(ws), ws.numel(), _stream())
+    if timing is not None:
+        check("lrmoe_pruned_backward_timed",
+              lib().lrmoe_pruned_backward_timed(*args, C.byref(timing.next_slots())))
+    else:
+        check("lrmoe_pruned_backward", lib().lrmoe_pruned_backward(*args))
     return out

@@ -204,6 +204,26 @@ def test_grouped_backward_glu_validation():
     assert f(None, *ok) == 1
 
 
+def test_pruned_backward_validation():
+    """The whole-path call checks what its two steps check, before any launch."""
+    f = L.lib().lrmoe_pruned_backward
+    p = plan()
+    n = p.workspace_bytes()
+    # g_row_index alpha g phi W scores keep seg perm g_c phi_c alpha_c dW dphi ws
+    ok = [None] + [FAKE] * 14 + [n, None]
+    for i in (1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 14):   # 13: dphi may be NULL
+        a = list(ok)
+        a[i] = None
+        assert f(C.byref(p.struct), *a) == 1, i
+    a = list(ok)
+    a[15] = n - 1
+    assert f(C.byref(p.struct), *a) == 6
+    a = list(ok)
+    a[12] = FAKE + 4
+    assert f(C.byref(p.struct), *a) == 4
+    assert f(None, *ok) == 1
+
+
 def test_gather_compact_validation():
     p = plan()
     f = L.lib().lrmoe_gather_compact

@@ -284,6 +284,51 @@ def test_glu_chain_edges():
             assert e <= U.TOL, (i, k, e)
 
 
+WHOLE = [
+    ("bf16-exact-alpha-on-phi", dict(P=3000, E=5, d_out=264, d_in=200, dtype="bf16",
+                                     counts=[1400, 0, 977, 7, 616]), lrmoe.DW_EXACT),
+    ("bf16-exact-alpha-on-g", dict(P=2500, E=4, d_out=136, d_in=392, dtype="bf16", zipf=1.6),
+     lrmoe.DW_EXACT),
+    ("bf16-single-rounding", dict(P=2000, E=3, d_out=256, d_in=128, dtype="bf16", zipf=1.2),
+     lrmoe.DW_BF16),
+    ("fp32", dict(P=1500, E=4, d_out=196, d_in=140, dtype="f32", zipf=1.2), lrmoe.DW_EXACT),
+    ("large-expert", dict(P=40000, E=2, d_out=64, d_in=72, dtype="bf16", counts=[39000, 1000]),
+     lrmoe.DW_EXACT),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(WHOLE)), ids=[w[0] for w in WHOLE])
+def test_whole_path_call_matches_separate_calls(idx):
+    """lrmoe_pruned_backward (one call; with bf16 storage the gather writes
+    the GEMM's operand planes) gives bit for bit the results of
+    lrmoe_score_select_compact followed by lrmoe_grouped_backward, including
+    an expert large enough for the multi-workgroup histogram, whose workspace
+    the planes reuse afterwards."""
+    name, kw, dw_mode = WHOLE[idx]
+    p = W.make_problem(seed=340 + idx, policy=("ratio", 4, 5), name=name, **kw)
+    q = lrmoe.plan_quota(p.counts, p.policy)
+    plan, sep, t = U.run_gpu(p, q, dw_mode=dw_mode)
+    one = lrmoe.pruned_backward(plan, t["alpha"], t["g"], t["phi"], t["W"], g_row_index=t["row"])
+    torch.cuda.synchronize()
+    for k in ("scores", "keep", "perm", "seg_offsets", "g_c", "phi_c", "alpha_c", "dW", "dphi"):
+        a, b = sep[k], one[k]
+        if a.dtype == torch.bfloat16:
+            a, b = a.view(torch.int16), b.view(torch.int16)
+        assert torch.equal(a, b), (name, k)
+    if idx == 0:   # and the oracle agrees with both
+        errs, _ = U.compare_full(p, q, one, dw_mode=dw_mode)
+        print(name, errs)
+
+
+def test_whole_path_call_nothing_kept():
+    p = W.make_problem(P=500, E=3, d_out=64, d_in=32, dtype="bf16", counts=[200, 0, 300], seed=9)
+    plan = lrmoe.Plan(p.counts, [0, 0, 0], p.d_out, p.d_in, lrmoe.BF16)
+    one = lrmoe.pruned_backward(plan, U.dev(p.alpha), U.dev(p.g), U.dev(p.phi), U.dev(p.W))
+    torch.cuda.synchronize()
+    assert float(one["dW"].abs().max()) == 0.0 and float(one["dphi"].abs().max()) == 0.0
+    assert not one["keep"].cpu().numpy().any()
+
+
 def test_empty_problem_pieces():
     """All experts empty but one; quotas zero everywhere (M = 0)."""
     p = W.make_problem(P=300, E=4, d_out=64, d_in=64, dtype="bf16", counts=[0, 300, 0, 0], seed=2)
