@@ -359,3 +359,43 @@ def test_plan_quota_device(policy):
         assert np.array_equal(out["quotas"].cpu().numpy(), q)
         assert np.array_equal(out["seg_offsets"].cpu().numpy(), np.concatenate([[0], np.cumsum(q)]))
         assert int(out["invalid"].cpu()[0]) == n - valid.size
+
+
+def test_whole_path_in_a_hip_graph():
+    """The one-call path captured in a HIP graph (the library launches only
+    kernels on the caller's stream: no allocation, no memset, no host sync)
+    and replayed several times, with eager work and synchronisations in
+    between: every replay equals the eager result bit for bit."""
+    p = W.make_problem(P=3000, E=5, d_out=264, d_in=200, dtype="bf16",
+                       counts=[1400, 0, 977, 7, 616], seed=361, policy=("ratio", 4, 5))
+    q = lrmoe.plan_quota(p.counts, p.policy)
+    plan = lrmoe.Plan(p.counts, q, p.d_out, p.d_in, lrmoe.BF16)
+    t = dict(alpha=U.dev(p.alpha), g=U.dev(p.g), phi=U.dev(p.phi), W=U.dev(p.W))
+    ws = lrmoe.workspace(plan, U.DEV)
+    eager = lrmoe.pruned_backward(plan, t["alpha"], t["g"], t["phi"], t["W"], ws=ws)
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in eager.items()}
+    out = {k: torch.empty_like(v) for k, v in eager.items()}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up on the capture stream
+        lrmoe.pruned_backward(plan, t["alpha"], t["g"], t["phi"], t["W"], out=out, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        lrmoe.pruned_backward(plan, t["alpha"], t["g"], t["phi"], t["W"], out=out, ws=ws)
+    for r in range(3):
+        for v in out.values():
+            v.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, v in ref.items():
+            a, b = v, out[k]
+            if a.dtype == torch.bfloat16:
+                a, b = a.view(torch.int16), b.view(torch.int16)
+            assert torch.equal(a, b), (r, k)
+        # eager work between replays, on the same buffers' inputs
+        lrmoe.pruned_backward(plan, t["alpha"], t["g"], t["phi"], t["W"], ws=ws)
+        torch.cuda.synchronize()
