@@ -1,5 +1,5 @@
 """GPU parity at the full workload sizes, in the launch configuration the
-benchmark times.  Keep sets, offsets, permutation and compacted buffers are
+benchmark times (the one-call path, lrmoe_pruned_backward).  Keep sets, offsets, permutation and compacted buffers are
 compared in full; dW and dphi on sampled outputs the oracle computes one by
 one (a row/column block of every expert's dW; kept and dropped dphi rows),
 with the tolerance taken against the sample's own max |ref| (stricter than
@@ -38,7 +38,11 @@ def oracle_scores(p, block=8192):
 def check_fullsize(p, dw_mode=lrmoe.DW_EXACT, gate_up=False, seed=0):
     q = lrmoe.plan_quota(p.counts, p.policy)
     assert q == O.plan_quota(p.counts, p.policy)
-    plan, out, t = U.run_gpu(p, q, dw_mode=dw_mode)
+    plan = lrmoe.Plan(p.counts, q, p.d_out, p.d_in, U.dtype_code(p), T=p.T, dw_mode=dw_mode)
+    t = dict(alpha=U.dev(p.alpha), g=U.dev(p.g), phi=U.dev(p.phi), W=U.dev(p.W),
+             row=U.dev(p.row_index))
+    out = lrmoe.pruned_backward(plan, t["alpha"], t["g"], t["phi"], t["W"], g_row_index=t["row"])
+    torch.cuda.synchronize()
     R = oracle_scores(p)
     keep_ref, taus = O.select_top_quota(R, p.counts, q)
     keep_gpu = out["keep"].cpu().numpy().astype(bool)
@@ -90,6 +94,13 @@ def check_fullsize(p, dw_mode=lrmoe.DW_EXACT, gate_up=False, seed=0):
 @pytest.mark.parametrize("c", [1, 3])
 def test_fullsize_down_projection(c):
     check_fullsize(W.config(c), seed=c)
+
+
+@pytest.mark.parametrize("c", [1, 3])
+def test_fullsize_down_projection_single_rounding(c):
+    """The single-rounding dW mode (alpha * phi rounded once to bf16) meets the
+    same tolerance at full size."""
+    check_fullsize(W.config(c), dw_mode=lrmoe.DW_BF16, seed=10 + c)
 
 
 def test_fullsize_qwen3_c30_with_gate_up():
