@@ -289,15 +289,10 @@ def main():
         if not whole:
             lrmoe.grouped_backward(plan, out["perm"], out["alpha_c"], out["g_c"], out["phi_c"],
                                    W, dW=dW, dphi=out["dphi"], ws=ws, timing=gb_t)
-        if gu is not None:
-            if gu_events is not None:
-                gu_events[0].record(stream)
-            lrmoe.gather_compact(plan2, out["perm"], out["keep"], alpha, g2, x, out=out2)
-            if gu_events is not None:
-                gu_events[1].record(stream)
-            lrmoe.grouped_backward(plan2, out["perm"], out2["alpha_c"], out2["g_c"],
-                                   out2["phi_c"], W2, dW=dW2, dphi=out2["dphi"], ws=ws2,
-                                   timing=gu_t)
+        if gu is not None:   # gather (with operand planes) + grouped GEMM in one call
+            out2["dW"] = dW2
+            lrmoe.gather_backward(plan2, out["perm"], out["keep"], alpha, g2, x, W2, out=out2,
+                                  ws=ws2, timing=gu_t)
 
     for _ in range(args.warmup):
         step()
@@ -306,11 +301,13 @@ def main():
     # kernel (the grouped GEMM launch; in the MLP chain the larger gate/up
     # one), recorded by the library on the stream it launches on; events
     # around every kernel would add gaps to the step.
-    gemm_slot = 3 if whole else 1
+    # the dominant GEMM: the gate/up projection's where there is one (the
+    # larger), else the down projection's
+    gemm_slot = 1 if chain or not (whole or gu is not None) else 3
     gemm_timer = lrmoe.KernelTimer(args.steps, slots=(gemm_slot,))
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        if chain:
+        if gu is not None:
             step(gu_t=gemm_timer)
         elif whole:
             step(ssc_t=gemm_timer)
@@ -381,13 +378,13 @@ def main():
     nbytes = algorithmic_bytes(p, M, args.score_mode)
     if chain:   # no dphi rows to zero in the original layout
         nbytes -= (P - M) * 4 * d_i
-    dominant_flops = 4.0 * M * gu.d_out * gu.d_in if chain else work["grouped_gemm"]
+    dominant_flops = 4.0 * M * gu.d_out * gu.d_in if gu is not None else work["grouped_gemm"]
     gemm_tf = dominant_flops / gemm_live["mean"] / 1e6
     # MFMA work the kernel executes: products of split operands cost one MFMA
     # pass per term (exact mode: alpha * (narrower operand) as hi + lo).
     terms_dw = 1 + (args.dw_mode == "exact" or p.dtype != "bf16") + (p.dtype != "bf16")
     terms_dp = 1 if p.dtype == "bf16" else 3
-    if chain:
+    if gu is not None:
         exec_flops = 2.0 * M * gu.d_out * gu.d_in * (terms_dw + terms_dp)
     else:
         Mx = p.P if dense_path else M
@@ -397,10 +394,10 @@ def main():
                 mfma_executed_TFLOPs=exec_flops / gemm_live["mean"] / 1e6,
                 launch_us_mean=gemm_live["mean"], launch_us_median=gemm_live["median"],
                 launches=gemm_live["launches"],
-                traffic=None if chain else read_counters(p.name, args.dw_mode),
+                traffic=None if gu is not None else read_counters(p.name, args.dw_mode),
                 traffic_unit="bytes per launch",
                 algorithmic_bytes_floor=gemm_floor_bytes(p, M))
-    if chain:
+    if gu is not None:
         roof["note"] = "the gate/up projection's grouped GEMM (its flops 4 M d_out2 d_in2)"
         es2 = 2
         roof["algorithmic_bytes_floor"] = (M * es2 * (gu.d_out + gu.d_in)
@@ -436,8 +433,14 @@ def main():
                         "around every kernel",
     }
     if gu is not None:
-        gd = stats_us([a.elapsed_time(b) * 1e3 for a, b in gu_ev])
-        gg = stats_us(gu_timer.durations_us(1))
+        if chain:
+            gd = stats_us([a.elapsed_time(b) * 1e3 for a, b in gu_ev])
+            gg = stats_us(gu_timer.durations_us(1))
+            gpro, gred = gu_timer.mean_us(0), gu_timer.mean_us(2)
+        else:   # lrmoe_gather_backward slots: gather 2, GEMM 3, reduction 4
+            gd = stats_us(gu_timer.durations_us(2))
+            gg = stats_us(gu_timer.durations_us(3))
+            gpro, gred = gu_timer.mean_us(5), gu_timer.mean_us(4)
         if chain:   # x rows and alpha only: the gate/up gradient is already compacted
             gbytes = M * (2 * es * gu.d_in + 12) + (P - M) * 4 * gu.d_in
         else:
@@ -451,7 +454,7 @@ def main():
             "grouped_gemm": {"us": gg["mean"], "us_median": gg["median"],
                              "algorithmic_flops": gfl, "TFLOPs": gfl / gg["mean"] / 1e6,
                              "mfma_frac": gfl / gg["mean"] / 1e6 / MFMA_BF16_PEAK_TFLOPS},
-            "operand_prologue_us": gu_timer.mean_us(0), "splitk_reduce_us": gu_timer.mean_us(2)}
+            "operand_prologue_us": gpro, "splitk_reduce_us": gred}
         gu_timer.close()
     if dense_path:
         sd = stats_us([a.elapsed_time(b) * 1e3 for a, b in gu_ev])

@@ -238,6 +238,21 @@ lrmoe_status lrmoe_gather_compact(
     const float* alpha, const void* g, const void* phi, void* g_c,
     void* phi_c, float* alpha_c, float* dphi_zero, void* stream);
 
+/* lrmoe_gather_compact followed by lrmoe_grouped_backward on the same
+ * buffers, for a projection on an inherited keep set (the gate/up projection
+ * above), in one call.  With bf16 storage the gather also writes the GEMM's
+ * operand planes from the rows it moves (as in lrmoe_pruned_backward), bit
+ * for bit the separate calls' results.  g and g_c are required here; dphi is
+ * both the zero target of dropped rows and the output of kept rows (or
+ * NULL).  workspace: lrmoe_workspace_size bytes.  Errors as for the two
+ * calls. */
+lrmoe_status lrmoe_gather_backward(
+    const lrmoe_problem* pb, const int32_t* perm, const uint8_t* keep,
+    const int32_t* g_row_index, const int32_t* phi_row_index,
+    const float* alpha, const void* g, const void* phi, const void* W,
+    void* g_c, void* phi_c, float* alpha_c, float* dW, float* dphi,
+    void* workspace, size_t ws_bytes, void* stream);
+
 /* Step 5: variable-length grouped GEMMs over the compacted buffers.
  *   dW   f32 [E, d_out, d_in]: fully overwritten (zero for q_e = 0)
  *   dphi f32 [P, d_in] or NULL: rows perm[j] receive alpha_c[j] W_e^T g_c[j];
@@ -305,6 +320,9 @@ lrmoe_status lrmoe_pruned_backward(
  *                                     [2] split-K reduction
  *   lrmoe_pruned_backward_timed:      [0] score  [1] select+scan  [2] gather
  *                                     [3] grouped GEMM  [4] split-K reduction
+ *                                     [5] operand prologue (float32 storage)
+ *   lrmoe_gather_backward_timed:      [2] gather  [3] grouped GEMM
+ *                                     [4] split-K reduction
  *                                     [5] operand prologue (float32 storage) */
 #define LRMOE_TIMING_SLOTS 8
 typedef struct {
@@ -341,6 +359,14 @@ lrmoe_status lrmoe_pruned_backward_timed(
     int32_t* seg_offsets, int32_t* perm, void* g_c, void* phi_c, float* alpha_c,
     float* dW, float* dphi, void* workspace, size_t ws_bytes, void* stream,
     const lrmoe_timing* timing);
+
+/* lrmoe_gather_backward with per-kernel events (timing may be NULL). */
+lrmoe_status lrmoe_gather_backward_timed(
+    const lrmoe_problem* pb, const int32_t* perm, const uint8_t* keep,
+    const int32_t* g_row_index, const int32_t* phi_row_index,
+    const float* alpha, const void* g, const void* phi, const void* W,
+    void* g_c, void* phi_c, float* alpha_c, float* dW, float* dphi,
+    void* workspace, size_t ws_bytes, void* stream, const lrmoe_timing* timing);
 
 /* lrmoe_grouped_backward_glu with per-kernel events (timing may be NULL). */
 lrmoe_status lrmoe_grouped_backward_glu_timed(

@@ -476,6 +476,78 @@ lrmoe_status pruned_backward(const lrmoe_problem* pb, const int32_t* g_row_index
                           nullptr, workspace, ws_bytes, stream, timing, fused, ts);
 }
 
+
+lrmoe_status gather_compact(const lrmoe_problem* pb, const int32_t* perm, const uint8_t* keep,
+                            const int32_t* g_row_index, const int32_t* phi_row_index,
+                            const float* alpha, const void* g, const void* phi, void* g_c,
+                            void* phi_c, float* alpha_c, float* dphi_zero, void* stream,
+                            const lrmoe_timing* timing, const GatherPlanes& planes) {
+  Checked c;
+  LRMOE_TRY(check_problem(pb, c));
+  const int64_t P = pb->P, M = c.M;
+  const bool with_g = g != nullptr || g_c != nullptr;   // both NULL: phi rows only
+  if (with_g && g_row_index == nullptr && pb->T != P) return LRMOE_ERR_SHAPE;
+  LRMOE_TRY(need(perm, M));
+  LRMOE_TRY(need(alpha, P));
+  if (with_g) {
+    LRMOE_TRY(need(g, M > 0 ? pb->T : 0));
+    LRMOE_TRY(need(g_c, M));
+  }
+  LRMOE_TRY(need(phi, M));
+  LRMOE_TRY(optional(g_row_index));
+  LRMOE_TRY(optional(phi_row_index));
+  LRMOE_TRY(need(phi_c, M));
+  LRMOE_TRY(need(alpha_c, M));
+  LRMOE_TRY(optional(dphi_zero));
+  if (dphi_zero != nullptr) LRMOE_TRY(need(keep, P));
+  if (planes.hi != nullptr && !with_g && !planes.from_phi) return LRMOE_ERR_NULL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  LRMOE_TRY(mark(timing, false, 2, s));
+  LRMOE_TRY(hip_status(launch_gather(pb->dtype, perm, keep, g_row_index, phi_row_index, alpha, g,
+                                     phi, g_c, phi_c, alpha_c, dphi_zero, (int32_t)M,
+                                     (int32_t)P, pb->d_out, pb->d_in, s, planes)));
+  LRMOE_TRY(mark(timing, true, 2, s));
+  return LRMOE_OK;
+}
+
+// Step 4 + step 5 for a projection on an inherited keep set: the gather also
+// writes the GEMM's operand planes (bf16 storage), then the grouped GEMMs.
+lrmoe_status gather_backward(const lrmoe_problem* pb, const int32_t* perm, const uint8_t* keep,
+                             const int32_t* g_row_index, const int32_t* phi_row_index,
+                             const float* alpha, const void* g, const void* phi, const void* W,
+                             void* g_c, void* phi_c, float* alpha_c, float* dW, float* dphi,
+                             void* workspace, size_t ws_bytes, void* stream,
+                             const lrmoe_timing* timing) {
+  Checked c;
+  LRMOE_TRY(check_problem(pb, c));
+  LRMOE_TRY(need(W, 1));
+  LRMOE_TRY(need(dW, 1));
+  LRMOE_TRY(need(g, c.M > 0 ? pb->T : 0));   // the GEMM needs g rows: no NULL g here
+  LRMOE_TRY(need(g_c, c.M));
+  const GemmWorkspace wl = gemm_workspace(pb, c.M);
+  if (ws_bytes < wl.total) return LRMOE_ERR_WORKSPACE;
+  LRMOE_TRY(need(workspace, (int64_t)wl.total));
+  GatherPlanes planes;
+  const bool fused = pb->dtype == LRMOE_BF16;
+  if (fused) {
+    char* ws = reinterpret_cast<char*>(workspace);
+    planes.hi = reinterpret_cast<uint16_t*>(ws + wl.b_hi);
+    planes.lo = pb->dw_mode == LRMOE_DW_EXACT ? reinterpret_cast<uint16_t*>(ws + wl.b_lo)
+                                              : nullptr;
+    planes.from_phi = wl.alpha_on_phi;
+    planes.zero = reinterpret_cast<int32_t*>(ws + wl.heads);
+    planes.nzero = kXcds;
+  }
+  LRMOE_TRY(gather_compact(pb, perm, keep, g_row_index, phi_row_index, alpha, g, phi, g_c, phi_c,
+                           alpha_c, dphi, stream, timing, planes));
+  TimingSlots ts;
+  ts.gemm = 3;
+  ts.reduce = 4;
+  ts.prologue = 5;
+  return grouped_backward(pb, perm, alpha_c, g_c, phi_c, W, dW, dphi, false, nullptr, nullptr,
+                          nullptr, workspace, ws_bytes, stream, timing, fused, ts);
+}
+
 }  // namespace
 
 extern "C" {
@@ -632,29 +704,31 @@ lrmoe_status lrmoe_gather_compact(const lrmoe_problem* pb, const int32_t* perm,
                                   const int32_t* phi_row_index, const float* alpha,
                                   const void* g, const void* phi, void* g_c, void* phi_c,
                                   float* alpha_c, float* dphi_zero, void* stream) {
-  Checked c;
-  LRMOE_TRY(check_problem(pb, c));
-  const int64_t P = pb->P, M = c.M;
-  const bool with_g = g != nullptr || g_c != nullptr;   // both NULL: phi rows only
-  if (with_g && g_row_index == nullptr && pb->T != P) return LRMOE_ERR_SHAPE;
-  LRMOE_TRY(need(perm, M));
-  LRMOE_TRY(need(alpha, P));
-  if (with_g) {
-    LRMOE_TRY(need(g, M > 0 ? pb->T : 0));
-    LRMOE_TRY(need(g_c, M));
-  }
-  LRMOE_TRY(need(phi, M));
-  LRMOE_TRY(optional(g_row_index));
-  LRMOE_TRY(optional(phi_row_index));
-  LRMOE_TRY(need(phi_c, M));
-  LRMOE_TRY(need(alpha_c, M));
-  LRMOE_TRY(optional(dphi_zero));
-  if (dphi_zero != nullptr) LRMOE_TRY(need(keep, P));
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  return hip_status(launch_gather(pb->dtype, perm, keep, g_row_index, phi_row_index, alpha, g,
-                                  phi, g_c, phi_c, alpha_c, dphi_zero, (int32_t)M, (int32_t)P,
-                                  pb->d_out, pb->d_in, s));
+  return gather_compact(pb, perm, keep, g_row_index, phi_row_index, alpha, g, phi, g_c, phi_c,
+                        alpha_c, dphi_zero, stream, nullptr, GatherPlanes());
 }
+
+lrmoe_status lrmoe_gather_backward(const lrmoe_problem* pb, const int32_t* perm,
+                                   const uint8_t* keep, const int32_t* g_row_index,
+                                   const int32_t* phi_row_index, const float* alpha,
+                                   const void* g, const void* phi, const void* W, void* g_c,
+                                   void* phi_c, float* alpha_c, float* dW, float* dphi,
+                                   void* workspace, size_t ws_bytes, void* stream) {
+  return gather_backward(pb, perm, keep, g_row_index, phi_row_index, alpha, g, phi, W, g_c,
+                         phi_c, alpha_c, dW, dphi, workspace, ws_bytes, stream, nullptr);
+}
+
+lrmoe_status lrmoe_gather_backward_timed(const lrmoe_problem* pb, const int32_t* perm,
+                                         const uint8_t* keep, const int32_t* g_row_index,
+                                         const int32_t* phi_row_index, const float* alpha,
+                                         const void* g, const void* phi, const void* W,
+                                         void* g_c, void* phi_c, float* alpha_c, float* dW,
+                                         float* dphi, void* workspace, size_t ws_bytes,
+                                         void* stream, const lrmoe_timing* timing) {
+  return gather_backward(pb, perm, keep, g_row_index, phi_row_index, alpha, g, phi, W, g_c,
+                         phi_c, alpha_c, dW, dphi, workspace, ws_bytes, stream, timing);
+}
+
 
 lrmoe_status lrmoe_grouped_backward(const lrmoe_problem* pb, const int32_t* perm,
                                     const float* alpha_c, const void* g_c, const void* phi_c,

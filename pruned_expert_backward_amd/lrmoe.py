@@ -33,7 +33,8 @@ EXPORTS = ["lrmoe_abi_version", "lrmoe_status_string", "lrmoe_plan_quota",
            "lrmoe_select_compact_timed", "lrmoe_grouped_backward_timed", "lrmoe_score_select",
            "lrmoe_mask_alpha", "lrmoe_plan_quota_device", "lrmoe_grouped_backward_glu",
            "lrmoe_grouped_backward_glu_timed", "lrmoe_pruned_backward",
-           "lrmoe_pruned_backward_timed"]
+           "lrmoe_pruned_backward_timed", "lrmoe_gather_backward",
+           "lrmoe_gather_backward_timed"]
 TIMING_SLOTS = 8
 
 
@@ -108,6 +109,11 @@ def lib() -> C.CDLL:
     L.lrmoe_pruned_backward.argtypes = [C.POINTER(Problem)] + [_P] * 15 + [C.c_size_t, _P]
     L.lrmoe_pruned_backward_timed.restype = C.c_int
     L.lrmoe_pruned_backward_timed.argtypes = ([C.POINTER(Problem)] + [_P] * 15 +
+                                              [C.c_size_t, _P, C.POINTER(Timing)])
+    L.lrmoe_gather_backward.restype = C.c_int
+    L.lrmoe_gather_backward.argtypes = [C.POINTER(Problem)] + [_P] * 14 + [C.c_size_t, _P]
+    L.lrmoe_gather_backward_timed.restype = C.c_int
+    L.lrmoe_gather_backward_timed.argtypes = ([C.POINTER(Problem)] + [_P] * 14 +
                                               [C.c_size_t, _P, C.POINTER(Timing)])
     L.lrmoe_grouped_backward_glu.restype = C.c_int
     L.lrmoe_grouped_backward_glu.argtypes = [C.POINTER(Problem)] + [_P] * 10 + [C.c_size_t, _P]
@@ -363,6 +369,36 @@ def grouped_backward(plan: Plan, perm, alpha_c, g_c, phi_c, W, dW=None, dphi=Non
     else:
         check("lrmoe_grouped_backward", lib().lrmoe_grouped_backward(*args))
     return dW
+
+
+def gather_backward(plan: Plan, perm, keep, alpha, g, phi, W, g_row_index=None,
+                    phi_row_index=None, out=None, ws=None,
+                    timing: Optional["KernelTimer"] = None) -> dict:
+    """gather_compact + grouped_backward for a projection on an inherited keep
+    set, in one library call (lrmoe_gather_backward): returns g_c, phi_c,
+    alpha_c, dW and dphi (dropped rows zero)."""
+    dev = phi.device
+    dt = plan.torch_dtype
+    if out is None:
+        out = {}
+    for k, shape, t in (("g_c", (plan.M, plan.d_out), dt), ("phi_c", (plan.M, plan.d_in), dt),
+                        ("alpha_c", (plan.M,), torch.float32),
+                        ("dW", (plan.E, plan.d_out, plan.d_in), torch.float32),
+                        ("dphi", (plan.P, plan.d_in), torch.float32)):
+        if out.get(k) is None:
+            out[k] = _empty(shape, t, dev)
+    if ws is None:
+        ws = workspace(plan, dev)
+    args = (C.byref(plan.struct), _ptr(perm), _ptr(keep), _ptr(g_row_index), _ptr(phi_row_index),
+            _ptr(alpha), _ptr(g), _ptr(phi), _ptr(W), _ptr(out["g_c"]), _ptr(out["phi_c"]),
+            _ptr(out["alpha_c"]), _ptr(out["dW"]), _ptr(out["dphi"]), _ptr(ws), ws.numel(),
+            _stream())
+    if timing is not None:
+        check("lrmoe_gather_backward_timed",
+              lib().lrmoe_gather_backward_timed(*args, C.byref(timing.next_slots())))
+    else:
+        check("lrmoe_gather_backward", lib().lrmoe_gather_backward(*args))
+    return out
 
 
 def grouped_backward_glu(plan: Plan, perm, alpha_c, g_c, phi_c, W, act_a, act_b, dW=None,

@@ -224,6 +224,25 @@ def test_pruned_backward_validation():
     assert f(None, *ok) == 1
 
 
+def test_gather_backward_validation():
+    f = L.lib().lrmoe_gather_backward
+    p = plan()
+    n = p.workspace_bytes()
+    # perm keep g_row phi_row alpha g phi W g_c phi_c alpha_c dW dphi ws
+    ok = [FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+          n, None]
+    for i in (0, 4, 5, 6, 7, 8, 9, 10, 11, 13):   # g is required here (the GEMM reads g_c)
+        a = list(ok)
+        a[i] = None
+        assert f(C.byref(p.struct), *a) == 1, i
+    a = list(ok)
+    a[14] = n - 1
+    assert f(C.byref(p.struct), *a) == 6
+    a = list(ok)
+    a[1], a[12] = None, FAKE   # zero target needs the keep flags
+    assert f(C.byref(p.struct), *a) == 1
+
+
 def test_gather_compact_validation():
     p = plan()
     f = L.lib().lrmoe_gather_compact

@@ -194,6 +194,13 @@ def test_gate_up_inherits_keep_set():
     e1 = U.rel_err(dW2.cpu().numpy(), ref["dW2"])
     e2 = U.rel_err(c2["dphi"].cpu().numpy(), ref["dx"])
     assert e1 <= U.TOL and e2 <= U.TOL, (e1, e2)
+    # the same in one call (gather writing the GEMM's operand planes): bit for bit
+    one = lrmoe.gather_backward(plan2, out["perm"], out["keep"], t["alpha"], U.dev(gu.g2),
+                                U.dev(gu.x), U.dev(gu.W2))
+    torch.cuda.synchronize()
+    assert torch.equal(one["dW"], dW2) and torch.equal(one["dphi"], c2["dphi"])
+    for k in ("g_c", "phi_c"):
+        assert torch.equal(one[k].view(torch.int16), c2[k].view(torch.int16)), k
 
 
 GLU_CASES = [
