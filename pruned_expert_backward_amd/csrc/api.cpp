@@ -154,8 +154,12 @@ GemmWorkspace gemm_workspace(const lrmoe_problem* pb, int64_t M) {
 }
 
 // Selection: one kHistBins-bin histogram per chunk of a large expert.
+// plus tau and need per expert and the (above, equal) counts of every chunk,
+// for the chunk-parallel scan of large experts.
 size_t select_workspace(const Checked& c) {
-  return (size_t)c.tab.hist_off[c.tab.E] * kHistBins * sizeof(uint32_t);
+  const size_t chunks = (size_t)c.tab.hist_off[c.tab.E];
+  if (chunks == 0) return 0;
+  return (chunks * kHistBins + 2 * (size_t)kMaxE + 2 * chunks) * sizeof(uint32_t);
 }
 
 size_t workspace_bytes(const lrmoe_problem* pb, const Checked& c) {

@@ -232,10 +232,103 @@ __device__ __forceinline__ float4 load4(const float* __restrict__ scores, int a,
   return v;
 }
 
+// ---- stable scan in pair order over pairs [base, end) of one expert: keep =
+// key > tau, or key == tau among the first `need` of the expert's equal keys;
+// kept pairs get consecutive compacted rows from seg.  run_gt / run_eq: the
+// expert's keys above / equal to tau before `base`.  Keys come from keys_lds
+// (pair g at keys_lds[g - lds_base]) or, when keys_lds is null, from the
+// global scores.  Tiles start at the aligned index base & ~3; thread t owns 8
+// consecutive pairs of a tile (those outside [base, end) are skipped); one
+// workgroup scan of (#gt, #eq) per tile gives every position.  The next
+// tile's loads go out before this tile is scanned.
+__device__ __forceinline__ void scan_keep(const uint32_t* keys_lds, const float* __restrict__ scores,
+                                          int P, int base, int end, int lds_base, uint32_t tau,
+                                          uint32_t need, uint32_t run_gt, uint32_t run_eq,
+                                          uint32_t q, int seg, uint8_t* __restrict__ keep,
+                                          int32_t* __restrict__ perm, uint32_t* wsum) {
+  const int tid = threadIdx.x;
+  const int gbeg = base & ~3;
+  const bool cached = keys_lds != nullptr;
+  auto load_tile = [&](int c, uint32_t (&kk)[kScanPer]) {
+    const int g0 = c + tid * kScanPer;
+    if (cached) {
+#pragma unroll
+      for (int j = 0; j < kScanPer; ++j) {
+        const int g = g0 + j;
+        kk[j] = (g >= base && g < end) ? keys_lds[g - lds_base] : 0u;
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < kScanPer / 4; ++h) {
+        const float4 v = load4(scores, g0 + 4 * h, P);
+        kk[4 * h] = score_key(v.x);
+        kk[4 * h + 1] = score_key(v.y);
+        kk[4 * h + 2] = score_key(v.z);
+        kk[4 * h + 3] = score_key(v.w);
+      }
+    }
+  };
+  uint32_t key[kScanPer], key_next[kScanPer];
+  load_tile(gbeg, key);
+  for (int c = gbeg; c < end; c += kScanTile) {
+    const int g0 = c + tid * kScanPer;
+    if (c + kScanTile < end) load_tile(c + kScanTile, key_next);
+    uint32_t ngt = 0, neq = 0;
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) {
+      const bool ok = g0 + j >= base && g0 + j < end;
+      ngt += (ok && key[j] > tau) ? 1u : 0u;
+      neq += (ok && key[j] == tau) ? 1u : 0u;
+    }
+    uint32_t tot;
+    const uint32_t incl = block_scan((ngt << 16) | neq, wsum, tot);   // per tile < 2^16 each
+    const uint32_t excl = incl - ((ngt << 16) | neq);
+    uint32_t gt_before = run_gt + (excl >> 16);
+    uint32_t eq_before = run_eq + (excl & 0xFFFFu);
+    // kept keys before this thread: every greater key, and the equal keys
+    // among the first `need` equal ones
+    uint32_t pos = gt_before + (eq_before < need ? eq_before : need);
+    uint32_t kept_bits = 0, valid_bits = 0;
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) {
+      const int g = g0 + j;
+      if (g >= base && g < end) {
+        const bool gt = key[j] > tau, eq = key[j] == tau;
+        const bool kp = gt || (eq && eq_before < need);
+        eq_before += eq ? 1u : 0u;
+        valid_bits |= 1u << j;
+        kept_bits |= (kp ? 1u : 0u) << j;
+        if (kp) {
+          if (pos < q) perm[seg + pos] = g;   // pos < q holds by construction
+          ++pos;
+        }
+      }
+    }
+    // keep flags: whole 4-byte groups at once when the range owns all four
+#pragma unroll
+    for (int h = 0; h < kScanPer / 4; ++h) {
+      const uint32_t vb = (valid_bits >> (4 * h)) & 15u, kb = (kept_bits >> (4 * h)) & 15u;
+      const int g = g0 + 4 * h;
+      if (vb == 15u) {
+        *reinterpret_cast<uint32_t*>(keep + g) =
+            (kb & 1u) | ((kb & 2u) << 7) | ((kb & 4u) << 14) | ((kb & 8u) << 21);
+      } else if (vb != 0u) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          if (vb & (1u << t)) keep[g + t] = (kb >> t) & 1u;
+      }
+    }
+    run_gt += tot >> 16;
+    run_eq += tot & 0xFFFFu;
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) key[j] = key_next[j];
+  }
+}
+
 __global__ __launch_bounds__(kSelThreads) void select_scan_kernel(
     ExpertTable tab, const float* __restrict__ scores, uint8_t* __restrict__ keep,
     int32_t* __restrict__ perm, int32_t* __restrict__ seg_offsets_out,
-    const uint32_t* __restrict__ hist_in) {
+    const uint32_t* __restrict__ hist_in, uint32_t* __restrict__ tau_need) {
   __shared__ uint32_t keys_lds[kSelLdsKeys];   // the expert's keys, or the candidates
   __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
   __shared__ uint32_t wsum[kSelWaves];
@@ -346,86 +439,64 @@ __global__ __launch_bounds__(kSelThreads) void select_scan_kernel(
     need = k;
   }
 
-  // ---- stable scan in pair order: keep = key > tau, or key == tau among
-  // the first `need` of those.  Tiles start at the aligned index gbeg; thread
-  // t owns 8 consecutive pairs of a tile (those outside the expert are
-  // skipped); one workgroup scan of (#gt, #eq) per tile gives every
-  // position.  The next tile's loads go out before this tile is scanned.
-  uint32_t run_gt = 0, run_eq = 0;
-  auto load_tile = [&](int c, uint32_t (&kk)[kScanPer]) {
-    const int g0 = c + tid * kScanPer;
-    if (cached) {
-#pragma unroll
-      for (int j = 0; j < kScanPer; ++j) {
-        const int g = g0 + j;
-        kk[j] = (g >= base && g < end) ? keys_lds[g - base] : 0u;
-      }
-    } else {
-#pragma unroll
-      for (int h = 0; h < kScanPer / 4; ++h) {
-        const float4 v = load4(scores, g0 + 4 * h, P);
-        kk[4 * h] = score_key(v.x);
-        kk[4 * h + 1] = score_key(v.y);
-        kk[4 * h + 2] = score_key(v.z);
-        kk[4 * h + 3] = score_key(v.w);
-      }
+  if (!cached) {   // the chunk kernels scan large experts, many workgroups at once
+    if (tid == 0) {
+      tau_need[2 * e] = tau;
+      tau_need[2 * e + 1] = need;
     }
-  };
-  uint32_t key[kScanPer], key_next[kScanPer];
-  load_tile(gbeg, key);
-  for (int c = gbeg; c < end; c += kScanTile) {
-    const int g0 = c + tid * kScanPer;
-    if (c + kScanTile < end) load_tile(c + kScanTile, key_next);
-    uint32_t ngt = 0, neq = 0;
-#pragma unroll
-    for (int j = 0; j < kScanPer; ++j) {
-      const bool ok = g0 + j >= base && g0 + j < end;
-      ngt += (ok && key[j] > tau) ? 1u : 0u;
-      neq += (ok && key[j] == tau) ? 1u : 0u;
-    }
-    uint32_t tot;
-    const uint32_t incl = block_scan((ngt << 16) | neq, wsum, tot);   // per tile < 2^16 each
-    const uint32_t excl = incl - ((ngt << 16) | neq);
-    uint32_t gt_before = run_gt + (excl >> 16);
-    uint32_t eq_before = run_eq + (excl & 0xFFFFu);
-    // kept keys before this thread: every greater key, and the equal keys
-    // among the first `need` equal ones
-    uint32_t pos = gt_before + (eq_before < need ? eq_before : need);
-    uint32_t kept_bits = 0, valid_bits = 0;
-#pragma unroll
-    for (int j = 0; j < kScanPer; ++j) {
-      const int g = g0 + j;
-      if (g >= base && g < end) {
-        const bool gt = key[j] > tau, eq = key[j] == tau;
-        const bool kp = gt || (eq && eq_before < need);
-        eq_before += eq ? 1u : 0u;
-        valid_bits |= 1u << j;
-        kept_bits |= (kp ? 1u : 0u) << j;
-        if (kp) {
-          if (pos < q) perm[seg + pos] = g;   // pos < q holds by construction
-          ++pos;
-        }
-      }
-    }
-    // keep flags: whole 4-byte groups at once when the expert owns all four
-#pragma unroll
-    for (int h = 0; h < kScanPer / 4; ++h) {
-      const uint32_t vb = (valid_bits >> (4 * h)) & 15u, kb = (kept_bits >> (4 * h)) & 15u;
-      const int g = g0 + 4 * h;
-      if (vb == 15u) {
-        *reinterpret_cast<uint32_t*>(keep + g) =
-            (kb & 1u) | ((kb & 2u) << 7) | ((kb & 4u) << 14) | ((kb & 8u) << 21);
-      } else if (vb != 0u) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          if (vb & (1u << t)) keep[g + t] = (kb >> t) & 1u;
-      }
-    }
-    run_gt += tot >> 16;
-    run_eq += tot & 0xFFFFu;
-#pragma unroll
-    for (int j = 0; j < kScanPer; ++j) key[j] = key_next[j];
+    return;
   }
+  scan_keep(keys_lds, scores, P, base, end, base, tau, need, 0u, 0u, q, seg, keep, perm, wsum);
+}
+
+// Large experts (more than kSelLdsKeys pairs), after select_scan_kernel has
+// found their tau and need: chunk b (the kHistChunk pairs of select_hist_kernel's
+// chunk b) counts its keys above and equal to tau ...
+__global__ __launch_bounds__(kSelThreads) void select_chunk_count_kernel(
+    ExpertTable tab, const float* __restrict__ scores, const uint32_t* __restrict__ tau_need,
+    uint32_t* __restrict__ counts) {
+  __shared__ uint32_t wsum[kSelWaves];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  int e = 0;
+  while (e + 1 < tab.E && tab.hist_off[e + 1] <= b) ++e;
+  const int lo = tab.pair_off[e] + (b - tab.hist_off[e]) * kHistChunk;
+  const int hi = min(lo + kHistChunk, tab.pair_off[e + 1]);
+  const uint32_t tau = tau_need[2 * e];
+  uint32_t ngt = 0, neq = 0;
+  for (int i = lo + tid; i < hi; i += kSelThreads) {
+    const uint32_t k = score_key(scores[i]);
+    ngt += k > tau ? 1u : 0u;
+    neq += k == tau ? 1u : 0u;
+  }
+  uint32_t tot;
+  block_scan((ngt << 16) | neq, wsum, tot);   // chunk < 2^16 pairs
+  if (tid == 0) {
+    counts[2 * b] = tot >> 16;
+    counts[2 * b + 1] = tot & 0xFFFFu;
+  }
+}
+
+// ... and then scans its pairs, starting from the counts of the expert's
+// earlier chunks: keep flags and compacted rows of many chunks at once.
+__global__ __launch_bounds__(kSelThreads) void select_chunk_scan_kernel(
+    ExpertTable tab, const float* __restrict__ scores, uint8_t* __restrict__ keep,
+    int32_t* __restrict__ perm, const uint32_t* __restrict__ tau_need,
+    const uint32_t* __restrict__ counts) {
+  __shared__ uint32_t wsum[kSelWaves];
+  const int b = blockIdx.x;
+  int e = 0;
+  while (e + 1 < tab.E && tab.hist_off[e + 1] <= b) ++e;
+  const int lo = tab.pair_off[e] + (b - tab.hist_off[e]) * kHistChunk;
+  const int hi = min(lo + kHistChunk, tab.pair_off[e + 1]);
+  uint32_t run_gt = 0, run_eq = 0;
+  for (int c = tab.hist_off[e]; c < b; ++c) {
+    run_gt += counts[2 * c];
+    run_eq += counts[2 * c + 1];
+  }
+  const int seg = tab.seg_off[e];
+  const uint32_t q = (uint32_t)(tab.seg_off[e + 1] - seg);
+  scan_keep(nullptr, scores, tab.pair_off[tab.E], lo, hi, 0, tau_need[2 * e],
+            tau_need[2 * e + 1], run_gt, run_eq, q, seg, keep, perm, wsum);
 }
 
 }  // namespace
@@ -466,6 +537,9 @@ hipError_t launch_select_scan(const ExpertTable& tab, const float* scores, uint8
                               int32_t* perm, int32_t* seg_offsets_out, uint32_t* hist,
                               hipStream_t s) {
   const int chunks = tab.hist_off[tab.E];
+  // workspace: chunk histograms, then tau / need per expert, then per-chunk counts
+  uint32_t* tau_need = hist + (size_t)chunks * kBins;
+  uint32_t* counts = tau_need + 2 * kMaxE;
   if (chunks > 0) {
     hipLaunchKernelGGL(select_hist_kernel, dim3(chunks), dim3(kSelThreads), 0, s, tab, scores,
                        hist);
@@ -473,7 +547,15 @@ hipError_t launch_select_scan(const ExpertTable& tab, const float* scores, uint8
     if (err != hipSuccess) return err;
   }
   hipLaunchKernelGGL(select_scan_kernel, dim3(tab.E), dim3(kSelThreads), 0, s, tab, scores,
-                     keep, perm, seg_offsets_out, hist);
+                     keep, perm, seg_offsets_out, hist, tau_need);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || chunks == 0) return err;
+  hipLaunchKernelGGL(select_chunk_count_kernel, dim3(chunks), dim3(kSelThreads), 0, s, tab,
+                     scores, tau_need, counts);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(select_chunk_scan_kernel, dim3(chunks), dim3(kSelThreads), 0, s, tab,
+                     scores, keep, perm, tau_need, counts);
   return hipGetLastError();
 }
 

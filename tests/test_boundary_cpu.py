@@ -152,10 +152,14 @@ def test_workspace_size_and_check():
 def test_select_workspace_for_large_experts():
     """An expert with more than 24576 pairs gets its first radix digit counted
     by one workgroup per 16384-pair chunk, into 16 KiB histograms in the
-    workspace: the selection calls then need that much workspace."""
+    workspace, and its scan split over the same chunks (tau / need per
+    expert, counts per chunk): the selection calls then need that much
+    workspace."""
     counts, quotas = (60000, 24576, 100), (48000, 19660, 80)
     p = plan(counts=counts, quotas=quotas, d_out=8, d_in=8)
-    hist = ((60000 + 16383) // 16384) * 4096 * 4   # only the first expert is large
+    chunks = (60000 + 16383) // 16384   # only the first expert is large
+    # chunk histograms, tau / need per expert (256 experts max), chunk counts
+    hist = (chunks * 4096 + 2 * 256 + 2 * chunks) * 4
     n = p.workspace_bytes()
     assert n >= hist
     assert sscc(p, ws=FAKE, ws_bytes=hist - 1) == 6
