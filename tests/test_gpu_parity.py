@@ -406,3 +406,44 @@ def test_whole_path_in_a_hip_graph():
         # eager work between replays, on the same buffers' inputs
         lrmoe.pruned_backward(plan, t["alpha"], t["g"], t["phi"], t["W"], ws=ws)
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gather_backward_token_rows(dtype):
+    """lrmoe_gather_backward with the second projection's input gathered
+    through a row index (x is one row per token, g2 one row per pair), in both
+    storage types: bit for bit the separate gather + grouped-backward calls,
+    which the oracle checks."""
+    p = W.make_token_problem(T=700, E=6, topk=2, d_out=48, d_in=40, dtype=dtype, seed=371,
+                             policy=("ratio", 3, 4))
+    q = lrmoe.plan_quota(p.counts, p.policy)
+    plan, out, t = U.run_gpu(p, q)
+    rng = np.random.default_rng(371)
+    d2o, d2i = 96, 56
+    mk = (lambda a: W.to_bf16_bits(a)) if dtype == "bf16" else (lambda a: a.astype(np.float32))
+    g2 = mk(rng.standard_normal((p.P, d2o)).astype(np.float32))
+    x = mk(rng.standard_normal((p.T, d2i)).astype(np.float32))
+    W2 = mk((0.02 * rng.standard_normal((p.E, d2o, d2i))).astype(np.float32))
+    plan2 = lrmoe.Plan(p.counts, q, d2o, d2i, U.dtype_code(p), T=p.P)
+    rows = t["row"]
+    c2 = lrmoe.gather_compact(plan2, out["perm"], out["keep"], t["alpha"], U.dev(g2), U.dev(x),
+                              phi_row_index=rows)
+    dW2 = lrmoe.grouped_backward(plan2, out["perm"], c2["alpha_c"], c2["g_c"], c2["phi_c"],
+                                 U.dev(W2), dphi=c2["dphi"])
+    one = lrmoe.gather_backward(plan2, out["perm"], out["keep"], t["alpha"], U.dev(g2), U.dev(x),
+                                U.dev(W2), phi_row_index=rows)
+    torch.cuda.synchronize()
+    assert torch.equal(one["dW"], dW2) and torch.equal(one["dphi"], c2["dphi"])
+    for k in ("g_c", "phi_c", "alpha_c"):
+        a, b = one[k], c2[k]
+        if a.dtype == torch.bfloat16:
+            a, b = a.view(torch.int16), b.view(torch.int16)
+        assert torch.equal(a, b), k
+    # and the oracle: x rows of the kept pairs' tokens, the second projection's dW and dx
+    perm = out["perm"].cpu().numpy()
+    seg = out["seg_offsets"].cpu().numpy()
+    xr = x[p.row_index.astype(np.int64)]          # x per pair
+    ref_dW = O.weight_grad(seg, p.alpha[perm], g2[perm], xr[perm], dtype, p.E, d2o, d2i)
+    ref_dx = O.input_grad(seg, perm, p.alpha[perm], g2[perm], W2, dtype, p.P)
+    assert U.rel_err(one["dW"].cpu().numpy(), ref_dW) <= U.TOL
+    assert U.rel_err(one["dphi"].cpu().numpy(), ref_dx) <= U.TOL
