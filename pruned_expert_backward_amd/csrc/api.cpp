@@ -196,8 +196,6 @@ lrmoe_status mark(const lrmoe_timing* t, bool after, int slot, hipStream_t s) {
   return hip_status(hipEventRecord(reinterpret_cast<hipEvent_t>(ev), s));
 }
 
-int64_t elem_bytes(const lrmoe_problem* pb) { return pb->dtype == LRMOE_BF16 ? 2 : 4; }
-
 // Shared body of the two select entry points.
 lrmoe_status select_compact(const lrmoe_problem* pb, bool compute_scores, const float* scores_in,
                             const int32_t* g_row_index, const float* alpha, const void* g,

@@ -81,7 +81,6 @@ constexpr int BM = kTile, BN = kTile, BK = 32;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kPlaneBytes = kTile * BK * 2;   // one bf16 operand plane of one K step (16 KB)
-constexpr int kChunksPerPlane = kTile * BK / 8 / kThreads;   // 16-byte chunks per thread
 
 // ------------------------------------------------------------ LDS layouts
 // KC: row r (0..255) holds K 0..31 as 4 chunks of 16 B; chunk c of row r
@@ -95,31 +94,15 @@ __device__ __forceinline__ int kc_off(int r, int c) { return r * 64 + ((c ^ kc_s
 // MC: row k (0..31) holds M/N 0..255 as 32 chunks of 16 B.
 __device__ __forceinline__ int mc_off(int k, int c) { return k * 512 + ((c ^ ((k & 3) << 2)) << 4); }
 
-// Fragment: 8 bf16 along K for MN index (mb + lane%32), K = kb + 8*(lane/32) + 0..7.
-__device__ __forceinline__ i16x8 frag_kc(LDS_AS const char* t, int mb, int kb, int lane) {
-  const int r = mb + (lane & 31);
-  const int c = (kb >> 3) + (lane >> 5);
-  return *reinterpret_cast<LDS_AS const i16x8*>(t + kc_off(r, c));
-}
-
-// ds_read_b64_tr_b16: within each 16-lane group, source lane s reads 4 bf16
-// of row k0 + s/4 at columns n + 4*(s%4); lane l then holds column n + l%16
-// for rows k0 .. k0+3.
-__device__ __forceinline__ i16x8 frag_mc(LDS_AS const char* t, int mb, int kb, int lane) {
-  const int G = lane >> 4, s = lane & 15;
-  const int c = (mb >> 3) + 2 * (G & 1) + ((s & 3) >> 1);
-  const int half = (s & 1) * 8;
-  const int k0 = kb + 8 * (G >> 1) + (s >> 2);
-  LDS_AS char* base = const_cast<LDS_AS char*>(t);
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      reinterpret_cast<LDS_AS i16x4*>(base + mc_off(k0, c) + half));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      reinterpret_cast<LDS_AS i16x4*>(base + mc_off(k0 + 4, c) + half));
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// The same fragments read at a precomputed LDS byte address (see the tile's
-// la / lb): MC = two transposing reads 4 rows apart, KC = one 16-byte read.
+// Fragments (8 bf16 per lane), read at precomputed LDS byte addresses (the
+// tile's la / lb).
+//   KC: lane l holds MN index mb + l%32 and K = kb + 8*(l/32) + 0..7: one
+//       16-byte read at kc_off(mb + l%32, kb/8 + l/32).
+//   MC: ds_read_b64_tr_b16 -- within each 16-lane group G = l/16, source lane
+//       s = l%16 reads 4 bf16 of row k0 = kb + 8*(G/2) + s/4 at chunk
+//       mb/8 + 2*(G%2) + (s%4)/2, half (s%2)*8 bytes; after the transpose lane
+//       l holds one MN column for rows k0 .. k0 + 3.  Two such reads 4 rows
+//       (2 KiB) apart give the 8 K values.
 __device__ __forceinline__ i16x8 frag_mc_at(uint32_t addr) {
   LDS_AS char* p = (LDS_AS char*)(uintptr_t)addr;
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<LDS_AS i16x4*>(p));
@@ -129,12 +112,6 @@ __device__ __forceinline__ i16x8 frag_mc_at(uint32_t addr) {
 }
 __device__ __forceinline__ i16x8 frag_kc_at(uint32_t addr) {
   return *reinterpret_cast<LDS_AS const i16x8*>((LDS_AS char*)(uintptr_t)addr);
-}
-
-template <bool MC>
-__device__ __forceinline__ i16x8 frag(LDS_AS const char* t, int mb, int kb, int lane) {
-  if constexpr (MC) return frag_mc(t, mb, kb, lane);
-  else return frag_kc(t, mb, kb, lane);
 }
 
 __device__ __forceinline__ f32x16 mfma(i16x8 a, i16x8 b, f32x16 c) {
@@ -222,10 +199,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint16_t* base, int
   const int n = bytes <= 0 ? 0 : (int)(bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, n,
                                            (int)kBufferFlags);
-}
-
-__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
 }
 
 // global -> LDS copy of 16 bytes per lane: lane i writes LDS bytes
@@ -357,7 +330,7 @@ struct Tile {
         aoff[j] = (uint32_t)(r * d_out + 8 * lc) * 2u;
       }
     }
-    // Fragment addresses (see frag_mc / frag_kc for the lane layouts).
+    // Fragment addresses (lane layouts: see the fragment reads above).
     const uint32_t base = lds_addr(smem);
     {
       const int G = lane >> 4, s = lane & 15;
