@@ -78,8 +78,18 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = kTile, BN = kTile, BK = 32;
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
+// Wave grid of a tile.  2 x 2 waves of 128 x 128 (one wave per SIMD, 256
+// accumulators each).  2 x 4 waves of 128 x 64 (two waves per SIMD) were
+// measured as well: correct, and no faster (the second wave hides no more
+// than the extra fragment reads cost).
+constexpr int kWavesM = 2;                 // wave rows of a tile
+constexpr int kWavesN = 2;                 // wave columns
+constexpr int kWaves = kWavesM * kWavesN;
+constexpr int kThreads = 64 * kWaves;
+constexpr int WTM = BM / kWavesM;          // rows of one wave's block
+constexpr int WTN = BN / kWavesN;          // columns of one wave's block
+constexpr int kMB = WTM / 32;              // 32x32 accumulator blocks per wave: kMB x kNB
+constexpr int kNB = WTN / 32;
 constexpr int kPlaneBytes = kTile * BK * 2;   // one bf16 operand plane of one K step (16 KB)
 
 // ------------------------------------------------------------ LDS layouts
@@ -260,13 +270,13 @@ struct Tile {
   static constexpr int kPerWave = kBlocks / kWaves;      // ... filled by each wave
   static constexpr int kLoads = (PA + PB) * kPerWave;    // load instructions per stage per wave
   static constexpr int kTerms = 1 + (PA == 2) + (PB == 2);
-  static constexpr int kHalfMfmas = 16 * kTerms;         // per wave per half step
-  static constexpr int kFrags = (PA + PB) * 4;           // fragments per half step
+  static constexpr int kHalfMfmas = kMB * kNB * kTerms; // per wave per half step
+  static constexpr int kFrags = PA * kMB + PB * kNB;     // fragments per half step
   static_assert(kFrags <= kHalfMfmas && kLoads <= kHalfMfmas, "interleave slots");
 
   struct Frags {
-    i16x8 a[PA][4];
-    i16x8 b[PB][4];
+    i16x8 a[PA][kMB];
+    i16x8 b[PB][kNB];
   };
 
   int e, m0, n0, chunk, chunks, q, seg, K, mrows, nk;
@@ -278,7 +288,7 @@ struct Tile {
   // LDS byte addresses of this lane's fragment reads in stage 0, plane 0:
   // MC operands: one per 32-wide fragment (half 0; half 1 is +8 KiB);
   // KC operand: one per half (fragment a is +2 KiB * a).
-  uint32_t la[4], lb[4];
+  uint32_t la[kMB], lb[kNB];
   LDS_AS char* sink;   // kWaves x 1 KiB of LDS that only dead loads write
 
   __device__ __forceinline__ Tile(const Args& args, const GemmTable& tab, const TileJob& job,
@@ -286,8 +296,8 @@ struct Tile {
     const int tid = threadIdx.x;
     lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    wm = wave >> 1;   // wave tile rows wm*128, cols wn*128
-    wn = wave & 1;
+    wm = wave / kWavesN;   // wave block rows wm*WTM, columns wn*WTN
+    wn = wave % kWavesN;
     // Tile coordinates are workgroup-uniform; say so, so that buffer
     // descriptors and LDS bases stay in scalar registers.
     e = __builtin_amdgcn_readfirstlane(job.e);
@@ -338,16 +348,20 @@ struct Tile {
       const int cl = 2 * (G & 1) + ((s & 3) >> 1);
       const int half = (s & 1) * 8;
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        lb[f] = base + (uint32_t)(mc_off(k0, (wn * 128 + f * 32) / 8 + cl) + half);
-        if (A_MC) la[f] = base + (uint32_t)(mc_off(k0, (wm * 128 + f * 32) / 8 + cl) + half);
+      for (int f = 0; f < kNB; ++f)
+        lb[f] = base + (uint32_t)(mc_off(k0, (wn * WTN + f * 32) / 8 + cl) + half);
+      if (A_MC) {
+#pragma unroll
+        for (int f = 0; f < kMB; ++f)
+          la[f] = base + (uint32_t)(mc_off(k0, (wm * WTM + f * 32) / 8 + cl) + half);
       }
     }
     if (!A_MC) {
-      const int r = wm * 128 + (lane & 31);
+      const int r = wm * WTM + (lane & 31);
 #pragma unroll
       for (int h = 0; h < 2; ++h) la[h] = base + (uint32_t)kc_off(r, 2 * h + (lane >> 5));
-      la[2] = la[3] = 0;
+#pragma unroll
+      for (int h = 2; h < kMB; ++h) la[h] = 0;
     }
   }
 
@@ -391,13 +405,13 @@ struct Tile {
   // ---- fragment i (0 .. kFrags-1) of half h of stage s: A fragments first.
   __device__ __forceinline__ void read_frag(int s, int h, Frags& f, int i) const {
     const uint32_t so = (uint32_t)(s * kStage);
-    if (i < PA * 4) {
-      const int p = i / 4, a = i % 4;
+    if (i < PA * kMB) {
+      const int p = i / kMB, a = i % kMB;
       const uint32_t po = so + (uint32_t)(p * kPlaneBytes);
       if (A_MC) f.a[p][a] = frag_mc_at(la[a] + po + (uint32_t)(h * 8192));
       else f.a[p][a] = frag_kc_at(la[h] + po + (uint32_t)(a * 2048));
     } else {
-      const int p = (i - PA * 4) / 4, b = (i - PA * 4) % 4;
+      const int p = (i - PA * kMB) / kNB, b = (i - PA * kMB) % kNB;
       f.b[p][b] = frag_mc_at(lb[b] + so + (uint32_t)((PA + p) * kPlaneBytes + h * 8192));
     }
   }
@@ -407,8 +421,8 @@ struct Tile {
   // accumulator holds the block transposed: lane = tile row (M), registers =
   // columns (N), four consecutive columns per register quad.  That lets the
   // epilogue write 16 bytes per lane.
-  __device__ __forceinline__ static void mfma_i(const Frags& f, f32x16 (&acc)[4][4], int i) {
-    const int t = i / 16, a = (i % 16) / 4, b = i % 4;
+  __device__ __forceinline__ static void mfma_i(const Frags& f, f32x16 (&acc)[kMB][kNB], int i) {
+    const int t = i / (kMB * kNB), a = (i % (kMB * kNB)) / kNB, b = i % kNB;
     const int pa = (t == 2 || (t == 1 && PB == 1)) ? PA - 1 : 0;
     const int pb = (t == 1 && PB == 2) ? 1 : 0;
     acc[a][b] = mfma(f.b[pb][b], f.a[pa][a], acc[a][b]);
@@ -437,7 +451,7 @@ struct Tile {
   }
 
   __device__ __forceinline__ void step(const Args& args, LDS_AS char* smem, int kt, Frags& f0,
-                                       Frags& f1, f32x16 (&acc)[4][4]) const {
+                                       Frags& f1, f32x16 (&acc)[kMB][kNB]) const {
     const int S = kt % NS, SN = S + 1 == NS ? 0 : S + 1, SP = S == 0 ? NS - 1 : S - 1;
     // phase 1: second half of stage kt + NS - 1 (buffer SP); the prologue
     // already issued it when kt == 0
@@ -476,11 +490,11 @@ struct Tile {
   // every load of the tile consumed; LDS reads of the last stage may still be
   // in flight (the caller's barrier covers them).
   __device__ __forceinline__ void mainloop(const Args& args, LDS_AS char* smem,
-                                           f32x16 (&acc)[4][4]) const {
+                                           f32x16 (&acc)[kMB][kNB]) const {
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < kMB; ++a)
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < kNB; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
     if (nk == 0) return;
@@ -522,12 +536,12 @@ struct Tile {
   // a row (u < 0) or past the matrix edge (column counts are multiples of 8)
   // load column 0 of row 0 instead.
   struct GluRow {
-    u32x4 a[4][2], b[4][2];   // [block b][group pair h]
+    u32x4 a[kNB][2], b[kNB][2];   // [block b][group pair h]
   };
 
   // First column of the 8-column group this lane moves for pair (b, h).
   __device__ __forceinline__ int glu_col(int ln, int b, int h) const {
-    return wn * 128 + b * 32 + 16 * h + 8 * (ln >> 5);
+    return wn * WTN + b * 32 + 16 * h + 8 * (ln >> 5);
   }
 
   __device__ __forceinline__ void glu_load(const Args& args, int32_t u, int ln, int ncols,
@@ -538,7 +552,7 @@ struct Tile {
     const uint16_t* arow = args.ops.glu_a + src;
     const uint16_t* brow = args.ops.glu_b + src;
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < kNB; ++b)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int col = glu_col(ln, b, h);
@@ -574,14 +588,14 @@ struct Tile {
   }
 
   __device__ __forceinline__ void glu_store(const Args& args, int32_t u, int64_t j, int ln,
-                                            int ncols, const f32x16 (&acc)[4][4], int a,
+                                            int ncols, const f32x16 (&acc)[kMB][kNB], int a,
                                             const GluRow& r) const {
     const int d_in = args.d_in;
     uint16_t* gate = args.ops.glu_out + j * (2 * (int64_t)d_in) + n0;
     uint16_t* up = gate + d_in;
     const bool hi = ln >= 32;
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < kNB; ++b)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         // this lane's quads of groups g0 and g1: its own half of the 16 bytes
@@ -626,7 +640,7 @@ struct Tile {
   }
 
   __device__ __forceinline__ void glu_epilogue(const Args& args, LDS_AS const char* prm,
-                                               const f32x16 (&acc)[4][4]) const {
+                                               const f32x16 (&acc)[kMB][kNB]) const {
     LDS_AS const int32_t* s_perm = reinterpret_cast<LDS_AS const int32_t*>(prm);
     // Opaque copies: keep the compiler from computing the column offsets and
     // edge predicates of every quad ahead of the main loop, where they would
@@ -635,18 +649,18 @@ struct Tile {
     asm volatile("" : "+v"(ln));
     int ncols = args.d_in - n0;
     asm volatile("" : "+s"(ncols));
-    int32_t u[4];
+    int32_t u[kMB];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) u[a] = s_perm[wm * 128 + a * 32 + (ln & 31)];
+    for (int a = 0; a < kMB; ++a) u[a] = s_perm[wm * WTM + a * 32 + (ln & 31)];
     GluRow r[2];
     glu_load(args, u[0], ln, ncols, r[0]);
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      if (a < 3) glu_load(args, u[a + 1], ln, ncols, r[(a + 1) & 1]);
+    for (int a = 0; a < kMB; ++a) {
+      if (a + 1 < kMB) glu_load(args, u[a + 1], ln, ncols, r[(a + 1) & 1]);
       // at most two rows of loads live (128 VGPRs): the accumulators hold
       // every AGPR, so nothing more may be hoisted
       __builtin_amdgcn_sched_barrier(0);
-      glu_store(args, u[a], seg + m0 + wm * 128 + a * 32 + (ln & 31), ln, ncols, acc, a,
+      glu_store(args, u[a], seg + m0 + wm * WTM + a * 32 + (ln & 31), ln, ncols, acc, a,
                 r[a & 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -659,7 +673,7 @@ struct Tile {
   // so a quad never straddles the matrix edge.
   __device__ __forceinline__ void epilogue(const Args& args, const GemmTable& tab,
                                            LDS_AS const char* prm,
-                                           const f32x16 (&acc)[4][4]) const {
+                                           const f32x16 (&acc)[kMB][kNB]) const {
     const int d_out = args.d_out, d_in = args.d_in;
     LDS_AS const int32_t* s_perm = reinterpret_cast<LDS_AS const int32_t*>(prm);
     LDS_AS const float* s_alpha = reinterpret_cast<LDS_AS const float*>(prm + BM * 4);
@@ -675,8 +689,8 @@ struct Tile {
     }
     const int cq = 4 * (lane >> 5);   // this lane's column offset inside each group of 8
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int lrow = wm * 128 + a * 32 + (lane & 31);
+    for (int a = 0; a < kMB; ++a) {
+      const int lrow = wm * WTM + a * 32 + (lane & 31);
       const int mrow = m0 + lrow;
       // destination of tile column 0 of this row, and how many columns exist
       float* orow = nullptr;
@@ -696,10 +710,10 @@ struct Tile {
       }
       if (orow == nullptr) continue;
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < kNB; ++b)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int col = wn * 128 + b * 32 + 8 * g + cq;
+          const int col = wn * WTN + b * 32 + 8 * g + cq;
           f32x4 v = {acc[a][b][4 * g], acc[a][b][4 * g + 1], acc[a][b][4 * g + 2],
                      acc[a][b][4 * g + 3]};
           if (!IS_DW) v *= scale;
@@ -765,7 +779,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_backward_kernel(Args args
     return -1;
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[kMB][kNB];
   bool cur_dw;
   TileJob cur;
   if (fetch(cur_dw, cur) < 0) return;
