@@ -68,6 +68,29 @@ def check_keep(ref_scores, counts, quotas, keep_gpu, keep_ref, taus):
     return bool((keep_gpu == keep_ref).all())
 
 
+def abs_rows(x):
+    """|x| of stored rows: clears the sign bit of bf16 bit patterns."""
+    return x & np.uint16(0x7FFF) if x.dtype == np.uint16 else np.abs(x)
+
+
+def single_rounding_bound(sum_abs, k_max):
+    """Per-element error bound of the single-rounding dW mode.  Each term
+    alpha_j g_j[o] phi_j[i] uses bf16(alpha_j phi_j[i]) (or bf16(alpha_j
+    g_j[o])): one round to nearest with 8 significant bits, relative error at
+    most 2^-8, on top of the float32 product (2^-24).  The fp32 sum of up to
+    k_max terms (MFMA accumulation and the split-K partial sums) adds at most
+    k_max * 2^-24 relative per term; doubled here for slack.  sum_abs is
+    sum_j |alpha_j g_j[o] phi_j[i]|, computed by the oracle on |inputs|."""
+    return (2.0 ** -8 + 2.0 ** -24 + 2 * k_max * 2.0 ** -24) * sum_abs + 1e-30
+
+
+def check_single_rounding(got, ref, sum_abs, k_max, what):
+    bound = single_rounding_bound(sum_abs, k_max)
+    excess = np.abs(got.astype(np.float64) - ref) / bound
+    assert excess.max() <= 1.0, f"{what}: error {excess.max():.3f} x the single-rounding bound"
+    return float(excess.max())
+
+
 def rel_err(got, ref):
     m = np.abs(ref).max()
     if m == 0:
@@ -96,10 +119,19 @@ def compare_full(p, quotas, out, dw_mode=lrmoe.DW_EXACT, scores_in=None, score_m
         assert np.all(np.abs(s - R) <= 1e-5 * np.maximum(R, 1e-30))
     dW_ref = O.weight_grad(seg, a_c, g_c, phi_c, p.dtype, p.E, p.d_out, p.d_in)
     dphi_ref = O.input_grad(seg, perm, a_c, g_c, p.W, p.dtype, p.P)
-    errs = dict(dW=rel_err(out["dW"].cpu().numpy(), dW_ref),
-                dphi=rel_err(out["dphi"].cpu().numpy(), dphi_ref))
-    for k, v in errs.items():
-        assert v <= TOL, f"{k}: max err / max|ref| = {v:.3e}"
+    dW_gpu = out["dW"].cpu().numpy()
+    errs = dict(dW=rel_err(dW_gpu, dW_ref), dphi=rel_err(out["dphi"].cpu().numpy(), dphi_ref))
+    assert errs["dphi"] <= TOL, f"dphi: max err / max|ref| = {errs['dphi']:.3e}"
+    if dw_mode == lrmoe.DW_BF16 and p.dtype == "bf16":
+        # single rounding of alpha * x to bf16: not within TOL in general (few
+        # rows per expert leave the 2^-8 rounding unaveraged), but within its
+        # per-element bound
+        s_abs = O.weight_grad(seg, np.abs(a_c), abs_rows(g_c), abs_rows(phi_c), p.dtype, p.E,
+                              p.d_out, p.d_in)
+        k_max = int(np.max(np.diff(seg))) if len(seg) > 1 else 0
+        errs["dW_bound_use"] = check_single_rounding(dW_gpu, dW_ref, s_abs, k_max, "dW")
+    else:
+        assert errs["dW"] <= TOL, f"dW: max err / max|ref| = {errs['dW']:.3e}"
     dphi_gpu = out["dphi"].cpu().numpy()
     assert np.all(dphi_gpu[~keep_used] == 0)
     return errs, same

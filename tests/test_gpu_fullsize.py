@@ -66,13 +66,23 @@ def check_fullsize(p, dw_mode=lrmoe.DW_EXACT, gate_up=False, seed=0):
     o_idx = np.unique(np.concatenate([[0, p.d_out - 1], rng.integers(0, p.d_out, 40)]))
     i_idx = np.unique(np.concatenate([[0, p.d_in - 1], rng.integers(0, p.d_in, 40)]))
     dW = out["dW"]
-    got, ref = [], []
+    single = dw_mode == lrmoe.DW_BF16 and p.dtype == "bf16"
+    got, ref, s_abs = [], [], []
+    if single:
+        a_abs, g_abs, phi_abs = np.abs(p.alpha), U.abs_rows(p.g), U.abs_rows(p.phi)
     for e in range(p.E):
         ref.append(O.weight_grad_block(seg, perm, None, p.alpha, p.g, p.phi, p.dtype, e,
                                        o_idx, i_idx))
+        if single:
+            s_abs.append(O.weight_grad_block(seg, perm, None, a_abs, g_abs, phi_abs, p.dtype, e,
+                                             o_idx, i_idx))
         got.append(dW[e][torch.as_tensor(o_idx, device=dW.device)][
             :, torch.as_tensor(i_idx, device=dW.device)].cpu().numpy())
     dw_err = U.rel_err(np.stack(got), np.stack(ref))
+    if single:
+        U.check_single_rounding(np.stack(got), np.stack(ref), np.stack(s_abs),
+                                int(np.max(np.diff(seg))), "dW")
+        del a_abs, g_abs, phi_abs
     # dphi: kept and dropped rows, including the first and last pair
     kept = np.nonzero(keep_used)[0]
     dropped = np.nonzero(~keep_used)[0]
@@ -86,7 +96,8 @@ def check_fullsize(p, dw_mode=lrmoe.DW_EXACT, gate_up=False, seed=0):
     assert np.all(got_rows[~keep_used[pairs]] == 0)
     print(f"{p.name}: M={sum(q)} keep identical={same} score rel err={score_err:.2e} "
           f"dW err={dw_err:.3e} dphi err={dphi_err:.3e}", flush=True)
-    assert dw_err <= U.TOL and dphi_err <= U.TOL
+    assert dphi_err <= U.TOL
+    assert single or dw_err <= U.TOL
     res = dict(out=out, t=t, q=q, perm=perm, keep=keep_used, plan=plan)
     return res
 
@@ -98,8 +109,9 @@ def test_fullsize_down_projection(c):
 
 @pytest.mark.parametrize("c", [1, 3])
 def test_fullsize_down_projection_single_rounding(c):
-    """The single-rounding dW mode (alpha * phi rounded once to bf16) meets the
-    same tolerance at full size."""
+    """The single-rounding dW mode (alpha * phi rounded once to bf16): dW
+    within that rounding's per-element bound (at these sizes also within
+    2e-3 of max |ref|, by about 1 %, which the mode does not promise)."""
     check_fullsize(W.config(c), dw_mode=lrmoe.DW_BF16, seed=10 + c)
 
 
