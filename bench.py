@@ -148,9 +148,17 @@ def cpu_baseline(p, budget_s: float = 12.0, chain: bool = False):
         el = time.perf_counter() - t0
         if el >= budget_s or runs >= 200:
             break
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                         None)
+    except OSError:  # pragma: no cover
+        pass
     return dict(value=M * runs / el, unit="kept pairs/s", cores=int(threads), kind="oracle",
                 sample=f"{runs} full pass(es) of the same workload ({p.name}, P={p.P}, M={M}), "
-                       f"{el:.1f} s, numpy float64")
+                       f"{el:.1f} s, numpy float64",
+                host_cpus=os.cpu_count(), cpu_model=model)
 
 
 def main():
