@@ -34,7 +34,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, TFLOP/s
 GEMM_SOURCES = ("pruned_expert_backward_amd/csrc/grouped_gemm.hip",
                 "pruned_expert_backward_amd/csrc/lrmoe_internal.h",
                 "pruned_expert_backward_amd/csrc/api.cpp")
-COUNTERS_FILE = "profiles/grouped_backward_kernel.qwen3-down-c20.counters.txt"
+COUNTERS_GLOB = "profiles/grouped_backward_kernel.*.counters.txt"
 COPY_BYTES = 1 << 30           # plain copy used to calibrate FETCH_SIZE / WRITE_SIZE
 
 
@@ -73,30 +73,33 @@ def gemm_sources_sha256() -> str:
 
 
 def read_counters(workload: str, dw_mode: str):
-    """HBM bytes per launch of the grouped GEMM from the committed rocprofv3
+    """HBM bytes per launch of the grouped GEMM from a committed rocprofv3
     counter summary: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
-    scaled by bytes / counter of a plain copy of known size.  None when the
-    summary is missing, was taken on another workload, or the kernel sources
+    scaled by bytes / counter of a plain copy of known size.  None when no
+    summary was taken on this workload and dW mode, or the kernel sources
     changed since."""
-    path = os.path.join(ROOT, COUNTERS_FILE)
-    if not os.path.exists(path):
-        return None
-    kv = {}
-    with open(path) as f:
-        for line in f:
-            line = line.strip()
-            if line and not line.startswith("#") and "=" in line:
-                k, v = line.split("=", 1)
-                kv[k.strip()] = v.strip()
-    try:
-        if (kv["workload"] != workload or kv["dw_mode"] != dw_mode
-                or kv["kernel_sources_sha256"] != gemm_sources_sha256()):
-            return None
-        fetch = float(kv["gemm_fetch_kib"]) * float(kv["copy_bytes"]) / float(kv["copy_fetch_kib"])
-        write = float(kv["gemm_write_kib"]) * float(kv["copy_bytes"]) / float(kv["copy_write_kib"])
-    except (KeyError, ValueError, ZeroDivisionError):
-        return None
-    return fetch + write
+    import glob
+    sha = gemm_sources_sha256()
+    for path in sorted(glob.glob(os.path.join(ROOT, COUNTERS_GLOB))):
+        kv = {}
+        with open(path) as f:
+            for line in f:
+                line = line.strip()
+                if line and not line.startswith("#") and "=" in line:
+                    k, v = line.split("=", 1)
+                    kv[k.strip()] = v.strip()
+        try:
+            if (kv["workload"] != workload or kv["dw_mode"] != dw_mode
+                    or kv["kernel_sources_sha256"] != sha):
+                continue
+            fetch = (float(kv["gemm_fetch_kib"]) * float(kv["copy_bytes"])
+                     / float(kv["copy_fetch_kib"]))
+            write = (float(kv["gemm_write_kib"]) * float(kv["copy_bytes"])
+                     / float(kv["copy_write_kib"]))
+        except (KeyError, ValueError, ZeroDivisionError):
+            continue
+        return fetch + write
+    return None
 
 
 def copy_calibration(reps: int = 10):
