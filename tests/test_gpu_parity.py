@@ -250,9 +250,127 @@ def test_glu_chain(idx):
                 dW2=U.rel_err(out["dW2"].cpu().numpy(), ref["dW2"]),
                 dx=U.rel_err(out["dx"].cpu().numpy(), ref["dx"]))
     print(name, errs)
+    if dw_mode == lrmoe.DW_BF16:   # one bf16 rounding of alpha * x per term: its bound
+        _check_chain_single_rounding(p, ref, out)
+        errs = dict(dx=errs["dx"])
     for k, v in errs.items():
         assert v <= U.TOL, (k, v)
     assert np.all(out["dx"].cpu().numpy()[~ref["keep"]] == 0)
+
+
+def _check_chain_single_rounding(p, ref, out):
+    """dW and dW2 of the single-rounding mode against its per-element bound:
+    the oracle's sums of |alpha g phi| and |alpha dgu x|.  For dW2 each term
+    may also differ by one bf16 ulp of dgu (2^-7 relative), where the two
+    sides round dgu from float32 and float64 to different neighbours: three
+    times the 2^-8 rounding term covers both."""
+    perm, seg = ref["perm"], ref["seg"]
+    g_c, phi_c, a_c = O.gather(perm, p.row_index, p.g, p.phi, p.alpha)
+    a = np.abs(a_c)
+    k_max = int(np.max(np.diff(seg)))
+    s1 = O.weight_grad(seg, a, U.abs_rows(g_c), U.abs_rows(phi_c), "bf16", p.E, p.d_out,
+                       p.d_in)
+    U.check_single_rounding(out["dW"].cpu().numpy(), ref["dW"], s1, k_max, "dW")
+    gu = p.gate_up
+    s2 = 3.0 * O.weight_grad(seg, a, np.abs(ref["dgu_c"]) * (1 + 2.0 ** -8),
+                             O.to_f64(U.abs_rows(gu.x[perm]), "bf16"), "f64", p.E, gu.d_out,
+                             gu.d_in)
+    U.check_single_rounding(out["dW2"].cpu().numpy(), ref["dW2"], s2, k_max, "dW2")
+
+
+def _random_chain_problem(seed):
+    """Seeded random MLP-chain shape: P from 1 to 4000, 1 to 10 experts,
+    the expert's hidden width d_in (gate and up each), the model width
+    d_out, both any multiple of 8 up to 520."""
+    rng = np.random.default_rng(7000 + seed)
+    E = int(rng.integers(1, 11))
+    P = int(rng.integers(1, 64)) if seed % 3 == 1 else int(rng.integers(64, 4001))
+    d_out = 8 * int(rng.integers(1, 66))
+    d_in = 8 * int(rng.integers(1, 66))
+    w = rng.random(E) * (rng.random(E) > 0.2)
+    if w.sum() == 0:
+        w[0] = 1.0
+    counts = rng.multinomial(P, w / w.sum())
+    den = int(rng.integers(1, 11))
+    policy = ("ratio", int(rng.integers(0, den + 1)), den)
+    return W.make_problem(P=P, E=E, d_out=d_out, d_in=d_in, dtype="bf16", counts=counts,
+                          seed=600 + seed, policy=policy, glu=True, gate_up=(2 * d_in, d_out),
+                          name=f"random-chain-{seed}")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_glu_chain_random_shapes(seed):
+    """The MLP chain on random shapes: keep set and perm exactly, dgu_c within
+    its bf16 rounding, dW, dW2 and dx within 2e-3 max|ref| of the oracle."""
+    p = _random_chain_problem(seed)
+    gu, gl = p.gate_up, p.glu
+    q = lrmoe.plan_quota(p.counts, p.policy)
+    print(f"random-chain-{seed}: P={p.P} E={p.E} d_out={p.d_out} d_in={p.d_in} "
+          f"{p.policy} M={sum(q)}", flush=True)
+    plan = lrmoe.Plan(p.counts, q, p.d_out, p.d_in, lrmoe.BF16)
+    plan2 = lrmoe.Plan(p.counts, q, gu.d_out, gu.d_in, lrmoe.BF16)
+    d = U.dev
+    out = lrmoe.glu_chain_backward(plan, plan2, d(p.alpha), d(p.g), d(p.phi), d(p.W), d(gl.a),
+                                   d(gl.b), d(gu.x), d(gu.W2))
+    torch.cuda.synchronize()
+    ref = O.pruned_backward(p.counts, p.policy, p.alpha, p.g, p.phi, p.W, None, "bf16",
+                            glu=(gl.a, gl.b, gu.x, gu.W2))
+    same = U.check_keep(ref["scores"], p.counts, q, out["keep"].cpu().numpy().astype(bool),
+                        ref["keep"], ref["taus"])
+    assert same, "keep set inside the threshold band: reseed"
+    assert np.array_equal(out["perm"].cpu().numpy(), ref["perm"])
+    dgu = U.host_bits(out["dgu_c"])
+    dgu = (dgu.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    r = ref["dgu_c"]
+    if r.size:
+        bound = 2.0 ** -8 * np.abs(r) + 2e-5 * np.abs(r).max()
+        assert np.all(np.abs(dgu - r) <= bound)
+    errs = dict(dW=U.rel_err(out["dW"].cpu().numpy(), ref["dW"]),
+                dW2=U.rel_err(out["dW2"].cpu().numpy(), ref["dW2"]),
+                dx=U.rel_err(out["dx"].cpu().numpy(), ref["dx"]))
+    print(f"random-chain-{seed}", errs)
+    for k, v in errs.items():
+        assert v <= U.TOL, (k, v)
+    assert np.all(out["dx"].cpu().numpy()[~ref["keep"]] == 0)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_gate_up_random_shapes(seed):
+    """A second projection on the first one's keep set (lrmoe_gather_backward)
+    on random shapes, against the oracle."""
+    rng = np.random.default_rng(8000 + seed)
+    E = int(rng.integers(1, 11))
+    P = int(rng.integers(1, 64)) if seed % 3 == 1 else int(rng.integers(64, 4001))
+    d_out, d_in = 8 * int(rng.integers(1, 66)), 8 * int(rng.integers(1, 66))
+    d2o, d2i = 8 * int(rng.integers(1, 66)), 8 * int(rng.integers(1, 66))
+    counts = rng.multinomial(P, np.full(E, 1.0 / E))
+    den = int(rng.integers(1, 11))
+    policy = ("ratio", int(rng.integers(0, den + 1)), den)
+    p = W.make_problem(P=P, E=E, d_out=d_out, d_in=d_in, dtype="bf16", counts=counts,
+                       seed=650 + seed, gate_up=(d2o, d2i), name=f"random-gu-{seed}")
+    q = lrmoe.plan_quota(p.counts, policy)
+    print(f"random-gu-{seed}: P={P} E={E} down {d_out}x{d_in} gate/up {d2o}x{d2i} {policy} "
+          f"M={sum(q)}", flush=True)
+    plan, out, t = U.run_gpu(p, q)
+    gu = p.gate_up
+    plan2 = lrmoe.Plan(p.counts, q, gu.d_out, gu.d_in, lrmoe.BF16)
+    one = lrmoe.gather_backward(plan2, out["perm"], out["keep"], t["alpha"], U.dev(gu.g2),
+                                U.dev(gu.x), U.dev(gu.W2))
+    torch.cuda.synchronize()
+    ref = O.pruned_backward(p.counts, policy, p.alpha, p.g, p.phi, p.W, None, "bf16",
+                            gate_up=(gu.g2, gu.x, gu.W2))
+    U.check_keep(ref["scores"], p.counts, q, out["keep"].cpu().numpy().astype(bool),
+                 ref["keep"], ref["taus"])
+    keep = out["keep"].cpu().numpy().astype(bool)
+    if not np.array_equal(keep, ref["keep"]):
+        pytest.skip("keep set differs inside the threshold band (checked above)")
+    assert np.array_equal(U.host_bits(one["g_c"]), gu.g2[ref["perm"]])
+    assert np.array_equal(U.host_bits(one["phi_c"]), gu.x[ref["perm"]])
+    e1 = U.rel_err(one["dW"].cpu().numpy(), ref["dW2"])
+    e2 = U.rel_err(one["dphi"].cpu().numpy(), ref["dx"])
+    print(f"random-gu-{seed}", dict(dW2=e1, dx=e2))
+    assert e1 <= U.TOL and e2 <= U.TOL, (e1, e2)
+    assert np.all(one["dphi"].cpu().numpy()[~keep] == 0)
 
 
 def test_glu_chain_edges():
