@@ -343,21 +343,32 @@ def main():
              gu_ev[i] if (gu is not None or dense_path) else None)
     torch.cuda.synchronize()
 
-    # Cold pass: before each step, write a 512 MiB scratch buffer (evicts L2
-    # and the 256 MB MALL), then time score, select and gather again.
-    cold = None
+    # Cold passes: before each step, evict L2 and the 256 MB MALL, then time
+    # score, select and gather again.  "read": a 512 MiB buffer is summed, so
+    # the caches hold clean lines only (the kernels' own cost from HBM).
+    # "write": a 512 MiB buffer is filled, so its dirty lines are written
+    # back while the timed kernels run -- what a kernel pays after a
+    # write-heavy one.
+    cold = {}
     if not dense_path:
         nc = min(nb, 50)
         flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        cold_timer = lrmoe.KernelTimer(nc)
-        for i in range(nc):
-            flush.fill_(i & 0xFF)
-            step(cold_timer, None, None, None)
-        torch.cuda.synchronize()
-        cold = {n: stats_us(cold_timer.durations_us(slot))
-                for n, slot in (("lrm_score", 0), ("select_scan", 1), ("gather", 2))}
-        cold_timer.close()
-        del flush
+        flush_r = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+        sink = torch.empty(1, dtype=torch.float32, device=dev)
+        for how in ("read", "write"):
+            cold_timer = lrmoe.KernelTimer(nc)
+            for i in range(nc):
+                if how == "read":
+                    torch.sum(flush_r, dim=0, keepdim=True, out=sink)
+                else:
+                    flush.fill_(i & 0xFF)
+                step(cold_timer, None, None, None)
+            torch.cuda.synchronize()
+            st = {n: stats_us(cold_timer.durations_us(slot))
+                  for n, slot in (("lrm_score", 0), ("select_scan", 1), ("gather", 2))}
+            cold[how] = {n: v for n, v in st.items() if v is not None}
+            cold_timer.close()
+        del flush, flush_r
 
     es = 2 if p.dtype == "bf16" else 4
     P, d_o, d_i = p.P, p.d_out, p.d_in
@@ -450,12 +461,16 @@ def main():
         "score_select_compact": {"us": ssc_us, "algorithmic_bytes": nbytes,
                                  "GBps": nbytes / ssc_us / 1e3 if ssc_us else None,
                                  "hbm_frac": nbytes / ssc_us / 1e3 / HBM_PEAK_GBS if ssc_us else None},
-        "score_select_compact_cold": None if cold is None else {
-            "us": sum(v["mean"] for v in cold.values()),
-            "kernels_us": {k: v["mean"] for k, v in cold.items()},
-            "GBps": nbytes / sum(v["mean"] for v in cold.values()) / 1e3,
-            "hbm_frac": nbytes / sum(v["mean"] for v in cold.values()) / 1e3 / HBM_PEAK_GBS,
-            "note": "a 512 MiB scratch write before each of these steps evicts L2 and MALL"},
+        "score_select_compact_cold": None if not cold else {
+            how: {"us": sum(v["mean"] for v in c.values()),
+                  "kernels_us": {k: v["mean"] for k, v in c.items()},
+                  "GBps": nbytes / sum(v["mean"] for v in c.values()) / 1e3,
+                  "hbm_frac": nbytes / sum(v["mean"] for v in c.values()) / 1e3 / HBM_PEAK_GBS}
+            for how, c in cold.items()},
+        "score_select_compact_cold_note": ("before each of these steps a 512 MiB buffer is "
+                                           "read (clean eviction of L2 and MALL) or written "
+                                           "(its dirty lines are written back while the "
+                                           "kernels run)") if cold else None,
         "score_select_compact_note": ("the gather also writes the GEMM's operand planes "
                                       "(kernels.gather.gemm_plane_bytes), which the operand "
                                       "prologue would otherwise write; they are not counted "
