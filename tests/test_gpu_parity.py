@@ -46,6 +46,12 @@ MEDIUM = [
      ("ratio", 80, 100)),
     ("bf16-one-expert", dict(P=777, E=1, d_out=128, d_in=264, dtype="bf16", zipf=1.0),
      ("ratio", 1, 2)),
+    # 256 experts (the most the ABI takes), 16 row tiles and one column tile:
+    # two weight-gradient groups per expert and one input-gradient group make
+    # about 768 tile groups, more than the schedule table holds, so the GEMM
+    # runs on its formula-order schedule
+    ("bf16-256-experts-formula-schedule",
+     dict(P=16384, E=256, d_out=4096, d_in=64, dtype="bf16", zipf=1.0), ("ratio", 80, 100)),
 ]
 
 
