@@ -46,6 +46,10 @@ MEDIUM = [
      ("ratio", 80, 100)),
     ("bf16-one-expert", dict(P=777, E=1, d_out=128, d_in=264, dtype="bf16", zipf=1.0),
      ("ratio", 1, 2)),
+    # float32 storage (four operand planes) with an expert split along K:
+    # 2400 kept rows make three chunks whose partial tiles are reduced
+    ("fp32-split-k", dict(P=4000, E=3, d_out=136, d_in=200, dtype="f32",
+                          counts=[3000, 700, 300]), ("ratio", 80, 100)),
     # 256 experts (the most the ABI takes), 16 row tiles and one column tile:
     # two weight-gradient groups per expert and one input-gradient group make
     # about 768 tile groups, more than the schedule table holds, so the GEMM
