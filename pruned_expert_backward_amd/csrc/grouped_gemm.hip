@@ -24,7 +24,8 @@
 //     K step, and LDS reads and global->LDS loads are placed between MFMAs
 //     (see Tile).  Accumulators hold each 32x32 block transposed (lane = row,
 //     register quad = 4 consecutive columns), so results leave as 16-byte
-//     stores.
+//     stores; adjacent lanes swap one quad each first, so that every store
+//     instruction writes 64-byte row pieces from adjacent lane pairs.
 //   * Every operand is a bf16 plane in global memory.  alpha multiplies the
 //     reduction index of dW, so it cannot be applied after the product: a
 //     prologue writes alpha * (the narrower of g_c, phi_c) as bf16 hi + lo
@@ -669,8 +670,18 @@ struct Tile {
   // ---- epilogue.  Accumulator block (a, b) holds D[m][n] for tile row
   // m = wm*128 + a*32 + lane%32 and column n = wn*128 + b*32 + 8*(r/4) +
   // 4*(lane/32) + r%4 in register r: each register quad is 4 consecutive
-  // columns, stored as one 16-byte write.  Column counts are multiples of 4,
-  // so a quad never straddles the matrix edge.
+  // columns of the lane's own row.  Stores are paired by quads (2p, 2p+1):
+  // adjacent lanes (r, r^1) swap one quad each (one DPP lane swap per
+  // register), after which the first store of the pair writes the even row
+  // of each lane pair and the second the odd row, and each row's 64 bytes
+  // 16p .. 16p+15 come from the four lanes r, r^1, r+32, r^1+32 -- two
+  // coalesced 32-byte lane pairs instead of two lanes 32 apart per 32 bytes.
+  // Column counts are multiples of 4, so a quad never straddles the edge.
+  __device__ __forceinline__ static float swap_adjacent(float v) {
+    // quad_perm [1, 0, 3, 2]: lane l reads lane l ^ 1
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1,
+                                                              0xF, 0xF, false));
+  }
   __device__ __forceinline__ void epilogue(const Args& args, const GemmTable& tab,
                                            LDS_AS const char* prm,
                                            const f32x16 (&acc)[kMB][kNB]) const {
@@ -687,37 +698,59 @@ struct Tile {
       glu_epilogue(args, prm, acc);
       return;
     }
-    const int cq = 4 * (lane >> 5);   // this lane's column offset inside each group of 8
+    // Opaque copies: keep the compiler from computing every quad's column
+    // and edge predicate ahead of the main loop, where they would stay live.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    int ncols = (IS_DW && part != nullptr) ? BN : d_in - n0;
+    asm volatile("" : "+s"(ncols));
+    const bool odd = (ln & 1) != 0;
+    // this lane's column inside each 16-column group: 0/4 (lane half) + 8 (odd lane)
+    const int cq = 4 * (ln >> 5) + (odd ? 8 : 0);
 #pragma unroll
     for (int a = 0; a < kMB; ++a) {
-      const int lrow = wm * WTM + a * 32 + (lane & 31);
-      const int mrow = m0 + lrow;
-      // destination of tile column 0 of this row, and how many columns exist
-      float* orow = nullptr;
-      int ncols = d_in - n0;
-      float scale = 1.f;
-      if (IS_DW) {
-        if (part != nullptr) {
-          orow = part + lrow * BN;
-          ncols = BN;
-        } else if (mrow < mrows) {
-          orow = args.dW + ((int64_t)e * d_out + mrow) * d_in + n0;
+      // rows of this lane's two stores: the even and the odd row of its pair
+      const int lrow0 = wm * WTM + a * 32 + (ln & 30);
+      float* orow[2] = {nullptr, nullptr};
+      float scale[2] = {1.f, 1.f};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int lrow = lrow0 + h;
+        if (IS_DW) {
+          if (part != nullptr) orow[h] = part + lrow * BN;
+          else if (m0 + lrow < mrows) orow[h] = args.dW + ((int64_t)e * d_out + m0 + lrow) * d_in + n0;
+        } else {
+          const int32_t u = s_perm[lrow];
+          scale[h] = s_alpha[lrow];
+          if (u >= 0) orow[h] = args.dphi + (int64_t)u * d_in + n0;
         }
-      } else {
-        const int32_t u = s_perm[lrow];
-        scale = s_alpha[lrow];
-        if (u >= 0) orow = args.dphi + (int64_t)u * d_in + n0;
       }
-      if (orow == nullptr) continue;
 #pragma unroll
       for (int b = 0; b < kNB; ++b)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = wn * WTN + b * 32 + 8 * g + cq;
-          f32x4 v = {acc[a][b][4 * g], acc[a][b][4 * g + 1], acc[a][b][4 * g + 2],
-                     acc[a][b][4 * g + 3]};
-          if (!IS_DW) v *= scale;
-          if (col < ncols) *reinterpret_cast<f32x4*>(orow + col) = v;
+        for (int p = 0; p < 2; ++p) {
+          const int col = wn * WTN + b * 32 + 16 * p + cq;
+          f32x4 v0, v1;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            // read straight from the accumulation registers, here: a plain
+            // use makes the compiler copy all 256 accumulators at once
+            float q0, q1;
+            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(q0) : "a"(acc[a][b][8 * p + i]));
+            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(q1) : "a"(acc[a][b][8 * p + 4 + i]));
+            // even lanes pass quad 2p+1 of their row, odd lanes quad 2p
+            const float got = swap_adjacent(odd ? q0 : q1);
+            v0[i] = odd ? got : q0;   // even row of the pair
+            v1[i] = odd ? q1 : got;   // odd row
+          }
+          if (!IS_DW) {
+            v0 *= scale[0];
+            v1 *= scale[1];
+          }
+          if (col < ncols) {
+            if (orow[0] != nullptr) *reinterpret_cast<f32x4*>(orow[0] + col) = v0;
+            if (orow[1] != nullptr) *reinterpret_cast<f32x4*>(orow[1] + col) = v1;
+          }
         }
     }
   }
