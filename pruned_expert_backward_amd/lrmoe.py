@@ -490,8 +490,13 @@ class KernelTimer:
                 continue
             ms = C.c_float()
             # hipEventElapsedTime fails for events that were never recorded
+            # (a kernel the call did not launch); that failure also stays in
+            # HIP's last-error slot, where the next launch check of another
+            # caller (torch) would report it, so it is cleared here
             if self._hip.hipEventElapsedTime(C.byref(ms), t.before[slot], t.after[slot]) == 0:
                 out.append(ms.value * 1e3)
+            else:
+                self._hip.hipGetLastError()
         return out
 
     def mean_us(self, slot: int) -> Optional[float]:

@@ -622,3 +622,24 @@ def test_gather_backward_token_rows(dtype):
     ref_dx = O.input_grad(seg, perm, p.alpha[perm], g2[perm], W2, dtype, p.P)
     assert U.rel_err(one["dW"].cpu().numpy(), ref_dW) <= U.TOL
     assert U.rel_err(one["dphi"].cpu().numpy(), ref_dx) <= U.TOL
+
+
+def test_timer_leaves_no_hip_error_for_unlaunched_kernels():
+    """Given scores skip the score kernel, so its timing events are never
+    recorded.  Reading their duration fails inside HIP; that failure must not
+    stay behind for the next torch launch check to report."""
+    p = W.make_problem(P=600, E=3, d_out=64, d_in=32, dtype="bf16", counts=[250, 50, 300], seed=21)
+    plan = lrmoe.Plan(p.counts, [200, 40, 240], p.d_out, p.d_in, lrmoe.BF16)
+    timer = lrmoe.KernelTimer(1)
+    try:
+        lrmoe.score_select_compact(plan, U.dev(p.alpha), U.dev(p.g), U.dev(p.phi),
+                                   scores=U.dev(W.random_scores(p.P, 5)), timing=timer)
+        torch.cuda.synchronize()
+        assert timer.durations_us(0) == []        # score slot: kernel not launched
+        assert len(timer.durations_us(1)) == 1    # select
+        x = torch.empty(4096, device="cuda:0")
+        x.fill_(2.0)                              # a torch launch checks HIP's last error
+        torch.cuda.synchronize()
+        assert float(x.sum()) == 8192.0
+    finally:
+        timer.close()
