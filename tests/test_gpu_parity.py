@@ -643,3 +643,18 @@ def test_timer_leaves_no_hip_error_for_unlaunched_kernels():
         assert float(x.sum()) == 8192.0
     finally:
         timer.close()
+
+
+@pytest.mark.parametrize("dtype,d_out,d_in", [("f32", 68, 36), ("bf16", 72, 264)])
+def test_epilogue_column_edges(dtype, d_out, d_in):
+    """Matrix edges inside the epilogue's 16-column store groups: the last
+    tile column holds 4 (float32) or 8 (bfloat16) columns, so in each lane
+    pair only some lanes' quads are inside the matrix, for both rows of the
+    pair; one expert spans two row tiles."""
+    counts = [450, 250]
+    p = W.make_problem(P=sum(counts), E=2, d_out=d_out, d_in=d_in, dtype=dtype, counts=counts,
+                       seed=77)
+    q = lrmoe.plan_quota(p.counts, ("ratio", 4, 5))
+    print(f"edges: {dtype} d_out={d_out} d_in={d_in} quotas={q}", flush=True)
+    _, out, _ = U.run_gpu(p, q)
+    U.compare_full(p, q, out)
