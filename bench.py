@@ -13,7 +13,10 @@ launches on, in every timed step (the only events in the timed region).
 `kernels` gives every kernel's time and rate from a separate pass with events
 around each kernel; `cpu_baseline` times the CPU oracle on the host cores.
 
-Usage: python bench.py [--gpus 1] [--steps 1000] [--warmup 50] [--config 1]
+The default workload is the largest single-GPU one: the GLM4.5-106B-A12B-shaped
+20x batch-pressure share (655360 routed pairs, 24 GiB token-buffer budget).
+
+Usage: python bench.py [--gpus 1] [--steps 1000] [--warmup 50] [--config 4]
 """
 from __future__ import annotations
 
@@ -169,7 +172,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--config", type=int, default=4,
+                    help="workload (4: GLM4.5 20x batch-pressure share, the largest)")
     ap.add_argument("--dw-mode", choices=["exact", "bf16"], default="exact")
     ap.add_argument("--score-mode", choices=["lrm", "grad-sqnorm", "grad-l1", "random"],
                     default="lrm", help="scoring rule (the method, or an ablation baseline)")

@@ -41,6 +41,14 @@
  *    buffers are disjoint.  Outputs must not alias inputs.
  *  - Device pointers must be 16-byte aligned.  d_out and d_in must be
  *    multiples of 8 (bf16) or 4 (float32).
+ *  - Row indices are a precondition the host cannot check (they live in
+ *    device memory): 0 <= g_row_index[u] < T and 0 <= phi_row_index[u] <
+ *    T_phi.  The kernels still bound every index they read, so a violation
+ *    does not fault: a g or phi row whose index is out of range reads as a
+ *    row of zeros (score 0, zero compacted row), and a perm entry outside
+ *    0..P-1 is skipped.  A call that reads g rows for P > 0 pairs needs
+ *    T >= 1 (LRMOE_ERR_SHAPE otherwise), and one that reads phi through a
+ *    row index for M > 0 kept pairs needs 1 <= T_phi < 2^31.
  *  - Errors: every host-detectable problem is reported before anything is
  *    launched, and no entry point aborts or prints.  A failed kernel launch
  *    returns LRMOE_ERR_HIP; faults inside kernels surface at the caller's
@@ -56,7 +64,7 @@
 extern "C" {
 #endif
 
-#define LRMOE_ABI_VERSION 3
+#define LRMOE_ABI_VERSION 4
 #define LRMOE_MAX_EXPERTS 256
 
 typedef enum {
@@ -123,6 +131,9 @@ typedef struct {
   const int64_t* quotas;   /* host [E]: q_e, 0 <= q_e <= n_e                  */
   int32_t dw_mode;         /* lrmoe_dw_mode                                  */
   int32_t score_mode;      /* lrmoe_score_mode (0 = LRM)                     */
+  int64_t T_phi;           /* rows of phi when a phi_row_index is passed
+                              (lrmoe_gather_compact, lrmoe_gather_backward);
+                              ignored otherwise, where phi has P rows        */
 } lrmoe_problem;
 
 /* ABI version of the loaded library (LRMOE_ABI_VERSION at build time). */

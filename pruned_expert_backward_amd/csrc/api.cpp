@@ -208,8 +208,11 @@ lrmoe_status select_compact(const lrmoe_problem* pb, bool compute_scores, const 
   LRMOE_TRY(check_problem(pb, c));
   const int64_t P = pb->P, M = c.M;
   if (g_row_index == nullptr && pb->T != P) return LRMOE_ERR_SHAPE;
+  // g rows are read by the score pass (every pair) and by the gather (kept pairs)
+  const bool reads_g = P > 0 && (compute_scores || (gather && M > 0));
+  if (reads_g && pb->T < 1) return LRMOE_ERR_SHAPE;
   LRMOE_TRY(need(alpha, P));
-  LRMOE_TRY(need(g, P > 0 ? pb->T : 0));
+  LRMOE_TRY(need(g, reads_g ? pb->T : 0));
   LRMOE_TRY(need(phi, P));
   LRMOE_TRY(optional(g_row_index));
   if (compute_scores) {
@@ -236,7 +239,8 @@ lrmoe_status select_compact(const lrmoe_problem* pb, bool compute_scores, const 
   if (compute_scores) {
     LRMOE_TRY(mark(timing, false, 0, s));
     LRMOE_TRY(hip_status(launch_score(pb->dtype, pb->score_mode, g, phi, alpha, g_row_index,
-                                      (int32_t)P, pb->d_out, pb->d_in, scores_out, s)));
+                                      (int32_t)P, (int32_t)pb->T, pb->d_out, pb->d_in,
+                                      scores_out, s)));
     LRMOE_TRY(mark(timing, true, 0, s));
     scores = scores_out;
   }
@@ -248,7 +252,8 @@ lrmoe_status select_compact(const lrmoe_problem* pb, bool compute_scores, const 
   LRMOE_TRY(mark(timing, false, 2, s));
   LRMOE_TRY(hip_status(launch_gather(pb->dtype, perm, keep, g_row_index, nullptr, alpha, g, phi,
                                      g_c, phi_c, alpha_c, dphi_zero, (int32_t)M, (int32_t)P,
-                                     pb->d_out, pb->d_in, s, planes)));
+                                     (int32_t)pb->T, (int32_t)P, pb->d_out, pb->d_in, s,
+                                     planes)));
   LRMOE_TRY(mark(timing, true, 2, s));
   return LRMOE_OK;
 }
@@ -489,13 +494,19 @@ lrmoe_status gather_compact(const lrmoe_problem* pb, const int32_t* perm, const 
   const int64_t P = pb->P, M = c.M;
   const bool with_g = g != nullptr || g_c != nullptr;   // both NULL: phi rows only
   if (with_g && g_row_index == nullptr && pb->T != P) return LRMOE_ERR_SHAPE;
+  if (with_g && M > 0 && pb->T < 1) return LRMOE_ERR_SHAPE;
+  // rows of phi: T_phi through a row index, else one per pair
+  const int64_t phi_rows = phi_row_index != nullptr ? pb->T_phi : P;
+  if (phi_row_index != nullptr && M > 0 &&
+      (pb->T_phi < 1 || pb->T_phi >= (int64_t(1) << 31)))
+    return LRMOE_ERR_SHAPE;
   LRMOE_TRY(need(perm, M));
   LRMOE_TRY(need(alpha, P));
   if (with_g) {
     LRMOE_TRY(need(g, M > 0 ? pb->T : 0));
     LRMOE_TRY(need(g_c, M));
   }
-  LRMOE_TRY(need(phi, M));
+  LRMOE_TRY(need(phi, M > 0 ? phi_rows : 0));
   LRMOE_TRY(optional(g_row_index));
   LRMOE_TRY(optional(phi_row_index));
   LRMOE_TRY(need(phi_c, M));
@@ -507,7 +518,8 @@ lrmoe_status gather_compact(const lrmoe_problem* pb, const int32_t* perm, const 
   LRMOE_TRY(mark(timing, false, 2, s));
   LRMOE_TRY(hip_status(launch_gather(pb->dtype, perm, keep, g_row_index, phi_row_index, alpha, g,
                                      phi, g_c, phi_c, alpha_c, dphi_zero, (int32_t)M,
-                                     (int32_t)P, pb->d_out, pb->d_in, s, planes)));
+                                     (int32_t)P, (int32_t)pb->T, (int32_t)phi_rows, pb->d_out,
+                                     pb->d_in, s, planes)));
   LRMOE_TRY(mark(timing, true, 2, s));
   return LRMOE_OK;
 }
@@ -524,6 +536,7 @@ lrmoe_status gather_backward(const lrmoe_problem* pb, const int32_t* perm, const
   LRMOE_TRY(check_problem(pb, c));
   LRMOE_TRY(need(W, 1));
   LRMOE_TRY(need(dW, 1));
+  if (c.M > 0 && pb->T < 1) return LRMOE_ERR_SHAPE;
   LRMOE_TRY(need(g, c.M > 0 ? pb->T : 0));   // the GEMM needs g rows: no NULL g here
   LRMOE_TRY(need(g_c, c.M));
   const GemmWorkspace wl = gemm_workspace(pb, c.M);

@@ -15,6 +15,17 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
+// Zero row (a source row index out of range reads as zeros), and its planes.
+__device__ __forceinline__ void zero_row(uint4* __restrict__ dst, uint4* __restrict__ hi,
+                                         uint4* __restrict__ lo, int nchunk, int lane) {
+  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+  for (int c = lane; c < nchunk; c += 64) {
+    if (dst != nullptr) dst[c] = z;
+    if (hi != nullptr) hi[c] = z;
+    if (lo != nullptr) lo[c] = z;
+  }
+}
+
 __device__ __forceinline__ void copy_row(const uint4* __restrict__ src, uint4* __restrict__ dst,
                                          int nchunk, int lane) {
   int c = lane;
@@ -61,9 +72,9 @@ __global__ __launch_bounds__(256) void gather_kernel(
     const int32_t* __restrict__ g_row_index, const int32_t* __restrict__ phi_row_index,
     const float* __restrict__ alpha, const uint4* __restrict__ g, const uint4* __restrict__ phi,
     uint4* __restrict__ g_c, uint4* __restrict__ phi_c, float* __restrict__ alpha_c,
-    float4* __restrict__ dphi_zero, int32_t M, int32_t P, int32_t gch, int32_t pch,
-    int32_t zch, uint4* __restrict__ pl_hi, uint4* __restrict__ pl_lo, int pl_from_phi,
-    int32_t* __restrict__ zero, int nzero) {
+    float4* __restrict__ dphi_zero, int32_t M, int32_t P, int32_t g_rows, int32_t phi_rows,
+    int32_t gch, int32_t pch, int32_t zch, uint4* __restrict__ pl_hi, uint4* __restrict__ pl_lo,
+    int pl_from_phi, int32_t* __restrict__ zero, int nzero) {
   const int lane = threadIdx.x & 63;
   if (blockIdx.x == 0 && (int)threadIdx.x < nzero) zero[threadIdx.x] = 0;
   const int64_t job = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -73,17 +84,30 @@ __global__ __launch_bounds__(256) void gather_kernel(
     if ((uint32_t)u >= (uint32_t)P) return;   // perm holds pair indices < P
     const int64_t gr = g_row_index ? (int64_t)g_row_index[u] : (int64_t)u;
     const int64_t pr = phi_row_index ? (int64_t)phi_row_index[u] : (int64_t)u;
+    // source rows outside g's / phi's rows read as zeros
+    const bool g_ok = (uint64_t)gr < (uint64_t)g_rows;
+    const bool p_ok = (uint64_t)pr < (uint64_t)phi_rows;
     const float a = alpha[u];
-    if (pl_hi != nullptr && !pl_from_phi)
-      copy_row_split(g + gr * gch, g_c + (int64_t)j * gch, pl_hi + (int64_t)j * gch,
-                     pl_lo ? pl_lo + (int64_t)j * gch : nullptr, a, gch, lane);
-    else if (g_c != nullptr)
-      copy_row(g + gr * gch, g_c + (int64_t)j * gch, gch, lane);
-    if (pl_hi != nullptr && pl_from_phi)
-      copy_row_split(phi + pr * pch, phi_c + (int64_t)j * pch, pl_hi + (int64_t)j * pch,
-                     pl_lo ? pl_lo + (int64_t)j * pch : nullptr, a, pch, lane);
-    else
-      copy_row(phi + pr * pch, phi_c + (int64_t)j * pch, pch, lane);
+    uint4* gdst = g_c != nullptr ? g_c + (int64_t)j * gch : nullptr;
+    uint4* pdst = phi_c + (int64_t)j * pch;
+    if (pl_hi != nullptr && !pl_from_phi) {
+      uint4* h = pl_hi + (int64_t)j * gch;
+      uint4* l = pl_lo ? pl_lo + (int64_t)j * gch : nullptr;
+      if (g_ok) copy_row_split(g + gr * gch, gdst, h, l, a, gch, lane);
+      else zero_row(gdst, h, l, gch, lane);
+    } else if (gdst != nullptr) {
+      if (g_ok) copy_row(g + gr * gch, gdst, gch, lane);
+      else zero_row(gdst, nullptr, nullptr, gch, lane);
+    }
+    if (pl_hi != nullptr && pl_from_phi) {
+      uint4* h = pl_hi + (int64_t)j * pch;
+      uint4* l = pl_lo ? pl_lo + (int64_t)j * pch : nullptr;
+      if (p_ok) copy_row_split(phi + pr * pch, pdst, h, l, a, pch, lane);
+      else zero_row(pdst, h, l, pch, lane);
+    } else {
+      if (p_ok) copy_row(phi + pr * pch, pdst, pch, lane);
+      else zero_row(pdst, nullptr, nullptr, pch, lane);
+    }
     if (lane == 0) alpha_c[j] = a;
   } else if (dphi_zero != nullptr && job < (int64_t)M + P) {
     const int64_t u = job - M;
@@ -128,8 +152,8 @@ hipError_t launch_gather(int dtype, const int32_t* perm, const uint8_t* keep,
                          const int32_t* g_row_index, const int32_t* phi_row_index,
                          const float* alpha, const void* g, const void* phi, void* g_c,
                          void* phi_c, float* alpha_c, float* dphi_zero, int32_t M,
-                         int32_t P, int32_t d_out, int32_t d_in, hipStream_t s,
-                         const GatherPlanes& planes) {
+                         int32_t P, int32_t g_rows, int32_t phi_rows, int32_t d_out,
+                         int32_t d_in, hipStream_t s, const GatherPlanes& planes) {
   const int per = (dtype == LRMOE_BF16) ? 8 : 4;
   if (planes.hi != nullptr && dtype != LRMOE_BF16) return hipErrorInvalidValue;
   const int64_t jobs = (int64_t)M + (dphi_zero ? (int64_t)P : 0);
@@ -137,8 +161,8 @@ hipError_t launch_gather(int dtype, const int32_t* perm, const uint8_t* keep,
   const int64_t blocks = (jobs + 3) / 4;
   hipLaunchKernelGGL(gather_kernel, dim3((unsigned)blocks), dim3(256), 0, s, perm, keep,
                      g_row_index, phi_row_index, alpha, (const uint4*)g, (const uint4*)phi,
-                     (uint4*)g_c, (uint4*)phi_c, alpha_c, (float4*)dphi_zero, M, P,
-                     d_out / per, d_in / per, d_in / 4, (uint4*)planes.hi, (uint4*)planes.lo,
+                     (uint4*)g_c, (uint4*)phi_c, alpha_c, (float4*)dphi_zero, M, P, g_rows,
+                     phi_rows, d_out / per, d_in / per, d_in / 4, (uint4*)planes.hi, (uint4*)planes.lo,
                      planes.from_phi ? 1 : 0, planes.zero, planes.nzero);
   return hipGetLastError();
 }

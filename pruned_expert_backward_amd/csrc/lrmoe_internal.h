@@ -123,9 +123,10 @@ __device__ __forceinline__ HiLo alpha_split(float a, float x) {
 }
 
 // Launchers (return hipSuccess or the launch error).
+// g has T rows; a row index outside [0, T) reads as a zero row.
 hipError_t launch_score(int dtype, int mode, const void* g, const void* phi, const float* alpha,
-                        const int32_t* row_index, int32_t P, int32_t d_out, int32_t d_in,
-                        float* scores, hipStream_t s);
+                        const int32_t* row_index, int32_t P, int32_t T, int32_t d_out,
+                        int32_t d_in, float* scores, hipStream_t s);
 
 hipError_t launch_select_scan(const ExpertTable& tab, const float* scores, uint8_t* keep,
                               int32_t* perm, int32_t* seg_offsets_out, uint32_t* hist,
@@ -151,11 +152,14 @@ struct GatherPlanes {
   int nzero = 0;
 };
 
+// g has g_rows rows and phi phi_rows rows; a source row index outside them
+// reads as a zero row.
 hipError_t launch_gather(int dtype, const int32_t* perm, const uint8_t* keep,
                          const int32_t* g_row_index, const int32_t* phi_row_index,
                          const float* alpha, const void* g, const void* phi, void* g_c,
                          void* phi_c, float* alpha_c, float* dphi_zero, int32_t M,
-                         int32_t P, int32_t d_out, int32_t d_in, hipStream_t s,
+                         int32_t P, int32_t g_rows, int32_t phi_rows, int32_t d_out,
+                         int32_t d_in, hipStream_t s,
                          const GatherPlanes& planes = GatherPlanes());
 
 // hi (and lo, if non-null) bf16 planes of alpha[row] * src[row][col] (alpha

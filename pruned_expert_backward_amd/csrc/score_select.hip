@@ -84,7 +84,7 @@ __device__ __forceinline__ float row_sumsq(const V* __restrict__ row, int nchunk
 template <bool BF16, int MODE>
 __global__ __launch_bounds__(256) void lrm_score_kernel(
     const void* __restrict__ g, const void* __restrict__ phi, const float* __restrict__ alpha,
-    const int32_t* __restrict__ row_index, int32_t P, int32_t d_out, int32_t d_in,
+    const int32_t* __restrict__ row_index, int32_t P, int32_t T, int32_t d_out, int32_t d_in,
     float* __restrict__ scores) {
   const int lane = threadIdx.x & 63;
   const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
@@ -93,14 +93,16 @@ __global__ __launch_bounds__(256) void lrm_score_kernel(
   const int gc = d_out / per, pc = d_in / per;
   for (int u = wave; u < P; u += nwaves) {
     const int64_t r = row_index ? (int64_t)row_index[u] : (int64_t)u;
+    // a row index outside g's T rows reads as a zero row: no load at all
+    const int gcr = (uint64_t)r < (uint64_t)T ? gc : 0;
     constexpr bool L1 = MODE == LRMOE_SCORE_GRAD_L1;
     float gs, ps = 1.f;
     if (BF16) {
-      gs = row_sumsq<L1>(reinterpret_cast<const uint4*>(g) + r * gc, gc, lane);
+      gs = row_sumsq<L1>(reinterpret_cast<const uint4*>(g) + r * gc, gcr, lane);
       if (MODE == LRMOE_SCORE_LRM)
         ps = row_sumsq(reinterpret_cast<const uint4*>(phi) + (int64_t)u * pc, pc, lane);
     } else {
-      gs = row_sumsq<L1>(reinterpret_cast<const float4*>(g) + r * gc, gc, lane);
+      gs = row_sumsq<L1>(reinterpret_cast<const float4*>(g) + r * gc, gcr, lane);
       if (MODE == LRMOE_SCORE_LRM)
         ps = row_sumsq(reinterpret_cast<const float4*>(phi) + (int64_t)u * pc, pc, lane);
     }
@@ -503,33 +505,33 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_scan_kernel(
 
 template <int MODE>
 void launch_score_mode(int dtype, dim3 grid, hipStream_t s, const void* g, const void* phi,
-                       const float* alpha, const int32_t* row_index, int32_t P, int32_t d_out,
-                       int32_t d_in, float* scores) {
+                       const float* alpha, const int32_t* row_index, int32_t P, int32_t T,
+                       int32_t d_out, int32_t d_in, float* scores) {
   if (dtype == LRMOE_BF16)
     hipLaunchKernelGGL((lrm_score_kernel<true, MODE>), grid, dim3(256), 0, s, g, phi, alpha,
-                       row_index, P, d_out, d_in, scores);
+                       row_index, P, T, d_out, d_in, scores);
   else
     hipLaunchKernelGGL((lrm_score_kernel<false, MODE>), grid, dim3(256), 0, s, g, phi, alpha,
-                       row_index, P, d_out, d_in, scores);
+                       row_index, P, T, d_out, d_in, scores);
 }
 
 hipError_t launch_score(int dtype, int mode, const void* g, const void* phi, const float* alpha,
-                        const int32_t* row_index, int32_t P, int32_t d_out, int32_t d_in,
-                        float* scores, hipStream_t s) {
+                        const int32_t* row_index, int32_t P, int32_t T, int32_t d_out,
+                        int32_t d_in, float* scores, hipStream_t s) {
   if (P <= 0) return hipSuccess;
   const int waves_per_block = 4;
   int blocks = (P + waves_per_block - 1) / waves_per_block;
   if (blocks > 256 * 8) blocks = 256 * 8;   // 32 waves per CU, each looping over pairs
   const dim3 grid(blocks);
   if (mode == LRMOE_SCORE_GRAD_SQNORM)
-    launch_score_mode<LRMOE_SCORE_GRAD_SQNORM>(dtype, grid, s, g, phi, alpha, row_index, P,
+    launch_score_mode<LRMOE_SCORE_GRAD_SQNORM>(dtype, grid, s, g, phi, alpha, row_index, P, T,
                                                d_out, d_in, scores);
   else if (mode == LRMOE_SCORE_GRAD_L1)
-    launch_score_mode<LRMOE_SCORE_GRAD_L1>(dtype, grid, s, g, phi, alpha, row_index, P, d_out,
-                                           d_in, scores);
+    launch_score_mode<LRMOE_SCORE_GRAD_L1>(dtype, grid, s, g, phi, alpha, row_index, P, T,
+                                           d_out, d_in, scores);
   else
-    launch_score_mode<LRMOE_SCORE_LRM>(dtype, grid, s, g, phi, alpha, row_index, P, d_out, d_in,
-                                       scores);
+    launch_score_mode<LRMOE_SCORE_LRM>(dtype, grid, s, g, phi, alpha, row_index, P, T, d_out,
+                                       d_in, scores);
   return hipGetLastError();
 }
 

@@ -21,7 +21,7 @@ DW_EXACT, DW_BF16 = 0, 1
 SCORE_LRM, SCORE_GRAD_SQNORM, SCORE_GRAD_L1 = 0, 1, 2
 QUOTA_RATIO, QUOTA_BUDGET = 0, 1
 MAX_EXPERTS = 256
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 STATUS = {0: "LRMOE_OK", 1: "LRMOE_ERR_NULL", 2: "LRMOE_ERR_INVALID", 3: "LRMOE_ERR_SHAPE",
           4: "LRMOE_ERR_ALIGN", 5: "LRMOE_ERR_DTYPE", 6: "LRMOE_ERR_WORKSPACE",
@@ -48,7 +48,7 @@ class Problem(C.Structure):
     _fields_ = [("E", C.c_int32), ("dtype", C.c_int32), ("P", C.c_int64), ("T", C.c_int64),
                 ("d_out", C.c_int32), ("d_in", C.c_int32),
                 ("counts", C.POINTER(C.c_int64)), ("quotas", C.POINTER(C.c_int64)),
-                ("dw_mode", C.c_int32), ("score_mode", C.c_int32)]
+                ("dw_mode", C.c_int32), ("score_mode", C.c_int32), ("T_phi", C.c_int64)]
 
 
 class Timing(C.Structure):
@@ -188,7 +188,7 @@ class Plan:
         self.struct = Problem(self.E, self.dtype, self.P, self.T, self.d_out, self.d_in,
                               C.cast(self._cnt, C.POINTER(C.c_int64)),
                               C.cast(self._q, C.POINTER(C.c_int64)), self.dw_mode,
-                              int(score_mode))
+                              int(score_mode), 0)
 
     @property
     def torch_dtype(self):
@@ -345,6 +345,8 @@ def gather_compact(plan: Plan, perm, keep, alpha, g, phi, g_row_index=None, phi_
                    alpha_c=_empty((plan.M,), torch.float32, dev))
         if zero_target:
             out["dphi"] = _empty((plan.P, plan.d_in), torch.float32, dev)
+    # rows of phi that phi_row_index addresses (the library bounds the index by them)
+    plan.struct.T_phi = phi.shape[0] if phi_row_index is not None else 0
     st = lib().lrmoe_gather_compact(C.byref(plan.struct), _ptr(perm), _ptr(keep),
                                     _ptr(g_row_index), _ptr(phi_row_index), _ptr(alpha), _ptr(g),
                                     _ptr(phi), _ptr(out.get("g_c")), _ptr(out["phi_c"]),
@@ -389,6 +391,7 @@ def gather_backward(plan: Plan, perm, keep, alpha, g, phi, W, g_row_index=None,
             out[k] = _empty(shape, t, dev)
     if ws is None:
         ws = workspace(plan, dev)
+    plan.struct.T_phi = phi.shape[0] if phi_row_index is not None else 0
     args = (C.byref(plan.struct), _ptr(perm), _ptr(keep), _ptr(g_row_index), _ptr(phi_row_index),
             _ptr(alpha), _ptr(g), _ptr(phi), _ptr(W), _ptr(out["g_c"]), _ptr(out["phi_c"]),
             _ptr(out["alpha_c"]), _ptr(out["dW"]), _ptr(out["dphi"]), _ptr(ws), ws.numel(),

@@ -135,6 +135,37 @@ def test_row_index_required_when_g_is_per_token():
     assert sscc(plan(), row=FAKE + 8) == 4
 
 
+def test_row_index_needs_rows_to_index():
+    """With a g row index, g must have at least one row when any pair is
+    read (T = 0 would let a NULL g through to the kernels); with a phi row
+    index, phi's row count T_phi must be given when rows are gathered.  The
+    index values themselves live on the device: the kernels bound them by T
+    and T_phi (reading a zero row), which no CPU test can launch."""
+    assert sscc(plan(T=0), row=FAKE) == 3
+    assert sscc(plan(T=0), row=FAKE, g=None) == 3
+    gc = L.lib().lrmoe_gather_compact
+    # perm keep g_row phi_row alpha g phi g_c phi_c alpha_c dphi_zero stream
+    ok = [FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None]
+    p = plan(T=0)
+    assert gc(C.byref(p.struct), *ok) == 3                  # g rows gathered, T = 0
+    a = list(ok)
+    a[3] = FAKE                                            # phi row index ...
+    p = plan(T=4)
+    p.struct.T_phi = 0
+    assert gc(C.byref(p.struct), *a) == 3                  # ... with no phi rows
+    p.struct.T_phi = 2**31
+    assert gc(C.byref(p.struct), *a) == 3
+    gb = L.lib().lrmoe_gather_backward
+    p = plan(T=0)
+    n = p.workspace_bytes()
+    okb = [FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+           n, None]
+    assert gb(C.byref(p.struct), *okb) == 3
+    pb = L.lib().lrmoe_pruned_backward
+    okp = [FAKE] + [FAKE] * 14 + [n, None]
+    assert pb(C.byref(p.struct), *okp) == 3
+
+
 def test_workspace_size_and_check():
     p = plan(counts=(40, 20, 30), quotas=(30, 10, 20), d_out=64, d_in=32)
     n = p.workspace_bytes()

@@ -154,10 +154,12 @@ def test_masked_dense_matches_compacted(dw_mode):
     if dw_mode == lrmoe.DW_EXACT:
         assert U.rel_err(out["dW"].cpu().numpy(), dW_ref) <= U.TOL
     else:
-        # single rounding of alpha * operand: the compacted GPU path rounds the
-        # same products, so the two agree up to float32 summation order
-        _, comp, _ = U.run_gpu(p, q, dw_mode=dw_mode)
-        assert U.rel_err(out["dW"].cpu().numpy(), comp["dW"].cpu().numpy().astype(np.float64)) <= 1e-5
+        # single rounding of alpha * operand: within that rounding's per-element
+        # bound around the oracle (dropped pairs enter with alpha = 0, exactly
+        # nothing; the float32 sums run over every routed pair of an expert)
+        s_abs = O.weight_grad(seg, np.abs(a_c), U.abs_rows(g_c), U.abs_rows(phi_c), "bf16", p.E,
+                              p.d_out, p.d_in)
+        U.check_single_rounding(out["dW"].cpu().numpy(), dW_ref, s_abs, int(max(p.counts)), "dW")
     am = out["alpha_masked"].cpu().numpy()
     assert np.array_equal(am, np.where(keep, p.alpha, np.float32(0)))
     assert np.array_equal(out["perm_identity"].cpu().numpy(), np.arange(p.P))
@@ -372,12 +374,17 @@ def test_gate_up_random_shapes(seed):
     U.check_keep(ref["scores"], p.counts, q, out["keep"].cpu().numpy().astype(bool),
                  ref["keep"], ref["taus"])
     keep = out["keep"].cpu().numpy().astype(bool)
-    if not np.array_equal(keep, ref["keep"]):
-        pytest.skip("keep set differs inside the threshold band (checked above)")
-    assert np.array_equal(U.host_bits(one["g_c"]), gu.g2[ref["perm"]])
-    assert np.array_equal(U.host_bits(one["phi_c"]), gu.x[ref["perm"]])
-    e1 = U.rel_err(one["dW"].cpu().numpy(), ref["dW2"])
-    e2 = U.rel_err(one["dphi"].cpu().numpy(), ref["dx"])
+    # the oracle's compaction of the GPU keep set (equal to its own where the
+    # keep sets agree; they may differ only inside the threshold band)
+    perm, seg = O.compact(keep, p.counts, q)
+    assert np.array_equal(out["perm"].cpu().numpy(), perm)
+    g2_c, x_c, a_c = O.gather(perm, None, gu.g2, gu.x, p.alpha)
+    assert np.array_equal(U.host_bits(one["g_c"]), g2_c)
+    assert np.array_equal(U.host_bits(one["phi_c"]), x_c)
+    dW2_ref = O.weight_grad(seg, a_c, g2_c, x_c, "bf16", p.E, gu.d_out, gu.d_in)
+    dx_ref = O.input_grad(seg, perm, a_c, g2_c, gu.W2, "bf16", p.P)
+    e1 = U.rel_err(one["dW"].cpu().numpy(), dW2_ref)
+    e2 = U.rel_err(one["dphi"].cpu().numpy(), dx_ref)
     print(f"random-gu-{seed}", dict(dW2=e1, dx=e2))
     assert e1 <= U.TOL and e2 <= U.TOL, (e1, e2)
     assert np.all(one["dphi"].cpu().numpy()[~keep] == 0)
