@@ -244,7 +244,8 @@ def main():
         if chain:   # gate/up output gradient comes from the down GEMM, already compacted
             act_a, act_b = d(p.glu.a), d(p.glu.b)
             out2["g_c"] = None
-            dgu = torch.empty((M, gu.d_out), dtype=torch.bfloat16, device=dev)
+            # float32 hand-off (bf16 in the single-rounding mode)
+            dgu = torch.empty((M, gu.d_out), dtype=lrmoe.glu_grad_dtype(plan), device=dev)
 
     given_scores = None
     if args.score_mode == "random":   # random dropping: seeded scores drawn once, as input
@@ -298,8 +299,13 @@ def main():
             lrmoe.gather_compact(plan2, out["perm"], out["keep"], alpha, None, x, out=out2)
             if gu_events is not None:
                 gu_events[1].record(stream)
-            lrmoe.grouped_backward(plan2, out["perm"], out2["alpha_c"], dgu, out2["phi_c"], W2,
-                                   dW=dW2, dphi=out2["dphi"], ws=ws2, timing=gu_t)
+            if dgu.dtype == torch.float32:
+                lrmoe.grouped_backward_gate_up(plan2, out["perm"], out2["alpha_c"], dgu,
+                                               out2["phi_c"], W2, dW=dW2, dx=out2["dphi"],
+                                               ws=ws2, timing=gu_t)
+            else:
+                lrmoe.grouped_backward(plan2, out["perm"], out2["alpha_c"], dgu, out2["phi_c"],
+                                       W2, dW=dW2, dphi=out2["dphi"], ws=ws2, timing=gu_t)
             return
         if not whole:
             lrmoe.grouped_backward(plan, out["perm"], out["alpha_c"], out["g_c"], out["phi_c"],
@@ -426,6 +432,8 @@ def main():
     # pass per term (exact mode: alpha * (narrower operand) as hi + lo).
     terms_dw = 1 + (args.dw_mode == "exact" or p.dtype != "bf16") + (p.dtype != "bf16")
     terms_dp = 1 if p.dtype == "bf16" else 3
+    if chain:   # gate/up on the float32 hand-off: alpha * dgu (hi + lo) feeds both products
+        terms_dp = terms_dw
     if gu is not None:
         exec_flops = 2.0 * M * gu.d_out * gu.d_in * (terms_dw + terms_dp)
     else:

@@ -173,10 +173,11 @@ lrmoe_status lrmoe_plan_quota_device(int32_t E, const int32_t* expert_ids, int64
                                      int64_t* quotas_out, int64_t* seg_offsets_out,
                                      int64_t* invalid_out, void* stream);
 
-/* Workspace bytes needed by lrmoe_score_select_compact,
- * lrmoe_select_compact and lrmoe_grouped_backward for this problem (one
- * buffer may serve all of them when they run in order on one stream).
- * Validates the problem like the calls that use it. */
+/* Workspace bytes needed by every call of this problem that takes a
+ * workspace (one buffer may serve all of them when they run in order on one
+ * stream).  Validates the problem like the calls that use it.  The size is
+ * returned through bytes_out, so that a bad problem is reported as a status
+ * like everywhere else. */
 lrmoe_status lrmoe_workspace_size(const lrmoe_problem* pb, size_t* bytes_out);
 
 /* Steps 2-4.  Inputs: alpha f32 [P]; g [T, d_out]; phi [P, d_in];
@@ -287,13 +288,16 @@ lrmoe_status lrmoe_grouped_backward(
  * but instead of dphi it writes, for every compacted row j (pair
  * u = perm[j] of expert e), with d = W_e^T g_c[j] before the routing weight:
  *   dgu_c[j] = [ d * b_u * SiLU'(a_u)  |  d * SiLU(a_u) ]
- * SiLU'(a) = s (1 + a (1 - s)), s = sigmoid(a), in float32, each entry
- * rounded once to bf16.  dgu_c is bf16 [M, 2 d_in], gate half first: the
- * gate/up projection's output gradient, already compacted, so that
- * lrmoe_gather_compact (g = g_c = NULL) of that projection's inputs and
- * lrmoe_grouped_backward with g_c = dgu_c and the same perm and alpha_c
- * (alpha applied once, there) finish the chain.  No original-layout dphi is
- * written and none needs zeroing.
+ * SiLU'(a) = s (1 + a (1 - s)), s = sigmoid(a), computed in float32.  dgu_c
+ * is [M, 2 d_in], gate half first: the gate/up projection's output gradient,
+ * already compacted.  Its storage follows pb->dw_mode: float32 (unrounded)
+ * unless dw_mode is LRMOE_DW_BF16, where each entry is rounded once to bf16
+ * (the single-rounding mode, with that mode's error bound).  The chain ends
+ * with lrmoe_gather_compact (g = g_c = NULL) of the gate/up projection's
+ * inputs x, then, with the same perm and alpha_c (alpha applied once,
+ * there), lrmoe_grouped_backward_gate_up on the float32 dgu_c, or
+ * lrmoe_grouped_backward with g_c = dgu_c on the bf16 one.  No
+ * original-layout dphi is written and none needs zeroing.
  *   act_a, act_b  bf16 [P, d_in], pair-indexed like phi.
  * act_a, act_b and dgu_c may be NULL when no pair is kept (M = 0).  bf16
  * storage only (LRMOE_ERR_DTYPE otherwise); other errors as for
@@ -303,6 +307,22 @@ lrmoe_status lrmoe_grouped_backward_glu(
     const void* g_c, const void* phi_c, const void* W, float* dW,
     const void* act_a, const void* act_b, void* dgu_c, void* workspace,
     size_t ws_bytes, void* stream);
+
+/* The gate/up projection's backward at the end of the MLP chain above: the
+ * same products as lrmoe_grouped_backward (dW [E, d_out, d_in] of the gate/up
+ * weight, dx rows perm[j] of [P, d_in], alpha applied once) with the float32
+ * output gradient dgu_c [M, d_out] of lrmoe_grouped_backward_glu (d_out = 2
+ * d_in of the down projection) as g_c, and bf16 x_c [M, d_in] and W
+ * [E, d_out, d_in].  alpha * dgu_c is split into a bf16 high part and
+ * residual (hi only when dw_mode is LRMOE_DW_BF16) that feed both products,
+ * so the gradient handed over keeps float32-level precision.  dx may be NULL
+ * (dW only).  pb->dtype must be LRMOE_BF16 (LRMOE_ERR_DTYPE otherwise);
+ * workspace: lrmoe_workspace_size of pb; other errors as for
+ * lrmoe_grouped_backward. */
+lrmoe_status lrmoe_grouped_backward_gate_up(
+    const lrmoe_problem* pb, const int32_t* perm, const float* alpha_c, const float* dgu_c,
+    const void* x_c, const void* W, float* dW, float* dx, void* workspace, size_t ws_bytes,
+    void* stream);
 
 /* Steps 2-5 in one call: lrmoe_score_select_compact followed by
  * lrmoe_grouped_backward on the same buffers, with the same arguments and
@@ -327,7 +347,9 @@ lrmoe_status lrmoe_pruned_backward(
  *   lrmoe_score_select_compact_timed: [0] score  [1] select+scan  [2] gather
  *   lrmoe_select_compact_timed:       [1] select+scan  [2] gather
  *   lrmoe_grouped_backward_timed,
- *   lrmoe_grouped_backward_glu_timed: [0] operand prologue  [1] grouped GEMM
+ *   lrmoe_grouped_backward_glu_timed,
+ *   lrmoe_grouped_backward_gate_up_timed:
+ *                                     [0] operand prologue  [1] grouped GEMM
  *                                     [2] split-K reduction
  *   lrmoe_pruned_backward_timed:      [0] score  [1] select+scan  [2] gather
  *                                     [3] grouped GEMM  [4] split-K reduction
@@ -385,6 +407,12 @@ lrmoe_status lrmoe_grouped_backward_glu_timed(
     const void* g_c, const void* phi_c, const void* W, float* dW,
     const void* act_a, const void* act_b, void* dgu_c, void* workspace,
     size_t ws_bytes, void* stream, const lrmoe_timing* timing);
+
+/* lrmoe_grouped_backward_gate_up with per-kernel events (timing may be NULL). */
+lrmoe_status lrmoe_grouped_backward_gate_up_timed(
+    const lrmoe_problem* pb, const int32_t* perm, const float* alpha_c, const float* dgu_c,
+    const void* x_c, const void* W, float* dW, float* dx, void* workspace, size_t ws_bytes,
+    void* stream, const lrmoe_timing* timing);
 
 #ifdef __cplusplus
 }

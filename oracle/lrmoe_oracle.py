@@ -46,9 +46,10 @@ Readings where the pages are silent (each also listed in the design notes):
   * the routing weight enters the MLP chain once: the gate/up output gradient
     is formed from W_e^T g before alpha, and the gate/up backward applies
     alpha, as for a projection whose output gradient is given pre-alpha;
-  * that gate/up output gradient is handed to the gate/up backward as a
-    stored tensor in the storage type (one rounding, store()), like every
-    other gradient tensor of a BF16 training step.
+  * that gate/up output gradient goes on to the gate/up backward as the
+    exact float64 value: the pages fix no storage rounding for it (they only
+    say the result returns to the original layout afterwards, [PT]
+    "Compactacao fisica").
 
 Pins: every function here is checked in tests/test_oracle_pins.py against
 something other than itself (brute force of the definition, the pages'
@@ -76,24 +77,6 @@ def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
         return a
     assert a.dtype == np.float32
     return a.astype(np.float64)
-
-
-def store(x: np.ndarray, dtype: str) -> np.ndarray:
-    """float64 values as stored in the storage type: "bf16" rounds to the
-    nearest value with 8 significant bits (ties to the even significand;
-    float32's exponent range, subnormal spacing 2^-133) and returns the
-    uint16 bit patterns; "f32" rounds to float32; "f64" keeps the values.
-    Finite inputs within the float32 range."""
-    if dtype == "f64":
-        return np.asarray(x, dtype=np.float64)
-    if dtype == "f32":
-        return np.asarray(x, dtype=np.float64).astype(np.float32)
-    assert dtype == "bf16"
-    x = np.asarray(x, dtype=np.float64)
-    _, e = np.frexp(x)                                  # |x| = m 2^e, m in [0.5, 1)
-    ulp = np.ldexp(1.0, np.maximum(e - 8, -133))        # spacing of 8-bit significands
-    r = np.rint(x / ulp) * ulp                          # rint: half to even
-    return (r.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
 # ---------------------------------------------------------------- a0: quota
@@ -302,11 +285,10 @@ def pruned_backward(counts, policy, alpha, g, phi, W, row_index, dtype,
         if glu is not None:
             a, b, x, W2 = glu
             dgu_c = glu_chain_grad(seg, perm, g_c, W, a, b, dtype)
-            dgu_s = store(dgu_c, dtype)
             out["dgu_c"] = dgu_c
-            out["dW2"] = weight_grad(seg, alpha_c, dgu_s, x[perm], dtype, E, W2.shape[1],
-                                     W2.shape[2])
-            out["dx"] = input_grad(seg, perm, alpha_c, dgu_s, W2, dtype, P)
+            out["dW2"] = weight_grad(seg, alpha_c, dgu_c, to_f64(x[perm], dtype), "f64", E,
+                                     W2.shape[1], W2.shape[2])
+            out["dx"] = input_grad(seg, perm, alpha_c, dgu_c, to_f64(W2, dtype), "f64", P)
     return out
 
 
@@ -363,7 +345,7 @@ def glu_chain_rows(seg, perm, row_index, g, W, a, b, dtype, js) -> np.ndarray:
 def glu_weight_grad_block(seg, perm, row_index, alpha, g, W, a, b, x, dtype, e: int,
                           o_idx, i_idx) -> np.ndarray:
     """dW2_e[o_idx][:, i_idx] of the chained gate/up projection: the sum over
-    expert e's kept pairs of alpha_u stored(dgu_u)[o] x_u[i], with only the needed
+    expert e's kept pairs of alpha_u dgu_u[o] x_u[i], with only the needed
     gate/up columns of dgu formed (gate column c and up column c both need
     column c of W_e^T g)."""
     s, t = int(seg[e]), int(seg[e + 1])
@@ -377,13 +359,13 @@ def glu_weight_grad_block(seg, perm, row_index, alpha, g, W, a, b, x, dtype, e: 
     dphi = to_f64(g[rows], dtype) @ to_f64(W[e][:, cols], dtype)
     full = silu_glu_grad(dphi, to_f64(a[u][:, cols], dtype), to_f64(b[u][:, cols], dtype))
     pos = np.searchsorted(cols, o_idx % d_in) + np.where(o_idx >= d_in, len(cols), 0)
-    ga = alpha[u].astype(np.float64)[:, None] * to_f64(store(full[:, pos], dtype), dtype)
+    ga = alpha[u].astype(np.float64)[:, None] * full[:, pos]
     return ga.T @ to_f64(x[u][:, i_idx], dtype)
 
 
 def glu_input_grad_rows(counts, keep, row_index, alpha, g, W, a, b, W2, dtype, pairs) -> np.ndarray:
     """dx of the chained gate/up projection for the requested original pair
-    indices: alpha_u W2_e^T stored(dgu_u), zero rows for dropped pairs."""
+    indices: alpha_u W2_e^T dgu_u, zero rows for dropped pairs."""
     offs = np.concatenate([[0], np.cumsum(np.asarray(counts, dtype=np.int64))])
     out = np.zeros((len(pairs), W2.shape[2]))
     expert = np.searchsorted(offs, np.asarray(pairs, dtype=np.int64), side="right") - 1
@@ -394,5 +376,5 @@ def glu_input_grad_rows(counts, keep, row_index, alpha, g, W, a, b, W2, dtype, p
         r = u if row_index is None else int(row_index[u])
         dphi = to_f64(g[r:r + 1], dtype) @ to_f64(W[e], dtype)
         dgu = silu_glu_grad(dphi, to_f64(a[u:u + 1], dtype), to_f64(b[u:u + 1], dtype))
-        out[k] = float(alpha[u]) * (to_f64(W2[e], dtype).T @ to_f64(store(dgu, dtype), dtype)[0])
+        out[k] = float(alpha[u]) * (to_f64(W2[e], dtype).T @ dgu[0])
     return out

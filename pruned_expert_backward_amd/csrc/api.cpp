@@ -85,7 +85,8 @@ size_t round256(size_t n) { return (n + 255) & ~size_t(255); }
 // prologue, then the fp32 partial dW tiles of experts split along K.
 // bf16 storage: alpha times the narrower of g_c / phi_c, as hi + lo planes
 // (exact) or hi only.  float32 storage: hi + lo planes of g_c, alpha*phi_c
-// and W.
+// and W.  g_f32 (lrmoe_grouped_backward_gate_up: float32 g_c, bf16 phi_c and
+// W): hi (+ lo) planes of alpha*g_c, read by both products.
 struct GemmWorkspace {
   bool alpha_on_phi = true;
   size_t a_hi = 0, a_lo = 0, b_hi = 0, b_lo = 0, w_hi = 0, w_lo = 0, partials = 0, total = 0;
@@ -97,10 +98,18 @@ struct GemmWorkspace {
 
 constexpr int kStepK = 32;   // K rows per pipeline step of the GEMM kernel
 
-GemmWorkspace gemm_workspace(const lrmoe_problem* pb, int64_t M) {
+GemmWorkspace gemm_workspace(const lrmoe_problem* pb, int64_t M, bool g_f32 = false) {
   GemmWorkspace w;
   const size_t Mz = (size_t)M;
-  if (pb->dtype == LRMOE_BF16) {
+  if (g_f32) {
+    w.alpha_on_phi = false;
+    const size_t plane = round256(Mz * (size_t)pb->d_out * 2);
+    const bool exact = pb->dw_mode != LRMOE_DW_BF16;
+    w.b_hi = 0;
+    w.b_lo = plane;
+    w.total = exact ? 2 * plane : plane;
+    w.dw_pa = w.dp_pa = exact ? 2 : 1;
+  } else if (pb->dtype == LRMOE_BF16) {
     w.alpha_on_phi = pb->d_in <= pb->d_out;
     const size_t plane = round256(Mz * (size_t)(w.alpha_on_phi ? pb->d_in : pb->d_out) * 2);
     const bool exact = pb->dw_mode == LRMOE_DW_EXACT;
@@ -162,9 +171,12 @@ size_t select_workspace(const Checked& c) {
   return (chunks * kHistBins + 2 * (size_t)kMaxE + 2 * chunks) * sizeof(uint32_t);
 }
 
+// One size for every call of the problem: the selection, the grouped GEMMs,
+// and (bf16 storage) the gate/up variant with a float32 output gradient.
 size_t workspace_bytes(const lrmoe_problem* pb, const Checked& c) {
-  const size_t g = gemm_workspace(pb, c.M).total, sel = select_workspace(c);
-  return g > sel ? g : sel;
+  size_t n = std::max(gemm_workspace(pb, c.M).total, select_workspace(c));
+  if (pb->dtype == LRMOE_BF16) n = std::max(n, gemm_workspace(pb, c.M, true).total);
+  return n;
 }
 
 // Group shape gm x gn (gm * gn = kGroupSlots) over an expert's tile grid with
@@ -270,14 +282,18 @@ struct TimingSlots {
   int prologue = 0, gemm = 1, reduce = 2;
 };
 
+// g_f32: g_c is float32 while phi_c and W are bf16 (the gate/up projection of
+// the MLP chain on the float32 output gradient of the SiLU-GLU epilogue).
 lrmoe_status grouped_backward(const lrmoe_problem* pb, const int32_t* perm, const float* alpha_c,
                               const void* g_c, const void* phi_c, const void* W, float* dW,
                               float* dphi, bool glu, const uint16_t* glu_a,
-                              const uint16_t* glu_b, uint16_t* glu_out, void* workspace,
+                              const uint16_t* glu_b, void* glu_out, void* workspace,
                               size_t ws_bytes, void* stream, const lrmoe_timing* timing,
-                              bool planes_ready = false, TimingSlots ts = TimingSlots()) {
+                              bool planes_ready = false, TimingSlots ts = TimingSlots(),
+                              bool g_f32 = false) {
   Checked c;
   LRMOE_TRY(check_problem(pb, c));
+  if (g_f32 && pb->dtype != LRMOE_BF16) return LRMOE_ERR_DTYPE;
   const int64_t M = c.M;
   LRMOE_TRY(need(alpha_c, M));
   LRMOE_TRY(need(g_c, M));
@@ -292,8 +308,8 @@ lrmoe_status grouped_backward(const lrmoe_problem* pb, const int32_t* perm, cons
     if (M == 0) glu_out = nullptr;   // no input-gradient tile: the plain kernel runs
   }
   if (dphi != nullptr || glu) LRMOE_TRY(need(perm, M));
-  const GemmWorkspace wl = gemm_workspace(pb, M);
-  if (ws_bytes < wl.total) return LRMOE_ERR_WORKSPACE;
+  const GemmWorkspace wl = gemm_workspace(pb, M, g_f32);
+  if (ws_bytes < workspace_bytes(pb, c)) return LRMOE_ERR_WORKSPACE;
   LRMOE_TRY(need(workspace, (int64_t)wl.total));
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
@@ -389,7 +405,20 @@ lrmoe_status grouped_backward(const lrmoe_problem* pb, const int32_t* perm, cons
   const uint16_t* g16 = reinterpret_cast<const uint16_t*>(g_c);
   const uint16_t* p16 = reinterpret_cast<const uint16_t*>(phi_c);
   const uint16_t* w16 = reinterpret_cast<const uint16_t*>(W);
-  if (pb->dtype == LRMOE_BF16) {
+  if (g_f32) {
+    // alpha * g_c (float32) as bf16 hi (+ lo) planes, the A operand of both
+    // products; the input-gradient epilogue then applies no alpha
+    uint16_t* hi = plane(wl.b_hi);
+    uint16_t* lo = wl.dw_pa == 2 ? plane(wl.b_lo) : nullptr;
+    LRMOE_TRY(hip_status(launch_split(LRMOE_F32, g_c, M, d_out, alpha_c, hi, lo, s, heads, kXcds)));
+    ops.dw_a[0] = ops.dp_a[0] = hi;
+    ops.dw_a[1] = ops.dp_a[1] = lo;
+    ops.dw_b[0] = p16;
+    ops.dp_b[0] = w16;
+    ops.dw_pa = ops.dp_pa = wl.dw_pa;
+    ops.dw_pb = ops.dp_pb = 1;
+    ops.dp_alpha_folded = 1;
+  } else if (pb->dtype == LRMOE_BF16) {
     const bool exact = pb->dw_mode == LRMOE_DW_EXACT;
     uint16_t* hi = plane(wl.b_hi);
     uint16_t* lo = exact ? plane(wl.b_lo) : nullptr;
@@ -434,6 +463,7 @@ lrmoe_status grouped_backward(const lrmoe_problem* pb, const int32_t* perm, cons
   ops.glu_a = glu_a;
   ops.glu_b = glu_b;
   ops.glu_out = glu_out;
+  ops.glu_f32 = pb->dw_mode != LRMOE_DW_BF16;   // exact modes hand dgu on unrounded
   LRMOE_TRY(mark(timing, false, ts.gemm, s));
   LRMOE_TRY(hip_status(launch_grouped_backward(t, ops, perm, alpha_c, dW, dphi, d_out, d_in,
                                                (int32_t)pb->P, s)));
@@ -540,7 +570,7 @@ lrmoe_status gather_backward(const lrmoe_problem* pb, const int32_t* perm, const
   LRMOE_TRY(need(g, c.M > 0 ? pb->T : 0));   // the GEMM needs g rows: no NULL g here
   LRMOE_TRY(need(g_c, c.M));
   const GemmWorkspace wl = gemm_workspace(pb, c.M);
-  if (ws_bytes < wl.total) return LRMOE_ERR_WORKSPACE;
+  if (ws_bytes < workspace_bytes(pb, c)) return LRMOE_ERR_WORKSPACE;
   LRMOE_TRY(need(workspace, (int64_t)wl.total));
   GatherPlanes planes;
   const bool fused = pb->dtype == LRMOE_BF16;
@@ -802,9 +832,26 @@ lrmoe_status lrmoe_grouped_backward_glu_timed(const lrmoe_problem* pb, const int
   if (pb->dtype != LRMOE_BF16) return LRMOE_ERR_DTYPE;
   return grouped_backward(pb, perm, alpha_c, g_c, phi_c, W, dW, nullptr, true,
                           reinterpret_cast<const uint16_t*>(act_a),
-                          reinterpret_cast<const uint16_t*>(act_b),
-                          reinterpret_cast<uint16_t*>(dgu_c), workspace, ws_bytes, stream,
-                          timing);
+                          reinterpret_cast<const uint16_t*>(act_b), dgu_c, workspace, ws_bytes,
+                          stream, timing);
+}
+
+lrmoe_status lrmoe_grouped_backward_gate_up(const lrmoe_problem* pb, const int32_t* perm,
+                                            const float* alpha_c, const float* dgu_c,
+                                            const void* x_c, const void* W, float* dW, float* dx,
+                                            void* workspace, size_t ws_bytes, void* stream) {
+  return lrmoe_grouped_backward_gate_up_timed(pb, perm, alpha_c, dgu_c, x_c, W, dW, dx, workspace,
+                                              ws_bytes, stream, nullptr);
+}
+
+lrmoe_status lrmoe_grouped_backward_gate_up_timed(const lrmoe_problem* pb, const int32_t* perm,
+                                                  const float* alpha_c, const float* dgu_c,
+                                                  const void* x_c, const void* W, float* dW,
+                                                  float* dx, void* workspace, size_t ws_bytes,
+                                                  void* stream, const lrmoe_timing* timing) {
+  return grouped_backward(pb, perm, alpha_c, dgu_c, x_c, W, dW, dx, false, nullptr, nullptr,
+                          nullptr, workspace, ws_bytes, stream, timing, false, TimingSlots(),
+                          true);
 }
 
 }  // extern "C"

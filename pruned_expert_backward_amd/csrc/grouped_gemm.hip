@@ -59,9 +59,13 @@
 //     queues.  An expert whose kept rows exceed one K chunk has its dW split
 //     along K: each chunk writes an fp32 partial tile and a second kernel
 //     sums them in chunk order, so the result does not depend on timing.
-//   * SiLU-GLU variant (GLU = true): the input-gradient tiles write the
-//     gate/up output gradient of the expert MLP, compacted, instead of dphi
-//     (see Tile::glu_epilogue).
+//   * SiLU-GLU variant (GLU = 1: bf16 output, 2: float32 output): the
+//     input-gradient tiles write the gate/up output gradient of the expert
+//     MLP, compacted, instead of dphi (see Tile::glu_epilogue).
+//   * The gate/up projection behind it reads that gradient as float32: a
+//     prologue splits alpha * g_c into bf16 hi + lo planes that feed both
+//     products (PA = 2 for the input gradient too), and the input-gradient
+//     epilogue then applies no alpha (dp_alpha_folded).
 #include "lrmoe_internal.h"
 
 namespace lrmoe {
@@ -263,7 +267,7 @@ constexpr int kPermBytes = BM * 8;   // dphi epilogue: destination row + alpha p
 // The matrix core always has independent MFMAs queued while fragments and
 // stages move, and the global loads trickle out between MFMAs instead of
 // stalling the wave in a burst.
-template <bool IS_DW, int PA, int PB, int NS, bool GLU = false>
+template <bool IS_DW, int PA, int PB, int NS, int GLU = 0>
 struct Tile {
   static constexpr bool A_MC = IS_DW;
   static constexpr int kStage = (PA + PB) * kPlaneBytes;
@@ -517,7 +521,7 @@ struct Tile {
       const bool ok = m0 + tid < q;
       const int32_t u = ok ? args.perm[seg + m0 + tid] : -1;
       s_perm[tid] = (uint32_t)u < (uint32_t)args.P ? u : -1;   // perm holds pair indices < P
-      s_alpha[tid] = ok ? args.alpha_c[seg + m0 + tid] : 0.f;
+      s_alpha[tid] = !ok ? 0.f : args.ops.dp_alpha_folded ? 1.f : args.alpha_c[seg + m0 + tid];
     }
   }
 
@@ -588,13 +592,65 @@ struct Tile {
     up = __builtin_bit_cast(u32x2, uo);
   }
 
+  // The same in float32, unrounded: gate and up gradients of the quad.
+  __device__ __forceinline__ static void glu_quad_f32(u32x2 av, u32x2 bv, const float (&d)[4],
+                                                      f32x4& gate, f32x4& up) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t aw = av[k >> 1], bw = bv[k >> 1];
+      const float x = __uint_as_float((k & 1) ? (aw & 0xFFFF0000u) : (aw << 16));
+      const float y = __uint_as_float((k & 1) ? (bw & 0xFFFF0000u) : (bw << 16));
+      const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.44269504f * x));
+      gate[k] = d[k] * y * (sg * (1.f + x * (1.f - sg)));
+      up[k] = d[k] * (x * sg);
+    }
+  }
+
   __device__ __forceinline__ void glu_store(const Args& args, int32_t u, int64_t j, int ln,
                                             int ncols, const f32x16 (&acc)[kMB][kNB], int a,
                                             const GluRow& r) const {
     const int d_in = args.d_in;
-    uint16_t* gate = args.ops.glu_out + j * (2 * (int64_t)d_in) + n0;
-    uint16_t* up = gate + d_in;
     const bool hi = ln >= 32;
+    if constexpr (GLU == 2) {
+      // float32 output: each lane's register quad is 4 consecutive columns of
+      // its own row, 16 bytes, stored as they are (no partner exchange)
+      float* gate = reinterpret_cast<float*>(args.ops.glu_out) + j * (2 * (int64_t)d_in) + n0;
+      float* up = gate + d_in;
+#pragma unroll
+      for (int b = 0; b < kNB; ++b)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          u32x2 qa[2], qb[2];
+          {
+            const u32x4 A = r.a[b][h], B = r.b[b][h];
+            const uint32_t ra0 = swap32(hi ? A[0] : A[2], ln), ra1 = swap32(hi ? A[1] : A[3], ln);
+            const uint32_t rb0 = swap32(hi ? B[0] : B[2], ln), rb1 = swap32(hi ? B[1] : B[3], ln);
+            qa[0] = hi ? u32x2{ra0, ra1} : u32x2{A[0], A[1]};
+            qa[1] = hi ? u32x2{A[2], A[3]} : u32x2{ra0, ra1};
+            qb[0] = hi ? u32x2{rb0, rb1} : u32x2{B[0], B[1]};
+            qb[1] = hi ? u32x2{B[2], B[3]} : u32x2{rb0, rb1};
+          }
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int g = 2 * h + t;
+            float d[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(d[k]) : "a"(acc[a][b][4 * g + k]));
+            f32x4 gv, uv;
+            glu_quad_f32(qa[t], qb[t], d, gv, uv);
+            // columns of register quad g: 8 g + 4 (lane / 32) .. + 3 of block b
+            const int col = wn * WTN + b * 32 + 8 * g + 4 * (ln >> 5);
+            if (u >= 0 && col < ncols) {
+              *reinterpret_cast<f32x4*>(gate + col) = gv;
+              *reinterpret_cast<f32x4*>(up + col) = uv;
+            }
+          }
+        }
+      return;
+    }
+    uint16_t* gate = reinterpret_cast<uint16_t*>(args.ops.glu_out) + j * (2 * (int64_t)d_in) + n0;
+    uint16_t* up = gate + d_in;
 #pragma unroll
     for (int b = 0; b < kNB; ++b)
 #pragma unroll
@@ -694,7 +750,7 @@ struct Tile {
       const int tile = (m0 / BM) * tab.tiles_n + n0 / BN;
       part = args.ops.partials + ((partial_base(tab, e) + (int64_t)tile * chunks + chunk) << 16);
     }
-    if constexpr (GLU) {   // SiLU-GLU chain: no dphi, no alpha
+    if constexpr (GLU != 0) {   // SiLU-GLU chain: no dphi, no alpha
       glu_epilogue(args, prm, acc);
       return;
     }
@@ -777,7 +833,7 @@ struct Cfg {
 // next tile's first loads are issued before the finished tile's stores, so
 // the store drain overlaps the next load latency.  Every workgroup exits when
 // its queue's counter passes the queue length.
-template <int DW_PA, int DW_PB, int DP_PA, int DP_PB, bool GLU>
+template <int DW_PA, int DW_PB, int DP_PA, int DP_PB, int GLU>
 __global__ __launch_bounds__(kThreads, 1) void grouped_backward_kernel(Args args, GemmTable tab) {
   using C = Cfg<DW_PA, DW_PB, DP_PA, DP_PB>;
   using DwTile = Tile<true, DW_PA, DW_PB, C::NS_DW>;
@@ -838,7 +894,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_backward_kernel(Args args
   }
 }
 
-template <int DW_PA, int DW_PB, int DP_PA, int DP_PB, bool GLU = false>
+template <int DW_PA, int DW_PB, int DP_PA, int DP_PB, int GLU = 0>
 hipError_t launch(const Args& args, const GemmTable& tab, hipStream_t s) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -1002,10 +1058,15 @@ hipError_t launch_grouped_backward(const GemmTable& tab, const GemmOperands& ops
   const Args args{ops, alpha_c, perm, dW, dphi, d_out, d_in, P};
   const int key = ops.dw_pa * 1000 + ops.dw_pb * 100 + ops.dp_pa * 10 + ops.dp_pb;
   if (ops.glu_out != nullptr) {   // SiLU-GLU chain: bf16 storage only
-    switch (key) {
-      case 1211: return launch<1, 2, 1, 1, true>(args, tab, s);
-      case 2111: return launch<2, 1, 1, 1, true>(args, tab, s);
-      case 1111: return launch<1, 1, 1, 1, true>(args, tab, s);
+    if (ops.glu_f32) {            // exact weight gradient, float32 hand-off
+      switch (key) {
+        case 1211: return launch<1, 2, 1, 1, 2>(args, tab, s);
+        case 2111: return launch<2, 1, 1, 1, 2>(args, tab, s);
+        default: return hipErrorInvalidValue;
+      }
+    }
+    switch (key) {                // single rounding, bf16 hand-off
+      case 1111: return launch<1, 1, 1, 1, 1>(args, tab, s);
       default: return hipErrorInvalidValue;
     }
   }
@@ -1013,6 +1074,7 @@ hipError_t launch_grouped_backward(const GemmTable& tab, const GemmOperands& ops
     case 1211: return launch<1, 2, 1, 1>(args, tab, s);   // bf16, alpha folded into phi
     case 2111: return launch<2, 1, 1, 1>(args, tab, s);   // bf16, alpha folded into g
     case 1111: return launch<1, 1, 1, 1>(args, tab, s);   // bf16, single rounding
+    case 2121: return launch<2, 1, 2, 1>(args, tab, s);   // float32 g_c, bf16 phi_c and W
     case 2222: return launch<2, 2, 2, 2>(args, tab, s);   // float32 storage
     default: return hipErrorInvalidValue;
   }

@@ -90,10 +90,14 @@ struct GemmOperands {
   // writing alpha * dphi, write the gate/up output gradient of each kept
   // pair from its saved pre-activations a = glu_a[u], b = glu_b[u] ([P,
   // d_in] bf16, u = perm[j]): glu_out[j] = [dphi*b*silu'(a), dphi*silu(a)]
-  // ([M, 2 d_in] bf16), dphi before alpha.
+  // ([M, 2 d_in], float32 if glu_f32 else bf16), dphi before alpha.
   const uint16_t* glu_a;
   const uint16_t* glu_b;
-  uint16_t* glu_out;
+  void* glu_out;
+  int32_t glu_f32;
+  // 1: the input-gradient A planes already carry alpha (alpha * g_c split),
+  // so the epilogue does not scale the rows again.
+  int32_t dp_alpha_folded;
 };
 
 // Number of K chunks of an expert with q kept rows.

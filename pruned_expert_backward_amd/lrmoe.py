@@ -34,7 +34,8 @@ EXPORTS = ["lrmoe_abi_version", "lrmoe_status_string", "lrmoe_plan_quota",
            "lrmoe_mask_alpha", "lrmoe_plan_quota_device", "lrmoe_grouped_backward_glu",
            "lrmoe_grouped_backward_glu_timed", "lrmoe_pruned_backward",
            "lrmoe_pruned_backward_timed", "lrmoe_gather_backward",
-           "lrmoe_gather_backward_timed"]
+           "lrmoe_gather_backward_timed", "lrmoe_grouped_backward_gate_up",
+           "lrmoe_grouped_backward_gate_up_timed"]
 TIMING_SLOTS = 8
 
 
@@ -120,6 +121,11 @@ def lib() -> C.CDLL:
     L.lrmoe_grouped_backward_glu_timed.restype = C.c_int
     L.lrmoe_grouped_backward_glu_timed.argtypes = ([C.POINTER(Problem)] + [_P] * 10 +
                                                    [C.c_size_t, _P, C.POINTER(Timing)])
+    L.lrmoe_grouped_backward_gate_up.restype = C.c_int
+    L.lrmoe_grouped_backward_gate_up.argtypes = [C.POINTER(Problem)] + [_P] * 8 + [C.c_size_t, _P]
+    L.lrmoe_grouped_backward_gate_up_timed.restype = C.c_int
+    L.lrmoe_grouped_backward_gate_up_timed.argtypes = ([C.POINTER(Problem)] + [_P] * 8 +
+                                                       [C.c_size_t, _P, C.POINTER(Timing)])
     if L.lrmoe_abi_version() != ABI_VERSION:
         raise RuntimeError("liblrmoe ABI version mismatch; rebuild the library")
     _lib_handle = L
@@ -404,16 +410,22 @@ def gather_backward(plan: Plan, perm, keep, alpha, g, phi, W, g_row_index=None,
     return out
 
 
+def glu_grad_dtype(plan: Plan) -> torch.dtype:
+    """Storage of the SiLU-GLU chain's hand-off gradient: float32, or bf16 in
+    the single-rounding dW mode."""
+    return torch.bfloat16 if plan.dw_mode == DW_BF16 else torch.float32
+
+
 def grouped_backward_glu(plan: Plan, perm, alpha_c, g_c, phi_c, W, act_a, act_b, dW=None,
                          dgu_c=None, ws=None, timing: Optional["KernelTimer"] = None):
     """Down projection's dW and, through the SiLU-GLU backward, the gate/up
     output gradient of the kept pairs, compacted: returns (dW, dgu_c) with
-    dgu_c bf16 [M, 2 d_in] (gate half first, before alpha)."""
+    dgu_c [M, 2 d_in] (gate half first, before alpha) in glu_grad_dtype."""
     dev = W.device
     if dW is None:
         dW = _empty((plan.E, plan.d_out, plan.d_in), torch.float32, dev)
     if dgu_c is None:
-        dgu_c = _empty((plan.M, 2 * plan.d_in), torch.bfloat16, dev)
+        dgu_c = _empty((plan.M, 2 * plan.d_in), glu_grad_dtype(plan), dev)
     if ws is None:
         ws = workspace(plan, dev)
     args = (C.byref(plan.struct), _ptr(perm), _ptr(alpha_c), _ptr(g_c), _ptr(phi_c), _ptr(W),
@@ -424,6 +436,26 @@ def grouped_backward_glu(plan: Plan, perm, alpha_c, g_c, phi_c, W, act_a, act_b,
     else:
         check("lrmoe_grouped_backward_glu", lib().lrmoe_grouped_backward_glu(*args))
     return dW, dgu_c
+
+
+def grouped_backward_gate_up(plan: Plan, perm, alpha_c, dgu_c, x_c, W, dW=None, dx=None,
+                             ws=None, timing: Optional["KernelTimer"] = None) -> torch.Tensor:
+    """The gate/up projection's backward on the float32 output gradient of
+    grouped_backward_glu: dW [E, d_out, d_in] (returned) and the kept rows of
+    dx (in place)."""
+    dev = W.device
+    if dW is None:
+        dW = _empty((plan.E, plan.d_out, plan.d_in), torch.float32, dev)
+    if ws is None:
+        ws = workspace(plan, dev)
+    args = (C.byref(plan.struct), _ptr(perm), _ptr(alpha_c), _ptr(dgu_c), _ptr(x_c), _ptr(W),
+            _ptr(dW), _ptr(dx), _ptr(ws), ws.numel(), _stream())
+    if timing is not None:
+        check("lrmoe_grouped_backward_gate_up_timed",
+              lib().lrmoe_grouped_backward_gate_up_timed(*args, C.byref(timing.next_slots())))
+    else:
+        check("lrmoe_grouped_backward_gate_up", lib().lrmoe_grouped_backward_gate_up(*args))
+    return dW
 
 
 def glu_chain_backward(plan: Plan, plan2: Plan, alpha, g, phi, W, act_a, act_b, x, W2,
@@ -447,8 +479,12 @@ def glu_chain_backward(plan: Plan, plan2: Plan, alpha, g, phi, W, act_a, act_b, 
                         phi_row_index=x_row_index)
     out["x_c"] = c2["phi_c"]
     out["dx"] = c2["dphi"]
-    out["dW2"] = grouped_backward(plan2, out["perm"], c2["alpha_c"], out["dgu_c"], c2["phi_c"],
-                                  W2, dphi=c2["dphi"], ws=ws)
+    if out["dgu_c"].dtype == torch.float32:   # unrounded hand-off
+        out["dW2"] = grouped_backward_gate_up(plan2, out["perm"], c2["alpha_c"], out["dgu_c"],
+                                              c2["phi_c"], W2, dx=c2["dphi"], ws=ws)
+    else:                                     # single-rounding mode: bf16 hand-off
+        out["dW2"] = grouped_backward(plan2, out["perm"], c2["alpha_c"], out["dgu_c"],
+                                      c2["phi_c"], W2, dphi=c2["dphi"], ws=ws)
     return out
 
 

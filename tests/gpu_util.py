@@ -135,3 +135,25 @@ def compare_full(p, quotas, out, dw_mode=lrmoe.DW_EXACT, scores_in=None, score_m
     dphi_gpu = out["dphi"].cpu().numpy()
     assert np.all(dphi_gpu[~keep_used] == 0)
     return errs, same
+
+
+def check_dgu(got, ref):
+    """The chain's compacted gate/up output gradient against the oracle's
+    float64 value.  float32 hand-off: float32 arithmetic (the hardware exp2
+    and reciprocal in the sigmoid, about one ulp each) within 2^-16 of each
+    entry, plus 2e-5 max|ref| for the float32 sum of W^T g.  bf16 hand-off
+    (single-rounding mode): one rounding to 8 significant bits on top,
+    2^-8 of each entry."""
+    if got.dtype == torch.bfloat16:
+        v = (host_bits(got).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        rel = 2.0 ** -8
+    else:
+        assert got.dtype == torch.float32
+        v = got.cpu().numpy().astype(np.float64)
+        rel = 2.0 ** -16
+    if ref.size == 0:
+        return 0.0
+    bound = rel * np.abs(ref) + 2e-5 * np.abs(ref).max()
+    excess = np.abs(v - ref) - bound
+    assert np.all(excess <= 0), float(excess.max())
+    return float(np.abs(v - ref).max() / max(np.abs(ref).max(), 1e-300))

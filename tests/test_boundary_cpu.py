@@ -169,15 +169,40 @@ def test_row_index_needs_rows_to_index():
 def test_workspace_size_and_check():
     p = plan(counts=(40, 20, 30), quotas=(30, 10, 20), d_out=64, d_in=32)
     n = p.workspace_bytes()
-    # exact mode, bf16: alpha * phi (the narrower operand) as hi + lo planes,
-    # no split-K partials at this size, 256 bytes of GEMM queue counters
-    plane = (60 * 32 * 2 + 255) // 256 * 256
-    assert n == 2 * plane + 256
-    f = L.lib().lrmoe_grouped_backward
-    assert f(C.byref(p.struct), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n - 1, None) == 6
-    assert f(C.byref(p.struct), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, n, None) == 1
+    # exact mode, bf16: the plain grouped backward keeps alpha * phi (the
+    # narrower operand) as hi + lo planes; the gate/up variant (float32 g_c)
+    # alpha * g_c as hi + lo planes; no split-K partials at this size, 256
+    # bytes of GEMM queue counters.  One size serves every call: the larger.
+    plane_phi = (60 * 32 * 2 + 255) // 256 * 256
+    plane_g = (60 * 64 * 2 + 255) // 256 * 256
+    assert n == max(2 * plane_phi, 2 * plane_g) + 256
+    for f in (L.lib().lrmoe_grouped_backward, L.lib().lrmoe_grouped_backward_gate_up):
+        assert f(C.byref(p.struct), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n - 1,
+                 None) == 6
+        assert f(C.byref(p.struct), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, n, None) == 1
     p1 = plan(counts=(40, 20, 30), quotas=(30, 10, 20), d_out=64, d_in=32, dw_mode=L.DW_BF16)
-    assert p1.workspace_bytes() == plane + 256
+    assert p1.workspace_bytes() == max(plane_phi, plane_g) + 256
+
+
+def test_grouped_backward_gate_up_validation():
+    """The MLP chain's gate/up call: bf16 x and W only (the float32 output
+    gradient is the only float32 operand); the usual pointer rules."""
+    f = L.lib().lrmoe_grouped_backward_gate_up
+    p = plan()
+    n = p.workspace_bytes()
+    ok = [FAKE] * 6 + [None, FAKE, n, None]   # perm alpha_c dgu_c x_c W dW dx ws
+    assert f(C.byref(plan(dtype=L.F32).struct), *ok) == 5
+    for i in (1, 2, 3, 4, 5, 7):
+        a = list(ok)
+        a[i] = None
+        assert f(C.byref(p.struct), *a) == 1, i
+    a = list(ok)
+    a[0], a[6] = None, FAKE        # perm needed when dx is requested
+    assert f(C.byref(p.struct), *a) == 1
+    a = list(ok)
+    a[2] = FAKE + 4
+    assert f(C.byref(p.struct), *a) == 4
+    assert f(None, *ok) == 1
 
 
 def test_select_workspace_for_large_experts():
