@@ -75,7 +75,9 @@ typedef enum {
   LRMOE_ERR_ALIGN = 4,     /* pointer or row length misaligned               */
   LRMOE_ERR_DTYPE = 5,     /* unknown storage type                           */
   LRMOE_ERR_WORKSPACE = 6, /* workspace smaller than lrmoe_workspace_size    */
-  LRMOE_ERR_HIP = 7        /* a HIP runtime call or launch failed            */
+  LRMOE_ERR_HIP = 7,       /* a HIP runtime call or launch failed            */
+  LRMOE_ERR_SCRATCH = 8    /* more scratch than the static buffer holds
+                              (lrmoe_score_select_compact_noalloc)           */
 } lrmoe_status;
 
 typedef enum { LRMOE_F32 = 0, LRMOE_BF16 = 1 } lrmoe_dtype;
@@ -202,6 +204,27 @@ lrmoe_status lrmoe_score_select_compact(
     const void* g, const void* phi, float* scores, uint8_t* keep,
     int32_t* seg_offsets, int32_t* perm, void* g_c, void* phi_c, float* alpha_c,
     float* dphi_zero, void* workspace, size_t ws_bytes, void* stream);
+
+/* lrmoe_score_select_compact for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): no workspace argument.  The selection's scratch -- the
+ * first-digit histograms, thresholds and chunk counts of experts with more
+ * than 24576 pairs -- lives in a static device array of the library,
+ * 8 MiB, which every GPU the library runs on holds until the process ends.
+ * Problems whose large experts need more (about 8.3 million pairs in
+ * experts above 24576 pairs) are rejected with LRMOE_ERR_SCRATCH before
+ * anything is launched.  The call allocates nothing; on its first call on a
+ * device it looks up that device's copy of the array (the current device,
+ * which `stream` must belong to).  Nothing in the scratch needs to start at
+ * zero: every call writes what it later reads.  All calls on one GPU share
+ * that GPU's array, so calls that overlap in time on one GPU (different
+ * streams, or different host threads) race and must not be issued.
+ * Arguments, results and other errors as for lrmoe_score_select_compact. */
+lrmoe_status lrmoe_score_select_compact_noalloc(
+    const lrmoe_problem* pb, const int32_t* g_row_index, const float* alpha,
+    const void* g, const void* phi, float* scores, uint8_t* keep,
+    int32_t* seg_offsets, int32_t* perm, void* g_c, void* phi_c, float* alpha_c,
+    float* dphi_zero, void* stream);
 
 /* Steps 3-4 on caller-provided scores (float32 [P], finite; -0.0 counts as
  * 0.0), for scoring rules other than LRM.  Arguments as above. */

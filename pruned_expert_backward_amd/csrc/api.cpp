@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <numeric>
 #include <vector>
 
@@ -200,6 +201,33 @@ void group_shape(int nt, int pref, int32_t& gm, int32_t& gn) {
 
 lrmoe_status hip_status(hipError_t e) { return e == hipSuccess ? LRMOE_OK : LRMOE_ERR_HIP; }
 
+// ---- Selection scratch for callers that cannot allocate
+// (lrmoe_score_select_compact_noalloc).  A file-scope device array: every GPU
+// the library runs on holds its own copy of kScratchBytes until the process
+// ends.  In host code `scratch` names a host-side stand-in, not device
+// memory, so kernels get the address hipGetSymbolAddress returns for the
+// current device, looked up once per device and kept.
+constexpr size_t kScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+lrmoe_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LRMOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return LRMOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LRMOE_OK;
+}
+
 // Records the caller's event of one timing slot (if any) on the stream.
 lrmoe_status mark(const lrmoe_timing* t, bool after, int slot, hipStream_t s) {
   if (t == nullptr) return LRMOE_OK;
@@ -215,7 +243,8 @@ lrmoe_status select_compact(const lrmoe_problem* pb, bool compute_scores, const 
                             int32_t* seg_offsets, int32_t* perm, void* g_c, void* phi_c,
                             float* alpha_c, float* dphi_zero, void* workspace, size_t ws_bytes,
                             void* stream, const lrmoe_timing* timing, bool gather = true,
-                            const GatherPlanes& planes = GatherPlanes()) {
+                            const GatherPlanes& planes = GatherPlanes(),
+                            bool use_scratch = false) {
   Checked c;
   LRMOE_TRY(check_problem(pb, c));
   const int64_t P = pb->P, M = c.M;
@@ -242,7 +271,11 @@ lrmoe_status select_compact(const lrmoe_problem* pb, bool compute_scores, const 
     LRMOE_TRY(optional(dphi_zero));
   }
   const size_t ws_need = select_workspace(c);   // 0 unless an expert is large
-  if (ws_need > 0) {
+  if (use_scratch) {   // the library's static scratch instead of a workspace
+    if (ws_need > kScratchBytes) return LRMOE_ERR_SCRATCH;
+    LRMOE_TRY(scratch_address(&workspace));
+    ws_bytes = kScratchBytes;
+  } else if (ws_need > 0) {
     LRMOE_TRY(need(workspace, 1));
     if (ws_bytes < ws_need) return LRMOE_ERR_WORKSPACE;
   }
@@ -609,6 +642,7 @@ const char* lrmoe_status_string(lrmoe_status s) {
     case LRMOE_ERR_DTYPE: return "unknown storage dtype";
     case LRMOE_ERR_WORKSPACE: return "workspace too small";
     case LRMOE_ERR_HIP: return "HIP runtime error";
+    case LRMOE_ERR_SCRATCH: return "problem needs more selection scratch than the library's static buffer holds";
   }
   return "unknown status";
 }
@@ -699,6 +733,17 @@ lrmoe_status lrmoe_score_select_compact_timed(const lrmoe_problem* pb, const int
                                               const lrmoe_timing* timing) {
   return select_compact(pb, true, nullptr, g_row_index, alpha, g, phi, scores, keep, seg_offsets,
                         perm, g_c, phi_c, alpha_c, dphi_zero, workspace, ws_bytes, stream, timing);
+}
+
+lrmoe_status lrmoe_score_select_compact_noalloc(const lrmoe_problem* pb,
+                                                const int32_t* g_row_index, const float* alpha,
+                                                const void* g, const void* phi, float* scores,
+                                                uint8_t* keep, int32_t* seg_offsets,
+                                                int32_t* perm, void* g_c, void* phi_c,
+                                                float* alpha_c, float* dphi_zero, void* stream) {
+  return select_compact(pb, true, nullptr, g_row_index, alpha, g, phi, scores, keep, seg_offsets,
+                        perm, g_c, phi_c, alpha_c, dphi_zero, nullptr, 0, stream, nullptr, true,
+                        GatherPlanes(), true);
 }
 
 lrmoe_status lrmoe_select_compact(const lrmoe_problem* pb, const float* scores,

@@ -25,7 +25,7 @@ ABI_VERSION = 4
 
 STATUS = {0: "LRMOE_OK", 1: "LRMOE_ERR_NULL", 2: "LRMOE_ERR_INVALID", 3: "LRMOE_ERR_SHAPE",
           4: "LRMOE_ERR_ALIGN", 5: "LRMOE_ERR_DTYPE", 6: "LRMOE_ERR_WORKSPACE",
-          7: "LRMOE_ERR_HIP"}
+          7: "LRMOE_ERR_HIP", 8: "LRMOE_ERR_SCRATCH"}
 
 EXPORTS = ["lrmoe_abi_version", "lrmoe_status_string", "lrmoe_plan_quota",
            "lrmoe_workspace_size", "lrmoe_score_select_compact", "lrmoe_select_compact",
@@ -35,7 +35,7 @@ EXPORTS = ["lrmoe_abi_version", "lrmoe_status_string", "lrmoe_plan_quota",
            "lrmoe_grouped_backward_glu_timed", "lrmoe_pruned_backward",
            "lrmoe_pruned_backward_timed", "lrmoe_gather_backward",
            "lrmoe_gather_backward_timed", "lrmoe_grouped_backward_gate_up",
-           "lrmoe_grouped_backward_gate_up_timed"]
+           "lrmoe_grouped_backward_gate_up_timed", "lrmoe_score_select_compact_noalloc"]
 TIMING_SLOTS = 8
 
 
@@ -126,6 +126,8 @@ def lib() -> C.CDLL:
     L.lrmoe_grouped_backward_gate_up_timed.restype = C.c_int
     L.lrmoe_grouped_backward_gate_up_timed.argtypes = ([C.POINTER(Problem)] + [_P] * 8 +
                                                        [C.c_size_t, _P, C.POINTER(Timing)])
+    L.lrmoe_score_select_compact_noalloc.restype = C.c_int
+    L.lrmoe_score_select_compact_noalloc.argtypes = [C.POINTER(Problem)] + [_P] * 13
     if L.lrmoe_abi_version() != ABI_VERSION:
         raise RuntimeError("liblrmoe ABI version mismatch; rebuild the library")
     _lib_handle = L
@@ -282,6 +284,20 @@ def score_select_compact(plan: Plan, alpha, g, phi, g_row_index=None, out=None, 
     else:
         st = L.lrmoe_select_compact(C.byref(plan.struct), _ptr(scores), *common, *tail)
         check("lrmoe_select_compact", st)
+    return out
+
+
+def score_select_compact_noalloc(plan: Plan, alpha, g, phi, g_row_index=None, out=None) -> dict:
+    """score_select_compact through the entry point that takes no workspace
+    (its selection scratch is the library's static device buffer)."""
+    if out is None:
+        out = alloc_select_outputs(plan, phi.device)
+    st = lib().lrmoe_score_select_compact_noalloc(
+        C.byref(plan.struct), _ptr(g_row_index), _ptr(alpha), _ptr(g), _ptr(phi),
+        _ptr(out["scores"]), _ptr(out["keep"]), _ptr(out["seg_offsets"]), _ptr(out["perm"]),
+        _ptr(out["g_c"]), _ptr(out["phi_c"]), _ptr(out["alpha_c"]), _ptr(out.get("dphi")),
+        _stream())
+    check("lrmoe_score_select_compact_noalloc", st)
     return out
 
 

@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert lib.lrmoe_abi_version() == L.ABI_VERSION
-    for s in range(8):
+    for s in range(9):
         assert lib.lrmoe_status_string(s)
 
 
@@ -348,3 +348,23 @@ def test_plan_quota_device_validation():
     assert f(4, None, 10, C.byref(ok), FAKE, FAKE, FAKE, None, None) == 1
     assert f(4, FAKE, 10, C.byref(ok), FAKE + 4, FAKE, FAKE, None, None) == 4
     assert f(4, FAKE, 10, C.byref(ok), FAKE, FAKE, FAKE, FAKE + 8, None) == 4
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch():
+    """The entry point without a workspace holds the selection scratch of
+    large experts in an 8 MiB static device buffer: a problem needing more
+    (here 550 first-digit histograms of 16 KiB for a 9-million-pair expert)
+    is rejected before any HIP call; so are the usual bad arguments."""
+    f = L.lib().lrmoe_score_select_compact_noalloc
+    big = plan(counts=(9_000_000, 5), quotas=(7_200_000, 4), d_out=8, d_in=8)
+    args = [None] + [FAKE] * 11 + [None, None]   # row alpha g phi scores keep seg perm g_c phi_c alpha_c dphi
+    assert f(C.byref(big.struct), *args) == 8
+    assert L.lib().lrmoe_status_string(8)
+    p = plan()
+    a = list(args)
+    a[1] = None                                   # alpha
+    assert f(C.byref(p.struct), *a) == 1
+    a = list(args)
+    a[5] = FAKE + 4                               # keep misaligned
+    assert f(C.byref(p.struct), *a) == 4
+    assert f(None, *args) == 1
