@@ -174,7 +174,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=4,
                     help="workload (4: GLM4.5 20x batch-pressure share, the largest)")
-    ap.add_argument("--dw-mode", choices=["exact", "bf16"], default="exact")
+    ap.add_argument("--dw-mode", choices=["exact", "bf16", "f16"], default="exact",
+                    help="weight-gradient folding of alpha: exact (bf16 hi + lo, two "
+                         "passes), bf16 (one rounding), f16 (one pass on float16 planes)")
     ap.add_argument("--score-mode", choices=["lrm", "grad-sqnorm", "grad-l1", "random"],
                     default="lrm", help="scoring rule (the method, or an ablation baseline)")
     ap.add_argument("--path", choices=["compacted", "masked-dense", "glu-chain"],
@@ -213,7 +215,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     dtc = lrmoe.BF16 if p.dtype == "bf16" else lrmoe.F32
-    mode = lrmoe.DW_EXACT if args.dw_mode == "exact" else lrmoe.DW_BF16
+    mode = {"exact": lrmoe.DW_EXACT, "bf16": lrmoe.DW_BF16, "f16": lrmoe.DW_F16}[args.dw_mode]
     smode = {"lrm": lrmoe.SCORE_LRM, "grad-sqnorm": lrmoe.SCORE_GRAD_SQNORM,
              "grad-l1": lrmoe.SCORE_GRAD_L1, "random": lrmoe.SCORE_LRM}[args.score_mode]
     plan = lrmoe.Plan(p.counts, q, p.d_out, p.d_in, dtc, T=p.T, dw_mode=mode, score_mode=smode)
@@ -419,9 +421,11 @@ def main():
         kernels[name] = k
     if whole and p.dtype == "bf16" and "gather" in kernels:
         # what the gather writes beyond the method's bytes: the GEMM's operand
-        # planes (alpha times the narrower operand, hi + lo in exact mode)
-        kernels["gather"]["gemm_plane_bytes"] = (M * min(d_o, d_i) * 2 *
-                                                 (2 if args.dw_mode == "exact" else 1))
+        # planes (alpha times the narrower operand, hi + lo in exact mode; in
+        # the float16 mode both operands as scaled float16)
+        kernels["gather"]["gemm_plane_bytes"] = (
+            M * (d_o + d_i) * 2 if args.dw_mode == "f16"       # both float16 planes
+            else M * min(d_o, d_i) * 2 * (2 if args.dw_mode == "exact" else 1))
     ssc_us = sum(us[n] for n in ("lrm_score", "select_scan", "gather") if us[n] is not None)
     nbytes = algorithmic_bytes(p, M, args.score_mode)
     if chain:   # no dphi rows to zero in the original layout
@@ -432,8 +436,9 @@ def main():
     # pass per term (exact mode: alpha * (narrower operand) as hi + lo).
     terms_dw = 1 + (args.dw_mode == "exact" or p.dtype != "bf16") + (p.dtype != "bf16")
     terms_dp = 1 if p.dtype == "bf16" else 3
-    if chain:   # gate/up on the float32 hand-off: alpha * dgu (hi + lo) feeds both products
-        terms_dp = terms_dw
+    if chain:   # gate/up on the float32 hand-off: alpha * dgu (hi + lo unless single
+        # rounding) feeds both products
+        terms_dw = terms_dp = 1 if args.dw_mode == "bf16" else 2
     if gu is not None:
         exec_flops = 2.0 * M * gu.d_out * gu.d_in * (terms_dw + terms_dp)
     else:

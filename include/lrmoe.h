@@ -97,15 +97,24 @@ typedef struct {
   int64_t budget_pairs;  /* BUDGET: >= 0                                    */
 } lrmoe_quota_policy;
 
-/* How the GEMMs fold alpha into the weight gradient.
- * EXACT (default): alpha*g is split into a bf16 high part and a bf16
- *   residual and both are multiplied (two matrix-core passes for dW), so dW
- *   carries float32-level error.
- * BF16: alpha*g is rounded once to bf16 (the rounding a bf16 training step
- *   applies); one pass, about 2e-3 relative error in dW.
+/* How the GEMMs fold alpha into the weight gradient.  alpha multiplies the
+ * reduction index of dW_e = sum_j (alpha_j g_j) phi_j^T, so it enters an
+ * operand before the matrix cores (the narrower of g and phi carries it).
+ * EXACT (0): alpha*x is split into a bf16 high part and a bf16 residual and
+ *   both are multiplied (two matrix-core passes for dW), so dW carries
+ *   float32-level error (about 2^-16 relative per term).
+ * BF16 (1): alpha*x is rounded once to bf16 (the rounding a bf16 training
+ *   step applies); one pass, up to 2^-8 relative per term.
+ * F16 (2): one pass on float16 matrix cores (the same rate as bf16): the
+ *   other operand converts from bf16 exactly, alpha*x is rounded once to
+ *   float16 (2^-11 relative per term, eight times finer than bf16).  Both
+ *   are scaled per expert by powers of two taken from the largest row norm
+ *   over the expert's kept rows (a bound of the largest magnitude), so any
+ *   bf16 range maps into float16's; the product is unscaled exactly.  bf16
+ *   storage only (float32 storage uses EXACT).
  * dphi always applies alpha in float32 after the product.  float32 storage
  * always splits both operands (three bf16 passes). */
-typedef enum { LRMOE_DW_EXACT = 0, LRMOE_DW_BF16 = 1 } lrmoe_dw_mode;
+typedef enum { LRMOE_DW_EXACT = 0, LRMOE_DW_BF16 = 1, LRMOE_DW_F16 = 2 } lrmoe_dw_mode;
 
 /* Scoring rule of lrmoe_score_select_compact.  LRM is the method's metric
  * R_u = alpha_u^2 * ||g_t||^2 * ||phi_u||^2.  The others are the ablation

@@ -45,7 +45,9 @@ lrmoe_status check_problem(const lrmoe_problem* pb, Checked& c) {
   if (pb == nullptr || pb->counts == nullptr || pb->quotas == nullptr) return LRMOE_ERR_NULL;
   if (pb->E < 1 || pb->E > kMaxE) return LRMOE_ERR_INVALID;
   if (pb->dtype != LRMOE_F32 && pb->dtype != LRMOE_BF16) return LRMOE_ERR_DTYPE;
-  if (pb->dw_mode != LRMOE_DW_EXACT && pb->dw_mode != LRMOE_DW_BF16) return LRMOE_ERR_INVALID;
+  if (pb->dw_mode != LRMOE_DW_EXACT && pb->dw_mode != LRMOE_DW_BF16 &&
+      pb->dw_mode != LRMOE_DW_F16)
+    return LRMOE_ERR_INVALID;
   if (pb->score_mode < LRMOE_SCORE_LRM || pb->score_mode > LRMOE_SCORE_GRAD_L1)
     return LRMOE_ERR_INVALID;
   if (pb->P < 0 || pb->P >= (int64_t(1) << 31)) return LRMOE_ERR_SHAPE;
@@ -94,15 +96,34 @@ struct GemmWorkspace {
   int dw_pa = 1, dw_pb = 1, dp_pa = 1, dp_pb = 1;
   int32_t kc = 0;          // dW K-chunk length
   int64_t part_tiles = 0;  // partial tiles of split experts
-  size_t heads = 0;        // queue counters
+  size_t heads = 0;        // queue counters (kXcds int32), then at +kEmaxOff ...
+  bool f16 = false;        // float16 weight gradient: a_hi / b_hi are its two planes
+  size_t rnorm = 0;        // ... the per-expert bounds ebound; here per-pair row norms
 };
+
+// Float16 mode: the expert bounds (largest kept row norms) sit right behind
+// the queue counters, so that one fill kernel clears both.
+constexpr size_t kEmaxOff = 256;
+constexpr size_t kHeadsBytes = kEmaxOff + 2 * kMaxE * sizeof(float);
 
 constexpr int kStepK = 32;   // K rows per pipeline step of the GEMM kernel
 
 GemmWorkspace gemm_workspace(const lrmoe_problem* pb, int64_t M, bool g_f32 = false) {
   GemmWorkspace w;
   const size_t Mz = (size_t)M;
-  if (g_f32) {
+  if (!g_f32 && pb->dtype == LRMOE_BF16 && pb->dw_mode == LRMOE_DW_F16) {
+    // queue counters and expert bounds, the score pass's per-pair row norms,
+    // then the float16 planes of both weight-gradient operands (alpha on the
+    // narrower); the selection's scratch of the one-call path goes where the
+    // planes will be, so that it never meets the norms it runs beside
+    w.f16 = true;
+    w.alpha_on_phi = pb->d_in <= pb->d_out;
+    w.heads = 0;
+    w.rnorm = kHeadsBytes;
+    w.a_hi = round256(w.rnorm + (size_t)pb->P * 8);
+    w.b_hi = w.a_hi + round256(Mz * (size_t)pb->d_out * 2);
+    w.total = w.b_hi + round256(Mz * (size_t)pb->d_in * 2);
+  } else if (g_f32) {
     w.alpha_on_phi = false;
     const size_t plane = round256(Mz * (size_t)pb->d_out * 2);
     const bool exact = pb->dw_mode != LRMOE_DW_BF16;
@@ -158,8 +179,12 @@ GemmWorkspace gemm_workspace(const lrmoe_problem* pb, int64_t M, bool g_f32 = fa
     if (S > 1) w.part_tiles += tiles_m * tiles_n * S;
   }
   w.partials = round256(w.total);
+  if (w.f16) {   // counters and bounds were placed first
+    w.total = w.partials + (size_t)w.part_tiles * kTile * kTile * 4;
+    return w;
+  }
   w.heads = w.partials + (size_t)w.part_tiles * kTile * kTile * 4;
-  w.total = w.heads + 256;   // per-XCD queue counters of the grouped GEMM
+  w.total = w.heads + kHeadsBytes;   // per-XCD queue counters of the grouped GEMM
   return w;
 }
 
@@ -175,7 +200,9 @@ size_t select_workspace(const Checked& c) {
 // One size for every call of the problem: the selection, the grouped GEMMs,
 // and (bf16 storage) the gate/up variant with a float32 output gradient.
 size_t workspace_bytes(const lrmoe_problem* pb, const Checked& c) {
-  size_t n = std::max(gemm_workspace(pb, c.M).total, select_workspace(c));
+  const GemmWorkspace w = gemm_workspace(pb, c.M);
+  // the one-call float16 path runs the selection in the plane region
+  size_t n = std::max(w.total, (w.f16 ? w.a_hi : 0) + select_workspace(c));
   if (pb->dtype == LRMOE_BF16) n = std::max(n, gemm_workspace(pb, c.M, true).total);
   return n;
 }
@@ -244,7 +271,8 @@ lrmoe_status select_compact(const lrmoe_problem* pb, bool compute_scores, const 
                             float* alpha_c, float* dphi_zero, void* workspace, size_t ws_bytes,
                             void* stream, const lrmoe_timing* timing, bool gather = true,
                             const GatherPlanes& planes = GatherPlanes(),
-                            bool use_scratch = false) {
+                            bool use_scratch = false, float2* rnorm = nullptr,
+                            float* ebound = nullptr) {
   Checked c;
   LRMOE_TRY(check_problem(pb, c));
   const int64_t P = pb->P, M = c.M;
@@ -285,13 +313,14 @@ lrmoe_status select_compact(const lrmoe_problem* pb, bool compute_scores, const 
     LRMOE_TRY(mark(timing, false, 0, s));
     LRMOE_TRY(hip_status(launch_score(pb->dtype, pb->score_mode, g, phi, alpha, g_row_index,
                                       (int32_t)P, (int32_t)pb->T, pb->d_out, pb->d_in,
-                                      scores_out, s)));
+                                      scores_out, s, rnorm, planes.from_phi ? 1 : 0)));
     LRMOE_TRY(mark(timing, true, 0, s));
     scores = scores_out;
   }
   LRMOE_TRY(mark(timing, false, 1, s));
   LRMOE_TRY(hip_status(launch_select_scan(c.tab, scores, keep, perm, seg_offsets,
-                                          reinterpret_cast<uint32_t*>(workspace), s)));
+                                          reinterpret_cast<uint32_t*>(workspace), s, rnorm,
+                                          ebound)));
   LRMOE_TRY(mark(timing, true, 1, s));
   if (!gather) return LRMOE_OK;
   LRMOE_TRY(mark(timing, false, 2, s));
@@ -438,7 +467,35 @@ lrmoe_status grouped_backward(const lrmoe_problem* pb, const int32_t* perm, cons
   const uint16_t* g16 = reinterpret_cast<const uint16_t*>(g_c);
   const uint16_t* p16 = reinterpret_cast<const uint16_t*>(phi_c);
   const uint16_t* w16 = reinterpret_cast<const uint16_t*>(W);
-  if (g_f32) {
+  float* ebound = reinterpret_cast<float*>(ws + wl.heads + kEmaxOff);
+  if (wl.f16) {
+    // float16 planes of both weight-gradient operands, scaled per expert by
+    // the powers of two of the kept rows' largest norms (the gather wrote
+    // them in the one-call path; here: clear counters and bounds, bounds,
+    // planes)
+    uint16_t* fa = plane(wl.a_hi);
+    uint16_t* fb = plane(wl.b_hi);
+    if (!planes_ready) {
+      SegTable seg;
+      seg.E = E;
+      for (int e = 0; e <= E; ++e) seg.off[e] = c.tab.seg_off[e];
+      const uint16_t* gc16 = reinterpret_cast<const uint16_t*>(g_c);
+      const uint16_t* pc16 = reinterpret_cast<const uint16_t*>(phi_c);
+      LRMOE_TRY(hip_status(launch_zero(heads, (int)((kEmaxOff + 2 * E * sizeof(float)) / 4), s)));
+      LRMOE_TRY(hip_status(launch_rows_bound(seg, gc16, pc16, alpha_c, (int32_t)M, d_out, d_in,
+                                              wl.alpha_on_phi, ebound, s)));
+      LRMOE_TRY(hip_status(launch_split_f16(seg, gc16, pc16, alpha_c, (int32_t)M, d_out, d_in,
+                                            wl.alpha_on_phi, ebound, fa, fb, s)));
+    }
+    ops.dw_a[0] = fa;
+    ops.dw_b[0] = fb;
+    ops.dw_pa = ops.dw_pb = 1;
+    ops.dp_a[0] = g16;
+    ops.dp_b[0] = w16;
+    ops.dp_pa = ops.dp_pb = 1;
+    ops.dw_f16 = 1;
+    ops.dw_ebound = ebound;
+  } else if (g_f32) {
     // alpha * g_c (float32) as bf16 hi (+ lo) planes, the A operand of both
     // products; the input-gradient epilogue then applies no alpha
     uint16_t* hi = plane(wl.b_hi);
@@ -526,18 +583,36 @@ lrmoe_status pruned_backward(const lrmoe_problem* pb, const int32_t* g_row_index
   LRMOE_TRY(need(workspace, (int64_t)wl.total));
   GatherPlanes planes;
   const bool fused = pb->dtype == LRMOE_BF16;
+  float2* rnorm = nullptr;
+  float* ebound = nullptr;
   if (fused) {
     char* ws = reinterpret_cast<char*>(workspace);
-    planes.hi = reinterpret_cast<uint16_t*>(ws + wl.b_hi);
-    planes.lo = pb->dw_mode == LRMOE_DW_EXACT ? reinterpret_cast<uint16_t*>(ws + wl.b_lo)
-                                              : nullptr;
     planes.from_phi = wl.alpha_on_phi;
     planes.zero = reinterpret_cast<int32_t*>(ws + wl.heads);
     planes.nzero = kXcds;
+    if (wl.f16) {
+      // the score pass writes per-pair row norms, the select reduces them
+      // over each expert's kept pairs, the gather writes the float16 planes
+      rnorm = reinterpret_cast<float2*>(ws + wl.rnorm);
+      ebound = reinterpret_cast<float*>(ws + wl.heads + kEmaxOff);
+      planes.f16_a = reinterpret_cast<uint16_t*>(ws + wl.a_hi);
+      planes.f16_b = reinterpret_cast<uint16_t*>(ws + wl.b_hi);
+      planes.ebound = ebound;
+      planes.seg.E = pb->E;
+      for (int e = 0; e <= pb->E; ++e) planes.seg.off[e] = c.tab.seg_off[e];
+    } else {
+      planes.hi = reinterpret_cast<uint16_t*>(ws + wl.b_hi);
+      planes.lo = pb->dw_mode == LRMOE_DW_EXACT ? reinterpret_cast<uint16_t*>(ws + wl.b_lo)
+                                                : nullptr;
+    }
   }
+  // float16: the selection's scratch sits where the planes will be (the
+  // counters and bounds come first)
+  const size_t sel_off = wl.f16 ? wl.a_hi : 0;
   LRMOE_TRY(select_compact(pb, true, nullptr, g_row_index, alpha, g, phi, scores, keep,
-                           seg_offsets, perm, g_c, phi_c, alpha_c, dphi, workspace, ws_bytes,
-                           stream, timing, true, planes));
+                           seg_offsets, perm, g_c, phi_c, alpha_c, dphi,
+                           reinterpret_cast<char*>(workspace) + sel_off, ws_bytes - sel_off,
+                           stream, timing, true, planes, false, rnorm, ebound));
   TimingSlots ts;
   ts.gemm = 3;
   ts.reduce = 4;
@@ -606,7 +681,9 @@ lrmoe_status gather_backward(const lrmoe_problem* pb, const int32_t* perm, const
   if (ws_bytes < workspace_bytes(pb, c)) return LRMOE_ERR_WORKSPACE;
   LRMOE_TRY(need(workspace, (int64_t)wl.total));
   GatherPlanes planes;
-  const bool fused = pb->dtype == LRMOE_BF16;
+  // float16 mode: no score pass to take the expert bounds from, so the
+  // grouped backward's own prologue finds them from the compacted rows
+  const bool fused = pb->dtype == LRMOE_BF16 && !wl.f16;
   if (fused) {
     char* ws = reinterpret_cast<char*>(workspace);
     planes.hi = reinterpret_cast<uint16_t*>(ws + wl.b_hi);

@@ -9,6 +9,7 @@
 // Jobs [0, M) gather compacted row j; jobs [M, M + P) zero dphi row u when
 // pair u was dropped (only when a zero target is given).
 #include "lrmoe_internal.h"
+#include "row_norm.h"
 
 namespace lrmoe {
 namespace {
@@ -67,6 +68,48 @@ __device__ __forceinline__ void copy_row_split(const uint4* __restrict__ src,
   }
 }
 
+// ---- float16 weight-gradient planes
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// 8 bf16 of a 16-byte chunk -> float16 of 2^s * a * x: the product rounded
+// once to float32 (exact when a == 1), the power of two exact, then one
+// rounding to float16 (nearest even).
+__device__ __forceinline__ uint4 f16_chunk(const uint4& x, float a, int s) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  f16x8 h;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[2 * i] = (_Float16)__builtin_amdgcn_ldexpf(a * __uint_as_float(w[i] << 16), s);
+    h[2 * i + 1] = (_Float16)__builtin_amdgcn_ldexpf(a * __uint_as_float(w[i] & 0xFFFF0000u), s);
+  }
+  return __builtin_bit_cast(uint4, h);
+}
+
+// Copy of one bf16 row (dst may be null) and its float16 plane row.
+__device__ __forceinline__ void copy_row_f16(const uint4* __restrict__ src,
+                                             uint4* __restrict__ dst, uint4* __restrict__ pl,
+                                             float a, int s, int nchunk, int lane) {
+  int c = lane;
+  for (; c + 64 < nchunk; c += 128) {
+    const uint4 x0 = src[c], x1 = src[c + 64];
+    if (dst != nullptr) { dst[c] = x0; dst[c + 64] = x1; }
+    pl[c] = f16_chunk(x0, a, s);
+    pl[c + 64] = f16_chunk(x1, a, s);
+  }
+  for (; c < nchunk; c += 64) {
+    const uint4 x = src[c];
+    if (dst != nullptr) dst[c] = x;
+    pl[c] = f16_chunk(x, a, s);
+  }
+}
+
+struct F16Planes {
+  uint4* a;            // [M, d_out / 8] chunks, or null: no float16 planes
+  uint4* b;            // [M, d_in / 8]
+  const float* ebound;   // [E][2]
+  SegTable seg;
+};
+
 __global__ __launch_bounds__(256) void gather_kernel(
     const int32_t* __restrict__ perm, const uint8_t* __restrict__ keep,
     const int32_t* __restrict__ g_row_index, const int32_t* __restrict__ phi_row_index,
@@ -74,7 +117,7 @@ __global__ __launch_bounds__(256) void gather_kernel(
     uint4* __restrict__ g_c, uint4* __restrict__ phi_c, float* __restrict__ alpha_c,
     float4* __restrict__ dphi_zero, int32_t M, int32_t P, int32_t g_rows, int32_t phi_rows,
     int32_t gch, int32_t pch, int32_t zch, uint4* __restrict__ pl_hi, uint4* __restrict__ pl_lo,
-    int pl_from_phi, int32_t* __restrict__ zero, int nzero) {
+    int pl_from_phi, int32_t* __restrict__ zero, int nzero, F16Planes f16) {
   const int lane = threadIdx.x & 63;
   if (blockIdx.x == 0 && (int)threadIdx.x < nzero) zero[threadIdx.x] = 0;
   const int64_t job = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -90,7 +133,16 @@ __global__ __launch_bounds__(256) void gather_kernel(
     const float a = alpha[u];
     uint4* gdst = g_c != nullptr ? g_c + (int64_t)j * gch : nullptr;
     uint4* pdst = phi_c + (int64_t)j * pch;
-    if (pl_hi != nullptr && !pl_from_phi) {
+    if (f16.a != nullptr) {   // float16 weight-gradient planes of both operands
+      const int e = expert_of_row(f16.seg, j);
+      const int sa = f16_scale_exp(f16.ebound[2 * e]), sb = f16_scale_exp(f16.ebound[2 * e + 1]);
+      uint4* pa = f16.a + (int64_t)j * gch;
+      uint4* pb = f16.b + (int64_t)j * pch;
+      if (g_ok) copy_row_f16(g + gr * gch, gdst, pa, pl_from_phi ? 1.f : a, sa, gch, lane);
+      else zero_row(gdst, pa, nullptr, gch, lane);
+      if (p_ok) copy_row_f16(phi + pr * pch, pdst, pb, pl_from_phi ? a : 1.f, sb, pch, lane);
+      else zero_row(pdst, pb, nullptr, pch, lane);
+    } else if (pl_hi != nullptr && !pl_from_phi) {
       uint4* h = pl_hi + (int64_t)j * gch;
       uint4* l = pl_lo ? pl_lo + (int64_t)j * gch : nullptr;
       if (g_ok) copy_row_split(g + gr * gch, gdst, h, l, a, gch, lane);
@@ -99,7 +151,9 @@ __global__ __launch_bounds__(256) void gather_kernel(
       if (g_ok) copy_row(g + gr * gch, gdst, gch, lane);
       else zero_row(gdst, nullptr, nullptr, gch, lane);
     }
-    if (pl_hi != nullptr && pl_from_phi) {
+    if (f16.a != nullptr) {
+      // both planes written above
+    } else if (pl_hi != nullptr && pl_from_phi) {
       uint4* h = pl_hi + (int64_t)j * pch;
       uint4* l = pl_lo ? pl_lo + (int64_t)j * pch : nullptr;
       if (p_ok) copy_row_split(phi + pr * pch, pdst, h, l, a, pch, lane);
@@ -117,6 +171,64 @@ __global__ __launch_bounds__(256) void gather_kernel(
       for (int c = lane; c < zch; c += 64) row[c] = z;
     }
   }
+}
+
+// Float16 weight-gradient mode, separate-call path, step 1: per expert, the
+// largest row norm of A and of B over its compacted rows, the side carrying
+// alpha times |alpha_j| (bit for bit the values the score pass produces per
+// pair in the one-call path: the same row_norm_bf16).  Each wave takes a
+// contiguous range of rows and merges its running largest norms into ebound
+// (atomicMax on non-negative float32 bits) whenever the expert changes and
+// at the end.
+__global__ __launch_bounds__(256) void rows_bound_kernel(
+    SegTable seg, const uint4* __restrict__ g_c, const uint4* __restrict__ phi_c,
+    const float* __restrict__ alpha_c, int32_t M, int32_t gch, int32_t pch, int alpha_on_phi,
+    float* __restrict__ ebound) {
+  const int lane = threadIdx.x & 63;
+  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int nwaves = (gridDim.x * blockDim.x) >> 6;
+  const int per = (M + nwaves - 1) / nwaves;
+  const int j0 = wave * per, j1 = min(M, j0 + per);
+  uint32_t* em = reinterpret_cast<uint32_t*>(ebound);
+  int cur = -1;
+  uint32_t ma = 0u, mb = 0u;
+  for (int j = j0; j < j1; ++j) {
+    const int e = expert_of_row(seg, j);
+    if (e != cur) {
+      if (cur >= 0 && lane == 0) {
+        atomicMax(em + 2 * cur, ma);
+        atomicMax(em + 2 * cur + 1, mb);
+      }
+      cur = e;
+      ma = mb = 0u;
+    }
+    const float aa = fabsf(alpha_c[j]);
+    float ra = row_norm_bf16(g_c + (int64_t)j * gch, gch, lane);
+    float rb = row_norm_bf16(phi_c + (int64_t)j * pch, pch, lane);
+    if (alpha_on_phi) rb = aa * rb; else ra = aa * ra;
+    ma = max(ma, __float_as_uint(ra));
+    mb = max(mb, __float_as_uint(rb));
+  }
+  if (cur >= 0 && lane == 0) {
+    atomicMax(em + 2 * cur, ma);
+    atomicMax(em + 2 * cur + 1, mb);
+  }
+}
+
+// Step 2: the two float16 planes from the compacted rows, one wave per row
+// (bit for bit the gather's planes of the one-call path).
+__global__ __launch_bounds__(256) void split_f16_kernel(
+    SegTable seg, const uint4* __restrict__ g_c, const uint4* __restrict__ phi_c,
+    const float* __restrict__ alpha_c, int32_t M, int32_t gch, int32_t pch, int alpha_on_phi,
+    const float* __restrict__ ebound, uint4* __restrict__ pa, uint4* __restrict__ pb) {
+  const int lane = threadIdx.x & 63;
+  const int64_t j = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (j >= M) return;
+  const int e = expert_of_row(seg, (int)j);
+  const int sa = f16_scale_exp(ebound[2 * e]), sb = f16_scale_exp(ebound[2 * e + 1]);
+  const float a = alpha_c[j];
+  copy_row_f16(g_c + j * gch, nullptr, pa + j * gch, alpha_on_phi ? 1.f : a, sa, gch, lane);
+  copy_row_f16(phi_c + j * pch, nullptr, pb + j * pch, alpha_on_phi ? a : 1.f, sb, pch, lane);
 }
 
 // Zero-masked dense alternative: alpha of dropped pairs set to 0 in the
@@ -155,7 +267,9 @@ hipError_t launch_gather(int dtype, const int32_t* perm, const uint8_t* keep,
                          int32_t P, int32_t g_rows, int32_t phi_rows, int32_t d_out,
                          int32_t d_in, hipStream_t s, const GatherPlanes& planes) {
   const int per = (dtype == LRMOE_BF16) ? 8 : 4;
-  if (planes.hi != nullptr && dtype != LRMOE_BF16) return hipErrorInvalidValue;
+  if ((planes.hi != nullptr || planes.f16_a != nullptr) && dtype != LRMOE_BF16)
+    return hipErrorInvalidValue;
+  F16Planes f16{(uint4*)planes.f16_a, (uint4*)planes.f16_b, planes.ebound, planes.seg};
   const int64_t jobs = (int64_t)M + (dphi_zero ? (int64_t)P : 0);
   if (jobs == 0) return planes.nzero > 0 ? launch_zero(planes.zero, planes.nzero, s) : hipSuccess;
   const int64_t blocks = (jobs + 3) / 4;
@@ -163,7 +277,30 @@ hipError_t launch_gather(int dtype, const int32_t* perm, const uint8_t* keep,
                      g_row_index, phi_row_index, alpha, (const uint4*)g, (const uint4*)phi,
                      (uint4*)g_c, (uint4*)phi_c, alpha_c, (float4*)dphi_zero, M, P, g_rows,
                      phi_rows, d_out / per, d_in / per, d_in / 4, (uint4*)planes.hi, (uint4*)planes.lo,
-                     planes.from_phi ? 1 : 0, planes.zero, planes.nzero);
+                     planes.from_phi ? 1 : 0, planes.zero, planes.nzero, f16);
+  return hipGetLastError();
+}
+
+hipError_t launch_rows_bound(const SegTable& seg, const uint16_t* g_c, const uint16_t* phi_c,
+                             const float* alpha_c, int32_t M, int32_t d_out, int32_t d_in,
+                             bool alpha_on_phi, float* ebound, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  int blocks = (M + 3) / 4;
+  if (blocks > 256 * 4) blocks = 256 * 4;
+  hipLaunchKernelGGL(rows_bound_kernel, dim3(blocks), dim3(256), 0, s, seg, (const uint4*)g_c,
+                     (const uint4*)phi_c, alpha_c, M, d_out / 8, d_in / 8, alpha_on_phi ? 1 : 0,
+                     ebound);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_f16(const SegTable& seg, const uint16_t* g_c, const uint16_t* phi_c,
+                            const float* alpha_c, int32_t M, int32_t d_out, int32_t d_in,
+                            bool alpha_on_phi, const float* ebound, uint16_t* f16_a,
+                            uint16_t* f16_b, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  hipLaunchKernelGGL(split_f16_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, s, seg,
+                     (const uint4*)g_c, (const uint4*)phi_c, alpha_c, M, d_out / 8, d_in / 8,
+                     alpha_on_phi ? 1 : 0, ebound, (uint4*)f16_a, (uint4*)f16_b);
   return hipGetLastError();
 }
 

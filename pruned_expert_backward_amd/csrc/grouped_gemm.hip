@@ -133,6 +133,12 @@ __device__ __forceinline__ f32x16 mfma(i16x8 a, i16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+// float16 operands (the float16 weight-gradient mode): same shape and rate
+__device__ __forceinline__ f32x16 mfma_f16(i16x8 a, i16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
 
 struct TileJob {
   int e, m0, n0;
@@ -267,7 +273,9 @@ constexpr int kPermBytes = BM * 8;   // dphi epilogue: destination row + alpha p
 // The matrix core always has independent MFMAs queued while fragments and
 // stages move, and the global loads trickle out between MFMAs instead of
 // stalling the wave in a burst.
-template <bool IS_DW, int PA, int PB, int NS, int GLU = 0>
+// F16 (weight-gradient tiles only): float16 operand planes, float16 MFMAs,
+// and the epilogue undoes the expert's power-of-two scales.
+template <bool IS_DW, int PA, int PB, int NS, int GLU = 0, bool F16 = false>
 struct Tile {
   static constexpr bool A_MC = IS_DW;
   static constexpr int kStage = (PA + PB) * kPlaneBytes;
@@ -430,7 +438,8 @@ struct Tile {
     const int t = i / (kMB * kNB), a = (i % (kMB * kNB)) / kNB, b = i % kNB;
     const int pa = (t == 2 || (t == 1 && PB == 1)) ? PA - 1 : 0;
     const int pb = (t == 1 && PB == 2) ? 1 : 0;
-    acc[a][b] = mfma(f.b[pb][b], f.a[pa][a], acc[a][b]);
+    if constexpr (IS_DW && F16) acc[a][b] = mfma_f16(f.b[pb][b], f.a[pa][a], acc[a][b]);
+    else acc[a][b] = mfma(f.b[pb][b], f.a[pa][a], acc[a][b]);
   }
 
   // Barrier of step kt: stage kt + 1 is complete for every wave.  Stages
@@ -763,6 +772,11 @@ struct Tile {
     const bool odd = (ln & 1) != 0;
     // this lane's column inside each 16-column group: 0/4 (lane half) + 8 (odd lane)
     const int cq = 4 * (ln >> 5) + (odd ? 8 : 0);
+    // float16 weight gradient: 2^-(sA + sB) of the expert, applied exactly
+    int unscale = 0;
+    if constexpr (IS_DW && F16)
+      unscale = -(f16_scale_exp(args.ops.dw_ebound[2 * e]) +
+                  f16_scale_exp(args.ops.dw_ebound[2 * e + 1]));
 #pragma unroll
     for (int a = 0; a < kMB; ++a) {
       // rows of this lane's two stores: the even and the odd row of its pair
@@ -803,6 +817,13 @@ struct Tile {
             v0 *= scale[0];
             v1 *= scale[1];
           }
+          if constexpr (IS_DW && F16) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              v0[i] = __builtin_amdgcn_ldexpf(v0[i], unscale);
+              v1[i] = __builtin_amdgcn_ldexpf(v1[i], unscale);
+            }
+          }
           if (col < ncols) {
             if (orow[0] != nullptr) *reinterpret_cast<f32x4*>(orow[0] + col) = v0;
             if (orow[1] != nullptr) *reinterpret_cast<f32x4*>(orow[1] + col) = v1;
@@ -833,10 +854,10 @@ struct Cfg {
 // next tile's first loads are issued before the finished tile's stores, so
 // the store drain overlaps the next load latency.  Every workgroup exits when
 // its queue's counter passes the queue length.
-template <int DW_PA, int DW_PB, int DP_PA, int DP_PB, int GLU>
+template <int DW_PA, int DW_PB, int DP_PA, int DP_PB, int GLU, bool DW_F16>
 __global__ __launch_bounds__(kThreads, 1) void grouped_backward_kernel(Args args, GemmTable tab) {
   using C = Cfg<DW_PA, DW_PB, DP_PA, DP_PB>;
-  using DwTile = Tile<true, DW_PA, DW_PB, C::NS_DW>;
+  using DwTile = Tile<true, DW_PA, DW_PB, C::NS_DW, 0, DW_F16>;
   using DpTile = Tile<false, DP_PA, DP_PB, C::NS_DP, GLU>;
   __shared__ __attribute__((aligned(16))) char smem_raw[C::bytes];
   LDS_AS char* smem = (LDS_AS char*)(smem_raw);
@@ -894,14 +915,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_backward_kernel(Args args
   }
 }
 
-template <int DW_PA, int DW_PB, int DP_PA, int DP_PB, int GLU = 0>
+template <int DW_PA, int DW_PB, int DP_PA, int DP_PB, int GLU = 0, bool DW_F16 = false>
 hipError_t launch(const Args& args, const GemmTable& tab, hipStream_t s) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
   const int blocks = (cus + kXcds - 1) / kXcds * kXcds;   // one per CU, a multiple of 8
-  hipLaunchKernelGGL((grouped_backward_kernel<DW_PA, DW_PB, DP_PA, DP_PB, GLU>), dim3(blocks),
+  hipLaunchKernelGGL((grouped_backward_kernel<DW_PA, DW_PB, DP_PA, DP_PB, GLU, DW_F16>), dim3(blocks),
                      dim3(kThreads), 0, s, args, tab);
   return hipGetLastError();
 }
@@ -1057,6 +1078,12 @@ hipError_t launch_grouped_backward(const GemmTable& tab, const GemmOperands& ops
                                    hipStream_t s) {
   const Args args{ops, alpha_c, perm, dW, dphi, d_out, d_in, P};
   const int key = ops.dw_pa * 1000 + ops.dw_pb * 100 + ops.dp_pa * 10 + ops.dp_pb;
+  if (ops.dw_f16) {   // float16 weight-gradient planes, bf16 input gradient
+    if (key != 1111 || ops.dw_ebound == nullptr) return hipErrorInvalidValue;
+    if (ops.glu_out != nullptr)
+      return ops.glu_f32 ? launch<1, 1, 1, 1, 2, true>(args, tab, s) : hipErrorInvalidValue;
+    return launch<1, 1, 1, 1, 0, true>(args, tab, s);
+  }
   if (ops.glu_out != nullptr) {   // SiLU-GLU chain: bf16 storage only
     if (ops.glu_f32) {            // exact weight gradient, float32 hand-off
       switch (key) {

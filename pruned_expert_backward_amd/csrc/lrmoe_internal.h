@@ -95,6 +95,10 @@ struct GemmOperands {
   const uint16_t* glu_b;
   void* glu_out;
   int32_t glu_f32;
+  // float16 weight gradient: dw_a / dw_b are float16 planes scaled by the
+  // powers of two of dw_ebound (see f16_scale_exp)
+  int32_t dw_f16;
+  const float* dw_ebound;
   // 1: the input-gradient A planes already carry alpha (alpha * g_c split),
   // so the epilogue does not scale the rows again.
   int32_t dp_alpha_folded;
@@ -126,15 +130,52 @@ __device__ __forceinline__ HiLo alpha_split(float a, float x) {
   return {h, (__bf16)__builtin_fmaf(a, x, -(float)h)};
 }
 
+// ---- float16 weight-gradient mode (LRMOE_DW_F16)
+// dW_e = sum_j A_j B_j^T runs on float16 matrix cores: A = 2^sA (the g row),
+// B = 2^sB (the phi row), alpha folded into one side and rounded once to 11
+// significant bits (the other side converts from bf16 exactly).  sA, sB are
+// per-expert powers of two from the largest row norm over the expert's kept
+// rows (ebound[e] = {max |A row|, max |B row|}, each at least the largest
+// magnitude): 2^s ebound lands in [2^14, 2^15), so every scaled value stays
+// below 65504, and values down to 2^-28 of it (2^-34 for rows of 4096)
+// stay normal.  The epilogue multiplies by 2^-(sA + sB), exactly.
+__device__ __forceinline__ int f16_scale_exp(float m) {
+  if (!(m > 0.f) || !(m <= 3.4028235e38f)) return 0;   // 0 (no kept row) or not finite
+  return 15 - __builtin_amdgcn_frexp_expf(m);             // m = f 2^e, f in [0.5, 1)
+}
+
+// Compacted segment offsets by value (row j of expert e: seg_off[e] <= j <
+// seg_off[e + 1]).
+struct SegTable {
+  int32_t E;
+  int32_t off[kMaxE + 1];
+};
+
+__device__ __forceinline__ int expert_of_row(const SegTable& t, int j) {
+  int lo = 0, hi = t.E - 1;   // last e with off[e] <= j
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (t.off[mid] <= j) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
 // Launchers (return hipSuccess or the launch error).
-// g has T rows; a row index outside [0, T) reads as a zero row.
+// g has T rows; a row index outside [0, T) reads as a zero row.  rnorm (bf16
+// storage, float16 weight-gradient mode; else null): per pair the Euclidean
+// norms of the weight-gradient operand rows (A the g row, B the phi row,
+// alpha on the phi side if alpha_on_phi, else on the g side).
 hipError_t launch_score(int dtype, int mode, const void* g, const void* phi, const float* alpha,
                         const int32_t* row_index, int32_t P, int32_t T, int32_t d_out,
-                        int32_t d_in, float* scores, hipStream_t s);
+                        int32_t d_in, float* scores, hipStream_t s, float2* rnorm = nullptr,
+                        int alpha_on_phi = 1);
 
+// ebound (or null): float32 [E][2], the largest rnorm over each expert's kept
+// pairs (0 for an expert that keeps nothing).
 hipError_t launch_select_scan(const ExpertTable& tab, const float* scores, uint8_t* keep,
                               int32_t* perm, int32_t* seg_offsets_out, uint32_t* hist,
-                              hipStream_t s);
+                              hipStream_t s, const float2* rnorm = nullptr,
+                              float* ebound = nullptr);
 
 hipError_t launch_plan_quota_device(const int32_t* ids, int32_t n_ids, int32_t E, int32_t mode,
                                     int64_t num, int64_t den, int64_t Q, int64_t* counts,
@@ -154,6 +195,13 @@ struct GatherPlanes {
   bool from_phi = true;
   int32_t* zero = nullptr;
   int nzero = 0;
+  // float16 weight-gradient mode instead: both operand planes, f16_a [M,
+  // d_out] from the g rows and f16_b [M, d_in] from the phi rows, scaled by
+  // the expert's powers of two from ebound, alpha on the phi side if from_phi
+  uint16_t* f16_a = nullptr;
+  uint16_t* f16_b = nullptr;
+  const float* ebound = nullptr;
+  SegTable seg;
 };
 
 // g has g_rows rows and phi phi_rows rows; a source row index outside them
@@ -165,6 +213,19 @@ hipError_t launch_gather(int dtype, const int32_t* perm, const uint8_t* keep,
                          int32_t P, int32_t g_rows, int32_t phi_rows, int32_t d_out,
                          int32_t d_in, hipStream_t s,
                          const GatherPlanes& planes = GatherPlanes());
+
+// float16 weight-gradient mode, separate-call path: ebound[e] = the largest
+// A and B row norms over expert e's compacted rows (merged with atomicMax
+// into ebound, which must be zero), then the two scaled float16 planes from
+// the compacted bf16 rows (bit for bit what the gather writes in the
+// one-call path).
+hipError_t launch_rows_bound(const SegTable& seg, const uint16_t* g_c, const uint16_t* phi_c,
+                             const float* alpha_c, int32_t M, int32_t d_out, int32_t d_in,
+                             bool alpha_on_phi, float* ebound, hipStream_t s);
+hipError_t launch_split_f16(const SegTable& seg, const uint16_t* g_c, const uint16_t* phi_c,
+                            const float* alpha_c, int32_t M, int32_t d_out, int32_t d_in,
+                            bool alpha_on_phi, const float* ebound, uint16_t* f16_a,
+                            uint16_t* f16_b, hipStream_t s);
 
 // hi (and lo, if non-null) bf16 planes of alpha[row] * src[row][col] (alpha
 // may be null); src is bf16 or float32 storage.

@@ -22,6 +22,7 @@
 // Global score reads are 16-byte vectors from an aligned start (a single
 // workgroup's bandwidth is bounded by its vector memory instructions).
 #include "lrmoe_internal.h"
+#include "row_norm.h"
 
 namespace lrmoe {
 namespace {
@@ -29,20 +30,6 @@ namespace {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
-__device__ __forceinline__ float sumsq8(uint4 x) {
-  float a = 0.f, v;
-  v = bf16_lo(x.x); a = fmaf(v, v, a); v = bf16_hi(x.x); a = fmaf(v, v, a);
-  v = bf16_lo(x.y); a = fmaf(v, v, a); v = bf16_hi(x.y); a = fmaf(v, v, a);
-  v = bf16_lo(x.z); a = fmaf(v, v, a); v = bf16_hi(x.z); a = fmaf(v, v, a);
-  v = bf16_lo(x.w); a = fmaf(v, v, a); v = bf16_hi(x.w); a = fmaf(v, v, a);
-  return a;
-}
 __device__ __forceinline__ float sumsq4(float4 x) {
   return fmaf(x.w, x.w, fmaf(x.z, x.z, fmaf(x.y, x.y, x.x * x.x)));
 }
@@ -75,41 +62,57 @@ __device__ __forceinline__ float row_sumsq(const V* __restrict__ row, int nchunk
     a0 += reduce16<ABS>(x0); a1 += reduce16<ABS>(x1);
     a2 += reduce16<ABS>(x2); a3 += reduce16<ABS>(x3);
   }
-  for (; c < nchunk; c += 64) a0 += reduce16<ABS>(row[c]);
+  if (c < nchunk) {
+    V x0, x1, x2;
+    tail3(row, c, nchunk, x0, x1, x2);
+    a0 += reduce16<ABS>(x0); a1 += reduce16<ABS>(x1); a2 += reduce16<ABS>(x2);
+  }
   return (a0 + a1) + (a2 + a3);
 }
 
 // MODE: LRMOE_SCORE_LRM (alpha^2 ||g||^2 ||phi||^2), _GRAD_SQNORM (||g||^2)
-// or _GRAD_L1 (sum |g_i|); the gradient-only rules never touch phi.
-template <bool BF16, int MODE>
+// or _GRAD_L1 (sum |g_i|); the gradient-only rules never touch phi, unless
+// RNORM.  RNORM (bf16 storage, the float16 weight-gradient mode): also write
+// per pair the Euclidean norms of the two weight-gradient operand rows,
+// rnorm[u] = {|A row|, |B row|}, A = the g row, B = the phi row, the side
+// that carries alpha (alpha_on_phi) times |alpha_u|.  A row norm bounds the
+// row's largest magnitude; the float16 planes' scales come from them.
+template <bool BF16, int MODE, bool RNORM = false>
 __global__ __launch_bounds__(256) void lrm_score_kernel(
     const void* __restrict__ g, const void* __restrict__ phi, const float* __restrict__ alpha,
     const int32_t* __restrict__ row_index, int32_t P, int32_t T, int32_t d_out, int32_t d_in,
-    float* __restrict__ scores) {
+    float* __restrict__ scores, float2* __restrict__ rnorm, int alpha_on_phi) {
   const int lane = threadIdx.x & 63;
   const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int nwaves = (gridDim.x * blockDim.x) >> 6;
   const int per = BF16 ? 8 : 4;  // elements per 16-byte chunk
   const int gc = d_out / per, pc = d_in / per;
+  constexpr bool L1 = MODE == LRMOE_SCORE_GRAD_L1;
+  constexpr bool LRM = MODE == LRMOE_SCORE_LRM;
   for (int u = wave; u < P; u += nwaves) {
     const int64_t r = row_index ? (int64_t)row_index[u] : (int64_t)u;
     // a row index outside g's T rows reads as a zero row: no load at all
     const int gcr = (uint64_t)r < (uint64_t)T ? gc : 0;
-    constexpr bool L1 = MODE == LRMOE_SCORE_GRAD_L1;
-    float gs, ps = 1.f;
-    if (BF16) {
-      gs = row_sumsq<L1>(reinterpret_cast<const uint4*>(g) + r * gc, gcr, lane);
-      if (MODE == LRMOE_SCORE_LRM)
-        ps = row_sumsq(reinterpret_cast<const uint4*>(phi) + (int64_t)u * pc, pc, lane);
+    float gs, ps = 1.f;   // wave totals
+    if constexpr (BF16) {
+      const uint4* grow = reinterpret_cast<const uint4*>(g) + r * gc;
+      const uint4* prow = reinterpret_cast<const uint4*>(phi) + (int64_t)u * pc;
+      const float gsq = (!L1 || RNORM) ? wave_sum(row_sumsq_bf16(grow, gcr, lane)) : 0.f;
+      gs = L1 ? wave_sum(row_sumsq<true>(grow, gcr, lane)) : gsq;
+      const float psq = (LRM || RNORM) ? wave_sum(row_sumsq_bf16(prow, pc, lane)) : 0.f;
+      if (LRM) ps = psq;
+      if (RNORM && lane == 0) {
+        const float aa = fabsf(alpha[u]);
+        const float ng = sqrtf(gsq), np = sqrtf(psq);
+        rnorm[u] = alpha_on_phi ? make_float2(ng, aa * np) : make_float2(aa * ng, np);
+      }
     } else {
-      gs = row_sumsq<L1>(reinterpret_cast<const float4*>(g) + r * gc, gcr, lane);
-      if (MODE == LRMOE_SCORE_LRM)
-        ps = row_sumsq(reinterpret_cast<const float4*>(phi) + (int64_t)u * pc, pc, lane);
+      gs = wave_sum(row_sumsq<L1>(reinterpret_cast<const float4*>(g) + r * gc, gcr, lane));
+      if (LRM)
+        ps = wave_sum(row_sumsq(reinterpret_cast<const float4*>(phi) + (int64_t)u * pc, pc, lane));
     }
-    gs = wave_sum(gs);
-    if (MODE == LRMOE_SCORE_LRM) ps = wave_sum(ps);
     if (lane == 0) {
-      if (MODE == LRMOE_SCORE_LRM) {
+      if (LRM) {
         const float a = alpha[u];
         scores[u] = ((a * a) * gs) * ps;
       } else {
@@ -159,6 +162,40 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wsum, uint3
   __syncthreads();   // wsum may be reused
   total = t;
   return before + x;
+}
+
+// Largest of v over the workgroup (every thread gets it).  wsum: kSelWaves
+// LDS words.
+__device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+  if (lane == 0) wsum[wave] = v;
+  __syncthreads();
+  uint32_t m = 0u;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) m = max(m, wsum[w]);
+  __syncthreads();   // wsum may be reused
+  return m;
+}
+
+// Largest operand row norms of expert e's kept pairs (float16 weight-gradient
+// mode): the workgroup's accumulators reduced and stored (whole expert) or
+// merged with atomicMax (one chunk of a large expert; non-negative float32
+// bit patterns order like their values).
+__device__ __forceinline__ void put_kept_bound(const uint32_t (&kbound)[2], uint32_t* wsum,
+                                             float* ebound, int e, bool merge) {
+  const uint32_t a = block_max(kbound[0], wsum);
+  const uint32_t b = block_max(kbound[1], wsum);
+  if (threadIdx.x == 0) {
+    if (merge) {
+      atomicMax(reinterpret_cast<uint32_t*>(ebound) + 2 * e, a);
+      atomicMax(reinterpret_cast<uint32_t*>(ebound) + 2 * e + 1, b);
+    } else {
+      ebound[2 * e] = __uint_as_float(a);
+      ebound[2 * e + 1] = __uint_as_float(b);
+    }
+  }
 }
 
 struct Digit {
@@ -243,11 +280,16 @@ __device__ __forceinline__ float4 load4(const float* __restrict__ scores, int a,
 // consecutive pairs of a tile (those outside [base, end) are skipped); one
 // workgroup scan of (#gt, #eq) per tile gives every position.  The next
 // tile's loads go out before this tile is scanned.
+//
+// rnorm (or null): per-pair operand row norms of the float16 weight-gradient
+// mode; the thread's largest over its kept pairs accumulate into kbound
+// (float32 bits).
 __device__ __forceinline__ void scan_keep(const uint32_t* keys_lds, const float* __restrict__ scores,
                                           int P, int base, int end, int lds_base, uint32_t tau,
                                           uint32_t need, uint32_t run_gt, uint32_t run_eq,
                                           uint32_t q, int seg, uint8_t* __restrict__ keep,
-                                          int32_t* __restrict__ perm, uint32_t* wsum) {
+                                          int32_t* __restrict__ perm, uint32_t* wsum,
+                                          const float2* __restrict__ rnorm, uint32_t (&kbound)[2]) {
   const int tid = threadIdx.x;
   const int gbeg = base & ~3;
   const bool cached = keys_lds != nullptr;
@@ -303,6 +345,11 @@ __device__ __forceinline__ void scan_keep(const uint32_t* keys_lds, const float*
         if (kp) {
           if (pos < q) perm[seg + pos] = g;   // pos < q holds by construction
           ++pos;
+          if (rnorm != nullptr) {
+            const float2 m = rnorm[g];
+            kbound[0] = max(kbound[0], __float_as_uint(m.x));
+            kbound[1] = max(kbound[1], __float_as_uint(m.y));
+          }
         }
       }
     }
@@ -330,7 +377,8 @@ __device__ __forceinline__ void scan_keep(const uint32_t* keys_lds, const float*
 __global__ __launch_bounds__(kSelThreads) void select_scan_kernel(
     ExpertTable tab, const float* __restrict__ scores, uint8_t* __restrict__ keep,
     int32_t* __restrict__ perm, int32_t* __restrict__ seg_offsets_out,
-    const uint32_t* __restrict__ hist_in, uint32_t* __restrict__ tau_need) {
+    const uint32_t* __restrict__ hist_in, uint32_t* __restrict__ tau_need,
+    const float2* __restrict__ rnorm, float* __restrict__ ebound) {
   __shared__ uint32_t keys_lds[kSelLdsKeys];   // the expert's keys, or the candidates
   __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
   __shared__ uint32_t wsum[kSelWaves];
@@ -347,12 +395,18 @@ __global__ __launch_bounds__(kSelThreads) void select_scan_kernel(
   const int seg = tab.seg_off[e];
   const uint32_t q = (uint32_t)(tab.seg_off[e + 1] - seg);
 
+  const bool cached = n <= kSelLdsKeys;
   if (tid == 0) {
     seg_offsets_out[e] = seg;
     if (e == tab.E - 1) seg_offsets_out[tab.E] = tab.seg_off[tab.E];
+    // largest kept row norms: an empty expert keeps 0; a large one starts at 0 and
+    // its chunk scans merge into it
+    if (ebound != nullptr && (n == 0 || !cached)) {
+      ebound[2 * e] = 0.f;
+      ebound[2 * e + 1] = 0.f;
+    }
   }
   if (n == 0) return;
-  const bool cached = n <= kSelLdsKeys;
   if (cached) {
     for (int a = gbeg + 4 * tid; a < end; a += 4 * kSelThreads) {
       const float4 v = load4(scores, a, P);
@@ -448,7 +502,10 @@ __global__ __launch_bounds__(kSelThreads) void select_scan_kernel(
     }
     return;
   }
-  scan_keep(keys_lds, scores, P, base, end, base, tau, need, 0u, 0u, q, seg, keep, perm, wsum);
+  uint32_t kbound[2] = {0u, 0u};
+  scan_keep(keys_lds, scores, P, base, end, base, tau, need, 0u, 0u, q, seg, keep, perm, wsum,
+            ebound != nullptr ? rnorm : nullptr, kbound);
+  if (ebound != nullptr) put_kept_bound(kbound, wsum, ebound, e, false);
 }
 
 // Large experts (more than kSelLdsKeys pairs), after select_scan_kernel has
@@ -483,7 +540,8 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_count_kernel(
 __global__ __launch_bounds__(kSelThreads) void select_chunk_scan_kernel(
     ExpertTable tab, const float* __restrict__ scores, uint8_t* __restrict__ keep,
     int32_t* __restrict__ perm, const uint32_t* __restrict__ tau_need,
-    const uint32_t* __restrict__ counts) {
+    const uint32_t* __restrict__ counts, const float2* __restrict__ rnorm,
+    float* __restrict__ ebound) {
   __shared__ uint32_t wsum[kSelWaves];
   const int b = blockIdx.x;
   int e = 0;
@@ -497,8 +555,11 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_scan_kernel(
   }
   const int seg = tab.seg_off[e];
   const uint32_t q = (uint32_t)(tab.seg_off[e + 1] - seg);
+  uint32_t kbound[2] = {0u, 0u};
   scan_keep(nullptr, scores, tab.pair_off[tab.E], lo, hi, 0, tau_need[2 * e],
-            tau_need[2 * e + 1], run_gt, run_eq, q, seg, keep, perm, wsum);
+            tau_need[2 * e + 1], run_gt, run_eq, q, seg, keep, perm, wsum,
+            ebound != nullptr ? rnorm : nullptr, kbound);
+  if (ebound != nullptr) put_kept_bound(kbound, wsum, ebound, e, true);
 }
 
 }  // namespace
@@ -506,18 +567,23 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_scan_kernel(
 template <int MODE>
 void launch_score_mode(int dtype, dim3 grid, hipStream_t s, const void* g, const void* phi,
                        const float* alpha, const int32_t* row_index, int32_t P, int32_t T,
-                       int32_t d_out, int32_t d_in, float* scores) {
-  if (dtype == LRMOE_BF16)
+                       int32_t d_out, int32_t d_in, float* scores, float2* rnorm,
+                       int alpha_on_phi) {
+  if (dtype == LRMOE_BF16 && rnorm != nullptr)
+    hipLaunchKernelGGL((lrm_score_kernel<true, MODE, true>), grid, dim3(256), 0, s, g, phi, alpha,
+                       row_index, P, T, d_out, d_in, scores, rnorm, alpha_on_phi);
+  else if (dtype == LRMOE_BF16)
     hipLaunchKernelGGL((lrm_score_kernel<true, MODE>), grid, dim3(256), 0, s, g, phi, alpha,
-                       row_index, P, T, d_out, d_in, scores);
+                       row_index, P, T, d_out, d_in, scores, rnorm, alpha_on_phi);
   else
     hipLaunchKernelGGL((lrm_score_kernel<false, MODE>), grid, dim3(256), 0, s, g, phi, alpha,
-                       row_index, P, T, d_out, d_in, scores);
+                       row_index, P, T, d_out, d_in, scores, rnorm, alpha_on_phi);
 }
 
 hipError_t launch_score(int dtype, int mode, const void* g, const void* phi, const float* alpha,
                         const int32_t* row_index, int32_t P, int32_t T, int32_t d_out,
-                        int32_t d_in, float* scores, hipStream_t s) {
+                        int32_t d_in, float* scores, hipStream_t s, float2* rnorm,
+                        int alpha_on_phi) {
   if (P <= 0) return hipSuccess;
   const int waves_per_block = 4;
   int blocks = (P + waves_per_block - 1) / waves_per_block;
@@ -525,19 +591,19 @@ hipError_t launch_score(int dtype, int mode, const void* g, const void* phi, con
   const dim3 grid(blocks);
   if (mode == LRMOE_SCORE_GRAD_SQNORM)
     launch_score_mode<LRMOE_SCORE_GRAD_SQNORM>(dtype, grid, s, g, phi, alpha, row_index, P, T,
-                                               d_out, d_in, scores);
+                                               d_out, d_in, scores, rnorm, alpha_on_phi);
   else if (mode == LRMOE_SCORE_GRAD_L1)
     launch_score_mode<LRMOE_SCORE_GRAD_L1>(dtype, grid, s, g, phi, alpha, row_index, P, T,
-                                           d_out, d_in, scores);
+                                           d_out, d_in, scores, rnorm, alpha_on_phi);
   else
     launch_score_mode<LRMOE_SCORE_LRM>(dtype, grid, s, g, phi, alpha, row_index, P, T, d_out,
-                                       d_in, scores);
+                                       d_in, scores, rnorm, alpha_on_phi);
   return hipGetLastError();
 }
 
 hipError_t launch_select_scan(const ExpertTable& tab, const float* scores, uint8_t* keep,
                               int32_t* perm, int32_t* seg_offsets_out, uint32_t* hist,
-                              hipStream_t s) {
+                              hipStream_t s, const float2* rnorm, float* ebound) {
   const int chunks = tab.hist_off[tab.E];
   // workspace: chunk histograms, then tau / need per expert, then per-chunk counts
   uint32_t* tau_need = hist + (size_t)chunks * kBins;
@@ -549,7 +615,7 @@ hipError_t launch_select_scan(const ExpertTable& tab, const float* scores, uint8
     if (err != hipSuccess) return err;
   }
   hipLaunchKernelGGL(select_scan_kernel, dim3(tab.E), dim3(kSelThreads), 0, s, tab, scores,
-                     keep, perm, seg_offsets_out, hist, tau_need);
+                     keep, perm, seg_offsets_out, hist, tau_need, rnorm, ebound);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || chunks == 0) return err;
   hipLaunchKernelGGL(select_chunk_count_kernel, dim3(chunks), dim3(kSelThreads), 0, s, tab,
@@ -557,7 +623,7 @@ hipError_t launch_select_scan(const ExpertTable& tab, const float* scores, uint8
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(select_chunk_scan_kernel, dim3(chunks), dim3(kSelThreads), 0, s, tab,
-                     scores, keep, perm, tau_need, counts);
+                     scores, keep, perm, tau_need, counts, rnorm, ebound);
   return hipGetLastError();
 }
 

@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "liblrmoe.so")
 
 F32, BF16 = 0, 1
-DW_EXACT, DW_BF16 = 0, 1
+DW_EXACT, DW_BF16, DW_F16 = 0, 1, 2
 SCORE_LRM, SCORE_GRAD_SQNORM, SCORE_GRAD_L1 = 0, 1, 2
 QUOTA_RATIO, QUOTA_BUDGET = 0, 1
 MAX_EXPERTS = 256

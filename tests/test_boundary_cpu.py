@@ -171,17 +171,25 @@ def test_workspace_size_and_check():
     n = p.workspace_bytes()
     # exact mode, bf16: the plain grouped backward keeps alpha * phi (the
     # narrower operand) as hi + lo planes; the gate/up variant (float32 g_c)
-    # alpha * g_c as hi + lo planes; no split-K partials at this size, 256
-    # bytes of GEMM queue counters.  One size serves every call: the larger.
+    # alpha * g_c as hi + lo planes; no split-K partials at this size, then
+    # the GEMM's queue counters (256 bytes) and the float16 mode's expert
+    # maxima (2 floats for each of up to 256 experts).  One size serves every
+    # call: the larger.
+    heads = 256 + 2 * 256 * 4
     plane_phi = (60 * 32 * 2 + 255) // 256 * 256
     plane_g = (60 * 64 * 2 + 255) // 256 * 256
-    assert n == max(2 * plane_phi, 2 * plane_g) + 256
+    assert n == max(2 * plane_phi, 2 * plane_g) + heads
     for f in (L.lib().lrmoe_grouped_backward, L.lib().lrmoe_grouped_backward_gate_up):
         assert f(C.byref(p.struct), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n - 1,
                  None) == 6
         assert f(C.byref(p.struct), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, n, None) == 1
     p1 = plan(counts=(40, 20, 30), quotas=(30, 10, 20), d_out=64, d_in=32, dw_mode=L.DW_BF16)
-    assert p1.workspace_bytes() == max(plane_phi, plane_g) + 256
+    assert p1.workspace_bytes() == max(plane_phi, plane_g) + heads
+    # float16 mode: counters and maxima, the score pass's per-pair row maxima
+    # (8 bytes per routed pair), then both float16 operand planes
+    p2 = plan(counts=(40, 20, 30), quotas=(30, 10, 20), d_out=64, d_in=32, dw_mode=L.DW_F16)
+    f16 = (heads + 90 * 8 + 255) // 256 * 256 + plane_g + plane_phi
+    assert p2.workspace_bytes() == max(f16, 2 * plane_g + heads)
 
 
 def test_grouped_backward_gate_up_validation():

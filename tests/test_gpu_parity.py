@@ -70,6 +70,86 @@ def test_medium(idx):
     print(name, errs, "keep identical" if same else "keep differs inside band")
 
 
+MEDIUM_F16 = [(i, m) for i, m in enumerate(MEDIUM) if m[1]["dtype"] == "bf16"]
+
+
+@pytest.mark.parametrize("j", range(len(MEDIUM_F16)), ids=[m[0] + "-f16" for _, m in MEDIUM_F16])
+def test_medium_f16(j):
+    """The float16 weight-gradient mode (one matrix-core pass on float16
+    planes, alpha * operand rounded once to 11 significant bits, per-expert
+    power-of-two scales) on the medium shapes: keep set, compaction and dphi
+    as always, dW within 2e-3 max|ref| of the oracle."""
+    idx, (name, kw, policy) = MEDIUM_F16[j]
+    p = W.make_problem(seed=100 + idx, policy=policy, name=name, **kw)
+    q = lrmoe.plan_quota(p.counts, policy)
+    plan, out, _ = U.run_gpu(p, q, dw_mode=lrmoe.DW_F16)
+    errs, same = U.compare_full(p, q, out, dw_mode=lrmoe.DW_F16)
+    print(name, "f16", errs)
+
+
+def _scaled_rows(x, offsets, factors):
+    """bf16 rows of each expert multiplied by its factor (rounded to bf16)."""
+    v = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for e, f in enumerate(factors):
+        v[offsets[e]:offsets[e + 1]] *= f
+    return W.to_bf16_bits(v.astype(np.float32))
+
+
+@pytest.mark.parametrize("swap", [False, True], ids=["alpha-on-phi", "alpha-on-g"])
+def test_f16_wide_range_per_expert(swap):
+    """The float16 mode on inputs far outside float16's range: every expert's
+    g rows and phi rows carry their own power of ten (g from 1e-7 to 1e5,
+    phi from 1e-4 to 1e3), so unscaled products would overflow 65504 or
+    vanish below float16's smallest normal.  The per-expert scales must map
+    each expert into range: every expert's dW within 2e-3 of its own max|ref|
+    (not just of the whole tensor's), through both paths (one call, and the
+    separate calls whose prologue finds the scales), bit for bit alike."""
+    import dataclasses
+    counts = [400, 300, 350, 250, 300]
+    d_out, d_in = (136, 200) if swap else (200, 136)
+    p = W.make_problem(P=sum(counts), E=5, d_out=d_out, d_in=d_in, dtype="bf16", counts=counts,
+                       seed=61, policy=("ratio", 4, 5), name="wide-range")
+    off = p.offsets
+    p = dataclasses.replace(p, g=_scaled_rows(p.g, off, [1e-7, 1e-2, 1.0, 1e3, 1e5]),
+                            phi=_scaled_rows(p.phi, off, [1e3, 1e-4, 1.0, 10.0, 1e-2]))
+    q = lrmoe.plan_quota(p.counts, p.policy)
+    plan, sep, t = U.run_gpu(p, q, dw_mode=lrmoe.DW_F16)
+    one = lrmoe.pruned_backward(plan, t["alpha"], t["g"], t["phi"], t["W"])
+    torch.cuda.synchronize()
+    for k in ("keep", "perm", "dW", "dphi"):
+        assert torch.equal(sep[k], one[k]), k
+    keep = sep["keep"].cpu().numpy().astype(bool)
+    perm, seg = O.compact(keep, p.counts, q)
+    g_c, phi_c, a_c = O.gather(perm, None, p.g, p.phi, p.alpha)
+    dW_ref = O.weight_grad(seg, a_c, g_c, phi_c, "bf16", p.E, p.d_out, p.d_in)
+    dW = sep["dW"].cpu().numpy()
+    per_expert = [U.rel_err(dW[e], dW_ref[e]) for e in range(p.E)]
+    print("wide-range per-expert dW err", per_expert)
+    assert max(per_expert) <= U.TOL, per_expert
+    dphi_ref = O.input_grad(seg, perm, a_c, g_c, p.W, "bf16", p.P)
+    dphi = sep["dphi"].cpu().numpy()
+    for e in range(p.E):   # dphi per expert block too (bf16 matrix cores, alpha in float32)
+        lo, hi = off[e], off[e + 1]
+        assert U.rel_err(dphi[lo:hi], dphi_ref[lo:hi]) <= U.TOL, e
+
+
+def test_f16_token_rows():
+    """The float16 mode with per-token g rows through a row index (top-2
+    routing of 700 tokens): the score pass takes each pair's g row maximum
+    through the index.  Oracle parity, and the one-call path bit for bit the
+    separate calls."""
+    p = W.make_token_problem(T=700, E=6, topk=2, d_out=48, d_in=40, dtype="bf16", seed=373,
+                             policy=("ratio", 3, 4))
+    q = lrmoe.plan_quota(p.counts, p.policy)
+    plan, sep, t = U.run_gpu(p, q, dw_mode=lrmoe.DW_F16)
+    errs, _ = U.compare_full(p, q, sep, dw_mode=lrmoe.DW_F16)
+    one = lrmoe.pruned_backward(plan, t["alpha"], t["g"], t["phi"], t["W"], g_row_index=t["row"])
+    torch.cuda.synchronize()
+    for k in ("keep", "perm", "dW", "dphi"):
+        assert torch.equal(sep[k], one[k]), k
+    print("f16 token rows", errs)
+
+
 def test_dw_single_rounding_mode():
     """The one-pass bf16(alpha*x) mode: same keep set and dphi; dW within the
     per-element bound of that one bf16 rounding."""
@@ -127,7 +207,7 @@ def test_ablation_score_modes(mode, name):
         print(name, p.name, errs)
 
 
-@pytest.mark.parametrize("dw_mode", [lrmoe.DW_EXACT, lrmoe.DW_BF16])
+@pytest.mark.parametrize("dw_mode", [lrmoe.DW_EXACT, lrmoe.DW_BF16, lrmoe.DW_F16])
 def test_masked_dense_matches_compacted(dw_mode):
     """The zero-masked dense alternative (alpha := 0 on dropped pairs, the
     same GEMMs over every routed pair, nothing compacted) reproduces the
@@ -151,7 +231,7 @@ def test_masked_dense_matches_compacted(dw_mode):
     dphi = out["dphi"].cpu().numpy()
     assert U.rel_err(dphi, dphi_ref) <= U.TOL
     assert np.all(dphi[~keep] == 0)
-    if dw_mode == lrmoe.DW_EXACT:
+    if dw_mode != lrmoe.DW_BF16:
         assert U.rel_err(out["dW"].cpu().numpy(), dW_ref) <= U.TOL
     else:
         # single rounding of alpha * operand: within that rounding's per-element
@@ -224,6 +304,8 @@ GLU_CASES = [
                             gate_up=(656, 264)), lrmoe.DW_EXACT),
     ("glu-bf16-single-rounding", dict(P=2000, E=6, d_out=256, d_in=256, zipf=1.2,
                                       gate_up=(512, 128)), lrmoe.DW_BF16),
+    ("glu-f16", dict(P=2200, E=5, d_out=264, d_in=200, zipf=1.4, gate_up=(400, 136)),
+     lrmoe.DW_F16),
 ]
 
 
@@ -432,6 +514,15 @@ WHOLE = [
     ("fp32", dict(P=1500, E=4, d_out=196, d_in=140, dtype="f32", zipf=1.2), lrmoe.DW_EXACT),
     ("large-expert", dict(P=40000, E=2, d_out=64, d_in=72, dtype="bf16", counts=[39000, 1000]),
      lrmoe.DW_EXACT),
+    # float16 weight gradient: the one call takes the expert scales from the
+    # score pass and the select (a large expert's chunks merge them), the
+    # separate calls from their own prologue over the compacted rows
+    ("f16-alpha-on-phi", dict(P=3000, E=5, d_out=264, d_in=200, dtype="bf16",
+                              counts=[1400, 0, 977, 7, 616]), lrmoe.DW_F16),
+    ("f16-alpha-on-g", dict(P=2500, E=4, d_out=136, d_in=392, dtype="bf16", zipf=1.6),
+     lrmoe.DW_F16),
+    ("f16-large-expert", dict(P=40000, E=2, d_out=64, d_in=72, dtype="bf16",
+                              counts=[39000, 1000]), lrmoe.DW_F16),
 ]
 
 
@@ -453,7 +544,7 @@ def test_whole_path_call_matches_separate_calls(idx):
         if a.dtype == torch.bfloat16:
             a, b = a.view(torch.int16), b.view(torch.int16)
         assert torch.equal(a, b), (name, k)
-    if idx == 0:   # and the oracle agrees with both
+    if idx == 0 or dw_mode == lrmoe.DW_F16:   # and the oracle agrees with both
         errs, _ = U.compare_full(p, q, one, dw_mode=dw_mode)
         print(name, errs)
 
@@ -483,6 +574,40 @@ def _random_problem(seed):
     p = W.make_problem(P=P, E=E, d_out=d_out, d_in=d_in, dtype=dtype, counts=counts,
                        seed=500 + seed, policy=policy, name=f"random-{seed}")
     return p, policy, dw_mode
+
+
+def _random_problem_f16(seed):
+    """Seeded random bf16 shape for the float16 mode (as _random_problem)."""
+    rng = np.random.default_rng(9500 + seed)
+    E = int(rng.integers(1, 13))
+    P = int(rng.integers(1, 64)) if seed % 3 == 1 else int(rng.integers(64, 6001))
+    d_out, d_in = 8 * int(rng.integers(1, 76)), 8 * int(rng.integers(1, 76))
+    w = rng.random(E) * (rng.random(E) > 0.2)
+    if w.sum() == 0:
+        w[0] = 1.0
+    counts = rng.multinomial(P, w / w.sum())
+    den = int(rng.integers(1, 11))
+    policy = ("ratio", int(rng.integers(0, den + 1)), den)
+    p = W.make_problem(P=P, E=E, d_out=d_out, d_in=d_in, dtype="bf16", counts=counts,
+                       seed=550 + seed, policy=policy, name=f"random-f16-{seed}")
+    return p, policy
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_shapes_f16(seed):
+    """The float16 mode on random shapes: oracle parity (dW and dphi within
+    2e-3 max|ref|) and the one call bit for bit the separate calls."""
+    p, policy = _random_problem_f16(seed)
+    q = lrmoe.plan_quota(p.counts, policy)
+    print(f"random-f16-{seed}: P={p.P} E={p.E} d_out={p.d_out} d_in={p.d_in} {policy} "
+          f"M={sum(q)}", flush=True)
+    plan, sep, t = U.run_gpu(p, q, dw_mode=lrmoe.DW_F16)
+    errs, same = U.compare_full(p, q, sep, dw_mode=lrmoe.DW_F16)
+    one = lrmoe.pruned_backward(plan, t["alpha"], t["g"], t["phi"], t["W"])
+    torch.cuda.synchronize()
+    for k in ("keep", "perm", "seg_offsets", "dW", "dphi"):
+        assert torch.equal(sep[k], one[k]), (seed, k)
+    print(f"random-f16-{seed}", errs)
 
 
 @pytest.mark.parametrize("seed", range(10))
