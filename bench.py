@@ -75,12 +75,13 @@ def gemm_sources_sha256() -> str:
     return h.hexdigest()
 
 
-def read_counters(workload: str, dw_mode: str):
-    """HBM bytes per launch of the grouped GEMM from a committed rocprofv3
-    counter summary: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
-    scaled by bytes / counter of a plain copy of known size.  None when no
-    summary was taken on this workload and dW mode, or the kernel sources
-    changed since."""
+def read_counters(workload: str, dw_mode: str, leg: str = "down"):
+    """Counters of the grouped GEMM from a committed rocprofv3 summary:
+    HBM bytes per launch (FETCH_SIZE and WRITE_SIZE, KiB per dispatch, each
+    scaled by bytes / counter of a plain copy of known size) and the MFMA
+    busy fraction.  (None, None) when no summary was taken on this workload,
+    dW mode and leg (the down projection, or the gate/up one), or the kernel
+    sources changed since."""
     import glob
     sha = gemm_sources_sha256()
     for path in sorted(glob.glob(os.path.join(ROOT, COUNTERS_GLOB))):
@@ -93,16 +94,17 @@ def read_counters(workload: str, dw_mode: str):
                     kv[k.strip()] = v.strip()
         try:
             if (kv["workload"] != workload or kv["dw_mode"] != dw_mode
-                    or kv["kernel_sources_sha256"] != sha):
+                    or kv.get("leg", "down") != leg or kv["kernel_sources_sha256"] != sha):
                 continue
             fetch = (float(kv["gemm_fetch_kib"]) * float(kv["copy_bytes"])
                      / float(kv["copy_fetch_kib"]))
             write = (float(kv["gemm_write_kib"]) * float(kv["copy_bytes"])
                      / float(kv["copy_write_kib"]))
+            busy = float(kv["mfma_busy_frac"]) if "mfma_busy_frac" in kv else None
         except (KeyError, ValueError, ZeroDivisionError):
             continue
-        return fetch + write
-    return None
+        return fetch + write, busy
+    return None, None
 
 
 def copy_calibration(reps: int = 10):
@@ -174,7 +176,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=4,
                     help="workload (4: GLM4.5 20x batch-pressure share, the largest)")
-    ap.add_argument("--dw-mode", choices=["exact", "bf16", "f16"], default="exact",
+    ap.add_argument("--dw-mode", choices=["exact", "bf16", "f16"], default="f16",
                     help="weight-gradient folding of alpha: exact (bf16 hi + lo, two "
                          "passes), bf16 (one rounding), f16 (one pass on float16 planes)")
     ap.add_argument("--score-mode", choices=["lrm", "grad-sqnorm", "grad-l1", "random"],
@@ -444,13 +446,16 @@ def main():
     else:
         Mx = p.P if dense_path else M
         exec_flops = 2.0 * Mx * p.d_out * p.d_in * (terms_dw + terms_dp)
+    # committed counters of the dominant launch (the gate/up leg where there is one)
+    traffic, mfma_busy = (None, None) if chain or dense_path else read_counters(
+        p.name, args.dw_mode, "gate_up" if gu is not None else "down")
     roof = dict(kernel="grouped_backward_kernel", bound="mfma", achieved=gemm_tf,
                 peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s", frac=gemm_tf / MFMA_BF16_PEAK_TFLOPS,
                 mfma_executed_TFLOPs=exec_flops / gemm_live["mean"] / 1e6,
                 launch_us_mean=gemm_live["mean"], launch_us_median=gemm_live["median"],
                 launches=gemm_live["launches"],
-                traffic=None if gu is not None else read_counters(p.name, args.dw_mode),
-                traffic_unit="bytes per launch",
+                traffic=traffic, traffic_unit="bytes per launch",
+                mfma_busy_frac=mfma_busy,
                 algorithmic_bytes_floor=gemm_floor_bytes(p, M))
     if gu is not None:
         roof["note"] = "the gate/up projection's grouped GEMM (its flops 4 M d_out2 d_in2)"
