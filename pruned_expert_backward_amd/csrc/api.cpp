@@ -471,8 +471,8 @@ lrmoe_status grouped_backward(const lrmoe_problem* pb, const int32_t* perm, cons
   if (wl.f16) {
     // float16 planes of both weight-gradient operands, scaled per expert by
     // the powers of two of the kept rows' largest norms (the gather wrote
-    // them in the one-call path; here: clear counters and bounds, bounds,
-    // planes)
+    // them in the one-call path; here: clear the counters, then the bounds
+    // from the compacted rows, then the planes)
     uint16_t* fa = plane(wl.a_hi);
     uint16_t* fb = plane(wl.b_hi);
     if (!planes_ready) {
@@ -481,9 +481,11 @@ lrmoe_status grouped_backward(const lrmoe_problem* pb, const int32_t* perm, cons
       for (int e = 0; e <= E; ++e) seg.off[e] = c.tab.seg_off[e];
       const uint16_t* gc16 = reinterpret_cast<const uint16_t*>(g_c);
       const uint16_t* pc16 = reinterpret_cast<const uint16_t*>(phi_c);
-      LRMOE_TRY(hip_status(launch_zero(heads, (int)((kEmaxOff + 2 * E * sizeof(float)) / 4), s)));
-      LRMOE_TRY(hip_status(launch_rows_bound(seg, gc16, pc16, alpha_c, (int32_t)M, d_out, d_in,
-                                              wl.alpha_on_phi, ebound, s)));
+      LRMOE_TRY(hip_status(launch_zero(heads, kXcds, s)));
+      LRMOE_TRY(hip_status(launch_expert_bounds(
+          seg, gc16, pc16, alpha_c, nullptr, nullptr, nullptr, (int32_t)M, (int32_t)M,
+          (int32_t)M, (int32_t)M, d_out, d_in, wl.alpha_on_phi,
+          reinterpret_cast<float2*>(ws + wl.rnorm), ebound, s)));
       LRMOE_TRY(hip_status(launch_split_f16(seg, gc16, pc16, alpha_c, (int32_t)M, d_out, d_in,
                                             wl.alpha_on_phi, ebound, fa, fb, s)));
     }
@@ -622,19 +624,19 @@ lrmoe_status pruned_backward(const lrmoe_problem* pb, const int32_t* g_row_index
 }
 
 
-lrmoe_status gather_compact(const lrmoe_problem* pb, const int32_t* perm, const uint8_t* keep,
-                            const int32_t* g_row_index, const int32_t* phi_row_index,
-                            const float* alpha, const void* g, const void* phi, void* g_c,
-                            void* phi_c, float* alpha_c, float* dphi_zero, void* stream,
-                            const lrmoe_timing* timing, const GatherPlanes& planes) {
-  Checked c;
-  LRMOE_TRY(check_problem(pb, c));
+// Validation of a gather on an inherited keep set (every host-detectable
+// problem); phi_rows: the rows of phi its row index may address.
+lrmoe_status check_gather(const lrmoe_problem* pb, const Checked& c, const int32_t* perm,
+                          const uint8_t* keep, const int32_t* g_row_index,
+                          const int32_t* phi_row_index, const float* alpha, const void* g,
+                          const void* phi, void* g_c, void* phi_c, float* alpha_c,
+                          float* dphi_zero, const GatherPlanes& planes, int64_t& phi_rows) {
   const int64_t P = pb->P, M = c.M;
   const bool with_g = g != nullptr || g_c != nullptr;   // both NULL: phi rows only
   if (with_g && g_row_index == nullptr && pb->T != P) return LRMOE_ERR_SHAPE;
   if (with_g && M > 0 && pb->T < 1) return LRMOE_ERR_SHAPE;
   // rows of phi: T_phi through a row index, else one per pair
-  const int64_t phi_rows = phi_row_index != nullptr ? pb->T_phi : P;
+  phi_rows = phi_row_index != nullptr ? pb->T_phi : P;
   if (phi_row_index != nullptr && M > 0 &&
       (pb->T_phi < 1 || pb->T_phi >= (int64_t(1) << 31)))
     return LRMOE_ERR_SHAPE;
@@ -651,15 +653,38 @@ lrmoe_status gather_compact(const lrmoe_problem* pb, const int32_t* perm, const 
   LRMOE_TRY(need(alpha_c, M));
   LRMOE_TRY(optional(dphi_zero));
   if (dphi_zero != nullptr) LRMOE_TRY(need(keep, P));
-  if (planes.hi != nullptr && !with_g && !planes.from_phi) return LRMOE_ERR_NULL;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if ((planes.hi != nullptr || planes.f16_a != nullptr) && !with_g) return LRMOE_ERR_NULL;
+  return LRMOE_OK;
+}
+
+lrmoe_status launch_gather_timed(const lrmoe_problem* pb, const Checked& c, const int32_t* perm,
+                                 const uint8_t* keep, const int32_t* g_row_index,
+                                 const int32_t* phi_row_index, const float* alpha,
+                                 const void* g, const void* phi, void* g_c, void* phi_c,
+                                 float* alpha_c, float* dphi_zero, int64_t phi_rows,
+                                 hipStream_t s, const lrmoe_timing* timing,
+                                 const GatherPlanes& planes) {
   LRMOE_TRY(mark(timing, false, 2, s));
   LRMOE_TRY(hip_status(launch_gather(pb->dtype, perm, keep, g_row_index, phi_row_index, alpha, g,
-                                     phi, g_c, phi_c, alpha_c, dphi_zero, (int32_t)M,
-                                     (int32_t)P, (int32_t)pb->T, (int32_t)phi_rows, pb->d_out,
-                                     pb->d_in, s, planes)));
-  LRMOE_TRY(mark(timing, true, 2, s));
-  return LRMOE_OK;
+                                     phi, g_c, phi_c, alpha_c, dphi_zero, (int32_t)c.M,
+                                     (int32_t)pb->P, (int32_t)pb->T, (int32_t)phi_rows,
+                                     pb->d_out, pb->d_in, s, planes)));
+  return mark(timing, true, 2, s);
+}
+
+lrmoe_status gather_compact(const lrmoe_problem* pb, const int32_t* perm, const uint8_t* keep,
+                            const int32_t* g_row_index, const int32_t* phi_row_index,
+                            const float* alpha, const void* g, const void* phi, void* g_c,
+                            void* phi_c, float* alpha_c, float* dphi_zero, void* stream,
+                            const lrmoe_timing* timing, const GatherPlanes& planes) {
+  Checked c;
+  LRMOE_TRY(check_problem(pb, c));
+  int64_t phi_rows = 0;
+  LRMOE_TRY(check_gather(pb, c, perm, keep, g_row_index, phi_row_index, alpha, g, phi, g_c, phi_c,
+                         alpha_c, dphi_zero, planes, phi_rows));
+  return launch_gather_timed(pb, c, perm, keep, g_row_index, phi_row_index, alpha, g, phi, g_c,
+                             phi_c, alpha_c, dphi_zero, phi_rows,
+                             reinterpret_cast<hipStream_t>(stream), timing, planes);
 }
 
 // Step 4 + step 5 for a projection on an inherited keep set: the gather also
@@ -681,24 +706,45 @@ lrmoe_status gather_backward(const lrmoe_problem* pb, const int32_t* perm, const
   if (ws_bytes < workspace_bytes(pb, c)) return LRMOE_ERR_WORKSPACE;
   LRMOE_TRY(need(workspace, (int64_t)wl.total));
   GatherPlanes planes;
-  // float16 mode: no score pass to take the expert bounds from, so the
-  // grouped backward's own prologue finds them from the compacted rows
-  const bool fused = pb->dtype == LRMOE_BF16 && !wl.f16;
+  const bool fused = pb->dtype == LRMOE_BF16;   // the gather writes the GEMM's planes
+  char* ws = reinterpret_cast<char*>(workspace);
   if (fused) {
-    char* ws = reinterpret_cast<char*>(workspace);
-    planes.hi = reinterpret_cast<uint16_t*>(ws + wl.b_hi);
-    planes.lo = pb->dw_mode == LRMOE_DW_EXACT ? reinterpret_cast<uint16_t*>(ws + wl.b_lo)
-                                              : nullptr;
     planes.from_phi = wl.alpha_on_phi;
     planes.zero = reinterpret_cast<int32_t*>(ws + wl.heads);
     planes.nzero = kXcds;
+    if (wl.f16) {
+      planes.f16_a = reinterpret_cast<uint16_t*>(ws + wl.a_hi);
+      planes.f16_b = reinterpret_cast<uint16_t*>(ws + wl.b_hi);
+      planes.ebound = reinterpret_cast<float*>(ws + wl.heads + kEmaxOff);
+      planes.seg.E = pb->E;
+      for (int e = 0; e <= pb->E; ++e) planes.seg.off[e] = c.tab.seg_off[e];
+    } else {
+      planes.hi = reinterpret_cast<uint16_t*>(ws + wl.b_hi);
+      planes.lo = pb->dw_mode == LRMOE_DW_EXACT ? reinterpret_cast<uint16_t*>(ws + wl.b_lo)
+                                                : nullptr;
+    }
   }
-  LRMOE_TRY(gather_compact(pb, perm, keep, g_row_index, phi_row_index, alpha, g, phi, g_c, phi_c,
-                           alpha_c, dphi, stream, timing, planes));
+  int64_t phi_rows = 0;
+  LRMOE_TRY(check_gather(pb, c, perm, keep, g_row_index, phi_row_index, alpha, g, phi, g_c, phi_c,
+                         alpha_c, dphi, planes, phi_rows));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   TimingSlots ts;
   ts.gemm = 3;
   ts.reduce = 4;
   ts.prologue = 5;
+  if (fused && wl.f16) {
+    // float16 planes: no score pass to take the expert bounds from, so they
+    // come from the source rows the gather is about to copy (slot 5)
+    LRMOE_TRY(mark(timing, false, ts.prologue, s));
+    LRMOE_TRY(hip_status(launch_expert_bounds(
+        planes.seg, reinterpret_cast<const uint16_t*>(g), reinterpret_cast<const uint16_t*>(phi),
+        alpha, perm, g_row_index, phi_row_index, (int32_t)c.M, (int32_t)pb->P, (int32_t)pb->T,
+        (int32_t)phi_rows, pb->d_out, pb->d_in, wl.alpha_on_phi,
+        reinterpret_cast<float2*>(ws + wl.rnorm), planes.ebound, s)));
+    LRMOE_TRY(mark(timing, true, ts.prologue, s));
+  }
+  LRMOE_TRY(launch_gather_timed(pb, c, perm, keep, g_row_index, phi_row_index, alpha, g, phi, g_c,
+                                phi_c, alpha_c, dphi, phi_rows, s, timing, planes));
   return grouped_backward(pb, perm, alpha_c, g_c, phi_c, W, dW, dphi, false, nullptr, nullptr,
                           nullptr, workspace, ws_bytes, stream, timing, fused, ts);
 }

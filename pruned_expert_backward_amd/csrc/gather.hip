@@ -173,45 +173,72 @@ __global__ __launch_bounds__(256) void gather_kernel(
   }
 }
 
-// Float16 weight-gradient mode, separate-call path, step 1: per expert, the
-// largest row norm of A and of B over its compacted rows, the side carrying
-// alpha times |alpha_j| (bit for bit the values the score pass produces per
-// pair in the one-call path: the same row_norm_bf16).  Each wave takes a
-// contiguous range of rows and merges its running largest norms into ebound
-// (atomicMax on non-negative float32 bits) whenever the expert changes and
-// at the end.
-__global__ __launch_bounds__(256) void rows_bound_kernel(
-    SegTable seg, const uint4* __restrict__ g_c, const uint4* __restrict__ phi_c,
-    const float* __restrict__ alpha_c, int32_t M, int32_t gch, int32_t pch, int alpha_on_phi,
-    float* __restrict__ ebound) {
+// Float16 weight-gradient mode, step 1: the Euclidean norms of both
+// weight-gradient operand rows of every compacted row j into rn[j] = {|A
+// row|, |B row|} (A the g row, B the phi row, the side carrying alpha times
+// |alpha|), one wave per row, grid-strided.  The rows are read from the
+// compacted buffers (perm null: row j, alpha[j] = alpha_c[j]), or through
+// perm from the source rows the gather is about to copy.  Either way the
+// values are bit for bit the score pass's per-pair norms (row_norm_bf16);
+// rows outside the sources read as zero rows, as in the gather.
+__global__ __launch_bounds__(256) void row_norms_kernel(
+    const uint4* __restrict__ g, const uint4* __restrict__ phi, const float* __restrict__ alpha,
+    const int32_t* __restrict__ perm, const int32_t* __restrict__ g_row_index,
+    const int32_t* __restrict__ phi_row_index, int32_t M, int32_t P, int32_t g_rows,
+    int32_t phi_rows, int32_t gch, int32_t pch, int alpha_on_phi, float2* __restrict__ rn) {
   const int lane = threadIdx.x & 63;
   const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int nwaves = (gridDim.x * blockDim.x) >> 6;
-  const int per = (M + nwaves - 1) / nwaves;
-  const int j0 = wave * per, j1 = min(M, j0 + per);
-  uint32_t* em = reinterpret_cast<uint32_t*>(ebound);
-  int cur = -1;
-  uint32_t ma = 0u, mb = 0u;
-  for (int j = j0; j < j1; ++j) {
-    const int e = expert_of_row(seg, j);
-    if (e != cur) {
-      if (cur >= 0 && lane == 0) {
-        atomicMax(em + 2 * cur, ma);
-        atomicMax(em + 2 * cur + 1, mb);
+  for (int j = wave; j < M; j += nwaves) {
+    int64_t gr = j, pr = j;
+    int32_t u = j;
+    bool ok = true;
+    if (perm != nullptr) {
+      u = perm[j];
+      ok = (uint32_t)u < (uint32_t)P;
+      if (ok) {
+        gr = g_row_index ? (int64_t)g_row_index[u] : (int64_t)u;
+        pr = phi_row_index ? (int64_t)phi_row_index[u] : (int64_t)u;
       }
-      cur = e;
-      ma = mb = 0u;
     }
-    const float aa = fabsf(alpha_c[j]);
-    float ra = row_norm_bf16(g_c + (int64_t)j * gch, gch, lane);
-    float rb = row_norm_bf16(phi_c + (int64_t)j * pch, pch, lane);
-    if (alpha_on_phi) rb = aa * rb; else ra = aa * ra;
-    ma = max(ma, __float_as_uint(ra));
-    mb = max(mb, __float_as_uint(rb));
+    const bool g_ok = ok && (uint64_t)gr < (uint64_t)g_rows;
+    const bool p_ok = ok && (uint64_t)pr < (uint64_t)phi_rows;
+    const float na = g_ok ? row_norm_bf16(g + gr * gch, gch, lane) : 0.f;
+    const float nb = p_ok ? row_norm_bf16(phi + pr * pch, pch, lane) : 0.f;
+    if (lane == 0) {
+      const float aa = ok ? fabsf(alpha[u]) : 0.f;
+      rn[j] = alpha_on_phi ? make_float2(na, aa * nb) : make_float2(aa * na, nb);
+    }
   }
-  if (cur >= 0 && lane == 0) {
-    atomicMax(em + 2 * cur, ma);
-    atomicMax(em + 2 * cur + 1, mb);
+}
+
+// Step 2: ebound[e] = the largest rn over expert e's rows (0 when it has
+// none), one workgroup per expert.
+__global__ __launch_bounds__(256) void expert_bound_kernel(SegTable seg,
+                                                           const float2* __restrict__ rn,
+                                                           float* __restrict__ ebound) {
+  __shared__ uint32_t part[2][4];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  uint32_t a = 0u, b = 0u;   // non-negative float32 bit patterns order like their values
+  for (int j = seg.off[e] + tid; j < seg.off[e + 1]; j += 256) {
+    const float2 v = rn[j];
+    a = max(a, __float_as_uint(v.x));
+    b = max(b, __float_as_uint(v.y));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    a = max(a, (uint32_t)__shfl_xor((int)a, off, 64));
+    b = max(b, (uint32_t)__shfl_xor((int)b, off, 64));
+  }
+  if ((tid & 63) == 0) {
+    part[0][tid >> 6] = a;
+    part[1][tid >> 6] = b;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    ebound[2 * e] = __uint_as_float(max(max(part[0][0], part[0][1]), max(part[0][2], part[0][3])));
+    ebound[2 * e + 1] =
+        __uint_as_float(max(max(part[1][0], part[1][1]), max(part[1][2], part[1][3])));
   }
 }
 
@@ -281,15 +308,22 @@ hipError_t launch_gather(int dtype, const int32_t* perm, const uint8_t* keep,
   return hipGetLastError();
 }
 
-hipError_t launch_rows_bound(const SegTable& seg, const uint16_t* g_c, const uint16_t* phi_c,
-                             const float* alpha_c, int32_t M, int32_t d_out, int32_t d_in,
-                             bool alpha_on_phi, float* ebound, hipStream_t s) {
-  if (M <= 0) return hipSuccess;
-  int blocks = (M + 3) / 4;
-  if (blocks > 256 * 4) blocks = 256 * 4;
-  hipLaunchKernelGGL(rows_bound_kernel, dim3(blocks), dim3(256), 0, s, seg, (const uint4*)g_c,
-                     (const uint4*)phi_c, alpha_c, M, d_out / 8, d_in / 8, alpha_on_phi ? 1 : 0,
-                     ebound);
+hipError_t launch_expert_bounds(const SegTable& seg, const uint16_t* g, const uint16_t* phi,
+                                const float* alpha, const int32_t* perm,
+                                const int32_t* g_row_index, const int32_t* phi_row_index,
+                                int32_t M, int32_t P, int32_t g_rows, int32_t phi_rows,
+                                int32_t d_out, int32_t d_in, bool alpha_on_phi, float2* rn,
+                                float* ebound, hipStream_t s) {
+  if (M > 0) {
+    int blocks = (M + 3) / 4;
+    if (blocks > 256 * 8) blocks = 256 * 8;   // 32 waves per CU, each looping over rows
+    hipLaunchKernelGGL(row_norms_kernel, dim3(blocks), dim3(256), 0, s, (const uint4*)g,
+                       (const uint4*)phi, alpha, perm, g_row_index, phi_row_index, M, P, g_rows,
+                       phi_rows, d_out / 8, d_in / 8, alpha_on_phi ? 1 : 0, rn);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(expert_bound_kernel, dim3(seg.E), dim3(256), 0, s, seg, rn, ebound);
   return hipGetLastError();
 }
 

@@ -200,7 +200,7 @@ struct GatherPlanes {
   // the expert's powers of two from ebound, alpha on the phi side if from_phi
   uint16_t* f16_a = nullptr;
   uint16_t* f16_b = nullptr;
-  const float* ebound = nullptr;
+  float* ebound = nullptr;
   SegTable seg;
 };
 
@@ -214,14 +214,19 @@ hipError_t launch_gather(int dtype, const int32_t* perm, const uint8_t* keep,
                          int32_t d_in, hipStream_t s,
                          const GatherPlanes& planes = GatherPlanes());
 
-// float16 weight-gradient mode, separate-call path: ebound[e] = the largest
-// A and B row norms over expert e's compacted rows (merged with atomicMax
-// into ebound, which must be zero), then the two scaled float16 planes from
-// the compacted bf16 rows (bit for bit what the gather writes in the
-// one-call path).
-hipError_t launch_rows_bound(const SegTable& seg, const uint16_t* g_c, const uint16_t* phi_c,
-                             const float* alpha_c, int32_t M, int32_t d_out, int32_t d_in,
-                             bool alpha_on_phi, float* ebound, hipStream_t s);
+// float16 weight-gradient mode without a score pass to take the bounds
+// from: ebound[e] = the largest operand row norm over expert e's M rows
+// (rn: M float2 of scratch), from the compacted rows (perm null: g = g_c,
+// phi = phi_c, alpha = alpha_c, row j) or through perm from the source rows
+// (bit for bit the score pass's per-pair norms either way).  Then
+// launch_split_f16 writes the two scaled float16 planes from the compacted
+// bf16 rows (bit for bit what the gather writes in the one-call path).
+hipError_t launch_expert_bounds(const SegTable& seg, const uint16_t* g, const uint16_t* phi,
+                                const float* alpha, const int32_t* perm,
+                                const int32_t* g_row_index, const int32_t* phi_row_index,
+                                int32_t M, int32_t P, int32_t g_rows, int32_t phi_rows,
+                                int32_t d_out, int32_t d_in, bool alpha_on_phi, float2* rn,
+                                float* ebound, hipStream_t s);
 hipError_t launch_split_f16(const SegTable& seg, const uint16_t* g_c, const uint16_t* phi_c,
                             const float* alpha_c, int32_t M, int32_t d_out, int32_t d_in,
                             bool alpha_on_phi, const float* ebound, uint16_t* f16_a,
