@@ -179,7 +179,7 @@ __global__ __launch_bounds__(256) void gather_kernel(
 // |alpha|), one wave per row, grid-strided.  The rows are read from the
 // compacted buffers (perm null: row j, alpha[j] = alpha_c[j]), or through
 // perm from the source rows the gather is about to copy.  Either way the
-// values are bit for bit the score pass's per-pair norms (row_norm_bf16);
+// values are bit for bit the score pass's per-pair norms (pair_sumsq_bf16);
 // rows outside the sources read as zero rows, as in the gather.
 __global__ __launch_bounds__(256) void row_norms_kernel(
     const uint4* __restrict__ g, const uint4* __restrict__ phi, const float* __restrict__ alpha,
@@ -203,8 +203,9 @@ __global__ __launch_bounds__(256) void row_norms_kernel(
     }
     const bool g_ok = ok && (uint64_t)gr < (uint64_t)g_rows;
     const bool p_ok = ok && (uint64_t)pr < (uint64_t)phi_rows;
-    const float na = g_ok ? row_norm_bf16(g + gr * gch, gch, lane) : 0.f;
-    const float nb = p_ok ? row_norm_bf16(phi + pr * pch, pch, lane) : 0.f;
+    const float2 sq = pair_sumsq_bf16(g + (g_ok ? gr : 0) * gch, gch, g_ok,
+                                      phi + (p_ok ? pr : 0) * pch, pch, p_ok, lane);
+    const float na = sqrtf(wave_sum(sq.x)), nb = sqrtf(wave_sum(sq.y));
     if (lane == 0) {
       const float aa = ok ? fabsf(alpha[u]) : 0.f;
       rn[j] = alpha_on_phi ? make_float2(na, aa * nb) : make_float2(aa * na, nb);

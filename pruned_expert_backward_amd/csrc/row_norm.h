@@ -1,4 +1,4 @@
-// Sum of squares of one bf16 row, reduced over the wave64 that reads it.
+// Sums of squares of bf16 rows, reduced over the wave64 that reads them.
 // Shared by the score pass and the float16 weight-gradient planes' bounds, so
 // that both compute bit for bit the same row norms.
 #pragma once
@@ -53,30 +53,36 @@ __device__ __forceinline__ void tail3(const V* __restrict__ row, int c, int nchu
   x2 = c + 128 < nchunk ? row[c + 128] : z;
 }
 
-// This lane's share of the sum of squares of a bf16 row of nchunk 16-byte
-// chunks (lane-strided, four independent loads in flight per lane); the
-// caller reduces it with wave_sum.
-__device__ __forceinline__ float row_sumsq_bf16(const uint4* __restrict__ row, int nchunk,
-                                                int lane) {
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-  int c = lane;
-  for (; c + 192 < nchunk; c += 256) {
-    const uint4 x0 = row[c], x1 = row[c + 64], x2 = row[c + 128], x3 = row[c + 192];
-    a0 += sumsq8(x0); a1 += sumsq8(x1); a2 += sumsq8(x2); a3 += sumsq8(x3);
+// This lane's shares of the sums of squares of a pair's two bf16 rows: the
+// g row (gc 16-byte chunks) and the phi row (pc chunks), read as one
+// sequence of chunks c = lane + 64 k (c < gc from g, else chunk c - gc of
+// phi), eight loads in flight per lane, so that a pair costs as few memory
+// round trips as its bytes allow.  A row that is not there (g_ok / p_ok
+// false) reads as zeros but keeps its chunk positions, so the other row's
+// sum is the same either way.  {x: g, y: phi}; reduce each with wave_sum.
+__device__ __forceinline__ float2 pair_sumsq_bf16(const uint4* __restrict__ g, int gc, bool g_ok,
+                                                  const uint4* __restrict__ phi, int pc,
+                                                  bool p_ok, int lane) {
+  float ag[4] = {0.f, 0.f, 0.f, 0.f}, ap[4] = {0.f, 0.f, 0.f, 0.f};
+  const int n = gc + pc;
+  for (int base = lane; base < n; base += 64 * 8) {
+    uint4 x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = base + 64 * i;
+      const bool in_g = c < gc;
+      const uint4* src = in_g ? g + c : phi + (c - gc);
+      const bool ok = c < n && (in_g ? g_ok : p_ok);
+      x[i] = ok ? *src : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float v = sumsq8(x[i]);
+      if (base + 64 * i < gc) ag[i & 3] += v;
+      else ap[i & 3] += v;
+    }
   }
-  if (c < nchunk) {
-    uint4 x0, x1, x2;
-    tail3(row, c, nchunk, x0, x1, x2);
-    a0 += sumsq8(x0); a1 += sumsq8(x1); a2 += sumsq8(x2);
-  }
-  return (a0 + a1) + (a2 + a3);
-}
-
-// Euclidean norm of a bf16 row (an upper bound of its largest |x|; wave
-// uniform).
-__device__ __forceinline__ float row_norm_bf16(const uint4* __restrict__ row, int nchunk,
-                                               int lane) {
-  return sqrtf(wave_sum(row_sumsq_bf16(row, nchunk, lane)));
+  return make_float2((ag[0] + ag[1]) + (ag[2] + ag[3]), (ap[0] + ap[1]) + (ap[2] + ap[3]));
 }
 
 }  // namespace lrmoe
