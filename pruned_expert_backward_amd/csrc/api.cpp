@@ -385,6 +385,9 @@ lrmoe_status grouped_backward(const lrmoe_problem* pb, const int32_t* perm, cons
   t.kc = wl.kc;
   group_shape(t.tiles_n, 3, t.dw_gm, t.dw_gn);
   group_shape(t.tiles_n, 6, t.dp_gm, t.dp_gn);
+  // a last column of at most 128 columns: 512 x 128 input-gradient tiles
+  // there, none of them half empty (the SiLU-GLU epilogue keeps square tiles)
+  t.tall = !glu && d_in % kTile != 0 && d_in % kTile <= kTile / 2;
   for (int e = 0; e <= E; ++e) t.seg_off[e] = c.tab.seg_off[e];
 
   // Groups.  Weight gradient: every expert (zeros for q_e = 0) and K chunk;

@@ -83,16 +83,16 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = kTile, BN = kTile, BK = 32;
-// Wave grid of a tile.  2 x 2 waves of 128 x 128 (one wave per SIMD, 256
-// accumulators each).  2 x 4 waves of 128 x 64 (two waves per SIMD) were
-// measured as well: correct, and no faster (the second wave hides no more
-// than the extra fragment reads cost).
-constexpr int kWavesM = 2;                 // wave rows of a tile
-constexpr int kWavesN = 2;                 // wave columns
-constexpr int kWaves = kWavesM * kWavesN;
+// Four waves per tile, each computing a 128 x 128 block (one wave per SIMD,
+// 256 accumulators each).  A square tile stacks them 2 x 2; the tall edge
+// tile (512 x 128, for a last column that holds at most 128 columns) stacks
+// them 4 x 1.  2 x 4 waves of 128 x 64 (two waves per SIMD) were measured as
+// well: correct, and no faster (the second wave hides no more than the extra
+// fragment reads cost).
+constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int WTM = BM / kWavesM;          // rows of one wave's block
-constexpr int WTN = BN / kWavesN;          // columns of one wave's block
+constexpr int WTM = 128;                   // rows of one wave's block
+constexpr int WTN = 128;                   // columns of one wave's block
 constexpr int kMB = WTM / 32;              // 32x32 accumulator blocks per wave: kMB x kNB
 constexpr int kNB = WTN / 32;
 constexpr int kPlaneBytes = kTile * BK * 2;   // one bf16 operand plane of one K step (16 KB)
@@ -106,8 +106,12 @@ constexpr int kPlaneBytes = kTile * BK * 2;   // one bf16 operand plane of one K
 // linear b128 read).
 __device__ __forceinline__ int kc_swz(int r) { return (r ^ (r >> 2)) & 3; }
 __device__ __forceinline__ int kc_off(int r, int c) { return r * 64 + ((c ^ kc_swz(r)) << 4); }
-// MC: row k (0..31) holds M/N 0..255 as 32 chunks of 16 B.
-__device__ __forceinline__ int mc_off(int k, int c) { return k * 512 + ((c ^ ((k & 3) << 2)) << 4); }
+// MC: row k (0..31) holds the tile's M or N extent (128, 256 or 512) as
+// RB / 16 chunks of 16 B, RB bytes per row.  The swizzle moves rows k and
+// k + 1 .. k + 3 by 4 chunks each; every row width is a multiple of 256 B,
+// so all widths see the same bank pattern.
+template <int RB>
+__device__ __forceinline__ int mc_off(int k, int c) { return k * RB + ((c ^ ((k & 3) << 2)) << 4); }
 
 // Fragments (8 bf16 per lane), read at precomputed LDS byte addresses (the
 // tile's la / lb).
@@ -117,12 +121,13 @@ __device__ __forceinline__ int mc_off(int k, int c) { return k * 512 + ((c ^ ((k
 //       s = l%16 reads 4 bf16 of row k0 = kb + 8*(G/2) + s/4 at chunk
 //       mb/8 + 2*(G%2) + (s%4)/2, half (s%2)*8 bytes; after the transpose lane
 //       l holds one MN column for rows k0 .. k0 + 3.  Two such reads 4 rows
-//       (2 KiB) apart give the 8 K values.
+//       (4 * RB bytes) apart give the 8 K values.
+template <int RB>
 __device__ __forceinline__ i16x8 frag_mc_at(uint32_t addr) {
   LDS_AS char* p = (LDS_AS char*)(uintptr_t)addr;
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<LDS_AS i16x4*>(p));
   const i16x4 hi =
-      __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<LDS_AS i16x4*>(p + 2048));
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<LDS_AS i16x4*>(p + 4 * RB));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 __device__ __forceinline__ i16x8 frag_kc_at(uint32_t addr) {
@@ -143,6 +148,7 @@ __device__ __forceinline__ f32x16 mfma_f16(i16x8 a, i16x8 b, f32x16 c) {
 struct TileJob {
   int e, m0, n0;
   int chunk, chunks;   // dW K chunk of this tile and the expert's chunk count
+  bool tall;           // dphi: 512 x 128 edge tile over row tiles m0 / 256 and m0 / 256 + 1
 };
 
 // Queue length of XCD x in item slots.
@@ -152,9 +158,12 @@ __device__ __forceinline__ int queue_items(const GemmTable& tab, int x) {
   return ng * kGroupSlots;
 }
 
-// Item `i` of XCD x's queue -> tile; false for an idle slot.
+// Item `i` of XCD x's queue -> tile; false for an idle slot.  With `tall`,
+// the last input-gradient column tile of every even row tile becomes a
+// 512 x 128 tile that also covers the odd row tile below it, whose slot then
+// idles.
 __device__ __forceinline__ bool decode(const GemmTable& tab, int x, int i, bool& is_dw,
-                                      TileJob& job) {
+                                      TileJob& job, bool tall) {
   const int p = i / kGroupSlots, t = i % kGroupSlots;
   int e, chunk, lg;
   if (tab.use_table) {
@@ -194,6 +203,8 @@ __device__ __forceinline__ bool decode(const GemmTable& tab, int x, int i, bool&
   const int tn = (lg % ngn) * gn + t % gn;
   const int tiles_m = is_dw ? tab.dw_tiles_m : (q + BM - 1) / BM;
   if (tm >= tiles_m || tn >= tab.tiles_n) return false;
+  job.tall = tall && !is_dw && tn == tab.tiles_n - 1;
+  if (job.tall && (tm & 1)) return false;
   job.e = e;
   job.m0 = tm * BM;
   job.n0 = tn * BN;
@@ -254,7 +265,9 @@ __device__ __forceinline__ void wait_loads_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-constexpr int kPermBytes = BM * 8;   // dphi epilogue: destination row + alpha per tile row
+// dphi epilogue: destination row + alpha of each of the (at most 512) tile rows
+constexpr int kMaxRows = 2 * kTile;
+constexpr int kPermBytes = kMaxRows * 8;
 
 // Everything one tile needs, derived from its job.  IS_DW: A (MC, rows = K)
 // and B (MC, rows = K) are [M, d_out] / [M, d_in] segment rows.  Else A (KC,
@@ -275,13 +288,27 @@ constexpr int kPermBytes = BM * 8;   // dphi epilogue: destination row + alpha p
 // stalling the wave in a burst.
 // F16 (weight-gradient tiles only): float16 operand planes, float16 MFMAs,
 // and the epilogue undoes the expert's power-of-two scales.
-template <bool IS_DW, int PA, int PB, int NS, int GLU = 0, bool F16 = false>
+// TALL: a 512 x 128 tile (waves stacked 4 x 1) instead of 256 x 256.
+template <bool IS_DW, int PA, int PB, int NS, int GLU = 0, bool F16 = false, bool TALL = false>
 struct Tile {
   static constexpr bool A_MC = IS_DW;
-  static constexpr int kStage = (PA + PB) * kPlaneBytes;
-  static constexpr int kBlocks = kPlaneBytes / 1024;     // 1 KiB LDS blocks per plane
-  static constexpr int kPerWave = kBlocks / kWaves;      // ... filled by each wave
-  static constexpr int kLoads = (PA + PB) * kPerWave;    // load instructions per stage per wave
+  static constexpr int TBM = TALL ? 2 * kTile : kTile;   // tile rows (M)
+  static constexpr int TBN = TALL ? kTile / 2 : kTile;   // tile columns (N)
+  static constexpr int kWN = TBN / WTN;                  // wave columns (1 or 2)
+  static_assert((TBM / WTM) * kWN == kWaves, "wave grid");
+  // Tall tiles serve the input gradient only: as weight-gradient tiles
+  // (which read every g_c byte once per column tile anyway) they halved the
+  // number of tiles in flight and lost more to that than the edge waste cost.
+  static_assert(!(TALL && IS_DW), "tall tiles are input-gradient tiles");
+  // One K step of an operand plane: TBM (A) or TBN (B) values per K row.
+  // MC rows are RA / RB bytes long (RA: weight-gradient tiles, 256 wide);
+  // KC rows are 64 bytes.
+  static constexpr int RA = 2 * TBM, RB = 2 * TBN;
+  static constexpr int kPlaneA = TBM * BK * 2, kPlaneB = TBN * BK * 2;
+  static constexpr int kStage = PA * kPlaneA + PB * kPlaneB;
+  // 1 KiB LDS blocks of one plane filled by each wave
+  static constexpr int kPwA = kPlaneA / 1024 / kWaves, kPwB = kPlaneB / 1024 / kWaves;
+  static constexpr int kLoads = PA * kPwA + PB * kPwB;   // load instructions per stage per wave
   static constexpr int kTerms = 1 + (PA == 2) + (PB == 2);
   static constexpr int kHalfMfmas = kMB * kNB * kTerms; // per wave per half step
   static constexpr int kFrags = PA * kMB + PB * kNB;     // fragments per half step
@@ -296,10 +323,10 @@ struct Tile {
   int lane, wave, wm, wn;
   const uint16_t* A[2];
   const uint16_t* B[2];
-  uint32_t aoff[kPerWave], boff[kPerWave];
-  int acol[kPerWave];
+  uint32_t aoff[kPwA], boff[kPwB];
+  int acol[kPwA];
   // LDS byte addresses of this lane's fragment reads in stage 0, plane 0:
-  // MC operands: one per 32-wide fragment (half 0; half 1 is +8 KiB);
+  // MC operands: one per 32-wide fragment (half 0; half 1 is 16 rows on);
   // KC operand: one per half (fragment a is +2 KiB * a).
   uint32_t la[kMB], lb[kNB];
   LDS_AS char* sink;   // kWaves x 1 KiB of LDS that only dead loads write
@@ -309,8 +336,8 @@ struct Tile {
     const int tid = threadIdx.x;
     lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    wm = wave / kWavesN;   // wave block rows wm*WTM, columns wn*WTN
-    wn = wave % kWavesN;
+    wm = wave / kWN;   // wave block rows wm*WTM, columns wn*WTN
+    wn = wave % kWN;
     // Tile coordinates are workgroup-uniform; say so, so that buffer
     // descriptors and LDS bases stay in scalar registers.
     e = __builtin_amdgcn_readfirstlane(job.e);
@@ -332,21 +359,24 @@ struct Tile {
       B[p] = IS_DW ? args.ops.dw_b[p] : args.ops.dp_b[p];
     }
     // Byte offsets (within one K step) of the global chunk each lane fetches
-    // for each of its LDS blocks: block b = wave*kPerWave + j.
+    // for each of its LDS blocks: block wave*kPwA + j of an A plane, wave*kPwB
+    // + j of a B plane.  An MC block holds 1024 / RB K rows of RB / 16 chunks
+    // (lane -> row lane / (RB/16), physical chunk lane % (RB/16)).
 #pragma unroll
-    for (int j = 0; j < kPerWave; ++j) {
-      const int blk = wave * kPerWave + j;
-      {   // MC block: rows 2*blk, 2*blk+1 of the step, 32 chunks each
+    for (int j = 0; j < kPwB; ++j) {
+      constexpr int cpr = RB / 16;
+      const int k = (64 / cpr) * (wave * kPwB + j) + lane / cpr, pc = lane % cpr;
+      const int col = n0 + 8 * (pc ^ ((k & 3) << 2));
+      boff[j] = col < d_in ? (uint32_t)(k * d_in + col) * 2u : kOutOfRange;
+    }
+#pragma unroll
+    for (int j = 0; j < kPwA; ++j) {
+      const int blk = wave * kPwA + j;
+      if (A_MC) {   // MC block: rows 2*blk, 2*blk+1 of the step, 32 chunks each
         const int k = 2 * blk + (lane >> 5), pc = lane & 31;
-        const int lc = pc ^ ((k & 3) << 2);
-        const int col = n0 + 8 * lc;
-        boff[j] = col < d_in ? (uint32_t)(k * d_in + col) * 2u : kOutOfRange;
-        if (A_MC) {
-          const int acolm = m0 + 8 * lc;
-          aoff[j] = acolm < d_out ? (uint32_t)(k * d_out + acolm) * 2u : kOutOfRange;
-        }
-      }
-      if (!A_MC) {   // KC block: rows 16*blk .. +15 of the tile, 4 chunks each
+        const int acolm = m0 + 8 * (pc ^ ((k & 3) << 2));
+        aoff[j] = acolm < d_out ? (uint32_t)(k * d_out + acolm) * 2u : kOutOfRange;
+      } else {   // KC block: rows 16*blk .. +15 of the tile, 4 chunks each
         const int r = 16 * blk + (lane >> 2), pc = lane & 3;
         const int lc = pc ^ kc_swz(r);
         acol[j] = 8 * lc;
@@ -362,11 +392,11 @@ struct Tile {
       const int half = (s & 1) * 8;
 #pragma unroll
       for (int f = 0; f < kNB; ++f)
-        lb[f] = base + (uint32_t)(mc_off(k0, (wn * WTN + f * 32) / 8 + cl) + half);
+        lb[f] = base + (uint32_t)(mc_off<RB>(k0, (wn * WTN + f * 32) / 8 + cl) + half);
       if (A_MC) {
 #pragma unroll
         for (int f = 0; f < kMB; ++f)
-          la[f] = base + (uint32_t)(mc_off(k0, (wm * WTM + f * 32) / 8 + cl) + half);
+          la[f] = base + (uint32_t)(mc_off<RA>(k0, (wm * WTM + f * 32) / 8 + cl) + half);
       }
     }
     if (!A_MC) {
@@ -379,18 +409,18 @@ struct Tile {
   }
 
   // ---- global -> LDS: load instruction `idx` (0 .. kLoads-1) of this wave
-  // for the K step starting at k0.  Instruction idx fills LDS block
-  // wave * kPerWave + idx % kPerWave of plane idx / kPerWave (A planes first).
-  // When !live the instruction keeps its place in the stream but reads an
-  // empty range and writes only zeros, into this wave's sink block.
+  // for the K step starting at k0.  Instructions 0 .. PA*kPwA-1 fill block
+  // wave * kPwA + idx % kPwA of A plane idx / kPwA; the rest fill the B
+  // planes the same way.  When !live the instruction keeps its place in the
+  // stream but reads an empty range and writes only zeros, into this wave's
+  // sink block.
   __device__ __forceinline__ void issue_one(const Args& args, int k0, LDS_AS char* stage,
                                             int idx, bool live = true) const {
     const int d_out = args.d_out, d_in = args.d_in;
     const int krows = live ? (K - k0 < BK ? K - k0 : BK) : 0;
-    const int p = idx / kPerWave, j = idx % kPerWave;
-    LDS_AS char* dst = live ? stage + p * kPlaneBytes + (wave * kPerWave + j) * 1024
-                            : sink + wave * 1024;
-    if (p < PA) {
+    if (idx < PA * kPwA) {
+      const int p = idx / kPwA, j = idx % kPwA;
+      LDS_AS char* dst = live ? stage + p * kPlaneA + (wave * kPwA + j) * 1024 : sink + wave * 1024;
       __amdgpu_buffer_rsrc_t r =
           A_MC ? rsrc(A[p] + ((int64_t)seg + k0) * d_out, (int64_t)krows * d_out * 2)
                : rsrc(A[p] + ((int64_t)seg + m0) * d_out,
@@ -399,8 +429,11 @@ struct Tile {
       if (!A_MC) off = (k0 + acol[j]) < K ? off + (uint32_t)k0 * 2u : kOutOfRange;
       load_lds16(r, lds_addr(dst), off);
     } else {
-      const uint16_t* b0 = IS_DW ? B[p - PA] + ((int64_t)seg + k0) * d_in
-                                 : B[p - PA] + ((int64_t)e * d_out + k0) * d_in;
+      const int p = (idx - PA * kPwA) / kPwB, j = (idx - PA * kPwA) % kPwB;
+      LDS_AS char* dst = live ? stage + PA * kPlaneA + p * kPlaneB + (wave * kPwB + j) * 1024
+                              : sink + wave * 1024;
+      const uint16_t* b0 = IS_DW ? B[p] + ((int64_t)seg + k0) * d_in
+                                 : B[p] + ((int64_t)e * d_out + k0) * d_in;
       load_lds16(rsrc(b0, (int64_t)krows * d_in * 2), lds_addr(dst), boff[j]);
     }
   }
@@ -420,12 +453,13 @@ struct Tile {
     const uint32_t so = (uint32_t)(s * kStage);
     if (i < PA * kMB) {
       const int p = i / kMB, a = i % kMB;
-      const uint32_t po = so + (uint32_t)(p * kPlaneBytes);
-      if (A_MC) f.a[p][a] = frag_mc_at(la[a] + po + (uint32_t)(h * 8192));
+      const uint32_t po = so + (uint32_t)(p * kPlaneA);
+      if (A_MC) f.a[p][a] = frag_mc_at<RA>(la[a] + po + (uint32_t)(h * 16 * RA));
       else f.a[p][a] = frag_kc_at(la[h] + po + (uint32_t)(a * 2048));
     } else {
       const int p = (i - PA * kMB) / kNB, b = (i - PA * kMB) % kNB;
-      f.b[p][b] = frag_mc_at(lb[b] + so + (uint32_t)((PA + p) * kPlaneBytes + h * 8192));
+      f.b[p][b] =
+          frag_mc_at<RB>(lb[b] + so + (uint32_t)(PA * kPlaneA + p * kPlaneB + h * 16 * RB));
     }
   }
 
@@ -525,12 +559,13 @@ struct Tile {
     if (IS_DW) return;
     const int tid = threadIdx.x;
     LDS_AS int32_t* s_perm = reinterpret_cast<LDS_AS int32_t*>(prm);
-    LDS_AS float* s_alpha = reinterpret_cast<LDS_AS float*>(prm + BM * 4);
-    if (tid < BM) {
-      const bool ok = m0 + tid < q;
-      const int32_t u = ok ? args.perm[seg + m0 + tid] : -1;
-      s_perm[tid] = (uint32_t)u < (uint32_t)args.P ? u : -1;   // perm holds pair indices < P
-      s_alpha[tid] = !ok ? 0.f : args.ops.dp_alpha_folded ? 1.f : args.alpha_c[seg + m0 + tid];
+    LDS_AS float* s_alpha = reinterpret_cast<LDS_AS float*>(prm + kMaxRows * 4);
+#pragma unroll
+    for (int r = tid; r < TBM; r += kThreads) {
+      const bool ok = m0 + r < q;
+      const int32_t u = ok ? args.perm[seg + m0 + r] : -1;
+      s_perm[r] = (uint32_t)u < (uint32_t)args.P ? u : -1;   // perm holds pair indices < P
+      s_alpha[r] = !ok ? 0.f : args.ops.dp_alpha_folded ? 1.f : args.alpha_c[seg + m0 + r];
     }
   }
 
@@ -752,7 +787,7 @@ struct Tile {
                                            const f32x16 (&acc)[kMB][kNB]) const {
     const int d_out = args.d_out, d_in = args.d_in;
     LDS_AS const int32_t* s_perm = reinterpret_cast<LDS_AS const int32_t*>(prm);
-    LDS_AS const float* s_alpha = reinterpret_cast<LDS_AS const float*>(prm + BM * 4);
+    LDS_AS const float* s_alpha = reinterpret_cast<LDS_AS const float*>(prm + kMaxRows * 4);
     // Split dW tiles go to their chunk's partial tile (full 256x256, row-major).
     float* part = nullptr;
     if (IS_DW && chunks > 1) {
@@ -833,21 +868,31 @@ struct Tile {
   }
 };
 
-// LDS stages for a tile with `planes` operand planes: as many as fit in
-// 144 KiB, at most 4.
-constexpr int stages_for(int planes) {
-  return planes * 4 * kPlaneBytes <= 144 * 1024 ? 4 : planes * 3 * kPlaneBytes <= 144 * 1024 ? 3 : 2;
+// LDS stages for a tile whose stage is `bytes` long: as many as fit in
+// 144 KiB, at most 4 (0 when not even 2 fit).
+constexpr int kStageBudget = 144 * 1024;
+constexpr int stages_for(int bytes) {
+  return 4 * bytes <= kStageBudget ? 4 : 3 * bytes <= kStageBudget ? 3 : 2 * bytes <= kStageBudget ? 2 : 0;
 }
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
+// Stage counts of the square tiles of both products and of the tall
+// input-gradient tile, which runs only where its stage fits twice.
 template <int DW_PA, int DW_PB, int DP_PA, int DP_PB>
 struct Cfg {
-  static constexpr int NS_DW = stages_for(DW_PA + DW_PB);
-  static constexpr int NS_DP = stages_for(DP_PA + DP_PB);
-  static constexpr int dw_bytes = NS_DW * (DW_PA + DW_PB) * kPlaneBytes;
-  static constexpr int dp_bytes = NS_DP * (DP_PA + DP_PB) * kPlaneBytes;
-  static constexpr int stages = dw_bytes > dp_bytes ? dw_bytes : dp_bytes;
+  static constexpr int sq = kPlaneBytes;                         // square tile plane
+  static constexpr int ta = 2 * kPlaneBytes, tb = kPlaneBytes / 2;   // tall tile A / B plane
+  static constexpr int NS_DW = stages_for((DW_PA + DW_PB) * sq);
+  static constexpr int NS_DP = stages_for((DP_PA + DP_PB) * sq);
+  static constexpr int NS_DPT = stages_for(DP_PA * ta + DP_PB * tb);
+  static constexpr bool tall_fits = NS_DPT >= 2;
+  static constexpr int stages =
+      cmax(cmax(NS_DW * (DW_PA + DW_PB) * sq, NS_DP * (DP_PA + DP_PB) * sq),
+           tall_fits ? NS_DPT * (DP_PA * ta + DP_PB * tb) : 0);
   static constexpr int sink = stages + kPermBytes + 16;   // kWaves x 1 KiB
   static constexpr int bytes = sink + kWaves * 1024;
+  static_assert(NS_DW >= 2 && NS_DP >= 2, "stages");
+  static_assert(bytes <= 160 * 1024, "LDS");
 };
 
 // Persistent: one workgroup per CU drains its XCD's queue.  Between tiles the
@@ -859,6 +904,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_backward_kernel(Args args
   using C = Cfg<DW_PA, DW_PB, DP_PA, DP_PB>;
   using DwTile = Tile<true, DW_PA, DW_PB, C::NS_DW, 0, DW_F16>;
   using DpTile = Tile<false, DP_PA, DP_PB, C::NS_DP, GLU>;
+  // tall input-gradient edge tiles: not with the SiLU-GLU epilogue
+  constexpr bool kTall = GLU == 0 && C::tall_fits;
+  using DpTall = Tile<false, DP_PA, DP_PB, kTall ? C::NS_DPT : 2, 0, false, true>;
+  const bool tall_on = kTall && tab.tall != 0;
   __shared__ __attribute__((aligned(16))) char smem_raw[C::bytes];
   LDS_AS char* smem = (LDS_AS char*)(smem_raw);
   LDS_AS char* prm = smem + C::stages;
@@ -884,30 +933,43 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_backward_kernel(Args args
         ++hop;
         continue;
       }
-      if (decode(tab, qx, i, is_dw, job)) return i;
+      if (decode(tab, qx, i, is_dw, job, tall_on)) return i;
     }
     return -1;
+  };
+  // Runs fn on the tile of job j (one of three tile types).
+  auto with_tile = [&](bool is_dw, const TileJob& j, auto&& fn) __attribute__((always_inline)) {
+    if (is_dw) {
+      fn(DwTile(args, tab, j, smem, sink));
+      return;
+    }
+    if constexpr (kTall) {
+      if (j.tall) {
+        fn(DpTall(args, tab, j, smem, sink));
+        return;
+      }
+    }
+    fn(DpTile(args, tab, j, smem, sink));
   };
 
   f32x16 acc[kMB][kNB];
   bool cur_dw;
   TileJob cur;
   if (fetch(cur_dw, cur) < 0) return;
-  if (cur_dw) DwTile(args, tab, cur, smem, sink).prologue(args, smem);
-  else DpTile(args, tab, cur, smem, sink).prologue(args, smem);
+  with_tile(cur_dw, cur, [&](const auto& t) __attribute__((always_inline)) { t.prologue(args, smem); });
   for (;;) {
-    if (cur_dw) DwTile(args, tab, cur, smem, sink).mainloop(args, smem, acc);
-    else DpTile(args, tab, cur, smem, sink).mainloop(args, smem, acc);
-    if (!cur_dw) DpTile(args, tab, cur, smem, sink).stage_rows(args, prm);
+    with_tile(cur_dw, cur, [&](const auto& t) __attribute__((always_inline)) {
+      t.mainloop(args, smem, acc);
+      t.stage_rows(args, prm);   // dphi tiles only
+    });
     bool nxt_dw;
     TileJob nxt;
     const bool more = fetch(nxt_dw, nxt) >= 0;   // its barrier also frees every stage
-    if (more) {
-      if (nxt_dw) DwTile(args, tab, nxt, smem, sink).prologue(args, smem);
-      else DpTile(args, tab, nxt, smem, sink).prologue(args, smem);
-    }
-    if (cur_dw) DwTile(args, tab, cur, smem, sink).epilogue(args, tab, prm, acc);
-    else DpTile(args, tab, cur, smem, sink).epilogue(args, tab, prm, acc);
+    if (more)
+      with_tile(nxt_dw, nxt, [&](const auto& t) __attribute__((always_inline)) { t.prologue(args, smem); });
+    with_tile(cur_dw, cur, [&](const auto& t) __attribute__((always_inline)) {
+      t.epilogue(args, tab, prm, acc);
+    });
     if (!more) break;
     lds_barrier();   // the perm/alpha rows are read before the next tile restages them
     cur_dw = nxt_dw;

@@ -62,6 +62,9 @@ struct GemmTable {
   int32_t dp_gm, dp_gn;           // dphi group shape
   int32_t kc;                     // dW K-chunk length (multiple of the K step)
   int32_t use_table;              // 1: groups[] below; 0: formula order (fallback)
+  int32_t tall;                   // 1: the last column holds <= kTile/2 columns; its
+                                  //    input-gradient tiles are 512 x 128, each over two
+                                  //    row tiles
   int32_t dw_groups;              // formula order: dW groups first ...
   int32_t total_groups;           // ... then dphi groups
   int32_t qoff[kXcds + 1];        // table: XCD x drains groups [qoff[x], qoff[x+1])
