@@ -404,9 +404,13 @@ def main():
     # algorithmic bytes (HBM-bound kernels) and FLOP (the GEMM) per launch
     score_bytes = (P * (es * (d_o + d_i) + 8) if args.score_mode == "lrm"
                    else P * (es * d_o + 4))   # gradient-only rules read no phi, no alpha
+    # the dropped pairs' dphi rows: zeroed by the gather, except in the one-call
+    # path, whose grouped GEMM launch clears them beside its tiles
+    zero_bytes = 0 if chain or dense_path else (P - M) * 4 * d_i
+    zero_in_gemm = whole
     work = {"lrm_score": score_bytes,
             "select_scan": P * 5,
-            "gather": M * (2 * es * (d_o + d_i) + 12) + (0 if chain else (P - M) * 4 * d_i),
+            "gather": M * (2 * es * (d_o + d_i) + 12) + (0 if zero_in_gemm else zero_bytes),
             "grouped_gemm": gemm_flops(p, p.P if dense_path else M)}
     kernels = {}
     for name, t in us.items():
@@ -417,6 +421,8 @@ def main():
         if name == "grouped_gemm":
             k.update(algorithmic_flops=work[name], TFLOPs=work[name] / t / 1e6,
                      mfma_frac=work[name] / t / 1e6 / MFMA_BF16_PEAK_TFLOPS)
+            if zero_in_gemm:
+                k.update(zero_fill_bytes=zero_bytes)
         elif name in work:
             k.update(algorithmic_bytes=work[name], GBps=work[name] / t / 1e3,
                      hbm_frac=work[name] / t / 1e3 / HBM_PEAK_GBS)
@@ -430,8 +436,8 @@ def main():
             else M * min(d_o, d_i) * 2 * (2 if args.dw_mode == "exact" else 1))
     ssc_us = sum(us[n] for n in ("lrm_score", "select_scan", "gather") if us[n] is not None)
     nbytes = algorithmic_bytes(p, M, args.score_mode)
-    if chain:   # no dphi rows to zero in the original layout
-        nbytes -= (P - M) * 4 * d_i
+    if chain or zero_in_gemm:   # no dphi rows to zero in the original layout, or
+        nbytes -= (P - M) * 4 * d_i   # they are zeroed inside the GEMM launch
     dominant_flops = 4.0 * M * gu.d_out * gu.d_in if gu is not None else work["grouped_gemm"]
     gemm_tf = dominant_flops / gemm_live["mean"] / 1e6
     # MFMA work the kernel executes: products of split operands cost one MFMA
@@ -456,13 +462,23 @@ def main():
                 launches=gemm_live["launches"],
                 traffic=traffic, traffic_unit="bytes per launch",
                 mfma_busy_frac=mfma_busy,
-                algorithmic_bytes_floor=gemm_floor_bytes(p, M))
+                algorithmic_bytes_floor=gemm_floor_bytes(p, M) + (zero_bytes if zero_in_gemm else 0))
+    if zero_in_gemm:
+        roof["zero_fill_bytes"] = zero_bytes
+        roof["zero_fill_note"] = ("the launch also clears the dropped pairs' dphi rows "
+                                  "(zero_fill_bytes of stores beside the tiles), which the "
+                                  "gather would otherwise write")
     if gu is not None:
         roof["note"] = "the gate/up projection's grouped GEMM (its flops 4 M d_out2 d_in2)"
         es2 = 2
+        gu_zero = 0 if chain else (P - M) * 4 * gu.d_in   # cleared in that launch
         roof["algorithmic_bytes_floor"] = (M * es2 * (gu.d_out + gu.d_in)
                                            + p.E * gu.d_out * gu.d_in * (es2 + 4)
-                                           + M * gu.d_in * 4)
+                                           + M * gu.d_in * 4 + gu_zero)
+        roof.pop("zero_fill_bytes", None)
+        roof.pop("zero_fill_note", None)
+        if gu_zero:
+            roof["zero_fill_bytes"] = gu_zero
     rec = {
         "metric": "kept pairs/s + grouped-GEMM TFLOP/s (% MFMA peak), score/compact % HBM BW",
         "value": M * args.steps / elapsed,
@@ -513,8 +529,8 @@ def main():
             gpro, gred = gu_timer.mean_us(5), gu_timer.mean_us(4)
         if chain:   # x rows and alpha only: the gate/up gradient is already compacted
             gbytes = M * (2 * es * gu.d_in + 12) + (P - M) * 4 * gu.d_in
-        else:
-            gbytes = M * (2 * es * (gu.d_out + gu.d_in) + 12) + (P - M) * 4 * gu.d_in
+        else:   # its dropped dphi rows are cleared in the GEMM launch
+            gbytes = M * (2 * es * (gu.d_out + gu.d_in) + 12)
         gfl = 4.0 * M * gu.d_out * gu.d_in
         rec["gate_up"] = {
             "d_out": gu.d_out, "d_in": gu.d_in,
@@ -523,7 +539,9 @@ def main():
                                "hbm_frac": gbytes / gd["mean"] / 1e3 / HBM_PEAK_GBS},
             "grouped_gemm": {"us": gg["mean"], "us_median": gg["median"],
                              "algorithmic_flops": gfl, "TFLOPs": gfl / gg["mean"] / 1e6,
-                             "mfma_frac": gfl / gg["mean"] / 1e6 / MFMA_BF16_PEAK_TFLOPS},
+                             "mfma_frac": gfl / gg["mean"] / 1e6 / MFMA_BF16_PEAK_TFLOPS,
+                             **({} if chain else
+                                {"zero_fill_bytes": (P - M) * 4 * gu.d_in})},
             "operand_prologue_us": gpro, "splitk_reduce_us": gred}
         gu_timer.close()
     if dense_path:

@@ -96,7 +96,7 @@ struct GemmWorkspace {
   int dw_pa = 1, dw_pb = 1, dp_pa = 1, dp_pb = 1;
   int32_t kc = 0;          // dW K-chunk length
   int64_t part_tiles = 0;  // partial tiles of split experts
-  size_t heads = 0;        // queue counters (kXcds int32), then at +kEmaxOff ...
+  size_t heads = 0;        // work counters (kHeadCounters int32), then at +kEmaxOff ...
   bool f16 = false;        // float16 weight gradient: a_hi / b_hi are its two planes
   size_t rnorm = 0;        // ... the per-expert bounds ebound; here per-pair row norms
 };
@@ -107,6 +107,9 @@ constexpr size_t kEmaxOff = 256;
 constexpr size_t kHeadsBytes = kEmaxOff + 2 * kMaxE * sizeof(float);
 
 constexpr int kStepK = 32;   // K rows per pipeline step of the GEMM kernel
+// Workgroups of the grouped GEMM launch that start with the zero-fill of the
+// dropped pairs' dphi rows (3 per XCD) instead of tiles.
+constexpr int kZeroStarters = 24;
 
 GemmWorkspace gemm_workspace(const lrmoe_problem* pb, int64_t M, bool g_f32 = false) {
   GemmWorkspace w;
@@ -352,7 +355,7 @@ lrmoe_status grouped_backward(const lrmoe_problem* pb, const int32_t* perm, cons
                               const uint16_t* glu_b, void* glu_out, void* workspace,
                               size_t ws_bytes, void* stream, const lrmoe_timing* timing,
                               bool planes_ready = false, TimingSlots ts = TimingSlots(),
-                              bool g_f32 = false) {
+                              bool g_f32 = false, const uint8_t* zero_keep = nullptr) {
   Checked c;
   LRMOE_TRY(check_problem(pb, c));
   if (g_f32 && pb->dtype != LRMOE_BF16) return LRMOE_ERR_DTYPE;
@@ -484,7 +487,7 @@ lrmoe_status grouped_backward(const lrmoe_problem* pb, const int32_t* perm, cons
       for (int e = 0; e <= E; ++e) seg.off[e] = c.tab.seg_off[e];
       const uint16_t* gc16 = reinterpret_cast<const uint16_t*>(g_c);
       const uint16_t* pc16 = reinterpret_cast<const uint16_t*>(phi_c);
-      LRMOE_TRY(hip_status(launch_zero(heads, kXcds, s)));
+      LRMOE_TRY(hip_status(launch_zero(heads, kHeadCounters, s)));
       LRMOE_TRY(hip_status(launch_expert_bounds(
           seg, gc16, pc16, alpha_c, nullptr, nullptr, nullptr, (int32_t)M, (int32_t)M,
           (int32_t)M, (int32_t)M, d_out, d_in, wl.alpha_on_phi,
@@ -505,7 +508,7 @@ lrmoe_status grouped_backward(const lrmoe_problem* pb, const int32_t* perm, cons
     // products; the input-gradient epilogue then applies no alpha
     uint16_t* hi = plane(wl.b_hi);
     uint16_t* lo = wl.dw_pa == 2 ? plane(wl.b_lo) : nullptr;
-    LRMOE_TRY(hip_status(launch_split(LRMOE_F32, g_c, M, d_out, alpha_c, hi, lo, s, heads, kXcds)));
+    LRMOE_TRY(hip_status(launch_split(LRMOE_F32, g_c, M, d_out, alpha_c, hi, lo, s, heads, kHeadCounters)));
     ops.dw_a[0] = ops.dp_a[0] = hi;
     ops.dw_a[1] = ops.dp_a[1] = lo;
     ops.dw_b[0] = p16;
@@ -520,7 +523,7 @@ lrmoe_status grouped_backward(const lrmoe_problem* pb, const int32_t* perm, cons
     const void* src = wl.alpha_on_phi ? phi_c : g_c;
     const int cols = wl.alpha_on_phi ? d_in : d_out;
     if (!planes_ready)
-      LRMOE_TRY(hip_status(launch_split(LRMOE_BF16, src, M, cols, alpha_c, hi, lo, s, heads, kXcds)));
+      LRMOE_TRY(hip_status(launch_split(LRMOE_BF16, src, M, cols, alpha_c, hi, lo, s, heads, kHeadCounters)));
     if (wl.alpha_on_phi) {
       ops.dw_a[0] = g16;
       ops.dw_b[0] = hi;
@@ -537,7 +540,7 @@ lrmoe_status grouped_backward(const lrmoe_problem* pb, const int32_t* perm, cons
     ops.dp_pa = ops.dp_pb = 1;
   } else {
     LRMOE_TRY(hip_status(launch_split(LRMOE_F32, g_c, M, d_out, nullptr, plane(wl.a_hi),
-                                      plane(wl.a_lo), s, heads, kXcds)));
+                                      plane(wl.a_lo), s, heads, kHeadCounters)));
     LRMOE_TRY(hip_status(launch_split(LRMOE_F32, phi_c, M, d_in, alpha_c, plane(wl.b_hi),
                                       plane(wl.b_lo), s)));
     if (dphi != nullptr)
@@ -559,6 +562,13 @@ lrmoe_status grouped_backward(const lrmoe_problem* pb, const int32_t* perm, cons
   ops.glu_b = glu_b;
   ops.glu_out = glu_out;
   ops.glu_f32 = pb->dw_mode != LRMOE_DW_BF16;   // exact modes hand dgu on unrounded
+  if (zero_keep != nullptr && dphi != nullptr && !glu) {
+    // the dropped pairs' dphi rows are cleared inside the launch, beside the
+    // tiles: kZeroStarters workgroups start with them, the rest join later
+    ops.zero_keep = zero_keep;
+    ops.zero_rows = dphi;
+    ops.zero_first = kZeroStarters;
+  }
   LRMOE_TRY(mark(timing, false, ts.gemm, s));
   LRMOE_TRY(hip_status(launch_grouped_backward(t, ops, perm, alpha_c, dW, dphi, d_out, d_in,
                                                (int32_t)pb->P, s)));
@@ -594,7 +604,7 @@ lrmoe_status pruned_backward(const lrmoe_problem* pb, const int32_t* g_row_index
     char* ws = reinterpret_cast<char*>(workspace);
     planes.from_phi = wl.alpha_on_phi;
     planes.zero = reinterpret_cast<int32_t*>(ws + wl.heads);
-    planes.nzero = kXcds;
+    planes.nzero = kHeadCounters;
     if (wl.f16) {
       // the score pass writes per-pair row norms, the select reduces them
       // over each expert's kept pairs, the gather writes the float16 planes
@@ -612,10 +622,13 @@ lrmoe_status pruned_backward(const lrmoe_problem* pb, const int32_t* g_row_index
     }
   }
   // float16: the selection's scratch sits where the planes will be (the
-  // counters and bounds come first)
+  // counters and bounds come first).  The dropped pairs' dphi rows are not
+  // cleared by the gather but by the grouped GEMM launch, where the stores
+  // overlap the matrix-core work.
   const size_t sel_off = wl.f16 ? wl.a_hi : 0;
+  LRMOE_TRY(optional(dphi));
   LRMOE_TRY(select_compact(pb, true, nullptr, g_row_index, alpha, g, phi, scores, keep,
-                           seg_offsets, perm, g_c, phi_c, alpha_c, dphi,
+                           seg_offsets, perm, g_c, phi_c, alpha_c, nullptr,
                            reinterpret_cast<char*>(workspace) + sel_off, ws_bytes - sel_off,
                            stream, timing, true, planes, false, rnorm, ebound));
   TimingSlots ts;
@@ -623,7 +636,7 @@ lrmoe_status pruned_backward(const lrmoe_problem* pb, const int32_t* g_row_index
   ts.reduce = 4;
   ts.prologue = 5;
   return grouped_backward(pb, perm, alpha_c, g_c, phi_c, W, dW, dphi, false, nullptr, nullptr,
-                          nullptr, workspace, ws_bytes, stream, timing, fused, ts);
+                          nullptr, workspace, ws_bytes, stream, timing, fused, ts, false, keep);
 }
 
 
@@ -714,7 +727,7 @@ lrmoe_status gather_backward(const lrmoe_problem* pb, const int32_t* perm, const
   if (fused) {
     planes.from_phi = wl.alpha_on_phi;
     planes.zero = reinterpret_cast<int32_t*>(ws + wl.heads);
-    planes.nzero = kXcds;
+    planes.nzero = kHeadCounters;
     if (wl.f16) {
       planes.f16_a = reinterpret_cast<uint16_t*>(ws + wl.a_hi);
       planes.f16_b = reinterpret_cast<uint16_t*>(ws + wl.b_hi);
@@ -746,10 +759,12 @@ lrmoe_status gather_backward(const lrmoe_problem* pb, const int32_t* perm, const
         reinterpret_cast<float2*>(ws + wl.rnorm), planes.ebound, s)));
     LRMOE_TRY(mark(timing, true, ts.prologue, s));
   }
+  // the dropped pairs' dphi rows: cleared inside the grouped GEMM launch
   LRMOE_TRY(launch_gather_timed(pb, c, perm, keep, g_row_index, phi_row_index, alpha, g, phi, g_c,
-                                phi_c, alpha_c, dphi, phi_rows, s, timing, planes));
+                                phi_c, alpha_c, nullptr, phi_rows, s, timing, planes));
   return grouped_backward(pb, perm, alpha_c, g_c, phi_c, W, dW, dphi, false, nullptr, nullptr,
-                          nullptr, workspace, ws_bytes, stream, timing, fused, ts);
+                          nullptr, workspace, ws_bytes, stream, timing, fused, ts, false,
+                          dphi != nullptr ? keep : nullptr);
 }
 
 }  // namespace

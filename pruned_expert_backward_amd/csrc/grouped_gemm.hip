@@ -895,10 +895,44 @@ struct Cfg {
   static_assert(bytes <= 160 * 1024, "LDS");
 };
 
+// Zero-fill of the input-gradient rows of dropped pairs (zero_keep[u] == 0),
+// memory-bound work that runs beside the matrix-core-bound tiles of the same
+// launch.  A workgroup claims kZeroChunk consecutive pairs at a time from the
+// zero counter; each wave reads the keep bytes of 64 of them, one per lane,
+// and clears the rows whose ballot bit is set, 16 bytes per lane per store,
+// marked non-temporal (nothing reads them back in this launch; as ordinary
+// stores they evicted the tiles' operands from the caches and cost the
+// launch about 4% more).  Returns when every chunk has been claimed.
+constexpr int kZeroChunk = 256;
+__device__ __forceinline__ void zero_dropped(const Args& args, LDS_AS int32_t* s_next) {
+  if (args.ops.zero_rows == nullptr) return;
+  const int64_t P = args.P;
+  const int nchunks = (int)((P + kZeroChunk - 1) / kZeroChunk);
+  const int zch = args.d_in / 4;   // float4 per row (d_in % 4 == 0)
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (;;) {
+    if (threadIdx.x == 0) s_next[0] = atomicAdd(args.ops.queue_heads + kZeroCounter, 1);
+    lds_barrier();
+    const int c = __builtin_amdgcn_readfirstlane(s_next[0]);
+    lds_barrier();   // everyone has read s_next before it is rewritten
+    if (c >= nchunks) return;
+    const int64_t u0 = (int64_t)c * kZeroChunk + 64 * wave;
+    const bool drop = u0 + lane < P && args.ops.zero_keep[u0 + lane] == 0;
+    uint64_t m = __ballot(drop);
+    while (m != 0) {
+      const int r = __builtin_ctzll(m);
+      m &= m - 1;
+      f32x4* row = reinterpret_cast<f32x4*>(args.ops.zero_rows) + (u0 + r) * zch;
+      for (int i = lane; i < zch; i += 64)
+        __builtin_nontemporal_store(f32x4{0.f, 0.f, 0.f, 0.f}, row + i);
+    }
+  }
+}
+
 // Persistent: one workgroup per CU drains its XCD's queue.  Between tiles the
 // next tile's first loads are issued before the finished tile's stores, so
 // the store drain overlaps the next load latency.  Every workgroup exits when
-// its queue's counter passes the queue length.
+// every queue's counter and the zero-fill counter have passed their ends.
 template <int DW_PA, int DW_PB, int DP_PA, int DP_PB, int GLU, bool DW_F16>
 __global__ __launch_bounds__(kThreads, 1) void grouped_backward_kernel(Args args, GemmTable tab) {
   using C = Cfg<DW_PA, DW_PB, DP_PA, DP_PB>;
@@ -953,9 +987,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_backward_kernel(Args args
   };
 
   f32x16 acc[kMB][kNB];
+  if ((int)blockIdx.x < args.ops.zero_first) zero_dropped(args, s_next);
   bool cur_dw;
   TileJob cur;
-  if (fetch(cur_dw, cur) < 0) return;
+  if (fetch(cur_dw, cur) < 0) {
+    zero_dropped(args, s_next);
+    return;
+  }
   with_tile(cur_dw, cur, [&](const auto& t) __attribute__((always_inline)) { t.prologue(args, smem); });
   for (;;) {
     with_tile(cur_dw, cur, [&](const auto& t) __attribute__((always_inline)) {
@@ -975,6 +1013,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_backward_kernel(Args args
     cur_dw = nxt_dw;
     cur = nxt;
   }
+  zero_dropped(args, s_next);   // help with what is left of the zero-fill
 }
 
 template <int DW_PA, int DW_PB, int DP_PA, int DP_PB, int GLU = 0, bool DW_F16 = false>

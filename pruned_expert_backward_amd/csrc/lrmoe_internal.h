@@ -46,6 +46,10 @@ inline int hist_chunks(int64_t n) {
 constexpr int kTile = 256;
 constexpr int kGroupSlots = 12;
 constexpr int kXcds = 8;
+// Work counters of the grouped GEMM launch: one tile queue per XCD, then the
+// zero-fill of dropped input-gradient rows.
+constexpr int kZeroCounter = kXcds;
+constexpr int kHeadCounters = kXcds + 1;
 constexpr int kMaxGroups = 600;
 
 // Group descriptor: bit 31 = weight gradient, bits 23..30 expert,
@@ -88,7 +92,14 @@ struct GemmOperands {
   const uint16_t* dp_b[2];        // [E, d_out, d_in]: W
   int32_t dw_pa, dw_pb, dp_pa, dp_pb;   // planes in use (1 or 2)
   float* partials;                // fp32 partial dW tiles of split experts
-  int32_t* queue_heads;           // kXcds counters, zeroed by the prologue
+  int32_t* queue_heads;           // kHeadCounters counters, zeroed by the prologue
+  // Zero-fill carried by the launch (zero_rows != nullptr): the rows u of
+  // zero_rows ([P, d_in] float32) with zero_keep[u] == 0 are cleared.  The
+  // first zero_first workgroups start with it, every workgroup helps once
+  // its tile queues are empty.
+  const uint8_t* zero_keep;
+  float* zero_rows;
+  int32_t zero_first;
   // SiLU-GLU chain (glu_out != nullptr): the input-gradient tiles, instead of
   // writing alpha * dphi, write the gate/up output gradient of each kept
   // pair from its saved pre-activations a = glu_a[u], b = glu_b[u] ([P,

@@ -629,6 +629,39 @@ def test_random_shapes(seed):
     print(f"random-{seed}", errs, "keep identical" if same else "keep differs inside band")
 
 
+@pytest.mark.parametrize("P,E,d_in,frac,dw_mode", [
+    (37, 2, 136, (1, 2), lrmoe.DW_F16),       # fewer pairs than one wave's keep bytes
+    (4099, 3, 200, (1, 5), lrmoe.DW_EXACT),   # ragged last chunk of 256 pairs
+    (9000, 4, 1408, (1, 10), lrmoe.DW_F16),   # GLM-width rows, many chunks
+    (777, 3, 72, (0, 1), lrmoe.DW_F16),       # nothing kept: every row dropped
+])
+def test_dropped_rows_cleared(P, E, d_in, frac, dw_mode):
+    """The one-call path and lrmoe_gather_backward clear the dropped pairs'
+    dphi rows inside the grouped GEMM launch, beside its tiles.  On dphi
+    buffers filled with NaN beforehand, every dropped row comes back exactly
+    zero and the whole buffer equals the separate calls' (whose gather clears
+    the rows)."""
+    p = W.make_problem(P=P, E=E, d_out=64, d_in=d_in, dtype="bf16", zipf=1.1, seed=P + d_in)
+    q = [c * frac[0] // frac[1] for c in p.counts]
+    print(f"cleared rows: P={P} E={E} d_in={d_in} M={sum(q)}", flush=True)
+    plan, sep, t = U.run_gpu(p, q, dw_mode=dw_mode)
+    out = lrmoe.alloc_select_outputs(plan, t["g"].device)
+    out["dphi"].fill_(float("nan"))
+    one = lrmoe.pruned_backward(plan, t["alpha"], t["g"], t["phi"], t["W"], g_row_index=t["row"],
+                                out=out)
+    gb = lrmoe.gather_backward(plan, sep["perm"], sep["keep"], t["alpha"], t["g"], t["phi"],
+                               t["W"], g_row_index=t["row"],
+                               out={"dphi": torch.full((P, d_in), float("nan"),
+                                                       device=t["g"].device)})
+    torch.cuda.synchronize()
+    dropped = ~sep["keep"].bool()
+    for name, res in (("one call", one["dphi"]), ("gather_backward", gb["dphi"])):
+        assert not torch.isnan(res).any(), name
+        if bool(dropped.any()):
+            assert float(res[dropped].abs().max()) == 0.0, name
+        assert torch.equal(res, sep["dphi"]), name
+
+
 def test_whole_path_call_nothing_kept():
     p = W.make_problem(P=500, E=3, d_out=64, d_in=32, dtype="bf16", counts=[200, 0, 300], seed=9)
     plan = lrmoe.Plan(p.counts, [0, 0, 0], p.d_out, p.d_in, lrmoe.BF16)
