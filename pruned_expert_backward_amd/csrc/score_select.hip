@@ -145,6 +145,7 @@ constexpr int kBins = kHistBins;     // first and second digits: 12 bits; last d
 constexpr int kHistPer = kHistChunk / kSelThreads;   // keys per thread in a histogram chunk
 constexpr int kScanPer = 8;          // keys per thread per scan tile
 constexpr int kScanTile = kSelThreads * kScanPer;
+constexpr int kCandLoads = 16;       // 16-byte score loads in flight per thread (candidates)
 
 // Inclusive prefix sum of v over the workgroup in thread order; `total`
 // receives the workgroup sum.  wsum: kSelWaves LDS words.
@@ -308,9 +309,13 @@ __device__ __forceinline__ void scan_keep(const uint32_t* keys_lds, const float*
         kk[j] = (g >= base && g < end) ? keys_lds[g - lds_base] : 0u;
       }
     } else {
+      // a tile wholly inside the score array: plain vector loads (load4's
+      // per-lane bounds branch would wait for each load in turn)
+      const bool full = c + kScanTile <= P;   // workgroup-uniform
 #pragma unroll
       for (int h = 0; h < kScanPer / 4; ++h) {
-        const float4 v = load4(scores, g0 + 4 * h, P);
+        const float4 v = full ? *reinterpret_cast<const float4*>(scores + g0 + 4 * h)
+                              : load4(scores, g0 + 4 * h, P);
         kk[4 * h] = score_key(v.x);
         kk[4 * h + 1] = score_key(v.y);
         kk[4 * h + 2] = score_key(v.z);
@@ -318,11 +323,27 @@ __device__ __forceinline__ void scan_keep(const uint32_t* keys_lds, const float*
       }
     }
   };
+  // operand row norms of the tile's pairs, loaded with its keys (loaded
+  // only for kept pairs, each was a dependent load inside the scan)
+  auto load_rn = [&](int c, float2 (&r)[kScanPer]) {
+    if (rnorm == nullptr) return;
+    const int g0 = c + tid * kScanPer;
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) {
+      const int g = g0 + j;
+      r[j] = (g >= base && g < end) ? rnorm[g] : make_float2(0.f, 0.f);
+    }
+  };
   uint32_t key[kScanPer], key_next[kScanPer];
+  float2 rn[kScanPer], rn_next[kScanPer];
   load_tile(gbeg, key);
+  load_rn(gbeg, rn);
   for (int c = gbeg; c < end; c += kScanTile) {
     const int g0 = c + tid * kScanPer;
-    if (c + kScanTile < end) load_tile(c + kScanTile, key_next);
+    if (c + kScanTile < end) {
+      load_tile(c + kScanTile, key_next);
+      load_rn(c + kScanTile, rn_next);
+    }
     uint32_t ngt = 0, neq = 0;
 #pragma unroll
     for (int j = 0; j < kScanPer; ++j) {
@@ -352,9 +373,8 @@ __device__ __forceinline__ void scan_keep(const uint32_t* keys_lds, const float*
           if (pos < q) perm[seg + pos] = g;   // pos < q holds by construction
           ++pos;
           if (rnorm != nullptr) {
-            const float2 m = rnorm[g];
-            kbound[0] = max(kbound[0], __float_as_uint(m.x));
-            kbound[1] = max(kbound[1], __float_as_uint(m.y));
+            kbound[0] = max(kbound[0], __float_as_uint(rn[j].x));
+            kbound[1] = max(kbound[1], __float_as_uint(rn[j].y));
           }
         }
       }
@@ -376,7 +396,10 @@ __device__ __forceinline__ void scan_keep(const uint32_t* keys_lds, const float*
     run_gt += tot >> 16;
     run_eq += tot & 0xFFFFu;
 #pragma unroll
-    for (int j = 0; j < kScanPer; ++j) key[j] = key_next[j];
+    for (int j = 0; j < kScanPer; ++j) {
+      key[j] = key_next[j];
+      rn[j] = rn_next[j];
+    }
   }
 }
 
@@ -435,9 +458,19 @@ __global__ __launch_bounds__(kSelThreads) void select_scan_kernel(
       __syncthreads();
       for (int i = tid; i < n; i += kSelThreads) atomicAdd(&hist[keys_lds[i] >> 20], 1u);
     } else {
+      // eight chunk histograms in flight per thread (one at a time, the
+      // latency of each load was paid in full)
       u32x4 h = {0u, 0u, 0u, 0u};
-      for (int c = tab.hist_off[e]; c < tab.hist_off[e + 1]; ++c)
-        h += reinterpret_cast<const u32x4*>(hist_in + (size_t)c * kBins)[tid];
+      const int c1 = tab.hist_off[e + 1];
+      for (int c = tab.hist_off[e]; c < c1; c += 8) {
+        u32x4 t[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          t[j] = c + j < c1 ? reinterpret_cast<const u32x4*>(hist_in + (size_t)(c + j) * kBins)[tid]
+                            : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) h += t[j];
+      }
       reinterpret_cast<u32x4*>(hist)[tid] = h;   // kSelThreads * 4 == kBins
     }
     __syncthreads();
@@ -454,13 +487,25 @@ __global__ __launch_bounds__(kSelThreads) void select_scan_kernel(
       if (d1.count <= (uint32_t)kSelLdsKeys) {
         if (tid == 0) cand_n = 0;
         __syncthreads();
-        // four 16-byte loads in flight per thread: one workgroup streams the expert
-        for (int a0 = gbeg; a0 < end; a0 += 16 * kSelThreads) {
-          float4 v[4];
+        // one workgroup streams the expert, kCandLoads 16-byte loads in
+        // flight per thread; steps wholly inside the score array use plain
+        // vector loads (no per-lane bounds branch).  This phase is bound by
+        // what one CU can stream (about 35 GB/s measured: 9 us per 256 KiB
+        // step) and by the LDS atomics of the appends; on a 286k-pair expert
+        // it is still the selection's longest (about 45 us).
+        for (int a0 = gbeg; a0 < end; a0 += 4 * kCandLoads * kSelThreads) {
+          float4 v[kCandLoads];
+          if (a0 + 4 * kCandLoads * kSelThreads <= P) {   // workgroup-uniform
 #pragma unroll
-          for (int j = 0; j < 4; ++j) v[j] = load4(scores, a0 + 4 * (j * kSelThreads + tid), P);
+            for (int j = 0; j < kCandLoads; ++j)
+              v[j] = *reinterpret_cast<const float4*>(scores + a0 + 4 * (j * kSelThreads + tid));
+          } else {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < kCandLoads; ++j)
+              v[j] = load4(scores, a0 + 4 * (j * kSelThreads + tid), P);
+          }
+#pragma unroll
+          for (int j = 0; j < kCandLoads; ++j) {
             const int a = a0 + 4 * (j * kSelThreads + tid);
             const float x[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
 #pragma unroll
@@ -528,10 +573,18 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_count_kernel(
   const int hi = min(lo + kHistChunk, tab.pair_off[e + 1]);
   const uint32_t tau = tau_need[2 * e];
   uint32_t ngt = 0, neq = 0;
-  for (int i = lo + tid; i < hi; i += kSelThreads) {
-    const uint32_t k = score_key(scores[i]);
-    ngt += k > tau ? 1u : 0u;
-    neq += k == tau ? 1u : 0u;
+  float v[kHistPer];   // every load of the chunk in flight at once
+#pragma unroll
+  for (int j = 0; j < kHistPer; ++j) {
+    const int i = lo + j * kSelThreads + tid;
+    v[j] = i < hi ? scores[i] : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < kHistPer; ++j) {
+    const uint32_t k = score_key(v[j]);
+    const bool ok = lo + j * kSelThreads + tid < hi;
+    ngt += ok && k > tau ? 1u : 0u;
+    neq += ok && k == tau ? 1u : 0u;
   }
   uint32_t tot;
   block_scan((ngt << 16) | neq, wsum, tot);   // chunk < 2^16 pairs
@@ -554,11 +607,16 @@ __global__ __launch_bounds__(kSelThreads) void select_chunk_scan_kernel(
   while (e + 1 < tab.E && tab.hist_off[e + 1] <= b) ++e;
   const int lo = tab.pair_off[e] + (b - tab.hist_off[e]) * kHistChunk;
   const int hi = min(lo + kHistChunk, tab.pair_off[e + 1]);
-  uint32_t run_gt = 0, run_eq = 0;
-  for (int c = tab.hist_off[e]; c < b; ++c) {
-    run_gt += counts[2 * c];
-    run_eq += counts[2 * c + 1];
+  // counts of the expert's earlier chunks, summed over the workgroup (one
+  // load per thread instead of a serial chain of them)
+  uint32_t pgt = 0, peq = 0;
+  for (int c = tab.hist_off[e] + (int)threadIdx.x; c < b; c += kSelThreads) {
+    pgt += counts[2 * c];
+    peq += counts[2 * c + 1];
   }
+  uint32_t run_gt, run_eq;
+  block_scan(pgt, wsum, run_gt);
+  block_scan(peq, wsum, run_eq);
   const int seg = tab.seg_off[e];
   const uint32_t q = (uint32_t)(tab.seg_off[e + 1] - seg);
   uint32_t kbound[2] = {0u, 0u};
