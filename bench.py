@@ -404,10 +404,10 @@ def main():
     # algorithmic bytes (HBM-bound kernels) and FLOP (the GEMM) per launch
     score_bytes = (P * (es * (d_o + d_i) + 8) if args.score_mode == "lrm"
                    else P * (es * d_o + 4))   # gradient-only rules read no phi, no alpha
-    # the dropped pairs' dphi rows: zeroed by the gather, except in the one-call
-    # path, whose grouped GEMM launch clears them beside its tiles
+    # the dropped pairs' dphi rows: zeroed by the gather, except for large fills
+    # in the one-call path, whose grouped GEMM launch clears them beside its tiles
     zero_bytes = 0 if chain or dense_path else (P - M) * 4 * d_i
-    zero_in_gemm = whole
+    zero_in_gemm = whole and lrmoe.zero_fill_in_gemm(plan)
     work = {"lrm_score": score_bytes,
             "select_scan": P * 5,
             "gather": M * (2 * es * (d_o + d_i) + 12) + (0 if zero_in_gemm else zero_bytes),
@@ -463,6 +463,9 @@ def main():
                 traffic=traffic, traffic_unit="bytes per launch",
                 mfma_busy_frac=mfma_busy,
                 algorithmic_bytes_floor=gemm_floor_bytes(p, M) + (zero_bytes if zero_in_gemm else 0))
+    if traffic is not None:   # the launch's measured HBM traffic per second of its duration
+        roof["traffic_GBps"] = traffic / gemm_live["mean"] / 1e3
+        roof["traffic_hbm_frac"] = roof["traffic_GBps"] / HBM_PEAK_GBS
     if zero_in_gemm:
         roof["zero_fill_bytes"] = zero_bytes
         roof["zero_fill_note"] = ("the launch also clears the dropped pairs' dphi rows "
@@ -471,7 +474,8 @@ def main():
     if gu is not None:
         roof["note"] = "the gate/up projection's grouped GEMM (its flops 4 M d_out2 d_in2)"
         es2 = 2
-        gu_zero = 0 if chain else (P - M) * 4 * gu.d_in   # cleared in that launch
+        gu_zero = (0 if chain or not lrmoe.zero_fill_in_gemm(plan2)
+                   else (P - M) * 4 * gu.d_in)   # cleared in that launch
         roof["algorithmic_bytes_floor"] = (M * es2 * (gu.d_out + gu.d_in)
                                            + p.E * gu.d_out * gu.d_in * (es2 + 4)
                                            + M * gu.d_in * 4 + gu_zero)
@@ -529,8 +533,9 @@ def main():
             gpro, gred = gu_timer.mean_us(5), gu_timer.mean_us(4)
         if chain:   # x rows and alpha only: the gate/up gradient is already compacted
             gbytes = M * (2 * es * gu.d_in + 12) + (P - M) * 4 * gu.d_in
-        else:   # its dropped dphi rows are cleared in the GEMM launch
-            gbytes = M * (2 * es * (gu.d_out + gu.d_in) + 12)
+        else:   # its dropped dphi rows: in the gather unless cleared in the GEMM launch
+            gbytes = M * (2 * es * (gu.d_out + gu.d_in) + 12) + (
+                0 if lrmoe.zero_fill_in_gemm(plan2) else (P - M) * 4 * gu.d_in)
         gfl = 4.0 * M * gu.d_out * gu.d_in
         rec["gate_up"] = {
             "d_out": gu.d_out, "d_in": gu.d_in,
@@ -540,7 +545,7 @@ def main():
             "grouped_gemm": {"us": gg["mean"], "us_median": gg["median"],
                              "algorithmic_flops": gfl, "TFLOPs": gfl / gg["mean"] / 1e6,
                              "mfma_frac": gfl / gg["mean"] / 1e6 / MFMA_BF16_PEAK_TFLOPS,
-                             **({} if chain else
+                             **({} if chain or not lrmoe.zero_fill_in_gemm(plan2) else
                                 {"zero_fill_bytes": (P - M) * 4 * gu.d_in})},
             "operand_prologue_us": gpro, "splitk_reduce_us": gred}
         gu_timer.close()

@@ -110,6 +110,15 @@ constexpr int kStepK = 32;   // K rows per pipeline step of the GEMM kernel
 // Workgroups of the grouped GEMM launch that start with the zero-fill of the
 // dropped pairs' dphi rows (3 per XCD) instead of tiles.
 constexpr int kZeroStarters = 24;
+// The one-call paths clear the dropped pairs' dphi rows inside the grouped
+// GEMM launch when those rows hold at least this many bytes (there the stores
+// overlap the matrix-core work: 3.3 GB cost the launch 0.4 ms against 0.58 ms
+// in the gather); smaller fills stay in the gather, where they cost less than
+// the starters delay a short launch.
+constexpr int64_t kZeroInGemmBytes = int64_t(512) << 20;
+bool zero_in_gemm(const lrmoe_problem* pb, int64_t M) {
+  return (pb->P - M) * (int64_t)pb->d_in * 4 >= kZeroInGemmBytes;
+}
 
 GemmWorkspace gemm_workspace(const lrmoe_problem* pb, int64_t M, bool g_f32 = false) {
   GemmWorkspace w;
@@ -622,13 +631,14 @@ lrmoe_status pruned_backward(const lrmoe_problem* pb, const int32_t* g_row_index
     }
   }
   // float16: the selection's scratch sits where the planes will be (the
-  // counters and bounds come first).  The dropped pairs' dphi rows are not
-  // cleared by the gather but by the grouped GEMM launch, where the stores
-  // overlap the matrix-core work.
+  // counters and bounds come first).  The dropped pairs' dphi rows are
+  // cleared by the gather, or (large fills) by the grouped GEMM launch, where
+  // the stores overlap the matrix-core work.
   const size_t sel_off = wl.f16 ? wl.a_hi : 0;
   LRMOE_TRY(optional(dphi));
+  const bool zfill = dphi != nullptr && zero_in_gemm(pb, M);
   LRMOE_TRY(select_compact(pb, true, nullptr, g_row_index, alpha, g, phi, scores, keep,
-                           seg_offsets, perm, g_c, phi_c, alpha_c, nullptr,
+                           seg_offsets, perm, g_c, phi_c, alpha_c, zfill ? nullptr : dphi,
                            reinterpret_cast<char*>(workspace) + sel_off, ws_bytes - sel_off,
                            stream, timing, true, planes, false, rnorm, ebound));
   TimingSlots ts;
@@ -636,7 +646,8 @@ lrmoe_status pruned_backward(const lrmoe_problem* pb, const int32_t* g_row_index
   ts.reduce = 4;
   ts.prologue = 5;
   return grouped_backward(pb, perm, alpha_c, g_c, phi_c, W, dW, dphi, false, nullptr, nullptr,
-                          nullptr, workspace, ws_bytes, stream, timing, fused, ts, false, keep);
+                          nullptr, workspace, ws_bytes, stream, timing, fused, ts, false,
+                          zfill ? keep : nullptr);
 }
 
 
@@ -759,12 +770,15 @@ lrmoe_status gather_backward(const lrmoe_problem* pb, const int32_t* perm, const
         reinterpret_cast<float2*>(ws + wl.rnorm), planes.ebound, s)));
     LRMOE_TRY(mark(timing, true, ts.prologue, s));
   }
-  // the dropped pairs' dphi rows: cleared inside the grouped GEMM launch
+  // the dropped pairs' dphi rows: cleared by the gather, or (large fills)
+  // inside the grouped GEMM launch
+  const bool zfill = dphi != nullptr && zero_in_gemm(pb, c.M);
   LRMOE_TRY(launch_gather_timed(pb, c, perm, keep, g_row_index, phi_row_index, alpha, g, phi, g_c,
-                                phi_c, alpha_c, nullptr, phi_rows, s, timing, planes));
+                                phi_c, alpha_c, zfill ? nullptr : dphi, phi_rows, s, timing,
+                                planes));
   return grouped_backward(pb, perm, alpha_c, g_c, phi_c, W, dW, dphi, false, nullptr, nullptr,
                           nullptr, workspace, ws_bytes, stream, timing, fused, ts, false,
-                          dphi != nullptr ? keep : nullptr);
+                          zfill ? keep : nullptr);
 }
 
 }  // namespace

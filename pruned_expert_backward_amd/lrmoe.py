@@ -426,6 +426,19 @@ def gather_backward(plan: Plan, perm, keep, alpha, g, phi, W, g_row_index=None,
     return out
 
 
+# The one-call entry points (lrmoe_pruned_backward, lrmoe_gather_backward)
+# clear the dropped pairs' dphi rows inside the grouped GEMM launch when they
+# hold at least this many bytes, else in the gather (the library's rule,
+# restated for accounting).
+ZERO_IN_GEMM_BYTES = 512 << 20
+
+
+def zero_fill_in_gemm(plan: Plan) -> bool:
+    """Where the one-call entry points clear the dropped dphi rows: True for
+    the grouped GEMM launch, False for the gather."""
+    return (plan.P - plan.M) * plan.d_in * 4 >= ZERO_IN_GEMM_BYTES
+
+
 def glu_grad_dtype(plan: Plan) -> torch.dtype:
     """Storage of the SiLU-GLU chain's hand-off gradient: float32, or bf16 in
     the single-rounding dW mode."""

@@ -634,17 +634,19 @@ def test_random_shapes(seed):
     (4099, 3, 200, (1, 5), lrmoe.DW_EXACT),   # ragged last chunk of 256 pairs
     (9000, 4, 1408, (1, 10), lrmoe.DW_F16),   # GLM-width rows, many chunks
     (777, 3, 72, (0, 1), lrmoe.DW_F16),       # nothing kept: every row dropped
+    (120000, 4, 1408, (1, 10), lrmoe.DW_F16), # 608 MB of dropped rows: cleared in the GEMM launch
 ])
 def test_dropped_rows_cleared(P, E, d_in, frac, dw_mode):
     """The one-call path and lrmoe_gather_backward clear the dropped pairs'
-    dphi rows inside the grouped GEMM launch, beside its tiles.  On dphi
-    buffers filled with NaN beforehand, every dropped row comes back exactly
-    zero and the whole buffer equals the separate calls' (whose gather clears
-    the rows)."""
+    dphi rows: in the gather, or (at least 512 MiB of them) inside the grouped
+    GEMM launch, beside its tiles.  On dphi buffers filled with NaN
+    beforehand, every dropped row comes back exactly zero and the whole buffer
+    equals the separate calls' (whose gather clears the rows)."""
     p = W.make_problem(P=P, E=E, d_out=64, d_in=d_in, dtype="bf16", zipf=1.1, seed=P + d_in)
     q = [c * frac[0] // frac[1] for c in p.counts]
-    print(f"cleared rows: P={P} E={E} d_in={d_in} M={sum(q)}", flush=True)
     plan, sep, t = U.run_gpu(p, q, dw_mode=dw_mode)
+    print(f"cleared rows: P={P} E={E} d_in={d_in} M={sum(q)} "
+          f"in the GEMM launch: {lrmoe.zero_fill_in_gemm(plan)}", flush=True)
     out = lrmoe.alloc_select_outputs(plan, t["g"].device)
     out["dphi"].fill_(float("nan"))
     one = lrmoe.pruned_backward(plan, t["alpha"], t["g"], t["phi"], t["W"], g_row_index=t["row"],
