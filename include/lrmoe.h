@@ -288,8 +288,9 @@ lrmoe_status lrmoe_gather_compact(
  * operand planes from the rows it moves (as in lrmoe_pruned_backward), bit
  * for bit the separate calls' results.  g and g_c are required here; dphi is
  * both the zero target of dropped rows and the output of kept rows (or
- * NULL).  workspace: lrmoe_workspace_size bytes.  Errors as for the two
- * calls. */
+ * NULL); dropped rows of at least 512 MiB in all are cleared inside the
+ * grouped GEMM launch, as in lrmoe_pruned_backward.  workspace:
+ * lrmoe_workspace_size bytes.  Errors as for the two calls. */
 lrmoe_status lrmoe_gather_backward(
     const lrmoe_problem* pb, const int32_t* perm, const uint8_t* keep,
     const int32_t* g_row_index, const int32_t* phi_row_index,
@@ -363,8 +364,10 @@ lrmoe_status lrmoe_grouped_backward_gate_up(
  * GEMM's operand planes (alpha times the narrower compacted operand, as bf16
  * hi and, in exact mode, lo) from the rows it moves, so no separate pass
  * reads the compacted operand again; the planes and every result are bit for
- * bit those of the two separate calls.  workspace: lrmoe_workspace_size
- * bytes.  Errors as for the two calls. */
+ * bit those of the two separate calls.  When the dropped pairs' dphi rows
+ * hold at least 512 MiB ((P - M) * d_in * 4 bytes), the grouped GEMM launch
+ * clears them beside its tiles instead of the gather (same results).
+ * workspace: lrmoe_workspace_size bytes.  Errors as for the two calls. */
 lrmoe_status lrmoe_pruned_backward(
     const lrmoe_problem* pb, const int32_t* g_row_index, const float* alpha,
     const void* g, const void* phi, const void* W, float* scores, uint8_t* keep,
