@@ -56,8 +56,11 @@ __device__ __forceinline__ void tail3(const V* __restrict__ row, int c, int nchu
 // This lane's shares of the sums of squares of a pair's two bf16 rows: the
 // g row (gc 16-byte chunks) and the phi row (pc chunks), read as one
 // sequence of chunks c = lane + 64 k (c < gc from g, else chunk c - gc of
-// phi), eight loads in flight per lane, so that a pair costs as few memory
-// round trips as its bytes allow.  A row that is not there (g_ok / p_ok
+// phi), sixteen loads in flight per lane (one round trip for a GLM pair's
+// 688 chunks; with eight, two, and the score pass ran 2.4 % slower on the
+// 655 360-pair workload despite twice the waves per SIMD).  Chunk i of a
+// batch adds into accumulator i % 4 in increasing i, so the sums do not
+// depend on the batch size.  A row that is not there (g_ok / p_ok
 // false) reads as zeros but keeps its chunk positions, so the other row's
 // sum is the same either way.  {x: g, y: phi}; reduce each with wave_sum.
 __device__ __forceinline__ float2 pair_sumsq_bf16(const uint4* __restrict__ g, int gc, bool g_ok,
@@ -65,10 +68,10 @@ __device__ __forceinline__ float2 pair_sumsq_bf16(const uint4* __restrict__ g, i
                                                   bool p_ok, int lane) {
   float ag[4] = {0.f, 0.f, 0.f, 0.f}, ap[4] = {0.f, 0.f, 0.f, 0.f};
   const int n = gc + pc;
-  for (int base = lane; base < n; base += 64 * 8) {
-    uint4 x[8];
+  for (int base = lane; base < n; base += 64 * 16) {
+    uint4 x[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 16; ++i) {
       const int c = base + 64 * i;
       const bool in_g = c < gc;
       const uint4* src = in_g ? g + c : phi + (c - gc);
@@ -76,7 +79,7 @@ __device__ __forceinline__ float2 pair_sumsq_bf16(const uint4* __restrict__ g, i
       x[i] = ok ? *src : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 16; ++i) {
       const float v = sumsq8(x[i]);
       if (base + 64 * i < gc) ag[i & 3] += v;
       else ap[i & 3] += v;
