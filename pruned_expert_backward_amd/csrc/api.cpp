@@ -73,10 +73,10 @@ lrmoe_status check_problem(const lrmoe_problem* pb, Checked& c) {
   c.tab.seg_off[pb->E] = (int32_t)M;
   int32_t hc = 0;
   for (int e = 0; e < pb->E; ++e) {
-    c.tab.hist_off[e] = hc;
-    hc += hist_chunks(pb->counts[e]);
+    c.tab.chunk_off[e] = hc;
+    hc += sel_chunks(pb->counts[e]);
   }
-  c.tab.hist_off[pb->E] = hc;
+  c.tab.chunk_off[pb->E] = hc;
   c.tab.M = (int32_t)M;
   c.M = M;
   return LRMOE_OK;
@@ -200,14 +200,9 @@ GemmWorkspace gemm_workspace(const lrmoe_problem* pb, int64_t M, bool g_f32 = fa
   return w;
 }
 
-// Selection: one kHistBins-bin histogram per chunk of a large expert.
-// plus tau and need per expert and the (above, equal) counts of every chunk,
-// for the chunk-parallel scan of large experts.
-size_t select_workspace(const Checked& c) {
-  const size_t chunks = (size_t)c.tab.hist_off[c.tab.E];
-  if (chunks == 0) return 0;
-  return (chunks * kHistBins + 2 * (size_t)kMaxE + 2 * chunks) * sizeof(uint32_t);
-}
+// Selection: three digit histograms and the select state per expert, two
+// counts per chunk.
+size_t select_workspace(const Checked& c) { return select_workspace_bytes(c.tab); }
 
 // One size for every call of the problem: the selection, the grouped GEMMs,
 // and (bf16 storage) the gate/up variant with a float32 output gradient.
@@ -310,7 +305,7 @@ lrmoe_status select_compact(const lrmoe_problem* pb, bool compute_scores, const 
     LRMOE_TRY(need(alpha_c, M));
     LRMOE_TRY(optional(dphi_zero));
   }
-  const size_t ws_need = select_workspace(c);   // 0 unless an expert is large
+  const size_t ws_need = select_workspace(c);   // 0 unless an expert is above kSelLdsKeys
   if (use_scratch) {   // the library's static scratch instead of a workspace
     if (ws_need > kScratchBytes) return LRMOE_ERR_SCRATCH;
     LRMOE_TRY(scratch_address(&workspace));
@@ -330,9 +325,8 @@ lrmoe_status select_compact(const lrmoe_problem* pb, bool compute_scores, const 
     scores = scores_out;
   }
   LRMOE_TRY(mark(timing, false, 1, s));
-  LRMOE_TRY(hip_status(launch_select_scan(c.tab, scores, keep, perm, seg_offsets,
-                                          reinterpret_cast<uint32_t*>(workspace), s, rnorm,
-                                          ebound)));
+  LRMOE_TRY(hip_status(launch_select(c.tab, scores, keep, perm, seg_offsets,
+                                     reinterpret_cast<uint32_t*>(workspace), s, rnorm, ebound)));
   LRMOE_TRY(mark(timing, true, 1, s));
   if (!gather) return LRMOE_OK;
   LRMOE_TRY(mark(timing, false, 2, s));

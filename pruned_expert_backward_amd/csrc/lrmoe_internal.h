@@ -14,26 +14,23 @@ constexpr int kMaxE = LRMOE_MAX_EXPERTS;
 // Per-expert offsets, known on the host before the backward starts (the
 // quotas are fixed ahead of it), passed to kernels by value so that no
 // host-to-device copy or device-side prefix sum is needed.
-// Selection: experts with more pairs than fit in the select kernel's LDS key
-// cache get their first radix digit counted by many workgroups, one per
-// chunk of kHistChunk pairs, each writing a kHistBins-bin histogram to the
-// workspace.
+// Selection.  Problems whose experts all have at most kSelLdsKeys pairs are
+// selected by one workgroup per expert with the keys in LDS.  Otherwise every
+// expert's pairs are cut into chunks of kSelChunk, and each pass of the radix
+// select and the scan runs one workgroup per chunk.
 constexpr int kSelLdsKeys = 24576;
-constexpr int kHistChunk = 16384;
-constexpr int kHistBins = 4096;
+constexpr int kSelChunk = 4096;
 
 struct ExpertTable {
   int32_t E;
   int32_t M;                      // total kept pairs
   int32_t pair_off[kMaxE + 1];    // first pair of expert e (expert-sorted)
   int32_t seg_off[kMaxE + 1];     // first compacted row of expert e
-  int32_t hist_off[kMaxE + 1];    // first histogram chunk of expert e (large experts only)
+  int32_t chunk_off[kMaxE + 1];   // first selection chunk of expert e
 };
 
-// Histogram chunks of expert e (0 unless it has more than kSelLdsKeys pairs).
-inline int hist_chunks(int64_t n) {
-  return n > kSelLdsKeys ? (int)((n + kHistChunk - 1) / kHistChunk) : 0;
-}
+// Selection chunks of an expert with n pairs.
+inline int sel_chunks(int64_t n) { return (int)((n + kSelChunk - 1) / kSelChunk); }
 
 // Tile schedule of the grouped GEMMs (host-built, by value).  Output tiles
 // are kTile x kTile.  Tiles are handed out in groups of kGroupSlots slots
@@ -184,12 +181,18 @@ hipError_t launch_score(int dtype, int mode, const void* g, const void* phi, con
                         int32_t d_in, float* scores, hipStream_t s, float2* rnorm = nullptr,
                         int alpha_on_phi = 1);
 
-// ebound (or null): float32 [E][2], the largest rnorm over each expert's kept
-// pairs (0 for an expert that keeps nothing).
-hipError_t launch_select_scan(const ExpertTable& tab, const float* scores, uint8_t* keep,
-                              int32_t* perm, int32_t* seg_offsets_out, uint32_t* hist,
-                              hipStream_t s, const float2* rnorm = nullptr,
-                              float* ebound = nullptr);
+// Bytes of the selection's workspace (digit histograms, select state and
+// chunk counts of the chunked passes; 0 for the LDS path).
+size_t select_workspace_bytes(const ExpertTable& tab);
+
+// Per-expert top-quota selection and the compaction scan: keep flags, perm
+// and seg_offsets.  ws: select_workspace_bytes(tab) bytes, 16-byte aligned;
+// nothing in it needs to start at zero.  ebound (or null): float32 [E][2],
+// the largest rnorm over each expert's kept pairs (0 for an expert that
+// keeps nothing).
+hipError_t launch_select(const ExpertTable& tab, const float* scores, uint8_t* keep,
+                         int32_t* perm, int32_t* seg_offsets_out, uint32_t* ws, hipStream_t s,
+                         const float2* rnorm = nullptr, float* ebound = nullptr);
 
 hipError_t launch_plan_quota_device(const int32_t* ids, int32_t n_ids, int32_t E, int32_t mode,
                                     int64_t num, int64_t den, int64_t Q, int64_t* counts,

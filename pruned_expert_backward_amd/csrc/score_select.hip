@@ -8,19 +8,20 @@
 //
 // Select + scan: within each expert's quota the highest-scoring pairs are kept
 // (Portuguese write-up "LRMoE poda a passagem reversa do MoE ...", selection
-// bullet).  One 1024-thread workgroup per expert runs an MSB-first radix
-// select (12 + 12 + 8-bit digits) on an order-preserving integer image of the
-// float32 scores to find the q_e-th largest key tau_e and how many keys equal
-// to tau_e are still needed; ties go to the lower pair index.  Keys of experts
-// up to 24576 pairs are cached in LDS.  For larger experts the first digit is
-// counted by many workgroups at once (select_hist_kernel, one per 16384-pair
-// chunk, histograms in the workspace), and only the keys in that digit's bin
-// are gathered into LDS for the later digits.  The same
-// workgroup then scans the expert's pairs in index order (8 consecutive keys
-// per thread, one workgroup prefix sum per 8192 keys), writes the keep flags
-// and the compacted permutation (ascending pair index inside the segment).
-// Global score reads are 16-byte vectors from an aligned start (a single
-// workgroup's bandwidth is bounded by its vector memory instructions).
+// bullet).  An MSB-first radix select (12 + 12 + 8-bit digits) on an
+// order-preserving integer image of the float32 scores finds each expert's
+// q_e-th largest key tau_e and how many keys equal to tau_e are still
+// needed; ties go to the lower pair index.  Every expert's pairs are cut into
+// chunks of 4096, and every pass runs one 256-thread workgroup per chunk:
+// three digit passes (each chunk counts its digit in LDS and adds the
+// nonzero bins into the expert's histogram in the workspace; the next pass
+// finds the digit from it), a count pass (keys above and equal to tau per
+// chunk) and a stable scan in pair order (each chunk starts from the counts
+// of the expert's earlier chunks) that writes the keep flags and the
+// compacted permutation (ascending pair index inside the segment).  One
+// workgroup per expert, as an earlier design had it, streams scores it did
+// not write at only about 35 GB/s, which made the largest expert the
+// critical path.
 #include "lrmoe_internal.h"
 #include "row_norm.h"
 
@@ -138,17 +139,30 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kSelThreads = 1024;
-constexpr int kSelWaves = kSelThreads / 64;
-// kSelLdsKeys (96 KiB): keys of one expert, or first-digit candidates
-constexpr int kBins = kHistBins;     // first and second digits: 12 bits; last digit: 8 bits
-constexpr int kHistPer = kHistChunk / kSelThreads;   // keys per thread in a histogram chunk
-constexpr int kScanPer = 8;          // keys per thread per scan tile
-constexpr int kScanTile = kSelThreads * kScanPer;
-constexpr int kCandLoads = 16;       // 16-byte score loads in flight per thread (candidates)
+// Selection: every expert's pairs are cut into chunks of kSelChunk, one
+// 256-thread workgroup per chunk in every pass.
+constexpr int kSelT = 256;
+constexpr int kSelW = kSelT / 64;
+constexpr int kKeysPer = kSelChunk / kSelT;   // 16 keys per thread
+constexpr int kB12 = 4096;                    // bins of digits 1 and 2 (12 bits)
+constexpr int kB8 = 256;                      // bins of digit 3 (8 bits)
+static_assert(kSelChunk % (4 * kSelT) == 0, "chunk shape");
 
-// Inclusive prefix sum of v over the workgroup in thread order; `total`
-// receives the workgroup sum.  wsum: kSelWaves LDS words.
+// Selection workspace: per expert the three digit histograms (h1, h2, h3
+// contiguous), the state of the radix select st[8e + ...] = {prefix after
+// digit 1, its rank, prefix after digit 2, its rank, tau, need}, and two
+// counts per chunk (keys above and equal to tau).
+struct SelWs {
+  uint32_t* h1;        // [E][kB12]
+  uint32_t* h2;        // [E][kB12]
+  uint32_t* h3;        // [E][kB8]
+  uint32_t* st;        // [E][8]
+  uint32_t* counts;    // [chunks][2]
+};
+
+// Inclusive prefix sum of v over a workgroup of W waves in thread order;
+// `total` receives the workgroup sum.  wsum: W LDS words.
+template <int W = kSelW>
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wsum, uint32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t x = v;
@@ -161,7 +175,7 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wsum, uint3
   __syncthreads();
   uint32_t before = 0, t = 0;
 #pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) {
+  for (int w = 0; w < W; ++w) {
     const uint32_t sw = wsum[w];
     before += (w < wave) ? sw : 0u;
     t += sw;
@@ -171,8 +185,8 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wsum, uint3
   return before + x;
 }
 
-// Largest of v over the workgroup (every thread gets it).  wsum: kSelWaves
-// LDS words.
+// Largest of v over a workgroup of W waves (every thread gets it).
+template <int W = kSelW>
 __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -181,59 +195,58 @@ __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* wsum) {
   __syncthreads();
   uint32_t m = 0u;
 #pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) m = max(m, wsum[w]);
+  for (int w = 0; w < W; ++w) m = max(m, wsum[w]);
   __syncthreads();   // wsum may be reused
   return m;
 }
 
-// Largest operand row norms of expert e's kept pairs (float16 weight-gradient
-// mode): the workgroup's accumulators reduced and stored (whole expert) or
-// merged with atomicMax (one chunk of a large expert; non-negative float32
-// bit patterns order like their values).
-__device__ __forceinline__ void put_kept_bound(const uint32_t (&kbound)[2], uint32_t* wsum,
-                                             float* ebound, int e, bool merge) {
-  const uint32_t a = block_max(kbound[0], wsum);
-  const uint32_t b = block_max(kbound[1], wsum);
-  if (threadIdx.x == 0) {
-    if (merge) {
-      atomicMax(reinterpret_cast<uint32_t*>(ebound) + 2 * e, a);
-      atomicMax(reinterpret_cast<uint32_t*>(ebound) + 2 * e + 1, b);
-    } else {
-      ebound[2 * e] = __uint_as_float(a);
-      ebound[2 * e + 1] = __uint_as_float(b);
-    }
-  }
-}
-
 struct Digit {
-  uint32_t digit;   // bin holding the k-th largest key among the counted ones
+  uint32_t digit;   // bin holding the k-th largest counted key
   uint32_t k;       // its rank inside that bin (1-based, from the top)
-  uint32_t count;   // keys in that bin
 };
 
-// Given a histogram of `nbins` (<= 4 per thread) bins in LDS, find the bin
-// that holds the k-th largest counted key.  Thread t owns the 4 bins just
-// below bin nbins - 4t, so the thread-order scan counts from the top bin.
-__device__ __forceinline__ Digit find_digit(const uint32_t* hist, int nbins, uint32_t k,
+// Bin of the k-th largest key of a global histogram of NB bins (1 <= k <=
+// the histogram's total).  Thread t owns the NB / kSelT bins just below bin
+// NB - (NB / kSelT) t, so the thread-order scan counts from the top bin.
+template <int NB>
+__device__ __forceinline__ Digit find_digit(const uint32_t* __restrict__ hist, uint32_t k,
                                             uint32_t* wsum, Digit* out) {
+  constexpr int PER = NB / kSelT;
   const int tid = threadIdx.x;
-  const int top = nbins - 4 * tid;   // this thread's bins: top-1 .. top-4
-  uint32_t c[4] = {0u, 0u, 0u, 0u};
-  if (top > 0) {
+  const int top = NB - PER * tid;   // this thread's bins: top-1 .. top-PER
+  uint32_t c[PER];
+  if constexpr (PER % 4 == 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) c[j] = hist[top - 1 - j];
+    for (int q = 0; q < PER / 4; ++q) {
+      const u32x4 v = reinterpret_cast<const u32x4*>(hist + top - PER)[q];
+      // bins top-PER+4q .. +3 -> c[PER-1-4q] .. c[PER-4-4q]
+      c[PER - 1 - 4 * q] = v[0];
+      c[PER - 2 - 4 * q] = v[1];
+      c[PER - 3 - 4 * q] = v[2];
+      c[PER - 4 - 4 * q] = v[3];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) c[j] = hist[top - 1 - j];
   }
-  const uint32_t local = c[0] + c[1] + c[2] + c[3];
+  uint32_t local = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) local += c[j];
+  if (tid == 0) *out = Digit{0u, 1u};   // stays only if the counts are inconsistent
   uint32_t total;
-  const uint32_t incl = block_scan(local, wsum, total);
+  const uint32_t incl = block_scan(local, wsum, total);   // its barriers order the write above
   const uint32_t above = incl - local;
   if (local > 0 && above < k && k <= incl) {
     uint32_t cum = above;
-    int j = 0;
-    while (cum + c[j] < k) cum += c[j++];   // terminates: cum + sum(c) >= k
-    out->digit = (uint32_t)(top - 1 - j);
-    out->k = k - cum;
-    out->count = c[j];
+    bool found = false;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (!found && cum + c[j] >= k) {
+        found = true;
+        *out = Digit{(uint32_t)(top - 1 - j), k - cum};
+      }
+      if (!found) cum += c[j];
+    }
   }
   __syncthreads();
   const Digit d = *out;
@@ -241,30 +254,139 @@ __device__ __forceinline__ Digit find_digit(const uint32_t* hist, int nbins, uin
   return d;
 }
 
-// First-digit (key bits 31..20) histogram of one kHistChunk-pair chunk of a
-// large expert, written to hist[chunk][kBins].
-__global__ __launch_bounds__(kSelThreads) void select_hist_kernel(
-    ExpertTable tab, const float* __restrict__ scores, uint32_t* __restrict__ hist_out) {
-  __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
-  const int b = blockIdx.x, tid = threadIdx.x;
+// Chunk b -> its expert e and pair range [lo, hi).
+struct Chunk {
+  int e, lo, hi;
+};
+__device__ __forceinline__ Chunk chunk_of(const ExpertTable& tab, int b) {
   int e = 0;
-  while (e + 1 < tab.E && tab.hist_off[e + 1] <= b) ++e;   // chunk b belongs to expert e
-  const int lo = tab.pair_off[e] + (b - tab.hist_off[e]) * kHistChunk;
-  const int hi = min(lo + kHistChunk, tab.pair_off[e + 1]);
-  for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0;
-  __syncthreads();
-  float v[kHistPer];
+  while (e + 1 < tab.E && tab.chunk_off[e + 1] <= b) ++e;
+  const int lo = tab.pair_off[e] + (b - tab.chunk_off[e]) * kSelChunk;
+  return Chunk{e, lo, min(lo + kSelChunk, tab.pair_off[e + 1])};
+}
+
+// The chunk's keys, kKeysPer per thread, thread-strided (key j of thread t is
+// pair lo + j kSelT + t); pairs past hi read as 0 and are not valid.
+__device__ __forceinline__ void load_keys(const float* __restrict__ scores, const Chunk& ch,
+                                          uint32_t (&key)[kKeysPer]) {
+  float v[kKeysPer];
 #pragma unroll
-  for (int j = 0; j < kHistPer; ++j) {
-    const int i = lo + j * kSelThreads + tid;
-    v[j] = i < hi ? scores[i] : 0.f;
+  for (int j = 0; j < kKeysPer; ++j) {
+    const int i = ch.lo + j * kSelT + (int)threadIdx.x;
+    v[j] = i < ch.hi ? scores[i] : 0.f;
   }
 #pragma unroll
-  for (int j = 0; j < kHistPer; ++j)
-    if (lo + j * kSelThreads + tid < hi) atomicAdd(&hist[score_key(v[j]) >> 20], 1u);
+  for (int j = 0; j < kKeysPer; ++j) key[j] = score_key(v[j]);
+}
+__device__ __forceinline__ bool key_valid(const Chunk& ch, int j) {
+  return ch.lo + j * kSelT + (int)threadIdx.x < ch.hi;
+}
+
+// Clears the digit histograms, writes seg_offsets and zeroes the expert
+// bounds that the scans merge into.
+__global__ __launch_bounds__(256) void select_init_kernel(ExpertTable tab, SelWs w,
+                                                          int32_t* __restrict__ seg_offsets_out,
+                                                          float* __restrict__ ebound) {
+  const int n = tab.E * (2 * kB12 + kB8);   // h1, h2, h3 are contiguous
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) w.h1[i] = 0u;
+  if (blockIdx.x == 0) {
+    for (int e = threadIdx.x; e <= tab.E; e += 256) seg_offsets_out[e] = tab.seg_off[e];
+    if (ebound != nullptr)
+      for (int i = threadIdx.x; i < 2 * tab.E; i += 256) ebound[i] = 0.f;
+  }
+}
+
+// Radix pass PASS (1, 2, 3) over one chunk: the histogram of digit PASS
+// (key bits 31..20, 19..8, 7..0) of the chunk's keys that carry the prefix
+// found so far, counted in LDS and added into the expert's global histogram.
+// Passes 2 and 3 first find the previous digit from the previous pass's
+// global histogram (every chunk of the expert does, and gets the same; the
+// expert's first chunk records it).  Experts that keep nothing are skipped.
+template <int PASS>
+__global__ __launch_bounds__(kSelT) void select_digit_kernel(ExpertTable tab,
+                                                             const float* __restrict__ scores,
+                                                             SelWs w) {
+  constexpr int NB = PASS == 3 ? kB8 : kB12;
+  constexpr int SHIFT = PASS == 1 ? 20 : PASS == 2 ? 8 : 0;
+  constexpr uint32_t PMASK = PASS == 1 ? 0u : PASS == 2 ? 0xFFF00000u : 0xFFFFFF00u;
+  __shared__ __attribute__((aligned(16))) uint32_t hist[NB];
+  __shared__ uint32_t wsum[kSelW];
+  __shared__ Digit dig;
+  const Chunk ch = chunk_of(tab, blockIdx.x);
+  const int e = ch.e;
+  const uint32_t q = (uint32_t)(tab.seg_off[e + 1] - tab.seg_off[e]);
+  if (q == 0) return;   // workgroup-uniform
+  uint32_t key[kKeysPer];
+  load_keys(scores, ch, key);   // in flight while the previous digit is found
+  const bool first = (int)blockIdx.x == tab.chunk_off[e];
+  uint32_t prefix = 0u;
+  if (PASS == 2) {
+    const Digit d1 = find_digit<kB12>(w.h1 + (size_t)e * kB12, q, wsum, &dig);
+    prefix = d1.digit << 20;
+    if (first && threadIdx.x == 0) {
+      w.st[8 * e + 0] = prefix;
+      w.st[8 * e + 1] = d1.k;
+    }
+  } else if (PASS == 3) {
+    const Digit d2 = find_digit<kB12>(w.h2 + (size_t)e * kB12, w.st[8 * e + 1], wsum, &dig);
+    prefix = w.st[8 * e + 0] | (d2.digit << 8);
+    if (first && threadIdx.x == 0) {
+      w.st[8 * e + 2] = prefix;
+      w.st[8 * e + 3] = d2.k;
+    }
+  }
+  for (int i = threadIdx.x; i < NB; i += kSelT) hist[i] = 0u;
   __syncthreads();
-  reinterpret_cast<u32x4*>(hist_out + (size_t)b * kBins)[tid] =
-      reinterpret_cast<const u32x4*>(hist)[tid];
+#pragma unroll
+  for (int j = 0; j < kKeysPer; ++j)
+    if (key_valid(ch, j) && (key[j] & PMASK) == prefix)
+      atomicAdd(&hist[(key[j] >> SHIFT) & (uint32_t)(NB - 1)], 1u);
+  __syncthreads();
+  uint32_t* gh = (PASS == 1 ? w.h1 : PASS == 2 ? w.h2 : w.h3) + (size_t)e * NB;
+  for (int i = threadIdx.x; i < NB; i += kSelT) {
+    const uint32_t c = hist[i];
+    if (c != 0u) atomicAdd(gh + i, c);
+  }
+}
+
+// Last digit -> tau (the q-th largest key) and need (how many keys equal to
+// tau are kept: the first `need` of them in pair order); then the chunk's
+// counts of keys above and equal to tau.
+__global__ __launch_bounds__(kSelT) void select_count_kernel(ExpertTable tab,
+                                                             const float* __restrict__ scores,
+                                                             SelWs w) {
+  __shared__ uint32_t wsum[kSelW];
+  __shared__ Digit dig;
+  const int b = blockIdx.x;
+  const Chunk ch = chunk_of(tab, b);
+  const int e = ch.e;
+  const uint32_t q = (uint32_t)(tab.seg_off[e + 1] - tab.seg_off[e]);
+  const bool first = b == tab.chunk_off[e];
+  uint32_t key[kKeysPer];
+  load_keys(scores, ch, key);
+  uint32_t tau = 0xFFFFFFFFu, need = 0u;   // q == 0: no key is above or equal
+  if (q > 0) {
+    const Digit d3 = find_digit<kB8>(w.h3 + (size_t)e * kB8, w.st[8 * e + 3], wsum, &dig);
+    tau = w.st[8 * e + 2] | d3.digit;
+    need = d3.k;
+  }
+  if (first && threadIdx.x == 0) {
+    w.st[8 * e + 4] = tau;
+    w.st[8 * e + 5] = need;
+  }
+  uint32_t ngt = 0, neq = 0;
+#pragma unroll
+  for (int j = 0; j < kKeysPer; ++j) {
+    const bool ok = key_valid(ch, j);
+    ngt += ok && key[j] > tau ? 1u : 0u;
+    neq += ok && key[j] == tau ? 1u : 0u;
+  }
+  uint32_t tot;
+  block_scan((ngt << 16) | neq, wsum, tot);   // a chunk has < 2^16 keys
+  if (threadIdx.x == 0) {
+    w.counts[2 * b] = tot >> 16;
+    w.counts[2 * b + 1] = tot & 0xFFFFu;
+  }
 }
 
 // Scores [a, a + 4) for a multiple of 4 (the score array is 16-byte
@@ -278,90 +400,247 @@ __device__ __forceinline__ float4 load4(const float* __restrict__ scores, int a,
   return v;
 }
 
-// ---- stable scan in pair order over pairs [base, end) of one expert: keep =
-// key > tau, or key == tau among the first `need` of the expert's equal keys;
-// kept pairs get consecutive compacted rows from seg.  run_gt / run_eq: the
-// expert's keys above / equal to tau before `base`.  Keys come from keys_lds
-// (pair g at keys_lds[g - lds_base]) or, when keys_lds is null, from the
-// global scores.  Tiles start at the aligned index base & ~3; thread t owns 8
-// consecutive pairs of a tile (those outside [base, end) are skipped); one
-// workgroup scan of (#gt, #eq) per tile gives every position.  The next
-// tile's loads go out before this tile is scanned.
-//
-// rnorm (or null): per-pair operand row norms of the float16 weight-gradient
-// mode; the thread's largest over its kept pairs accumulate into kbound
-// (float32 bits).
-__device__ __forceinline__ void scan_keep(const uint32_t* keys_lds, const float* __restrict__ scores,
-                                          int P, int base, int end, int lds_base, uint32_t tau,
-                                          uint32_t need, uint32_t run_gt, uint32_t run_eq,
-                                          uint32_t q, int seg, uint8_t* __restrict__ keep,
-                                          int32_t* __restrict__ perm, uint32_t* wsum,
-                                          const float2* __restrict__ rnorm, uint32_t (&kbound)[2]) {
-  const int tid = threadIdx.x;
-  const int gbeg = base & ~3;
-  const bool cached = keys_lds != nullptr;
-  auto load_tile = [&](int c, uint32_t (&kk)[kScanPer]) {
-    const int g0 = c + tid * kScanPer;
-    if (cached) {
+// Stable scan of one chunk in pair order: keep = key > tau, or key == tau
+// among the first `need` of the expert's equal keys; kept pairs get
+// consecutive compacted rows from seg (ascending pair index in the segment).
+// The counts of the expert's earlier chunks give the chunk's start.  Thread t
+// owns 16 consecutive pairs of a tile that starts at an aligned index (so
+// that keep flags go out as whole 4-byte words), and one workgroup scan per
+// tile places them; a chunk that starts unaligned takes a second, short
+// tile.  In the float16 mode the largest row norms of the kept pairs are
+// merged into the expert's bounds.
+__global__ __launch_bounds__(kSelT) void select_scan_kernel(
+    ExpertTable tab, const float* __restrict__ scores, uint8_t* __restrict__ keep,
+    int32_t* __restrict__ perm, SelWs w, const float2* __restrict__ rnorm,
+    float* __restrict__ ebound) {
+  __shared__ uint32_t wsum[kSelW];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const Chunk ch = chunk_of(tab, b);
+  const int e = ch.e;
+  const int P = tab.pair_off[tab.E];
+  const int seg = tab.seg_off[e];
+  const uint32_t q = (uint32_t)(tab.seg_off[e + 1] - seg);
+  const uint32_t tau = w.st[8 * e + 4], need = w.st[8 * e + 5];
+  // keys above / equal to tau in the expert's earlier chunks
+  uint32_t pgt = 0, peq = 0;
+  for (int c = tab.chunk_off[e] + tid; c < b; c += kSelT) {
+    pgt += w.counts[2 * c];
+    peq += w.counts[2 * c + 1];
+  }
+  uint32_t run_gt, run_eq;
+  block_scan(pgt, wsum, run_gt);
+  block_scan(peq, wsum, run_eq);
+  uint32_t kbound[2] = {0u, 0u};
+  for (int c = ch.lo & ~3; c < ch.hi; c += kSelChunk) {
+    const int g0 = c + tid * kKeysPer;
+    const bool full = c + kSelChunk <= P;   // workgroup-uniform: plain vector loads
+    uint32_t key[kKeysPer];
 #pragma unroll
-      for (int j = 0; j < kScanPer; ++j) {
+    for (int h = 0; h < kKeysPer / 4; ++h) {
+      const float4 v = full ? *reinterpret_cast<const float4*>(scores + g0 + 4 * h)
+                            : load4(scores, g0 + 4 * h, P);
+      key[4 * h] = score_key(v.x);
+      key[4 * h + 1] = score_key(v.y);
+      key[4 * h + 2] = score_key(v.z);
+      key[4 * h + 3] = score_key(v.w);
+    }
+    float2 rn[kKeysPer];
+    if (rnorm != nullptr) {
+#pragma unroll
+      for (int j = 0; j < kKeysPer; ++j) {
         const int g = g0 + j;
-        kk[j] = (g >= base && g < end) ? keys_lds[g - lds_base] : 0u;
+        rn[j] = (g >= ch.lo && g < ch.hi) ? rnorm[g] : make_float2(0.f, 0.f);
       }
-    } else {
-      // a tile wholly inside the score array: plain vector loads (load4's
-      // per-lane bounds branch would wait for each load in turn)
-      const bool full = c + kScanTile <= P;   // workgroup-uniform
-#pragma unroll
-      for (int h = 0; h < kScanPer / 4; ++h) {
-        const float4 v = full ? *reinterpret_cast<const float4*>(scores + g0 + 4 * h)
-                              : load4(scores, g0 + 4 * h, P);
-        kk[4 * h] = score_key(v.x);
-        kk[4 * h + 1] = score_key(v.y);
-        kk[4 * h + 2] = score_key(v.z);
-        kk[4 * h + 3] = score_key(v.w);
-      }
-    }
-  };
-  // operand row norms of the tile's pairs, loaded with its keys (loaded
-  // only for kept pairs, each was a dependent load inside the scan)
-  auto load_rn = [&](int c, float2 (&r)[kScanPer]) {
-    if (rnorm == nullptr) return;
-    const int g0 = c + tid * kScanPer;
-#pragma unroll
-    for (int j = 0; j < kScanPer; ++j) {
-      const int g = g0 + j;
-      r[j] = (g >= base && g < end) ? rnorm[g] : make_float2(0.f, 0.f);
-    }
-  };
-  uint32_t key[kScanPer], key_next[kScanPer];
-  float2 rn[kScanPer], rn_next[kScanPer];
-  load_tile(gbeg, key);
-  load_rn(gbeg, rn);
-  for (int c = gbeg; c < end; c += kScanTile) {
-    const int g0 = c + tid * kScanPer;
-    if (c + kScanTile < end) {
-      load_tile(c + kScanTile, key_next);
-      load_rn(c + kScanTile, rn_next);
     }
     uint32_t ngt = 0, neq = 0;
 #pragma unroll
-    for (int j = 0; j < kScanPer; ++j) {
-      const bool ok = g0 + j >= base && g0 + j < end;
+    for (int j = 0; j < kKeysPer; ++j) {
+      const bool ok = g0 + j >= ch.lo && g0 + j < ch.hi;
       ngt += (ok && key[j] > tau) ? 1u : 0u;
       neq += (ok && key[j] == tau) ? 1u : 0u;
     }
     uint32_t tot;
     const uint32_t incl = block_scan((ngt << 16) | neq, wsum, tot);   // per tile < 2^16 each
     const uint32_t excl = incl - ((ngt << 16) | neq);
-    uint32_t gt_before = run_gt + (excl >> 16);
     uint32_t eq_before = run_eq + (excl & 0xFFFFu);
     // kept keys before this thread: every greater key, and the equal keys
     // among the first `need` equal ones
-    uint32_t pos = gt_before + (eq_before < need ? eq_before : need);
+    uint32_t pos = run_gt + (excl >> 16) + (eq_before < need ? eq_before : need);
     uint32_t kept_bits = 0, valid_bits = 0;
 #pragma unroll
-    for (int j = 0; j < kScanPer; ++j) {
+    for (int j = 0; j < kKeysPer; ++j) {
+      const int g = g0 + j;
+      if (g >= ch.lo && g < ch.hi) {
+        const bool gt = key[j] > tau, eq = key[j] == tau;
+        const bool kp = gt || (eq && eq_before < need);
+        eq_before += eq ? 1u : 0u;
+        valid_bits |= 1u << j;
+        kept_bits |= (kp ? 1u : 0u) << j;
+        if (kp) {
+          if (pos < q) perm[seg + pos] = g;   // pos < q holds by construction
+          ++pos;
+          if (rnorm != nullptr) {
+            kbound[0] = max(kbound[0], __float_as_uint(rn[j].x));
+            kbound[1] = max(kbound[1], __float_as_uint(rn[j].y));
+          }
+        }
+      }
+    }
+    // keep flags: whole 4-byte groups at once when the chunk owns all four
+#pragma unroll
+    for (int h = 0; h < kKeysPer / 4; ++h) {
+      const uint32_t vb = (valid_bits >> (4 * h)) & 15u, kb = (kept_bits >> (4 * h)) & 15u;
+      const int g = g0 + 4 * h;
+      if (vb == 15u) {
+        *reinterpret_cast<uint32_t*>(keep + g) =
+            (kb & 1u) | ((kb & 2u) << 7) | ((kb & 4u) << 14) | ((kb & 8u) << 21);
+      } else if (vb != 0u) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          if (vb & (1u << t)) keep[g + t] = (kb >> t) & 1u;
+      }
+    }
+    run_gt += tot >> 16;
+    run_eq += tot & 0xFFFFu;
+  }
+  if (ebound != nullptr) {   // non-negative float32 bit patterns order like their values
+    const uint32_t a = block_max(kbound[0], wsum);
+    const uint32_t m = block_max(kbound[1], wsum);
+    if (tid == 0) {
+      atomicMax(reinterpret_cast<uint32_t*>(ebound) + 2 * e, a);
+      atomicMax(reinterpret_cast<uint32_t*>(ebound) + 2 * e + 1, m);
+    }
+  }
+}
+
+// ---- Problems whose experts all have at most kSelLdsKeys pairs: one
+// 1024-thread workgroup per expert does the whole selection with the keys in
+// LDS, in one launch (the chunked passes above cost about 45 us in six
+// launches whatever the size; this takes about 23 us on 32 K-pair problems).
+constexpr int kLdsT = 1024;
+constexpr int kLdsW = kLdsT / 64;
+constexpr int kLdsPer = 8;                 // keys per thread per scan tile
+constexpr int kLdsTile = kLdsT * kLdsPer;
+
+// Bin of the k-th largest key of an LDS histogram of nbins <= 4 kLdsT bins:
+// thread t owns the 4 bins just below bin nbins - 4 t.
+__device__ __forceinline__ Digit find_digit_lds(const uint32_t* hist, int nbins, uint32_t k,
+                                                uint32_t* wsum, Digit* out) {
+  const int tid = threadIdx.x;
+  const int top = nbins - 4 * tid;
+  uint32_t c[4] = {0u, 0u, 0u, 0u};
+  if (top > 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c[j] = hist[top - 1 - j];
+  }
+  const uint32_t local = c[0] + c[1] + c[2] + c[3];
+  if (tid == 0) *out = Digit{0u, 1u};   // stays only if the counts are inconsistent
+  uint32_t total;
+  const uint32_t incl = block_scan<kLdsW>(local, wsum, total);
+  const uint32_t above = incl - local;
+  if (local > 0 && above < k && k <= incl) {
+    uint32_t cum = above;
+    bool found = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (!found && cum + c[j] >= k) {
+        found = true;
+        *out = Digit{(uint32_t)(top - 1 - j), k - cum};
+      }
+      if (!found) cum += c[j];
+    }
+  }
+  __syncthreads();
+  const Digit d = *out;
+  __syncthreads();
+  return d;
+}
+
+__global__ __launch_bounds__(kLdsT) void select_lds_kernel(
+    ExpertTable tab, const float* __restrict__ scores, uint8_t* __restrict__ keep,
+    int32_t* __restrict__ perm, int32_t* __restrict__ seg_offsets_out,
+    const float2* __restrict__ rnorm, float* __restrict__ ebound) {
+  __shared__ uint32_t keys_lds[kSelLdsKeys];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kB12];
+  __shared__ uint32_t wsum[kLdsW];
+  __shared__ Digit dig;
+  const int e = blockIdx.x, tid = threadIdx.x;
+  const int P = tab.pair_off[tab.E];
+  const int base = tab.pair_off[e], end = tab.pair_off[e + 1];
+  const int n = end - base;
+  const int gbeg = base & ~3;   // 16-byte aligned start for vector reads
+  const int seg = tab.seg_off[e];
+  const uint32_t q = (uint32_t)(tab.seg_off[e + 1] - seg);
+  if (tid == 0) {
+    seg_offsets_out[e] = seg;
+    if (e == tab.E - 1) seg_offsets_out[tab.E] = tab.seg_off[tab.E];
+    if (ebound != nullptr && n == 0) {   // an empty expert keeps nothing
+      ebound[2 * e] = 0.f;
+      ebound[2 * e + 1] = 0.f;
+    }
+  }
+  if (n == 0) return;
+  for (int a = gbeg + 4 * tid; a < end; a += 4 * kLdsT) {
+    const float4 v = load4(scores, a, P);
+    const float x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (a + j >= base && a + j < end) keys_lds[a + j - base] = score_key(x[j]);
+  }
+  __syncthreads();
+  // radix select, most significant digit first: 12 + 12 + 8 bits
+  uint32_t tau = 0xFFFFFFFFu, need = 0u;   // q == 0: no key is above or equal
+  if (q > 0) {
+    uint32_t prefix = 0u, k = q;
+#pragma unroll 1
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = pass == 0 ? 20 : pass == 1 ? 8 : 0;
+      const int nb = pass == 2 ? kB8 : kB12;
+      const uint32_t pmask = pass == 0 ? 0u : pass == 1 ? 0xFFF00000u : 0xFFFFFF00u;
+      for (int i = tid; i < nb; i += kLdsT) hist[i] = 0u;
+      __syncthreads();
+      for (int i = tid; i < n; i += kLdsT) {
+        const uint32_t key = keys_lds[i];
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
+      }
+      __syncthreads();
+      const Digit d = find_digit_lds(hist, nb, k, wsum, &dig);
+      prefix |= d.digit << shift;
+      k = d.k;
+    }
+    tau = prefix;
+    need = k;
+  }
+  // stable scan in pair order, 8 consecutive keys per thread, one workgroup
+  // scan per 8192 keys
+  uint32_t run_gt = 0, run_eq = 0;
+  uint32_t kbound[2] = {0u, 0u};
+  for (int c = gbeg; c < end; c += kLdsTile) {
+    const int g0 = c + tid * kLdsPer;
+    uint32_t key[kLdsPer];
+    float2 rn[kLdsPer];
+#pragma unroll
+    for (int j = 0; j < kLdsPer; ++j) {
+      const int g = g0 + j;
+      const bool ok = g >= base && g < end;
+      key[j] = ok ? keys_lds[g - base] : 0u;
+      if (rnorm != nullptr) rn[j] = ok ? rnorm[g] : make_float2(0.f, 0.f);
+    }
+    uint32_t ngt = 0, neq = 0;
+#pragma unroll
+    for (int j = 0; j < kLdsPer; ++j) {
+      const bool ok = g0 + j >= base && g0 + j < end;
+      ngt += (ok && key[j] > tau) ? 1u : 0u;
+      neq += (ok && key[j] == tau) ? 1u : 0u;
+    }
+    uint32_t tot;
+    const uint32_t incl = block_scan<kLdsW>((ngt << 16) | neq, wsum, tot);   // < 2^16 each
+    const uint32_t excl = incl - ((ngt << 16) | neq);
+    uint32_t eq_before = run_eq + (excl & 0xFFFFu);
+    uint32_t pos = run_gt + (excl >> 16) + (eq_before < need ? eq_before : need);
+    uint32_t kept_bits = 0, valid_bits = 0;
+#pragma unroll
+    for (int j = 0; j < kLdsPer; ++j) {
       const int g = g0 + j;
       if (g >= base && g < end) {
         const bool gt = key[j] > tau, eq = key[j] == tau;
@@ -379,9 +658,8 @@ __device__ __forceinline__ void scan_keep(const uint32_t* keys_lds, const float*
         }
       }
     }
-    // keep flags: whole 4-byte groups at once when the range owns all four
 #pragma unroll
-    for (int h = 0; h < kScanPer / 4; ++h) {
+    for (int h = 0; h < kLdsPer / 4; ++h) {
       const uint32_t vb = (valid_bits >> (4 * h)) & 15u, kb = (kept_bits >> (4 * h)) & 15u;
       const int g = g0 + 4 * h;
       if (vb == 15u) {
@@ -395,235 +673,15 @@ __device__ __forceinline__ void scan_keep(const uint32_t* keys_lds, const float*
     }
     run_gt += tot >> 16;
     run_eq += tot & 0xFFFFu;
-#pragma unroll
-    for (int j = 0; j < kScanPer; ++j) {
-      key[j] = key_next[j];
-      rn[j] = rn_next[j];
-    }
   }
-}
-
-__global__ __launch_bounds__(kSelThreads) void select_scan_kernel(
-    ExpertTable tab, const float* __restrict__ scores, uint8_t* __restrict__ keep,
-    int32_t* __restrict__ perm, int32_t* __restrict__ seg_offsets_out,
-    const uint32_t* __restrict__ hist_in, uint32_t* __restrict__ tau_need,
-    const float2* __restrict__ rnorm, float* __restrict__ ebound) {
-  __shared__ uint32_t keys_lds[kSelLdsKeys];   // the expert's keys, or the candidates
-  __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
-  __shared__ uint32_t wsum[kSelWaves];
-  __shared__ uint32_t cand_n;
-  __shared__ Digit dig;
-
-  const int e = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int P = tab.pair_off[tab.E];
-  const int base = tab.pair_off[e];
-  const int end = tab.pair_off[e + 1];
-  const int n = end - base;
-  const int gbeg = base & ~3;   // 16-byte aligned start for vector reads of global scores
-  const int seg = tab.seg_off[e];
-  const uint32_t q = (uint32_t)(tab.seg_off[e + 1] - seg);
-
-  const bool cached = n <= kSelLdsKeys;
-  if (tid == 0) {
-    seg_offsets_out[e] = seg;
-    if (e == tab.E - 1) seg_offsets_out[tab.E] = tab.seg_off[tab.E];
-    // largest kept row norms: an empty expert keeps 0; a large one starts at 0 and
-    // its chunk scans merge into it
-    if (ebound != nullptr && (n == 0 || !cached)) {
-      ebound[2 * e] = 0.f;
-      ebound[2 * e + 1] = 0.f;
-    }
-  }
-  if (n == 0) return;
-  if (cached) {
-    for (int a = gbeg + 4 * tid; a < end; a += 4 * kSelThreads) {
-      const float4 v = load4(scores, a, P);
-      const float x[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (a + j >= base && a + j < end) keys_lds[a + j - base] = score_key(x[j]);
-    }
-    __syncthreads();
-  }
-
-  // ---- radix select, most significant digit first: 12 + 12 + 8 bits.
-  // tau = the q-th largest key; need = how many keys equal to tau are kept.
-  uint32_t tau = 0xFFFFFFFFu, need = 0;   // q == 0: no key is above or equal
-  if (q > 0) {
-    // digit 1 (key bits 31..20) over every key: counted here from the LDS
-    // cache, or summed from the chunk histograms of select_hist_kernel
-    if (cached) {
-      for (int i = tid; i < kBins; i += kSelThreads) hist[i] = 0;
-      __syncthreads();
-      for (int i = tid; i < n; i += kSelThreads) atomicAdd(&hist[keys_lds[i] >> 20], 1u);
-    } else {
-      // eight chunk histograms in flight per thread (one at a time, the
-      // latency of each load was paid in full)
-      u32x4 h = {0u, 0u, 0u, 0u};
-      const int c1 = tab.hist_off[e + 1];
-      for (int c = tab.hist_off[e]; c < c1; c += 8) {
-        u32x4 t[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          t[j] = c + j < c1 ? reinterpret_cast<const u32x4*>(hist_in + (size_t)(c + j) * kBins)[tid]
-                            : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) h += t[j];
-      }
-      reinterpret_cast<u32x4*>(hist)[tid] = h;   // kSelThreads * 4 == kBins
-    }
-    __syncthreads();
-    Digit d1 = find_digit(hist, kBins, q, wsum, &dig);
-    uint32_t prefix = d1.digit << 20;
-    uint32_t k = d1.k;
-
-    // Remaining digits look only at keys whose top bits equal `prefix`: the
-    // cached keys, or (large experts) the first-digit candidates collected
-    // into LDS, or -- if there are too many of those -- all keys again.
-    int nlist = n;
-    bool from_global = false;
-    if (!cached) {
-      if (d1.count <= (uint32_t)kSelLdsKeys) {
-        if (tid == 0) cand_n = 0;
-        __syncthreads();
-        // one workgroup streams the expert, kCandLoads 16-byte loads in
-        // flight per thread; steps wholly inside the score array use plain
-        // vector loads (no per-lane bounds branch).  This phase is bound by
-        // what one CU can stream (about 35 GB/s measured: 9 us per 256 KiB
-        // step) and by the LDS atomics of the appends; on a 286k-pair expert
-        // it is still the selection's longest (about 45 us).
-        for (int a0 = gbeg; a0 < end; a0 += 4 * kCandLoads * kSelThreads) {
-          float4 v[kCandLoads];
-          if (a0 + 4 * kCandLoads * kSelThreads <= P) {   // workgroup-uniform
-#pragma unroll
-            for (int j = 0; j < kCandLoads; ++j)
-              v[j] = *reinterpret_cast<const float4*>(scores + a0 + 4 * (j * kSelThreads + tid));
-          } else {
-#pragma unroll
-            for (int j = 0; j < kCandLoads; ++j)
-              v[j] = load4(scores, a0 + 4 * (j * kSelThreads + tid), P);
-          }
-#pragma unroll
-          for (int j = 0; j < kCandLoads; ++j) {
-            const int a = a0 + 4 * (j * kSelThreads + tid);
-            const float x[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const uint32_t key = score_key(x[t]);
-              if (a + t >= base && a + t < end && (key >> 20) == d1.digit)
-                keys_lds[atomicAdd(&cand_n, 1u)] = key;
-            }
-          }
-        }
-        __syncthreads();
-        nlist = (int)d1.count;   // == cand_n
-      } else {
-        from_global = true;
-      }
-    }
-    auto list_key = [&](int i) -> uint32_t {
-      return from_global ? score_key(scores[base + i]) : keys_lds[i];
-    };
-    // digit 2 (bits 19..8), then digit 3 (bits 7..0)
-#pragma unroll 1
-    for (int pass = 0; pass < 2; ++pass) {
-      const int shift = pass == 0 ? 8 : 0;
-      const int nb = pass == 0 ? kBins : 256;
-      const uint32_t pmask = pass == 0 ? 0xFFF00000u : 0xFFFFFF00u;
-      for (int i = tid; i < nb; i += kSelThreads) hist[i] = 0;
-      __syncthreads();
-      for (int i = tid; i < nlist; i += kSelThreads) {
-        const uint32_t key = list_key(i);
-        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
-      }
-      __syncthreads();
-      const Digit dd = find_digit(hist, nb, k, wsum, &dig);
-      prefix |= dd.digit << shift;
-      k = dd.k;
-    }
-    tau = prefix;
-    need = k;
-  }
-
-  if (!cached) {   // the chunk kernels scan large experts, many workgroups at once
+  if (ebound != nullptr) {
+    const uint32_t a = block_max<kLdsW>(kbound[0], wsum);
+    const uint32_t m = block_max<kLdsW>(kbound[1], wsum);
     if (tid == 0) {
-      tau_need[2 * e] = tau;
-      tau_need[2 * e + 1] = need;
+      ebound[2 * e] = __uint_as_float(a);
+      ebound[2 * e + 1] = __uint_as_float(m);
     }
-    return;
   }
-  uint32_t kbound[2] = {0u, 0u};
-  scan_keep(keys_lds, scores, P, base, end, base, tau, need, 0u, 0u, q, seg, keep, perm, wsum,
-            ebound != nullptr ? rnorm : nullptr, kbound);
-  if (ebound != nullptr) put_kept_bound(kbound, wsum, ebound, e, false);
-}
-
-// Large experts (more than kSelLdsKeys pairs), after select_scan_kernel has
-// found their tau and need: chunk b (the kHistChunk pairs of select_hist_kernel's
-// chunk b) counts its keys above and equal to tau ...
-__global__ __launch_bounds__(kSelThreads) void select_chunk_count_kernel(
-    ExpertTable tab, const float* __restrict__ scores, const uint32_t* __restrict__ tau_need,
-    uint32_t* __restrict__ counts) {
-  __shared__ uint32_t wsum[kSelWaves];
-  const int b = blockIdx.x, tid = threadIdx.x;
-  int e = 0;
-  while (e + 1 < tab.E && tab.hist_off[e + 1] <= b) ++e;
-  const int lo = tab.pair_off[e] + (b - tab.hist_off[e]) * kHistChunk;
-  const int hi = min(lo + kHistChunk, tab.pair_off[e + 1]);
-  const uint32_t tau = tau_need[2 * e];
-  uint32_t ngt = 0, neq = 0;
-  float v[kHistPer];   // every load of the chunk in flight at once
-#pragma unroll
-  for (int j = 0; j < kHistPer; ++j) {
-    const int i = lo + j * kSelThreads + tid;
-    v[j] = i < hi ? scores[i] : 0.f;
-  }
-#pragma unroll
-  for (int j = 0; j < kHistPer; ++j) {
-    const uint32_t k = score_key(v[j]);
-    const bool ok = lo + j * kSelThreads + tid < hi;
-    ngt += ok && k > tau ? 1u : 0u;
-    neq += ok && k == tau ? 1u : 0u;
-  }
-  uint32_t tot;
-  block_scan((ngt << 16) | neq, wsum, tot);   // chunk < 2^16 pairs
-  if (tid == 0) {
-    counts[2 * b] = tot >> 16;
-    counts[2 * b + 1] = tot & 0xFFFFu;
-  }
-}
-
-// ... and then scans its pairs, starting from the counts of the expert's
-// earlier chunks: keep flags and compacted rows of many chunks at once.
-__global__ __launch_bounds__(kSelThreads) void select_chunk_scan_kernel(
-    ExpertTable tab, const float* __restrict__ scores, uint8_t* __restrict__ keep,
-    int32_t* __restrict__ perm, const uint32_t* __restrict__ tau_need,
-    const uint32_t* __restrict__ counts, const float2* __restrict__ rnorm,
-    float* __restrict__ ebound) {
-  __shared__ uint32_t wsum[kSelWaves];
-  const int b = blockIdx.x;
-  int e = 0;
-  while (e + 1 < tab.E && tab.hist_off[e + 1] <= b) ++e;
-  const int lo = tab.pair_off[e] + (b - tab.hist_off[e]) * kHistChunk;
-  const int hi = min(lo + kHistChunk, tab.pair_off[e + 1]);
-  // counts of the expert's earlier chunks, summed over the workgroup (one
-  // load per thread instead of a serial chain of them)
-  uint32_t pgt = 0, peq = 0;
-  for (int c = tab.hist_off[e] + (int)threadIdx.x; c < b; c += kSelThreads) {
-    pgt += counts[2 * c];
-    peq += counts[2 * c + 1];
-  }
-  uint32_t run_gt, run_eq;
-  block_scan(pgt, wsum, run_gt);
-  block_scan(peq, wsum, run_eq);
-  const int seg = tab.seg_off[e];
-  const uint32_t q = (uint32_t)(tab.seg_off[e + 1] - seg);
-  uint32_t kbound[2] = {0u, 0u};
-  scan_keep(nullptr, scores, tab.pair_off[tab.E], lo, hi, 0, tau_need[2 * e],
-            tau_need[2 * e + 1], run_gt, run_eq, q, seg, keep, perm, wsum,
-            ebound != nullptr ? rnorm : nullptr, kbound);
-  if (ebound != nullptr) put_kept_bound(kbound, wsum, ebound, e, true);
 }
 
 }  // namespace
@@ -669,29 +727,52 @@ hipError_t launch_score(int dtype, int mode, const void* g, const void* phi, con
   return hipGetLastError();
 }
 
-hipError_t launch_select_scan(const ExpertTable& tab, const float* scores, uint8_t* keep,
-                              int32_t* perm, int32_t* seg_offsets_out, uint32_t* hist,
-                              hipStream_t s, const float2* rnorm, float* ebound) {
-  const int chunks = tab.hist_off[tab.E];
-  // workspace: chunk histograms, then tau / need per expert, then per-chunk counts
-  uint32_t* tau_need = hist + (size_t)chunks * kBins;
-  uint32_t* counts = tau_need + 2 * kMaxE;
-  if (chunks > 0) {
-    hipLaunchKernelGGL(select_hist_kernel, dim3(chunks), dim3(kSelThreads), 0, s, tab, scores,
-                       hist);
-    const hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+// The chunked passes serve problems with an expert above kSelLdsKeys pairs;
+// the others take the one-launch LDS path, which needs no workspace.
+static bool select_chunked(const ExpertTable& tab) {
+  for (int e = 0; e < tab.E; ++e)
+    if (tab.pair_off[e + 1] - tab.pair_off[e] > kSelLdsKeys) return true;
+  return false;
+}
+
+size_t select_workspace_bytes(const ExpertTable& tab) {
+  if (!select_chunked(tab)) return 0;
+  return ((size_t)tab.E * (2 * kB12 + kB8 + 8) + 2 * (size_t)tab.chunk_off[tab.E]) *
+         sizeof(uint32_t);
+}
+
+hipError_t launch_select(const ExpertTable& tab, const float* scores, uint8_t* keep,
+                         int32_t* perm, int32_t* seg_offsets_out, uint32_t* ws, hipStream_t s,
+                         const float2* rnorm, float* ebound) {
+  if (!select_chunked(tab)) {
+    hipLaunchKernelGGL(select_lds_kernel, dim3(tab.E), dim3(kLdsT), 0, s, tab, scores, keep,
+                       perm, seg_offsets_out, rnorm, ebound);
+    return hipGetLastError();
   }
-  hipLaunchKernelGGL(select_scan_kernel, dim3(tab.E), dim3(kSelThreads), 0, s, tab, scores,
-                     keep, perm, seg_offsets_out, hist, tau_need, rnorm, ebound);
+  SelWs w;
+  w.h1 = ws;
+  w.h2 = w.h1 + (size_t)tab.E * kB12;
+  w.h3 = w.h2 + (size_t)tab.E * kB12;
+  w.st = w.h3 + (size_t)tab.E * kB8;
+  w.counts = w.st + 8 * (size_t)tab.E;
+  const int chunks = tab.chunk_off[tab.E];
+  const int init_words = tab.E * (2 * kB12 + kB8);
+  int init_blocks = (init_words + 4 * 256 - 1) / (4 * 256);
+  if (init_blocks < 1) init_blocks = 1;
+  hipLaunchKernelGGL(select_init_kernel, dim3(init_blocks), dim3(256), 0, s, tab, w,
+                     seg_offsets_out, ebound);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || chunks == 0) return err;
-  hipLaunchKernelGGL(select_chunk_count_kernel, dim3(chunks), dim3(kSelThreads), 0, s, tab,
-                     scores, tau_need, counts);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(select_chunk_scan_kernel, dim3(chunks), dim3(kSelThreads), 0, s, tab,
-                     scores, keep, perm, tau_need, counts, rnorm, ebound);
+  hipLaunchKernelGGL(select_digit_kernel<1>, dim3(chunks), dim3(kSelT), 0, s, tab, scores, w);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(select_digit_kernel<2>, dim3(chunks), dim3(kSelT), 0, s, tab, scores, w);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(select_digit_kernel<3>, dim3(chunks), dim3(kSelT), 0, s, tab, scores, w);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(select_count_kernel, dim3(chunks), dim3(kSelT), 0, s, tab, scores, w);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(select_scan_kernel, dim3(chunks), dim3(kSelT), 0, s, tab, scores, keep,
+                     perm, w, rnorm, ebound);
   return hipGetLastError();
 }
 

@@ -178,6 +178,7 @@ def test_workspace_size_and_check():
     heads = 256 + 2 * 256 * 4
     plane_phi = (60 * 32 * 2 + 255) // 256 * 256
     plane_g = (60 * 64 * 2 + 255) // 256 * 256
+    assert select_bytes((40, 20, 30)) == 0   # small experts: the selection needs none
     assert n == max(2 * plane_phi, 2 * plane_g) + heads
     for f in (L.lib().lrmoe_grouped_backward, L.lib().lrmoe_grouped_backward_gate_up):
         assert f(C.byref(p.struct), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n - 1,
@@ -213,24 +214,36 @@ def test_grouped_backward_gate_up_validation():
     assert f(None, *ok) == 1
 
 
-def test_select_workspace_for_large_experts():
-    """An expert with more than 24576 pairs gets its first radix digit counted
-    by one workgroup per 16384-pair chunk, into 16 KiB histograms in the
-    workspace, and its scan split over the same chunks (tau / need per
-    expert, counts per chunk): the selection calls then need that much
-    workspace."""
+def select_bytes(counts):
+    """The selection's workspace: none when every expert has at most 24576
+    pairs (one workgroup per expert, keys in LDS); else, for the chunked
+    passes, per expert two 4096-bin and one 256-bin digit histogram and 8
+    words of select state, per 4096-pair chunk two counts (32-bit words)."""
+    if max(counts) <= 24576:
+        return 0
+    chunks = sum((n + 4095) // 4096 for n in counts)
+    return (len(counts) * (2 * 4096 + 256 + 8) + 2 * chunks) * 4
+
+
+def test_select_workspace():
+    """A problem with an expert above 24576 pairs is selected in chunked
+    passes over 4096-pair chunks of every expert, which keep their digit
+    histograms, state and chunk counts in the workspace: the selection calls
+    then need that much.  Otherwise they need none."""
     counts, quotas = (60000, 24576, 100), (48000, 19660, 80)
     p = plan(counts=counts, quotas=quotas, d_out=8, d_in=8)
-    chunks = (60000 + 16383) // 16384   # only the first expert is large
-    # chunk histograms, tau / need per expert (256 experts max), chunk counts
-    hist = (chunks * 4096 + 2 * 256 + 2 * chunks) * 4
+    sel = select_bytes(counts)
+    assert sel == (3 * 8456 + 2 * (15 + 6 + 1)) * 4
     n = p.workspace_bytes()
-    assert n >= hist
-    assert sscc(p, ws=FAKE, ws_bytes=hist - 1) == 6
-    assert sscc(p, ws=None, ws_bytes=hist) == 1
-    assert sscc(p, ws=FAKE + 4, ws_bytes=hist) == 4
-    # no large expert: the selection needs no workspace at all
-    assert sscc(plan(counts=(24576, 10), quotas=(10, 5), d_out=8, d_in=8), alpha=None) == 1
+    assert n >= sel
+    assert sscc(p, ws=FAKE, ws_bytes=sel - 1) == 6
+    assert sscc(p, ws=None, ws_bytes=sel) == 1
+    assert sscc(p, ws=FAKE + 4, ws_bytes=sel) == 4
+    # no expert above 24576 pairs: no workspace (the only error is the NULL alpha)
+    assert sscc(plan(counts=(24576, 10), quotas=(10, 5), d_out=8, d_in=8), alpha=None,
+                ws=None, ws_bytes=0) == 1
+    assert sscc(plan(counts=(24576, 10), quotas=(10, 5), d_out=8, d_in=8), alpha=None,
+                ws=FAKE + 4, ws_bytes=0) == 1   # and its alignment is not checked either
 
 
 def test_grouped_backward_validation():
@@ -359,12 +372,15 @@ def test_plan_quota_device_validation():
 
 
 def test_noalloc_rejects_problems_beyond_its_scratch():
-    """The entry point without a workspace holds the selection scratch of
-    large experts in an 8 MiB static device buffer: a problem needing more
-    (here 550 first-digit histograms of 16 KiB for a 9-million-pair expert)
-    is rejected before any HIP call; so are the usual bad arguments."""
+    """The entry point without a workspace holds the selection scratch of the
+    chunked passes in an 8 MiB static device buffer: a problem needing more
+    (here 250 experts, one above 24576 pairs: 33 KiB of digit histograms and
+    state each) is rejected before any HIP call; so are the usual bad
+    arguments.  A 9-million-pair expert fits."""
     f = L.lib().lrmoe_score_select_compact_noalloc
-    big = plan(counts=(9_000_000, 5), quotas=(7_200_000, 4), d_out=8, d_in=8)
+    many = (30000,) + (4,) * 249
+    assert select_bytes((9_000_000, 5)) <= 8 << 20 < select_bytes(many)
+    big = plan(counts=many, quotas=(2,) * 250, d_out=8, d_in=8)
     args = [None] + [FAKE] * 11 + [None, None]   # row alpha g phi scores keep seg perm g_c phi_c alpha_c dphi
     assert f(C.byref(big.struct), *args) == 8
     assert L.lib().lrmoe_status_string(8)

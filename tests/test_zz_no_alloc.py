@@ -2,7 +2,8 @@
 scratch is the library's static device array) against
 lrmoe_score_select_compact with a caller workspace, on two calls in a row,
 the second smaller, both with experts above 24576 pairs so that the scratch
-is used (chunk histograms, thresholds, chunk counts).  Results must be bit
+is used (the chunked passes' digit histograms, select state and chunk
+counts).  Results must be bit
 for bit the same: both run the same kernels on the same inputs."""
 import numpy as np
 import pytest
