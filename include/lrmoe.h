@@ -216,13 +216,13 @@ lrmoe_status lrmoe_score_select_compact(
 
 /* lrmoe_score_select_compact for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
- * hipMalloc): no workspace argument.  The selection's scratch -- the
- * first-digit histograms, thresholds and chunk counts of experts with more
- * than 24576 pairs -- lives in a static device array of the library,
- * 8 MiB, which every GPU the library runs on holds until the process ends.
- * Problems whose large experts need more (about 8.3 million pairs in
- * experts above 24576 pairs) are rejected with LRMOE_ERR_SCRATCH before
- * anything is launched.  The call allocates nothing; on its first call on a
+ * hipMalloc): no workspace argument.  The selection's scratch -- used when
+ * an expert has more than 24576 pairs: three radix-digit histograms and the
+ * select state per expert (33 KiB) and two counts per 4096-pair chunk --
+ * lives in a static device array of the library, 8 MiB, which every GPU the
+ * library runs on holds until the process ends.  Problems that need more
+ * (about 240 experts or more, with one of them above 24576 pairs) are
+ * rejected with LRMOE_ERR_SCRATCH before anything is launched.  The call allocates nothing; on its first call on a
  * device it looks up that device's copy of the array (the current device,
  * which `stream` must belong to).  Nothing in the scratch needs to start at
  * zero: every call writes what it later reads.  All calls on one GPU share
