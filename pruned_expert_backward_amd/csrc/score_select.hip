@@ -709,11 +709,12 @@ hipError_t launch_score(int dtype, int mode, const void* g, const void* phi, con
   if (P <= 0) return hipSuccess;
   const int waves_per_block = 4;
   int blocks = (P + waves_per_block - 1) / waves_per_block;
-  // 8 workgroups (32 waves) fit on a CU at a time; eight times that many
-  // let the dispatcher balance CUs and channels as workgroups finish (a
-  // streaming read reaches 6.3 TB/s so, against 5.9 with one resident wave
-  // per slot looping over the whole range)
-  if (blocks > 256 * 64) blocks = 256 * 64;
+  // One pair per wave: the dispatcher hands out fresh workgroups as others
+  // finish, which balances CUs and memory channels better than waves that
+  // loop over many pairs (655 360-pair workload: 1214 us, against 1274 us
+  // with 64 workgroups per CU looping and 1330 us with 16).  Beyond 4 M
+  // pairs the waves loop (grid-stride).
+  if (blocks > 256 * 4096) blocks = 256 * 4096;
   const dim3 grid(blocks);
   if (mode == LRMOE_SCORE_GRAD_SQNORM)
     launch_score_mode<LRMOE_SCORE_GRAD_SQNORM>(dtype, grid, s, g, phi, alpha, row_index, P, T,
