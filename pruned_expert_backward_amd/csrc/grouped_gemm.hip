@@ -148,7 +148,7 @@ __device__ __forceinline__ f32x16 mfma_f16(i16x8 a, i16x8 b, f32x16 c) {
 struct TileJob {
   int e, m0, n0;
   int chunk, chunks;   // dW K chunk of this tile and the expert's chunk count
-  bool tall;           // dphi: 512 x 128 edge tile over row tiles m0 / 256 and m0 / 256 + 1
+  bool tall;           // 512 x 128 edge tile over row tiles m0 / 256 and m0 / 256 + 1
 };
 
 // Queue length of XCD x in item slots.
@@ -159,11 +159,11 @@ __device__ __forceinline__ int queue_items(const GemmTable& tab, int x) {
 }
 
 // Item `i` of XCD x's queue -> tile; false for an idle slot.  With `tall`,
-// the last input-gradient column tile of every even row tile becomes a
-// 512 x 128 tile that also covers the odd row tile below it, whose slot then
-// idles.
+// the last input-gradient column tile (and with `tall_dw` the last
+// weight-gradient one) of every even row tile becomes a 512 x 128 tile that
+// also covers the odd row tile below it, whose slot then idles.
 __device__ __forceinline__ bool decode(const GemmTable& tab, int x, int i, bool& is_dw,
-                                      TileJob& job, bool tall) {
+                                      TileJob& job, bool tall, bool tall_dw) {
   const int p = i / kGroupSlots, t = i % kGroupSlots;
   int e, chunk, lg;
   if (tab.use_table) {
@@ -203,7 +203,7 @@ __device__ __forceinline__ bool decode(const GemmTable& tab, int x, int i, bool&
   const int tn = (lg % ngn) * gn + t % gn;
   const int tiles_m = is_dw ? tab.dw_tiles_m : (q + BM - 1) / BM;
   if (tm >= tiles_m || tn >= tab.tiles_n) return false;
-  job.tall = tall && !is_dw && tn == tab.tiles_n - 1;
+  job.tall = tall && (!is_dw || tall_dw) && tn == tab.tiles_n - 1;
   if (job.tall && (tm & 1)) return false;
   job.e = e;
   job.m0 = tm * BM;
@@ -296,13 +296,9 @@ struct Tile {
   static constexpr int TBN = TALL ? kTile / 2 : kTile;   // tile columns (N)
   static constexpr int kWN = TBN / WTN;                  // wave columns (1 or 2)
   static_assert((TBM / WTM) * kWN == kWaves, "wave grid");
-  // Tall tiles serve the input gradient only: as weight-gradient tiles
-  // (which read every g_c byte once per column tile anyway) they halved the
-  // number of tiles in flight and lost more to that than the edge waste cost.
-  static_assert(!(TALL && IS_DW), "tall tiles are input-gradient tiles");
   // One K step of an operand plane: TBM (A) or TBN (B) values per K row.
-  // MC rows are RA / RB bytes long (RA: weight-gradient tiles, 256 wide);
-  // KC rows are 64 bytes.
+  // MC rows are RA / RB bytes long (RA: weight-gradient tiles, 256 or 512
+  // wide); KC rows are 64 bytes.
   static constexpr int RA = 2 * TBM, RB = 2 * TBN;
   static constexpr int kPlaneA = TBM * BK * 2, kPlaneB = TBN * BK * 2;
   static constexpr int kStage = PA * kPlaneA + PB * kPlaneB;
@@ -372,8 +368,9 @@ struct Tile {
 #pragma unroll
     for (int j = 0; j < kPwA; ++j) {
       const int blk = wave * kPwA + j;
-      if (A_MC) {   // MC block: rows 2*blk, 2*blk+1 of the step, 32 chunks each
-        const int k = 2 * blk + (lane >> 5), pc = lane & 31;
+      if (A_MC) {   // MC block: 1024 / RA K rows of RA / 16 chunks each
+        constexpr int cpr = RA / 16;
+        const int k = (64 / cpr) * blk + lane / cpr, pc = lane % cpr;
         const int acolm = m0 + 8 * (pc ^ ((k & 3) << 2));
         aoff[j] = acolm < d_out ? (uint32_t)(k * d_out + acolm) * 2u : kOutOfRange;
       } else {   // KC block: rows 16*blk .. +15 of the tile, 4 chunks each
@@ -788,10 +785,15 @@ struct Tile {
     const int d_out = args.d_out, d_in = args.d_in;
     LDS_AS const int32_t* s_perm = reinterpret_cast<LDS_AS const int32_t*>(prm);
     LDS_AS const float* s_alpha = reinterpret_cast<LDS_AS const float*>(prm + kMaxRows * 4);
-    // Split dW tiles go to their chunk's partial tile (full 256x256, row-major).
+    // Split dW tiles go to their chunk's partial tile (full 256x256, row-major;
+    // the reduction crops it to the matrix edge).  A tall weight-gradient tile
+    // spans two row tiles of that grid: waves 0-1 write the upper one, waves
+    // 2-3 the lower one (columns 0..127 only, the rest lies past d_in); rows
+    // past d_out are not written, so the lower tile may lie past the grid.
     float* part = nullptr;
+    const int prow0 = TALL ? (wm >> 1) * kTile : 0;   // first tile row of this wave's partial
     if (IS_DW && chunks > 1) {
-      const int tile = (m0 / BM) * tab.tiles_n + n0 / BN;
+      const int tile = ((m0 + prow0) / kTile) * tab.tiles_n + n0 / kTile;
       part = args.ops.partials + ((partial_base(tab, e) + (int64_t)tile * chunks + chunk) << 16);
     }
     if constexpr (GLU != 0) {   // SiLU-GLU chain: no dphi, no alpha
@@ -802,7 +804,7 @@ struct Tile {
     // and edge predicate ahead of the main loop, where they would stay live.
     int ln = lane;
     asm volatile("" : "+v"(ln));
-    int ncols = (IS_DW && part != nullptr) ? BN : d_in - n0;
+    int ncols = (IS_DW && part != nullptr) ? TBN : d_in - n0;
     asm volatile("" : "+s"(ncols));
     const bool odd = (ln & 1) != 0;
     // this lane's column inside each 16-column group: 0/4 (lane half) + 8 (odd lane)
@@ -822,7 +824,9 @@ struct Tile {
       for (int h = 0; h < 2; ++h) {
         const int lrow = lrow0 + h;
         if (IS_DW) {
-          if (part != nullptr) orow[h] = part + lrow * BN;
+          if (part != nullptr) {
+            if (!TALL || m0 + lrow < mrows) orow[h] = part + (lrow - prow0) * kTile;
+          }
           else if (m0 + lrow < mrows) orow[h] = args.dW + ((int64_t)e * d_out + m0 + lrow) * d_in + n0;
         } else {
           const int32_t u = s_perm[lrow];
@@ -876,8 +880,11 @@ constexpr int stages_for(int bytes) {
 }
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-// Stage counts of the square tiles of both products and of the tall
-// input-gradient tile, which runs only where its stage fits twice.
+// Stage counts of the square tiles of both products and of the tall tiles.
+// Tall input-gradient tiles run where their stage fits twice.  Tall
+// weight-gradient tiles run only in kernels whose dW reads a two-plane
+// operand (the exact mode): there they made the GLM 20x GEMM 4.7 % faster;
+// with single-pass dW tiles, which halved the tiles in flight, 12 % slower.
 template <int DW_PA, int DW_PB, int DP_PA, int DP_PB>
 struct Cfg {
   static constexpr int sq = kPlaneBytes;                         // square tile plane
@@ -885,10 +892,13 @@ struct Cfg {
   static constexpr int NS_DW = stages_for((DW_PA + DW_PB) * sq);
   static constexpr int NS_DP = stages_for((DP_PA + DP_PB) * sq);
   static constexpr int NS_DPT = stages_for(DP_PA * ta + DP_PB * tb);
+  static constexpr int NS_DWT = stages_for(DW_PA * ta + DW_PB * tb);
   static constexpr bool tall_fits = NS_DPT >= 2;
+  static constexpr bool tall_dw = tall_fits && DW_PA + DW_PB >= 3 && NS_DWT >= 2;
   static constexpr int stages =
       cmax(cmax(NS_DW * (DW_PA + DW_PB) * sq, NS_DP * (DP_PA + DP_PB) * sq),
-           tall_fits ? NS_DPT * (DP_PA * ta + DP_PB * tb) : 0);
+           cmax(tall_fits ? NS_DPT * (DP_PA * ta + DP_PB * tb) : 0,
+                tall_dw ? NS_DWT * (DW_PA * ta + DW_PB * tb) : 0));
   static constexpr int sink = stages + kPermBytes + 16;   // kWaves x 1 KiB
   static constexpr int bytes = sink + kWaves * 1024;
   static_assert(NS_DW >= 2 && NS_DP >= 2, "stages");
@@ -938,9 +948,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_backward_kernel(Args args
   using C = Cfg<DW_PA, DW_PB, DP_PA, DP_PB>;
   using DwTile = Tile<true, DW_PA, DW_PB, C::NS_DW, 0, DW_F16>;
   using DpTile = Tile<false, DP_PA, DP_PB, C::NS_DP, GLU>;
-  // tall input-gradient edge tiles: not with the SiLU-GLU epilogue
+  // tall edge tiles: not with the SiLU-GLU epilogue
   constexpr bool kTall = GLU == 0 && C::tall_fits;
+  constexpr bool kTallDw = kTall && C::tall_dw;
   using DpTall = Tile<false, DP_PA, DP_PB, kTall ? C::NS_DPT : 2, 0, false, true>;
+  using DwTall = Tile<true, DW_PA, DW_PB, kTallDw ? C::NS_DWT : 2, 0, DW_F16, true>;
   const bool tall_on = kTall && tab.tall != 0;
   __shared__ __attribute__((aligned(16))) char smem_raw[C::bytes];
   LDS_AS char* smem = (LDS_AS char*)(smem_raw);
@@ -967,13 +979,19 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_backward_kernel(Args args
         ++hop;
         continue;
       }
-      if (decode(tab, qx, i, is_dw, job, tall_on)) return i;
+      if (decode(tab, qx, i, is_dw, job, tall_on, kTallDw)) return i;
     }
     return -1;
   };
-  // Runs fn on the tile of job j (one of three tile types).
+  // Runs fn on the tile of job j (one of up to four tile types).
   auto with_tile = [&](bool is_dw, const TileJob& j, auto&& fn) __attribute__((always_inline)) {
     if (is_dw) {
+      if constexpr (kTallDw) {
+        if (j.tall) {
+          fn(DwTall(args, tab, j, smem, sink));
+          return;
+        }
+      }
       fn(DwTile(args, tab, j, smem, sink));
       return;
     }
