@@ -174,14 +174,18 @@ def test_ties_given_scores(distinct):
         U.compare_full(p, q, out, scores_in=s)
 
 
-@pytest.mark.parametrize("distinct,layout", [(0, 0), (3, 0), (1, 0), (0, 1), (3, 1)])
+@pytest.mark.parametrize("distinct,layout", [(0, 0), (3, 0), (1, 0), (0, 1), (3, 1), (0, 2),
+                                             (3, 2)])
 def test_select_large_experts(distinct, layout):
     """An expert above the LDS key cache (24576 pairs) sends the problem
     through the chunked passes (4096-pair chunks of every expert): continuous
     scores, 3 values, or one value for all pairs; experts starting at
     unaligned pair offsets (the scan's second, short tile), of one, two or
-    several chunks, empty, keeping nothing or everything."""
-    counts = [[90000, 30000, 4000, 1, 0], [30001, 4097, 3, 0, 8190, 2, 4096]][layout]
+    several chunks, empty, keeping nothing or everything; 64 experts (the
+    per-expert histograms and state at larger offsets, the chunk-to-expert
+    lookup over many experts)."""
+    many = [30001] + [((7 * i) % 50) * 37 for i in range(1, 64)]   # zeros among them
+    counts = [[90000, 30000, 4000, 1, 0], [30001, 4097, 3, 0, 8190, 2, 4096], many][layout]
     p = W.make_problem(P=sum(counts), E=len(counts), d_out=8, d_in=8, dtype="bf16",
                        counts=counts, seed=40 + layout)
     s = W.random_scores(p.P, seed=40 + distinct, distinct=distinct)
