@@ -104,8 +104,8 @@ __device__ __forceinline__ void copy_row_f16(const uint4* __restrict__ src,
 }
 
 struct F16Planes {
-  uint4* a;            // [M, d_out / 8] chunks, or null: no float16 planes
-  uint4* b;            // [M, d_in / 8]
+  uint4* g;              // [M, d_out / 8] chunks, or null
+  uint4* phi;            // [M, d_in / 8], or null; both null: no float16 planes
   const float* ebound;   // [E][2]
   SegTable seg;
 };
@@ -133,15 +133,17 @@ __global__ __launch_bounds__(256) void gather_kernel(
     const float a = alpha[u];
     uint4* gdst = g_c != nullptr ? g_c + (int64_t)j * gch : nullptr;
     uint4* pdst = phi_c + (int64_t)j * pch;
-    if (f16.a != nullptr) {   // float16 weight-gradient planes of both operands
+    if (f16.g != nullptr || f16.phi != nullptr) {   // float16 weight-gradient planes
       const int e = expert_of_row(f16.seg, j);
       const int sa = f16_scale_exp(f16.ebound[2 * e]), sb = f16_scale_exp(f16.ebound[2 * e + 1]);
-      uint4* pa = f16.a + (int64_t)j * gch;
-      uint4* pb = f16.b + (int64_t)j * pch;
-      if (g_ok) copy_row_f16(g + gr * gch, gdst, pa, pl_from_phi ? 1.f : a, sa, gch, lane);
-      else zero_row(gdst, pa, nullptr, gch, lane);
-      if (p_ok) copy_row_f16(phi + pr * pch, pdst, pb, pl_from_phi ? a : 1.f, sb, pch, lane);
-      else zero_row(pdst, pb, nullptr, pch, lane);
+      uint4* pg = f16.g != nullptr ? f16.g + (int64_t)j * gch : nullptr;
+      uint4* pp = f16.phi != nullptr ? f16.phi + (int64_t)j * pch : nullptr;
+      if (!g_ok) zero_row(gdst, pg, nullptr, gch, lane);
+      else if (pg != nullptr) copy_row_f16(g + gr * gch, gdst, pg, pl_from_phi ? 1.f : a, sa, gch, lane);
+      else if (gdst != nullptr) copy_row(g + gr * gch, gdst, gch, lane);
+      if (!p_ok) zero_row(pdst, pp, nullptr, pch, lane);
+      else if (pp != nullptr) copy_row_f16(phi + pr * pch, pdst, pp, pl_from_phi ? a : 1.f, sb, pch, lane);
+      else copy_row(phi + pr * pch, pdst, pch, lane);
     } else if (pl_hi != nullptr && !pl_from_phi) {
       uint4* h = pl_hi + (int64_t)j * gch;
       uint4* l = pl_lo ? pl_lo + (int64_t)j * gch : nullptr;
@@ -151,8 +153,8 @@ __global__ __launch_bounds__(256) void gather_kernel(
       if (g_ok) copy_row(g + gr * gch, gdst, gch, lane);
       else zero_row(gdst, nullptr, nullptr, gch, lane);
     }
-    if (f16.a != nullptr) {
-      // both planes written above
+    if (f16.g != nullptr || f16.phi != nullptr) {
+      // written above
     } else if (pl_hi != nullptr && pl_from_phi) {
       uint4* h = pl_hi + (int64_t)j * pch;
       uint4* l = pl_lo ? pl_lo + (int64_t)j * pch : nullptr;
@@ -243,8 +245,8 @@ __global__ __launch_bounds__(256) void expert_bound_kernel(SegTable seg,
   }
 }
 
-// Step 2: the two float16 planes from the compacted rows, one wave per row
-// (bit for bit the gather's planes of the one-call path).
+// Step 2: the float16 planes from the compacted rows (either may be null),
+// one wave per row (bit for bit the gather's planes of the one-call path).
 __global__ __launch_bounds__(256) void split_f16_kernel(
     SegTable seg, const uint4* __restrict__ g_c, const uint4* __restrict__ phi_c,
     const float* __restrict__ alpha_c, int32_t M, int32_t gch, int32_t pch, int alpha_on_phi,
@@ -253,10 +255,13 @@ __global__ __launch_bounds__(256) void split_f16_kernel(
   const int64_t j = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (j >= M) return;
   const int e = expert_of_row(seg, (int)j);
-  const int sa = f16_scale_exp(ebound[2 * e]), sb = f16_scale_exp(ebound[2 * e + 1]);
   const float a = alpha_c[j];
-  copy_row_f16(g_c + j * gch, nullptr, pa + j * gch, alpha_on_phi ? 1.f : a, sa, gch, lane);
-  copy_row_f16(phi_c + j * pch, nullptr, pb + j * pch, alpha_on_phi ? a : 1.f, sb, pch, lane);
+  if (pa != nullptr)
+    copy_row_f16(g_c + j * gch, nullptr, pa + j * gch, alpha_on_phi ? 1.f : a,
+                 f16_scale_exp(ebound[2 * e]), gch, lane);
+  if (pb != nullptr)
+    copy_row_f16(phi_c + j * pch, nullptr, pb + j * pch, alpha_on_phi ? a : 1.f,
+                 f16_scale_exp(ebound[2 * e + 1]), pch, lane);
 }
 
 // Zero-masked dense alternative: alpha of dropped pairs set to 0 in the
@@ -295,9 +300,10 @@ hipError_t launch_gather(int dtype, const int32_t* perm, const uint8_t* keep,
                          int32_t P, int32_t g_rows, int32_t phi_rows, int32_t d_out,
                          int32_t d_in, hipStream_t s, const GatherPlanes& planes) {
   const int per = (dtype == LRMOE_BF16) ? 8 : 4;
-  if ((planes.hi != nullptr || planes.f16_a != nullptr) && dtype != LRMOE_BF16)
+  if ((planes.hi != nullptr || planes.f16_g != nullptr || planes.f16_phi != nullptr) &&
+      dtype != LRMOE_BF16)
     return hipErrorInvalidValue;
-  F16Planes f16{(uint4*)planes.f16_a, (uint4*)planes.f16_b, planes.ebound, planes.seg};
+  F16Planes f16{(uint4*)planes.f16_g, (uint4*)planes.f16_phi, planes.ebound, planes.seg};
   const int64_t jobs = (int64_t)M + (dphi_zero ? (int64_t)P : 0);
   if (jobs == 0) return planes.nzero > 0 ? launch_zero(planes.zero, planes.nzero, s) : hipSuccess;
   const int64_t blocks = (jobs + 3) / 4;
@@ -330,12 +336,12 @@ hipError_t launch_expert_bounds(const SegTable& seg, const uint16_t* g, const ui
 
 hipError_t launch_split_f16(const SegTable& seg, const uint16_t* g_c, const uint16_t* phi_c,
                             const float* alpha_c, int32_t M, int32_t d_out, int32_t d_in,
-                            bool alpha_on_phi, const float* ebound, uint16_t* f16_a,
-                            uint16_t* f16_b, hipStream_t s) {
+                            bool alpha_on_phi, const float* ebound, uint16_t* f16_g,
+                            uint16_t* f16_phi, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   hipLaunchKernelGGL(split_f16_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, s, seg,
                      (const uint4*)g_c, (const uint4*)phi_c, alpha_c, M, d_out / 8, d_in / 8,
-                     alpha_on_phi ? 1 : 0, ebound, (uint4*)f16_a, (uint4*)f16_b);
+                     alpha_on_phi ? 1 : 0, ebound, (uint4*)f16_g, (uint4*)f16_phi);
   return hipGetLastError();
 }
 

@@ -31,7 +31,10 @@
 //     prologue writes alpha * (the narrower of g_c, phi_c) as bf16 hi + lo
 //     planes (exact mode; hi only in single-rounding mode), and float32
 //     storage is pre-split into hi + lo planes.  Products of split operands
-//     sum hi*hi + hi*lo + lo*hi.  The MFMA loop does no conversions.
+//     sum hi*hi + hi*lo + lo*hi.  In the float16 weight-gradient mode the
+//     operand with alpha is a scaled float16 plane, and the other one either
+//     a plane too or (narrow problems) its bf16 rows, converted to scaled
+//     float16 in registers inside the MFMA loop; no other mode converts.
 //   * Operand tiles of one K step (32) live in LDS in the global layout:
 //     "KC" tiles (rows along M/N, K contiguous: g_c rows of the input
 //     gradient) are read with 16-byte ds_read_b128 fragments; "MC" tiles
@@ -286,10 +289,14 @@ constexpr int kPermBytes = kMaxRows * 8;
 // The matrix core always has independent MFMAs queued while fragments and
 // stages move, and the global loads trickle out between MFMAs instead of
 // stalling the wave in a burst.
-// F16 (weight-gradient tiles only): float16 operand planes, float16 MFMAs,
-// and the epilogue undoes the expert's power-of-two scales.
+// F16 (weight-gradient tiles only): float16 MFMAs, and the epilogue undoes
+// the expert's power-of-two scales.  The operand that carries alpha comes as
+// a scaled float16 plane.  The other one is a scaled float16 plane too
+// (F16 == 3), or the compacted bf16 buffer itself, converted in registers
+// after its LDS fragment reads (A for F16 == 1, B for F16 == 2; see
+// cvt_slot).
 // TALL: a 512 x 128 tile (waves stacked 4 x 1) instead of 256 x 256.
-template <bool IS_DW, int PA, int PB, int NS, int GLU = 0, bool F16 = false, bool TALL = false>
+template <bool IS_DW, int PA, int PB, int NS, int GLU = 0, int F16 = 0, bool TALL = false>
 struct Tile {
   static constexpr bool A_MC = IS_DW;
   static constexpr int TBM = TALL ? 2 * kTile : kTile;   // tile rows (M)
@@ -309,6 +316,10 @@ struct Tile {
   static constexpr int kHalfMfmas = kMB * kNB * kTerms; // per wave per half step
   static constexpr int kFrags = PA * kMB + PB * kNB;     // fragments per half step
   static_assert(kFrags <= kHalfMfmas && kLoads <= kHalfMfmas, "interleave slots");
+  // float16 mode: one term, and a converted fragment's 4 dwords spread over
+  // the 4 MFMAs of the fragment before it
+  static constexpr bool kCvt = IS_DW && (F16 == 1 || F16 == 2);
+  static_assert(!kCvt || (kTerms == 1 && kMB == 4 && kNB == 4), "float16 slots");
 
   struct Frags {
     i16x8 a[PA][kMB];
@@ -317,6 +328,7 @@ struct Tile {
 
   int e, m0, n0, chunk, chunks, q, seg, K, mrows, nk;
   int lane, wave, wm, wn;
+  int cvs;   // float16 mode: power of two applied to the converted operand
   const uint16_t* A[2];
   const uint16_t* B[2];
   uint32_t aoff[kPwA], boff[kPwB];
@@ -349,6 +361,9 @@ struct Tile {
     K = IS_DW ? (q - kbeg < tab.kc ? q - kbeg : tab.kc) : d_out;
     mrows = IS_DW ? d_out : q;
     nk = (K + BK - 1) / BK;
+    cvs = 0;
+    if constexpr (kCvt)
+      cvs = __builtin_amdgcn_readfirstlane(f16_scale_exp(args.ops.dw_ebound[2 * e + (F16 == 2)]));
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       A[p] = IS_DW ? args.ops.dw_a[p] : args.ops.dp_a[p];
@@ -464,13 +479,51 @@ struct Tile {
   // The B fragment goes in the MFMA's first operand slot, so each 32x32
   // accumulator holds the block transposed: lane = tile row (M), registers =
   // columns (N), four consecutive columns per register quad.  That lets the
-  // epilogue write 16 bytes per lane.
+  // epilogue write 16 bytes per lane.  Within a term the MFMAs run A fragment
+  // by A fragment, or (F16 == 2) B fragment by B fragment: the converted
+  // operand's fragments are used one after the other.
   __device__ __forceinline__ static void mfma_i(const Frags& f, f32x16 (&acc)[kMB][kNB], int i) {
-    const int t = i / (kMB * kNB), a = (i % (kMB * kNB)) / kNB, b = i % kNB;
+    const int t = i / (kMB * kNB), r = i % (kMB * kNB);
+    const int a = (IS_DW && F16 == 2) ? r % kMB : r / kNB;
+    const int b = (IS_DW && F16 == 2) ? r / kMB : r % kNB;
     const int pa = (t == 2 || (t == 1 && PB == 1)) ? PA - 1 : 0;
     const int pb = (t == 1 && PB == 2) ? 1 : 0;
     if constexpr (IS_DW && F16) acc[a][b] = mfma_f16(f.b[pb][b], f.a[pa][a], acc[a][b]);
     else acc[a][b] = mfma(f.b[pb][b], f.a[pa][a], acc[a][b]);
+  }
+
+  // ---- float16 mode: bf16 -> float16 of 2^cvs * x, in place, for the two
+  // values of dword p of fragment x (the power of two is exact; one rounding
+  // to nearest even, the same as the scaled float16 planes get).
+  __device__ __forceinline__ void cvt_piece(i16x8& x, int p) const {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    u32x4 w = __builtin_bit_cast(u32x4, x);
+    const uint32_t d = w[p];
+    const float lo = __builtin_amdgcn_ldexpf(__uint_as_float(d << 16), cvs);
+    const float hi = __builtin_amdgcn_ldexpf(__uint_as_float(d & 0xFFFF0000u), cvs);
+    const f16x2 h = {(_Float16)lo, (_Float16)hi};
+    w[p] = __builtin_bit_cast(uint32_t, h);
+    x = __builtin_bit_cast(i16x8, w);
+  }
+  // Conversion work of MFMA slot i of a half that multiplies fragments F
+  // while G (the next half) is read: dword i % 4 of the converted operand's
+  // next fragment of F, and in the last 4 slots of G's first fragment (its
+  // LDS reads went out in the first half of the slots).  So every fragment is
+  // converted over the 4 MFMAs before its first use, 5 VALU instructions per
+  // 32-cycle MFMA.
+  __device__ __forceinline__ void cvt_slot(Frags& F, Frags& G, int i) const {
+    if constexpr (kCvt) {
+      const int grp = i / 4, p = i % 4;
+      if constexpr (F16 == 1) cvt_piece(grp + 1 < kMB ? F.a[0][grp + 1] : G.a[0][0], p);
+      else cvt_piece(grp + 1 < kNB ? F.b[0][grp + 1] : G.b[0][0], p);
+    }
+  }
+  // The first fragment of a freshly read set, all at once (tile start).
+  __device__ __forceinline__ void cvt_first(Frags& F) const {
+    if constexpr (kCvt) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) cvt_piece(F16 == 1 ? F.a[0][0] : F.b[0][0], p);
+    }
   }
 
   // Barrier of step kt: stage kt + 1 is complete for every wave.  Stages
@@ -505,6 +558,7 @@ struct Tile {
     for (int i = 0; i < kHalfMfmas; ++i) {
       mfma_i(f0, acc, i);
       if (i < kFrags) read_frag(S, 1, f1, i);
+      cvt_slot(f0, f1, i);
       if (load_at(i, kLoadsHi) >= 0)
         issue_one(args, (kt + NS - 1) * BK, smem + SP * kStage, kLoadsLo + load_at(i, kLoadsHi),
                   live1);
@@ -525,6 +579,7 @@ struct Tile {
     for (int i = 0; i < kHalfMfmas; ++i) {
       mfma_i(f1, acc, i);
       if (i < kFrags) read_frag(SN, 0, f0, i);
+      cvt_slot(f1, f0, i);
       if (load_at(i, kLoadsLo) >= 0)
         issue_one(args, (kt + NS) * BK, smem + S * kStage, load_at(i, kLoadsLo), live3);
       __builtin_amdgcn_sched_barrier(0);
@@ -547,6 +602,7 @@ struct Tile {
     Frags f0, f1;
 #pragma unroll
     for (int i = 0; i < kFrags; ++i) read_frag(0, 0, f0, i);
+    cvt_first(f0);
     for (int kt = 0; kt < nk; ++kt) step(args, smem, kt, f0, f1, acc);
   }
 
@@ -943,7 +999,7 @@ __device__ __forceinline__ void zero_dropped(const Args& args, LDS_AS int32_t* s
 // next tile's first loads are issued before the finished tile's stores, so
 // the store drain overlaps the next load latency.  Every workgroup exits when
 // every queue's counter and the zero-fill counter have passed their ends.
-template <int DW_PA, int DW_PB, int DP_PA, int DP_PB, int GLU, bool DW_F16>
+template <int DW_PA, int DW_PB, int DP_PA, int DP_PB, int GLU, int DW_F16>
 __global__ __launch_bounds__(kThreads, 1) void grouped_backward_kernel(Args args, GemmTable tab) {
   using C = Cfg<DW_PA, DW_PB, DP_PA, DP_PB>;
   using DwTile = Tile<true, DW_PA, DW_PB, C::NS_DW, 0, DW_F16>;
@@ -1034,7 +1090,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_backward_kernel(Args args
   zero_dropped(args, s_next);   // help with what is left of the zero-fill
 }
 
-template <int DW_PA, int DW_PB, int DP_PA, int DP_PB, int GLU = 0, bool DW_F16 = false>
+template <int DW_PA, int DW_PB, int DP_PA, int DP_PB, int GLU = 0, int DW_F16 = 0>
 hipError_t launch(const Args& args, const GemmTable& tab, hipStream_t s) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -1197,11 +1253,23 @@ hipError_t launch_grouped_backward(const GemmTable& tab, const GemmOperands& ops
                                    hipStream_t s) {
   const Args args{ops, alpha_c, perm, dW, dphi, d_out, d_in, P};
   const int key = ops.dw_pa * 1000 + ops.dw_pb * 100 + ops.dp_pa * 10 + ops.dp_pb;
-  if (ops.dw_f16) {   // float16 weight-gradient planes, bf16 input gradient
+  if (ops.dw_f16) {   // float16 weight gradient, bf16 input gradient
     if (key != 1111 || ops.dw_ebound == nullptr) return hipErrorInvalidValue;
-    if (ops.glu_out != nullptr)
-      return ops.glu_f32 ? launch<1, 1, 1, 1, 2, true>(args, tab, s) : hipErrorInvalidValue;
-    return launch<1, 1, 1, 1, 0, true>(args, tab, s);
+    if (ops.glu_out != nullptr) {
+      if (!ops.glu_f32) return hipErrorInvalidValue;
+      switch (ops.dw_f16) {
+        case 1: return launch<1, 1, 1, 1, 2, 1>(args, tab, s);
+        case 2: return launch<1, 1, 1, 1, 2, 2>(args, tab, s);
+        case 3: return launch<1, 1, 1, 1, 2, 3>(args, tab, s);
+        default: return hipErrorInvalidValue;
+      }
+    }
+    switch (ops.dw_f16) {
+      case 1: return launch<1, 1, 1, 1, 0, 1>(args, tab, s);
+      case 2: return launch<1, 1, 1, 1, 0, 2>(args, tab, s);
+      case 3: return launch<1, 1, 1, 1, 0, 3>(args, tab, s);
+      default: return hipErrorInvalidValue;
+    }
   }
   if (ops.glu_out != nullptr) {   // SiLU-GLU chain: bf16 storage only
     if (ops.glu_f32) {            // exact weight gradient, float32 hand-off

@@ -106,8 +106,11 @@ struct GemmOperands {
   const uint16_t* glu_b;
   void* glu_out;
   int32_t glu_f32;
-  // float16 weight gradient: dw_a / dw_b are float16 planes scaled by the
-  // powers of two of dw_ebound (see f16_scale_exp)
+  // float16 weight gradient (see f16_scale_exp), with powers of two from
+  // dw_ebound.  1: dw_a is the compacted bf16 g_c and dw_b the scaled
+  // float16 plane of alpha * phi_c; 2: dw_a the plane of alpha * g_c and dw_b
+  // the bf16 phi_c (the bf16 side is converted to scaled float16 in the
+  // GEMM's registers); 3: both are scaled float16 planes.
   int32_t dw_f16;
   const float* dw_ebound;
   // 1: the input-gradient A planes already carry alpha (alpha * g_c split),
@@ -144,7 +147,8 @@ __device__ __forceinline__ HiLo alpha_split(float a, float x) {
 // ---- float16 weight-gradient mode (LRMOE_DW_F16)
 // dW_e = sum_j A_j B_j^T runs on float16 matrix cores: A = 2^sA (the g row),
 // B = 2^sB (the phi row), alpha folded into one side and rounded once to 11
-// significant bits (the other side converts from bf16 exactly).  sA, sB are
+// significant bits (the other side converts from bf16 exactly, in its own
+// plane or inside the GEMM).  sA, sB are
 // per-expert powers of two from the largest row norm over the expert's kept
 // rows (ebound[e] = {max |A row|, max |B row|}, each at least the largest
 // magnitude): 2^s ebound lands in [2^14, 2^15), so every scaled value stays
@@ -212,11 +216,13 @@ struct GatherPlanes {
   bool from_phi = true;
   int32_t* zero = nullptr;
   int nzero = 0;
-  // float16 weight-gradient mode instead: both operand planes, f16_a [M,
-  // d_out] from the g rows and f16_b [M, d_in] from the phi rows, scaled by
-  // the expert's powers of two from ebound, alpha on the phi side if from_phi
-  uint16_t* f16_a = nullptr;
-  uint16_t* f16_b = nullptr;
+  // float16 weight-gradient mode instead: the planes of the g rows ([M,
+  // d_out]) and of the phi rows ([M, d_in]), each scaled by its side's power
+  // of two of the expert from ebound, alpha on the phi side if from_phi.  The
+  // plane of the side without alpha may be null (the GEMM converts that
+  // side's compacted bf16 rows itself).
+  uint16_t* f16_g = nullptr;
+  uint16_t* f16_phi = nullptr;
   float* ebound = nullptr;
   SegTable seg;
 };
@@ -236,8 +242,9 @@ hipError_t launch_gather(int dtype, const int32_t* perm, const uint8_t* keep,
 // (rn: M float2 of scratch), from the compacted rows (perm null: g = g_c,
 // phi = phi_c, alpha = alpha_c, row j) or through perm from the source rows
 // (bit for bit the score pass's per-pair norms either way).  Then
-// launch_split_f16 writes the two scaled float16 planes from the compacted
-// bf16 rows (bit for bit what the gather writes in the one-call path).
+// launch_split_f16 writes the scaled float16 planes (either may be null)
+// from the compacted bf16 rows, bit for bit what the gather writes in the
+// one-call path.
 hipError_t launch_expert_bounds(const SegTable& seg, const uint16_t* g, const uint16_t* phi,
                                 const float* alpha, const int32_t* perm,
                                 const int32_t* g_row_index, const int32_t* phi_row_index,
@@ -246,8 +253,8 @@ hipError_t launch_expert_bounds(const SegTable& seg, const uint16_t* g, const ui
                                 float* ebound, hipStream_t s);
 hipError_t launch_split_f16(const SegTable& seg, const uint16_t* g_c, const uint16_t* phi_c,
                             const float* alpha_c, int32_t M, int32_t d_out, int32_t d_in,
-                            bool alpha_on_phi, const float* ebound, uint16_t* f16_a,
-                            uint16_t* f16_b, hipStream_t s);
+                            bool alpha_on_phi, const float* ebound, uint16_t* f16_g,
+                            uint16_t* f16_phi, hipStream_t s);
 
 // hi (and lo, if non-null) bf16 planes of alpha[row] * src[row][col] (alpha
 // may be null); src is bf16 or float32 storage.

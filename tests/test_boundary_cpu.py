@@ -187,10 +187,17 @@ def test_workspace_size_and_check():
     p1 = plan(counts=(40, 20, 30), quotas=(30, 10, 20), d_out=64, d_in=32, dw_mode=L.DW_BF16)
     assert p1.workspace_bytes() == max(plane_phi, plane_g) + heads
     # float16 mode: counters and maxima, the score pass's per-pair row maxima
-    # (8 bytes per routed pair), then both float16 operand planes
+    # (8 bytes per routed pair), then the float16 plane of alpha * phi (the
+    # narrower operand; the GEMM converts g_c in registers)
     p2 = plan(counts=(40, 20, 30), quotas=(30, 10, 20), d_out=64, d_in=32, dw_mode=L.DW_F16)
-    f16 = (heads + 90 * 8 + 255) // 256 * 256 + plane_g + plane_phi
+    f16 = (heads + 90 * 8 + 255) // 256 * 256 + plane_phi
     assert p2.workspace_bytes() == max(f16, 2 * plane_g + heads)
+    # with the narrower operand wider than 1024, both float16 planes
+    p3 = plan(counts=(40, 20, 30), quotas=(30, 10, 20), d_out=2048, d_in=1152, dw_mode=L.DW_F16)
+    wide_g = (60 * 2048 * 2 + 255) // 256 * 256
+    wide_phi = (60 * 1152 * 2 + 255) // 256 * 256
+    f16 = (heads + 90 * 8 + 255) // 256 * 256 + wide_g + wide_phi
+    assert p3.workspace_bytes() == max(f16, 2 * wide_g + heads)
 
 
 def test_grouped_backward_gate_up_validation():

@@ -95,18 +95,20 @@ def _scaled_rows(x, offsets, factors):
     return W.to_bf16_bits(v.astype(np.float32))
 
 
-@pytest.mark.parametrize("swap", [False, True], ids=["alpha-on-phi", "alpha-on-g"])
-def test_f16_wide_range_per_expert(swap):
+@pytest.mark.parametrize("d_out,d_in", [(200, 136), (136, 200), (1160, 1040)],
+                         ids=["alpha-on-phi", "alpha-on-g", "two-planes"])
+def test_f16_wide_range_per_expert(d_out, d_in):
     """The float16 mode on inputs far outside float16's range: every expert's
     g rows and phi rows carry their own power of ten (g from 1e-7 to 1e5,
     phi from 1e-4 to 1e3), so unscaled products would overflow 65504 or
     vanish below float16's smallest normal.  The per-expert scales must map
     each expert into range: every expert's dW within 2e-3 of its own max|ref|
     (not just of the whole tensor's), through both paths (one call, and the
-    separate calls whose prologue finds the scales), bit for bit alike."""
+    separate calls whose prologue finds the scales), bit for bit alike.
+    Narrow shapes convert the operand without alpha in the GEMM's registers
+    (A or B); the last shape reads float16 planes of both."""
     import dataclasses
     counts = [400, 300, 350, 250, 300]
-    d_out, d_in = (136, 200) if swap else (200, 136)
     p = W.make_problem(P=sum(counts), E=5, d_out=d_out, d_in=d_in, dtype="bf16", counts=counts,
                        seed=61, policy=("ratio", 4, 5), name="wide-range")
     off = p.offsets
