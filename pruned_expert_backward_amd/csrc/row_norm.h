@@ -31,6 +31,19 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+
+// 16-byte load; NT marks it non-temporal (streamed once: the line is not kept
+// in the caches for reuse).
+template <bool NT>
+__device__ __forceinline__ uint4 load16(const uint4* __restrict__ p) {
+  if constexpr (NT) {
+    const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  } else {
+    return *p;
+  }
+}
 
 // Sum of squares of 8 bf16 values: one packed bf16 dot product per pair
 // (v_dot2c_f32_bf16: both products exact in float32, accumulated in float32).
@@ -40,17 +53,6 @@ __device__ __forceinline__ float dot2sq(uint32_t w, float acc) {
 }
 __device__ __forceinline__ float sumsq8(uint4 x) {
   return dot2sq(x.w, dot2sq(x.z, dot2sq(x.y, dot2sq(x.x, 0.f))));
-}
-
-// The lane's last 1..3 chunks of a row at once (zeros past the row end), so
-// that a short tail costs one memory round trip, not one per chunk.
-template <typename V>
-__device__ __forceinline__ void tail3(const V* __restrict__ row, int c, int nchunk, V& x0, V& x1,
-                                      V& x2) {
-  const V z = {};
-  x0 = row[c];
-  x1 = c + 64 < nchunk ? row[c + 64] : z;
-  x2 = c + 128 < nchunk ? row[c + 128] : z;
 }
 
 // This lane's shares of the sums of squares of a pair's two bf16 rows: the
@@ -63,6 +65,11 @@ __device__ __forceinline__ void tail3(const V* __restrict__ row, int c, int nchu
 // depend on the batch size.  A row that is not there (g_ok / p_ok
 // false) reads as zeros but keeps its chunk positions, so the other row's
 // sum is the same either way.  {x: g, y: phi}; reduce each with wave_sum.
+// NT: non-temporal loads, for the score pass, which streams every routed
+// row once (cached loads there left the previous step's dirty lines to be
+// written back under it: 8 % slower on the 655 360-pair workload, 29 % on
+// the 32 768-pair one).
+template <bool NT = false>
 __device__ __forceinline__ float2 pair_sumsq_bf16(const uint4* __restrict__ g, int gc, bool g_ok,
                                                   const uint4* __restrict__ phi, int pc,
                                                   bool p_ok, int lane) {
@@ -76,7 +83,7 @@ __device__ __forceinline__ float2 pair_sumsq_bf16(const uint4* __restrict__ g, i
       const bool in_g = c < gc;
       const uint4* src = in_g ? g + c : phi + (c - gc);
       const bool ok = c < n && (in_g ? g_ok : p_ok);
-      x[i] = ok ? *src : make_uint4(0u, 0u, 0u, 0u);
+      x[i] = ok ? load16<NT>(src) : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {

@@ -52,6 +52,14 @@ __device__ __forceinline__ float reduce16(const V& x) {
   else return ABS ? sumabs4(x) : sumsq4(x);
 }
 
+// Non-temporal 16-byte load of a uint4 or float4 chunk (the score pass
+// streams every row once).
+template <typename V>
+__device__ __forceinline__ V ld_stream(const V* __restrict__ p) {
+  const uint4 w = load16<true>(reinterpret_cast<const uint4*>(p));
+  return __builtin_bit_cast(V, w);
+}
+
 // Sum of squares (ABS: of absolute values) of one row held in 16-byte
 // chunks, lane-strided, four independent loads in flight per lane.
 template <bool ABS = false, typename V>
@@ -59,13 +67,17 @@ __device__ __forceinline__ float row_sumsq(const V* __restrict__ row, int nchunk
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
   int c = lane;
   for (; c + 192 < nchunk; c += 256) {
-    const V x0 = row[c], x1 = row[c + 64], x2 = row[c + 128], x3 = row[c + 192];
+    const V x0 = ld_stream(row + c), x1 = ld_stream(row + c + 64), x2 = ld_stream(row + c + 128),
+            x3 = ld_stream(row + c + 192);
     a0 += reduce16<ABS>(x0); a1 += reduce16<ABS>(x1);
     a2 += reduce16<ABS>(x2); a3 += reduce16<ABS>(x3);
   }
   if (c < nchunk) {
     V x0, x1, x2;
-    tail3(row, c, nchunk, x0, x1, x2);
+    const V z = {};   // the lane's last 1..3 chunks at once (zeros past the row end)
+    x0 = ld_stream(row + c);
+    x1 = c + 64 < nchunk ? ld_stream(row + c + 64) : z;
+    x2 = c + 128 < nchunk ? ld_stream(row + c + 128) : z;
     a0 += reduce16<ABS>(x0); a1 += reduce16<ABS>(x1); a2 += reduce16<ABS>(x2);
   }
   return (a0 + a1) + (a2 + a3);
@@ -102,7 +114,8 @@ __global__ __launch_bounds__(256) void lrm_score_kernel(
       constexpr bool WITH_PHI = LRM || RNORM;
       float gsq = 0.f, psq = 0.f;
       if (!L1 || RNORM) {
-        const float2 sq = pair_sumsq_bf16(grow, gc, gcr > 0, prow, WITH_PHI ? pc : 0, true, lane);
+        const float2 sq =
+            pair_sumsq_bf16<true>(grow, gc, gcr > 0, prow, WITH_PHI ? pc : 0, true, lane);
         gsq = wave_sum(sq.x);
         if (WITH_PHI) psq = wave_sum(sq.y);
       }
