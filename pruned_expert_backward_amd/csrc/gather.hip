@@ -216,17 +216,29 @@ __global__ __launch_bounds__(256) void row_norms_kernel(
 }
 
 // Step 2: ebound[e] = the largest rn over expert e's rows (0 when it has
-// none), one workgroup per expert.
-__global__ __launch_bounds__(256) void expert_bound_kernel(SegTable seg,
-                                                           const float2* __restrict__ rn,
-                                                           float* __restrict__ ebound) {
-  __shared__ uint32_t part[2][4];
+// none), one 1024-thread workgroup per expert, four independent loads in
+// flight per thread (one workgroup streams a 10 K-row expert in three
+// rounds, where one load per thread at a time took 44).
+constexpr int kBoundT = 1024;
+__global__ __launch_bounds__(kBoundT) void expert_bound_kernel(SegTable seg,
+                                                               const float2* __restrict__ rn,
+                                                               float* __restrict__ ebound) {
+  __shared__ uint32_t part[2][kBoundT / 64];
   const int e = blockIdx.x, tid = threadIdx.x;
+  const int lo = seg.off[e], hi = seg.off[e + 1];
   uint32_t a = 0u, b = 0u;   // non-negative float32 bit patterns order like their values
-  for (int j = seg.off[e] + tid; j < seg.off[e + 1]; j += 256) {
-    const float2 v = rn[j];
-    a = max(a, __float_as_uint(v.x));
-    b = max(b, __float_as_uint(v.y));
+  for (int j = lo + tid; j < hi; j += 4 * kBoundT) {
+    float2 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = j + i * kBoundT;
+      v[i] = r < hi ? rn[r] : make_float2(0.f, 0.f);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a = max(a, __float_as_uint(v[i].x));
+      b = max(b, __float_as_uint(v[i].y));
+    }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -239,9 +251,14 @@ __global__ __launch_bounds__(256) void expert_bound_kernel(SegTable seg,
   }
   __syncthreads();
   if (tid == 0) {
-    ebound[2 * e] = __uint_as_float(max(max(part[0][0], part[0][1]), max(part[0][2], part[0][3])));
-    ebound[2 * e + 1] =
-        __uint_as_float(max(max(part[1][0], part[1][1]), max(part[1][2], part[1][3])));
+    uint32_t ma = 0u, mb = 0u;
+#pragma unroll
+    for (int w = 0; w < kBoundT / 64; ++w) {
+      ma = max(ma, part[0][w]);
+      mb = max(mb, part[1][w]);
+    }
+    ebound[2 * e] = __uint_as_float(ma);
+    ebound[2 * e + 1] = __uint_as_float(mb);
   }
 }
 
@@ -322,15 +339,17 @@ hipError_t launch_expert_bounds(const SegTable& seg, const uint16_t* g, const ui
                                 int32_t d_out, int32_t d_in, bool alpha_on_phi, float2* rn,
                                 float* ebound, hipStream_t s) {
   if (M > 0) {
+    // one row per wave, as in the score pass (fresh workgroups balance the CUs
+    // better than waves looping over rows); grid-strided beyond 4 M rows
     int blocks = (M + 3) / 4;
-    if (blocks > 256 * 8) blocks = 256 * 8;   // 32 waves per CU, each looping over rows
+    if (blocks > 256 * 4096) blocks = 256 * 4096;
     hipLaunchKernelGGL(row_norms_kernel, dim3(blocks), dim3(256), 0, s, (const uint4*)g,
                        (const uint4*)phi, alpha, perm, g_row_index, phi_row_index, M, P, g_rows,
                        phi_rows, d_out / 8, d_in / 8, alpha_on_phi ? 1 : 0, rn);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(expert_bound_kernel, dim3(seg.E), dim3(256), 0, s, seg, rn, ebound);
+  hipLaunchKernelGGL(expert_bound_kernel, dim3(seg.E), dim3(kBoundT), 0, s, seg, rn, ebound);
   return hipGetLastError();
 }
 
