@@ -649,6 +649,7 @@ lrmoe_status pruned_backward(const lrmoe_problem* pb, const int32_t* g_row_index
   const size_t sel_off = wl.f16 ? wl.a_hi : 0;
   LRMOE_TRY(optional(dphi));
   const bool zfill = dphi != nullptr && zero_in_gemm(pb, M);
+  planes.stream_out = zfill;
   LRMOE_TRY(select_compact(pb, true, nullptr, g_row_index, alpha, g, phi, scores, keep,
                            seg_offsets, perm, g_c, phi_c, alpha_c, zfill ? nullptr : dphi,
                            reinterpret_cast<char*>(workspace) + sel_off, ws_bytes - sel_off,
@@ -786,6 +787,7 @@ lrmoe_status gather_backward(const lrmoe_problem* pb, const int32_t* perm, const
   // the dropped pairs' dphi rows: cleared by the gather, or (large fills)
   // inside the grouped GEMM launch
   const bool zfill = dphi != nullptr && zero_in_gemm(pb, c.M);
+  planes.stream_out = zfill;
   LRMOE_TRY(launch_gather_timed(pb, c, perm, keep, g_row_index, phi_row_index, alpha, g, phi, g_c,
                                 phi_c, alpha_c, zfill ? nullptr : dphi, phi_rows, s, timing,
                                 planes));

@@ -85,21 +85,42 @@ __device__ __forceinline__ uint4 f16_chunk(const uint4& x, float a, int s) {
   return __builtin_bit_cast(uint4, h);
 }
 
-// Copy of one bf16 row (dst may be null) and its float16 plane row.
+// 16-byte store; NT marks it non-temporal (the line is not kept in the
+// caches for reuse).
+template <bool NT>
+__device__ __forceinline__ void store16(uint4* __restrict__ p, const uint4& v) {
+  if constexpr (NT) {
+    typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(p));
+  } else {
+    *p = v;
+  }
+}
+
+// Copy of one bf16 row (dst may be null) and its float16 plane row.  NT:
+// non-temporal stores.  Where the grouped GEMM launch also clears the
+// dropped pairs' dphi rows (the 655 360-pair workload), the gather's 1.4 GB
+// of cached stores pushed the lines the GEMM re-reads out of the caches:
+// non-temporal ones cost the gather 14 us and saved the GEMM 40-55 us; on a
+// 32 768-pair workload they cost 23 us and saved 4-15.
+template <bool NT = false>
 __device__ __forceinline__ void copy_row_f16(const uint4* __restrict__ src,
                                              uint4* __restrict__ dst, uint4* __restrict__ pl,
                                              float a, int s, int nchunk, int lane) {
   int c = lane;
   for (; c + 64 < nchunk; c += 128) {
     const uint4 x0 = src[c], x1 = src[c + 64];
-    if (dst != nullptr) { dst[c] = x0; dst[c + 64] = x1; }
-    pl[c] = f16_chunk(x0, a, s);
-    pl[c + 64] = f16_chunk(x1, a, s);
+    if (dst != nullptr) {
+      store16<NT>(dst + c, x0);
+      store16<NT>(dst + c + 64, x1);
+    }
+    store16<NT>(pl + c, f16_chunk(x0, a, s));
+    store16<NT>(pl + c + 64, f16_chunk(x1, a, s));
   }
   for (; c < nchunk; c += 64) {
     const uint4 x = src[c];
-    if (dst != nullptr) dst[c] = x;
-    pl[c] = f16_chunk(x, a, s);
+    if (dst != nullptr) store16<NT>(dst + c, x);
+    store16<NT>(pl + c, f16_chunk(x, a, s));
   }
 }
 
@@ -108,6 +129,7 @@ struct F16Planes {
   uint4* phi;            // [M, d_in / 8], or null; both null: no float16 planes
   const float* ebound;   // [E][2]
   SegTable seg;
+  int nt;                // non-temporal stores of the copies and the planes
 };
 
 __global__ __launch_bounds__(256) void gather_kernel(
@@ -138,11 +160,14 @@ __global__ __launch_bounds__(256) void gather_kernel(
       const int sa = f16_scale_exp(f16.ebound[2 * e]), sb = f16_scale_exp(f16.ebound[2 * e + 1]);
       uint4* pg = f16.g != nullptr ? f16.g + (int64_t)j * gch : nullptr;
       uint4* pp = f16.phi != nullptr ? f16.phi + (int64_t)j * pch : nullptr;
+      const float ag = pl_from_phi ? 1.f : a, ap = pl_from_phi ? a : 1.f;
       if (!g_ok) zero_row(gdst, pg, nullptr, gch, lane);
-      else if (pg != nullptr) copy_row_f16(g + gr * gch, gdst, pg, pl_from_phi ? 1.f : a, sa, gch, lane);
+      else if (pg != nullptr && f16.nt) copy_row_f16<true>(g + gr * gch, gdst, pg, ag, sa, gch, lane);
+      else if (pg != nullptr) copy_row_f16(g + gr * gch, gdst, pg, ag, sa, gch, lane);
       else if (gdst != nullptr) copy_row(g + gr * gch, gdst, gch, lane);
       if (!p_ok) zero_row(pdst, pp, nullptr, pch, lane);
-      else if (pp != nullptr) copy_row_f16(phi + pr * pch, pdst, pp, pl_from_phi ? a : 1.f, sb, pch, lane);
+      else if (pp != nullptr && f16.nt) copy_row_f16<true>(phi + pr * pch, pdst, pp, ap, sb, pch, lane);
+      else if (pp != nullptr) copy_row_f16(phi + pr * pch, pdst, pp, ap, sb, pch, lane);
       else copy_row(phi + pr * pch, pdst, pch, lane);
     } else if (pl_hi != nullptr && !pl_from_phi) {
       uint4* h = pl_hi + (int64_t)j * gch;
@@ -320,7 +345,8 @@ hipError_t launch_gather(int dtype, const int32_t* perm, const uint8_t* keep,
   if ((planes.hi != nullptr || planes.f16_g != nullptr || planes.f16_phi != nullptr) &&
       dtype != LRMOE_BF16)
     return hipErrorInvalidValue;
-  F16Planes f16{(uint4*)planes.f16_g, (uint4*)planes.f16_phi, planes.ebound, planes.seg};
+  F16Planes f16{(uint4*)planes.f16_g, (uint4*)planes.f16_phi, planes.ebound, planes.seg,
+                planes.stream_out ? 1 : 0};
   const int64_t jobs = (int64_t)M + (dphi_zero ? (int64_t)P : 0);
   if (jobs == 0) return planes.nzero > 0 ? launch_zero(planes.zero, planes.nzero, s) : hipSuccess;
   const int64_t blocks = (jobs + 3) / 4;

@@ -225,6 +225,9 @@ struct GatherPlanes {
   uint16_t* f16_phi = nullptr;
   float* ebound = nullptr;
   SegTable seg;
+  // float16 mode: write the compacted rows and the planes with non-temporal
+  // stores (when the grouped GEMM launch also clears the dropped dphi rows)
+  bool stream_out = false;
 };
 
 // g has g_rows rows and phi phi_rows rows; a source row index outside them
