@@ -101,8 +101,8 @@ __device__ __forceinline__ void store16(uint4* __restrict__ p, const uint4& v) {
 // non-temporal stores.  Where the grouped GEMM launch also clears the
 // dropped pairs' dphi rows (the 655 360-pair workload), the gather's 1.4 GB
 // of cached stores pushed the lines the GEMM re-reads out of the caches:
-// non-temporal ones cost the gather 14 us and saved the GEMM 40-55 us; on a
-// 32 768-pair workload they cost 23 us and saved 4-15.
+// non-temporal ones cost the gather about 15 us and save the GEMM 30-55 us;
+// on a 32 768-pair workload without that fill they cost 23 us and saved 4-15.
 template <bool NT = false>
 __device__ __forceinline__ void copy_row_f16(const uint4* __restrict__ src,
                                              uint4* __restrict__ dst, uint4* __restrict__ pl,
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(256) void row_norms_kernel(
 // Step 2: ebound[e] = the largest rn over expert e's rows (0 when it has
 // none), one 1024-thread workgroup per expert, four independent loads in
 // flight per thread (one workgroup streams a 10 K-row expert in three
-// rounds, where one load per thread at a time took 44).
+// rounds, where 256 threads with one load each at a time took about 40).
 constexpr int kBoundT = 1024;
 __global__ __launch_bounds__(kBoundT) void expert_bound_kernel(SegTable seg,
                                                                const float2* __restrict__ rn,
