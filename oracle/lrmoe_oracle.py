@@ -54,8 +54,10 @@ Readings where the pages are silent (each also listed in the design notes):
 Pins: every function here is checked in tests/test_oracle_pins.py against
 something other than itself (brute force of the definition, the pages'
 worked example, autograd of the dense layer, algebraic identities).  The
-budget quota rule is a workload definition with no external value to pin
-against: parity unpinned for plan_quota's "budget" mode.
+budget quota rule is a reading (the pages give a budget but no formula for
+sharing it); its implementation is pinned by the properties every
+proportional share of a fixed budget has and by the pages' figures for the
+workload's budget, not by a value the pages print for it.
 """
 from __future__ import annotations
 

@@ -50,6 +50,46 @@ def check_quota_example(orc):
     assert orc.plan_quota([5, 0, 17, 1], ("ratio", 100, 100)) == [5, 0, 17, 1]
 
 
+def check_budget_quota(orc):
+    """The budget rule (a reading: the pages fix a token-buffer budget for the
+    20x batch-pressure run, [EN] "What the measurements show", but give no
+    formula for sharing it) against the properties any proportional share of
+    a fixed budget must have, on exact integers: no expert keeps more than it
+    routed; the kept total never exceeds the budget and loses less than one
+    pair per expert to rounding; every expert keeps the same fraction of its
+    pairs up to that rounding; a budget of every routed pair is the dense
+    backward and an empty budget keeps nothing.  Plus the budget of the
+    655 360-pair workload priced from the pages' figures (the fixed-ownership
+    token buffer of 12.46 GiB for the 32 768 pairs of a normal step, 8192
+    tokens x 4 microbatches per GPU, scaled to 24 GiB)."""
+    rng = np.random.default_rng(5)
+    cases = [[4, 2, 3], [0, 7, 0, 19, 1], [286057, 8823, 6455, 5898], [1] * 9, [0, 0]]
+    cases += [list(rng.integers(0, 400, size=int(rng.integers(1, 12)))) for _ in range(40)]
+    for counts in cases:
+        counts = [int(c) for c in counts]
+        P = sum(counts)
+        for Q in sorted({0, 1, P // 7, P // 2, max(P - 1, 0), P, P + 5, 3 * P + 1}):
+            q = orc.plan_quota(counts, ("budget", Q))
+            assert len(q) == len(counts)
+            assert all(0 <= a <= n for a, n in zip(q, counts))
+            if Q >= P:   # the budget covers every routed pair: the dense backward
+                assert q == counts
+                continue
+            assert sum(q) <= Q and Q - sum(q) < len([n for n in counts if n > 0])
+            for a, n in zip(q, counts):   # a / n = Q / P up to one pair: a <= nQ/P < a + 1
+                assert a * P <= n * Q < (a + 1) * P
+            if Q == 0:
+                assert q == [0] * len(counts)
+    # the workload's budget, from the pages' 12.46 GiB at 32 768 pairs
+    per_pair_gib = 12.46 / (8192 * 4)
+    assert W.GLM45_20X_BUDGET_PAIRS == int(24 / per_pair_gib + 1e-9)
+    p4_counts = W.zipf_counts(655360, 16, 1.4, 1004)
+    q4 = orc.plan_quota(p4_counts, ("budget", W.GLM45_20X_BUDGET_PAIRS))
+    assert W.GLM45_20X_BUDGET_PAIRS - 16 < sum(q4) <= W.GLM45_20X_BUDGET_PAIRS
+    # "most experts are cut well beyond 20 %": every expert keeps under 10 %
+    assert all(a < 0.1 * n for a, n in zip(q4, p4_counts))
+
+
 def check_score_bruteforce(orc):
     """R_u equals the squared Frobenius norm of the materialised rank-one
     gradient (alpha_u g_t) phi_u^T ([EN] "LRM: a decomposable contribution
@@ -326,7 +366,7 @@ def check_sampled_match_full(orc):
     assert np.allclose(rows, out["dphi"][pairs], rtol=1e-13, atol=0)
 
 
-CHECKS = [check_quota_example, check_score_bruteforce, check_gradient_scores,
+CHECKS = [check_quota_example, check_budget_quota, check_score_bruteforce, check_gradient_scores,
           check_select_bruteforce,
           check_compact_invariants, check_dense_equivalence, check_drop_identities,
           check_gate_up_inherits, check_glu_chain_autograd, check_glu_chain_sampled,
@@ -411,6 +451,20 @@ def _quota_round(counts, policy):
     return O.plan_quota(counts, policy)
 
 
+def _quota_budget_ceil(counts, policy):
+    if policy[0] == "budget":
+        Q, P = int(policy[1]), int(sum(counts))
+        return [int(c) if P == 0 else min(int(c), -(-int(c) * Q // P)) for c in counts]
+    return O.plan_quota(counts, policy)
+
+
+def _quota_budget_even(counts, policy):
+    if policy[0] == "budget":
+        per = int(policy[1]) // max(len(counts), 1)
+        return [min(int(c), per) for c in counts]
+    return O.plan_quota(counts, policy)
+
+
 def _input_grad_keep_dropped_rows(seg, perm, alpha_c, g_c, W, dtype, P):
     d = O.input_grad(seg, perm, alpha_c, g_c, W, dtype, P)
     d[d == 0] = 1e-3
@@ -466,6 +520,8 @@ MUTANTS = {
     "dW_drops_alpha": dict(weight_grad=_weight_grad_no_alpha),
     "perm_descending": dict(compact=_compact_unsorted),
     "quota_rounds": dict(plan_quota=_quota_round),
+    "budget_rounds_up": dict(plan_quota=_quota_budget_ceil),
+    "budget_split_evenly": dict(plan_quota=_quota_budget_even),
     "dropped_rows_nonzero": dict(input_grad=_input_grad_keep_dropped_rows),
     "l1_rule_uses_squares": dict(gradient_scores=_gradient_scores_l1_squares),
     "sqnorm_rule_not_squared": dict(gradient_scores=_gradient_scores_unsquared),
