@@ -152,6 +152,7 @@ struct TileJob {
   int e, m0, n0;
   int chunk, chunks;   // dW K chunk of this tile and the expert's chunk count
   bool tall;           // 512 x 128 edge tile over row tiles m0 / 256 and m0 / 256 + 1
+  bool half;           // 256 x 128 weight-gradient edge tile (waves of 128 x 64)
 };
 
 // Queue length of XCD x in item slots.
@@ -164,9 +165,10 @@ __device__ __forceinline__ int queue_items(const GemmTable& tab, int x) {
 // Item `i` of XCD x's queue -> tile; false for an idle slot.  With `tall`,
 // the last input-gradient column tile (and with `tall_dw` the last
 // weight-gradient one) of every even row tile becomes a 512 x 128 tile that
-// also covers the odd row tile below it, whose slot then idles.
+// also covers the odd row tile below it, whose slot then idles.  With
+// `half_dw` the last weight-gradient column tile is a 256 x 128 tile.
 __device__ __forceinline__ bool decode(const GemmTable& tab, int x, int i, bool& is_dw,
-                                      TileJob& job, bool tall, bool tall_dw) {
+                                      TileJob& job, bool tall, bool tall_dw, bool half_dw) {
   const int p = i / kGroupSlots, t = i % kGroupSlots;
   int e, chunk, lg;
   if (tab.use_table) {
@@ -207,6 +209,7 @@ __device__ __forceinline__ bool decode(const GemmTable& tab, int x, int i, bool&
   const int tiles_m = is_dw ? tab.dw_tiles_m : (q + BM - 1) / BM;
   if (tm >= tiles_m || tn >= tab.tiles_n) return false;
   job.tall = tall && (!is_dw || tall_dw) && tn == tab.tiles_n - 1;
+  job.half = half_dw && is_dw && tab.tall != 0 && tn == tab.tiles_n - 1;
   if (job.tall && (tm & 1)) return false;
   job.e = e;
   job.m0 = tm * BM;
@@ -296,12 +299,15 @@ constexpr int kPermBytes = kMaxRows * 8;
 // after its LDS fragment reads (A for F16 == 1, B for F16 == 2; see
 // cvt_slot).
 // TALL: a 512 x 128 tile (waves stacked 4 x 1) instead of 256 x 256.
-template <bool IS_DW, int PA, int PB, int NS, int GLU = 0, int F16 = 0, bool TALL = false>
+template <bool IS_DW, int PA, int PB, int NS, int GLU = 0, int F16 = 0, bool TALL = false,
+          bool HALF = false>
 struct Tile {
   static constexpr bool A_MC = IS_DW;
   static constexpr int TBM = TALL ? 2 * kTile : kTile;   // tile rows (M)
-  static constexpr int TBN = TALL ? kTile / 2 : kTile;   // tile columns (N)
-  static constexpr int kWN = TBN / WTN;                  // wave columns (1 or 2)
+  static constexpr int TBN = TALL || HALF ? kTile / 2 : kTile;   // tile columns (N)
+  static constexpr int WN = HALF ? WTN / 2 : WTN;       // columns of one wave's block
+  static constexpr int NB = WN / 32;                    // its 32-column accumulator blocks
+  static constexpr int kWN = TBN / WN;                  // wave columns (1 or 2)
   static_assert((TBM / WTM) * kWN == kWaves, "wave grid");
   // One K step of an operand plane: TBM (A) or TBN (B) values per K row.
   // MC rows are RA / RB bytes long (RA: weight-gradient tiles, 256 or 512
@@ -313,17 +319,17 @@ struct Tile {
   static constexpr int kPwA = kPlaneA / 1024 / kWaves, kPwB = kPlaneB / 1024 / kWaves;
   static constexpr int kLoads = PA * kPwA + PB * kPwB;   // load instructions per stage per wave
   static constexpr int kTerms = 1 + (PA == 2) + (PB == 2);
-  static constexpr int kHalfMfmas = kMB * kNB * kTerms; // per wave per half step
-  static constexpr int kFrags = PA * kMB + PB * kNB;     // fragments per half step
+  static constexpr int kHalfMfmas = kMB * NB * kTerms; // per wave per half step
+  static constexpr int kFrags = PA * kMB + PB * NB;     // fragments per half step
   static_assert(kFrags <= kHalfMfmas && kLoads <= kHalfMfmas, "interleave slots");
   // float16 mode: one term, and a converted fragment's 4 dwords spread over
   // the 4 MFMAs of the fragment before it
   static constexpr bool kCvt = IS_DW && (F16 == 1 || F16 == 2);
-  static_assert(!kCvt || (kTerms == 1 && kMB == 4 && kNB == 4), "float16 slots");
+  static_assert(!kCvt || (kTerms == 1 && kMB == 4 && NB == 4), "float16 slots");
 
   struct Frags {
     i16x8 a[PA][kMB];
-    i16x8 b[PB][kNB];
+    i16x8 b[PB][NB];
   };
 
   int e, m0, n0, chunk, chunks, q, seg, K, mrows, nk;
@@ -336,7 +342,7 @@ struct Tile {
   // LDS byte addresses of this lane's fragment reads in stage 0, plane 0:
   // MC operands: one per 32-wide fragment (half 0; half 1 is 16 rows on);
   // KC operand: one per half (fragment a is +2 KiB * a).
-  uint32_t la[kMB], lb[kNB];
+  uint32_t la[kMB], lb[NB];
   LDS_AS char* sink;   // kWaves x 1 KiB of LDS that only dead loads write
 
   __device__ __forceinline__ Tile(const Args& args, const GemmTable& tab, const TileJob& job,
@@ -344,7 +350,7 @@ struct Tile {
     const int tid = threadIdx.x;
     lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    wm = wave / kWN;   // wave block rows wm*WTM, columns wn*WTN
+    wm = wave / kWN;   // wave block rows wm*WTM, columns wn*WN
     wn = wave % kWN;
     // Tile coordinates are workgroup-uniform; say so, so that buffer
     // descriptors and LDS bases stay in scalar registers.
@@ -403,8 +409,8 @@ struct Tile {
       const int cl = 2 * (G & 1) + ((s & 3) >> 1);
       const int half = (s & 1) * 8;
 #pragma unroll
-      for (int f = 0; f < kNB; ++f)
-        lb[f] = base + (uint32_t)(mc_off<RB>(k0, (wn * WTN + f * 32) / 8 + cl) + half);
+      for (int f = 0; f < NB; ++f)
+        lb[f] = base + (uint32_t)(mc_off<RB>(k0, (wn * WN + f * 32) / 8 + cl) + half);
       if (A_MC) {
 #pragma unroll
         for (int f = 0; f < kMB; ++f)
@@ -469,7 +475,7 @@ struct Tile {
       if (A_MC) f.a[p][a] = frag_mc_at<RA>(la[a] + po + (uint32_t)(h * 16 * RA));
       else f.a[p][a] = frag_kc_at(la[h] + po + (uint32_t)(a * 2048));
     } else {
-      const int p = (i - PA * kMB) / kNB, b = (i - PA * kMB) % kNB;
+      const int p = (i - PA * kMB) / NB, b = (i - PA * kMB) % NB;
       f.b[p][b] =
           frag_mc_at<RB>(lb[b] + so + (uint32_t)(PA * kPlaneA + p * kPlaneB + h * 16 * RB));
     }
@@ -483,9 +489,9 @@ struct Tile {
   // by A fragment, or (F16 == 2) B fragment by B fragment: the converted
   // operand's fragments are used one after the other.
   __device__ __forceinline__ static void mfma_i(const Frags& f, f32x16 (&acc)[kMB][kNB], int i) {
-    const int t = i / (kMB * kNB), r = i % (kMB * kNB);
-    const int a = (IS_DW && F16 == 2) ? r % kMB : r / kNB;
-    const int b = (IS_DW && F16 == 2) ? r / kMB : r % kNB;
+    const int t = i / (kMB * NB), r = i % (kMB * NB);
+    const int a = (IS_DW && F16 == 2) ? r % kMB : r / NB;
+    const int b = (IS_DW && F16 == 2) ? r / kMB : r % NB;
     const int pa = (t == 2 || (t == 1 && PB == 1)) ? PA - 1 : 0;
     const int pb = (t == 1 && PB == 2) ? 1 : 0;
     if constexpr (IS_DW && F16) acc[a][b] = mfma_f16(f.b[pb][b], f.a[pa][a], acc[a][b]);
@@ -515,7 +521,7 @@ struct Tile {
     if constexpr (kCvt) {
       const int grp = i / 4, p = i % 4;
       if constexpr (F16 == 1) cvt_piece(grp + 1 < kMB ? F.a[0][grp + 1] : G.a[0][0], p);
-      else cvt_piece(grp + 1 < kNB ? F.b[0][grp + 1] : G.b[0][0], p);
+      else cvt_piece(grp + 1 < NB ? F.b[0][grp + 1] : G.b[0][0], p);
     }
   }
   // The first fragment of a freshly read set, all at once (tile start).
@@ -594,7 +600,7 @@ struct Tile {
 #pragma unroll
     for (int a = 0; a < kMB; ++a)
 #pragma unroll
-      for (int b = 0; b < kNB; ++b)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
     if (nk == 0) return;
@@ -638,12 +644,12 @@ struct Tile {
   // a row (u < 0) or past the matrix edge (column counts are multiples of 8)
   // load column 0 of row 0 instead.
   struct GluRow {
-    u32x4 a[kNB][2], b[kNB][2];   // [block b][group pair h]
+    u32x4 a[NB][2], b[NB][2];   // [block b][group pair h]
   };
 
   // First column of the 8-column group this lane moves for pair (b, h).
   __device__ __forceinline__ int glu_col(int ln, int b, int h) const {
-    return wn * WTN + b * 32 + 16 * h + 8 * (ln >> 5);
+    return wn * WN + b * 32 + 16 * h + 8 * (ln >> 5);
   }
 
   __device__ __forceinline__ void glu_load(const Args& args, int32_t u, int ln, int ncols,
@@ -654,7 +660,7 @@ struct Tile {
     const uint16_t* arow = args.ops.glu_a + src;
     const uint16_t* brow = args.ops.glu_b + src;
 #pragma unroll
-    for (int b = 0; b < kNB; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int col = glu_col(ln, b, h);
@@ -714,7 +720,7 @@ struct Tile {
       float* gate = reinterpret_cast<float*>(args.ops.glu_out) + j * (2 * (int64_t)d_in) + n0;
       float* up = gate + d_in;
 #pragma unroll
-      for (int b = 0; b < kNB; ++b)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           u32x2 qa[2], qb[2];
@@ -737,7 +743,7 @@ struct Tile {
             f32x4 gv, uv;
             glu_quad_f32(qa[t], qb[t], d, gv, uv);
             // columns of register quad g: 8 g + 4 (lane / 32) .. + 3 of block b
-            const int col = wn * WTN + b * 32 + 8 * g + 4 * (ln >> 5);
+            const int col = wn * WN + b * 32 + 8 * g + 4 * (ln >> 5);
             if (u >= 0 && col < ncols) {
               *reinterpret_cast<f32x4*>(gate + col) = gv;
               *reinterpret_cast<f32x4*>(up + col) = uv;
@@ -749,7 +755,7 @@ struct Tile {
     uint16_t* gate = reinterpret_cast<uint16_t*>(args.ops.glu_out) + j * (2 * (int64_t)d_in) + n0;
     uint16_t* up = gate + d_in;
 #pragma unroll
-    for (int b = 0; b < kNB; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         // this lane's quads of groups g0 and g1: its own half of the 16 bytes
@@ -891,10 +897,10 @@ struct Tile {
         }
       }
 #pragma unroll
-      for (int b = 0; b < kNB; ++b)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-          const int col = wn * WTN + b * 32 + 16 * p + cq;
+          const int col = wn * WN + b * 32 + 16 * p + cq;
           f32x4 v0, v1;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -1009,6 +1015,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_backward_kernel(Args args
   constexpr bool kTallDw = kTall && C::tall_dw;
   using DpTall = Tile<false, DP_PA, DP_PB, kTall ? C::NS_DPT : 2, 0, false, true>;
   using DwTall = Tile<true, DW_PA, DW_PB, kTallDw ? C::NS_DWT : 2, 0, DW_F16, true>;
+  // 256 x 128 weight-gradient tiles for a last column of at most 128 columns,
+  // where weight-gradient tiles are not tall (one operand plane per side, no
+  // conversion in registers): no MFMA works on the empty half
+  constexpr bool kHalfDw =
+      !kTallDw && GLU == 0 && DW_PA == 1 && DW_PB == 1 && (DW_F16 == 0 || DW_F16 == 3);
+  constexpr int kHalfStage = DW_PA * kPlaneBytes + DW_PB * kPlaneBytes / 2;
+  constexpr int kNsHalf = C::stages / kHalfStage > 4 ? 4 : C::stages / kHalfStage;
+  using DwHalf = Tile<true, DW_PA, DW_PB, kHalfDw ? kNsHalf : 2, 0, kHalfDw ? DW_F16 : 0, false,
+                      true>;
   const bool tall_on = kTall && tab.tall != 0;
   __shared__ __attribute__((aligned(16))) char smem_raw[C::bytes];
   LDS_AS char* smem = (LDS_AS char*)(smem_raw);
@@ -1035,7 +1050,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_backward_kernel(Args args
         ++hop;
         continue;
       }
-      if (decode(tab, qx, i, is_dw, job, tall_on, kTallDw)) return i;
+      if (decode(tab, qx, i, is_dw, job, tall_on, kTallDw, kHalfDw)) return i;
     }
     return -1;
   };
@@ -1045,6 +1060,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_backward_kernel(Args args
       if constexpr (kTallDw) {
         if (j.tall) {
           fn(DwTall(args, tab, j, smem, sink));
+          return;
+        }
+      }
+      if constexpr (kHalfDw) {
+        if (j.half) {
+          fn(DwHalf(args, tab, j, smem, sink));
           return;
         }
       }

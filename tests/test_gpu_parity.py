@@ -815,6 +815,23 @@ def test_timer_leaves_no_hip_error_for_unlaunched_kernels():
         timer.close()
 
 
+@pytest.mark.parametrize("dw_mode", [lrmoe.DW_F16, lrmoe.DW_BF16])
+def test_half_weight_gradient_edge_tiles(dw_mode):
+    """A last column of at most 128 columns (d_in = 1088 = 4 x 256 + 64) with
+    one operand plane per side: the weight-gradient tiles of that column are
+    256 x 128 (float16 mode with both sides wider than 1024, or single
+    rounding).  Expert 0 keeps more than one K chunk, so its half tiles also
+    write split-K partial tiles."""
+    counts = [2000, 700, 300]
+    p = W.make_problem(P=sum(counts), E=3, d_out=1152, d_in=1088, dtype="bf16", counts=counts,
+                       seed=91)
+    q = lrmoe.plan_quota(p.counts, ("ratio", 4, 5))
+    print(f"half dW edge tiles: mode {dw_mode} quotas={q}", flush=True)
+    _, out, _ = U.run_gpu(p, q, dw_mode=dw_mode)
+    errs, _ = U.compare_full(p, q, out, dw_mode=dw_mode)
+    print("half dW edge tiles", errs)
+
+
 @pytest.mark.parametrize("dtype,d_out,d_in", [("f32", 68, 36), ("bf16", 72, 264)])
 def test_epilogue_column_edges(dtype, d_out, d_in):
     """Matrix edges inside the epilogue's 16-column store groups: the last
