@@ -430,10 +430,14 @@ def main():
     if whole and p.dtype == "bf16" and "gather" in kernels:
         # what the gather writes beyond the method's bytes: the GEMM's operand
         # planes (alpha times the narrower operand, hi + lo in exact mode; in
-        # the float16 mode both operands as scaled float16)
-        kernels["gather"]["gemm_plane_bytes"] = (
-            M * (d_o + d_i) * 2 if args.dw_mode == "f16"       # both float16 planes
-            else M * min(d_o, d_i) * 2 * (2 if args.dw_mode == "exact" else 1))
+        # the float16 mode the scaled float16 planes: both operands when the
+        # narrower one is wider than 1024, else only the one with alpha, the
+        # GEMM converting the other in registers)
+        if args.dw_mode == "f16":
+            plane_cols = d_o + d_i if min(d_o, d_i) > 1024 else min(d_o, d_i)
+        else:
+            plane_cols = min(d_o, d_i) * (2 if args.dw_mode == "exact" else 1)
+        kernels["gather"]["gemm_plane_bytes"] = M * plane_cols * 2
     ssc_us = sum(us[n] for n in ("lrm_score", "select_scan", "gather") if us[n] is not None)
     nbytes = algorithmic_bytes(p, M, args.score_mode)
     if chain or zero_in_gemm:   # no dphi rows to zero in the original layout, or

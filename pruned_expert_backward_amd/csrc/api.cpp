@@ -594,9 +594,14 @@ lrmoe_status grouped_backward(const lrmoe_problem* pb, const int32_t* perm, cons
   LRMOE_TRY(hip_status(launch_grouped_backward(t, ops, perm, alpha_c, dW, dphi, d_out, d_in,
                                                (int32_t)pb->P, s)));
   LRMOE_TRY(mark(timing, true, ts.gemm, s));
-  LRMOE_TRY(mark(timing, false, ts.reduce, s));
+  // the reduction runs only when an expert's weight gradient was split along
+  // K; otherwise its timing events stay unrecorded, like those of any kernel
+  // a call does not launch
+  bool split = false;
+  for (int e = 0; e < E && !split; ++e) split = dw_chunks((int)pb->quotas[e], t.kc) > 1;
+  if (split) LRMOE_TRY(mark(timing, false, ts.reduce, s));
   LRMOE_TRY(hip_status(launch_reduce_partials(t, ops.partials, dW, d_out, d_in, s)));
-  LRMOE_TRY(mark(timing, true, ts.reduce, s));
+  if (split) LRMOE_TRY(mark(timing, true, ts.reduce, s));
   return LRMOE_OK;
 }
 
