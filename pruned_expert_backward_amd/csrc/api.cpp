@@ -233,17 +233,22 @@ size_t workspace_bytes(const lrmoe_problem* pb, const Checked& c) {
 }
 
 // Group shape gm x gn (gm * gn = kGroupSlots) over an expert's tile grid with
-// nt column tiles: gn among the divisors of kGroupSlots, least idle slots at
-// the grid edge, ties to `pref`.
+// nt column tiles.  A group reads gm row panels and gn column panels of equal
+// size (256 operand rows or columns by the K extent), so the shape takes the
+// least idle slots at the grid edge, then the least gm + gn, then gn nearest
+// `pref`.
 void group_shape(int nt, int pref, int32_t& gm, int32_t& gn) {
   const int cands[6] = {1, 2, 3, 4, 6, 12};
-  int best = -1, best_waste = 1 << 30, best_dist = 1 << 30;
+  int best = -1, best_waste = 1 << 30, best_sum = 1 << 30, best_dist = 1 << 30;
   for (int c : cands) {
     const int waste = ((nt + c - 1) / c) * c - nt;
+    const int sum = c + kGroupSlots / c;
     const int dist = c > pref ? c - pref : pref - c;
-    if (waste < best_waste || (waste == best_waste && dist < best_dist)) {
+    if (waste < best_waste || (waste == best_waste && sum < best_sum) ||
+        (waste == best_waste && sum == best_sum && dist < best_dist)) {
       best = c;
       best_waste = waste;
+      best_sum = sum;
       best_dist = dist;
     }
   }
@@ -408,7 +413,7 @@ lrmoe_status grouped_backward(const lrmoe_problem* pb, const int32_t* perm, cons
   t.dw_tiles_m = (d_out + kTile - 1) / kTile;
   t.kc = wl.kc;
   group_shape(t.tiles_n, 3, t.dw_gm, t.dw_gn);
-  group_shape(t.tiles_n, 6, t.dp_gm, t.dp_gn);
+  group_shape(t.tiles_n, 3, t.dp_gm, t.dp_gn);
   // a last column of at most 128 columns: 512 x 128 input-gradient tiles
   // there, none of them half empty (the SiLU-GLU epilogue keeps square tiles)
   t.tall = !glu && d_in % kTile != 0 && d_in % kTile <= kTile / 2;
