@@ -845,3 +845,30 @@ def test_epilogue_column_edges(dtype, d_out, d_in):
     print(f"edges: {dtype} d_out={d_out} d_in={d_in} quotas={q}", flush=True)
     _, out, _ = U.run_gpu(p, q)
     U.compare_full(p, q, out)
+
+
+@pytest.mark.parametrize("dtype,dw_mode,d_out,d_in", [
+    # four column tiles, the last one 32 wide: 3 x 4 groups (an odd number of
+    # row tiles per group) with tall 512 x 128 edge tiles of both products in
+    # the exact mode, and five row tiles of dW (the last tall dW tile covers a
+    # row tile past d_out)
+    ("bf16", lrmoe.DW_EXACT, 1280, 800),
+    # eight column tiles: 3 x 4 groups, float16 dW converted in registers
+    ("bf16", lrmoe.DW_F16, 1024, 2048),
+    # six column tiles (the GLM width): 4 x 3 groups, both float16 planes,
+    # half dW and tall input-gradient edge tiles
+    ("bf16", lrmoe.DW_F16, 2048, 1408),
+    # sixteen column tiles, single rounding
+    ("bf16", lrmoe.DW_BF16, 768, 4096),
+])
+def test_group_shapes(dtype, dw_mode, d_out, d_in):
+    """Tile groups of every shape the schedule picks for wide problems, with a
+    split-K expert (expert 0 keeps more rows than one K chunk)."""
+    counts = [3000, 900, 250]
+    p = W.make_problem(P=sum(counts), E=3, d_out=d_out, d_in=d_in, dtype=dtype, counts=counts,
+                       seed=d_out + d_in)
+    q = lrmoe.plan_quota(p.counts, ("ratio", 4, 5))
+    print(f"group shapes: mode {dw_mode} d_out={d_out} d_in={d_in} quotas={q}", flush=True)
+    _, out, _ = U.run_gpu(p, q, dw_mode=dw_mode)
+    errs, _ = U.compare_full(p, q, out, dw_mode=dw_mode)
+    print("group shapes", errs)
